@@ -1,0 +1,29 @@
+"""Compressed KV bytes, the closed form behind compressed_storage_bytes().
+
+FADE post, section "使用注意事项" (measure KV memory with the cache's own
+byte count rather than device-level tools) and "性能基准" (memory figures).
+Reading: the live bytes of every tier, per layer and sequence,
+
+  Hkv * [ F * d * 2 * 2                                  (fp16 K and V)
+        + M * ( (d*kb/8 + 2*d/G) + (d*vb/8 + 2*d/G) ) ]  (codes + fp16 scales)
+
+with F = sink + recent slots and M = middle slots. Scores and lengths are not
+KV bytes.
+"""
+
+
+def compressed_bytes(head_dim, n_kv_heads, kb, vb, group, fp16_slots, mid_slots):
+    """Sum over the given per-(layer, sequence) slot counts."""
+    d = head_dim
+    per_fp = n_kv_heads * d * 2 * 2
+    per_mid = n_kv_heads * ((d * kb // 8 + 2 * d // group) + (d * vb // 8 + 2 * d // group))
+    return sum(f * per_fp for f in fp16_slots) + sum(m * per_mid for m in mid_slots)
+
+
+def cache_bytes(cache):
+    """Live bytes of an oracle SeqCache, counted from its arrays."""
+    c = cache.cfg
+    n = cache.sink_k.nbytes + cache.sink_v.nbytes + cache.rec_k.nbytes + cache.rec_v.nbytes
+    n += cache.mid_k_u.size * c.middle_k_bits // 8 + cache.mid_k_s.nbytes
+    n += cache.mid_v_u.size * c.middle_v_bits // 8 + cache.mid_v_s.nbytes
+    return n

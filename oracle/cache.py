@@ -1,0 +1,300 @@
+"""The three-tier KV cache of one layer, as a plain logical state, float64.
+
+FADE post, section "核心机制：三层级缓存架构":
+  * tier 1 keeps the first N_SINK tokens (sinks) and the last RECENT_WINDOW
+    tokens at FP16;
+  * tier 2 stores the middle-aged tokens, the bulk of the cache, as bit-packed
+    4-bit codes; tier 3 (optional) goes down to 2 bits;
+  * once INT4_BUDGET is reached tokens are evicted, and surviving keys are
+    un-rotated at their old position and re-rotated at their contiguous
+    StreamingLLM position (also section "RoPE重计算").
+Transformer series (25), section 1.2.2 StreamingLLM: positions are taken
+inside the cache (sink tokens followed by the rolling window), which is what
+"contiguous position" means here: a slot's position is its index in the
+compacted cache.
+
+Readings taken where the pages are silent:
+  * Tier layout of T live slots: sink = [0, min(n_sink, T)); recent = the
+    last min(R, T - n_sink) slots; middle = the rest. R = recent_window
+    after maintenance and recent_window + 1 while the current token is in.
+  * The optional INT2 tier is the middle tier's V at middle_v_bits = 2 (FADE
+    post, "量化与Bit-Packing": K stays INT4, V may drop to INT2); K uses
+    middle_k_bits.
+  * Decode step order: append the new token (rotated by the caller at
+    position T) to the recent tier, attend over all T + 1 slots, update the
+    scores, demote the oldest recent token into the middle tier if the
+    window overflows, then run an eviction event if one is due.
+  * Eviction event: candidates are the middle slots only; they are ordered by
+    (score ascending, slot ascending) and the first M - budget are evicted
+    (lower score first, older first on ties - the position policy's "older
+    first", FADE post "位置策略"). Survivors keep their order.
+  * Re-RoPE: every surviving key whose slot index changed is un-rotated at
+    the old index and re-rotated at the new one, rounded once to fp16; a
+    middle key is dequantized first and requantized after. Values move
+    bit-for-bit. Slots whose index does not change are untouched.
+  * At prefill the order is score -> select -> compact / re-RoPE on the fp16
+    prefill -> quantize the middle survivors.
+"""
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from . import quant, rope
+from .attention import decode_attention
+from .h2o import update_accum, update_ema
+
+
+@dataclass
+class Config:
+    head_dim: int
+    n_q_heads: int
+    n_kv_heads: int
+    n_sink: int
+    recent_window: int
+    int4_budget: int            # -1: never evict (Safe preset)
+    middle_k_bits: int = 4
+    middle_v_bits: int = 4
+    group_size: int = 32
+    rope_theta: float = 10000.0
+    rope_type: str = "default"
+    rope_factor: float = 1.0
+    rope_low_freq_factor: float = 1.0
+    rope_high_freq_factor: float = 4.0
+    rope_original_max_position: int = 8192
+
+    def freqs(self):
+        return rope.inv_freq(self.head_dim, self.rope_theta, self.rope_type,
+                             self.rope_factor, self.rope_low_freq_factor,
+                             self.rope_high_freq_factor,
+                             self.rope_original_max_position)
+
+
+def tier_layout(t, n_sink, recent):
+    """(sink, middle, recent) counts for t live slots."""
+    s = min(n_sink, t)
+    r = min(recent, t - s)
+    return s, t - s - r, r
+
+
+def select_evicted(mid_scores, n_evict):
+    """Indices (ascending) of the n_evict middle slots to evict: order by
+    (score ascending, slot ascending) and take the first n_evict."""
+    mid_scores = np.asarray(mid_scores, dtype=np.float64)
+    if n_evict <= 0:
+        return np.zeros(0, dtype=np.int64)
+    order = np.lexsort((np.arange(mid_scores.size), mid_scores))
+    return np.sort(order[:n_evict])
+
+
+@dataclass
+class SeqCache:
+    """One sequence, all KV heads, one layer. Slot order = position order."""
+    cfg: Config
+    sink_k: np.ndarray          # float16 [Hkv, S, d]
+    sink_v: np.ndarray
+    mid_k_u: np.ndarray         # uint8 codes [Hkv, M, d]
+    mid_k_s: np.ndarray         # float16 scales [Hkv, M, d/G]
+    mid_v_u: np.ndarray
+    mid_v_s: np.ndarray
+    rec_k: np.ndarray           # float16 [Hkv, R, d], oldest first
+    rec_v: np.ndarray
+    scores: np.ndarray = field(default=None)   # float64 [T]
+
+    @property
+    def n_sink_live(self):
+        return self.sink_k.shape[1]
+
+    @property
+    def mid_len(self):
+        return self.mid_k_u.shape[1]
+
+    @property
+    def rec_len(self):
+        return self.rec_k.shape[1]
+
+    @property
+    def length(self):
+        return self.n_sink_live + self.mid_len + self.rec_len
+
+    def dense(self):
+        """(k_hat, v_hat) float64 [Hkv, T, d] in slot order."""
+        c = self.cfg
+        g = c.group_size
+        mk = quant.dequantize(self.mid_k_u, self.mid_k_s, c.middle_k_bits, g)
+        mv = quant.dequantize(self.mid_v_u, self.mid_v_s, c.middle_v_bits, g)
+        k = np.concatenate([self.sink_k.astype(np.float64), mk,
+                            self.rec_k.astype(np.float64)], axis=1)
+        v = np.concatenate([self.sink_v.astype(np.float64), mv,
+                            self.rec_v.astype(np.float64)], axis=1)
+        return k, v
+
+
+def _empty_codes(hkv, d, g):
+    return (np.zeros((hkv, 0, d), np.uint8), np.zeros((hkv, 0, d // g), np.float16))
+
+
+def build_from_prefill(cfg, k16, v16, scores=None):
+    """Tiered cache from a prefill of L tokens.
+
+    k16, v16: fp16 [Hkv, L, d], keys rotated at positions 0..L-1.
+    scores: float64 [L] H2O prefill scores, or None for the position policy
+    (older middle tokens evicted first)."""
+    k16 = np.asarray(k16, dtype=np.float16)
+    v16 = np.asarray(v16, dtype=np.float16)
+    hkv, L, d = k16.shape
+    s, m, r = tier_layout(L, cfg.n_sink, cfg.recent_window)
+    mid_scores = (np.arange(m, dtype=np.float64) if scores is None
+                  else np.asarray(scores, np.float64)[s:s + m])
+    n_evict = m - cfg.int4_budget if 0 <= cfg.int4_budget < m else 0
+    evicted = set(select_evicted(mid_scores, n_evict).tolist())
+    kept_mid = np.array([s + i for i in range(m) if i not in evicted], dtype=np.int64)
+    survivors = np.concatenate([np.arange(s), kept_mid, np.arange(s + m, L)]).astype(np.int64)
+    new_pos = np.arange(survivors.size)
+    freqs = cfg.freqs()
+    k_surv = k16[:, survivors].copy()
+    moved = survivors != new_pos
+    if moved.any():
+        k_surv[:, moved] = rope.rerope_fp16(k16[:, survivors[moved]],
+                                            survivors[moved], new_pos[moved], freqs)
+    v_surv = v16[:, survivors]
+    m2 = kept_mid.size
+    mk = k_surv[:, s:s + m2]
+    mv = v_surv[:, s:s + m2]
+    g = cfg.group_size
+    if m2:
+        mk_u, mk_s = quant.quantize(mk, cfg.middle_k_bits, g)
+        mv_u, mv_s = quant.quantize(mv, cfg.middle_v_bits, g)
+    else:
+        mk_u, mk_s = _empty_codes(hkv, d, g)
+        mv_u, mv_s = _empty_codes(hkv, d, g)
+    sc = (np.zeros(survivors.size) if scores is None
+          else np.asarray(scores, np.float64)[survivors].copy())
+    return SeqCache(cfg, k_surv[:, :s].copy(), v_surv[:, :s].copy(), mk_u, mk_s, mv_u, mv_s,
+                    k_surv[:, s + m2:].copy(), v_surv[:, s + m2:].copy(), sc)
+
+
+def append(cache, k_new16, v_new16):
+    """Add the newest token ([Hkv, d] fp16, key already rotated at position
+    cache.length) to the sink tier while it is not full, else to the recent
+    tier. Its score starts at 0."""
+    k_new16 = np.asarray(k_new16, np.float16)[:, None, :]
+    v_new16 = np.asarray(v_new16, np.float16)[:, None, :]
+    if cache.n_sink_live < cache.cfg.n_sink:
+        cache.sink_k = np.concatenate([cache.sink_k, k_new16], axis=1)
+        cache.sink_v = np.concatenate([cache.sink_v, v_new16], axis=1)
+    else:
+        cache.rec_k = np.concatenate([cache.rec_k, k_new16], axis=1)
+        cache.rec_v = np.concatenate([cache.rec_v, v_new16], axis=1)
+    cache.scores = np.concatenate([cache.scores, [0.0]])
+
+
+def attend(cache, q16):
+    """Decode attention of q [Hq, d] (fp16 or bf16 values) over every slot."""
+    k, v = cache.dense()
+    return decode_attention(np.asarray(q16).astype(np.float64), k, v)
+
+
+def demote(cache):
+    """Move the oldest recent tokens into the middle tail while the recent
+    tier holds more than recent_window tokens (positions do not change)."""
+    c = cache.cfg
+    while cache.rec_len > c.recent_window:
+        k0, v0 = cache.rec_k[:, :1], cache.rec_v[:, :1]
+        ku, ks = quant.quantize(k0, c.middle_k_bits, c.group_size)
+        vu, vs = quant.quantize(v0, c.middle_v_bits, c.group_size)
+        cache.mid_k_u = np.concatenate([cache.mid_k_u, ku], axis=1)
+        cache.mid_k_s = np.concatenate([cache.mid_k_s, ks], axis=1)
+        cache.mid_v_u = np.concatenate([cache.mid_v_u, vu], axis=1)
+        cache.mid_v_s = np.concatenate([cache.mid_v_s, vs], axis=1)
+        cache.rec_k = cache.rec_k[:, 1:]
+        cache.rec_v = cache.rec_v[:, 1:]
+
+
+def evict(cache, budget, policy="score", evicted=None):
+    """Eviction event: if the middle tier holds more than `budget` tokens,
+    evict down to `budget` and compact with un-RoPE / re-RoPE.
+
+    policy "score" ranks by cache.scores (H2O or EMA), "position" by slot.
+    `evicted` may force the evicted middle indices (used by multi-step tests
+    to follow the device's choice inside a near-tie band).
+    Returns the sorted evicted middle indices."""
+    c = cache.cfg
+    m = cache.mid_len
+    s = cache.n_sink_live
+    if budget < 0 or m <= budget:
+        return np.zeros(0, dtype=np.int64)
+    n_evict = m - budget
+    if evicted is None:
+        mid_scores = (np.arange(m, dtype=np.float64) if policy == "position"
+                      else cache.scores[s:s + m])
+        evicted = select_evicted(mid_scores, n_evict)
+    evicted = np.asarray(evicted, dtype=np.int64)
+    keep = np.ones(m, dtype=bool)
+    keep[evicted] = False
+    kept = np.nonzero(keep)[0]
+    freqs = c.freqs()
+    g = c.group_size
+    old_pos = s + kept
+    new_pos = s + np.arange(kept.size)
+    mk_u = cache.mid_k_u[:, kept].copy()
+    mk_s = cache.mid_k_s[:, kept].copy()
+    moved = old_pos != new_pos
+    if moved.any():
+        khat = quant.dequantize(mk_u[:, moved], mk_s[:, moved], c.middle_k_bits, g)
+        rot = rope.rerope_fp16(khat, old_pos[moved], new_pos[moved], freqs)
+        u2, s2 = quant.quantize(rot, c.middle_k_bits, g)
+        mk_u[:, moved] = u2
+        mk_s[:, moved] = s2
+    cache.mid_k_u, cache.mid_k_s = mk_u, mk_s
+    cache.mid_v_u = cache.mid_v_u[:, kept].copy()
+    cache.mid_v_s = cache.mid_v_s[:, kept].copy()
+    r = cache.rec_len
+    if r:
+        old_r = s + m + np.arange(r)
+        new_r = old_r - n_evict
+        cache.rec_k = rope.rerope_fp16(cache.rec_k, old_r, new_r, freqs)
+    survivors = np.concatenate([np.arange(s), s + kept, s + m + np.arange(r)])
+    cache.scores = cache.scores[survivors].copy()
+    return evicted
+
+
+def update_scores(caches, sides, mode, beta=0.9, shared=False):
+    """Apply the decode-time score update to every row. In shared mode the
+    side outputs are summed over rows and every row receives the same
+    update, so rows keep identical scores and identical decisions."""
+    if mode == "none":
+        return
+    if shared:
+        tot = np.sum(np.stack(sides), axis=0)
+        sides = [tot] * len(caches)
+    for cache, a in zip(caches, sides):
+        if mode == "accum":
+            cache.scores = update_accum(cache.scores, a)
+        elif mode == "ema":
+            cache.scores = update_ema(cache.scores, a, beta)
+        else:
+            raise ValueError(mode)
+
+
+def decode_step(caches, q16, k_new16, v_new16, mode="none", beta=0.9,
+                shared=False, evict_now=True, policy="score", forced=None):
+    """One decode step of one layer over a batch of SeqCache rows.
+
+    q16 [B, Hq, d], k_new16 / v_new16 [B, Hkv, d]. Returns
+    (out [B, Hq, d] float64, sides list of [T_b], evicted list)."""
+    outs, sides = [], []
+    for b, cache in enumerate(caches):
+        append(cache, k_new16[b], v_new16[b])
+        o, _, a = attend(cache, q16[b])
+        outs.append(o)
+        sides.append(a)
+    update_scores(caches, sides, mode, beta, shared)
+    ev = []
+    for b, cache in enumerate(caches):
+        demote(cache)
+        if evict_now:
+            f = None if forced is None else forced[b]
+            ev.append(evict(cache, cache.cfg.int4_budget, policy, f))
+        else:
+            ev.append(np.zeros(0, dtype=np.int64))
+    return np.stack(outs), sides, ev

@@ -1,0 +1,81 @@
+"""Rotary position embedding, float64.
+
+FADE post, section "RoPE方案兼容性" (RoPE scheme compatibility): the cache
+must handle standard RoPE (Qwen2/Qwen3, Mistral, Phi-3, Gemma-2) and
+Llama-3.x frequency-dependent scaling (scaling type "llama3"). The post
+names the schemes but prints no formula, so:
+
+* Pairing (reading): "rotate half" - channel i is paired with channel
+  i + d/2, the convention of the Qwen2 / Llama model families the post names.
+* Standard frequencies: inv_freq_i = theta^(-2i/d), i < d/2.
+* llama3 scaling (reading: the published Llama-3.1 rule, which the post
+  names only as "llama3"): with wavelength wl_i = 2*pi / inv_freq_i,
+    wl_i < orig/high_freq_factor  -> keep inv_freq_i (high frequencies)
+    wl_i > orig/low_freq_factor   -> inv_freq_i / factor (low frequencies)
+    otherwise interpolate with sigma = (orig/wl_i - low) / (high - low):
+      (1 - sigma) * inv_freq_i / factor + sigma * inv_freq_i
+  which is continuous at both band edges.
+
+Rotation by position p: for each pair (x_i, x_{i+d/2}) and angle
+a = p * inv_freq_i,
+    x_i'       = x_i * cos a - x_{i+d/2} * sin a
+    x_{i+d/2}' = x_{i+d/2} * cos a + x_i * sin a
+R(p)^T = R(-p) undoes it ("un-RoPE", FADE post section "驱逐策略").
+"""
+import numpy as np
+
+
+def inv_freq(head_dim, theta, rope_type="default", factor=1.0,
+             low_freq_factor=1.0, high_freq_factor=4.0,
+             original_max_position=8192):
+    """Per-pair angular frequencies, float64 [head_dim // 2]."""
+    if head_dim % 2:
+        raise ValueError("head_dim must be even")
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    f = np.power(float(theta), -2.0 * i / head_dim)
+    if rope_type == "default":
+        return f
+    if rope_type != "llama3":
+        raise ValueError(f"unsupported rope_type {rope_type!r}")
+    wavelen = 2.0 * np.pi / f
+    long_wl = original_max_position / low_freq_factor    # beyond: fully scaled
+    short_wl = original_max_position / high_freq_factor  # below: untouched
+    out = np.empty_like(f)
+    for k in range(f.size):
+        if wavelen[k] < short_wl:
+            out[k] = f[k]
+        elif wavelen[k] > long_wl:
+            out[k] = f[k] / factor
+        else:
+            sigma = ((original_max_position / wavelen[k]) - low_freq_factor) / (
+                high_freq_factor - low_freq_factor)
+            out[k] = (1.0 - sigma) * f[k] / factor + sigma * f[k]
+    return out
+
+
+def rotate(x, positions, freqs):
+    """Apply R(p) to x [..., d] at positions [...] (broadcast), float64."""
+    x = np.asarray(x, dtype=np.float64)
+    half = x.shape[-1] // 2
+    ang = np.asarray(positions, dtype=np.float64)[..., None] * freqs
+    c, s = np.cos(ang), np.sin(ang)
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def unrotate(x, positions, freqs):
+    """Apply R(p)^T = R(-p): the un-RoPE step."""
+    return rotate(x, -np.asarray(positions, dtype=np.float64), freqs)
+
+
+def rerope_fp16(k, old_pos, new_pos, freqs):
+    """Un-RoPE a key at its old position, re-RoPE it at the new (compacted)
+    position and round once to fp16 (FADE post, sections "驱逐策略" and
+    "RoPE重计算": surviving keys are re-rotated on eviction; the pages do the
+    rotation in float32, the oracle in float64 with a single rounding to the
+    storage type). `k` holds the key's exact values: fp16 storage, or the
+    float64 dequantized values of a middle-tier key."""
+    x = np.asarray(k)
+    x = x.astype(np.float64) if x.dtype != np.float64 else x
+    y = rotate(unrotate(x, old_pos, freqs), new_pos, freqs)
+    return y.astype(np.float16)

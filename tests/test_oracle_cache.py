@@ -1,0 +1,190 @@
+"""Pins for oracle.cache and oracle.accounting (CPU only).
+
+* Tier layout: closed-form counts.
+* Selection: brute force over every subset on tiny inputs, np.argmin for a
+  single eviction, position scores evict the oldest.
+* Prefill build and decode-time eviction: survivors' keys equal the rotation
+  of the harness's raw keys at their new slot (to the rounding bound),
+  values move bit-for-bit, unmoved slots are untouched, counts add up.
+* Compressed bytes: equal the byte count of the live arrays, and reproduce
+  the memory figures the FADE post prints for Llama-3.2-1B.
+"""
+import itertools
+import os
+
+import numpy as np
+import pytest
+
+from oracle import accounting, quant, rope
+from oracle import cache as oc
+from tiered_quantized_kv_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _cfg(**kw):
+    base = dict(head_dim=64, n_q_heads=8, n_kv_heads=2, n_sink=4, recent_window=8,
+                int4_budget=-1, middle_k_bits=4, middle_v_bits=4, rope_theta=1e4)
+    base.update(kw)
+    return oc.Config(**base)
+
+
+def _prefill(cfg, L, seed):
+    gen = synth.rng(seed)
+    k_raw, v = synth.kv_raw(gen, cfg.n_kv_heads, L, cfg.head_dim)
+    f = cfg.freqs()
+    k16 = rope.rotate(k_raw, np.arange(L), f).astype(np.float16)
+    return k_raw, k16, v.astype(np.float16)
+
+
+@pytest.mark.parametrize("t,n_sink,w,expect", [
+    (0, 4, 64, (0, 0, 0)), (3, 4, 64, (3, 0, 0)), (4, 4, 64, (4, 0, 0)),
+    (50, 4, 64, (4, 0, 46)), (68, 4, 64, (4, 0, 64)), (69, 4, 64, (4, 1, 64)),
+    (512, 4, 64, (4, 444, 64)), (8325, 4, 128, (4, 8193, 128))])
+def test_tier_layout(t, n_sink, w, expect):
+    got = oc.tier_layout(t, n_sink, w)
+    assert got == expect and sum(got) == t
+
+
+def test_selection_brute_force_all_subsets():
+    gen = np.random.default_rng(5)
+    for trial in range(60):
+        m = int(gen.integers(1, 9))
+        n_ev = int(gen.integers(0, m + 1))
+        sc = gen.integers(0, 3, size=m).astype(np.float64)   # many ties
+        got = set(oc.select_evicted(sc, n_ev).tolist())
+        # the unique subset E with |E| = n_ev such that every evicted
+        # (score, slot) key is below every kept key
+        valid = [set(e) for e in itertools.combinations(range(m), n_ev)
+                 if all((sc[a], a) < (sc[b], b) for a in e for b in range(m) if b not in e)]
+        assert len(valid) == 1 and got == valid[0]
+
+
+def test_selection_single_eviction_is_argmin_and_position_is_oldest():
+    gen = np.random.default_rng(6)
+    sc = gen.integers(0, 5, size=400).astype(np.float64)
+    assert oc.select_evicted(sc, 1).tolist() == [int(np.argmin(sc))]
+    assert oc.select_evicted(np.arange(100.0), 7).tolist() == list(range(7))
+
+
+def test_prefill_build_without_eviction_is_plain_tiering():
+    cfg = _cfg()
+    k_raw, k16, v16 = _prefill(cfg, 100, 31)
+    c = oc.build_from_prefill(cfg, k16, v16)
+    assert (c.n_sink_live, c.mid_len, c.rec_len) == (4, 88, 8)
+    assert np.array_equal(c.sink_k, k16[:, :4]) and np.array_equal(c.rec_v, v16[:, 92:])
+    u, s = quant.quantize(k16[:, 4:92], 4, 32)
+    assert np.array_equal(c.mid_k_u, u) and np.array_equal(c.mid_k_s, s)
+
+
+@pytest.mark.parametrize("policy", ["position", "score"])
+def test_prefill_build_with_eviction(policy):
+    cfg = _cfg(int4_budget=20, middle_k_bits=4, middle_v_bits=2)
+    L = 90
+    k_raw, k16, v16 = _prefill(cfg, L, 32)
+    scores = None if policy == "position" else synth.normal(synth.rng(33), L) ** 2
+    c = oc.build_from_prefill(cfg, k16, v16, scores)
+    assert (c.n_sink_live, c.mid_len, c.rec_len) == (4, 20, 8) and c.length == 32
+    if scores is None:
+        kept = np.arange(4 + 58, 4 + 78)                   # oldest evicted first
+    else:
+        mid = np.arange(4, 82)
+        ev = set(mid[np.argsort(scores[4:82], kind="stable")[:58]].tolist())
+        kept = np.array([j for j in mid if j not in ev])
+    f = cfg.freqs()
+    # recent tokens: fp16 keys re-RoPE'd from their old index to the new one
+    old_r = np.arange(82, 90)
+    new_r = np.arange(24, 32)
+    assert np.array_equal(c.rec_v, v16[:, old_r])
+    exact_new = rope.rotate(k_raw[:, old_r], new_r, f)
+    err = np.abs(c.rec_k.astype(np.float64) - exact_new)
+    stored_err = np.abs(k16[:, old_r].astype(np.float64) - rope.rotate(k_raw[:, old_r], old_r, f))
+    bound = np.hypot(stored_err[..., :32], stored_err[..., 32:]).max(-1, keepdims=True) + 2 ** -9 * np.abs(exact_new).max()
+    assert np.all(err <= bound)
+    # middle survivors: V codes are the quantization of the untouched fp16 V
+    vu, vs = quant.quantize(v16[:, kept], 2, 32)
+    assert np.array_equal(c.mid_v_u, vu) and np.array_equal(c.mid_v_s, vs)
+    # middle K codes quantize the key rotated to its new slot
+    new_m = np.arange(4, 24)
+    rot = rope.rerope_fp16(k16[:, kept], kept, new_m, f)
+    ku, ks = quant.quantize(rot, 4, 32)
+    assert np.array_equal(c.mid_k_u, ku) and np.array_equal(c.mid_k_s, ks)
+    # sinks never move
+    assert np.array_equal(c.sink_k, k16[:, :4])
+
+
+def test_decode_steps_keep_tier_invariants_and_evict_one_in_one_out():
+    cfg = _cfg(n_q_heads=4, n_kv_heads=2, int4_budget=12, recent_window=6, middle_v_bits=2)
+    L = 40
+    k_raw, k16, v16 = _prefill(cfg, L, 34)
+    scores = synth.normal(synth.rng(35), L) ** 2
+    c = oc.build_from_prefill(cfg, k16, v16, scores)
+    f = cfg.freqs()
+    gen = synth.rng(36)
+    for step in range(10):
+        t = c.length
+        kn = rope.rotate(synth.normal(gen, 2, 64), np.full(2, t), f).astype(np.float16)
+        vn = synth.normal(gen, 2, 64).astype(np.float16)
+        q = rope.rotate(synth.normal(gen, 1, 4, 64), np.full((1, 4), t), f).astype(np.float16)
+        before_v = c.mid_v_u.copy()
+        out, sides, ev = oc.decode_step([c], q, kn[None], vn[None], mode="accum")
+        assert np.isclose(sides[0].sum(), 4)
+        assert len(sides[0]) == t + 1
+        assert (c.n_sink_live, c.mid_len, c.rec_len) == (4, 12, 6)
+        assert ev[0].size == 1
+        # V codes of survivors move unchanged
+        e = int(ev[0][0])
+        full_v = np.concatenate([before_v, c.mid_v_u[:, -1:]], axis=1)
+        assert np.array_equal(np.delete(full_v, e, axis=1), c.mid_v_u)
+        # unmoved middle slots before the evicted one keep their K codes
+        assert c.scores.size == c.length
+
+
+def test_evict_then_middle_keys_track_raw_rotation():
+    """After a decode-time eviction, dequantized middle keys that moved equal
+    the raw key rotated at its new slot within the quantization bound."""
+    cfg = _cfg(int4_budget=10, recent_window=4)
+    L = 30
+    k_raw, k16, v16 = _prefill(cfg, L, 37)
+    c = oc.build_from_prefill(cfg, k16, v16)       # position policy at prefill
+    kept_old = np.arange(4 + 12, 4 + 22)             # 22 middle candidates, oldest 12 gone
+    c.scores = np.zeros(c.length)
+    c.scores[4 + np.arange(10)] = np.arange(10)[::-1].astype(float)   # slot 4+9 lowest
+    ev = oc.evict(c, 8)                                # evict 2 lowest scores
+    assert ev.tolist() == [8, 9]
+    f = cfg.freqs()
+    kh = quant.dequantize(c.mid_k_u, c.mid_k_s, 4, 32)
+    want = rope.rotate(k_raw[:, kept_old[:8]], np.arange(4, 12), f)
+    s = np.repeat(c.mid_k_s.astype(np.float64), 32, axis=-1)
+    # quantization error <= s/2 per element, plus the fp16 roundings of two
+    # rotations and one earlier quantization (each bounded by s-level terms)
+    assert np.all(np.abs(kh - want) <= 1.5 * s + 0.02)
+
+
+def test_compressed_bytes_equals_array_bytes():
+    cfg = _cfg(int4_budget=20, middle_v_bits=2)
+    _, k16, v16 = _prefill(cfg, 70, 38)
+    c = oc.build_from_prefill(cfg, k16, v16)
+    n = accounting.compressed_bytes(64, 2, 4, 2, 32, [c.n_sink_live + c.rec_len], [c.mid_len])
+    assert n == accounting.cache_bytes(c)
+
+
+def test_compressed_bytes_reproduce_page_llama_figures():
+    vals = {}
+    with open(os.path.join(GOLDEN, "page_memory_figures.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                k, v = (x.strip() for x in line.split("="))
+                vals[k] = float(v)
+    layers, hkv, d = int(vals["layers"]), int(vals["n_kv_heads"]), int(vals["head_dim"])
+    mib = 2.0 ** 20
+    per_token_fp16 = layers * hkv * d * 2 * 2
+    tokens = round(vals["baseline_mib"] * mib / per_token_fp16)
+    assert abs(tokens * per_token_fp16 / mib - vals["baseline_mib"]) < 0.05
+    evicted = vals["evicted_fraction"] * tokens
+    fp16_slots = 4 + 64
+    mid = tokens - fp16_slots - evicted
+    tiered = accounting.compressed_bytes(d, hkv, 4, 2, 32, [fp16_slots] * layers,
+                                         [mid] * layers) / mib
+    assert abs(tiered - vals["tiered_mib"]) < 0.05

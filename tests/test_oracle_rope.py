@@ -1,0 +1,132 @@
+"""Pins for oracle.rope (CPU only): identities of rotations, complex
+multiplication as an independent route, the relative-position property, and
+the llama3 band rule's closed-form edges."""
+import numpy as np
+import pytest
+
+from oracle import rope
+from tiered_quantized_kv_amd import synth
+
+
+def _x(seed, n, d):
+    return synth.normal(synth.rng(seed), n, d)
+
+
+@pytest.mark.parametrize("d,theta", [(64, 1e4), (128, 1e6), (128, 5e5)])
+def test_standard_freqs_closed_form(d, theta):
+    f = rope.inv_freq(d, theta)
+    assert f[0] == 1.0
+    ratios = f[1:] / f[:-1]
+    assert np.allclose(ratios, theta ** (-2.0 / d), rtol=1e-13)
+    assert np.isclose(f[d // 4], theta ** -0.5, rtol=1e-13)
+
+
+def test_identity_and_norm():
+    f = rope.inv_freq(128, 1e6)
+    x = _x(1, 40, 128)
+    assert np.array_equal(rope.rotate(x, np.zeros(40), f), x)
+    p = np.arange(40) * 997.0
+    y = rope.rotate(x, p, f)
+    assert np.allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1), rtol=1e-13)
+
+
+def test_matches_complex_multiplication():
+    """(x_i, x_{i+d/2}) as the complex number x_i + i x_{i+d/2}; RoPE at p is
+    multiplication by exp(i p f_i)."""
+    d = 64
+    f = rope.inv_freq(d, 1e4)
+    x = _x(2, 10, d)
+    p = np.array([0, 1, 2, 5, 100, 511, 4095, 8191, 65535, 131071], dtype=np.float64)
+    z = (x[:, : d // 2] + 1j * x[:, d // 2:]) * np.exp(1j * p[:, None] * f[None, :])
+    y = rope.rotate(x, p, f)
+    assert np.allclose(y[:, : d // 2], z.real, atol=1e-12)
+    assert np.allclose(y[:, d // 2:], z.imag, atol=1e-12)
+
+
+def test_unrope_then_rope_same_position_is_identity():
+    f = rope.inv_freq(128, 5e5)
+    x = _x(3, 50, 128)
+    p = np.linspace(0, 131071, 50)
+    assert np.allclose(rope.rotate(rope.unrotate(x, p, f), p, f), x, atol=1e-12)
+
+
+def test_rotation_composes():
+    f = rope.inv_freq(64, 1e4)
+    x = _x(4, 30, 64)
+    p1 = np.arange(30) * 13.0
+    p2 = np.arange(30) * 7.0 + 1000
+    assert np.allclose(rope.rotate(rope.rotate(x, p1, f), p2 - p1, f),
+                       rope.rotate(x, p2, f), atol=1e-10)
+
+
+def test_relative_position_property():
+    """<R(p) q, R(p') k> depends only on p - p'."""
+    f = rope.inv_freq(128, 1e6)
+    q = _x(5, 1, 128)[0]
+    k = _x(6, 1, 128)[0]
+    a = rope.rotate(q, 700.0, f) @ rope.rotate(k, 650.0, f)
+    b = rope.rotate(q, 50.0, f) @ rope.rotate(k, 0.0, f)
+    assert np.isclose(a, b, rtol=1e-11)
+
+
+def test_llama3_factor_one_is_standard():
+    a = rope.inv_freq(64, 5e5, "llama3", factor=1.0, low_freq_factor=1.0,
+                      high_freq_factor=4.0, original_max_position=8192)
+    assert np.allclose(a, rope.inv_freq(64, 5e5), rtol=1e-15)
+
+
+def test_llama3_bands():
+    d, theta, fac, lo, hi, orig = 64, 5e5, 32.0, 1.0, 4.0, 8192
+    base = rope.inv_freq(d, theta)
+    got = rope.inv_freq(d, theta, "llama3", fac, lo, hi, orig)
+    wl = 2 * np.pi / base
+    high = wl < orig / hi
+    low = wl > orig / lo
+    mid = ~(high | low)
+    assert high.any() and low.any() and mid.any()
+    assert np.array_equal(got[high], base[high])
+    assert np.allclose(got[low], base[low] / fac, rtol=1e-15)
+    # mid band lies strictly between the two edges' rules
+    assert np.all(got[mid] < base[mid]) and np.all(got[mid] > base[mid] / fac)
+
+
+def test_llama3_rule_continuous_at_edges():
+    """Place one frequency's wavelength exactly on each band edge (by choosing
+    the original context length); the oracle's value there must equal the
+    neighbouring band's rule from either side (continuity)."""
+    d, theta, fac, lo, hi = 64, 5e5, 8.0, 1.0, 4.0
+    base = rope.inv_freq(d, theta)
+    k = 9
+    wl = 2 * np.pi / base[k]
+    for orig, expect in ((wl * hi, base[k]), (wl * lo, base[k] / fac)):
+        for nudge in (1 - 1e-12, 1.0, 1 + 1e-12):
+            got = rope.inv_freq(d, theta, "llama3", fac, lo, hi, orig * nudge)[k]
+            assert np.isclose(got, expect, rtol=1e-9)
+
+
+def test_rerope_matches_rotation_of_raw_key():
+    """A key stored at p_old (fp16 of R(p_old) k_raw) re-RoPE'd to p_new is
+    R(p_new) k_raw up to the stored rounding error (rotated with the pair) plus
+    the final rounding: per rotation pair, in the 2-norm,
+    |moved - R(p_new) k_raw| <= |stored err| + |output half-ulps|."""
+    d = 128
+    f = rope.inv_freq(d, 5e5)
+    k_raw = _x(7, 64, d) * 3
+    p_old = np.arange(64) * 2003.0 + 122000
+    p_new = np.arange(64) + 4.0
+    exact_old = rope.rotate(k_raw, p_old, f)
+    stored = exact_old.astype(np.float16)
+    moved = rope.rerope_fp16(stored, p_old, p_new, f).astype(np.float64)
+    want = rope.rotate(k_raw, p_new, f)
+    h = d // 2
+
+    def pair_norm(a):
+        return np.hypot(a[:, :h], a[:, h:])
+
+    in_err = pair_norm(stored.astype(np.float64) - exact_old)
+    out_half_ulp = pair_norm(np.abs(np.spacing(moved.astype(np.float16))).astype(np.float64) / 2)
+    err = pair_norm(moved - want)
+    assert np.all(err <= (in_err + out_half_ulp) * (1 + 1e-9))
+    # and the identity case: same position leaves fp16 keys bit-identical
+    same = rope.rerope_fp16(stored, p_old, p_old, f)
+    assert np.array_equal(same, stored)
