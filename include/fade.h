@@ -1,0 +1,284 @@
+/*
+ * libfade — C ABI of the FADE tiered KV-cache hot path on AMD MI355X (gfx950).
+ *
+ * Sources, cited by page title and section:
+ *   "FADE：面向LLM推理的注意力感知分层KV缓存压缩技术" (zingnex.cn forum
+ *   thread; "FADE post" below) and "探秘Transformer系列之（25）--- KV Cache
+ *   优化之处理长文本序列" (dg7.cn; "Transformer series (25)" below).
+ *
+ * Conventions for every call
+ *   - Device pointers are plain pointers into HIP device memory owned by the
+ *     caller; the library never allocates or frees device memory. Scratch
+ *     space is a caller-provided `workspace` sized by fade_workspace_bytes().
+ *   - `stream` is a hipStream_t passed as void* (NULL = default stream). All
+ *     device work is enqueued asynchronously on it; nothing synchronizes.
+ *   - fp16 / bf16 data are passed as raw 16-bit storage.
+ *   - Every call returns a fade_status. Arguments are validated before any
+ *     launch; on error nothing is enqueued. HIP launch errors map to
+ *     FADE_ERR_HIP. Calls keep no global state and are thread-safe for
+ *     distinct buffers.
+ *   - Alignment: fp16 tiers, packed codes, queries, outputs, prefill
+ *     tensors and workspaces must be 16-byte aligned; scales 2-byte, lens,
+ *     scores and tok_attn 4-byte aligned.
+ */
+#ifndef FADE_H
+#define FADE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum fade_status {
+  FADE_OK = 0,
+  FADE_ERR_INVALID_ARG = 1,   /* null pointer, bad size, bad alignment      */
+  FADE_ERR_UNSUPPORTED = 2,   /* shape or option outside the built kernels   */
+  FADE_ERR_CAPACITY = 3,      /* a tier would exceed the caller's capacity   */
+  FADE_ERR_WORKSPACE = 4,     /* workspace missing or too small              */
+  FADE_ERR_HIP = 5            /* a HIP runtime call or launch failed         */
+};
+
+enum fade_rope_type { FADE_ROPE_DEFAULT = 0, FADE_ROPE_LLAMA3 = 1 };
+enum fade_dtype { FADE_DTYPE_F16 = 0, FADE_DTYPE_BF16 = 1, FADE_DTYPE_F32 = 2 };
+enum fade_score_mode { FADE_SCORE_PREFILL = 0, FADE_SCORE_ACCUM = 1, FADE_SCORE_EMA = 2 };
+enum fade_policy { FADE_POLICY_SCORE = 0, FADE_POLICY_POSITION = 1 };
+enum fade_ws_op {
+  FADE_WS_DECODE = 0,         /* fade_tiered_decode_attn      (max_len = cap_mid) */
+  FADE_WS_H2O_PREFILL = 1,    /* fade_h2o_scores PREFILL      (max_len = L)       */
+  FADE_WS_EVICT = 2,          /* fade_evict_rerope            (max_len = cap_mid) */
+  FADE_WS_PREFILL_BUILD = 3   /* fade_prefill_build           (max_len = L)       */
+};
+
+/*
+ * Static configuration of one attention layer's cache (host struct, read
+ * only). Fields follow the FADE post, section "自定义配置" (custom config):
+ * n_sink, recent_window, int4_budget, middle_k_bits, middle_v_bits; and
+ * section "RoPE方案兼容性" for the RoPE variants (standard and llama3).
+ *   head_dim        64 or 128
+ *   n_q_heads       query heads; n_q_heads / n_kv_heads = n_rep in {1,2,4,8}
+ *                   (GQA: query head h reads KV head h / n_rep)
+ *   n_sink          FP16 sink tokens kept at the start (0..64)
+ *   recent_window   FP16 recent tokens kept after maintenance (1..1024); the
+ *                   recent ring holds recent_window + 1 slots so the current
+ *                   token is FP16 while it is attended
+ *   int4_budget     maximum middle-tier tokens after an eviction event;
+ *                   -1 = never evict
+ *   middle_k_bits   4 or 2;  middle_v_bits 4 or 2 (INT2 V is the optional
+ *                   deep tier, FADE post "量化与Bit-Packing")
+ *   group_size      quantization group along head_dim; must be 32
+ *   rope_*          RoPE of the model; llama3 uses factor, low/high
+ *                   frequency factors and the original context length
+ *   q_dtype         FADE_DTYPE_F16 or FADE_DTYPE_BF16 (decode query)
+ *   out_dtype       FADE_DTYPE_F16, FADE_DTYPE_BF16 or FADE_DTYPE_F32
+ */
+typedef struct fade_config {
+  int32_t head_dim;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t n_sink;
+  int32_t recent_window;
+  int32_t int4_budget;
+  int32_t middle_k_bits;
+  int32_t middle_v_bits;
+  int32_t group_size;
+  int32_t rope_type;
+  double rope_theta;
+  double rope_factor;
+  double rope_low_freq_factor;
+  double rope_high_freq_factor;
+  int32_t rope_original_max_position;
+  int32_t q_dtype;
+  int32_t out_dtype;
+  int32_t reserved;
+} fade_config;
+
+/*
+ * Device-resident tiers of one layer (FADE post, section
+ * "核心机制：三层级缓存架构"). All arrays are caller-owned device memory.
+ *
+ *   fp_k, fp_v      fp16 [batch, Hkv, n_sink + recent_window + 1, head_dim].
+ *                   Slots [0, n_sink) are the sinks; slots [n_sink, ...) are
+ *                   the recent ring (Transformer series (25), 1.2.2: rolling
+ *                   buffer). Recent entry i (0 = oldest) lives at slot
+ *                   n_sink + (rec_head + i) % (recent_window + 1).
+ *   mid_k_codes     u8 [batch, Hkv, cap_mid, head_dim * middle_k_bits / 8]
+ *   mid_v_codes     u8 [batch, Hkv, cap_mid, head_dim * middle_v_bits / 8]
+ *                   Bit-packed offset-binary codes: channel c in byte
+ *                   c*b/8 at bit (c*b)%8, code = q + 2^(b-1).
+ *   mid_k_scales,
+ *   mid_v_scales    fp16 [batch, Hkv, cap_mid, head_dim / 32], one scale per
+ *                   32-channel group (s = fp16(amax / (2^(b-1)-1))).
+ *   lens            int32 [batch, 4] = {n_sink_live, mid_len, rec_len,
+ *                   rec_head}. Read and updated by the kernels only.
+ *   scores          f32 [shared ? 1 : batch, cap_T] per-slot importance
+ *                   (index = slot position); NULL when no policy uses it.
+ *   cap_T           n_sink + cap_mid + recent_window + 1.
+ *   shared          1: all rows share tier decisions (FADE post
+ *                   "批处理支持"); scores then has one row.
+ * Positions: a slot's RoPE position is its index in the compacted cache:
+ * sinks 0.., middle rows n_sink_live + r, recent entries after the middle.
+ */
+typedef struct fade_layer_cache {
+  int32_t batch;
+  int32_t cap_mid;
+  int32_t cap_T;
+  int32_t shared;
+  void* fp_k;
+  void* fp_v;
+  void* mid_k_codes;
+  void* mid_v_codes;
+  void* mid_k_scales;
+  void* mid_v_scales;
+  int32_t* lens;
+  float* scores;
+} fade_layer_cache;
+
+/* Human-readable name of a status code; never NULL. */
+const char* fade_status_string(int status);
+
+/* ABI version of this header (major * 100 + minor). */
+int fade_abi_version(void);
+
+/*
+ * Quantize-and-pack rows (FADE post, sections "第二层：INT4量化存储" and
+ * "量化与Bit-Packing": symmetric INTb with bit-packing).
+ *   src          fp16 rows of head_dim values; row i is read from
+ *                src + (src_row_idx ? src_row_idx[i] : i) * src_row_stride
+ *                (stride in elements, >= head_dim, multiple of 8)
+ *   dst_row_idx  if non-NULL, row i is written to codes/scales row
+ *                dst_row_idx[i], else to row i
+ *   bits         4 or 2
+ *   codes        u8 rows of head_dim*bits/8 bytes; scales fp16 rows of
+ *                head_dim/32 values
+ * Per 32-channel group: s = fp16_RNE(amax / qmax), q = clamp(RNE(x / s)),
+ * exact division (no reciprocal approximation); s == 0 gives q = 0.
+ */
+int fade_quantize_pack(const fade_config* cfg, const void* src, int64_t n_rows,
+                       int64_t src_row_stride, const int32_t* src_row_idx,
+                       const int32_t* dst_row_idx, int32_t bits, void* codes,
+                       void* scales, void* stream);
+
+/*
+ * Append the newest token of every sequence: k_new / v_new are fp16
+ * [batch, Hkv, head_dim] (k_new already rotated by the caller at position
+ * = current cache length). The token fills the sink tier while it has fewer
+ * than n_sink tokens, else the recent ring. Calling it while the ring holds
+ * recent_window + 1 tokens (no demotion since the last append) leaves that
+ * sequence unchanged.
+ */
+int fade_cache_append(const fade_config* cfg, fade_layer_cache* cache,
+                      const void* k_new, const void* v_new, void* stream);
+
+/*
+ * Demotion (FADE post, "核心机制": tokens age from the recent FP16 tier into
+ * the packed middle tier): while a sequence's ring holds more than
+ * recent_window tokens, quantize its oldest recent K (middle_k_bits) and V
+ * (middle_v_bits) into middle row mid_len. Positions do not change. A full
+ * middle tier (mid_len == cap_mid) leaves the sequence unchanged; size
+ * cap_mid >= int4_budget + eviction period to avoid it.
+ */
+int fade_cache_demote(const fade_config* cfg, fade_layer_cache* cache, void* stream);
+
+/*
+ * Decode attention read directly from the three tiers (FADE post, sections
+ * "核心机制" and "项目结构与代码质量": INT4 dequantization fused into the
+ * attention kernel). For each sequence b and query head h (KV head
+ * h / n_rep): one softmax over every live slot of every tier, scale
+ * 1/sqrt(head_dim), middle keys/values dequantized in-kernel.
+ *   q         [batch, n_q_heads, head_dim] in cfg->q_dtype
+ *   out       [batch, n_q_heads, head_dim] in cfg->out_dtype
+ *   tok_attn  optional f32 [batch, cap_T]: a_j = sum_h p_{h,j} per slot
+ *             position (0 beyond the live length), the decode-stage
+ *             attention the EMA / cumulative H2O policies consume
+ *   workspace >= fade_workspace_bytes(cfg, FADE_WS_DECODE, batch, cap_mid)
+ */
+int fade_tiered_decode_attn(const fade_config* cfg, const fade_layer_cache* cache,
+                            const void* q, void* out, float* tok_attn,
+                            void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * H2O / EMA scoring (Transformer series (25), 1.3.1 H2O: accumulated
+ * attention = attention-matrix column sums; FADE post, "H2O策略" and
+ * "EMA策略").
+ *   mode FADE_SCORE_PREFILL: scores_out[r, j] = sum over query heads h and
+ *        queries i >= j of the causal softmax P_h[i, j] of the rotated fp16
+ *        prefill q_prefill [batch, Hq, L, d] against k_prefill
+ *        [batch, Hkv, L, d]; summed over rows too when shared != 0
+ *        (scores_out then has one row). QK^T runs on MFMA.
+ *   mode FADE_SCORE_ACCUM: cache->scores[j] += a_j (from tok_attn)
+ *   mode FADE_SCORE_EMA:   cache->scores[j] = decay*scores[j] + (1-decay)*a_j
+ *        (shared caches add the rows' a_j first). Slots beyond the live
+ *        length are left untouched.
+ */
+int fade_h2o_scores(const fade_config* cfg, int32_t mode, fade_layer_cache* cache,
+                    const void* q_prefill, const void* k_prefill, int32_t batch,
+                    int32_t L, int32_t shared, float* scores_out,
+                    const float* tok_attn, float decay,
+                    void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Eviction event with un-RoPE / re-RoPE compaction (FADE post, sections
+ * "驱逐策略" and "RoPE重计算"; Transformer series (25), 1.2.2 StreamingLLM
+ * for in-cache positions). For every sequence (or once for a shared cache)
+ * whose middle tier holds M > int4_budget tokens: order the middle slots by
+ * (score ascending, slot ascending) — policy POSITION uses the slot alone —
+ * evict the first M - int4_budget, and move the survivors to contiguous
+ * slots. A surviving key whose position changes is rotated by the position
+ * delta in float64, rounded once to fp16, and (middle tier) requantized;
+ * values move bit-for-bit; unmoved slots are untouched; scores move with
+ * their slots.
+ *   max_evict  upper bound on M - int4_budget for this call (sizes the
+ *              rotation table); 0 means cap_mid - int4_budget
+ *   workspace  >= fade_workspace_bytes(cfg, FADE_WS_EVICT, batch, cap_mid)
+ */
+int fade_evict_rerope(const fade_config* cfg, fade_layer_cache* cache, int32_t policy,
+                      int32_t max_evict, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Build the tiers of an empty cache from a prefill of L tokens (k_prefill,
+ * v_prefill fp16 [batch, Hkv, L, d], keys rotated at positions 0..L-1).
+ * Sinks = first min(n_sink, L); recent = last min(recent_window, L - sinks);
+ * the middle candidates between are cut to int4_budget by
+ * prefill_scores (f32 [shared ? 1 : batch, L], H2O) or, when NULL, by
+ * position (oldest first); survivors are re-RoPE'd to contiguous positions,
+ * then middle survivors are quantized. cache->scores (if set) receives the
+ * survivors' prefill scores (zeros when prefill_scores is NULL).
+ *   workspace >= fade_workspace_bytes(cfg, FADE_WS_PREFILL_BUILD, batch, L)
+ */
+int fade_prefill_build(const fade_config* cfg, fade_layer_cache* cache,
+                       const void* k_prefill, const void* v_prefill, int32_t L,
+                       const float* prefill_scores, void* workspace, size_t ws_bytes,
+                       void* stream);
+
+/*
+ * Rotate rows in place by RoPE (the caller's duty for q and the new key).
+ * Row r of x (n_rows rows of head_dim values, dtype F16 or BF16) is rotated
+ * at position positions[r] if positions != NULL, else at
+ * pos_base + (r % pos_period). Angles and products in float64, one rounding
+ * to the storage type (FADE post, "RoPE重计算").
+ */
+int fade_rope_rotate(const fade_config* cfg, void* x, int32_t dtype, int64_t n_rows,
+                     const int32_t* positions, int32_t pos_base, int32_t pos_period,
+                     void* stream);
+
+/* Workspace bytes needed by `op` (enum fade_ws_op) for `batch` sequences
+ * and `max_len` (see enum). Returns 0 for an invalid configuration. */
+size_t fade_workspace_bytes(const fade_config* cfg, int32_t op, int32_t batch,
+                            int32_t max_len);
+
+/*
+ * Compressed KV bytes (FADE post, "使用注意事项": KV-only accounting), host
+ * only: sum over n entries of
+ *   Hkv * (fp16_slots[i] * d * 4 + mid_slots[i] * ((d*kb/8 + 2d/32) + (d*vb/8 + 2d/32))).
+ * One entry per (layer, sequence). Returns 0 on invalid arguments.
+ */
+uint64_t fade_compressed_bytes(const fade_config* cfg, const int32_t* fp16_slots,
+                               const int32_t* mid_slots, int32_t n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FADE_H */

@@ -79,3 +79,16 @@ def rerope_fp16(k, old_pos, new_pos, freqs):
     x = x.astype(np.float64) if x.dtype != np.float64 else x
     y = rotate(unrotate(x, old_pos, freqs), new_pos, freqs)
     return y.astype(np.float16)
+
+
+def round_bf16(x):
+    """Round float64 values to the nearest bfloat16 (ties to even) in one
+    step, returned as float64. Integer rounding of the float64 bit pattern at
+    the 8th significant bit; exact for the normal bfloat16 range."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    u = x.view(np.uint64)
+    keep = np.uint64(45)                                  # 52 - 7 dropped bits
+    lsb = (u >> keep) & np.uint64(1)
+    u = (u + (np.uint64(1) << (keep - np.uint64(1))) - np.uint64(1) + lsb) & ~((np.uint64(1) << keep) - np.uint64(1))
+    return u.view(np.float64)
+

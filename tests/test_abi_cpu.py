@@ -1,0 +1,108 @@
+"""C-ABI checks that need no GPU: libfade.so loads, exports every function
+include/fade.h declares, and its host-only paths (status strings, workspace
+sizing, the compressed-bytes closed form, argument validation that rejects
+before any launch) behave. No call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import accounting
+from tiered_quantized_kv_amd import fade
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    txt = open(os.path.join(ROOT, "include", "fade.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(fade_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_library_exports_every_header_function():
+    names = _header_functions()
+    assert len(names) >= 12
+    lib = fade.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(fade.exported_symbols()) == names
+
+
+def test_status_strings_and_version():
+    lib = fade.lib()
+    assert lib.fade_abi_version() == 100
+    for s in range(6):
+        assert lib.fade_status_string(s)
+    assert lib.fade_status_string(99) == b"unknown status"
+
+
+def _cfg(**kw):
+    base = dict(head_dim=128, n_q_heads=32, n_kv_heads=8, n_sink=4, recent_window=64, int4_budget=2048,
+                middle_k_bits=4, middle_v_bits=2, rope_theta=5e5)
+    base.update(kw)
+    return fade.make_config(**base)
+
+
+def test_struct_layout_matches_header():
+    # fade_config: 10 int32, 4 double, 4 int32 -> 10*4 (+0 pad) + 32 + 16 = 88
+    assert ctypes.sizeof(fade.FadeConfig) == 88
+    assert fade.FadeConfig.rope_theta.offset == 40
+    assert ctypes.sizeof(fade.LayerCache) == 16 + 8 * 8
+
+
+@pytest.mark.parametrize("d,hkv,kb,vb", [(128, 8, 4, 2), (64, 8, 4, 4), (128, 2, 2, 2)])
+def test_compressed_bytes_matches_oracle_closed_form(d, hkv, kb, vb):
+    cfg = _cfg(head_dim=d, n_kv_heads=hkv, n_q_heads=hkv * 4, middle_k_bits=kb, middle_v_bits=vb)
+    gen = np.random.default_rng(1)
+    fp = gen.integers(0, 200, size=37)
+    mid = gen.integers(0, 9000, size=37)
+    want = accounting.compressed_bytes(d, hkv, kb, vb, 32, fp.tolist(), mid.tolist())
+    assert fade.fade_compressed_bytes(cfg, fp, mid) == want
+
+
+def test_workspace_sizes_positive_and_monotone():
+    cfg = _cfg()
+    for op in (fade.WS_DECODE, fade.WS_H2O_PREFILL, fade.WS_EVICT, fade.WS_PREFILL_BUILD):
+        a = fade.workspace_bytes(cfg, op, 4, 1000)
+        b = fade.workspace_bytes(cfg, op, 8, 3000)
+        assert 0 < a <= b
+    bad = _cfg(head_dim=96)
+    assert fade.workspace_bytes(bad, fade.WS_DECODE, 1, 10) == 0
+
+
+def test_validation_rejects_before_launch():
+    lib = fade.lib()
+    cfg = _cfg()
+    null = ctypes.c_void_p(0)
+    # bits outside {2, 4}
+    assert lib.fade_quantize_pack(ctypes.byref(cfg), null, 4, 128, null, null, 3, null, null, null) == \
+        fade.FADE_ERR_UNSUPPORTED
+    # null source with rows to do
+    assert lib.fade_quantize_pack(ctypes.byref(cfg), null, 4, 128, null, null, 4, null, null, null) == \
+        fade.FADE_ERR_INVALID_ARG
+    # zero rows is a no-op even with nulls
+    assert lib.fade_quantize_pack(ctypes.byref(cfg), null, 0, 128, null, null, 4, null, null, null) == fade.FADE_OK
+    # unsupported head_dim / n_rep / group
+    for bad in (_cfg(head_dim=96), _cfg(n_q_heads=24, n_kv_heads=8), _cfg(group_size=64),
+                _cfg(middle_k_bits=3), _cfg(rope_type="llama3", rope_factor=0.0)):
+        st = lib.fade_rope_rotate(ctypes.byref(bad), null, 0, 1, null, 0, 1, null)
+        assert st in (fade.FADE_ERR_UNSUPPORTED, fade.FADE_ERR_INVALID_ARG)
+    # cache struct with a wrong cap_T
+    c = fade.LayerCache(1, 10, 999, 0, 16, 16, 16, 16, 16, 16, 16, None)
+    assert lib.fade_cache_demote(ctypes.byref(cfg), ctypes.byref(c), null) == fade.FADE_ERR_INVALID_ARG
+    # misaligned pointer
+    c = fade.LayerCache(1, 10, 4 + 10 + 65, 0, 17, 16, 16, 16, 16, 16, 16, None)
+    assert lib.fade_cache_demote(ctypes.byref(cfg), ctypes.byref(c), null) == fade.FADE_ERR_INVALID_ARG
+    # budget above capacity
+    c = fade.LayerCache(1, 10, 4 + 10 + 65, 0, 16, 16, 16, 16, 16, 16, 16, None)
+    assert lib.fade_cache_demote(ctypes.byref(cfg), ctypes.byref(c), null) == fade.FADE_ERR_CAPACITY
+    # decode with a missing workspace
+    c = fade.LayerCache(1, 4096, 4 + 4096 + 65, 0, 16, 16, 16, 16, 16, 16, 16, None)
+    st = lib.fade_tiered_decode_attn(ctypes.byref(cfg), ctypes.byref(c), ctypes.c_void_p(16),
+                                     ctypes.c_void_p(16), null, null, 0, null)
+    assert st == fade.FADE_ERR_WORKSPACE
+    # score policy without a score array
+    st = lib.fade_evict_rerope(ctypes.byref(cfg), ctypes.byref(c), fade.POLICY_SCORE, 0, null, 0, null)
+    assert st == fade.FADE_ERR_INVALID_ARG

@@ -130,3 +130,21 @@ def test_rerope_matches_rotation_of_raw_key():
     # and the identity case: same position leaves fp16 keys bit-identical
     same = rope.rerope_fp16(stored, p_old, p_old, f)
     assert np.array_equal(same, stored)
+
+
+def test_round_bf16_matches_exact_rational_rounding():
+    from fractions import Fraction
+    gen = np.random.default_rng(9)
+    x = np.concatenate([gen.standard_normal(3000) * 10.0 ** gen.integers(-20, 20, 3000),
+                        [1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), 255.5, 256.5, 1.0, -0.0]])
+    got = rope.round_bf16(x)
+    for v, g in zip(x, got):
+        if v == 0:
+            assert g == 0
+            continue
+        e = np.floor(np.log2(abs(v)))
+        ulp = Fraction(2) ** int(e - 7)
+        q = Fraction(float(v)) / ulp
+        n = round(q)                                      # ties to even
+        assert Fraction(float(g)) == n * ulp, (v, g)
+

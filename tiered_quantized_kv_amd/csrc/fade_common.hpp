@@ -1,0 +1,127 @@
+// Device helpers shared by the libfade kernels (gfx950, wave64).
+//
+// Storage types are raw 16-bit patterns; arithmetic uses _Float16 / float /
+// double. Every conversion to a 16-bit type rounds to nearest-even exactly
+// once (float64 values go through a round-to-odd float32, which makes the
+// second rounding exact because float32 carries more than 11 + 2 bits).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fade {
+
+typedef _Float16 f16;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kGroup = 32;          // quantization group along head_dim
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float h2f(uint16_t b) { return (float)__builtin_bit_cast(f16, b); }
+__device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (f16)f); }
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// float64 -> float32 rounding to odd: truncate toward zero, then set the last
+// bit if anything was discarded.
+__device__ __forceinline__ float d2f_odd(double d) {
+  float f = (float)d;
+  double back = (double)f;
+  if (back != d) {
+    uint32_t u = __float_as_uint(f);
+    if (fabs(back) > fabs(d)) u -= 1u;   // rounded away from zero: step back
+    u |= 1u;
+    f = __uint_as_float(u);
+  }
+  return f;
+}
+__device__ __forceinline__ uint16_t d2h(double d) { return f2h(d2f_odd(d)); }
+__device__ __forceinline__ uint16_t d2bf(double d) { return f2bf(d2f_odd(d)); }
+
+// ---- wave reductions -------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+      0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kRowRor2 = 0x122, kRowRor4 = 0x124, kRowRor8 = 0x128, kRowRor1 = 0x121;
+
+__device__ __forceinline__ float wave_sum(float x) {
+  x += dpp_f<kRowRor1>(x);
+  x += dpp_f<kRowRor2>(x);
+  x += dpp_f<kRowRor4>(x);
+  x += dpp_f<kRowRor8>(x);
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_f<kRowRor1>(x));
+  x = fmaxf(x, dpp_f<kRowRor2>(x));
+  x = fmaxf(x, dpp_f<kRowRor4>(x));
+  x = fmaxf(x, dpp_f<kRowRor8>(x));
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+// Sum over the lanes of a 16-lane row that share (lane % STRIDE); the result
+// is in every such lane. STRIDE in {1, 2, 4, 8}.
+template <int STRIDE>
+__device__ __forceinline__ float row_sum_strided(float x) {
+  if constexpr (STRIDE <= 1) x += dpp_f<kRowRor1>(x);
+  if constexpr (STRIDE <= 2) x += dpp_f<kRowRor2>(x);
+  if constexpr (STRIDE <= 4) x += dpp_f<kRowRor4>(x);
+  if constexpr (STRIDE <= 8) x += dpp_f<kRowRor8>(x);
+  return x;
+}
+
+// ---- symmetric group quantizer ---------------------------------------------
+// 32 values of one group (exact float copies of fp16 values) -> packed codes
+// (BITS 32-bit words, little-endian: channel c at bit (c*BITS) of the group's
+// byte stream) and the fp16 scale. s = fp16_RNE(amax / qmax); q = clamp(RNE(x
+// / s)) with IEEE division (never an approximate reciprocal); s == 0 -> q = 0.
+template <int BITS>
+__device__ __forceinline__ void quant_group32(const float* x, uint32_t* packed, uint16_t& scale) {
+  constexpr int kOff = 1 << (BITS - 1);
+  constexpr float kQmax = (float)((1 << (BITS - 1)) - 1);
+  float amax = 0.f;
+#pragma unroll
+  for (int c = 0; c < 32; ++c) amax = fmaxf(amax, fabsf(x[c]));
+  const uint16_t sb = f2h(amax / kQmax);
+  const float s = h2f(sb);
+#pragma unroll
+  for (int w = 0; w < BITS; ++w) packed[w] = 0u;
+#pragma unroll
+  for (int c = 0; c < 32; ++c) {
+    int q = 0;
+    if (s != 0.f) {
+      float t = rintf(x[c] / s);
+      t = fminf(fmaxf(t, -kQmax), kQmax);
+      q = (int)t;
+    }
+    const uint32_t u = (uint32_t)(q + kOff);
+    constexpr int kPerWord = 32 / BITS;
+    packed[c / kPerWord] |= u << ((c % kPerWord) * BITS);
+  }
+  scale = sb;
+}
+
+// Offset-removed code of channel c (0..31) of a packed group, as float.
+template <int BITS>
+__device__ __forceinline__ float code_at(const uint32_t* packed, int c) {
+  constexpr int kPerWord = 32 / BITS;
+  const uint32_t u = (packed[c / kPerWord] >> ((c % kPerWord) * BITS)) & ((1u << BITS) - 1u);
+  return (float)((int)u - (1 << (BITS - 1)));
+}
+
+}  // namespace fade

@@ -1,0 +1,67 @@
+// Internal launcher interface between the C-ABI layer (fade_api.hip) and the
+// kernel translation units. Host-side only types; no torch anywhere.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/fade.h"
+
+namespace fade {
+
+constexpr int kMaxHalfDim = 64;     // head_dim <= 128
+
+// Per-pair RoPE frequencies computed on the host in float64.
+struct RopeFreqs {
+  double f[kMaxHalfDim];
+};
+
+// Shape summary derived from fade_config + fade_layer_cache.
+struct Shape {
+  int D, Hq, Hkv, n_rep;
+  int n_sink, W, ring;        // ring = W + 1
+  int budget, kb, vb;
+  int batch, cap_mid, cap_T, shared;
+};
+
+// ---- quantize / append / demote (k_quant.hip) -------------------------------
+hipError_t launch_quantize_rows(int D, int bits, const uint16_t* src, int64_t n_rows,
+                                int64_t src_stride, const int32_t* src_idx,
+                                const int32_t* dst_idx, uint8_t* codes, uint16_t* scales,
+                                hipStream_t st);
+hipError_t launch_append(const Shape& s, const fade_layer_cache& c, const uint16_t* k_new,
+                         const uint16_t* v_new, hipStream_t st);
+hipError_t launch_demote(const Shape& s, const fade_layer_cache& c, hipStream_t st);
+
+// ---- decode attention (k_decode.hip) ---------------------------------------
+int decode_chunk(const Shape& s);                 // middle rows per split
+int decode_nsplit(const Shape& s);                // splits incl. the fp16 split
+size_t decode_ws_bytes(const Shape& s);
+hipError_t launch_decode(const Shape& s, const fade_layer_cache& c, const void* q,
+                         int q_bf16, void* out, int out_dtype, float* tok_attn, void* ws,
+                         hipStream_t st);
+hipError_t launch_score_update(const Shape& s, const fade_layer_cache& c, int mode,
+                               const float* tok_attn, float decay, hipStream_t st);
+
+// ---- H2O prefill column sums (k_h2o.hip) -----------------------------------
+size_t h2o_ws_bytes(int D, int Hq, int Hkv, int batch, int L);
+hipError_t launch_h2o_prefill(int D, int Hq, int Hkv, int batch, int L, int shared,
+                              const uint16_t* q, const uint16_t* k, float* scores_out,
+                              void* ws, hipStream_t st);
+
+// ---- eviction, compaction, prefill build, RoPE (k_evict.hip) ----------------
+size_t evict_ws_bytes(const Shape& s, int max_evict);
+hipError_t launch_evict(const Shape& s, const fade_layer_cache& c, int policy, int max_evict,
+                        const RopeFreqs& fr, void* ws, hipStream_t st);
+size_t prefill_build_ws_bytes(const Shape& s, int L);
+hipError_t launch_prefill_build(const Shape& s, const fade_layer_cache& c, const uint16_t* k,
+                                const uint16_t* v, int L, const float* scores,
+                                const RopeFreqs& fr, void* ws, hipStream_t st);
+hipError_t launch_rope_rotate(int D, uint16_t* x, int bf16, int64_t n_rows,
+                              const int32_t* positions, int pos_base, int pos_period,
+                              const RopeFreqs& fr, hipStream_t st);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace fade

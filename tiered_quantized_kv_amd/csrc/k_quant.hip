@@ -1,0 +1,176 @@
+// Quantize-and-pack, append and demotion kernels.
+//
+// FADE post (FADE：面向LLM推理的注意力感知分层KV缓存压缩技术), sections
+// "第二层：INT4量化存储" and "量化与Bit-Packing": middle-aged tokens are stored
+// as symmetric INT4 (V optionally INT2) codes with bit-packing; the group
+// quantizer itself lives in fade_common.hpp (quant_group32).
+//
+// Roofline: all three are HBM-bound streams. quantize_rows reads 2*D bytes
+// and writes D*b/8 + 2*D/32 bytes per row; append and demote touch one token
+// per (sequence, KV head).
+#include "fade_common.hpp"
+#include "fade_internal.hpp"
+
+namespace fade {
+
+__device__ __forceinline__ void load_group32_f16(const uint16_t* p, float* x) {
+  const uint4* v = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 w = v[i];
+    const uint32_t words[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[8 * i + 2 * j] = h2f((uint16_t)(words[j] & 0xFFFFu));
+      x[8 * i + 2 * j + 1] = h2f((uint16_t)(words[j] >> 16));
+    }
+  }
+}
+
+template <int BITS>
+__device__ __forceinline__ void store_group_codes(uint8_t* dst, const uint32_t* packed) {
+  if constexpr (BITS == 4) {
+    *reinterpret_cast<uint4*>(dst) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  } else {
+    *reinterpret_cast<uint2*>(dst) = make_uint2(packed[0], packed[1]);
+  }
+}
+
+// One thread per (row, 32-channel group).
+template <int BITS>
+__global__ __launch_bounds__(256) void k_quantize_rows(int D, const uint16_t* __restrict__ src,
+                                                       int64_t n_rows, int64_t stride,
+                                                       const int32_t* __restrict__ sidx,
+                                                       const int32_t* __restrict__ didx,
+                                                       uint8_t* __restrict__ codes,
+                                                       uint16_t* __restrict__ scales) {
+  const int ng = D / kGroup;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= n_rows * ng) return;
+  const int64_t row = gid / ng;
+  const int grp = (int)(gid - row * ng);
+  const int64_t srow = sidx ? (int64_t)sidx[row] : row;
+  const int64_t drow = didx ? (int64_t)didx[row] : row;
+  float x[32];
+  load_group32_f16(src + srow * stride + grp * kGroup, x);
+  uint32_t packed[BITS];
+  uint16_t sc;
+  quant_group32<BITS>(x, packed, sc);
+  store_group_codes<BITS>(codes + drow * (D * BITS / 8) + grp * (kGroup * BITS / 8), packed);
+  scales[drow * ng + grp] = sc;
+}
+
+hipError_t launch_quantize_rows(int D, int bits, const uint16_t* src, int64_t n_rows,
+                                int64_t src_stride, const int32_t* src_idx,
+                                const int32_t* dst_idx, uint8_t* codes, uint16_t* scales,
+                                hipStream_t st) {
+  if (n_rows == 0) return hipSuccess;
+  const int64_t threads = n_rows * (D / kGroup);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  if (bits == 4)
+    hipLaunchKernelGGL(k_quantize_rows<4>, grid, dim3(256), 0, st, D, src, n_rows, src_stride,
+                       src_idx, dst_idx, codes, scales);
+  else
+    hipLaunchKernelGGL(k_quantize_rows<2>, grid, dim3(256), 0, st, D, src, n_rows, src_stride,
+                       src_idx, dst_idx, codes, scales);
+  return hipGetLastError();
+}
+
+// Append the newest token of sequence blockIdx.x (all KV heads).
+__global__ __launch_bounds__(256) void k_append(Shape s, fade_layer_cache c,
+                                                const uint16_t* __restrict__ k_new,
+                                                const uint16_t* __restrict__ v_new) {
+  const int b = blockIdx.x;
+  int32_t* L = c.lens + 4 * b;
+  const int S = min(max(L[0], 0), s.n_sink), R = min(max(L[2], 0), s.ring);
+  const int head = min(max(L[3], 0), s.ring - 1);
+  int slot;
+  bool to_sink = false;
+  if (S < s.n_sink) {
+    slot = S;
+    to_sink = true;
+  } else if (R < s.ring) {
+    slot = s.n_sink + (head + R) % s.ring;
+  } else {
+    return;   // ring full: caller skipped demotion; leave the sequence unchanged
+  }
+  const int slots = s.n_sink + s.ring;
+  const int chunks = s.D / 8;                    // uint4 chunks per row
+  uint4* fk = reinterpret_cast<uint4*>(c.fp_k);
+  uint4* fv = reinterpret_cast<uint4*>(c.fp_v);
+  const uint4* kn = reinterpret_cast<const uint4*>(k_new);
+  const uint4* vn = reinterpret_cast<const uint4*>(v_new);
+  for (int t = threadIdx.x; t < s.Hkv * chunks; t += blockDim.x) {
+    const int g = t / chunks, ch = t - g * chunks;
+    const size_t dst = ((size_t)(b * s.Hkv + g) * slots + slot) * chunks + ch;
+    const size_t srcx = (size_t)(b * s.Hkv + g) * chunks + ch;
+    fk[dst] = kn[srcx];
+    fv[dst] = vn[srcx];
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if (to_sink) L[0] = S + 1;
+    else L[2] = R + 1;
+  }
+}
+
+hipError_t launch_append(const Shape& s, const fade_layer_cache& c, const uint16_t* k_new,
+                         const uint16_t* v_new, hipStream_t st) {
+  hipLaunchKernelGGL(k_append, dim3(s.batch), dim3(256), 0, st, s, c, k_new, v_new);
+  return hipGetLastError();
+}
+
+// Demote the oldest recent tokens of sequence blockIdx.x into the middle tail.
+// One thread per (K or V, KV head, group).
+__global__ __launch_bounds__(256) void k_demote(Shape s, fade_layer_cache c) {
+  const int b = blockIdx.x;
+  int32_t* L = c.lens + 4 * b;
+  int M = min(max(L[1], 0), s.cap_mid), R = min(max(L[2], 0), s.ring);
+  int head = min(max(L[3], 0), s.ring - 1);
+  const int ng = s.D / kGroup;
+  const int slots = s.n_sink + s.ring;
+  const int work = 2 * s.Hkv * ng;
+  while (R > s.W && M < s.cap_mid) {
+    const int slot = s.n_sink + head;
+    for (int t = threadIdx.x; t < work; t += blockDim.x) {
+      const int which = t / (s.Hkv * ng);
+      const int rem = t - which * s.Hkv * ng;
+      const int g = rem / ng, grp = rem - g * ng;
+      const uint16_t* src = reinterpret_cast<const uint16_t*>(which ? c.fp_v : c.fp_k) +
+                            ((size_t)(b * s.Hkv + g) * slots + slot) * s.D + grp * kGroup;
+      float x[32];
+      load_group32_f16(src, x);
+      const size_t drow = (size_t)(b * s.Hkv + g) * s.cap_mid + M;
+      const int bits = which ? s.vb : s.kb;
+      uint8_t* codes = reinterpret_cast<uint8_t*>(which ? c.mid_v_codes : c.mid_k_codes);
+      uint16_t* scales = reinterpret_cast<uint16_t*>(which ? c.mid_v_scales : c.mid_k_scales);
+      uint16_t sc;
+      if (bits == 4) {
+        uint32_t p[4];
+        quant_group32<4>(x, p, sc);
+        store_group_codes<4>(codes + drow * (s.D / 2) + grp * 16, p);
+      } else {
+        uint32_t p[2];
+        quant_group32<2>(x, p, sc);
+        store_group_codes<2>(codes + drow * (s.D / 4) + grp * 8, p);
+      }
+      scales[drow * ng + grp] = sc;
+    }
+    head = (head + 1) % s.ring;
+    --R;
+    ++M;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    L[1] = M;
+    L[2] = R;
+    L[3] = head;
+  }
+}
+
+hipError_t launch_demote(const Shape& s, const fade_layer_cache& c, hipStream_t st) {
+  hipLaunchKernelGGL(k_demote, dim3(s.batch), dim3(64), 0, st, s, c);
+  return hipGetLastError();
+}
+
+}  // namespace fade
