@@ -1,0 +1,382 @@
+"""Throughput of the FADE tiered-KV decode hot path on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c5]
+
+One step = one decode step of every layer of the workload through libfade:
+append the new token, tiered decode attention (with the per-slot side output
+when the policy needs it), score update, demotion, eviction / re-RoPE when
+due, and - for the serving workload - the H2O prefill column sums of one
+admitted sequence. All inputs are synthetic, seeded, and resident in HBM
+before the timed region.
+
+Prints one JSON line: decode KV tokens attended per second (whole job), the
+roofline of the dominant kernel (tiered decode attention: algorithmic
+compressed bytes per launch / its average duration measured with HIP events
+on the launch stream), and the CPU oracle timed on a bounded sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=None)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="c5", choices=["c1", "c2", "c3", "c4", "c5"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calib-copy-mib", type=int, default=0,
+                   help="run one device copy of this size before timing (HBM counter calibration)")
+    return p.parse_args()
+
+
+class Workload:
+    """Per-layer caches and per-step inputs of one workload, on the GPU."""
+
+    def __init__(self, name, dev):
+        import torch
+        from tiered_quantized_kv_amd import fade, synth
+        self.torch, self.fade, self.synth = torch, fade, synth
+        self.name = name
+        w = dict(synth.WORKLOADS[name])
+        self.w = w
+        self.dev = dev
+        self.seed = synth.base_seed(name)
+        self.layers = w["layers"]
+        self.B = w["batch"]
+        self.policy = w["policy"]
+        self.shared = bool(w.get("shared", False))
+        self.period = int(w.get("evict_period", 1))
+        self.d, self.hq, self.hkv = w["head_dim"], w["n_q_heads"], w["n_kv_heads"]
+        rope_kw = dict(rope_type=w["rope_type"], rope_theta=w["rope_theta"])
+        if w["rope_type"] == "llama3":
+            rope_kw.update(rope_factor=w["rope_factor"], rope_low_freq_factor=w["rope_low_freq_factor"],
+                           rope_high_freq_factor=w["rope_high_freq_factor"],
+                           rope_original_max_position=w["rope_original_max_position"])
+        common = dict(head_dim=self.d, n_q_heads=self.hq, n_kv_heads=self.hkv, n_sink=w["n_sink"],
+                      recent_window=w["recent_window"], middle_k_bits=w["middle_k_bits"],
+                      middle_v_bits=w["middle_v_bits"], q_dtype=w["q_dtype"], out_dtype="f16", **rope_kw)
+        self.cfg = fade.make_config(int4_budget=w["int4_budget"], **common)
+        self.cfg_build = fade.make_config(int4_budget=-1 if name == "c5" else w["int4_budget"], **common)
+        self.side = self.policy in ("h2o", "ema")
+
+    # ---- setup (untimed) ---------------------------------------------------
+    def _kv(self, seed, L):
+        """Rotated fp16 K and fp16 V [1, Hkv, L, d] on the device."""
+        torch, fade, synth = self.torch, self.fade, self.synth
+        k = synth.torch_normal((1, self.hkv, L, self.d), seed, self.dev, torch.float32)
+        v = synth.torch_normal((1, self.hkv, L, self.d), seed + 7919, self.dev, torch.float16)
+        gen = synth.rng(seed)
+        for h in range(self.hkv):
+            ch = torch.from_numpy(synth.outlier_channels(gen, self.d)).to(self.dev)
+            k[0, h][:, ch] *= 8.0
+        k = k.to(torch.float16).contiguous()
+        fade.fade_rope_rotate(self.cfg, k, fade.DTYPE_F16, self.hkv * L, None, 0, L)
+        return k, v
+
+    def setup(self, total_steps):
+        torch, fade, synth = self.torch, self.fade, self.synth
+        w, B = self.w, self.B
+        n_sink, W, budget = w["n_sink"], w["recent_window"], w["int4_budget"]
+        if self.name == "c5":
+            gen = synth.rng(self.seed, 1)
+            ctx = synth.ragged_lengths(gen, B, *w["context_range"])
+            self.T0 = [int(min(L, n_sink + W + budget)) for L in ctx]       # post-eviction live slots
+            self.M0 = [t - n_sink - W for t in self.T0]
+            self.ctx = [int(x) for x in ctx]
+            cap_mid = budget + 1
+        else:
+            L = w["context"]
+            S = min(n_sink, L)
+            R = min(W, L - S)
+            Mc = L - S - R
+            Mk = Mc if budget < 0 else min(Mc, budget)
+            self.T0 = [S + Mk + R] * B
+            self.M0 = [Mk] * B
+            self.ctx = [L] * B
+            cap_mid = (Mk + total_steps + 1) if budget < 0 else budget + self.period
+        self.cap_mid = cap_mid
+        self.caches = []
+        ws_build = None
+        for l in range(self.layers):
+            tc = fade.TieredCache(self.cfg, B, cap_mid, shared=self.shared, with_scores=self.side, device=self.dev)
+            if self.name == "c5":
+                for b in range(B):
+                    T = self.T0[b]
+                    k, v = self._kv(self.seed * 1000003 + l * 1009 + b, T)
+                    ws = fade.workspace(self.cfg_build, fade.WS_PREFILL_BUILD, 1, T, device=self.dev)
+                    fade.fade_prefill_build(self.cfg_build, tc.seq_view(b), k, v, T, None, ws)
+                # steady-state EMA scores: small positive values
+                tc.scores.copy_(torch.rand(tc.scores.shape, generator=torch.Generator(device=self.dev).manual_seed(l),
+                                           device=self.dev) * (2.0 / 2117))
+            else:
+                L = w["context"]
+                ks, vs = [], []
+                for b in range(B):
+                    k, v = self._kv(self.seed * 1000003 + l * 1009 + b, L)
+                    ks.append(k)
+                    vs.append(v)
+                k = torch.cat(ks) if B > 1 else ks[0]
+                v = torch.cat(vs) if B > 1 else vs[0]
+                del ks, vs
+                scores = None
+                if self.policy == "h2o":
+                    q = synth.torch_normal((B, self.hq, L, self.d), self.seed * 7 + l, self.dev, torch.float16)
+                    fade.fade_rope_rotate(self.cfg, q, fade.DTYPE_F16, B * self.hq * L, None, 0, L)
+                    rows = 1 if self.shared else B
+                    scores = torch.zeros(rows, L, dtype=torch.float32, device=self.dev)
+                    wsh = fade.workspace(self.cfg, fade.WS_H2O_PREFILL, B, L, device=self.dev)
+                    fade.fade_h2o_scores(self.cfg, fade.SCORE_PREFILL, q_prefill=q, k_prefill=k, batch=B, L=L,
+                                         shared=self.shared, scores_out=scores, ws=wsh)
+                    del q, wsh
+                ws_build = fade.workspace(self.cfg, fade.WS_PREFILL_BUILD, B, L, device=self.dev)
+                fade.fade_prefill_build(self.cfg, tc, k, v, L, scores, ws_build)
+                del k, v, scores
+            self.caches.append(tc)
+        torch.cuda.synchronize()
+        # per-step inputs: a pool of 4 per layer, cycled
+        self.pool = []
+        qdt = torch.bfloat16 if w["q_dtype"] == "bf16" else torch.float16
+        for l in range(self.layers):
+            entries = []
+            for p in range(4):
+                s = self.seed * 31 + l * 4 + p
+                q = synth.torch_normal((B, self.hq, self.d), s, self.dev, qdt)
+                kn = synth.torch_normal((B, self.hkv, self.d), s + 1, self.dev, torch.float16)
+                vn = synth.torch_normal((B, self.hkv, self.d), s + 2, self.dev, torch.float16)
+                entries.append((q, kn, vn))
+            self.pool.append(entries)
+        self.out = torch.zeros(B, self.hq, self.d, dtype=torch.float16, device=self.dev)
+        self.tok = torch.zeros(B, self.caches[0].cap_T, dtype=torch.float32, device=self.dev) if self.side else None
+        self.ws_dec = fade.workspace(self.cfg, fade.WS_DECODE, B, cap_mid, device=self.dev)
+        self.ws_ev = fade.workspace(self.cfg, fade.WS_EVICT, B, cap_mid, device=self.dev)
+        self.admit = None
+        if self.name == "c5":
+            La = w["admit_prefill"]
+            self.admit = []
+            for l in range(self.layers):
+                q = synth.torch_normal((1, self.hq, La, self.d), self.seed * 13 + l, self.dev, torch.float16)
+                k = synth.torch_normal((1, self.hkv, La, self.d), self.seed * 17 + l, self.dev, torch.float16)
+                self.admit.append((q, k))
+            self.admit_scores = torch.zeros(1, La, dtype=torch.float32, device=self.dev)
+            self.ws_h2o = fade.workspace(self.cfg, fade.WS_H2O_PREFILL, 1, La, device=self.dev)
+        self.step_idx = 0
+        self.M = list(self.M0)       # host mirror of middle lengths (at attention time)
+        torch.cuda.synchronize()
+
+    # ---- accounting --------------------------------------------------------
+    def decode_bytes_and_tokens(self):
+        """Algorithmic bytes and attended tokens of one decode-attention call
+        (one layer) at the current step, from the host mirror."""
+        w = self.w
+        d, hkv = self.d, self.hkv
+        per_fp = hkv * d * 4
+        per_mid = hkv * ((d * w["middle_k_bits"] // 8 + d // 16) + (d * w["middle_v_bits"] // 8 + d // 16))
+        F = w["n_sink"] + w["recent_window"] + 1
+        kv = sum(F * per_fp + m * per_mid for m in self.M)
+        qo = self.B * self.hq * d * 2 * 2
+        side = sum(F + m for m in self.M) * 4 if self.side else 0
+        tokens = sum(F + m for m in self.M)
+        return kv + qo + side, tokens
+
+    def advance_mirror(self):
+        budget = self.w["int4_budget"]
+        self.step_idx += 1
+        due = budget >= 0 and (self.step_idx % self.period == 0)
+        for b in range(self.B):
+            m = self.M[b] + 1                       # demotion
+            if due and m > budget:
+                m = budget
+            self.M[b] = m
+
+    # ---- one step --------------------------------------------------------------
+    def step(self, events=None):
+        fade = self.fade
+        t = self.step_idx
+        due = self.w["int4_budget"] >= 0 and ((t + 1) % self.period == 0)
+        pol = fade.POLICY_POSITION if self.policy == "position" else fade.POLICY_SCORE
+        for l in range(self.layers):
+            tc = self.caches[l]
+            q, kn, vn = self.pool[l][t % 4]
+            fade.fade_cache_append(self.cfg, tc, kn, vn)
+            if events is not None:
+                events[l][0].record()
+            fade.fade_tiered_decode_attn(self.cfg, tc, q, self.out, self.tok, self.ws_dec)
+            if events is not None:
+                events[l][1].record()
+            if self.policy == "h2o":
+                fade.fade_h2o_scores(self.cfg, fade.SCORE_ACCUM, cache=tc, tok_attn=self.tok)
+            elif self.policy == "ema":
+                fade.fade_h2o_scores(self.cfg, fade.SCORE_EMA, cache=tc, tok_attn=self.tok, decay=self.w["ema_decay"])
+            fade.fade_cache_demote(self.cfg, tc)
+            if due:
+                fade.fade_evict_rerope(self.cfg, tc, pol, self.ws_ev)
+            if self.admit is not None:
+                qa, ka = self.admit[l]
+                fade.fade_h2o_scores(self.cfg, fade.SCORE_PREFILL, q_prefill=qa, k_prefill=ka, batch=1,
+                                     L=qa.shape[2], shared=0, scores_out=self.admit_scores, ws=self.ws_h2o)
+
+
+def cpu_baseline(name, budget_s=20.0):
+    """The oracle, untuned, on a bounded sample of the workload: one layer of
+    one decode step (all sequences), timed on the host cores."""
+    from oracle import cache as oc
+    from oracle import rope
+    from tiered_quantized_kv_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    w = synth.WORKLOADS[name]
+    cfg = oc.Config(head_dim=w["head_dim"], n_q_heads=w["n_q_heads"], n_kv_heads=w["n_kv_heads"],
+                    n_sink=w["n_sink"], recent_window=w["recent_window"], int4_budget=w["int4_budget"],
+                    middle_k_bits=w["middle_k_bits"], middle_v_bits=w["middle_v_bits"],
+                    rope_theta=w["rope_theta"], rope_type=w["rope_type"],
+                    rope_factor=w.get("rope_factor", 1.0),
+                    rope_low_freq_factor=w.get("rope_low_freq_factor", 1.0),
+                    rope_high_freq_factor=w.get("rope_high_freq_factor", 4.0),
+                    rope_original_max_position=w.get("rope_original_max_position", 8192))
+    seed = synth.base_seed(name)
+    B = w["batch"]
+    n_sink, W, budget = w["n_sink"], w["recent_window"], w["int4_budget"]
+    if name == "c5":
+        ctx = synth.ragged_lengths(synth.rng(seed, 1), B, *w["context_range"])
+        T0 = [int(min(L, n_sink + W + budget)) for L in ctx]
+    else:
+        L = w["context"]
+        S = min(n_sink, L)
+        R = min(W, L - S)
+        Mc = L - S - R
+        T0 = [S + (Mc if budget < 0 else min(Mc, budget)) + R] * B
+    f = cfg.freqs()
+    gen = synth.rng(seed, 99)
+    caches = []
+    for b in range(B):
+        k_raw, v = synth.kv_raw(gen, cfg.n_kv_heads, T0[b], cfg.head_dim)
+        k16 = rope.rotate(k_raw, np.arange(T0[b]), f).astype(np.float16)
+        c = oc.build_from_prefill(oc.Config(**{**cfg.__dict__, "int4_budget": -1}), k16, v.astype(np.float16))
+        c.cfg = cfg
+        c.scores = gen.random(c.length) * (2.0 / max(c.length, 1))
+        caches.append(c)
+    q = [rope.rotate(synth.normal(gen, cfg.n_q_heads, cfg.head_dim), np.full(cfg.n_q_heads, caches[b].length), f)
+         .astype(np.float16) for b in range(B)]
+    kn = np.stack([rope.rotate(synth.normal(gen, cfg.n_kv_heads, cfg.head_dim),
+                               np.full(cfg.n_kv_heads, caches[b].length), f) for b in range(B)]).astype(np.float16)
+    vn = synth.normal(gen, B, cfg.n_kv_heads, cfg.head_dim).astype(np.float16)
+    mode = {"h2o": "accum", "ema": "ema", "position": "none", "none": "none"}[w["policy"]]
+    pol = "position" if w["policy"] == "position" else "score"
+    tokens = 0
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        out, sides, _ = oc.decode_step(caches, np.stack(q).astype(np.float64), kn, vn, mode=mode,
+                                       beta=w.get("ema_decay", 0.9), shared=w.get("shared", False),
+                                       evict_now=budget >= 0, policy=pol)
+        tokens += sum(len(s) for s in sides)
+        reps += 1
+        if time.perf_counter() - t0 > budget_s or reps >= 3:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{reps} x one layer of one decode step of workload {name} ({B} sequences, "
+                      f"{tokens // reps} KV tokens attended per layer-step): append, attend, score update, "
+                      f"demote, evict; float64 numpy, {dt:.1f} s"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; multi-GPU runs are not part of it",
+                          "n_gpus": a.gpus}))
+        sys.exit(2)
+    import torch
+    from tiered_quantized_kv_amd import fade
+    fade.lib()
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    steps = a.steps if a.steps is not None else {"c1": 50, "c2": 64, "c3": 64, "c4": 32, "c5": 32}[a.workload]
+    wl = Workload(a.workload, dev)
+    print(f"[bench] setting up workload {a.workload} ...", file=sys.stderr, flush=True)
+    t_setup = time.perf_counter()
+    wl.setup(a.warmup + steps)
+    print(f"[bench] setup {time.perf_counter() - t_setup:.1f}s; warmup {a.warmup} steps", file=sys.stderr, flush=True)
+    if a.calib_copy_mib:
+        n = a.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    for _ in range(a.warmup):
+        wl.step()
+        wl.advance_mirror()
+    torch.cuda.synchronize()
+    # timed region
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(wl.layers)]
+          for _ in range(steps)]
+    dec_bytes, dec_tokens = 0, 0
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_start.record()
+    for s in range(steps):
+        nb, nt = wl.decode_bytes_and_tokens()
+        dec_bytes += nb * wl.layers
+        dec_tokens += nt * wl.layers
+        wl.step(events=[(e[0], e[1]) for e in ev[s]])
+        wl.advance_mirror()
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    total_ms = t_start.elapsed_time(t_end)
+    dec_ms = sum(e0.elapsed_time(e1) for row in ev for (e0, e1) in row)
+    launches = steps * wl.layers
+    avg_dec_us = dec_ms * 1e3 / launches
+    bytes_per_launch = dec_bytes / launches
+    achieved = bytes_per_launch / (avg_dec_us * 1e-6) / 1e9
+    res = {
+        "metric": "decode KV tokens attended/sec (1 GPU)",
+        "value": dec_tokens / (total_ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": a.warmup,
+        "ms_per_step": total_ms / steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 (K/V fp16 + packed int4/int2 tiers, fp32 accumulate)",
+        "data": "synthetic",
+        "config": {"workload": {"c1": "1 layer, B1, 8q/2kv, d64, T512, K4/V4 (single-layer latency shape)",
+                                "c2": "Qwen2.5-3B-like: 36 layers, B1, 16q/2kv, d128, prefill 4096 H2O -> budget 400, K4/V2",
+                                "c3": "Llama-3.2-1B-like: 16 layers, B16 shared, 32q/8kv, d64, llama3 RoPE, budget 1024, K4/V4, evict every 256 steps",
+                                "c4": "Llama-3-8B-like: 32 layers, B1, 32q/8kv, d128, prefill 131072 -> position budget 8192, W128, K4/V2, bf16 q",
+                                "c5": "ragged serving batch: 64 sequences, context U[1024,32768], 32 layers, 32q/8kv, d128, K4/V2, EMA 0.9 eviction to 2048 per sequence, one 2048-token H2O prefill pass per step"}[a.workload],
+                   "name": a.workload, "layers": wl.layers, "batch": wl.B,
+                   "kv_tokens_attended_per_step": dec_tokens // steps},
+        "decode_attn": {"avg_us_per_launch": avg_dec_us, "bytes_per_launch": bytes_per_launch,
+                        "kernels": "k_decode_split + k_decode_combine" + (" + k_side_output" if wl.side else "")},
+        "wall_s_timed": wall,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+    }
+    if not a.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample ...", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(a.workload)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -55,6 +55,37 @@ constexpr int kQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
 constexpr int kQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
 constexpr int kRowRor2 = 0x122, kRowRor4 = 0x124, kRowRor8 = 0x128, kRowRor1 = 0x121;
 
+// Full-wave reductions without LDS: DPP inside each 16-lane row, then
+// row_bcast:15 / row_bcast:31 to fold the rows into lane 63, read back as a
+// wave-uniform value.
+__device__ __forceinline__ float wave_sum_u(float x) {
+  x += dpp_f<kRowRor1>(x);
+  x += dpp_f<kRowRor2>(x);
+  x += dpp_f<kRowRor4>(x);
+  x += dpp_f<kRowRor8>(x);
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x142, 0xA, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x143, 0xC, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+__device__ __forceinline__ float wave_max_u(float x) {
+  const int ninf = __builtin_bit_cast(int, -INFINITY);
+  x = fmaxf(x, dpp_f<kRowRor1>(x));
+  x = fmaxf(x, dpp_f<kRowRor2>(x));
+  x = fmaxf(x, dpp_f<kRowRor4>(x));
+  x = fmaxf(x, dpp_f<kRowRor8>(x));
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(ninf, __builtin_bit_cast(int, x), 0x142, 0xA, 0xF, false)));
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(ninf, __builtin_bit_cast(int, x), 0x143, 0xC, 0xF, false)));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+
+// (x & mask) | bits in one VALU op with every operand in a VGPR (VOP3 on gfx9
+// takes no 32-bit literal and one scalar operand at most).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t bits) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(mask), "v"(bits));
+  return r;
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
   x += dpp_f<kRowRor1>(x);
   x += dpp_f<kRowRor2>(x);
