@@ -17,12 +17,13 @@
 // each survivor its new slot. Integer work, bit-exact.
 //
 // In-place compaction of the middle tier: survivors only move toward lower
-// slots, so each workgroup reads its own chunk of source rows, waits, and
-// then writes every destination that lies inside its own chunk; the few
-// destinations that fall into the previous chunk go to a spill buffer that a
+// slots, so each workgroup stages the moved rows of its own chunk in LDS,
+// waits, and then writes every destination that lies inside its own chunk;
+// destinations that fall into an earlier chunk go to a spill region that a
 // second kernel copies after the grid has drained. Keys of moved rows are
 // dequantized, rotated by R(-delta) from a float64 cos/sin table, rounded to
-// fp16 and requantized; values are copied as packed bytes.
+// fp16 once and requantized, one lane per rotation pair; values move as
+// packed bytes.
 // Roofline: HBM (bytes of the moved rows read + written).
 #include "fade_common.hpp"
 #include "fade_internal.hpp"
@@ -208,39 +209,6 @@ __global__ void k_rope_table(RopeFreqs fr, int half, int n_delta, double2* tab) 
   tab[i] = make_double2(c, -s);
 }
 
-// Rotate a key pair-slice by the float64 (cos, sin) of the target shift.
-__device__ __forceinline__ void rotate_pair_block(const float* x1, const float* x2, const double2* cs,
-                                                  uint16_t* y1, uint16_t* y2) {
-#pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    const double c = cs[j].x, s = cs[j].y;
-    const double a = (double)x1[j], b = (double)x2[j];
-    y1[j] = d2h(a * c - b * s);
-    y2[j] = d2h(b * c + a * s);
-  }
-}
-
-template <int BITS>
-__device__ __forceinline__ void unpack_group(const uint8_t* p, uint16_t scale_bits, float* x) {
-  uint32_t w[BITS];
-  if constexpr (BITS == 4) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
-    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-  } else {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
-    w[0] = v.x; w[1] = v.y;
-  }
-  const float s = h2f(scale_bits);
-#pragma unroll
-  for (int c = 0; c < 32; ++c) x[c] = code_at<BITS>(w, c) * s;   // exact in fp32
-}
-
-template <int BITS>
-__device__ __forceinline__ void store_group(uint8_t* p, const uint32_t* w) {
-  if constexpr (BITS == 4) *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
-  else *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
-}
-
 struct CompactArgs {
   Shape s;
   fade_layer_cache c;
@@ -248,156 +216,241 @@ struct CompactArgs {
   int map_stride;
   const int32_t* info;
   const double2* tab;         // [(max_evict + 1) * D/2]
-  int chunk, nchunks, spill_rows;
-  int2* spill_info;           // [B][Hkv][nchunks]
-  uint8_t* spill;             // [B][Hkv][nchunks][spill_rows][rowbytes]
-  int rowbytes;
+  int nchunks, spill_rows;
+  size_t spill_stride;        // bytes of one (sequence, head, chunk) spill region
+  int2* spill_info;           // [B][Hkv][nchunks] = {first destination, spilled rows}
+  uint8_t* spill;             // [B][Hkv][nchunks] regions: K codes | V codes | K scales | V scales
 };
 
-// One thread per (row, rotation group pair) for the middle tier; the extra
-// x-block re-rotates the recent ring in place.
+constexpr int kCompactRows = 128;   // middle rows per compaction workgroup
+
+// OR over aligned groups of N lanes (N = 8 or 16), result in every lane of
+// the group: quad xor 1, quad xor 2, half-row mirror, then row mirror.
+template <int N>
+__device__ __forceinline__ uint32_t group_or(uint32_t x) {
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kQuadXor1, 0xF, 0xF, false);
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kQuadXor2, 0xF, 0xF, false);
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, false);
+  if constexpr (N == 16) x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x140, 0xF, 0xF, false);
+  return x;
+}
+
+// The group quantizer with one channel per lane: the 32 channels of a group
+// are the lanes of one half-wave (channel = lane % 32). Same arithmetic as
+// quant_group32: s = fp16_RNE(amax / qmax), q = clamp(RNE(x / s)) with IEEE
+// division. Returns the packed word that holds this lane's channel (in every
+// lane of the word's lane group) and the scale bits.
+template <int BITS>
+__device__ __forceinline__ uint32_t quant_lane(float x, int c, uint16_t& scale) {
+  constexpr int kOff = 1 << (BITS - 1);
+  constexpr float kQmax = (float)((1 << (BITS - 1)) - 1);
+  float amax = fabsf(x);
+  amax = fmaxf(amax, dpp_f<kRowRor1>(amax));
+  amax = fmaxf(amax, dpp_f<kRowRor2>(amax));
+  amax = fmaxf(amax, dpp_f<kRowRor4>(amax));
+  amax = fmaxf(amax, dpp_f<kRowRor8>(amax));
+  amax = fmaxf(amax, __shfl_xor(amax, 16));
+  const uint16_t sb = f2h(amax / kQmax);
+  const float s = h2f(sb);
+  int q = 0;
+  if (s != 0.f) {
+    float t = rintf(x / s);
+    t = fminf(fmaxf(t, -kQmax), kQmax);
+    q = (int)t;
+  }
+  constexpr int kPerWord = 32 / BITS;
+  scale = sb;
+  return group_or<kPerWord>((uint32_t)(q + kOff) << ((c % kPerWord) * BITS));
+}
+
+// Middle-tier compaction of one chunk of kCompactRows rows of one (sequence,
+// KV head); the extra x-block re-rotates the recent ring in place.
+//
+// Moved rows are staged in LDS with coalesced 16-byte loads. Each wave then
+// rebuilds one row per pass (two at D = 64) with one lane per rotation pair
+// (channels i and i + D/2): dequantize, rotate by the float64 cos/sin of the
+// shift, round to fp16, requantize with the group amax reduced across the
+// half-wave, and write the packed words back into LDS. After a barrier the
+// rows go out with coalesced stores, to their destination when it lies in
+// this chunk and to the spill region otherwise.
 template <int D, int KB, int VB>
 __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
-  constexpr int PAIRS = D / 64;                 // group pairs per row
-  constexpr int KROW = D * KB / 8, VROW = D * VB / 8;
-  constexpr int KG = 32 * KB / 8, VG = 32 * VB / 8;
+  constexpr int HALF = D / 2;                   // rotation pairs per row
+  constexpr int RPW = 64 / HALF;                // rows per wave pass
   constexpr int NG = D / 32;
-  __shared__ int s_first;
+  constexpr int KROW = D * KB / 8, VROW = D * VB / 8;
+  constexpr int CH = kCompactRows;
+  constexpr int KPW = 32 / KB;                  // channels per packed K word
+  constexpr uint32_t KMASK = (1u << KB) - 1u;
+  constexpr int KOFF = 1 << (KB - 1);
+  __shared__ __align__(16) uint32_t s_kc[CH * KROW / 4];
+  __shared__ __align__(16) uint32_t s_vc[CH * VROW / 4];
+  __shared__ __align__(16) uint16_t s_ks[CH * NG];
+  __shared__ __align__(16) uint16_t s_vs[CH * NG];
+  __shared__ int s_dst[CH];
+  __shared__ int s_first, s_lo, s_kept;
   const int cidx = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const Shape& s = a.s;
   const int mrow = s.shared ? 0 : b;
   const int M = a.info[4 * mrow + 0], n_ev = a.info[4 * mrow + 1];
-  const int Sl = a.info[4 * mrow + 2];
-  (void)Sl;
   if (n_ev == 0) return;
   const size_t bg = (size_t)(b * s.Hkv + g);
   const int tid = threadIdx.x;
-  const int pair = tid % PAIRS;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int p = lane % HALF, sub = lane / HALF;
 
   if (cidx == a.nchunks) {
     // Recent ring: every entry shifts by -n_ev positions; rotate fp16 K in place.
     const int32_t* L = a.c.lens + 4 * b;
     const int R = min(max(L[2], 0), s.ring), head = min(max(L[3], 0), s.ring - 1);
     const int slots = s.n_sink + s.ring;
-    const double2* cs = a.tab + (size_t)n_ev * (D / 2) + pair * 32;
-    for (int t = tid / PAIRS; t < R; t += 256 / PAIRS) {
+    const double2 cs = a.tab[(size_t)n_ev * HALF + p];
+    for (int t = wave * RPW + sub; t < R; t += 4 * RPW) {
       const int slot = s.n_sink + (head + t) % s.ring;
       uint16_t* kp = reinterpret_cast<uint16_t*>(a.c.fp_k) + (bg * slots + slot) * D;
-      float x1[32], x2[32];
-#pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        x1[j] = h2f(kp[pair * 32 + j]);
-        x2[j] = h2f(kp[pair * 32 + D / 2 + j]);
-      }
-      uint16_t y1[32], y2[32];
-      rotate_pair_block(x1, x2, cs, y1, y2);
-#pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        kp[pair * 32 + j] = y1[j];
-        kp[pair * 32 + D / 2 + j] = y2[j];
-      }
+      const double x1 = (double)h2f(kp[p]), x2 = (double)h2f(kp[p + HALF]);
+      kp[p] = d2h(x1 * cs.x - x2 * cs.y);
+      kp[p + HALF] = d2h(x2 * cs.x + x1 * cs.y);
     }
     return;
   }
 
   const int32_t* map = a.map + (size_t)mrow * a.map_stride;
-  const int r0 = cidx * a.chunk;
+  const int r0 = cidx * CH;
   if (r0 >= M) return;
-  const int rows_here = min(a.chunk, M - r0);
-  if (tid == 0) s_first = 0x7fffffff;
+  const int rows_here = min(CH, M - r0);
+  if (tid == 0) {
+    s_first = 0x7fffffff;
+    s_lo = CH;
+    s_kept = 0;
+  }
   __syncthreads();
   for (int t = tid; t < rows_here; t += 256) {
     const int d = map[r0 + t];
-    if (d >= 0) atomicMin(&s_first, d);
+    s_dst[t] = d;
+    if (d >= 0) {
+      atomicMin(&s_first, d);
+      atomicAdd(&s_kept, 1);
+      if (d != r0 + t) atomicMin(&s_lo, t);
+    }
   }
   __syncthreads();
-  const int first = s_first;
+  const int first = s_first, lo = s_lo, kept = s_kept;
+  if (tid == 0) {
+    // survivors of this chunk take the consecutive slots [first, first + kept)
+    const int cnt = first < r0 ? min(r0 - first, kept) : 0;
+    a.spill_info[bg * a.nchunks + cidx] = make_int2(first, cnt);
+  }
+  if (lo >= rows_here) return;                  // nothing moves in this chunk
+  const int n_rows = rows_here - lo;
   uint8_t* kc = reinterpret_cast<uint8_t*>(a.c.mid_k_codes);
   uint8_t* vc = reinterpret_cast<uint8_t*>(a.c.mid_v_codes);
-  uint16_t* ks = reinterpret_cast<uint16_t*>(a.c.mid_k_scales);
-  uint16_t* vs = reinterpret_cast<uint16_t*>(a.c.mid_v_scales);
-  // rows per pass: 256 / PAIRS
-  constexpr int RPP = 256 / PAIRS;
-  for (int base = 0; base < rows_here; base += RPP) {
-    const int t = base + tid / PAIRS;
-    const int r = r0 + t;
-    int d = -1;
-    if (t < rows_here) d = map[r];
-    const bool moved = d >= 0 && d != r;
-    uint32_t kw[2][KB];
-    uint16_t ksc[2];
-    uint8_t vbytes[2][VG];
-    uint16_t vsc[2];
-    if (moved) {
-      const int delta = r - d;
-      const size_t row = bg * s.cap_mid + r;
-      const int g1 = pair, g2 = pair + NG / 2;
-      float x1[32], x2[32];
-      unpack_group<KB>(kc + row * KROW + g1 * KG, ks[row * NG + g1], x1);
-      unpack_group<KB>(kc + row * KROW + g2 * KG, ks[row * NG + g2], x2);
-      uint16_t y1[32], y2[32];
-      rotate_pair_block(x1, x2, a.tab + (size_t)delta * (D / 2) + pair * 32, y1, y2);
-      float z[32];
-#pragma unroll
-      for (int j = 0; j < 32; ++j) z[j] = h2f(y1[j]);
-      quant_group32<KB>(z, kw[0], ksc[0]);
-#pragma unroll
-      for (int j = 0; j < 32; ++j) z[j] = h2f(y2[j]);
-      quant_group32<KB>(z, kw[1], ksc[1]);
-#pragma unroll
-      for (int j = 0; j < VG; ++j) {
-        vbytes[0][j] = vc[row * VROW + g1 * VG + j];
-        vbytes[1][j] = vc[row * VROW + g2 * VG + j];
-      }
-      vsc[0] = vs[row * NG + g1];
-      vsc[1] = vs[row * NG + g2];
-    }
-    __syncthreads();   // every source row of this pass has been read
-    if (moved) {
-      const int g1 = pair, g2 = pair + NG / 2;
-      if (d >= r0) {
-        const size_t row = bg * s.cap_mid + d;
-        store_group<KB>(kc + row * KROW + g1 * KG, kw[0]);
-        store_group<KB>(kc + row * KROW + g2 * KG, kw[1]);
-        ks[row * NG + g1] = ksc[0];
-        ks[row * NG + g2] = ksc[1];
-#pragma unroll
-        for (int j = 0; j < VG; ++j) {
-          vc[row * VROW + g1 * VG + j] = vbytes[0][j];
-          vc[row * VROW + g2 * VG + j] = vbytes[1][j];
-        }
-        vs[row * NG + g1] = vsc[0];
-        vs[row * NG + g2] = vsc[1];
-      } else {
-        const int slot = d - first;
-        uint8_t* sp = a.spill + ((bg * a.nchunks + cidx) * (size_t)a.spill_rows + slot) * a.rowbytes;
-        // spill row layout: K codes | K scales | V codes | V scales
-        store_group<KB>(sp + g1 * KG, kw[0]);
-        store_group<KB>(sp + g2 * KG, kw[1]);
-        uint16_t* sks = reinterpret_cast<uint16_t*>(sp + KROW);
-        sks[g1] = ksc[0];
-        sks[g2] = ksc[1];
-        uint8_t* svc = sp + KROW + 2 * NG;
-#pragma unroll
-        for (int j = 0; j < VG; ++j) {
-          svc[g1 * VG + j] = vbytes[0][j];
-          svc[g2 * VG + j] = vbytes[1][j];
-        }
-        uint16_t* svs = reinterpret_cast<uint16_t*>(svc + VROW);
-        svs[g1] = vsc[0];
-        svs[g2] = vsc[1];
-      }
-    }
-    // Rows of the next pass may be destinations of this pass's sources only
-    // if they lie below them, which they do not; still keep passes ordered.
-    __syncthreads();
+  uint8_t* ks = reinterpret_cast<uint8_t*>(a.c.mid_k_scales);
+  uint8_t* vs = reinterpret_cast<uint8_t*>(a.c.mid_v_scales);
+  const size_t row_lo = bg * s.cap_mid + r0 + lo;
+
+  // ---- stage rows [lo, rows_here) ----
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(kc + row_lo * KROW);
+    uint4* dst = reinterpret_cast<uint4*>(s_kc) + lo * (KROW / 16);
+    for (int i = tid; i < n_rows * (KROW / 16); i += 256) dst[i] = src[i];
   }
-  if (tid == 0) {
-    const int cnt = first < r0 ? min(r0 - first, rows_here) : 0;
-    a.spill_info[bg * a.nchunks + cidx] = make_int2(first, cnt);
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(vc + row_lo * VROW);
+    uint4* dst = reinterpret_cast<uint4*>(s_vc) + lo * (VROW / 16);
+    for (int i = tid; i < n_rows * (VROW / 16); i += 256) dst[i] = src[i];
+  }
+  {
+    const uint32_t* src_k = reinterpret_cast<const uint32_t*>(ks + row_lo * 2 * NG);
+    const uint32_t* src_v = reinterpret_cast<const uint32_t*>(vs + row_lo * 2 * NG);
+    uint32_t* dk = reinterpret_cast<uint32_t*>(s_ks) + lo * (NG / 2);
+    uint32_t* dv = reinterpret_cast<uint32_t*>(s_vs) + lo * (NG / 2);
+    for (int i = tid; i < n_rows * (NG / 2); i += 256) {
+      dk[i] = src_k[i];
+      dv[i] = src_v[i];
+    }
+  }
+  __syncthreads();
+
+  // ---- rebuild the keys of moved rows in LDS ----
+  int cur_delta = -1;
+  double2 cs = make_double2(1.0, 0.0);
+  const int c = p % 32;                          // channel within its group
+  for (int base = wave * RPW; base < n_rows; base += 4 * RPW) {
+    const int tt = base + sub;
+    const bool valid = tt < n_rows;
+    const int t = lo + min(tt, n_rows - 1);
+    const int d = s_dst[t];
+    const bool moved = valid && d >= 0 && d != r0 + t;
+    const int delta = moved ? r0 + t - d : 0;
+    if (delta != cur_delta) {
+      cs = a.tab[(size_t)delta * HALF + p];
+      cur_delta = delta;
+    }
+    const uint8_t* krow = reinterpret_cast<const uint8_t*>(s_kc) + t * KROW;
+    const uint32_t u1 = (krow[p * KB / 8] >> ((p * KB) % 8)) & KMASK;
+    const uint32_t u2 = (krow[(p + HALF) * KB / 8] >> (((p + HALF) * KB) % 8)) & KMASK;
+    const float x1 = (float)((int)u1 - KOFF) * h2f(s_ks[t * NG + p / 32]);          // exact
+    const float x2 = (float)((int)u2 - KOFF) * h2f(s_ks[t * NG + (p + HALF) / 32]);
+    const double a1 = (double)x1, a2 = (double)x2;
+    const float z1 = h2f(d2h(a1 * cs.x - a2 * cs.y));
+    const float z2 = h2f(d2h(a2 * cs.x + a1 * cs.y));
+    uint16_t sc1, sc2;
+    const uint32_t w1 = quant_lane<KB>(z1, c, sc1);
+    const uint32_t w2 = quant_lane<KB>(z2, c, sc2);
+    if (moved && c % KPW == 0) {
+      s_kc[t * (KROW / 4) + p / KPW] = w1;
+      s_kc[t * (KROW / 4) + (p + HALF) / KPW] = w2;
+    }
+    if (moved && c == 0) {
+      s_ks[t * NG + p / 32] = sc1;
+      s_ks[t * NG + (p + HALF) / 32] = sc2;
+    }
+  }
+  __syncthreads();
+
+  // ---- write moved rows: own chunk directly, earlier chunks via the spill ----
+  uint8_t* sp = a.spill + (bg * a.nchunks + cidx) * a.spill_stride;
+  uint8_t* sp_kc = sp;
+  uint8_t* sp_vc = sp_kc + (size_t)a.spill_rows * KROW;
+  uint8_t* sp_ks = sp_vc + (size_t)a.spill_rows * VROW;
+  uint8_t* sp_vs = sp_ks + (size_t)a.spill_rows * 2 * NG;
+  {
+    constexpr int U = KROW / 16;
+    for (int i = tid; i < n_rows * U; i += 256) {
+      const int t = lo + i / U, o = i % U;
+      const int d = s_dst[t];
+      if (d < 0 || d == r0 + t) continue;
+      uint8_t* rowp = d >= r0 ? kc + (bg * s.cap_mid + d) * KROW : sp_kc + (size_t)(d - first) * KROW;
+      reinterpret_cast<uint4*>(rowp)[o] = reinterpret_cast<const uint4*>(s_kc)[t * U + o];
+    }
+  }
+  {
+    constexpr int U = VROW / 16;
+    for (int i = tid; i < n_rows * U; i += 256) {
+      const int t = lo + i / U, o = i % U;
+      const int d = s_dst[t];
+      if (d < 0 || d == r0 + t) continue;
+      uint8_t* rowp = d >= r0 ? vc + (bg * s.cap_mid + d) * VROW : sp_vc + (size_t)(d - first) * VROW;
+      reinterpret_cast<uint4*>(rowp)[o] = reinterpret_cast<const uint4*>(s_vc)[t * U + o];
+    }
+  }
+  {
+    constexpr int U = NG / 2;
+    for (int i = tid; i < n_rows * U; i += 256) {
+      const int t = lo + i / U, o = i % U;
+      const int d = s_dst[t];
+      if (d < 0 || d == r0 + t) continue;
+      uint8_t* kp = d >= r0 ? ks + (bg * s.cap_mid + d) * 2 * NG : sp_ks + (size_t)(d - first) * 2 * NG;
+      uint8_t* vp = d >= r0 ? vs + (bg * s.cap_mid + d) * 2 * NG : sp_vs + (size_t)(d - first) * 2 * NG;
+      reinterpret_cast<uint32_t*>(kp)[o] = reinterpret_cast<const uint32_t*>(s_ks)[t * U + o];
+      reinterpret_cast<uint32_t*>(vp)[o] = reinterpret_cast<const uint32_t*>(s_vs)[t * U + o];
+    }
   }
 }
 
+// Copies the spilled rows of chunk blockIdx.x to their destinations, which
+// lie in earlier chunks; runs after every chunk has read its sources.
 template <int D, int KB, int VB>
 __global__ __launch_bounds__(256) void k_spill_copy(CompactArgs a) {
   constexpr int KROW = D * KB / 8, VROW = D * VB / 8, NG = D / 32;
@@ -405,38 +458,43 @@ __global__ __launch_bounds__(256) void k_spill_copy(CompactArgs a) {
   const int mrow = a.s.shared ? 0 : b;
   if (a.info[4 * mrow + 1] == 0) return;
   const int M = a.info[4 * mrow + 0];
-  if (cidx * a.chunk >= M) return;
+  if (cidx * kCompactRows >= M) return;
   const size_t bg = (size_t)(b * a.s.Hkv + g);
   const int2 si = a.spill_info[bg * a.nchunks + cidx];
   const int cnt = si.y;
-  uint8_t* kc = reinterpret_cast<uint8_t*>(a.c.mid_k_codes);
-  uint8_t* vc = reinterpret_cast<uint8_t*>(a.c.mid_v_codes);
-  uint8_t* ks = reinterpret_cast<uint8_t*>(a.c.mid_k_scales);
-  uint8_t* vs = reinterpret_cast<uint8_t*>(a.c.mid_v_scales);
-  for (int i = threadIdx.x; i < cnt * a.rowbytes; i += blockDim.x) {
-    const int t = i / a.rowbytes, o = i - t * a.rowbytes;
-    const uint8_t v = a.spill[((bg * a.nchunks + cidx) * (size_t)a.spill_rows + t) * a.rowbytes + o];
-    const size_t row = bg * a.s.cap_mid + si.x + t;
-    if (o < KROW) kc[row * KROW + o] = v;
-    else if (o < KROW + 2 * NG) ks[row * 2 * NG + (o - KROW)] = v;
-    else if (o < KROW + 2 * NG + VROW) vc[row * VROW + (o - KROW - 2 * NG)] = v;
-    else vs[row * 2 * NG + (o - KROW - 2 * NG - VROW)] = v;
+  if (cnt == 0) return;
+  const size_t row0 = bg * a.s.cap_mid + si.x;
+  const uint8_t* sp = a.spill + (bg * a.nchunks + cidx) * a.spill_stride;
+  const uint4* sk = reinterpret_cast<const uint4*>(sp);
+  const uint4* sv = reinterpret_cast<const uint4*>(sp + (size_t)a.spill_rows * KROW);
+  const uint32_t* sks = reinterpret_cast<const uint32_t*>(sp + (size_t)a.spill_rows * (KROW + VROW));
+  const uint32_t* svs = reinterpret_cast<const uint32_t*>(sp + (size_t)a.spill_rows * (KROW + VROW + 2 * NG));
+  uint4* kc = reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(a.c.mid_k_codes) + row0 * KROW);
+  uint4* vc = reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(a.c.mid_v_codes) + row0 * VROW);
+  uint32_t* ks = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(a.c.mid_k_scales) + row0 * 2 * NG);
+  uint32_t* vs = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(a.c.mid_v_scales) + row0 * 2 * NG);
+  for (int i = threadIdx.x; i < cnt * (KROW / 16); i += blockDim.x) kc[i] = sk[i];
+  for (int i = threadIdx.x; i < cnt * (VROW / 16); i += blockDim.x) vc[i] = sv[i];
+  for (int i = threadIdx.x; i < cnt * (NG / 2); i += blockDim.x) {
+    ks[i] = sks[i];
+    vs[i] = svs[i];
   }
 }
 
-static int compact_chunk(int D) { return 256 / (D / 64); }
+static size_t spill_stride_bytes(const Shape& s, int spill_rows) {
+  const int rowbytes = s.D * s.kb / 8 + s.D * s.vb / 8 + 2 * (s.D / 32) * 2;
+  return align_up((size_t)spill_rows * rowbytes, 16);
+}
 
 size_t evict_ws_bytes(const Shape& s, int max_evict) {
   const int rows = s.shared ? 1 : s.batch;
-  const int chunk = compact_chunk(s.D);
-  const int nchunks = (s.cap_mid + chunk - 1) / chunk;
-  const int spill_rows = max_evict < chunk ? max_evict : chunk;
-  const int rowbytes = s.D * s.kb / 8 + s.D / 16 + s.D * s.vb / 8 + s.D / 16;
+  const int nchunks = (s.cap_mid + kCompactRows - 1) / kCompactRows;
+  const int spill_rows = max_evict < kCompactRows ? max_evict : kCompactRows;
   size_t n = align_up((size_t)rows * 4 * 4, 256);
   n += align_up((size_t)rows * s.cap_mid * 4, 256);
   n += align_up((size_t)(max_evict + 1) * (s.D / 2) * 16, 256);
   n += align_up((size_t)s.batch * s.Hkv * nchunks * 8, 256);
-  n += align_up((size_t)s.batch * s.Hkv * nchunks * spill_rows * rowbytes, 256);
+  n += align_up((size_t)s.batch * s.Hkv * nchunks * spill_stride_bytes(s, spill_rows), 256);
   return n;
 }
 
@@ -458,10 +516,8 @@ static void launch_compact_d(const CompactArgs& a, hipStream_t st) {
 hipError_t launch_evict(const Shape& s, const fade_layer_cache& c, int policy, int max_evict,
                         const RopeFreqs& fr, void* ws, hipStream_t st) {
   const int rows = s.shared ? 1 : s.batch;
-  const int chunk = compact_chunk(s.D);
-  const int nchunks = (s.cap_mid + chunk - 1) / chunk;
-  const int spill_rows = max_evict < chunk ? max_evict : chunk;
-  const int rowbytes = s.D * s.kb / 8 + s.D / 16 + s.D * s.vb / 8 + s.D / 16;
+  const int nchunks = (s.cap_mid + kCompactRows - 1) / kCompactRows;
+  const int spill_rows = max_evict < kCompactRows ? max_evict : kCompactRows;
   char* w = reinterpret_cast<char*>(ws);
   int32_t* info = reinterpret_cast<int32_t*>(w);
   w += align_up((size_t)rows * 4 * 4, 256);
@@ -506,12 +562,11 @@ hipError_t launch_evict(const Shape& s, const fade_layer_cache& c, int policy, i
   ca.map_stride = s.cap_mid;
   ca.info = info;
   ca.tab = tab;
-  ca.chunk = chunk;
   ca.nchunks = nchunks;
   ca.spill_rows = spill_rows;
+  ca.spill_stride = spill_stride_bytes(s, spill_rows);
   ca.spill_info = spill_info;
   ca.spill = spill;
-  ca.rowbytes = rowbytes;
   if (s.D == 128) launch_compact_d<128>(ca, st);
   else launch_compact_d<64>(ca, st);
   return hipGetLastError();
@@ -535,103 +590,95 @@ struct BuildArgs {
   RopeFreqs fr;
 };
 
-// One thread per (prefill token, rotation group pair).
+constexpr int kBuildRows = 64;   // prefill tokens per build workgroup
+
+// One wave per prefill token (two at D = 64), one lane per rotation pair
+// (channels i and i + D/2). Keys whose position changes are rotated by the
+// float64 sin/cos of the shift (recomputed only when the shift changes) and
+// rounded to fp16 once; middle survivors are then quantized with the group
+// amax reduced across the half-wave, sink and recent tokens copied as fp16.
 template <int D, int KB, int VB>
 __global__ __launch_bounds__(256) void k_build(BuildArgs a) {
-  constexpr int PAIRS = D / 64, NG = D / 32;
-  constexpr int KROW = D * KB / 8, VROW = D * VB / 8, KG = 32 * KB / 8, VG = 32 * VB / 8;
+  constexpr int HALF = D / 2, RPW = 64 / HALF, NG = D / 32;
+  constexpr int KROW = D * KB / 8, VROW = D * VB / 8;
+  constexpr int KPW = 32 / KB, VPW = 32 / VB;
   const int g = blockIdx.y, b = blockIdx.z;
   const Shape& s = a.s;
   const int mrow = s.shared ? 0 : b;
   const int M = a.info[4 * mrow + 0], n_ev = a.info[4 * mrow + 1];
   const int S = a.info[4 * mrow + 2];
   const int Mk = M - n_ev;
-  const int j = blockIdx.x * (256 / PAIRS) + threadIdx.x / PAIRS;
-  const int pair = threadIdx.x % PAIRS;
-  if (j >= a.L) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int p = lane % HALF, sub = lane / HALF, c = p % 32;
   const size_t bg = (size_t)(b * s.Hkv + g);
-  const uint16_t* kr = a.k + (bg * a.L + j) * D;
-  const uint16_t* vr = a.v + (bg * a.L + j) * D;
-  int newpos;
-  int kind;   // 0 sink, 1 middle, 2 recent
-  int d = 0;
-  if (j < S) { kind = 0; newpos = j; }
-  else if (j < S + M) {
-    d = a.map[(size_t)mrow * a.L + (j - S)];
-    if (d < 0) return;
-    kind = 1;
-    newpos = S + d;
-  } else { kind = 2; newpos = S + Mk + (j - S - M); }
-  if (a.c.scores && pair == 0 && (!s.shared || b == 0) && g == 0)
-    a.c.scores[(size_t)mrow * s.cap_T + newpos] = a.pscores ? a.pscores[(size_t)mrow * a.L + j] : 0.f;
-  const int delta = j - newpos;
-  const int c1 = pair * 32, c2 = pair * 32 + D / 2;
-  uint16_t y1[32], y2[32];
-  if (delta != 0) {
-    float x1[32], x2[32];
-#pragma unroll
-    for (int t = 0; t < 32; ++t) {
-      x1[t] = h2f(kr[c1 + t]);
-      x2[t] = h2f(kr[c2 + t]);
-    }
-#pragma unroll
-    for (int t = 0; t < 32; ++t) {
-      double sn, cn;
-      sincos(-(double)delta * a.fr.f[c1 + t], &sn, &cn);
-      const double p = (double)x1[t], q = (double)x2[t];
-      y1[t] = d2h(p * cn - q * sn);
-      y2[t] = d2h(q * cn + p * sn);
-    }
-  } else {
-#pragma unroll
-    for (int t = 0; t < 32; ++t) {
-      y1[t] = kr[c1 + t];
-      y2[t] = kr[c2 + t];
-    }
-  }
   const int slots = s.n_sink + s.ring;
-  if (kind != 1) {
-    const int slot = kind == 0 ? j : s.n_sink + (j - S - M);
-    uint16_t* fk = reinterpret_cast<uint16_t*>(a.c.fp_k) + (bg * slots + slot) * D;
-    uint16_t* fv = reinterpret_cast<uint16_t*>(a.c.fp_v) + (bg * slots + slot) * D;
-#pragma unroll
-    for (int t = 0; t < 32; ++t) {
-      fk[c1 + t] = y1[t];
-      fk[c2 + t] = y2[t];
-      fv[c1 + t] = vr[c1 + t];
-      fv[c2 + t] = vr[c2 + t];
+  const double f = a.fr.f[p];
+  int cur_delta = 0;
+  double sn = 0.0, cn = 1.0;
+  const int j_end = min(a.L, (int)(blockIdx.x + 1) * kBuildRows);
+  for (int j0 = blockIdx.x * kBuildRows + wave * RPW; j0 < j_end; j0 += 4 * RPW) {
+    const int j = j0 + sub;
+    if (j >= j_end) continue;                   // half-wave granularity (D = 64)
+    int kind;   // 0 sink, 1 middle, 2 recent
+    int d = 0, newpos;
+    if (j < S) { kind = 0; newpos = j; }
+    else if (j < S + M) {
+      d = a.map[(size_t)mrow * a.L + (j - S)];
+      if (d < 0) continue;                      // evicted: the whole half-wave skips
+      kind = 1;
+      newpos = S + d;
+    } else { kind = 2; newpos = S + Mk + (j - S - M); }
+    if (a.c.scores && p == 0 && (!s.shared || b == 0) && g == 0)
+      a.c.scores[(size_t)mrow * s.cap_T + newpos] = a.pscores ? a.pscores[(size_t)mrow * a.L + j] : 0.f;
+    const uint16_t* kr = a.k + (bg * a.L + j) * D;
+    const uint16_t* vr = a.v + (bg * a.L + j) * D;
+    const uint16_t k1 = kr[p], k2 = kr[p + HALF], v1 = vr[p], v2 = vr[p + HALF];
+    const int delta = j - newpos;
+    uint16_t y1 = k1, y2 = k2;
+    if (delta != 0) {
+      if (delta != cur_delta) {
+        sincos(-(double)delta * f, &sn, &cn);
+        cur_delta = delta;
+      }
+      const double x1 = (double)h2f(k1), x2 = (double)h2f(k2);
+      y1 = d2h(x1 * cn - x2 * sn);
+      y2 = d2h(x2 * cn + x1 * sn);
     }
-    return;
+    if (kind != 1) {
+      const int slot = kind == 0 ? j : s.n_sink + (j - S - M);
+      uint16_t* fk = reinterpret_cast<uint16_t*>(a.c.fp_k) + (bg * slots + slot) * D;
+      uint16_t* fv = reinterpret_cast<uint16_t*>(a.c.fp_v) + (bg * slots + slot) * D;
+      fk[p] = y1;
+      fk[p + HALF] = y2;
+      fv[p] = v1;
+      fv[p + HALF] = v2;
+      continue;
+    }
+    const size_t row = bg * s.cap_mid + d;
+    uint32_t* kc = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(a.c.mid_k_codes) + row * KROW);
+    uint32_t* vc = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(a.c.mid_v_codes) + row * VROW);
+    uint16_t* ks = reinterpret_cast<uint16_t*>(a.c.mid_k_scales) + row * NG;
+    uint16_t* vs = reinterpret_cast<uint16_t*>(a.c.mid_v_scales) + row * NG;
+    uint16_t sk1, sk2, sv1, sv2;
+    const uint32_t wk1 = quant_lane<KB>(h2f(y1), c, sk1);
+    const uint32_t wk2 = quant_lane<KB>(h2f(y2), c, sk2);
+    const uint32_t wv1 = quant_lane<VB>(h2f(v1), c, sv1);
+    const uint32_t wv2 = quant_lane<VB>(h2f(v2), c, sv2);
+    if (c % KPW == 0) {
+      kc[p / KPW] = wk1;
+      kc[(p + HALF) / KPW] = wk2;
+    }
+    if (c % VPW == 0) {
+      vc[p / VPW] = wv1;
+      vc[(p + HALF) / VPW] = wv2;
+    }
+    if (c == 0) {
+      ks[p / 32] = sk1;
+      ks[(p + HALF) / 32] = sk2;
+      vs[p / 32] = sv1;
+      vs[(p + HALF) / 32] = sv2;
+    }
   }
-  const size_t row = bg * s.cap_mid + d;
-  uint8_t* kc = reinterpret_cast<uint8_t*>(a.c.mid_k_codes);
-  uint8_t* vc = reinterpret_cast<uint8_t*>(a.c.mid_v_codes);
-  uint16_t* ks = reinterpret_cast<uint16_t*>(a.c.mid_k_scales);
-  uint16_t* vs = reinterpret_cast<uint16_t*>(a.c.mid_v_scales);
-  const int g1 = pair, g2 = pair + NG / 2;
-  float z[32];
-  uint32_t w[4];
-  uint16_t sc;
-#pragma unroll
-  for (int t = 0; t < 32; ++t) z[t] = h2f(y1[t]);
-  quant_group32<KB>(z, w, sc);
-  store_group<KB>(kc + row * KROW + g1 * KG, w);
-  ks[row * NG + g1] = sc;
-#pragma unroll
-  for (int t = 0; t < 32; ++t) z[t] = h2f(y2[t]);
-  quant_group32<KB>(z, w, sc);
-  store_group<KB>(kc + row * KROW + g2 * KG, w);
-  ks[row * NG + g2] = sc;
-#pragma unroll
-  for (int t = 0; t < 32; ++t) z[t] = h2f(vr[c1 + t]);
-  quant_group32<VB>(z, w, sc);
-  store_group<VB>(vc + row * VROW + g1 * VG, w);
-  vs[row * NG + g1] = sc;
-#pragma unroll
-  for (int t = 0; t < 32; ++t) z[t] = h2f(vr[c2 + t]);
-  quant_group32<VB>(z, w, sc);
-  store_group<VB>(vc + row * VROW + g2 * VG, w);
-  vs[row * NG + g2] = sc;
 }
 
 __global__ void k_build_lens(const int32_t* info, int32_t* lens, int batch, int shared) {
@@ -688,8 +735,7 @@ hipError_t launch_prefill_build(const Shape& s, const fade_layer_cache& c, const
     ba.map = map;
     ba.info = info;
     ba.fr = fr;
-    const int tpb = 256 / (s.D / 64);
-    const dim3 grid((L + tpb - 1) / tpb, s.Hkv, s.batch);
+    const dim3 grid((L + kBuildRows - 1) / kBuildRows, s.Hkv, s.batch);
     if (s.D == 128) launch_build_d<128>(ba, grid, st);
     else launch_build_d<64>(ba, grid, st);
     e = hipGetLastError();
