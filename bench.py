@@ -367,7 +367,7 @@ def main():
                    "name": a.workload, "layers": wl.layers, "batch": wl.B,
                    "kv_tokens_attended_per_step": dec_tokens // steps},
         "decode_attn": {"avg_us_per_launch": avg_dec_us, "bytes_per_launch": bytes_per_launch,
-                        "kernels": "k_decode_mid + k_decode_fp16 + k_decode_combine" + (" + k_side_output" if wl.side else "")},
+                        "kernels": "k_decode_tiers + k_decode_combine" + (" + k_side_output" if wl.side else "")},
         "wall_s_timed": wall,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None},

@@ -1,27 +1,32 @@
 // Tiered decode attention (FADE post, FADE：面向LLM推理的注意力感知分层KV缓存
 // 压缩技术, sections "核心机制：三层级缓存架构" and "项目结构与代码质量": the
-// packed middle tier is dequantized inside the attention kernel).
+// packed middle tier is dequantized inside the attention kernel; one joint
+// softmax over sinks, middle and recent tokens).
 //
 // Work decomposition (one launch per layer):
-//   k_decode_split  grid (1 + nsplit_mid, Hkv, batch), 256 threads.
-//                   Split 0 streams the FP16 tier (sinks + recent ring);
-//                   split s >= 1 streams middle rows [(s-1)*chunk, s*chunk).
-//                   A workgroup serves all n_rep query heads of its KV head,
-//                   so every packed byte is read from HBM exactly once.
-//     phase 1  QK^T: lane = (token, 32-channel group); codes arrive as one
-//              16-byte (INT4) / 8-byte (INT2) load per lane, are unpacked
-//              with the fp16 magic-number trick (0x6400 | code = 1024 + code,
-//              then an exact packed subtraction of 1024 + offset) and fed to
-//              v_dot2_f32_f16 against the query pairs that match the nibble
-//              order; the per-group scale multiplies the fp32 group dot once.
-//              Group dots are summed across the token's lanes with DPP.
-//              Scores (log2 domain) go to LDS.
-//     phase 2  exact max and sum per head over the split (no online
-//              rescaling), p = 2^(s - m) in LDS.
-//     phase 3  PV: lane = (token, CPL-channel block); p * v_scale is folded
-//              into one fp32 weight per (token, head, group); the token-lane
-//              partial sums are reduced with DPP inside each 16-lane row and
-//              with LDS float atomics across rows and waves.
+//   k_decode_tiers  grid (nsplit, Hkv, batch), 256 threads. Split 0 streams
+//                   the FP16 tier (sinks + recent ring); split s >= 1 streams
+//                   middle rows [(s-1)*chunk, s*chunk). A workgroup serves
+//                   all n_rep query heads of its KV head, so every packed
+//                   byte is read from HBM once. Each wave takes 64-token
+//                   sub-chunks with one lane per token: the lane loads its
+//                   token's packed K row, K scales, V row and V scales with
+//                   16-byte loads (consecutive lanes read consecutive rows).
+//     QK^T  v_mfma_f32_4x4x4_16b_f16: A = four query heads (broadcast from
+//           block 0), B column = the lane's token, k = 4 channels. K codes
+//           are decoded to exact signed fp16 values (code - off) * 2^p with
+//           the fp16 bias trick and the query slots carry 2^-p, so the
+//           32-channel group dot is exact products summed in fp32, then
+//           scaled by the group scale. (fp16 subnormal operands would save
+//           one op per pair, but this MFMA sums them about 40x less
+//           accurately than fp32, which the per-slot attention cannot take.)
+//     softmax  per head, running max kept wave-uniform; it is rebuilt (and
+//           the accumulators rescaled) only when a sub-chunk exceeds it.
+//     PV    the same MFMA with blocks = 4-channel column blocks: A = fp16
+//           weights p * v_scale of four tokens (broadcast per 32-channel
+//           group), B = the signed codes of those tokens for the lane's
+//           channel, read from a per-wave LDS tile of V transposed to
+//           [16-bit unit][token] and decoded with the fp16 bias trick.
 //   k_decode_combine  log-sum-exp merge of the splits per (sequence, q head).
 //   k_side_output     a_j = sum_h 2^(s_hj - M_h) / L_h per slot position.
 // Roofline: HBM. Algorithmic bytes per launch = live tier bytes + q + out
@@ -42,18 +47,19 @@ struct DecodeArgs {
   const uint16_t* q;
   float* part;        // [B, Hq, nsplit, D + 2]
   float* raw;         // [B, Hq, cap_T] (log2-domain scores) or nullptr
-  int Hkv, n_sink, ring, cap_mid, cap_T, chunk, nsplit, lds_n;
+  int Hkv, n_sink, ring, cap_mid, cap_T, chunk, nsplit;
   float qk_scale;     // log2(e) / sqrt(D)
 };
 
 constexpr int kThreads = 256;
+constexpr int kSub = 64;          // tokens per wave sub-chunk (one per lane)
 
 int decode_chunk(const Shape& s) {
   // Middle rows per split: enough workgroups to cover 256 CUs several times,
   // but each split large enough that its partial (n_rep * (D + 2) floats) is
   // a small fraction of the bytes it streams.
   const int pairs = s.batch * s.Hkv;
-  const int unit = 4 * 64;                          // four waves x one 64-token sub-chunk
+  const int unit = 4 * kSub;                        // four waves x one sub-chunk
   int chunk = 2 * unit;
   while (chunk > unit && (long)pairs * ((s.cap_mid + chunk - 1) / chunk) < 2048) chunk /= 2;
   return chunk;
@@ -70,109 +76,75 @@ size_t decode_ws_bytes(const Shape& s) {
   return n;
 }
 
-// ---- K codes for QK^T: exact small integers in fp16 ---------------------------
-// (w >> s) & mask | 0x6400 per half is fp16(1024 + code); one packed
-// subtraction of fp16(1024 + 2^(b-1)) leaves the exact signed code. The
-// query is stored in pairs that match the field order:
-//   INT4 word j (channels 8j..8j+7): (w >> 4k) & 0x000F000F -> (c_k, c_k+4)
-//   INT2 word j (channels 16j..16j+15): (w >> 2k) & 0x00030003 -> (c_k, c_k+8)
-// v_dot2_f32_f16 then forms exact products into an fp32 accumulator, which
-// keeps the per-slot attention (the side output that drives eviction) at
-// about 1e-6 relative.
-template <int KB>
-__device__ __forceinline__ void load_q_pairs_mid(const float* qg, f16x2* qp) {
-  if constexpr (KB == 4) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) qp[4 * j + k] = f16x2{(f16)qg[8 * j + k], (f16)qg[8 * j + k + 4]};
-  } else {
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int k = 0; k < 8; ++k) qp[8 * j + k] = f16x2{(f16)qg[16 * j + k], (f16)qg[16 * j + k + 8]};
-  }
-}
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f16x2 as_h2(uint32_t w) { return __builtin_bit_cast(f16x2, w); }
+__device__ __forceinline__ uint32_t h2_bits(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ f16x4 as_h4(uint32_t lo, uint32_t hi) { return __builtin_bit_cast(f16x4, u32x2{lo, hi}); }
 
-__device__ __forceinline__ float fdot2(f16x2 a, f16x2 b, float c) {
-  return __builtin_amdgcn_fdot2(a, b, c, false);
+// v_mfma_f32_4x4x4_16b_f16: 16 independent 4x4x4 products. Lane l belongs to
+// block l / 4, supplies row l % 4 of A and column l % 4 of B (k = 0..3 in its
+// four halves) and receives rows 0..3 of column l % 4. CBSZ broadcasts the A
+// operand of the first block of each group of 2^CBSZ blocks to the group.
+template <int CBSZ>
+__device__ __forceinline__ f32x4 mfma4(f16x4 a, f16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_4x4x4f16(a, b, c, CBSZ, 0, 0);
 }
 
-// Sum_c q_c * (code_c - 2^(KB-1)) over one packed group, NREP heads.
-template <int KB, int NREP>
-__device__ __forceinline__ void group_dot_codes(const uint32_t* w, const f16x2 (*qp)[16], float* out) {
-  constexpr uint16_t kBias = (uint16_t)(0x6400 + (1 << (KB - 1)));   // fp16(1024 + offset)
-  const f16x2 bias = {__builtin_bit_cast(f16, kBias), __builtin_bit_cast(f16, kBias)};
-  constexpr uint32_t kMask = KB == 4 ? 0x000F000Fu : 0x00030003u;
-  constexpr int kPer = KB == 4 ? 4 : 8;      // pairs per 32-bit word
-#pragma unroll
-  for (int h = 0; h < NREP; ++h) out[h] = 0.f;
-#pragma unroll
-  for (int j = 0; j < KB; ++j) {
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const f16x2 kv = as_h2(((w[j] >> (KB * k)) & kMask) | 0x64006400u) - bias;
-#pragma unroll
-      for (int h = 0; h < NREP; ++h) out[h] = fdot2(qp[h][kPer * j + k], kv, out[h]);
-    }
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void lane_group_reduce(float& x) {
-  if constexpr (D == 128) {
-    x += dpp_f<kQuadXor1>(x);
-    x += dpp_f<kQuadXor2>(x);
-  } else {
-    x += dpp_f<kQuadXor1>(x);
-  }
-}
-
+// K codes as exact signed fp16 values (the bias trick: a b-bit field f at
+// bits p..p+b-1 of a half, OR-ed with 0x6400, reads 1024 + f * 2^p; one packed
+// subtraction of 1024 + off * 2^p leaves (f - off) * 2^p exactly). MFMA k-step
+// s of a row covers four channels; slot k of step s holds channel
+// key_channel(s, k) scaled by 2^key_shift(s, k), and the query slot carries
+// the inverse power of two.
+//   INT4 word j (channels 8j..8j+7, channel 8j+n at bits 4n): pairs
+//     n = 0..3 -> (8j+n, 8j+n+4), decoded in place (n = 0, 2: p = 0; n = 1,
+//     3: p = 4) from the word and from the word shifted right by 8.
+//   INT2 word j (channels 16j..16j+15, channel 16j+n at bits 2n): pairs
+//     n = 0..7 -> (16j+n, 16j+n+8), each from the word shifted right by 2n.
 template <int KB>
-struct KWords { uint32_t w[KB]; };
-
+__host__ __device__ constexpr int key_channel(int s, int k) {
+  if constexpr (KB == 4) return 8 * (s / 2) + 2 * (s % 2) + (k >> 1) + 4 * (k & 1);
+  else return 16 * (s / 4) + 2 * (s % 4) + (k >> 1) + 8 * (k & 1);
+}
 template <int KB>
-__device__ __forceinline__ KWords<KB> load_kwords(const uint8_t* p) {
-  KWords<KB> r;
+__host__ __device__ constexpr int key_shift(int s, int k) {
+  if constexpr (KB == 4) return ((2 * (s % 2) + (k >> 1)) & 1) ? 4 : 0;
+  else return 0;
+}
+// Constants of the decode, kept in VGPRs (VOP3 takes no 32-bit literal).
+struct KeyConst {
+  uint32_t m0, m1, bias;
+  f16x2 sub0, sub1;
+};
+template <int KB>
+__device__ __forceinline__ KeyConst key_const() {
+  KeyConst c;
+  c.m0 = KB == 4 ? 0x000F000Fu : 0x00030003u;
+  c.m1 = 0x00F000F0u;
+  c.bias = 0x64006400u;
+  asm volatile("" : "+v"(c.m0), "+v"(c.m1), "+v"(c.bias));
+  const f16 s0 = (f16)(1024.f + (float)(1 << (KB - 1))), s1 = (f16)(1024.f + 128.f);
+  c.sub0 = f16x2{s0, s0};
+  c.sub1 = f16x2{s1, s1};
+  return c;
+}
+// B operand of k-step s from the row's 32-bit words.
+template <int KB>
+__device__ __forceinline__ f16x4 key_operand(const uint32_t* w, int s, const KeyConst& c) {
   if constexpr (KB == 4) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
-    r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
+    const uint32_t x = (s & 1) ? (w[s >> 1] >> 8) : w[s >> 1];
+    const uint32_t p0 = h2_bits(as_h2(and_or(x, c.m0, c.bias)) - c.sub0);
+    const uint32_t p1 = h2_bits(as_h2(and_or(x, c.m1, c.bias)) - c.sub1);
+    return as_h4(p0, p1);
   } else {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
-    r.w[0] = v.x; r.w[1] = v.y;
+    const uint32_t word = w[s >> 2];
+    const int n0 = 2 * (s & 3);
+    const uint32_t p0 = h2_bits(as_h2(and_or(word >> (2 * n0), c.m0, c.bias)) - c.sub0);
+    const uint32_t p1 = h2_bits(as_h2(and_or(word >> (2 * n0 + 2), c.m0, c.bias)) - c.sub0);
+    return as_h4(p0, p1);
   }
-  return r;
-}
-
-// Lane-local packed V bytes of one token (CB bytes: CPL channels x VB bits).
-template <int CB>
-struct VBytes { uint32_t w[CB >= 4 ? CB / 4 : 1]; };
-
-template <int CB>
-__device__ __forceinline__ VBytes<CB> load_vbytes(const uint8_t* p) {
-  VBytes<CB> r;
-  if constexpr (CB == 16) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
-    r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
-  } else if constexpr (CB == 8) {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
-    r.w[0] = v.x; r.w[1] = v.y;
-  } else if constexpr (CB == 4) {
-    r.w[0] = *reinterpret_cast<const uint32_t*>(p);
-  } else {
-    r.w[0] = *reinterpret_cast<const uint16_t*>(p);
-  }
-  return r;
-}
-
-template <int CB>
-__device__ __forceinline__ VBytes<CB> zero_vbytes() {
-  VBytes<CB> r;
-#pragma unroll
-  for (int i = 0; i < (CB >= 4 ? CB / 4 : 1); ++i) r.w[i] = 0u;
-  return r;
 }
 
 // Orders this wave's LDS traffic: DS instructions of one wave complete in
@@ -183,103 +155,47 @@ __device__ __forceinline__ void wave_lds_sync() {
   asm volatile("" ::: "memory");
 }
 
-template <int D>
-__device__ __forceinline__ void load_f16x32(const uint16_t* p, float* x) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint4 w = reinterpret_cast<const uint4*>(p)[i];
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      x[8 * i + 2 * j] = h2f((uint16_t)(ws[j] & 0xFFFFu));
-      x[8 * i + 2 * j + 1] = h2f((uint16_t)(ws[j] >> 16));
-    }
-  }
-}
+template <int D, int NREP, int KB, int VB>
+struct TierLayout {
+  static constexpr int NG = D / 32, NI = D / 4, HQ4 = (NREP + 3) / 4, U = D * VB / 16;
+  static constexpr int PW = 72;                                   // halves per LDS token row
+  static constexpr int q_bytes = HQ4 * NI * 16 * 2;               // query fragments, fp16
+  static constexpr int kf_bytes = HQ4 * 4 * 4;                    // per-head score factor
+  static constexpr int wml_bytes = 4 * 2 * HQ4 * 4 * 4;           // per-wave (max, sum)
+  static constexpr int head_bytes = (q_bytes + kf_bytes + wml_bytes + 15) / 16 * 16;
+  static constexpr int pw_bytes = HQ4 * NG * 4 * PW * 2;          // weights [hq][g][row][token]
+  static constexpr int vt_bytes = U * PW * 2;                     // V units [unit][token]
+  static constexpr int wacc_bytes = HQ4 * 4 * D * 4;              // per-wave output [head][D]
+  static constexpr int wave_bytes = ((pw_bytes + vt_bytes > wacc_bytes ? pw_bytes + vt_bytes : wacc_bytes) + 15) / 16 * 16;
+  static constexpr int total = head_bytes + 4 * wave_bytes;
+};
 
-// MFMA operand pieces for QK^T (v_mfma_f32_16x16x32_f16): lane l supplies
-// A row (l % 16) = query head, B column (l % 16) = token, and k-slots
-// 8 * (l / 16) + i = channels 32 g + 8 Q + pi(i) of group g, Q = l / 16,
-// pi = [0, 4, 1, 5, 2, 6, 3, 7] (the order the bias unpack produces).
-// D row 4 Q + i, column l % 16.
-__device__ __forceinline__ f16x8 unpack8_int4(uint32_t w, uint32_t vmask, uint32_t vmagic) {
-  const f16 bh = __builtin_bit_cast(f16, (uint16_t)0x6408);          // 1024 + 8
-  const f16x2 bias = {bh, bh};
-  f16x8 r;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const f16x2 v = as_h2(and_or(w >> (4 * k), vmask, vmagic)) - bias;
-    r[2 * k] = v.x;
-    r[2 * k + 1] = v.y;
-  }
-  return r;
-}
-// 8 crumbs of a 16-bit unit (channel i at bits 2i) -> exact fp16, pi order.
-__device__ __forceinline__ f16x8 unpack8_int2(uint32_t unit16) {
-  const f16 bh = __builtin_bit_cast(f16, (uint16_t)0x6402);          // 1024 + 2
-  const f16x2 bias = {bh, bh};
-  // low byte -> half 0, high byte -> half 1
-  const uint32_t x = __builtin_amdgcn_perm(0u, unit16, 0x0C010C00u);
-  f16x8 r;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const f16x2 v = as_h2(((x >> (2 * k)) & 0x00030003u) | 0x64006400u) - bias;
-    r[2 * k] = v.x;
-    r[2 * k + 1] = v.y;
-  }
-  return r;
-}
-
-template <int D, int NREP>
-__device__ __forceinline__ void load_q_afrag(const float* q_lds, int lane, f16x8* afrag) {
-  constexpr int NG = D / 32;
-  const int h = lane & 15, Q = lane >> 4;
-  const int pi[8] = {0, 4, 1, 5, 2, 6, 3, 7};
-#pragma unroll
-  for (int g = 0; g < NG; ++g)
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      afrag[g][i] = h < NREP ? (f16)q_lds[h * D + 32 * g + 8 * Q + pi[i]] : (f16)0.f;
-}
-
-// Packed middle tiers. Each wave streams sub-chunks of SUB tokens of its
-// workgroup's split:
-//   1. issue the loads of the sub-chunk's K codes, V codes and scales together,
-//   2. QK^T on MFMA, 16 tokens per tile, one MFMA per 32-channel group whose
-//      fp32 result is scaled by that group's per-token scale,
-//   3. online softmax update of the wave's running max / sum (rescaling the
-//      PV accumulators once per sub-chunk),
-//   4. PV on VALU: token pairs, v_dot2_f32_f16 on subnormal-unpacked codes.
-// The four waves' partial (max, sum, accumulators) are merged once at the end.
 template <int D, int NREP, int KB, int VB, bool QBF>
-__global__ __launch_bounds__(kThreads) void k_decode_mid(DecodeArgs a) {
-  constexpr int NG = D / 32;
-  constexpr int SUB = 64;                    // tokens per wave sub-chunk
-  constexpr int TILES = SUB / 16;            // MFMA QK tiles per sub-chunk
-  constexpr int CPL = NREP <= 4 ? 16 : 8;    // channels per lane in PV
-  constexpr int LPP = D / CPL;               // lanes per token pair in PV
-  constexpr int PPW = kWave / LPP;           // token pairs per PV iteration
-  constexpr int UV = SUB / (2 * PPW);        // PV iterations per sub-chunk
+__global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
+  using Lay = TierLayout<D, NREP, KB, VB>;
+  constexpr int NG = Lay::NG, NI = Lay::NI, HQ4 = Lay::HQ4, U = Lay::U, PW = Lay::PW;
   constexpr int KROW = D * KB / 8, VROW = D * VB / 8;
-  constexpr int CB = CPL * VB / 8;           // packed V bytes per lane per token
-  constexpr int CPB = 8 / VB;                // channels per byte
+  constexpr int KW = KROW / 4, VW = VROW / 4;        // 32-bit words per row
+  constexpr int CPU = 16 / VB;                       // channels per 16-bit V unit
+  constexpr int NSIG = D / 64;                       // 64-channel PV passes
   constexpr int kOffV = 1 << (VB - 1);
 
-  extern __shared__ float smem[];
-  float* q_lds = smem;                                   // [NREP][D]
-  float* sc_all = q_lds + NREP * D;                      // [4][NREP][SUB]
-  float* wacc = sc_all + 4 * NREP * SUB;                 // [4][NREP][D]
-  float* wml = wacc + 4 * NREP * D;                      // [4][2][NREP]
-  float* raw_lds = wml + 8 * NREP;                       // [NREP][chunk] (side output only)
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint16_t* qf = reinterpret_cast<uint16_t*>(smem);                          // [HQ4][NI][4][4]
+  float* kf = reinterpret_cast<float*>(smem + Lay::q_bytes);                 // [HQ4 * 4]
+  float* wml = kf + HQ4 * 4;                                                 // [4][2][HQ4 * 4]
+  unsigned char* wreg = smem + Lay::head_bytes;
 
-  const int split = blockIdx.x + 1, g = blockIdx.y, b = blockIdx.z;
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int Hq = a.Hkv * NREP;
   const int32_t* L = a.lens + 4 * b;
   // Lengths are clamped to capacity so no value in lens can index out of bounds.
   const int S = min(max(L[0], 0), a.n_sink), M = min(max(L[1], 0), a.cap_mid);
-  const int row0 = (split - 1) * a.chunk;
-  const int n_tok = min(a.chunk, M - row0);
+  const int R = min(max(L[2], 0), a.ring), rhead = min(max(L[3], 0), a.ring - 1);
+  const bool fpt = split == 0;                       // FP16 tier
+  const int row0 = fpt ? 0 : (split - 1) * a.chunk;
+  const int n_tok = fpt ? S + R : min(a.chunk, M - row0);
 
   float* part_base = a.part + ((size_t)(b * Hq + g * NREP) * a.nsplit + split) * (D + 2);
   const size_t part_hstride = (size_t)a.nsplit * (D + 2);
@@ -290,228 +206,294 @@ __global__ __launch_bounds__(kThreads) void k_decode_mid(DecodeArgs a) {
     }
     return;
   }
+
+  // ---- query fragments ----
   const uint16_t* qrow = a.q + (size_t)(b * Hq + g * NREP) * D;   // NREP consecutive heads
-  for (int i = tid; i < NREP * D; i += kThreads) q_lds[i] = QBF ? bf2f(qrow[i]) : h2f(qrow[i]);
+  uint32_t* qexp = reinterpret_cast<uint32_t*>(wml);              // scratch: per-head max |q| bits
+  if constexpr (QBF) {
+    // bf16 queries are moved into fp16 range by a power of two per head.
+    if (tid < HQ4 * 4) qexp[tid] = 0u;
+    __syncthreads();
+    for (int i = tid; i < NREP * D; i += kThreads)
+      atomicMax(&qexp[i / D], __float_as_uint(fabsf(bf2f(qrow[i]))));
+    __syncthreads();
+  }
+  auto head_exp = [&](int h) -> int {
+    if constexpr (!QBF) return 0;
+    const int e = (int)((qexp[h] >> 23) & 0xFFu) - 127;
+    return e >= 15 ? e - 14 : 0;
+  };
+  for (int i = tid; i < HQ4 * NI * 16; i += kThreads) {
+    const int k = i & 3, r = (i >> 2) & 3, sidx = (i >> 4) % NI, hq = (i >> 4) / NI;
+    const int h = 4 * hq + r;
+    float v = 0.f;
+    if (h < NREP) {
+      const int ch = fpt ? 4 * sidx + k : key_channel<KB>(sidx, k);
+      const int e = fpt ? 0 : key_shift<KB>(sidx, k);
+      const float qv = QBF ? bf2f(qrow[h * D + ch]) : h2f(qrow[h * D + ch]);
+      v = ldexpf(qv, -head_exp(h) - e);
+    }
+    qf[i] = f2h(v);
+  }
+  __syncthreads();
+  if (tid < HQ4 * 4) {
+    const int h = tid;
+    kf[tid] = h < NREP ? ldexpf(a.qk_scale, head_exp(h)) : 0.f;
+  }
   __syncthreads();
 
-  const int n16 = lane & 15, Q = lane >> 4;        // MFMA lane role
-  const int cb = lane % LPP, tp = lane / LPP;      // PV lane role
   const size_t bg = (size_t)(b * a.Hkv + g);
-  float* sc = sc_all + wave * NREP * SUB;
   float* rawb = a.raw ? a.raw + (size_t)(b * Hq + g * NREP) * a.cap_T : nullptr;
+  uint16_t* pw = reinterpret_cast<uint16_t*>(wreg + wave * Lay::wave_bytes);   // [HQ4][NG][4][PW]
+  uint16_t* vt = pw + Lay::pw_bytes / 2;                                       // [U][PW]
+  const uint32_t* qf32 = reinterpret_cast<const uint32_t*>(qf);
 
-  float m_run[NREP], l_run[NREP], wsum[NREP];
-  float o[NREP][CPL];
+  float m_run[HQ4 * 4], l_lane[HQ4 * 4];
+  f32x4 o[NSIG][HQ4];
 #pragma unroll
-  for (int h = 0; h < NREP; ++h) {
+  for (int h = 0; h < HQ4 * 4; ++h) {
     m_run[h] = -INFINITY;
-    l_run[h] = 0.f;
-    wsum[h] = 0.f;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) o[h][c] = 0.f;
+    l_lane[h] = 0.f;
   }
-  f16x8 afrag[NG];
-  if constexpr (!QBF) load_q_afrag<D, NREP>(q_lds, lane, afrag);
-  uint32_t vmask4 = 0x000F000Fu, vmagic = 0x64006400u;   // kept in VGPRs for v_and_or_b32
-  asm volatile("" : "+v"(vmask4), "+v"(vmagic));
+#pragma unroll
+  for (int sg = 0; sg < NSIG; ++sg)
+#pragma unroll
+    for (int hq = 0; hq < HQ4; ++hq) o[sg][hq] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const uint8_t* krows = a.kc + (bg * a.cap_mid + row0) * KROW;
-  const uint16_t* kscl = a.ks + (bg * a.cap_mid + row0) * NG;
-  const uint8_t* vbase = a.vc + (bg * a.cap_mid + row0) * VROW + cb * CB;
-  const uint16_t* vsb = a.vs + (bg * a.cap_mid + row0) * NG + (cb * CPL) / 32;
-
-  // Loads of a sub-chunk: K words and scales of TILES MFMA tiles, V bytes and
-  // scales of UV PV iterations. Rows past the split's end are clamped to its
-  // last row, so the loads stay unconditional and in bounds; those tokens get
-  // zero weight below.
-  struct Loads {
-    uint32_t kd[TILES][NG];
-    uint32_t ksw[TILES][(NG + 1) / 2];
-    VBytes<CB> va[UV], vb[UV];
-    float sva[UV], svb[UV];
+  // Running softmax update of one head with this sub-chunk's scores.
+  auto softmax_step = [&](const float (&s2)[HQ4 * 4], float (&p)[HQ4 * 4], bool valid) {
+#pragma unroll
+    for (int h = 0; h < HQ4 * 4; ++h) {
+      p[h] = 0.f;
+      if (h >= NREP) continue;
+      if (__any(s2[h] > m_run[h])) {              // wave-uniform
+        const float mx = wave_max_u(s2[h]);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[h] - mx);
+        l_lane[h] *= alpha;
+#pragma unroll
+        for (int sg = 0; sg < NSIG; ++sg) o[sg][h / 4][h % 4] *= alpha;
+        m_run[h] = mx;
+      }
+      p[h] = valid ? __builtin_amdgcn_exp2f(s2[h] - m_run[h]) : 0.f;
+      l_lane[h] += p[h];
+    }
   };
-  auto issue = [&](Loads& L2, int base) {
-    const int last = n_tok - 1;
+
+  if (!fpt) {
+    // ---------------- packed middle tier ----------------
+    const uint8_t* krow0 = a.kc + (bg * a.cap_mid + row0) * KROW;
+    const uint16_t* ks0 = a.ks + (bg * a.cap_mid + row0) * NG;
+    const uint8_t* vrow0 = a.vc + (bg * a.cap_mid + row0) * VROW;
+    const uint16_t* vs0 = a.vs + (bg * a.cap_mid + row0) * NG;
+    // PV lane constants: channel 64 sg + lane, its 16-bit unit and field.
+    int vu[NSIG];
+    uint32_t vsh[NSIG], vmask[NSIG];
+    f16x2 vsub[NSIG];
+    float vscale[NSIG];
 #pragma unroll
-    for (int u = 0; u < TILES; ++u) {
-      const int t = min(base + 16 * u + n16, last);
-      const uint8_t* kr = krows + (size_t)t * KROW;
+    for (int sg = 0; sg < NSIG; ++sg) {
+      const int c = 64 * sg + lane;
+      vu[sg] = c / CPU;
+      const int bit = (c % CPU) * VB;
+      const int sh = bit + VB <= 10 ? 0 : (VB == 2 ? 10 : 8);
+      const int pos = bit - sh;
+      vsh[sg] = (uint32_t)sh;
+      vmask[sg] = (((1u << VB) - 1u) << pos) * 0x00010001u;
+      const f16 sub = (f16)(1024.f + (float)(kOffV << pos));
+      vsub[sg] = f16x2{sub, sub};
+      vscale[sg] = ldexpf(1.f, -pos);
+    }
+    struct Loads {
+      uint32_t k[KW];
+      uint32_t v[VW];
+      uint32_t ks[NG / 2];
+      uint32_t vs[NG / 2];
+    };
+    auto issue = [&](Loads& ld, int base) {
+      const int t = min(base + lane, n_tok - 1);
+      const uint4* kp = reinterpret_cast<const uint4*>(krow0 + (size_t)t * KROW);
 #pragma unroll
-      for (int gg = 0; gg < NG; ++gg) {
-        if constexpr (KB == 4) L2.kd[u][gg] = *reinterpret_cast<const uint32_t*>(kr + 16 * gg + 4 * Q);
-        else L2.kd[u][gg] = *reinterpret_cast<const uint32_t*>(kr + 8 * gg + 4 * (Q >> 1));
+      for (int i = 0; i < KW / 4; ++i) {
+        const uint4 w = kp[i];
+        ld.k[4 * i] = w.x; ld.k[4 * i + 1] = w.y; ld.k[4 * i + 2] = w.z; ld.k[4 * i + 3] = w.w;
+      }
+      const uint4* vp = reinterpret_cast<const uint4*>(vrow0 + (size_t)t * VROW);
+#pragma unroll
+      for (int i = 0; i < VW / 4; ++i) {
+        const uint4 w = vp[i];
+        ld.v[4 * i] = w.x; ld.v[4 * i + 1] = w.y; ld.v[4 * i + 2] = w.z; ld.v[4 * i + 3] = w.w;
       }
       if constexpr (NG == 4) {
-        const uint2 sv = *reinterpret_cast<const uint2*>(kscl + (size_t)t * NG);
-        L2.ksw[u][0] = sv.x;
-        L2.ksw[u][1] = sv.y;
+        const uint2 k2 = *reinterpret_cast<const uint2*>(ks0 + (size_t)t * NG);
+        const uint2 v2 = *reinterpret_cast<const uint2*>(vs0 + (size_t)t * NG);
+        ld.ks[0] = k2.x; ld.ks[1] = k2.y;
+        ld.vs[0] = v2.x; ld.vs[1] = v2.y;
       } else {
-        L2.ksw[u][0] = *reinterpret_cast<const uint32_t*>(kscl + (size_t)t * NG);
+        ld.ks[0] = *reinterpret_cast<const uint32_t*>(ks0 + (size_t)t * NG);
+        ld.vs[0] = *reinterpret_cast<const uint32_t*>(vs0 + (size_t)t * NG);
       }
-    }
+    };
+    const KeyConst kcon = key_const<KB>();
+    Loads nxt;
+    if (wave * kSub < n_tok) issue(nxt, wave * kSub);
+    for (int base = wave * kSub; base < n_tok; base += 4 * kSub) {
+      const Loads cur = nxt;
+      if (base + 4 * kSub < n_tok) issue(nxt, base + 4 * kSub);
+      const int t = base + lane;
+      const bool valid = t < n_tok;
+      // ---- QK^T ----
+      float s2[HQ4 * 4];
 #pragma unroll
-    for (int v = 0; v < UV; ++v) {
-      const int ta = min(base + v * 2 * PPW + tp, last), tb = min(base + v * 2 * PPW + tp + PPW, last);
-      L2.va[v] = load_vbytes<CB>(vbase + (size_t)ta * VROW);
-      L2.vb[v] = load_vbytes<CB>(vbase + (size_t)tb * VROW);
-      L2.sva[v] = h2f(vsb[(size_t)ta * NG]);
-      L2.svb[v] = h2f(vsb[(size_t)tb * NG]);
-    }
-  };
-  Loads nxt;
-  if (wave * SUB < n_tok) issue(nxt, wave * SUB);
-  for (int base = wave * SUB; base < n_tok; base += 4 * SUB) {
-    // ---- 1. take this sub-chunk's loads, start the next sub-chunk's ----
-    const Loads cur = nxt;
-    if (base + 4 * SUB < n_tok) issue(nxt, base + 4 * SUB);
-    const auto& kd = cur.kd;
-    const auto& ksw = cur.ksw;
-    const auto& va = cur.va;
-    const auto& vb = cur.vb;
-    const auto& sva = cur.sva;
-    const auto& svb = cur.svb;
-    // ---- 2. QK^T ----
+      for (int h = 0; h < HQ4 * 4; ++h) s2[h] = 0.f;
 #pragma unroll
-    for (int u = 0; u < TILES; ++u) {
-      const int t = base + 16 * u + n16;
-      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (!QBF) {
+      for (int gi = 0; gi < NG; ++gi) {
+        f32x4 d[HQ4];
 #pragma unroll
-        for (int gg = 0; gg < NG; ++gg) {
-          f16x8 bfrag;
-          if constexpr (KB == 4) bfrag = unpack8_int4(kd[u][gg], vmask4, vmagic);
-          else bfrag = unpack8_int2((Q & 1) ? (kd[u][gg] >> 16) : (kd[u][gg] & 0xFFFFu));
-          const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(afrag[gg], bfrag, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-          const uint32_t sw = ksw[u][gg >> 1];
-          const float scl = h2f((uint16_t)((gg & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
+        for (int hq = 0; hq < HQ4; ++hq) d[hq] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sacc[i] = fmaf(scl, d[i], sacc[i]);
+        for (int si = 0; si < 8; ++si) {
+          const int sidx = 8 * gi + si;
+          const f16x4 bop = key_operand<KB>(cur.k, sidx, kcon);
+#pragma unroll
+          for (int hq = 0; hq < HQ4; ++hq) {
+            const uint2 av = *reinterpret_cast<const uint2*>(qf32 + ((hq * NI + sidx) * 4 + (lane & 3)) * 2);
+            d[hq] = mfma4<4>(as_h4(av.x, av.y), bop, d[hq]);
+          }
         }
-      } else {
-        // bf16 query: exact fp32 products; lane (n16, Q) takes heads 4Q..4Q+3.
+        const uint32_t sw = cur.ks[gi >> 1];
+        const float scl = h2f((uint16_t)((gi & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int h = 4 * Q + i;
-          if (h < NREP) {
-            float acc = 0.f;
+        for (int hq = 0; hq < HQ4; ++hq)
 #pragma unroll
-            for (int gg = 0; gg < NG; ++gg) {
-              const uint32_t sw = ksw[u][gg >> 1];
-              const float scl = h2f((uint16_t)((gg & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
-              float part = 0.f;
-              // all 32 channels of the group: reload the codes of this token
-              const uint8_t* kr = krows + (size_t)(t < n_tok ? t : 0) * KROW + gg * (32 * KB / 8);
-              uint32_t w[KB];
+          for (int i = 0; i < 4; ++i) s2[4 * hq + i] = fmaf(scl, d[hq][i], s2[4 * hq + i]);
+      }
 #pragma unroll
-              for (int j = 0; j < KB; ++j) w[j] = reinterpret_cast<const uint32_t*>(kr)[j];
+      for (int h = 0; h < HQ4 * 4; ++h) {
+        s2[h] = valid ? s2[h] * kf[h] : -INFINITY;
+        if (h < NREP && rawb && valid) rawb[(size_t)h * a.cap_T + S + row0 + t] = s2[h];
+      }
+      // ---- softmax ----
+      float p[HQ4 * 4];
+      softmax_step(s2, p, valid);
+      // ---- weights p * v_scale and the transposed V tile into LDS ----
 #pragma unroll
-              for (int c = 0; c < 32; ++c) part = fmaf(q_lds[h * D + 32 * gg + c], code_at<KB>(w, c), part);
-              acc = fmaf(part, scl, acc);
-            }
-            sacc[i] = acc;
+      for (int gi = 0; gi < NG; ++gi) {
+        const uint32_t sw = cur.vs[gi >> 1];
+        const float sv = h2f((uint16_t)((gi & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
+#pragma unroll
+        for (int h = 0; h < HQ4 * 4; ++h)
+          pw[((h / 4 * NG + gi) * 4 + h % 4) * PW + lane] = f2h(p[h] * sv);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        vt[u * PW + lane] = (uint16_t)((u & 1) ? (cur.v[u >> 1] >> 16) : (cur.v[u >> 1] & 0xFFFFu));
+      wave_lds_sync();
+      // ---- PV ----
+#pragma unroll
+      for (int sg = 0; sg < NSIG; ++sg) {
+        const int gsel = 2 * sg + (lane >> 5);       // group of this lane's column block
+#pragma unroll
+        for (int t8 = 0; t8 < kSub / 8; ++t8) {
+          const uint4 x = *reinterpret_cast<const uint4*>(vt + vu[sg] * PW + 8 * t8);
+          const uint32_t y0 = h2_bits(as_h2(and_or(x.x >> vsh[sg], vmask[sg], 0x64006400u)) - vsub[sg]);
+          const uint32_t y1 = h2_bits(as_h2(and_or(x.y >> vsh[sg], vmask[sg], 0x64006400u)) - vsub[sg]);
+          const uint32_t y2 = h2_bits(as_h2(and_or(x.z >> vsh[sg], vmask[sg], 0x64006400u)) - vsub[sg]);
+          const uint32_t y3 = h2_bits(as_h2(and_or(x.w >> vsh[sg], vmask[sg], 0x64006400u)) - vsub[sg]);
+#pragma unroll
+          for (int hq = 0; hq < HQ4; ++hq) {
+            const uint4 av = *reinterpret_cast<const uint4*>(pw + ((hq * NG + gsel) * 4 + (lane & 3)) * PW + 8 * t8);
+            o[sg][hq] = mfma4<3>(as_h4(av.x, av.y), as_h4(y0, y1), o[sg][hq]);
+            o[sg][hq] = mfma4<3>(as_h4(av.z, av.w), as_h4(y2, y3), o[sg][hq]);
           }
         }
       }
-      if (t < n_tok) {
+      wave_lds_sync();
+    }
+#pragma unroll
+    for (int sg = 0; sg < NSIG; ++sg)
+#pragma unroll
+      for (int hq = 0; hq < HQ4; ++hq)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[sg][hq][i] *= vscale[sg];
+  } else {
+    // ---------------- FP16 tier: sinks then the recent ring ----------------
+    const int fp_slots = a.n_sink + a.ring;
+    const uint16_t* fk = a.fp_k + bg * fp_slots * D;
+    const uint16_t* fv = a.fp_v + bg * fp_slots * D;
+    auto slot_of = [&](int tt) { return tt < S ? tt : a.n_sink + (rhead + (tt - S)) % a.ring; };
+    for (int base = wave * kSub; base < n_tok; base += 4 * kSub) {
+      const int t = base + lane;
+      const bool valid = t < n_tok;
+      const int slot = slot_of(min(t, n_tok - 1));
+      const uint4* kp = reinterpret_cast<const uint4*>(fk + (size_t)slot * D);
+      f32x4 d[HQ4];
+#pragma unroll
+      for (int hq = 0; hq < HQ4; ++hq) d[hq] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        uint32_t w[16];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int h = 4 * Q + i;
-          if (h < NREP) {
-            const float s2 = sacc[i] * a.qk_scale;
-            sc[h * SUB + (t - base)] = s2;
-            if (rawb) raw_lds[h * a.chunk + t] = s2;
+          const uint4 x = kp[4 * gi + i];
+          w[4 * i] = x.x; w[4 * i + 1] = x.y; w[4 * i + 2] = x.z; w[4 * i + 3] = x.w;
+        }
+#pragma unroll
+        for (int si = 0; si < 8; ++si) {
+          const int sidx = 8 * gi + si;
+#pragma unroll
+          for (int hq = 0; hq < HQ4; ++hq) {
+            const uint2 av = *reinterpret_cast<const uint2*>(qf32 + ((hq * NI + sidx) * 4 + (lane & 3)) * 2);
+            d[hq] = mfma4<4>(as_h4(av.x, av.y), as_h4(w[2 * si], w[2 * si + 1]), d[hq]);
           }
         }
       }
-    }
-    wave_lds_sync();
-    // ---- 3. online softmax over the sub-chunk ----
-    const int nsub = min(SUB, n_tok - base);
+      float s2[HQ4 * 4];
+      const int pos = t < S ? t : S + M + (t - S);
 #pragma unroll
-    for (int h = 0; h < NREP; ++h) {
-      float mloc = -INFINITY;
-      for (int i = lane; i < nsub; i += kWave) mloc = fmaxf(mloc, sc[h * SUB + i]);
-      mloc = wave_max_u(mloc);
-      float ps = 0.f;
-      if (mloc > m_run[h]) {            // wave-uniform: rescale only when the max grows
-        const float alpha = m_run[h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[h] - mloc);
-        l_run[h] *= alpha;
-        wsum[h] *= alpha;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) o[h][c] *= alpha;
-        m_run[h] = mloc;
+      for (int h = 0; h < HQ4 * 4; ++h) {
+        s2[h] = valid ? d[h / 4][h % 4] * kf[h] : -INFINITY;
+        if (h < NREP && rawb && valid) rawb[(size_t)h * a.cap_T + pos] = s2[h];
       }
-      const float m_new = m_run[h];
-      for (int i = lane; i < SUB; i += kWave) {
-        const float p = i < nsub ? __builtin_amdgcn_exp2f(sc[h * SUB + i] - m_new) : 0.f;
-        sc[h * SUB + i] = p;
-        ps += p;
-      }
-      l_run[h] += wave_sum_u(ps);
-    }
-    wave_lds_sync();
-    // ---- 4. PV: token pairs (ta, tb), one dot2 per (head, channel). V codes
-    // are masked straight into fp16 subnormals (a b-bit field at bit j of a
-    // half reads as code * 2^(j - 24)); the power of two and the code offset
-    // are removed once per accumulator at the end. The weights p * v_scale
-    // are rounded to fp16 for the dot (as a fused attention's fp16
-    // probabilities are); the output tolerance is 2e-3.
+      float p[HQ4 * 4];
+      softmax_step(s2, p, valid);
 #pragma unroll
-    for (int v = 0; v < UV; ++v) {
-      const int ia = v * 2 * PPW + tp, ib = ia + PPW;   // offsets in the sub-chunk
-      f16x2 wp[NREP];
+      for (int h = 0; h < HQ4 * 4; ++h) pw[((h / 4 * NG) * 4 + h % 4) * PW + lane] = f2h(p[h]);
+      wave_lds_sync();
+      // PV: B = fp16 V of four tokens for the lane's channel, read from HBM.
+#pragma unroll 4
+      for (int t4 = 0; t4 < kSub / 4; ++t4) {
+        int sl[4];
 #pragma unroll
-      for (int h = 0; h < NREP; ++h) {
-        const f16 wa = (f16)(sc[h * SUB + ia] * sva[v]);
-        const f16 wb = (f16)(sc[h * SUB + ib] * svb[v]);
-        wp[h] = f16x2{wa, wb};
-        wsum[h] += (float)wa + (float)wb;
-      }
+        for (int k = 0; k < 4; ++k) sl[k] = slot_of(min(base + 4 * t4 + k, n_tok - 1));
 #pragma unroll
-      for (int byte = 0; byte < CB; ++byte) {
-        const int wi = byte / 4, bi = byte % 4;
-        const uint32_t sel = (uint32_t)bi | (0x0Cu << 8) | ((uint32_t)(4 + bi) << 16) | (0x0Cu << 24);
-        const uint32_t pr = __builtin_amdgcn_perm(vb[v].w[wi], va[v].w[wi], sel);   // [a.byte, 0, b.byte, 0]
+        for (int sg = 0; sg < NSIG; ++sg) {
+          const int c = 64 * sg + lane;
+          const uint32_t v0 = fv[(size_t)sl[0] * D + c], v1 = fv[(size_t)sl[1] * D + c];
+          const uint32_t v2 = fv[(size_t)sl[2] * D + c], v3 = fv[(size_t)sl[3] * D + c];
+          const f16x4 bop = as_h4(v0 | (v1 << 16), v2 | (v3 << 16));
 #pragma unroll
-        for (int k = 0; k < CPB; ++k) {
-          const uint32_t mask = (((1u << VB) - 1u) * 0x00010001u) << (VB * k);
-          const f16x2 v2 = as_h2(pr & mask);
-          const int c = byte * CPB + k;
-#pragma unroll
-          for (int h = 0; h < NREP; ++h) o[h][c] = fdot2(wp[h], v2, o[h][c]);
+          for (int hq = 0; hq < HQ4; ++hq) {
+            const uint2 av = *reinterpret_cast<const uint2*>(pw + ((hq * NG) * 4 + (lane & 3)) * PW + 4 * t4);
+            o[sg][hq] = mfma4<4>(as_h4(av.x, av.y), bop, o[sg][hq]);
+          }
         }
       }
+      wave_lds_sync();
     }
-    wave_lds_sync();
   }
 
-  // ---- finalize this wave: undo the code encoding, reduce over token lanes ----
+  // ---- merge the four waves into this split's partial ----
+  float* wacc = reinterpret_cast<float*>(wreg + wave * Lay::wave_bytes);   // [HQ4 * 4][D]
 #pragma unroll
-  for (int h = 0; h < NREP; ++h)
+  for (int h = 0; h < HQ4 * 4; ++h) {
+    const float lsum = wave_sum_u(l_lane[h]);
+    if (h < NREP) {
 #pragma unroll
-    for (int c = 0; c < CPL; ++c)
-      o[h][c] = o[h][c] * (float)(1 << (24 - VB * (c % CPB))) - (float)kOffV * wsum[h];
-  float* wa_ = wacc + wave * NREP * D;
-#pragma unroll
-  for (int h = 0; h < NREP; ++h)
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      float x = row_sum_strided<LPP>(o[h][c]);
-      x += __shfl_xor(x, 16);
-      x += __shfl_xor(x, 32);
-      o[h][c] = x;
-    }
-  if (lane < LPP) {
-#pragma unroll
-    for (int h = 0; h < NREP; ++h)
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) wa_[h * D + cb * CPL + c] = o[h][c];
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int h = 0; h < NREP; ++h) {
-      wml[wave * 2 * NREP + h] = m_run[h];
-      wml[wave * 2 * NREP + NREP + h] = l_run[h];
+      for (int sg = 0; sg < NSIG; ++sg) wacc[h * D + 64 * sg + lane] = o[sg][h / 4][h % 4];
+      if (lane == 0) {
+        wml[wave * 2 * HQ4 * 4 + h] = m_run[h];
+        wml[wave * 2 * HQ4 * 4 + HQ4 * 4 + h] = lsum;
+      }
     }
   }
   __syncthreads();
@@ -519,204 +501,17 @@ __global__ __launch_bounds__(kThreads) void k_decode_mid(DecodeArgs a) {
     const int h = i / (D + 2), c = i - h * (D + 2);
     float mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) mx = fmaxf(mx, wml[w * 2 * NREP + h]);
+    for (int w = 0; w < 4; ++w) mx = fmaxf(mx, wml[w * 2 * HQ4 * 4 + h]);
     float acc = 0.f, lsum = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float mw = wml[w * 2 * NREP + h];
+      const float mw = wml[w * 2 * HQ4 * 4 + h];
       if (mw == -INFINITY) continue;
       const float e = __builtin_amdgcn_exp2f(mw - mx);
-      lsum = fmaf(wml[w * 2 * NREP + NREP + h], e, lsum);
-      if (c < D) acc = fmaf(wacc[(w * NREP + h) * D + c], e, acc);
+      lsum = fmaf(wml[w * 2 * HQ4 * 4 + HQ4 * 4 + h], e, lsum);
+      if (c < D) acc = fmaf(reinterpret_cast<const float*>(wreg + w * Lay::wave_bytes)[h * D + c], e, acc);
     }
     part_base[h * part_hstride + c] = c < D ? acc : (c == D ? mx : lsum);
-  }
-  if (rawb) {
-    for (int i = tid; i < NREP * n_tok; i += kThreads) {
-      const int h = i / n_tok, t = i - h * n_tok;
-      rawb[(size_t)h * a.cap_T + S + row0 + t] = raw_lds[h * a.chunk + t];
-    }
-  }
-}
-
-// FP16 tier (sinks + recent ring): one workgroup per (KV head, sequence),
-// split 0 of the partials. At most n_sink + recent_window + 1 tokens, so a
-// plain two-phase pass: QK^T with fp32 products (query in LDS), exact max
-// and sum, then PV.
-template <int D, int NREP, bool QBF>
-__global__ __launch_bounds__(kThreads) void k_decode_fp16(DecodeArgs a) {
-  constexpr int LPT = D / 32, TPW = kWave / LPT;
-  constexpr int CPL = 16, LPT_V = D / CPL, TPW_V = kWave / LPT_V;
-  extern __shared__ float smem[];
-  float* q_lds = smem;                      // [NREP][D]
-  float* s_lds = q_lds + NREP * D;          // [NREP][lds_n]
-  float* acc_lds = s_lds + NREP * a.lds_n;  // [NREP][D]
-  float* red = acc_lds + NREP * D;          // [2][NREP]
-  const int g = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int Hq = a.Hkv * NREP;
-  const int32_t* L = a.lens + 4 * b;
-  const int S = min(max(L[0], 0), a.n_sink), M = min(max(L[1], 0), a.cap_mid);
-  const int R = min(max(L[2], 0), a.ring), head = min(max(L[3], 0), a.ring - 1);
-  const int n_tok = S + R;
-  float* part_base = a.part + ((size_t)(b * Hq + g * NREP) * a.nsplit) * (D + 2);
-  const size_t part_hstride = (size_t)a.nsplit * (D + 2);
-  if (n_tok <= 0) {
-    for (int i = tid; i < NREP * (D + 2); i += kThreads) {
-      const int h = i / (D + 2), c = i - h * (D + 2);
-      part_base[h * part_hstride + c] = (c == D) ? -INFINITY : 0.f;
-    }
-    return;
-  }
-  const uint16_t* qrow = a.q + (size_t)(b * Hq + g * NREP) * D;
-  for (int i = tid; i < NREP * D; i += kThreads) {
-    q_lds[i] = QBF ? bf2f(qrow[i]) : h2f(qrow[i]);
-    acc_lds[i] = 0.f;
-  }
-  __syncthreads();
-  const size_t bg = (size_t)(b * a.Hkv + g);
-  const int fp_slots = a.n_sink + a.ring;
-  const int grp = lane % LPT, tl = lane / LPT;
-  float* rawb = a.raw ? a.raw + (size_t)(b * Hq + g * NREP) * a.cap_T : nullptr;
-  constexpr int UK = 2;                       // QK tiles loaded together
-  for (int t0 = wave * TPW * UK; t0 < n_tok; t0 += 4 * TPW * UK) {
-   uint4 kraw[UK][4];
-#pragma unroll
-   for (int u = 0; u < UK; ++u) {
-     const int t = t0 + u * TPW + tl;
-     if (t < n_tok) {
-       const int slot = t < S ? t : a.n_sink + (head + (t - S)) % a.ring;
-       const uint4* kp = reinterpret_cast<const uint4*>(a.fp_k + (bg * fp_slots + slot) * D + grp * 32);
-#pragma unroll
-       for (int i = 0; i < 4; ++i) kraw[u][i] = kp[i];
-     }
-   }
-#pragma unroll
-   for (int u = 0; u < UK; ++u) {
-    const int t = t0 + u * TPW + tl;
-    float sh[NREP];
-#pragma unroll
-    for (int h = 0; h < NREP; ++h) sh[h] = 0.f;
-    int pos = 0;
-    if (t < n_tok) {
-      pos = t < S ? t : S + M + (t - S);
-      float kx[32];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t ws[4] = {kraw[u][i].x, kraw[u][i].y, kraw[u][i].z, kraw[u][i].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          kx[8 * i + 2 * j] = h2f((uint16_t)(ws[j] & 0xFFFFu));
-          kx[8 * i + 2 * j + 1] = h2f((uint16_t)(ws[j] >> 16));
-        }
-      }
-#pragma unroll
-      for (int h = 0; h < NREP; ++h) {
-        const float4* qv = reinterpret_cast<const float4*>(q_lds + h * D + grp * 32);
-        float acc = 0.f;
-#pragma unroll
-        for (int c4 = 0; c4 < 8; ++c4) {
-          const float4 qq = qv[c4];
-          acc = fmaf(qq.x, kx[4 * c4], acc);
-          acc = fmaf(qq.y, kx[4 * c4 + 1], acc);
-          acc = fmaf(qq.z, kx[4 * c4 + 2], acc);
-          acc = fmaf(qq.w, kx[4 * c4 + 3], acc);
-        }
-        sh[h] = acc;
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < NREP; ++h) lane_group_reduce<D>(sh[h]);
-    if (grp == 0 && t < n_tok) {
-#pragma unroll
-      for (int h = 0; h < NREP; ++h) {
-        const float s2 = sh[h] * a.qk_scale;
-        s_lds[h * a.lds_n + t] = s2;
-        if (rawb) rawb[(size_t)h * a.cap_T + pos] = s2;
-      }
-    }
-   }
-  }
-  __syncthreads();
-  for (int h = wave; h < NREP; h += 4) {
-    float m = -INFINITY;
-    for (int t = lane; t < n_tok; t += kWave) m = fmaxf(m, s_lds[h * a.lds_n + t]);
-    m = wave_max(m);
-    float sum = 0.f;
-    for (int t = lane; t < n_tok; t += kWave) {
-      const float p = __builtin_amdgcn_exp2f(s_lds[h * a.lds_n + t] - m);
-      s_lds[h * a.lds_n + t] = p;
-      sum += p;
-    }
-    sum = wave_sum(sum);
-    if (lane == 0) {
-      red[h] = m;
-      red[NREP + h] = sum;
-    }
-  }
-  __syncthreads();
-  const int cb = lane % LPT_V, tv = lane / LPT_V;
-  for (int h0 = 0; h0 < NREP; h0 += 4) {
-    float o[4][CPL];
-#pragma unroll
-    for (int h = 0; h < 4; ++h)
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) o[h][c] = 0.f;
-    constexpr int UVF = 3;                     // PV iterations loaded together
-    for (int t0 = wave * TPW_V * UVF; t0 < n_tok; t0 += 4 * TPW_V * UVF) {
-     uint4 vraw[UVF][CPL / 8];
-#pragma unroll
-     for (int u = 0; u < UVF; ++u) {
-       const int t = t0 + u * TPW_V + tv;
-       if (t < n_tok) {
-         const int slot = t < S ? t : a.n_sink + (head + (t - S)) % a.ring;
-         const uint4* vp = reinterpret_cast<const uint4*>(a.fp_v + (bg * fp_slots + slot) * D + cb * CPL);
-#pragma unroll
-         for (int i = 0; i < CPL / 8; ++i) vraw[u][i] = vp[i];
-       }
-     }
-#pragma unroll
-     for (int u = 0; u < UVF; ++u) {
-      const int t = t0 + u * TPW_V + tv;
-      if (t < n_tok) {
-        float vx[CPL];
-#pragma unroll
-        for (int i = 0; i < CPL / 8; ++i) {
-          const uint4 w = vraw[u][i];
-          const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            vx[8 * i + 2 * j] = h2f((uint16_t)(ws[j] & 0xFFFFu));
-            vx[8 * i + 2 * j + 1] = h2f((uint16_t)(ws[j] >> 16));
-          }
-        }
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          if (h0 + h < NREP) {
-            const float p = s_lds[(h0 + h) * a.lds_n + t];
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) o[h][c] = fmaf(p, vx[c], o[h][c]);
-          }
-        }
-      }
-     }
-    }
-#pragma unroll
-    for (int h = 0; h < 4; ++h)
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) o[h][c] = row_sum_strided<LPT_V>(o[h][c]);
-    if ((lane & 15) < LPT_V) {
-#pragma unroll
-      for (int h = 0; h < 4; ++h)
-        if (h0 + h < NREP)
-#pragma unroll
-          for (int c = 0; c < CPL; ++c) atomicAdd(&acc_lds[(h0 + h) * D + cb * CPL + c], o[h][c]);
-    }
-  }
-  __syncthreads();
-  for (int i = tid; i < NREP * (D + 2); i += kThreads) {
-    const int h = i / (D + 2), c = i - h * (D + 2);
-    part_base[h * part_hstride + c] = c < D ? acc_lds[h * D + c] : (c == D ? red[h] : red[NREP + h]);
   }
 }
 
@@ -769,38 +564,26 @@ __global__ __launch_bounds__(256) void k_side_output(const float* __restrict__ r
 }
 
 template <int D, int NREP, int KB, int VB, bool QBF>
-static void launch_mid(const DecodeArgs& a, dim3 grid, size_t lds, hipStream_t st) {
-  hipLaunchKernelGGL((k_decode_mid<D, NREP, KB, VB, QBF>), grid, dim3(kThreads), lds, st, a);
+static void launch_tiers(const DecodeArgs& a, dim3 grid, hipStream_t st) {
+  const size_t lds = (size_t)TierLayout<D, NREP, KB, VB>::total;
+  hipLaunchKernelGGL((k_decode_tiers<D, NREP, KB, VB, QBF>), grid, dim3(kThreads), lds, st, a);
 }
 
 template <int D, int NREP, bool QBF>
-static void dispatch_bits(int kb, int vb, const DecodeArgs& a, dim3 grid, size_t lds, hipStream_t st) {
-  if (kb == 4 && vb == 4) launch_mid<D, NREP, 4, 4, QBF>(a, grid, lds, st);
-  else if (kb == 4 && vb == 2) launch_mid<D, NREP, 4, 2, QBF>(a, grid, lds, st);
-  else if (kb == 2 && vb == 4) launch_mid<D, NREP, 2, 4, QBF>(a, grid, lds, st);
-  else launch_mid<D, NREP, 2, 2, QBF>(a, grid, lds, st);
+static void dispatch_bits(int kb, int vb, const DecodeArgs& a, dim3 grid, hipStream_t st) {
+  if (kb == 4 && vb == 4) launch_tiers<D, NREP, 4, 4, QBF>(a, grid, st);
+  else if (kb == 4 && vb == 2) launch_tiers<D, NREP, 4, 2, QBF>(a, grid, st);
+  else if (kb == 2 && vb == 4) launch_tiers<D, NREP, 2, 4, QBF>(a, grid, st);
+  else launch_tiers<D, NREP, 2, 2, QBF>(a, grid, st);
 }
 
 template <int D, bool QBF>
-static void dispatch_rep(int n_rep, int kb, int vb, const DecodeArgs& a, dim3 grid_mid, size_t lds_mid,
-                         dim3 grid_fp, size_t lds_fp, hipStream_t st) {
+static void dispatch_rep(int n_rep, int kb, int vb, const DecodeArgs& a, dim3 grid, hipStream_t st) {
   switch (n_rep) {
-    case 1:
-      hipLaunchKernelGGL((k_decode_fp16<D, 1, QBF>), grid_fp, dim3(kThreads), lds_fp, st, a);
-      if (grid_mid.x) dispatch_bits<D, 1, QBF>(kb, vb, a, grid_mid, lds_mid, st);
-      break;
-    case 2:
-      hipLaunchKernelGGL((k_decode_fp16<D, 2, QBF>), grid_fp, dim3(kThreads), lds_fp, st, a);
-      if (grid_mid.x) dispatch_bits<D, 2, QBF>(kb, vb, a, grid_mid, lds_mid, st);
-      break;
-    case 4:
-      hipLaunchKernelGGL((k_decode_fp16<D, 4, QBF>), grid_fp, dim3(kThreads), lds_fp, st, a);
-      if (grid_mid.x) dispatch_bits<D, 4, QBF>(kb, vb, a, grid_mid, lds_mid, st);
-      break;
-    default:
-      hipLaunchKernelGGL((k_decode_fp16<D, 8, QBF>), grid_fp, dim3(kThreads), lds_fp, st, a);
-      if (grid_mid.x) dispatch_bits<D, 8, QBF>(kb, vb, a, grid_mid, lds_mid, st);
-      break;
+    case 1: dispatch_bits<D, 1, QBF>(kb, vb, a, grid, st); break;
+    case 2: dispatch_bits<D, 2, QBF>(kb, vb, a, grid, st); break;
+    case 4: dispatch_bits<D, 4, QBF>(kb, vb, a, grid, st); break;
+    default: dispatch_bits<D, 8, QBF>(kb, vb, a, grid, st); break;
   }
 }
 
@@ -833,18 +616,14 @@ hipError_t launch_decode(const Shape& s, const fade_layer_cache& c, const void* 
   a.cap_T = s.cap_T;
   a.chunk = chunk;
   a.nsplit = nsplit;
-  a.lds_n = s.n_sink + s.ring;
   a.qk_scale = kLog2e / sqrtf((float)s.D);
-  const size_t nr = (size_t)s.n_rep;
-  const size_t lds_mid = (nr * s.D + 4 * nr * 64 + 4 * nr * s.D + 8 * nr + (tok_attn ? nr * chunk : 0)) * 4;
-  const size_t lds_fp = (nr * s.D + nr * a.lds_n + nr * s.D + 2 * nr) * 4;
-  const dim3 grid_mid(nsplit - 1, s.Hkv, s.batch), grid_fp(1, s.Hkv, s.batch);
+  const dim3 grid(nsplit, s.Hkv, s.batch);
   if (s.D == 128) {
-    if (q_bf16) dispatch_rep<128, true>(s.n_rep, s.kb, s.vb, a, grid_mid, lds_mid, grid_fp, lds_fp, st);
-    else dispatch_rep<128, false>(s.n_rep, s.kb, s.vb, a, grid_mid, lds_mid, grid_fp, lds_fp, st);
+    if (q_bf16) dispatch_rep<128, true>(s.n_rep, s.kb, s.vb, a, grid, st);
+    else dispatch_rep<128, false>(s.n_rep, s.kb, s.vb, a, grid, st);
   } else {
-    if (q_bf16) dispatch_rep<64, true>(s.n_rep, s.kb, s.vb, a, grid_mid, lds_mid, grid_fp, lds_fp, st);
-    else dispatch_rep<64, false>(s.n_rep, s.kb, s.vb, a, grid_mid, lds_mid, grid_fp, lds_fp, st);
+    if (q_bf16) dispatch_rep<64, true>(s.n_rep, s.kb, s.vb, a, grid, st);
+    else dispatch_rep<64, false>(s.n_rep, s.kb, s.vb, a, grid, st);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
