@@ -27,8 +27,9 @@
 //           group), B = the signed codes of those tokens for the lane's
 //           channel, read from a per-wave LDS tile of V transposed to
 //           [16-bit unit][token] and decoded with the fp16 bias trick.
-//   k_decode_combine  log-sum-exp merge of the splits per (sequence, q head).
-//   k_side_output     a_j = sum_h 2^(s_hj - M_h) / L_h per slot position.
+//   k_decode_finish   per sequence: log-sum-exp merge of the splits for every
+//                     query head and the side output
+//                     a_j = sum_h 2^(s_hj - M_h) / L_h per slot position.
 // Roofline: HBM. Algorithmic bytes per launch = live tier bytes + q + out
 // (+ the side output when requested).
 #include "fade_common.hpp"
@@ -72,7 +73,6 @@ int decode_nsplit(const Shape& s) {
 size_t decode_ws_bytes(const Shape& s) {
   size_t n = align_up((size_t)s.batch * s.Hq * decode_nsplit(s) * (s.D + 2) * 4, 256);
   n += align_up((size_t)s.batch * s.Hq * s.cap_T * 4, 256);   // raw scores
-  n += align_up((size_t)s.batch * s.Hq * 2 * 4, 256);         // per-head (M, L)
   return n;
 }
 
@@ -168,6 +168,7 @@ struct TierLayout {
   static constexpr int wacc_bytes = HQ4 * 4 * D * 4;              // per-wave output [head][D]
   static constexpr int wave_bytes = ((pw_bytes + vt_bytes > wacc_bytes ? pw_bytes + vt_bytes : wacc_bytes) + 15) / 16 * 16;
   static constexpr int total = head_bytes + 4 * wave_bytes;
+  static_assert(16 * HQ4 * 4 * 4 <= pw_bytes, "fp16-tier weights fit the weight tile");
 };
 
 template <int D, int NREP, int KB, int VB, bool QBF>
@@ -417,34 +418,34 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
         for (int i = 0; i < 4; ++i) o[sg][hq][i] *= vscale[sg];
   } else {
     // ---------------- FP16 tier: sinks then the recent ring ----------------
+    // 16-token slices, one per wave at a time (the tier holds at most
+    // n_sink + recent_window + 1 tokens): QK^T on the MFMA with lanes 16..63
+    // repeating lanes 0..15, PV on VALU with one lane per CPL channels.
+    constexpr int CPL = D / 64;
     const int fp_slots = a.n_sink + a.ring;
     const uint16_t* fk = a.fp_k + bg * fp_slots * D;
     const uint16_t* fv = a.fp_v + bg * fp_slots * D;
+    float* pf = reinterpret_cast<float*>(pw);               // [16 tokens][HQ4 * 4] weights
     auto slot_of = [&](int tt) { return tt < S ? tt : a.n_sink + (rhead + (tt - S)) % a.ring; };
-    for (int base = wave * kSub; base < n_tok; base += 4 * kSub) {
-      const int t = base + lane;
-      const bool valid = t < n_tok;
-      const int slot = slot_of(min(t, n_tok - 1));
-      const uint4* kp = reinterpret_cast<const uint4*>(fk + (size_t)slot * D);
+    for (int base = wave * 16; base < n_tok; base += 64) {
+      const int t = base + (lane & 15);
+      const bool valid = lane < 16 && t < n_tok;
+      const uint4* kp = reinterpret_cast<const uint4*>(fk + (size_t)slot_of(min(t, n_tok - 1)) * D);
+      uint32_t w[D / 2];
+#pragma unroll
+      for (int i = 0; i < D / 8; ++i) {
+        const uint4 x = kp[i];
+        w[4 * i] = x.x; w[4 * i + 1] = x.y; w[4 * i + 2] = x.z; w[4 * i + 3] = x.w;
+      }
       f32x4 d[HQ4];
 #pragma unroll
       for (int hq = 0; hq < HQ4; ++hq) d[hq] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int gi = 0; gi < NG; ++gi) {
-        uint32_t w[16];
+      for (int sidx = 0; sidx < NI; ++sidx) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint4 x = kp[4 * gi + i];
-          w[4 * i] = x.x; w[4 * i + 1] = x.y; w[4 * i + 2] = x.z; w[4 * i + 3] = x.w;
-        }
-#pragma unroll
-        for (int si = 0; si < 8; ++si) {
-          const int sidx = 8 * gi + si;
-#pragma unroll
-          for (int hq = 0; hq < HQ4; ++hq) {
-            const uint2 av = *reinterpret_cast<const uint2*>(qf32 + ((hq * NI + sidx) * 4 + (lane & 3)) * 2);
-            d[hq] = mfma4<4>(as_h4(av.x, av.y), as_h4(w[2 * si], w[2 * si + 1]), d[hq]);
-          }
+        for (int hq = 0; hq < HQ4; ++hq) {
+          const uint2 av = *reinterpret_cast<const uint2*>(qf32 + ((hq * NI + sidx) * 4 + (lane & 3)) * 2);
+          d[hq] = mfma4<4>(as_h4(av.x, av.y), as_h4(w[2 * sidx], w[2 * sidx + 1]), d[hq]);
         }
       }
       float s2[HQ4 * 4];
@@ -456,25 +457,33 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
       }
       float p[HQ4 * 4];
       softmax_step(s2, p, valid);
+      if (lane < 16) {
 #pragma unroll
-      for (int h = 0; h < HQ4 * 4; ++h) pw[((h / 4 * NG) * 4 + h % 4) * PW + lane] = f2h(p[h]);
+        for (int h = 0; h < HQ4 * 4; ++h) pf[lane * HQ4 * 4 + h] = p[h];
+      }
       wave_lds_sync();
-      // PV: B = fp16 V of four tokens for the lane's channel, read from HBM.
-#pragma unroll 4
-      for (int t4 = 0; t4 < kSub / 4; ++t4) {
-        int sl[4];
+      const int nt = min(16, n_tok - base);              // wave-uniform
+      uint32_t vv[16];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) sl[k] = slot_of(min(base + 4 * t4 + k, n_tok - 1));
+      for (int k = 0; k < 16; ++k) {
+        const uint16_t* vr = fv + (size_t)slot_of(base + min(k, nt - 1)) * D;
+        if constexpr (CPL == 2) vv[k] = *reinterpret_cast<const uint32_t*>(vr + 2 * lane);
+        else vv[k] = vr[lane];
+      }
 #pragma unroll
-        for (int sg = 0; sg < NSIG; ++sg) {
-          const int c = 64 * sg + lane;
-          const uint32_t v0 = fv[(size_t)sl[0] * D + c], v1 = fv[(size_t)sl[1] * D + c];
-          const uint32_t v2 = fv[(size_t)sl[2] * D + c], v3 = fv[(size_t)sl[3] * D + c];
-          const f16x4 bop = as_h4(v0 | (v1 << 16), v2 | (v3 << 16));
+      for (int k = 0; k < 16; ++k) {
+        if (k < nt) {
+          const float v0 = h2f((uint16_t)(vv[k] & 0xFFFFu)), v1 = h2f((uint16_t)(vv[k] >> 16));
 #pragma unroll
           for (int hq = 0; hq < HQ4; ++hq) {
-            const uint2 av = *reinterpret_cast<const uint2*>(pw + ((hq * NG) * 4 + (lane & 3)) * PW + 4 * t4);
-            o[sg][hq] = mfma4<4>(as_h4(av.x, av.y), bop, o[sg][hq]);
+            const float4 pq = *reinterpret_cast<const float4*>(pf + k * HQ4 * 4 + 4 * hq);
+            const float pp[4] = {pq.x, pq.y, pq.z, pq.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              // o[0] holds channel CPL * lane, o[1] (D = 128) channel CPL * lane + 1
+              o[0][hq][i] = fmaf(pp[i], v0, o[0][hq][i]);
+              if constexpr (CPL == 2) o[NSIG - 1][hq][i] = fmaf(pp[i], v1, o[NSIG - 1][hq][i]);
+            }
           }
         }
       }
@@ -489,7 +498,8 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
     const float lsum = wave_sum_u(l_lane[h]);
     if (h < NREP) {
 #pragma unroll
-      for (int sg = 0; sg < NSIG; ++sg) wacc[h * D + 64 * sg + lane] = o[sg][h / 4][h % 4];
+      for (int sg = 0; sg < NSIG; ++sg)
+        wacc[h * D + (fpt ? NSIG * lane + sg : 64 * sg + lane)] = o[sg][h / 4][h % 4];
       if (lane == 0) {
         wml[wave * 2 * HQ4 * 4 + h] = m_run[h];
         wml[wave * 2 * HQ4 * 4 + HQ4 * 4 + h] = lsum;
@@ -515,52 +525,100 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
   }
 }
 
-// One workgroup of D threads per (sequence, query head).
-template <int D>
-__global__ __launch_bounds__(128) void k_decode_combine(const float* __restrict__ part, int nsplit,
-                                                        void* out, int out_dtype,
-                                                        float* __restrict__ mstat) {
-  const int bh = blockIdx.x;
-  const int c = threadIdx.x;
-  const float* p = part + (size_t)bh * nsplit * (D + 2);
-  float m = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) m = fmaxf(m, p[s * (D + 2) + D]);
-  float l = 0.f, o = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float ms = p[s * (D + 2) + D];
-    if (ms == -INFINITY) continue;
-    const float w = __builtin_amdgcn_exp2f(ms - m);
-    l = fmaf(p[s * (D + 2) + D + 1], w, l);
-    o = fmaf(p[s * (D + 2) + c], w, o);
-  }
-  o = o / l;
-  const size_t oi = (size_t)bh * D + c;
-  if (out_dtype == FADE_DTYPE_F32) reinterpret_cast<float*>(out)[oi] = o;
-  else if (out_dtype == FADE_DTYPE_BF16) reinterpret_cast<uint16_t*>(out)[oi] = f2bf(o);
-  else reinterpret_cast<uint16_t*>(out)[oi] = f2h(o);
-  if (c == 0 && mstat) {
-    mstat[2 * bh] = m;
-    mstat[2 * bh + 1] = l;
-  }
-}
+// Finish of one sequence, spread over the workgroups blockIdx.y of its row:
+// each rebuilds the per-head softmax statistics (M_h, 1 / L_h) of all query
+// heads from the split partials, writes its share of the log-sum-exp merged
+// output, and, when requested, the side output a_j = sum_h 2^(s_hj - M_h) / L_h
+// of its 64 slots (four lane groups of 64 each sum a quarter of the heads).
+constexpr int kFinishSlots = 64;
 
-__global__ __launch_bounds__(256) void k_side_output(const float* __restrict__ raw,
-                                                     const float* __restrict__ mstat,
-                                                     const int32_t* __restrict__ lens, int Hq,
-                                                     int cap_T, float* __restrict__ tok_attn) {
-  extern __shared__ float ml[];   // [Hq][2]
-  const int b = blockIdx.y;
-  for (int i = threadIdx.x; i < 2 * Hq; i += blockDim.x) ml[i] = mstat[(size_t)b * Hq * 2 + i];
-  __syncthreads();
-  const int j = blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= cap_T) return;
-  const int T = lens[4 * b] + lens[4 * b + 1] + lens[4 * b + 2];
-  float a = 0.f;
-  if (j < T) {
-    for (int h = 0; h < Hq; ++h)
-      a += __builtin_amdgcn_exp2f(raw[((size_t)b * Hq + h) * cap_T + j] - ml[2 * h]) / ml[2 * h + 1];
+template <int D>
+__global__ __launch_bounds__(256) void k_decode_finish(const float* __restrict__ part, int nsplit, int Hq,
+                                                       void* out, int out_dtype,
+                                                       const float* __restrict__ raw,
+                                                       const int32_t* __restrict__ lens, int cap_T,
+                                                       float* __restrict__ tok_attn) {
+  constexpr int kB = 8;           // loads in flight per thread
+  extern __shared__ float ml[];   // [Hq][2] = (M_h, 1 / L_h), then [4][kFinishSlots] partial sums
+  const int b = blockIdx.x, j = blockIdx.y, nb = gridDim.y, tid = threadIdx.x;
+  const float* pb = part + (size_t)b * Hq * nsplit * (D + 2);
+  for (int h = tid; h < Hq; h += blockDim.x) {
+    const float* ph = pb + (size_t)h * nsplit * (D + 2) + D;
+    float m = -INFINITY, l = 0.f;
+    for (int s0 = 0; s0 < nsplit; s0 += kB) {
+      float ms[kB], ls[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const bool in = s0 + u < nsplit;
+        ms[u] = in ? ph[(s0 + u) * (D + 2)] : -INFINITY;
+        ls[u] = in ? ph[(s0 + u) * (D + 2) + 1] : 0.f;
+      }
+      float mb = m;
+#pragma unroll
+      for (int u = 0; u < kB; ++u) mb = fmaxf(mb, ms[u]);
+      l = m == -INFINITY ? 0.f : l * __builtin_amdgcn_exp2f(m - mb);
+#pragma unroll
+      for (int u = 0; u < kB; ++u)
+        if (ms[u] != -INFINITY) l = fmaf(ls[u], __builtin_amdgcn_exp2f(ms[u] - mb), l);
+      m = mb;
+    }
+    ml[2 * h] = m;
+    ml[2 * h + 1] = 1.f / l;
   }
-  tok_attn[(size_t)b * cap_T + j] = a;
+  __syncthreads();
+  const int n_out = Hq * D;
+  const int e0 = (int)((long)j * n_out / nb), e1 = (int)((long)(j + 1) * n_out / nb);
+  for (int i = e0 + tid; i < e1; i += blockDim.x) {
+    const int h = i / D, c = i % D;
+    const float* ph = pb + (size_t)h * nsplit * (D + 2);
+    const float m = ml[2 * h];
+    float o = 0.f;
+    for (int s0 = 0; s0 < nsplit; s0 += kB) {
+      float ms[kB], vs[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const bool in = s0 + u < nsplit;
+        ms[u] = in ? ph[(s0 + u) * (D + 2) + D] : -INFINITY;
+        vs[u] = in ? ph[(s0 + u) * (D + 2) + c] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kB; ++u)
+        if (ms[u] != -INFINITY) o = fmaf(vs[u], __builtin_amdgcn_exp2f(ms[u] - m), o);
+    }
+    o *= ml[2 * h + 1];
+    const size_t oi = (size_t)b * n_out + i;
+    if (out_dtype == FADE_DTYPE_F32) reinterpret_cast<float*>(out)[oi] = o;
+    else if (out_dtype == FADE_DTYPE_BF16) reinterpret_cast<uint16_t*>(out)[oi] = f2bf(o);
+    else reinterpret_cast<uint16_t*>(out)[oi] = f2h(o);
+  }
+  if (!tok_attn) return;
+  const int T = lens[4 * b] + lens[4 * b + 1] + lens[4 * b + 2];
+  float* red = ml + 2 * Hq;
+  for (int j0 = j * kFinishSlots; j0 < cap_T; j0 += nb * kFinishSlots) {
+    const int u0 = tid % kFinishSlots, jj = j0 + u0, hg = tid / kFinishSlots;
+    float acc = 0.f;
+    if (jj < T && jj < cap_T) {
+      for (int h0 = hg; h0 < Hq; h0 += 4 * kB) {
+        float rv[kB];
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+          const int h = h0 + 4 * u;
+          rv[u] = h < Hq ? raw[((size_t)b * Hq + h) * cap_T + jj] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+          const int h = h0 + 4 * u;
+          if (h < Hq) acc += __builtin_amdgcn_exp2f(rv[u] - ml[2 * h]) * ml[2 * h + 1];
+        }
+      }
+    }
+    red[hg * kFinishSlots + u0] = acc;
+    __syncthreads();
+    if (hg == 0 && jj < cap_T)
+      tok_attn[(size_t)b * cap_T + jj] = ((red[u0] + red[kFinishSlots + u0]) + red[2 * kFinishSlots + u0]) +
+                                         red[3 * kFinishSlots + u0];
+    __syncthreads();
+  }
 }
 
 template <int D, int NREP, int KB, int VB, bool QBF>
@@ -595,8 +653,6 @@ hipError_t launch_decode(const Shape& s, const fade_layer_cache& c, const void* 
   float* part = reinterpret_cast<float*>(w);
   w += align_up((size_t)s.batch * s.Hq * nsplit * (s.D + 2) * 4, 256);
   float* raw = reinterpret_cast<float*>(w);
-  w += align_up((size_t)s.batch * s.Hq * s.cap_T * 4, 256);
-  float* mstat = reinterpret_cast<float*>(w);
 
   DecodeArgs a;
   a.fp_k = reinterpret_cast<const uint16_t*>(c.fp_k);
@@ -627,17 +683,14 @@ hipError_t launch_decode(const Shape& s, const fade_layer_cache& c, const void* 
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  float* ms = tok_attn ? mstat : nullptr;
+  const dim3 fgrid(s.batch, (s.cap_T + kFinishSlots - 1) / kFinishSlots);
+  const size_t flds = ((size_t)2 * s.Hq + 4 * kFinishSlots) * 4;
   if (s.D == 128)
-    hipLaunchKernelGGL(k_decode_combine<128>, dim3(s.batch * s.Hq), dim3(128), 0, st, part, nsplit,
-                       out, out_dtype, ms);
+    hipLaunchKernelGGL(k_decode_finish<128>, fgrid, dim3(256), flds, st, part, nsplit, s.Hq, out, out_dtype,
+                       raw, c.lens, s.cap_T, tok_attn);
   else
-    hipLaunchKernelGGL(k_decode_combine<64>, dim3(s.batch * s.Hq), dim3(64), 0, st, part, nsplit,
-                       out, out_dtype, ms);
-  e = hipGetLastError();
-  if (e != hipSuccess || !tok_attn) return e;
-  hipLaunchKernelGGL(k_side_output, dim3((s.cap_T + 255) / 256, s.batch), dim3(256),
-                     (size_t)2 * s.Hq * 4, st, raw, mstat, c.lens, s.Hq, s.cap_T, tok_attn);
+    hipLaunchKernelGGL(k_decode_finish<64>, fgrid, dim3(256), flds, st, part, nsplit, s.Hq, out, out_dtype,
+                       raw, c.lens, s.cap_T, tok_attn);
   return hipGetLastError();
 }
 
