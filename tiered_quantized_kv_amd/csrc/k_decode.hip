@@ -56,13 +56,14 @@ constexpr int kThreads = 256;
 constexpr int kSub = 64;          // tokens per wave sub-chunk (one per lane)
 
 int decode_chunk(const Shape& s) {
-  // Middle rows per split: enough workgroups to cover 256 CUs several times,
-  // but each split large enough that its partial (n_rep * (D + 2) floats) is
-  // a small fraction of the bytes it streams.
-  const int pairs = s.batch * s.Hkv;
-  const int unit = 4 * kSub;                        // four waves x one sub-chunk
-  int chunk = 2 * unit;
-  while (chunk > unit && (long)pairs * ((s.cap_mid + chunk - 1) / chunk) < 2048) chunk /= 2;
+  // Middle rows per split: the largest power-of-two multiple of four waves x
+  // one sub-chunk (up to 4096) that still gives about 1024 middle
+  // workgroups, so each wave streams several sub-chunks with its loads
+  // prefetched, and the grid still covers the chip.
+  const long pairs = (long)s.batch * s.Hkv;
+  const int unit = 4 * kSub;
+  int chunk = 16 * unit;
+  while (chunk > unit && pairs * ((s.cap_mid + chunk - 1) / chunk) < 1024) chunk /= 2;
   return chunk;
 }
 
@@ -208,6 +209,46 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
     return;
   }
 
+  // The first sub-chunk's loads of a middle split go out before the query
+  // set-up so that their latency overlaps it.
+  const size_t bg = (size_t)(b * a.Hkv + g);
+  const uint8_t* krow0 = a.kc + (bg * a.cap_mid + row0) * KROW;
+  const uint16_t* ks0 = a.ks + (bg * a.cap_mid + row0) * NG;
+  const uint8_t* vrow0 = a.vc + (bg * a.cap_mid + row0) * VROW;
+  const uint16_t* vs0 = a.vs + (bg * a.cap_mid + row0) * NG;
+  struct Loads {
+    uint32_t k[KW];
+    uint32_t v[VW];
+    uint32_t ks[NG / 2];
+    uint32_t vs[NG / 2];
+  };
+  auto issue = [&](Loads& ld, int base) {
+    const int t = min(base + lane, n_tok - 1);
+    const uint4* kp = reinterpret_cast<const uint4*>(krow0 + (size_t)t * KROW);
+#pragma unroll
+    for (int i = 0; i < KW / 4; ++i) {
+      const uint4 w = kp[i];
+      ld.k[4 * i] = w.x; ld.k[4 * i + 1] = w.y; ld.k[4 * i + 2] = w.z; ld.k[4 * i + 3] = w.w;
+    }
+    const uint4* vp = reinterpret_cast<const uint4*>(vrow0 + (size_t)t * VROW);
+#pragma unroll
+    for (int i = 0; i < VW / 4; ++i) {
+      const uint4 w = vp[i];
+      ld.v[4 * i] = w.x; ld.v[4 * i + 1] = w.y; ld.v[4 * i + 2] = w.z; ld.v[4 * i + 3] = w.w;
+    }
+    if constexpr (NG == 4) {
+      const uint2 k2 = *reinterpret_cast<const uint2*>(ks0 + (size_t)t * NG);
+      const uint2 v2 = *reinterpret_cast<const uint2*>(vs0 + (size_t)t * NG);
+      ld.ks[0] = k2.x; ld.ks[1] = k2.y;
+      ld.vs[0] = v2.x; ld.vs[1] = v2.y;
+    } else {
+      ld.ks[0] = *reinterpret_cast<const uint32_t*>(ks0 + (size_t)t * NG);
+      ld.vs[0] = *reinterpret_cast<const uint32_t*>(vs0 + (size_t)t * NG);
+    }
+  };
+  Loads nxt;
+  if (!fpt && wave * kSub < n_tok) issue(nxt, wave * kSub);
+
   // ---- query fragments ----
   const uint16_t* qrow = a.q + (size_t)(b * Hq + g * NREP) * D;   // NREP consecutive heads
   uint32_t* qexp = reinterpret_cast<uint32_t*>(wml);              // scratch: per-head max |q| bits
@@ -243,7 +284,6 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
   }
   __syncthreads();
 
-  const size_t bg = (size_t)(b * a.Hkv + g);
   float* rawb = a.raw ? a.raw + (size_t)(b * Hq + g * NREP) * a.cap_T : nullptr;
   uint16_t* pw = reinterpret_cast<uint16_t*>(wreg + wave * Lay::wave_bytes);   // [HQ4][NG][4][PW]
   uint16_t* vt = pw + Lay::pw_bytes / 2;                                       // [U][PW]
@@ -282,10 +322,6 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
 
   if (!fpt) {
     // ---------------- packed middle tier ----------------
-    const uint8_t* krow0 = a.kc + (bg * a.cap_mid + row0) * KROW;
-    const uint16_t* ks0 = a.ks + (bg * a.cap_mid + row0) * NG;
-    const uint8_t* vrow0 = a.vc + (bg * a.cap_mid + row0) * VROW;
-    const uint16_t* vs0 = a.vs + (bg * a.cap_mid + row0) * NG;
     // PV lane constants: channel 64 sg + lane, its 16-bit unit and field.
     int vu[NSIG];
     uint32_t vsh[NSIG], vmask[NSIG];
@@ -304,39 +340,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
       vsub[sg] = f16x2{sub, sub};
       vscale[sg] = ldexpf(1.f, -pos);
     }
-    struct Loads {
-      uint32_t k[KW];
-      uint32_t v[VW];
-      uint32_t ks[NG / 2];
-      uint32_t vs[NG / 2];
-    };
-    auto issue = [&](Loads& ld, int base) {
-      const int t = min(base + lane, n_tok - 1);
-      const uint4* kp = reinterpret_cast<const uint4*>(krow0 + (size_t)t * KROW);
-#pragma unroll
-      for (int i = 0; i < KW / 4; ++i) {
-        const uint4 w = kp[i];
-        ld.k[4 * i] = w.x; ld.k[4 * i + 1] = w.y; ld.k[4 * i + 2] = w.z; ld.k[4 * i + 3] = w.w;
-      }
-      const uint4* vp = reinterpret_cast<const uint4*>(vrow0 + (size_t)t * VROW);
-#pragma unroll
-      for (int i = 0; i < VW / 4; ++i) {
-        const uint4 w = vp[i];
-        ld.v[4 * i] = w.x; ld.v[4 * i + 1] = w.y; ld.v[4 * i + 2] = w.z; ld.v[4 * i + 3] = w.w;
-      }
-      if constexpr (NG == 4) {
-        const uint2 k2 = *reinterpret_cast<const uint2*>(ks0 + (size_t)t * NG);
-        const uint2 v2 = *reinterpret_cast<const uint2*>(vs0 + (size_t)t * NG);
-        ld.ks[0] = k2.x; ld.ks[1] = k2.y;
-        ld.vs[0] = v2.x; ld.vs[1] = v2.y;
-      } else {
-        ld.ks[0] = *reinterpret_cast<const uint32_t*>(ks0 + (size_t)t * NG);
-        ld.vs[0] = *reinterpret_cast<const uint32_t*>(vs0 + (size_t)t * NG);
-      }
-    };
     const KeyConst kcon = key_const<KB>();
-    Loads nxt;
-    if (wave * kSub < n_tok) issue(nxt, wave * kSub);
     for (int base = wave * kSub; base < n_tok; base += 4 * kSub) {
       const Loads cur = nxt;
       if (base + 4 * kSub < n_tok) issue(nxt, base + 4 * kSub);
