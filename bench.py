@@ -227,6 +227,29 @@ class Workload:
                                      L=qa.shape[2], shared=0, scores_out=self.admit_scores, ws=self.ws_h2o)
 
 
+def measured_traffic(name):
+    """HBM bytes per decode-attention call from the committed counter summary
+    of this workload (FETCH_SIZE and WRITE_SIZE passes, copy-calibrated), or
+    None when there is none or the kernel sources changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"decode_attn_{name}_hbm.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            k, sep, v = line.partition(":")
+            if sep and k.strip() in ("traffic_bytes_per_call", "sources", "source_sha256"):
+                fields[k.strip()] = v.strip()
+    if len(fields) != 3:
+        return None
+    h = hashlib.sha256()
+    for src in fields["sources"].split():
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    return int(fields["traffic_bytes_per_call"]) if h.hexdigest() == fields["source_sha256"] else None
+
+
 def cpu_baseline(name, budget_s=20.0):
     """The oracle, untuned, on a bounded sample of the workload: one layer of
     one decode step (all sequences), timed on the host cores."""
@@ -297,7 +320,7 @@ def cpu_baseline(name, budget_s=20.0):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; multi-GPU runs are not part of it",
+        print(json.dumps({"error": "bench.py measures one GPU; runs on more than one GPU are not supported",
                           "n_gpus": a.gpus}))
         sys.exit(2)
     import torch
@@ -367,10 +390,10 @@ def main():
                    "name": a.workload, "layers": wl.layers, "batch": wl.B,
                    "kv_tokens_attended_per_step": dec_tokens // steps},
         "decode_attn": {"avg_us_per_launch": avg_dec_us, "bytes_per_launch": bytes_per_launch,
-                        "kernels": "k_decode_tiers + k_decode_combine" + (" + k_side_output" if wl.side else "")},
+                        "kernels": "k_decode_tiers + k_decode_finish"},
         "wall_s_timed": wall,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(a.workload)},
     }
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample ...", file=sys.stderr, flush=True)

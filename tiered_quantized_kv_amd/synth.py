@@ -17,7 +17,7 @@ its own.
 import numpy as np
 
 WORKLOADS = {
-    # name: shape of the workload (see the design doc for the recipe)
+    # name: shape of the workload; the module docstring gives the recipe
     "c1": dict(index=1, layers=1, batch=1, n_q_heads=8, n_kv_heads=2, head_dim=64,
                context=512, rope_type="default", rope_theta=1e4, n_sink=4,
                recent_window=64, int4_budget=-1, middle_k_bits=4, middle_v_bits=4,
