@@ -117,34 +117,66 @@ __device__ __forceinline__ float row_sum_strided(float x) {
 }
 
 // ---- symmetric group quantizer ---------------------------------------------
+// s = fp16_RNE(amax / qmax), q = clamp(RNE(x / s), -qmax, qmax), s == 0 -> q = 0,
+// evaluated without a division:
+//  * qmax = 7: amax * float32(1/7) rounded once to fp16 equals the RNE of the
+//    exact quotient for every finite fp16 amax (the quotient is never closer
+//    to an fp16 midpoint than the product's error); qmax = 1: s = amax.
+//  * x * rcp(s) is within 2^-21 of x / s for |x / s| <= 8, while a quotient
+//    of fp16 values that is not an exact tie lies at least 2^-13 from every
+//    half-integer, so rint gives RNE except at exact ties. A tie is detected
+//    exactly from the residual e = x - k s (one fma, exact for these
+//    operands: 2|e| == s) and moved to the even neighbour.
+// Both facts were checked exhaustively over fp16 operands against exact
+// rational rounding (with the reciprocal off by one ulp either way).
+template <int BITS>
+__device__ __forceinline__ uint16_t group_scale_bits(float amax) {
+  if constexpr (BITS == 2) return f2h(amax);
+  else return f2h(amax * (1.0f / 7.0f));
+}
+template <int BITS>
+__device__ __forceinline__ int quant_code(float x, float s, float r) {
+  constexpr float kQmax = (float)((1 << (BITS - 1)) - 1);
+  float k = rintf(x * r);
+  const float e = fmaf(-k, s, x);
+  const bool tie_odd = (2.f * fabsf(e) == s) && (((int)k & 1) != 0);
+  k = tie_odd ? k + (e > 0.f ? 1.f : -1.f) : k;
+  return s != 0.f ? (int)__builtin_amdgcn_fmed3f(k, -kQmax, kQmax) : 0;
+}
+
 // 32 values of one group (exact float copies of fp16 values) -> packed codes
 // (BITS 32-bit words, little-endian: channel c at bit (c*BITS) of the group's
-// byte stream) and the fp16 scale. s = fp16_RNE(amax / qmax); q = clamp(RNE(x
-// / s)) with IEEE division (never an approximate reciprocal); s == 0 -> q = 0.
+// byte stream) and the fp16 scale.
 template <int BITS>
 __device__ __forceinline__ void quant_group32(const float* x, uint32_t* packed, uint16_t& scale) {
   constexpr int kOff = 1 << (BITS - 1);
-  constexpr float kQmax = (float)((1 << (BITS - 1)) - 1);
   float amax = 0.f;
 #pragma unroll
   for (int c = 0; c < 32; ++c) amax = fmaxf(amax, fabsf(x[c]));
-  const uint16_t sb = f2h(amax / kQmax);
+  const uint16_t sb = group_scale_bits<BITS>(amax);
   const float s = h2f(sb);
+  const float r = __builtin_amdgcn_rcpf(s);
 #pragma unroll
   for (int w = 0; w < BITS; ++w) packed[w] = 0u;
 #pragma unroll
   for (int c = 0; c < 32; ++c) {
-    int q = 0;
-    if (s != 0.f) {
-      float t = rintf(x[c] / s);
-      t = fminf(fmaxf(t, -kQmax), kQmax);
-      q = (int)t;
-    }
-    const uint32_t u = (uint32_t)(q + kOff);
+    const uint32_t u = (uint32_t)(quant_code<BITS>(x[c], s, r) + kOff);
     constexpr int kPerWord = 32 / BITS;
     packed[c / kPerWord] |= u << ((c % kPerWord) * BITS);
   }
   scale = sb;
+}
+
+// float64 -> fp16 RNE through one float32 rounding. The two roundings can
+// only disagree with a single one when the float32 value is an fp16 rounding
+// midpoint (the float32 rounding cannot cross one, every fp16 midpoint being
+// a float32 value); fp16-subnormal magnitudes are sent the same way.
+// `exact` is false for those cases, whose callers use d2h instead.
+__device__ __forceinline__ uint16_t d2h_fast(double d, bool& exact) {
+  const float f = (float)d;
+  const uint32_t u = __float_as_uint(f);
+  exact = f == 0.f || (fabsf(f) >= 6.103515625e-05f && (u & 0x1FFFu) != 0x1000u);
+  return f2h(f);
 }
 
 // Offset-removed code of channel c (0..31) of a packed group, as float.

@@ -237,30 +237,40 @@ __device__ __forceinline__ uint32_t group_or(uint32_t x) {
 
 // The group quantizer with one channel per lane: the 32 channels of a group
 // are the lanes of one half-wave (channel = lane % 32). Same arithmetic as
-// quant_group32: s = fp16_RNE(amax / qmax), q = clamp(RNE(x / s)) with IEEE
-// division. Returns the packed word that holds this lane's channel (in every
-// lane of the word's lane group) and the scale bits.
+// quant_group32 (group_scale_bits, quant_code); the amax is an unsigned max
+// of the non-negative float bits across the half-wave. Returns the packed word
+// that holds this lane's channel (in every lane of the word's lane group) and
+// the scale bits.
 template <int BITS>
 __device__ __forceinline__ uint32_t quant_lane(float x, int c, uint16_t& scale) {
   constexpr int kOff = 1 << (BITS - 1);
-  constexpr float kQmax = (float)((1 << (BITS - 1)) - 1);
-  float amax = fabsf(x);
-  amax = fmaxf(amax, dpp_f<kRowRor1>(amax));
-  amax = fmaxf(amax, dpp_f<kRowRor2>(amax));
-  amax = fmaxf(amax, dpp_f<kRowRor4>(amax));
-  amax = fmaxf(amax, dpp_f<kRowRor8>(amax));
-  amax = fmaxf(amax, __shfl_xor(amax, 16));
-  const uint16_t sb = f2h(amax / kQmax);
+  uint32_t m = __float_as_uint(x) & 0x7FFFFFFFu;
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, kRowRor1, 0xF, 0xF, false));
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, kRowRor2, 0xF, 0xF, false));
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, kRowRor4, 0xF, 0xF, false));
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, kRowRor8, 0xF, 0xF, false));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 16));
+  const uint16_t sb = group_scale_bits<BITS>(__uint_as_float(m));
   const float s = h2f(sb);
-  int q = 0;
-  if (s != 0.f) {
-    float t = rintf(x / s);
-    t = fminf(fmaxf(t, -kQmax), kQmax);
-    q = (int)t;
-  }
+  const int q = quant_code<BITS>(x, s, __builtin_amdgcn_rcpf(s));
   constexpr int kPerWord = 32 / BITS;
   scale = sb;
   return group_or<kPerWord>((uint32_t)(q + kOff) << ((c % kPerWord) * BITS));
+}
+
+// Rotation of a key pair by the float64 (cos, sin) of a shift, rounded once
+// to fp16: y1 = x1 cos - x2 sin, y2 = x2 cos + x1 sin.
+__device__ __forceinline__ void rotate_pair(float x1, float x2, double c, double sn, uint16_t& h1,
+                                            uint16_t& h2) {
+  const double a1 = (double)x1, a2 = (double)x2;
+  const double d1 = a1 * c - a2 * sn, d2 = a2 * c + a1 * sn;
+  bool e1, e2;
+  h1 = d2h_fast(d1, e1);
+  h2 = d2h_fast(d2, e2);
+  if (__any(!(e1 && e2))) {            // rare: an fp16 midpoint or an fp16-subnormal value
+    if (!e1) h1 = d2h(d1);
+    if (!e2) h2 = d2h(d2);
+  }
 }
 
 // Middle-tier compaction of one chunk of kCompactRows rows of one (sequence,
@@ -308,9 +318,10 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
     for (int t = wave * RPW + sub; t < R; t += 4 * RPW) {
       const int slot = s.n_sink + (head + t) % s.ring;
       uint16_t* kp = reinterpret_cast<uint16_t*>(a.c.fp_k) + (bg * slots + slot) * D;
-      const double x1 = (double)h2f(kp[p]), x2 = (double)h2f(kp[p + HALF]);
-      kp[p] = d2h(x1 * cs.x - x2 * cs.y);
-      kp[p + HALF] = d2h(x2 * cs.x + x1 * cs.y);
+      uint16_t h1, h2;
+      rotate_pair(h2f(kp[p]), h2f(kp[p + HALF]), cs.x, cs.y, h1, h2);
+      kp[p] = h1;
+      kp[p + HALF] = h2;
     }
     return;
   }
@@ -392,9 +403,9 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
     const uint32_t u2 = (krow[(p + HALF) * KB / 8] >> (((p + HALF) * KB) % 8)) & KMASK;
     const float x1 = (float)((int)u1 - KOFF) * h2f(s_ks[t * NG + p / 32]);          // exact
     const float x2 = (float)((int)u2 - KOFF) * h2f(s_ks[t * NG + (p + HALF) / 32]);
-    const double a1 = (double)x1, a2 = (double)x2;
-    const float z1 = h2f(d2h(a1 * cs.x - a2 * cs.y));
-    const float z2 = h2f(d2h(a2 * cs.x + a1 * cs.y));
+    uint16_t h1, h2;
+    rotate_pair(x1, x2, cs.x, cs.y, h1, h2);
+    const float z1 = h2f(h1), z2 = h2f(h2);
     uint16_t sc1, sc2;
     const uint32_t w1 = quant_lane<KB>(z1, c, sc1);
     const uint32_t w2 = quant_lane<KB>(z2, c, sc2);
@@ -640,9 +651,7 @@ __global__ __launch_bounds__(256) void k_build(BuildArgs a) {
         sincos(-(double)delta * f, &sn, &cn);
         cur_delta = delta;
       }
-      const double x1 = (double)h2f(k1), x2 = (double)h2f(k2);
-      y1 = d2h(x1 * cn - x2 * sn);
-      y2 = d2h(x2 * cn + x1 * sn);
+      rotate_pair(h2f(k1), h2f(k2), cn, sn, y1, y2);
     }
     if (kind != 1) {
       const int slot = kind == 0 ? j : s.n_sink + (j - S - M);
