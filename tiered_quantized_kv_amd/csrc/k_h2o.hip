@@ -8,14 +8,15 @@
 // softmax_i(q_i . k / sqrt(d))_j.
 //
 // Two passes, both QK^T on v_mfma_f32_16x16x32_f16 (fp16 in, fp32 out):
-//   k_h2o_rowlse   grid (L/16, Hkv, B): 16 query rows of every query head of
+//   k_h2o_rowlse   (L/16) x Hkv x B workgroups: 16 query rows of every query head of
 //                  a KV group stream the causal 64-key tiles of that group
 //                  (staged once in LDS for all its heads) and keep an online
 //                  max / sum; writes the log2-domain LSE of each row.
-//   k_h2o_colsum   grid (L/64, Hkv, B * chunks): 64 keys held as MFMA B
+//   k_h2o_colsum   (L/64) x Hkv x B x chunks workgroups: 64 keys held as MFMA B
 //                  fragments in registers; the waves walk the (query head,
-//                  16-row query tile) items of a query-row chunk at or below
-//                  the diagonal, accumulating p = 2^(s - LSE_i) per key.
+//                  16-row query tile) items of a chunk of query tiles at or
+//                  below the diagonal, accumulating p = 2^(s - LSE_i)
+//                  per key.
 //   k_h2o_reduce   sums the partials over chunks, KV groups (and the batch
 //                  rows when shared) in a fixed order.
 // MFMA 16x16x32 lane layout: A row = lane % 16, k = 8 * (lane / 16) + [0, 8);
@@ -29,13 +30,25 @@
 namespace fade {
 
 constexpr int kTile = 64;
+constexpr float kMasked = -1.0e30f;     // score of a masked (non-causal) slot
 
-// Query-row chunks of the column pass: enough workgroups to cover the chip.
+// Column pass work split: the query tiles at or below a 64-key tile are cut
+// into chunks of qt_per 16-row tiles, one workgroup per (key tile, KV group,
+// row, chunk); enough chunks for about 4096 workgroups, each at least eight
+// tiles long. Chunks past a key tile's causal range exit at once.
+static void colsum_split(int Hkv, int batch, int L, int& n_chunks, int& qt_per) {
+  const long tiles = (L + kTile - 1) / kTile;
+  const int n_qt = (L + 15) / 16;
+  const long base = tiles * Hkv * batch;
+  int nch = (int)((4096 + base - 1) / base);
+  nch = max(1, min(nch, (n_qt + 7) / 8));
+  qt_per = (n_qt + nch - 1) / nch;
+  n_chunks = (n_qt + qt_per - 1) / qt_per;
+}
 static int colsum_chunks(int Hkv, int batch, int L) {
-  const int tiles = (L + kTile - 1) / kTile;
-  int c = 1;
-  while ((long)tiles * Hkv * batch * c < 1024 && c < tiles) c *= 2;
-  return c;
+  int nch, qp;
+  colsum_split(Hkv, batch, L, nch, qp);
+  return nch;
 }
 
 size_t h2o_ws_bytes(int D, int Hq, int Hkv, int batch, int L) {
@@ -50,24 +63,34 @@ __device__ __forceinline__ f16x8 load8(const uint16_t* p) {
 
 // Row pass. Workgroup = (16 query rows, KV group); wave w takes the group's
 // query heads w, w + 4, ... The 64-key tiles of the group's keys are staged
-// in LDS (double buffered, one barrier per tile) and shared by those heads.
+// in LDS (triple buffered, one barrier per tile) and shared by those heads.
 // Each lane keeps its own running max and sum for the four rows it holds;
 // the 16 lanes of a row are merged once at the end.
 template <int D, int HPW>
 __global__ __launch_bounds__(256) void k_h2o_rowlse(const uint16_t* __restrict__ q,
                                                     const uint16_t* __restrict__ k, int Hq, int Hkv,
-                                                    int L, float scale, float* __restrict__ lse) {
+                                                    int L, int batch, float scale, float* __restrict__ lse) {
   constexpr int KB = D / 32;
   constexpr int PITCH = D + 8;                  // halves per LDS row
   constexpr int CPT = kTile * (D / 8) / 256;    // 16-byte chunks per thread per tile
-  __shared__ __align__(16) uint16_t ktile[2][kTile * PITCH];
-  const int rt = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  __shared__ __align__(16) uint16_t ktile[3][kTile * PITCH];
+  // 1-D grid, XCD aware: id % 8 picks the XCD, and each XCD walks the row
+  // tiles of one (row, KV group) at a time, longest rows (most key tiles)
+  // first, so that group's keys stay in that XCD's L2.
+  const int n_rt = (L + 15) / 16;
+  const int id = blockIdx.x, xcd = id % 8, slot = id / 8;
+  const int rt = n_rt - 1 - slot % n_rt;
+  const int pair = (slot / n_rt) * 8 + xcd;
+  if (pair >= Hkv * batch) return;
+  const int g = pair % Hkv, b = pair / Hkv;
   const int n_rep = Hq / Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r0 = rt * 16;
   const uint16_t* kb_ = k + ((size_t)(b * Hkv + g) * L) * D;
   const int n_kt = min(r0 + 15, L - 1) / kTile + 1;
 
+  // Key tiles are triple buffered: tile kt + 2 is loaded into registers while
+  // tile kt is used, and stored to LDS after it.
   uint4 pre[CPT];
   auto gload = [&](int kt) {
 #pragma unroll
@@ -87,6 +110,8 @@ __global__ __launch_bounds__(256) void k_h2o_rowlse(const uint16_t* __restrict__
     }
   };
   gload(0);
+  lstore(0);
+  if (n_kt > 1) gload(1);
 
   f16x8 afrag[HPW][KB];
   float m_l[HPW][4], l_l[HPW][4];
@@ -101,15 +126,15 @@ __global__ __launch_bounds__(256) void k_h2o_rowlse(const uint16_t* __restrict__
       afrag[j][kb] = r < L ? load8(qb + (size_t)r * D + kb * 32 + 8 * (lane >> 4)) : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      m_l[j][i] = -INFINITY;
+      m_l[j][i] = kMasked;
       l_l[j][i] = 0.f;
     }
   }
-  lstore(0);
+  if (n_kt > 1) lstore(1);
+  if (n_kt > 2) gload(2);
   __syncthreads();
   for (int kt = 0; kt < n_kt; ++kt) {
-    if (kt + 1 < n_kt) gload(kt + 1);
-    const uint16_t* kt_lds = ktile[kt & 1];
+    const uint16_t* kt_lds = ktile[kt % 3];
     const bool edge = kt == n_kt - 1;            // the diagonal tile (and the end of L)
 #pragma unroll
     for (int j = 0; j < HPW; ++j) {
@@ -130,23 +155,27 @@ __global__ __launch_bounds__(256) void k_h2o_rowlse(const uint16_t* __restrict__
           const int key = kt * kTile + nb * 16 + (lane & 15);
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (key > row_base + i || key >= L) s[nb][i] = -INFINITY;
+            if (key > row_base + i || key >= L) s[nb][i] = kMasked;
         }
       }
+      // Masked scores are a large finite negative, so 2^(s - m) is exactly 0
+      // for them while a row has a live key, and the update needs no branch
+      // (rows past L keep finite garbage and are never written).
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float mt = fmaxf(fmaxf(s[0][i], s[1][i]), fmaxf(s[2][i], s[3][i]));
         const float mn = fmaxf(m_l[j][i], mt);
-        if (mn != -INFINITY) {
-          float acc = l_l[j][i] * __builtin_amdgcn_exp2f(m_l[j][i] - mn);
+        float acc = l_l[j][i] * __builtin_amdgcn_exp2f(m_l[j][i] - mn);
 #pragma unroll
-          for (int nb = 0; nb < 4; ++nb) acc += __builtin_amdgcn_exp2f(s[nb][i] - mn);
-          l_l[j][i] = acc;
-          m_l[j][i] = mn;
-        }
+        for (int nb = 0; nb < 4; ++nb) acc += __builtin_amdgcn_exp2f(s[nb][i] - mn);
+        l_l[j][i] = acc;
+        m_l[j][i] = mn;
       }
     }
-    if (kt + 1 < n_kt) lstore((kt + 1) & 1);
+    // buffer (kt + 2) % 3 was last read in iteration kt - 1, before the
+    // barrier that ended it
+    if (kt + 2 < n_kt) lstore((kt + 2) % 3);
+    if (kt + 3 < n_kt) gload(kt + 3);
     __syncthreads();
   }
   // merge the 16 lanes of each row: LSE = M + log2(sum_lanes l * 2^(m - M))
@@ -161,7 +190,7 @@ __global__ __launch_bounds__(256) void k_h2o_rowlse(const uint16_t* __restrict__
       M = fmaxf(M, dpp_f<kRowRor2>(M));
       M = fmaxf(M, dpp_f<kRowRor4>(M));
       M = fmaxf(M, dpp_f<kRowRor8>(M));
-      float l = m_l[j][i] == -INFINITY ? 0.f : l_l[j][i] * __builtin_amdgcn_exp2f(m_l[j][i] - M);
+      float l = l_l[j][i] * __builtin_amdgcn_exp2f(m_l[j][i] - M);
       l = row_sum_strided<1>(l);
       const int row = row_base + i;
       if ((lane & 15) == 0 && row < L)
@@ -179,20 +208,31 @@ __global__ __launch_bounds__(256) void k_h2o_rowlse(const uint16_t* __restrict__
 template <int D>
 __global__ __launch_bounds__(256) void k_h2o_colsum(const uint16_t* __restrict__ q,
                                                     const uint16_t* __restrict__ k, int Hq, int Hkv,
-                                                    int L, int n_chunks, float scale,
-                                                    const float* __restrict__ lse,
+                                                    int L, int batch, int n_chunks, int qt_per,
+                                                    float scale, const float* __restrict__ lse,
                                                     float* __restrict__ part) {
   constexpr int KB = D / 32;
   __shared__ float colred[4][kTile];
-  const int kt = blockIdx.x, g = blockIdx.y;
-  const int b = blockIdx.z / n_chunks, c = blockIdx.z % n_chunks;
+  // 1-D grid, XCD aware: workgroups are dealt to the 8 XCDs round-robin by
+  // id, so id % 8 picks the XCD and id / 8 walks, on that XCD, all key tiles
+  // of one (chunk, row, KV group) before the next: the chunk's query rows are
+  // fetched into that XCD's L2 once and reused by every key tile.
+  const int tiles = (L + kTile - 1) / kTile;
+  const int n_pairs = Hkv * batch * n_chunks;
+  const int id = blockIdx.x, xcd = id % 8, slot = id / 8;
+  const int kt = slot % tiles;
+  const int pair = (slot / tiles) * 8 + xcd;
+  if (pair >= n_pairs) return;
+  const int c = pair / (Hkv * batch), bg = pair % (Hkv * batch);
+  const int b = bg / Hkv, g = bg % Hkv;
   const int n_rep = Hq / Hkv;
-  const int batch = gridDim.z / n_chunks;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int k0 = kt * kTile;
   const uint16_t* kb_ = k + ((size_t)(b * Hkv + g) * L) * D;
-  const int rows_per = ((L + n_chunks - 1) / n_chunks + 15) / 16 * 16;
-  const int qlo = max(c * rows_per, k0), qhi = min(L, (c + 1) * rows_per);
+  // query tiles of this workgroup: the chunk c of the tiles at or below the
+  // key tile's first key
+  const int qt_lo = k0 / 16 + c * qt_per;
+  const int qlo = qt_lo * 16, qhi = min(L, (qt_lo + qt_per) * 16);
   float col[4] = {0.f, 0.f, 0.f, 0.f};
   if (qlo < qhi) {                               // workgroup-uniform
     f16x8 bfrag[4][KB];
@@ -206,30 +246,54 @@ __global__ __launch_bounds__(256) void k_h2o_colsum(const uint16_t* __restrict__
     const int first_qt = qlo / 16;
     const int n_qt = (qhi - qlo + 15) / 16;
     const int items = n_rep * n_qt;
+    // Items (query head hl, 16-row tile first_qt + qi) in the order
+    // hl * n_qt + qi; wave w takes items w, w + 4, ... walked incrementally.
     struct Item {
       f16x8 a[KB];
       float lrow[4];
     };
-    auto fetch = [&](Item& it, int idx) {
-      const int hl = idx / n_qt, qt16 = first_qt + (idx - hl * n_qt);
-      const size_t hrow = (size_t)(b * Hq + g * n_rep + hl) * L;
-      const int r = qt16 * 16 + (lane & 15);
-      const uint16_t* qb = q + hrow * D;
+    const size_t head0 = (size_t)(b * Hq + g * n_rep) * L;
+    auto fetch = [&](Item& it, int hl, int qi) {
+      const size_t hrow = head0 + (size_t)hl * L;
+      const int rt = (first_qt + qi) * 16;
+      const int r = rt + (lane & 15);
+      const uint16_t* qp = q + (hrow + r) * D + 8 * (lane >> 4);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
-        it.a[kb] = r < L ? load8(qb + (size_t)r * D + kb * 32 + 8 * (lane >> 4)) : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      const int rb = qt16 * 16 + 4 * (lane >> 4);
+        it.a[kb] = r < L ? load8(qp + kb * 32) : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      const int rb = rt + 4 * (lane >> 4);
 #pragma unroll
       for (int i = 0; i < 4; ++i) it.lrow[i] = rb + i < L ? lse[hrow + rb + i] : 0.f;
     };
-    Item nxt;
-    if (wave < items) fetch(nxt, wave);
+    auto advance = [&](int& hl, int& qi) {
+      qi += 4;
+      while (qi >= n_qt) {
+        qi -= n_qt;
+        ++hl;
+      }
+    };
+    int hl = 0, qi = wave;
+    while (qi >= n_qt && hl < n_rep) {
+      qi -= n_qt;
+      ++hl;
+    }
+    // two items in flight ahead of the one being computed
+    Item nx1, nx2;
+    int h1 = hl, q1 = qi;
+    advance(h1, q1);
+    if (wave < items) fetch(nx1, hl, qi);
+    if (wave + 4 < items) fetch(nx2, h1, q1);
     for (int idx = wave; idx < items; idx += 4) {
-      const Item cur = nxt;
-      if (idx + 4 < items) fetch(nxt, idx + 4);
-      const int hl = idx / n_qt, qt16 = first_qt + (idx - hl * n_qt);
-      const int rb = qt16 * 16 + 4 * (lane >> 4);
-      const bool edge = qt16 * 16 < k0 + kTile || qt16 * 16 + 16 > L;   // wave-uniform
+      const Item cur = nx1;
+      nx1 = nx2;
+      const int rt = (first_qt + qi) * 16;
+      int nhl = hl, nqi = qi;
+      advance(nhl, nqi);
+      int fhl = nhl, fqi = nqi;
+      advance(fhl, fqi);
+      if (idx + 8 < items) fetch(nx2, fhl, fqi);
+      const int rb = rt + 4 * (lane >> 4);
+      const bool edge = rt < k0 + kTile || rt + 16 > L;   // wave-uniform
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -247,6 +311,8 @@ __global__ __launch_bounds__(256) void k_h2o_colsum(const uint16_t* __restrict__
           for (int i = 0; i < 4; ++i) col[nb] += __builtin_amdgcn_exp2f(fmaf(acc[i], scale, -cur.lrow[i]));
         }
       }
+      hl = nhl;
+      qi = nqi;
     }
   }
 #pragma unroll
@@ -271,19 +337,39 @@ __global__ __launch_bounds__(256) void k_h2o_colsum(const uint16_t* __restrict__
 }
 
 // Sums the column partials over chunks, KV groups and (shared) batch rows in
-// a fixed order.
+// a fixed order: four lanes per key each sum a quarter of the (row, group,
+// chunk) partials with eight loads in flight, then the quarters are added.
 __global__ __launch_bounds__(256) void k_h2o_reduce(const float* __restrict__ part, int Hkv, int L,
                                                     int batch, int n_chunks, int shared,
                                                     float* __restrict__ out) {
+  __shared__ float red[4][64];
   const int r = blockIdx.y;
-  const int j = blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= L) return;
-  const int b0 = shared ? 0 : r, b1 = shared ? batch : r + 1;
+  const int u = threadIdx.x & 63, qtr = threadIdx.x >> 6;
+  const int j = blockIdx.x * 64 + u;
+  const int b0 = shared ? 0 : r, nb = shared ? batch : 1;
+  const int n = nb * Hkv * n_chunks;              // partials per key, ordered (b, g, c)
   float acc = 0.f;
-  for (int b = b0; b < b1; ++b)
-    for (int g = 0; g < Hkv; ++g)
-      for (int c = 0; c < n_chunks; ++c) acc += part[((size_t)(c * batch + b) * Hkv + g) * L + j];
-  out[(size_t)r * L + j] = acc;
+  if (j < L) {
+    for (int i0 = qtr; i0 < n; i0 += 32) {
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int i = i0 + 4 * k;
+        if (i < n) {
+          const int c = i % n_chunks, bg = i / n_chunks;
+          const int g = bg % Hkv, b = b0 + bg / Hkv;
+          v[k] = part[((size_t)(c * batch + b) * Hkv + g) * L + j];
+        } else {
+          v[k] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc += v[k];
+    }
+  }
+  red[qtr][u] = acc;
+  __syncthreads();
+  if (qtr == 0 && j < L) out[(size_t)r * L + j] = ((red[0][u] + red[1][u]) + red[2][u]) + red[3][u];
 }
 
 hipError_t launch_h2o_prefill(int D, int Hq, int Hkv, int batch, int L, int shared,
@@ -295,26 +381,28 @@ hipError_t launch_h2o_prefill(int D, int Hq, int Hkv, int batch, int L, int shar
                                          align_up((size_t)batch * Hq * L * 4, 256));
   const float scale = kLog2e / sqrtf((float)D);
   const int tiles = (L + kTile - 1) / kTile;
-  const int nch = colsum_chunks(Hkv, batch, L);
+  int nch, qt_per;
+  colsum_split(Hkv, batch, L, nch, qt_per);
   const int n_rep = Hq / Hkv;
-  const dim3 grow((L + 15) / 16, Hkv, batch), gcol(tiles, Hkv, batch * nch);
+  const int n_pairs8 = (Hkv * batch * nch + 7) / 8 * 8;
+  const dim3 grow(((L + 15) / 16) * ((Hkv * batch + 7) / 8 * 8)), gcol(tiles * n_pairs8);
   if (D == 128) {
     if (n_rep > 4)
-      hipLaunchKernelGGL((k_h2o_rowlse<128, 2>), grow, dim3(256), 0, st, q, k, Hq, Hkv, L, scale, lse);
+      hipLaunchKernelGGL((k_h2o_rowlse<128, 2>), grow, dim3(256), 0, st, q, k, Hq, Hkv, L, batch, scale, lse);
     else
-      hipLaunchKernelGGL((k_h2o_rowlse<128, 1>), grow, dim3(256), 0, st, q, k, Hq, Hkv, L, scale, lse);
-    hipLaunchKernelGGL(k_h2o_colsum<128>, gcol, dim3(256), 0, st, q, k, Hq, Hkv, L, nch, scale, lse, part);
+      hipLaunchKernelGGL((k_h2o_rowlse<128, 1>), grow, dim3(256), 0, st, q, k, Hq, Hkv, L, batch, scale, lse);
+    hipLaunchKernelGGL(k_h2o_colsum<128>, gcol, dim3(256), 0, st, q, k, Hq, Hkv, L, batch, nch, qt_per, scale, lse, part);
   } else {
     if (n_rep > 4)
-      hipLaunchKernelGGL((k_h2o_rowlse<64, 2>), grow, dim3(256), 0, st, q, k, Hq, Hkv, L, scale, lse);
+      hipLaunchKernelGGL((k_h2o_rowlse<64, 2>), grow, dim3(256), 0, st, q, k, Hq, Hkv, L, batch, scale, lse);
     else
-      hipLaunchKernelGGL((k_h2o_rowlse<64, 1>), grow, dim3(256), 0, st, q, k, Hq, Hkv, L, scale, lse);
-    hipLaunchKernelGGL(k_h2o_colsum<64>, gcol, dim3(256), 0, st, q, k, Hq, Hkv, L, nch, scale, lse, part);
+      hipLaunchKernelGGL((k_h2o_rowlse<64, 1>), grow, dim3(256), 0, st, q, k, Hq, Hkv, L, batch, scale, lse);
+    hipLaunchKernelGGL(k_h2o_colsum<64>, gcol, dim3(256), 0, st, q, k, Hq, Hkv, L, batch, nch, qt_per, scale, lse, part);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int rows = shared ? 1 : batch;
-  hipLaunchKernelGGL(k_h2o_reduce, dim3((L + 255) / 256, rows), dim3(256), 0, st, part, Hkv, L, batch, nch,
+  hipLaunchKernelGGL(k_h2o_reduce, dim3((L + 63) / 64, rows), dim3(256), 0, st, part, Hkv, L, batch, nch,
                      shared, scores_out);
   return hipGetLastError();
 }
