@@ -32,15 +32,12 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
 // float64 -> float32 rounding to odd: truncate toward zero, then set the last
 // bit if anything was discarded.
 __device__ __forceinline__ float d2f_odd(double d) {
-  float f = (float)d;
-  double back = (double)f;
-  if (back != d) {
-    uint32_t u = __float_as_uint(f);
-    if (fabs(back) > fabs(d)) u -= 1u;   // rounded away from zero: step back
-    u |= 1u;
-    f = __uint_as_float(u);
-  }
-  return f;
+  const float f = (float)d;
+  const double back = (double)f;
+  uint32_t u = __float_as_uint(f);
+  u -= (uint32_t)(fabs(back) > fabs(d));   // rounded away from zero: step back
+  u |= (uint32_t)(back != d);
+  return __uint_as_float(u);
 }
 __device__ __forceinline__ uint16_t d2h(double d) { return f2h(d2f_odd(d)); }
 __device__ __forceinline__ uint16_t d2bf(double d) { return f2bf(d2f_odd(d)); }
@@ -165,18 +162,6 @@ __device__ __forceinline__ void quant_group32(const float* x, uint32_t* packed, 
     packed[c / kPerWord] |= u << ((c % kPerWord) * BITS);
   }
   scale = sb;
-}
-
-// float64 -> fp16 RNE through one float32 rounding. The two roundings can
-// only disagree with a single one when the float32 value is an fp16 rounding
-// midpoint (the float32 rounding cannot cross one, every fp16 midpoint being
-// a float32 value); fp16-subnormal magnitudes are sent the same way.
-// `exact` is false for those cases, whose callers use d2h instead.
-__device__ __forceinline__ uint16_t d2h_fast(double d, bool& exact) {
-  const float f = (float)d;
-  const uint32_t u = __float_as_uint(f);
-  exact = f == 0.f || (fabsf(f) >= 6.103515625e-05f && (u & 0x1FFFu) != 0x1000u);
-  return f2h(f);
 }
 
 // Offset-removed code of channel c (0..31) of a packed group, as float.

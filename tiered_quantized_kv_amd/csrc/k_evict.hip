@@ -31,6 +31,8 @@
 namespace fade {
 
 constexpr int kSelThreads = 1024;
+constexpr int kInfo = 8;   // ints per row of the selection record:
+                           // {M, n_evict, S, R, first evicted middle slot (M if none)}
 
 __device__ __forceinline__ uint32_t ordered_key(float f) {
   if (f == 0.f) f = 0.f;                       // -0 and +0 are the same score
@@ -71,7 +73,7 @@ struct SelectArgs {
   int max_evict;         // events evicting more than this are skipped
   int32_t* map;          // [rows][map_stride] new middle index or -1
   int map_stride;
-  int32_t* info;         // [rows][4] = {M_old, n_evict, S, R}
+  int32_t* info;         // [rows][kInfo] selection record
   int budget;
   int policy;
   // decode mode (in-place): lens, compact the score row, update lens
@@ -108,10 +110,10 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
   const float* sc = a.scores ? a.scores + (size_t)row * a.score_stride + S : nullptr;
   int32_t* map = a.map + (size_t)row * a.map_stride;
   if (tid == 0) {
-    a.info[4 * row + 0] = M;
-    a.info[4 * row + 1] = n_ev;
-    a.info[4 * row + 2] = S;
-    a.info[4 * row + 3] = R;
+    a.info[kInfo * row + 0] = M;
+    a.info[kInfo * row + 1] = n_ev;
+    a.info[kInfo * row + 2] = S;
+    a.info[kInfo * row + 3] = R;
   }
   uint32_t thr = 0;
   int n_eq_ev = 0;
@@ -145,6 +147,9 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
     n_eq_ev = kk;
   }
   // Assign new slots in ascending slot order.
+  __shared__ int s_first_ev;
+  if (tid == 0) s_first_ev = M;
+  __syncthreads();
   int base_eq = 0, base_keep = 0;
   const bool by_score = n_ev > 0 && !by_pos;   // uniform over the workgroup
   for (int c0 = 0; c0 < M; c0 += kSelThreads) {
@@ -161,13 +166,18 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
       ev = r < n_ev;
     }
     const bool keep = r < M && !ev;
+    {
+      const uint64_t evm = __ballot(r < M && ev);     // first evicted slot, one atomic per wave
+      if ((tid & 63) == 0 && evm) atomicMin(&s_first_ev, c0 + (tid & ~63) + (int)__builtin_ctzll(evm));
+    }
     int tot_keep;
     const int keep_rank = block_excl_scan(keep ? 1 : 0, &tot_keep, wsum) + base_keep;
     base_keep += tot_keep;
     if (r < M) map[r] = keep ? keep_rank : -1;
   }
-  if (!a.decode || n_ev == 0) return;
   __syncthreads();
+  if (tid == 0) a.info[kInfo * row + 4] = s_first_ev;
+  if (!a.decode || n_ev == 0) return;
   // Compact this row's scores in place (destinations never exceed sources).
   if (a.cache_scores) {
     float* srow = a.cache_scores + (size_t)row * a.cap_T;
@@ -263,26 +273,20 @@ __device__ __forceinline__ uint32_t quant_lane(float x, int c, uint16_t& scale) 
 __device__ __forceinline__ void rotate_pair(float x1, float x2, double c, double sn, uint16_t& h1,
                                             uint16_t& h2) {
   const double a1 = (double)x1, a2 = (double)x2;
-  const double d1 = a1 * c - a2 * sn, d2 = a2 * c + a1 * sn;
-  bool e1, e2;
-  h1 = d2h_fast(d1, e1);
-  h2 = d2h_fast(d2, e2);
-  if (__any(!(e1 && e2))) {            // rare: an fp16 midpoint or an fp16-subnormal value
-    if (!e1) h1 = d2h(d1);
-    if (!e2) h2 = d2h(d2);
-  }
+  h1 = d2h(a1 * c - a2 * sn);
+  h2 = d2h(a2 * c + a1 * sn);
 }
 
 // Middle-tier compaction of one chunk of kCompactRows rows of one (sequence,
 // KV head); the extra x-block re-rotates the recent ring in place.
 //
 // Moved rows are staged in LDS with coalesced 16-byte loads. Each wave then
-// rebuilds one row per pass (two at D = 64) with one lane per rotation pair
-// (channels i and i + D/2): dequantize, rotate by the float64 cos/sin of the
-// shift, round to fp16, requantize with the group amax reduced across the
-// half-wave, and write the packed words back into LDS. After a barrier the
-// rows go out with coalesced stores, to their destination when it lies in
-// this chunk and to the spill region otherwise.
+// rebuilds 8 rows per pass (16 at D = 64) with one lane per 8 rotation pairs:
+// dequantize, rotate by the float64 cos/sin of the shift, round to fp16,
+// requantize (group amax across the 4 lanes of a group) and write the packed
+// words back into LDS. After a barrier the rows go out with coalesced
+// stores, to their destination when it lies in this chunk and to the spill
+// region otherwise.
 template <int D, int KB, int VB>
 __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
   constexpr int HALF = D / 2;                   // rotation pairs per row
@@ -290,7 +294,6 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
   constexpr int NG = D / 32;
   constexpr int KROW = D * KB / 8, VROW = D * VB / 8;
   constexpr int CH = kCompactRows;
-  constexpr int KPW = 32 / KB;                  // channels per packed K word
   constexpr uint32_t KMASK = (1u << KB) - 1u;
   constexpr int KOFF = 1 << (KB - 1);
   __shared__ __align__(16) uint32_t s_kc[CH * KROW / 4];
@@ -302,7 +305,7 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
   const int cidx = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const Shape& s = a.s;
   const int mrow = s.shared ? 0 : b;
-  const int M = a.info[4 * mrow + 0], n_ev = a.info[4 * mrow + 1];
+  const int M = a.info[kInfo * mrow + 0], n_ev = a.info[kInfo * mrow + 1];
   if (n_ev == 0) return;
   const size_t bg = (size_t)(b * s.Hkv + g);
   const int tid = threadIdx.x;
@@ -330,19 +333,31 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
   const int r0 = cidx * CH;
   if (r0 >= M) return;
   const int rows_here = min(CH, M - r0);
+  if (r0 + rows_here <= a.info[kInfo * mrow + 4]) {
+    // every row of this chunk lies before the first evicted slot: nothing moves
+    if (tid == 0) a.spill_info[bg * a.nchunks + cidx] = make_int2(0, 0);
+    return;
+  }
   if (tid == 0) {
     s_first = 0x7fffffff;
     s_lo = CH;
     s_kept = 0;
   }
   __syncthreads();
-  for (int t = tid; t < rows_here; t += 256) {
-    const int d = map[r0 + t];
-    s_dst[t] = d;
-    if (d >= 0) {
-      atomicMin(&s_first, d);
-      atomicAdd(&s_kept, 1);
-      if (d != r0 + t) atomicMin(&s_lo, t);
+  // Survivors keep their order, so the first destination is that of the
+  // first kept row; per-wave ballots give each wave's first kept row, first
+  // moved row and kept count, merged with one LDS atomic per wave.
+  for (int t0 = wave * 64; t0 < rows_here; t0 += 256) {
+    const int t = t0 + lane;
+    const int d = t < rows_here ? map[r0 + t] : -1;
+    if (t < rows_here) s_dst[t] = d;
+    const uint64_t kept_m = __ballot(d >= 0);
+    const uint64_t moved_m = __ballot(d >= 0 && d != r0 + t);
+    const int dfirst = __shfl(d, kept_m ? (int)__builtin_ctzll(kept_m) : 0);   // whole wave
+    if (lane == 0 && kept_m) {
+      atomicMin(&s_first, dfirst);
+      atomicAdd(&s_kept, (int)__builtin_popcountll(kept_m));
+      if (moved_m) atomicMin(&s_lo, t0 + (int)__builtin_ctzll(moved_m));
     }
   }
   __syncthreads();
@@ -384,38 +399,86 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
   __syncthreads();
 
   // ---- rebuild the keys of moved rows in LDS ----
-  int cur_delta = -1;
-  double2 cs = make_double2(1.0, 0.0);
-  const int c = p % 32;                          // channel within its group
-  for (int base = wave * RPW; base < n_rows; base += 4 * RPW) {
-    const int tt = base + sub;
-    const bool valid = tt < n_rows;
-    const int t = lo + min(tt, n_rows - 1);
-    const int d = s_dst[t];
-    const bool moved = valid && d >= 0 && d != r0 + t;
-    const int delta = moved ? r0 + t - d : 0;
-    if (delta != cur_delta) {
-      cs = a.tab[(size_t)delta * HALF + p];
-      cur_delta = delta;
-    }
-    const uint8_t* krow = reinterpret_cast<const uint8_t*>(s_kc) + t * KROW;
-    const uint32_t u1 = (krow[p * KB / 8] >> ((p * KB) % 8)) & KMASK;
-    const uint32_t u2 = (krow[(p + HALF) * KB / 8] >> (((p + HALF) * KB) % 8)) & KMASK;
-    const float x1 = (float)((int)u1 - KOFF) * h2f(s_ks[t * NG + p / 32]);          // exact
-    const float x2 = (float)((int)u2 - KOFF) * h2f(s_ks[t * NG + (p + HALF) / 32]);
-    uint16_t h1, h2;
-    rotate_pair(x1, x2, cs.x, cs.y, h1, h2);
-    const float z1 = h2f(h1), z2 = h2f(h2);
-    uint16_t sc1, sc2;
-    const uint32_t w1 = quant_lane<KB>(z1, c, sc1);
-    const uint32_t w2 = quant_lane<KB>(z2, c, sc2);
-    if (moved && c % KPW == 0) {
-      s_kc[t * (KROW / 4) + p / KPW] = w1;
-      s_kc[t * (KROW / 4) + (p + HALF) / KPW] = w2;
-    }
-    if (moved && c == 0) {
-      s_ks[t * NG + p / 32] = sc1;
-      s_ks[t * NG + (p + HALF) / 32] = sc2;
+  // One lane per PPL = 8 rotation pairs (channels j and j + D/2 for j in
+  // [8m, 8m + 8), m = lane % LPR), LPR = D/16 lanes per row: a 32-channel
+  // group lies in 4 adjacent lanes, so its amax is a local max and two quad
+  // DPP steps, and (INT4) the lane's 8 codes of a half are one packed word.
+  // The lane's cos/sin entries are reloaded only when its row's shift
+  // changes.
+  {
+    constexpr int PPL = 8, LPR = HALF / PPL, RPW2 = 64 / LPR;
+    constexpr int CW = PPL * KB / 8;            // bytes of 8 codes (4 or 2)
+    const int m = lane % LPR, rsub = lane / LPR;
+    int cur_delta = -1;
+    double2 csl[PPL];
+    for (int base = wave * RPW2; base < n_rows; base += 4 * RPW2) {
+      const int tt = base + rsub;
+      const bool valid = tt < n_rows;
+      const int t = lo + min(tt, n_rows - 1);
+      const int d = s_dst[t];
+      const bool moved = valid && d >= 0 && d != r0 + t;
+      const int delta = moved ? r0 + t - d : 0;
+      if (delta != cur_delta) {
+        const double2* tp = a.tab + (size_t)delta * HALF + PPL * m;
+#pragma unroll
+        for (int k = 0; k < PPL; ++k) csl[k] = tp[k];
+        cur_delta = delta;
+      }
+      const uint8_t* krow = reinterpret_cast<const uint8_t*>(s_kc) + t * KROW;
+      uint32_t w1, w2;
+      if constexpr (CW == 4) {
+        w1 = *reinterpret_cast<const uint32_t*>(krow + CW * m);
+        w2 = *reinterpret_cast<const uint32_t*>(krow + KROW / 2 + CW * m);
+      } else {
+        w1 = *reinterpret_cast<const uint16_t*>(krow + CW * m);
+        w2 = *reinterpret_cast<const uint16_t*>(krow + KROW / 2 + CW * m);
+      }
+      const int g1 = (PPL * m) / 32, g2 = (HALF + PPL * m) / 32;
+      const float sc1 = h2f(s_ks[t * NG + g1]), sc2 = h2f(s_ks[t * NG + g2]);
+      float z1[PPL], z2[PPL];
+#pragma unroll
+      for (int k = 0; k < PPL; ++k) {
+        const float x1 = (float)((int)((w1 >> (KB * k)) & KMASK) - KOFF) * sc1;   // exact
+        const float x2 = (float)((int)((w2 >> (KB * k)) & KMASK) - KOFF) * sc2;
+        const double a1 = (double)x1, a2 = (double)x2;
+        z1[k] = h2f(d2h(a1 * csl[k].x - a2 * csl[k].y));
+        z2[k] = h2f(d2h(a2 * csl[k].x + a1 * csl[k].y));
+      }
+      // group scales: amax over the 4 lanes of the group
+      uint32_t am1 = 0u, am2 = 0u;
+#pragma unroll
+      for (int k = 0; k < PPL; ++k) {
+        am1 = max(am1, __float_as_uint(z1[k]) & 0x7FFFFFFFu);
+        am2 = max(am2, __float_as_uint(z2[k]) & 0x7FFFFFFFu);
+      }
+      am1 = max(am1, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)am1, kQuadXor1, 0xF, 0xF, false));
+      am1 = max(am1, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)am1, kQuadXor2, 0xF, 0xF, false));
+      am2 = max(am2, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)am2, kQuadXor1, 0xF, 0xF, false));
+      am2 = max(am2, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)am2, kQuadXor2, 0xF, 0xF, false));
+      const uint16_t sb1 = group_scale_bits<KB>(__uint_as_float(am1));
+      const uint16_t sb2 = group_scale_bits<KB>(__uint_as_float(am2));
+      const float s1 = h2f(sb1), s2 = h2f(sb2);
+      const float r1 = __builtin_amdgcn_rcpf(s1), r2 = __builtin_amdgcn_rcpf(s2);
+      uint32_t o1 = 0u, o2 = 0u;
+#pragma unroll
+      for (int k = 0; k < PPL; ++k) {
+        o1 |= (uint32_t)(quant_code<KB>(z1[k], s1, r1) + KOFF) << (KB * k);
+        o2 |= (uint32_t)(quant_code<KB>(z2[k], s2, r2) + KOFF) << (KB * k);
+      }
+      if (moved) {
+        uint8_t* kw = reinterpret_cast<uint8_t*>(s_kc) + t * KROW;
+        if constexpr (CW == 4) {
+          *reinterpret_cast<uint32_t*>(kw + CW * m) = o1;
+          *reinterpret_cast<uint32_t*>(kw + KROW / 2 + CW * m) = o2;
+        } else {
+          *reinterpret_cast<uint16_t*>(kw + CW * m) = (uint16_t)o1;
+          *reinterpret_cast<uint16_t*>(kw + KROW / 2 + CW * m) = (uint16_t)o2;
+        }
+        if ((m & 3) == 0) {
+          s_ks[t * NG + g1] = sb1;
+          s_ks[t * NG + g2] = sb2;
+        }
+      }
     }
   }
   __syncthreads();
@@ -467,8 +530,8 @@ __global__ __launch_bounds__(256) void k_spill_copy(CompactArgs a) {
   constexpr int KROW = D * KB / 8, VROW = D * VB / 8, NG = D / 32;
   const int cidx = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int mrow = a.s.shared ? 0 : b;
-  if (a.info[4 * mrow + 1] == 0) return;
-  const int M = a.info[4 * mrow + 0];
+  if (a.info[kInfo * mrow + 1] == 0) return;
+  const int M = a.info[kInfo * mrow + 0];
   if (cidx * kCompactRows >= M) return;
   const size_t bg = (size_t)(b * a.s.Hkv + g);
   const int2 si = a.spill_info[bg * a.nchunks + cidx];
@@ -501,7 +564,7 @@ size_t evict_ws_bytes(const Shape& s, int max_evict) {
   const int rows = s.shared ? 1 : s.batch;
   const int nchunks = (s.cap_mid + kCompactRows - 1) / kCompactRows;
   const int spill_rows = max_evict < kCompactRows ? max_evict : kCompactRows;
-  size_t n = align_up((size_t)rows * 4 * 4, 256);
+  size_t n = align_up((size_t)rows * kInfo * 4, 256);
   n += align_up((size_t)rows * s.cap_mid * 4, 256);
   n += align_up((size_t)(max_evict + 1) * (s.D / 2) * 16, 256);
   n += align_up((size_t)s.batch * s.Hkv * nchunks * 8, 256);
@@ -531,7 +594,7 @@ hipError_t launch_evict(const Shape& s, const fade_layer_cache& c, int policy, i
   const int spill_rows = max_evict < kCompactRows ? max_evict : kCompactRows;
   char* w = reinterpret_cast<char*>(ws);
   int32_t* info = reinterpret_cast<int32_t*>(w);
-  w += align_up((size_t)rows * 4 * 4, 256);
+  w += align_up((size_t)rows * kInfo * 4, 256);
   int32_t* map = reinterpret_cast<int32_t*>(w);
   w += align_up((size_t)rows * s.cap_mid * 4, 256);
   double2* tab = reinterpret_cast<double2*>(w);
@@ -586,7 +649,7 @@ hipError_t launch_evict(const Shape& s, const fade_layer_cache& c, int policy, i
 // ---- prefill build -------------------------------------------------------------
 size_t prefill_build_ws_bytes(const Shape& s, int L) {
   const int rows = s.shared ? 1 : s.batch;
-  return align_up((size_t)rows * 4 * 4, 256) + align_up((size_t)rows * (L > 0 ? L : 1) * 4, 256);
+  return align_up((size_t)rows * kInfo * 4, 256) + align_up((size_t)rows * (L > 0 ? L : 1) * 4, 256);
 }
 
 struct BuildArgs {
@@ -597,7 +660,7 @@ struct BuildArgs {
   int L;
   const float* pscores;     // [rows][L] or nullptr
   const int32_t* map;       // [rows][L]
-  const int32_t* info;      // [rows][4]
+  const int32_t* info;      // [rows][kInfo]
   RopeFreqs fr;
 };
 
@@ -616,8 +679,8 @@ __global__ __launch_bounds__(256) void k_build(BuildArgs a) {
   const int g = blockIdx.y, b = blockIdx.z;
   const Shape& s = a.s;
   const int mrow = s.shared ? 0 : b;
-  const int M = a.info[4 * mrow + 0], n_ev = a.info[4 * mrow + 1];
-  const int S = a.info[4 * mrow + 2];
+  const int M = a.info[kInfo * mrow + 0], n_ev = a.info[kInfo * mrow + 1];
+  const int S = a.info[kInfo * mrow + 2];
   const int Mk = M - n_ev;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int p = lane % HALF, sub = lane / HALF, c = p % 32;
@@ -694,9 +757,9 @@ __global__ void k_build_lens(const int32_t* info, int32_t* lens, int batch, int 
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= batch) return;
   const int r = shared ? 0 : b;
-  lens[4 * b + 0] = info[4 * r + 2];
-  lens[4 * b + 1] = info[4 * r + 0] - info[4 * r + 1];
-  lens[4 * b + 2] = info[4 * r + 3];
+  lens[4 * b + 0] = info[kInfo * r + 2];
+  lens[4 * b + 1] = info[kInfo * r + 0] - info[kInfo * r + 1];
+  lens[4 * b + 2] = info[kInfo * r + 3];
   lens[4 * b + 3] = 0;
 }
 
@@ -715,7 +778,7 @@ hipError_t launch_prefill_build(const Shape& s, const fade_layer_cache& c, const
   const int rows = s.shared ? 1 : s.batch;
   char* w = reinterpret_cast<char*>(ws);
   int32_t* info = reinterpret_cast<int32_t*>(w);
-  w += align_up((size_t)rows * 4 * 4, 256);
+  w += align_up((size_t)rows * kInfo * 4, 256);
   int32_t* map = reinterpret_cast<int32_t*>(w);
   SelectArgs sa{};
   sa.scores = scores;
