@@ -39,7 +39,18 @@ __device__ __forceinline__ float d2f_odd(double d) {
   u |= (uint32_t)(back != d);
   return __uint_as_float(u);
 }
-__device__ __forceinline__ uint16_t d2h(double d) { return f2h(d2f_odd(d)); }
+// The same for a float64 headed for fp16, on the bit pattern: clear the 29
+// mantissa bits that float32 lacks (the conversion is then exact) and set the
+// last bit if any of them was set. Magnitudes below float32's normal range
+// land far below fp16's smallest subnormal and still round to a signed zero.
+__device__ __forceinline__ float d2f_odd_h(double d) {
+  const uint64_t u = (uint64_t)__double_as_longlong(d);
+  uint32_t st;   // 1 if any cleared bit was set (a 32-bit min; kept from becoming a 64-bit compare)
+  asm("v_min_u32 %0, 1, %1" : "=v"(st) : "v"((uint32_t)u & 0x1FFFFFFFu));
+  const float f = (float)__longlong_as_double((long long)(u & ~(uint64_t)0x1FFFFFFFu));
+  return __uint_as_float(__float_as_uint(f) | st);
+}
+__device__ __forceinline__ uint16_t d2h(double d) { return f2h(d2f_odd_h(d)); }
 __device__ __forceinline__ uint16_t d2bf(double d) { return f2bf(d2f_odd(d)); }
 
 // ---- wave reductions -------------------------------------------------------
@@ -115,30 +126,45 @@ __device__ __forceinline__ float row_sum_strided(float x) {
 
 // ---- symmetric group quantizer ---------------------------------------------
 // s = fp16_RNE(amax / qmax), q = clamp(RNE(x / s), -qmax, qmax), s == 0 -> q = 0,
-// evaluated without a division:
-//  * qmax = 7: amax * float32(1/7) rounded once to fp16 equals the RNE of the
-//    exact quotient for every finite fp16 amax (the quotient is never closer
-//    to an fp16 midpoint than the product's error); qmax = 1: s = amax.
-//  * x * rcp(s) is within 2^-21 of x / s for |x / s| <= 8, while a quotient
-//    of fp16 values that is not an exact tie lies at least 2^-13 from every
-//    half-integer, so rint gives RNE except at exact ties. A tie is detected
-//    exactly from the residual e = x - k s (one fma, exact for these
-//    operands: 2|e| == s) and moved to the even neighbour.
-// Both facts were checked exhaustively over fp16 operands against exact
-// rational rounding (with the reciprocal off by one ulp either way).
+// stored as the field q + 2^(BITS-1); evaluated without a division:
+//  * scale: for qmax = 7, amax * float32(1/7) rounded once to fp16 equals the
+//    RNE of the exact quotient for every finite fp16 amax; for qmax = 1, s = amax.
+//  * field: with r = rcp(s) (r = 0 when s == 0, which yields q = 0),
+//    a = fma(x, r, 192) rounds x * r to the 2^-16 grid. x * r lies within
+//    2^-21 of x / s, and a quotient of fp16 values is either a half-integer
+//    or at least 2^-13 away from every half-integer, with |x / s| <= 10 (the
+//    bound is reached only for subnormal scales); so a equals the quotient at
+//    a tie and lies on the quotient's side of every half-integer otherwise.
+//    Adding 1.5 * 2^23 + 2^(BITS-1) - 192 rounds that to an integer with
+//    ties to even, leaving the field in the low mantissa bits; fmed3 clamps.
+// All of it was checked exhaustively over fp16 operands against exact
+// rational rounding, with the reciprocal off by one ulp either way.
+constexpr float kFieldBase = 12582912.f;            // 1.5 * 2^23
+constexpr uint32_t kFieldBaseBits = 0x4B400000u;    // its bit pattern
+
 template <int BITS>
 __device__ __forceinline__ uint16_t group_scale_bits(float amax) {
   if constexpr (BITS == 2) return f2h(amax);
   else return f2h(amax * (1.0f / 7.0f));
 }
+__device__ __forceinline__ float quant_recip(float s) { return s != 0.f ? __builtin_amdgcn_rcpf(s) : 0.f; }
+
+// kFieldBaseBits + field of one value.
 template <int BITS>
-__device__ __forceinline__ int quant_code(float x, float s, float r) {
-  constexpr float kQmax = (float)((1 << (BITS - 1)) - 1);
-  float k = rintf(x * r);
-  const float e = fmaf(-k, s, x);
-  const bool tie_odd = (2.f * fabsf(e) == s) && (((int)k & 1) != 0);
-  k = tie_odd ? k + (e > 0.f ? 1.f : -1.f) : k;
-  return s != 0.f ? (int)__builtin_amdgcn_fmed3f(k, -kQmax, kQmax) : 0;
+__device__ __forceinline__ uint32_t quant_field(float x, float r) {
+  constexpr float kOff = (float)(1 << (BITS - 1));
+  constexpr float kQmax = kOff - 1.f;
+  const float a = __builtin_fmaf(x, r, 192.f);
+  const float b = a + (kFieldBase + kOff - 192.f);
+  return __float_as_uint(__builtin_amdgcn_fmed3f(b, kFieldBase + kOff - kQmax, kFieldBase + kOff + kQmax));
+}
+// Sum over k < N of kFieldBaseBits << (BITS * k), modulo 2^32: subtracting
+// it from the sum of quant_field(x_k) << (BITS * k) leaves the packed fields.
+template <int BITS, int N>
+__device__ __forceinline__ constexpr uint32_t field_bias() {
+  uint32_t c = 0u;
+  for (int k = 0; k < N; ++k) c += kFieldBaseBits << (BITS * k);
+  return c;
 }
 
 // 32 values of one group (exact float copies of fp16 values) -> packed codes
@@ -146,21 +172,16 @@ __device__ __forceinline__ int quant_code(float x, float s, float r) {
 // byte stream) and the fp16 scale.
 template <int BITS>
 __device__ __forceinline__ void quant_group32(const float* x, uint32_t* packed, uint16_t& scale) {
-  constexpr int kOff = 1 << (BITS - 1);
+  constexpr int kPerWord = 32 / BITS;
   float amax = 0.f;
 #pragma unroll
   for (int c = 0; c < 32; ++c) amax = fmaxf(amax, fabsf(x[c]));
   const uint16_t sb = group_scale_bits<BITS>(amax);
-  const float s = h2f(sb);
-  const float r = __builtin_amdgcn_rcpf(s);
+  const float r = quant_recip(h2f(sb));
 #pragma unroll
-  for (int w = 0; w < BITS; ++w) packed[w] = 0u;
+  for (int w = 0; w < BITS; ++w) packed[w] = 0u - field_bias<BITS, kPerWord>();
 #pragma unroll
-  for (int c = 0; c < 32; ++c) {
-    const uint32_t u = (uint32_t)(quant_code<BITS>(x[c], s, r) + kOff);
-    constexpr int kPerWord = 32 / BITS;
-    packed[c / kPerWord] |= u << ((c % kPerWord) * BITS);
-  }
+  for (int c = 0; c < 32; ++c) packed[c / kPerWord] += quant_field<BITS>(x[c], r) << ((c % kPerWord) * BITS);
   scale = sb;
 }
 

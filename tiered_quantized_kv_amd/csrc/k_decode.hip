@@ -4,7 +4,7 @@
 // softmax over sinks, middle and recent tokens).
 //
 // Work decomposition (one launch per layer):
-//   k_decode_tiers  grid (nsplit, Hkv, batch), 256 threads. Split 0 streams
+//   k_decode_tiers  nsplit x Hkv x batch workgroups, 256 threads. Split 0 streams
 //                   the FP16 tier (sinks + recent ring); split s >= 1 streams
 //                   middle rows [(s-1)*chunk, s*chunk). A workgroup serves
 //                   all n_rep query heads of its KV head, so every packed
@@ -48,22 +48,25 @@ struct DecodeArgs {
   const uint16_t* q;
   float* part;        // [B, Hq, nsplit, D + 2]
   float* raw;         // [B, Hq, cap_T] (log2-domain scores) or nullptr
-  int Hkv, n_sink, ring, cap_mid, cap_T, chunk, nsplit;
+  int batch, Hkv, n_sink, ring, cap_mid, cap_T, chunk, nsplit;
   float qk_scale;     // log2(e) / sqrt(D)
 };
 
 constexpr int kThreads = 256;
+constexpr float kLazyMax = 3.f;
 constexpr int kSub = 64;          // tokens per wave sub-chunk (one per lane)
+
+constexpr long kDecodeMiddleWGs = 1024;   // middle workgroups the split aims for
 
 int decode_chunk(const Shape& s) {
   // Middle rows per split: the largest power-of-two multiple of four waves x
-  // one sub-chunk (up to 4096) that still gives about 1024 middle
+  // one sub-chunk (up to 4096) that still gives about kDecodeMiddleWGs middle
   // workgroups, so each wave streams several sub-chunks with its loads
   // prefetched, and the grid still covers the chip.
   const long pairs = (long)s.batch * s.Hkv;
   const int unit = 4 * kSub;
   int chunk = 16 * unit;
-  while (chunk > unit && pairs * ((s.cap_mid + chunk - 1) / chunk) < 1024) chunk /= 2;
+  while (chunk > unit && pairs * ((s.cap_mid + chunk - 1) / chunk) < kDecodeMiddleWGs) chunk /= 2;
   return chunk;
 }
 
@@ -91,6 +94,20 @@ __device__ __forceinline__ f16x4 as_h4(uint32_t lo, uint32_t hi) { return __buil
 template <int CBSZ>
 __device__ __forceinline__ f32x4 mfma4(f16x4 a, f16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_4x4x4f16(a, b, c, CBSZ, 0, 0);
+}
+// ABID picks which block of each broadcast group supplies A, so one register
+// can hold the A operands of 2^CBSZ different products, one per block. abid
+// must fold to a constant (unrolled loops).
+template <int CBSZ>
+__device__ __forceinline__ f32x4 mfma4_ab(f16x4 a, f16x4 b, f32x4 c, int abid) {
+#define FADE_AB(i) \
+  case i: return __builtin_amdgcn_mfma_f32_4x4x4f16(a, b, c, CBSZ, (i) & ((1 << CBSZ) - 1), 0);
+  switch (abid) {
+    FADE_AB(0) FADE_AB(1) FADE_AB(2) FADE_AB(3) FADE_AB(4) FADE_AB(5) FADE_AB(6) FADE_AB(7)
+    FADE_AB(8) FADE_AB(9) FADE_AB(10) FADE_AB(11) FADE_AB(12) FADE_AB(13) FADE_AB(14)
+    default: return __builtin_amdgcn_mfma_f32_4x4x4f16(a, b, c, CBSZ, 15 & ((1 << CBSZ) - 1), 0);
+  }
+#undef FADE_AB
 }
 
 // K codes as exact signed fp16 values (the bias trick: a b-bit field f at
@@ -165,11 +182,11 @@ struct TierLayout {
   static constexpr int wml_bytes = 4 * 2 * HQ4 * 4 * 4;           // per-wave (max, sum)
   static constexpr int head_bytes = (q_bytes + kf_bytes + wml_bytes + 15) / 16 * 16;
   static constexpr int pw_bytes = HQ4 * NG * 4 * PW * 2;          // weights [hq][g][row][token]
-  static constexpr int vt_bytes = U * PW * 2;                     // V units [unit][token]
+  static constexpr int vt_bytes = 2 * U * PW * 2;                 // V units [unit][token], then >> 8
   static constexpr int wacc_bytes = HQ4 * 4 * D * 4;              // per-wave output [head][D]
   static constexpr int wave_bytes = ((pw_bytes + vt_bytes > wacc_bytes ? pw_bytes + vt_bytes : wacc_bytes) + 15) / 16 * 16;
   static constexpr int total = head_bytes + 4 * wave_bytes;
-  static_assert(16 * HQ4 * 4 * 4 <= pw_bytes, "fp16-tier weights fit the weight tile");
+  static_assert(64 * HQ4 * 4 * 4 <= pw_bytes + vt_bytes, "fp16-tier weights fit the wave tiles");
 };
 
 template <int D, int NREP, int KB, int VB, bool QBF>
@@ -188,7 +205,13 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
   float* wml = kf + HQ4 * 4;                                                 // [4][2][HQ4 * 4]
   unsigned char* wreg = smem + Lay::head_bytes;
 
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  // 1-D grid, middle splits first (split 1 of every (sequence, KV head),
+  // then split 2, ...) and the FP16 tier last: the long middle workgroups are
+  // dealt evenly over the CUs before the short ones fill the gaps.
+  const int n_pairs = a.batch * a.Hkv;
+  const int gsplit = blockIdx.x / n_pairs, pair = blockIdx.x - gsplit * n_pairs;
+  const int split = gsplit + 1 < a.nsplit ? gsplit + 1 : 0;
+  const int g = pair % a.Hkv, b = pair / a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int Hq = a.Hkv * NREP;
   const int32_t* L = a.lens + 4 * b;
@@ -222,7 +245,11 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
     uint32_t ks[NG / 2];
     uint32_t vs[NG / 2];
   };
-  auto issue = [&](Loads& ld, int base) {
+  // One register buffer per wave: the K part of the next sub-chunk is loaded
+  // as soon as QK^T has consumed the current one, the V part as soon as the
+  // current V is in the LDS tile, so each part's latency overlaps the rest
+  // of the sub-chunk's work.
+  auto issue_k = [&](Loads& ld, int base) {
     const int t = min(base + lane, n_tok - 1);
     const uint4* kp = reinterpret_cast<const uint4*>(krow0 + (size_t)t * KROW);
 #pragma unroll
@@ -230,6 +257,15 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
       const uint4 w = kp[i];
       ld.k[4 * i] = w.x; ld.k[4 * i + 1] = w.y; ld.k[4 * i + 2] = w.z; ld.k[4 * i + 3] = w.w;
     }
+    if constexpr (NG == 4) {
+      const uint2 k2 = *reinterpret_cast<const uint2*>(ks0 + (size_t)t * NG);
+      ld.ks[0] = k2.x; ld.ks[1] = k2.y;
+    } else {
+      ld.ks[0] = *reinterpret_cast<const uint32_t*>(ks0 + (size_t)t * NG);
+    }
+  };
+  auto issue_v = [&](Loads& ld, int base) {
+    const int t = min(base + lane, n_tok - 1);
     const uint4* vp = reinterpret_cast<const uint4*>(vrow0 + (size_t)t * VROW);
 #pragma unroll
     for (int i = 0; i < VW / 4; ++i) {
@@ -237,17 +273,17 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
       ld.v[4 * i] = w.x; ld.v[4 * i + 1] = w.y; ld.v[4 * i + 2] = w.z; ld.v[4 * i + 3] = w.w;
     }
     if constexpr (NG == 4) {
-      const uint2 k2 = *reinterpret_cast<const uint2*>(ks0 + (size_t)t * NG);
       const uint2 v2 = *reinterpret_cast<const uint2*>(vs0 + (size_t)t * NG);
-      ld.ks[0] = k2.x; ld.ks[1] = k2.y;
       ld.vs[0] = v2.x; ld.vs[1] = v2.y;
     } else {
-      ld.ks[0] = *reinterpret_cast<const uint32_t*>(ks0 + (size_t)t * NG);
       ld.vs[0] = *reinterpret_cast<const uint32_t*>(vs0 + (size_t)t * NG);
     }
   };
-  Loads nxt;
-  if (!fpt && wave * kSub < n_tok) issue(nxt, wave * kSub);
+  Loads cur;
+  if (!fpt && wave * kSub < n_tok) {
+    issue_k(cur, wave * kSub);
+    issue_v(cur, wave * kSub);
+  }
 
   // ---- query fragments ----
   const uint16_t* qrow = a.q + (size_t)(b * Hq + g * NREP) * D;   // NREP consecutive heads
@@ -286,7 +322,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
 
   float* rawb = a.raw ? a.raw + (size_t)(b * Hq + g * NREP) * a.cap_T : nullptr;
   uint16_t* pw = reinterpret_cast<uint16_t*>(wreg + wave * Lay::wave_bytes);   // [HQ4][NG][4][PW]
-  uint16_t* vt = pw + Lay::pw_bytes / 2;                                       // [U][PW]
+  uint16_t* vt = pw + Lay::pw_bytes / 2;                                       // [2][U][PW]
   const uint32_t* qf32 = reinterpret_cast<const uint32_t*>(qf);
 
   float m_run[HQ4 * 4], l_lane[HQ4 * 4];
@@ -307,7 +343,11 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
     for (int h = 0; h < HQ4 * 4; ++h) {
       p[h] = 0.f;
       if (h >= NREP) continue;
-      if (__any(s2[h] > m_run[h])) {              // wave-uniform
+      // The reference max is raised only when a score exceeds it by more
+      // than kLazyMax (log2 units): weights stay below 2^kLazyMax, well inside
+      // fp16 for the weight tile, and the rescale is rare after the first
+      // sub-chunk.
+      if (__any(s2[h] > m_run[h] + kLazyMax)) {   // wave-uniform
         const float mx = wave_max_u(s2[h]);
         const float alpha = __builtin_amdgcn_exp2f(m_run[h] - mx);
         l_lane[h] *= alpha;
@@ -324,7 +364,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
     // ---------------- packed middle tier ----------------
     // PV lane constants: channel 64 sg + lane, its 16-bit unit and field.
     int vu[NSIG];
-    uint32_t vsh[NSIG], vmask[NSIG];
+    uint32_t vmask[NSIG];
     f16x2 vsub[NSIG];
     float vscale[NSIG];
 #pragma unroll
@@ -332,18 +372,31 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
       const int c = 64 * sg + lane;
       vu[sg] = c / CPU;
       const int bit = (c % CPU) * VB;
-      const int sh = bit + VB <= 10 ? 0 : (VB == 2 ? 10 : 8);
+      // fields that do not fit below bit 10 of a half are read from the copy
+      // of the tile shifted right by 8
+      const int sh = bit + VB <= 10 ? 0 : 8;
       const int pos = bit - sh;
-      vsh[sg] = (uint32_t)sh;
+      vu[sg] += sh ? U : 0;
       vmask[sg] = (((1u << VB) - 1u) << pos) * 0x00010001u;
       const f16 sub = (f16)(1024.f + (float)(kOffV << pos));
       vsub[sg] = f16x2{sub, sub};
       vscale[sg] = ldexpf(1.f, -pos);
     }
     const KeyConst kcon = key_const<KB>();
+    // Query fragments in registers: lane 4j + r holds row r (head) of step
+    // 16 i + j, broadcast with ABID = j.
+    constexpr int NQR = (NI + 15) / 16;
+    f16x4 qreg[HQ4][NQR];
+#pragma unroll
+    for (int hq = 0; hq < HQ4; ++hq)
+#pragma unroll
+      for (int i = 0; i < NQR; ++i) {
+        const int sl = min(16 * i + (lane >> 2), NI - 1);
+        const uint2 av = *reinterpret_cast<const uint2*>(qf32 + ((hq * NI + sl) * 4 + (lane & 3)) * 2);
+        qreg[hq][i] = as_h4(av.x, av.y);
+      }
     for (int base = wave * kSub; base < n_tok; base += 4 * kSub) {
-      const Loads cur = nxt;
-      if (base + 4 * kSub < n_tok) issue(nxt, base + 4 * kSub);
+      const bool more = base + 4 * kSub < n_tok;   // wave-uniform
       const int t = base + lane;
       const bool valid = t < n_tok;
       // ---- QK^T ----
@@ -360,10 +413,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
           const int sidx = 8 * gi + si;
           const f16x4 bop = key_operand<KB>(cur.k, sidx, kcon);
 #pragma unroll
-          for (int hq = 0; hq < HQ4; ++hq) {
-            const uint2 av = *reinterpret_cast<const uint2*>(qf32 + ((hq * NI + sidx) * 4 + (lane & 3)) * 2);
-            d[hq] = mfma4<4>(as_h4(av.x, av.y), bop, d[hq]);
-          }
+          for (int hq = 0; hq < HQ4; ++hq) d[hq] = mfma4_ab<4>(qreg[hq][sidx >> 4], bop, d[hq], sidx & 15);
         }
         const uint32_t sw = cur.ks[gi >> 1];
         const float scl = h2f((uint16_t)((gi & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
@@ -372,6 +422,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) s2[4 * hq + i] = fmaf(scl, d[hq][i], s2[4 * hq + i]);
       }
+      if (more) issue_k(cur, base + 4 * kSub);
 #pragma unroll
       for (int h = 0; h < HQ4 * 4; ++h) {
         s2[h] = valid ? s2[h] * kf[h] : -INFINITY;
@@ -390,25 +441,44 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
           pw[((h / 4 * NG + gi) * 4 + h % 4) * PW + lane] = f2h(p[h] * sv);
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        vt[u * PW + lane] = (uint16_t)((u & 1) ? (cur.v[u >> 1] >> 16) : (cur.v[u >> 1] & 0xFFFFu));
+      for (int u = 0; u < U; ++u) {
+        const uint32_t w = cur.v[u >> 1], wh = (w >> 8) & 0x00FF00FFu;
+        vt[u * PW + lane] = (uint16_t)((u & 1) ? (w >> 16) : (w & 0xFFFFu));
+        vt[(U + u) * PW + lane] = (uint16_t)((u & 1) ? (wh >> 16) : (wh & 0xFFFFu));
+      }
+      if (more) issue_v(cur, base + 4 * kSub);
       wave_lds_sync();
       // ---- PV ----
+      // Weight fragments: step st (tokens 4 st .. 4 st + 3) of column group
+      // sg takes A from block st % 8 of each half-wave (ABID), so lane
+      // 4 j + r (j < 8) holds head r's weights of tokens 32 i + 4 j + [0, 4)
+      // for the group of its half-wave, i = st / 8.
+      f16x4 preg[NSIG][kSub / 32][HQ4];
 #pragma unroll
       for (int sg = 0; sg < NSIG; ++sg) {
         const int gsel = 2 * sg + (lane >> 5);       // group of this lane's column block
 #pragma unroll
-        for (int t8 = 0; t8 < kSub / 8; ++t8) {
-          const uint4 x = *reinterpret_cast<const uint4*>(vt + vu[sg] * PW + 8 * t8);
-          const uint32_t y0 = h2_bits(as_h2(and_or(x.x >> vsh[sg], vmask[sg], 0x64006400u)) - vsub[sg]);
-          const uint32_t y1 = h2_bits(as_h2(and_or(x.y >> vsh[sg], vmask[sg], 0x64006400u)) - vsub[sg]);
-          const uint32_t y2 = h2_bits(as_h2(and_or(x.z >> vsh[sg], vmask[sg], 0x64006400u)) - vsub[sg]);
-          const uint32_t y3 = h2_bits(as_h2(and_or(x.w >> vsh[sg], vmask[sg], 0x64006400u)) - vsub[sg]);
+        for (int i = 0; i < kSub / 32; ++i)
 #pragma unroll
           for (int hq = 0; hq < HQ4; ++hq) {
-            const uint4 av = *reinterpret_cast<const uint4*>(pw + ((hq * NG + gsel) * 4 + (lane & 3)) * PW + 8 * t8);
-            o[sg][hq] = mfma4<3>(as_h4(av.x, av.y), as_h4(y0, y1), o[sg][hq]);
-            o[sg][hq] = mfma4<3>(as_h4(av.z, av.w), as_h4(y2, y3), o[sg][hq]);
+            const uint2 av = *reinterpret_cast<const uint2*>(
+                pw + ((hq * NG + gsel) * 4 + (lane & 3)) * PW + 32 * i + 4 * ((lane >> 2) & 7));
+            preg[sg][i][hq] = as_h4(av.x, av.y);
+          }
+      }
+#pragma unroll
+      for (int sg = 0; sg < NSIG; ++sg) {
+#pragma unroll
+        for (int t8 = 0; t8 < kSub / 8; ++t8) {
+          const uint4 x = *reinterpret_cast<const uint4*>(vt + vu[sg] * PW + 8 * t8);
+          const uint32_t y0 = h2_bits(as_h2(and_or(x.x, vmask[sg], 0x64006400u)) - vsub[sg]);
+          const uint32_t y1 = h2_bits(as_h2(and_or(x.y, vmask[sg], 0x64006400u)) - vsub[sg]);
+          const uint32_t y2 = h2_bits(as_h2(and_or(x.z, vmask[sg], 0x64006400u)) - vsub[sg]);
+          const uint32_t y3 = h2_bits(as_h2(and_or(x.w, vmask[sg], 0x64006400u)) - vsub[sg]);
+#pragma unroll
+          for (int hq = 0; hq < HQ4; ++hq) {
+            o[sg][hq] = mfma4_ab<3>(preg[sg][t8 >> 2][hq], as_h4(y0, y1), o[sg][hq], (2 * t8) & 7);
+            o[sg][hq] = mfma4_ab<3>(preg[sg][t8 >> 2][hq], as_h4(y2, y3), o[sg][hq], (2 * t8 + 1) & 7);
           }
         }
       }
@@ -422,71 +492,83 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
         for (int i = 0; i < 4; ++i) o[sg][hq][i] *= vscale[sg];
   } else {
     // ---------------- FP16 tier: sinks then the recent ring ----------------
-    // 16-token slices, one per wave at a time (the tier holds at most
-    // n_sink + recent_window + 1 tokens): QK^T on the MFMA with lanes 16..63
-    // repeating lanes 0..15, PV on VALU with one lane per CPL channels.
+    // Each wave takes one slice of up to 64 consecutive tokens (a quarter of
+    // the tier per round), one token per lane: QK^T on the MFMA (lanes past
+    // the slice repeat its last token), then PV on VALU with one lane per CPL
+    // channels, its V elements loaded for up to 32 tokens at a time into the
+    // registers the keys no longer need.
     constexpr int CPL = D / 64;
     const int fp_slots = a.n_sink + a.ring;
     const uint16_t* fk = a.fp_k + bg * fp_slots * D;
     const uint16_t* fv = a.fp_v + bg * fp_slots * D;
-    float* pf = reinterpret_cast<float*>(pw);               // [16 tokens][HQ4 * 4] weights
+    float* pf = reinterpret_cast<float*>(pw);               // [64 tokens][HQ4 * 4] weights
     auto slot_of = [&](int tt) { return tt < S ? tt : a.n_sink + (rhead + (tt - S)) % a.ring; };
-    for (int base = wave * 16; base < n_tok; base += 64) {
-      const int t = base + (lane & 15);
-      const bool valid = lane < 16 && t < n_tok;
-      const uint4* kp = reinterpret_cast<const uint4*>(fk + (size_t)slot_of(min(t, n_tok - 1)) * D);
-      uint32_t w[D / 2];
+    const int sz = min(kSub, (n_tok + 3) / 4);             // tokens per wave slice
+    for (int base = wave * sz; base < n_tok; base += 4 * sz) {
+      const int ns = min(sz, n_tok - base);              // wave-uniform
+      const bool valid = lane < ns;
+      f32x4 d0[HQ4], d1[HQ4];
+      {
+        const uint4* kp = reinterpret_cast<const uint4*>(fk + (size_t)slot_of(base + min(lane, ns - 1)) * D);
+        uint32_t w[D / 2];
 #pragma unroll
-      for (int i = 0; i < D / 8; ++i) {
-        const uint4 x = kp[i];
-        w[4 * i] = x.x; w[4 * i + 1] = x.y; w[4 * i + 2] = x.z; w[4 * i + 3] = x.w;
-      }
-      f32x4 d[HQ4];
+        for (int i = 0; i < D / 8; ++i) {
+          const uint4 x = kp[i];
+          w[4 * i] = x.x; w[4 * i + 1] = x.y; w[4 * i + 2] = x.z; w[4 * i + 3] = x.w;
+        }
 #pragma unroll
-      for (int hq = 0; hq < HQ4; ++hq) d[hq] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int hq = 0; hq < HQ4; ++hq) d0[hq] = d1[hq] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int sidx = 0; sidx < NI; ++sidx) {
+        for (int sidx = 0; sidx < NI; ++sidx) {
 #pragma unroll
-        for (int hq = 0; hq < HQ4; ++hq) {
-          const uint2 av = *reinterpret_cast<const uint2*>(qf32 + ((hq * NI + sidx) * 4 + (lane & 3)) * 2);
-          d[hq] = mfma4<4>(as_h4(av.x, av.y), as_h4(w[2 * sidx], w[2 * sidx + 1]), d[hq]);
+          for (int hq = 0; hq < HQ4; ++hq) {
+            const uint2 av = *reinterpret_cast<const uint2*>(qf32 + ((hq * NI + sidx) * 4 + (lane & 3)) * 2);
+            if (sidx & 1) d1[hq] = mfma4<4>(as_h4(av.x, av.y), as_h4(w[2 * sidx], w[2 * sidx + 1]), d1[hq]);
+            else d0[hq] = mfma4<4>(as_h4(av.x, av.y), as_h4(w[2 * sidx], w[2 * sidx + 1]), d0[hq]);
+          }
         }
       }
+      constexpr int VB32 = 32;
+      uint32_t vv[VB32];
+      auto load_v = [&](int g0, int nt) {
+#pragma unroll
+        for (int k = 0; k < VB32; ++k) {
+          const uint16_t* vr = fv + (size_t)slot_of(base + g0 + min(k, nt - 1)) * D;
+          if constexpr (CPL == 2) vv[k] = *reinterpret_cast<const uint32_t*>(vr + 2 * lane);
+          else vv[k] = vr[lane];
+        }
+      };
+      load_v(0, min(VB32, ns));
       float s2[HQ4 * 4];
-      const int pos = t < S ? t : S + M + (t - S);
+      const int tv = base + lane;
+      const int pos = tv < S ? tv : S + M + (tv - S);
 #pragma unroll
       for (int h = 0; h < HQ4 * 4; ++h) {
-        s2[h] = valid ? d[h / 4][h % 4] * kf[h] : -INFINITY;
+        s2[h] = valid ? (d0[h / 4][h % 4] + d1[h / 4][h % 4]) * kf[h] : -INFINITY;
         if (h < NREP && rawb && valid) rawb[(size_t)h * a.cap_T + pos] = s2[h];
       }
       float p[HQ4 * 4];
       softmax_step(s2, p, valid);
-      if (lane < 16) {
 #pragma unroll
-        for (int h = 0; h < HQ4 * 4; ++h) pf[lane * HQ4 * 4 + h] = p[h];
-      }
+      for (int h = 0; h < HQ4 * 4; ++h) pf[lane * HQ4 * 4 + h] = p[h];
       wave_lds_sync();
-      const int nt = min(16, n_tok - base);              // wave-uniform
-      uint32_t vv[16];
+      for (int g0 = 0; g0 < ns; g0 += VB32) {
+        const int nt = min(VB32, ns - g0);               // wave-uniform
+        if (g0 > 0) load_v(g0, nt);
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const uint16_t* vr = fv + (size_t)slot_of(base + min(k, nt - 1)) * D;
-        if constexpr (CPL == 2) vv[k] = *reinterpret_cast<const uint32_t*>(vr + 2 * lane);
-        else vv[k] = vr[lane];
-      }
+        for (int k = 0; k < VB32; ++k) {
+          if (k < nt) {
+            const float v0 = h2f((uint16_t)(vv[k] & 0xFFFFu)), v1 = h2f((uint16_t)(vv[k] >> 16));
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        if (k < nt) {
-          const float v0 = h2f((uint16_t)(vv[k] & 0xFFFFu)), v1 = h2f((uint16_t)(vv[k] >> 16));
+            for (int hq = 0; hq < HQ4; ++hq) {
+              const float4 pq = *reinterpret_cast<const float4*>(pf + (g0 + k) * HQ4 * 4 + 4 * hq);
+              const float pp[4] = {pq.x, pq.y, pq.z, pq.w};
 #pragma unroll
-          for (int hq = 0; hq < HQ4; ++hq) {
-            const float4 pq = *reinterpret_cast<const float4*>(pf + k * HQ4 * 4 + 4 * hq);
-            const float pp[4] = {pq.x, pq.y, pq.z, pq.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              // o[0] holds channel CPL * lane, o[1] (D = 128) channel CPL * lane + 1
-              o[0][hq][i] = fmaf(pp[i], v0, o[0][hq][i]);
-              if constexpr (CPL == 2) o[NSIG - 1][hq][i] = fmaf(pp[i], v1, o[NSIG - 1][hq][i]);
+              for (int i = 0; i < 4; ++i) {
+                // o[0] holds channel CPL * lane, o[1] (D = 128) channel CPL * lane + 1
+                o[0][hq][i] = fmaf(pp[i], v0, o[0][hq][i]);
+                if constexpr (CPL == 2) o[NSIG - 1][hq][i] = fmaf(pp[i], v1, o[NSIG - 1][hq][i]);
+              }
             }
           }
         }
@@ -669,6 +751,7 @@ hipError_t launch_decode(const Shape& s, const fade_layer_cache& c, const void* 
   a.q = reinterpret_cast<const uint16_t*>(q);
   a.part = part;
   a.raw = tok_attn ? raw : nullptr;
+  a.batch = s.batch;
   a.Hkv = s.Hkv;
   a.n_sink = s.n_sink;
   a.ring = s.ring;
@@ -677,7 +760,7 @@ hipError_t launch_decode(const Shape& s, const fade_layer_cache& c, const void* 
   a.chunk = chunk;
   a.nsplit = nsplit;
   a.qk_scale = kLog2e / sqrtf((float)s.D);
-  const dim3 grid(nsplit, s.Hkv, s.batch);
+  const dim3 grid(nsplit * s.Hkv * s.batch);
   if (s.D == 128) {
     if (q_bf16) dispatch_rep<128, true>(s.n_rep, s.kb, s.vb, a, grid, st);
     else dispatch_rep<128, false>(s.n_rep, s.kb, s.vb, a, grid, st);

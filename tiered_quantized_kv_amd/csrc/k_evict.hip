@@ -247,13 +247,12 @@ __device__ __forceinline__ uint32_t group_or(uint32_t x) {
 
 // The group quantizer with one channel per lane: the 32 channels of a group
 // are the lanes of one half-wave (channel = lane % 32). Same arithmetic as
-// quant_group32 (group_scale_bits, quant_code); the amax is an unsigned max
+// quant_group32 (group_scale_bits, quant_field); the amax is an unsigned max
 // of the non-negative float bits across the half-wave. Returns the packed word
 // that holds this lane's channel (in every lane of the word's lane group) and
 // the scale bits.
 template <int BITS>
 __device__ __forceinline__ uint32_t quant_lane(float x, int c, uint16_t& scale) {
-  constexpr int kOff = 1 << (BITS - 1);
   uint32_t m = __float_as_uint(x) & 0x7FFFFFFFu;
   m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, kRowRor1, 0xF, 0xF, false));
   m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, kRowRor2, 0xF, 0xF, false));
@@ -261,11 +260,31 @@ __device__ __forceinline__ uint32_t quant_lane(float x, int c, uint16_t& scale) 
   m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, kRowRor8, 0xF, 0xF, false));
   m = max(m, (uint32_t)__shfl_xor((int)m, 16));
   const uint16_t sb = group_scale_bits<BITS>(__uint_as_float(m));
-  const float s = h2f(sb);
-  const int q = quant_code<BITS>(x, s, __builtin_amdgcn_rcpf(s));
+  const uint32_t q = quant_field<BITS>(x, quant_recip(h2f(sb))) - kFieldBaseBits;
   constexpr int kPerWord = 32 / BITS;
   scale = sb;
-  return group_or<kPerWord>((uint32_t)(q + kOff) << ((c % kPerWord) * BITS));
+  return group_or<kPerWord>(q << ((c % kPerWord) * BITS));
+}
+
+// The 8 codes of a packed word (BITS = 4: one dword, BITS = 2: the low 16
+// bits) as exact floats (code - offset) * scale; at 4 bits the even and odd
+// nibbles are split into bytes so that each converts in one instruction.
+template <int BITS>
+__device__ __forceinline__ void dequant8(uint32_t w, float sc, float* x) {
+  constexpr int kOff = 1 << (BITS - 1);
+  const float nb = -(float)kOff * sc;             // exact; fma(code, sc, nb) is exact too
+  if constexpr (BITS == 4) {
+    uint32_t ev = w & 0x0F0F0F0Fu, od = (w >> 4) & 0x0F0F0F0Fu;
+    asm("" : "+v"(ev), "+v"(od));   // keeps the byte conversions from becoming bit-field extracts
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = __builtin_fmaf((float)((ev >> (8 * j)) & 0xFFu), sc, nb);
+      x[2 * j + 1] = __builtin_fmaf((float)((od >> (8 * j)) & 0xFFu), sc, nb);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = __builtin_fmaf((float)((w >> (BITS * k)) & ((1u << BITS) - 1u)), sc, nb);
+  }
 }
 
 // Rotation of a key pair by the float64 (cos, sin) of a shift, rounded once
@@ -294,8 +313,6 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
   constexpr int NG = D / 32;
   constexpr int KROW = D * KB / 8, VROW = D * VB / 8;
   constexpr int CH = kCompactRows;
-  constexpr uint32_t KMASK = (1u << KB) - 1u;
-  constexpr int KOFF = 1 << (KB - 1);
   __shared__ __align__(16) uint32_t s_kc[CH * KROW / 4];
   __shared__ __align__(16) uint32_t s_vc[CH * VROW / 4];
   __shared__ __align__(16) uint16_t s_ks[CH * NG];
@@ -434,36 +451,36 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
         w2 = *reinterpret_cast<const uint16_t*>(krow + KROW / 2 + CW * m);
       }
       const int g1 = (PPL * m) / 32, g2 = (HALF + PPL * m) / 32;
-      const float sc1 = h2f(s_ks[t * NG + g1]), sc2 = h2f(s_ks[t * NG + g2]);
-      float z1[PPL], z2[PPL];
+      float x1[PPL], x2[PPL];
+      dequant8<KB>(w1, h2f(s_ks[t * NG + g1]), x1);
+      dequant8<KB>(w2, h2f(s_ks[t * NG + g2]), x2);
+      f16 z1[PPL], z2[PPL];
+      float am1 = 0.f, am2 = 0.f;
 #pragma unroll
       for (int k = 0; k < PPL; ++k) {
-        const float x1 = (float)((int)((w1 >> (KB * k)) & KMASK) - KOFF) * sc1;   // exact
-        const float x2 = (float)((int)((w2 >> (KB * k)) & KMASK) - KOFF) * sc2;
-        const double a1 = (double)x1, a2 = (double)x2;
-        z1[k] = h2f(d2h(a1 * csl[k].x - a2 * csl[k].y));
-        z2[k] = h2f(d2h(a2 * csl[k].x + a1 * csl[k].y));
+        const double a1 = (double)x1[k], a2 = (double)x2[k];
+        const float f1 = d2f_odd_h(a1 * csl[k].x - a2 * csl[k].y);
+        const float f2 = d2f_odd_h(a2 * csl[k].x + a1 * csl[k].y);
+        z1[k] = (f16)f1;
+        z2[k] = (f16)f2;
+        // fp16 rounding is monotonic: the group amax of the rounded values is
+        // the rounding of the amax
+        am1 = fmaxf(am1, fabsf(f1));
+        am2 = fmaxf(am2, fabsf(f2));
       }
       // group scales: amax over the 4 lanes of the group
-      uint32_t am1 = 0u, am2 = 0u;
+      am1 = fmaxf(am1, dpp_f<kQuadXor1>(am1));
+      am1 = fmaxf(am1, dpp_f<kQuadXor2>(am1));
+      am2 = fmaxf(am2, dpp_f<kQuadXor1>(am2));
+      am2 = fmaxf(am2, dpp_f<kQuadXor2>(am2));
+      const uint16_t sb1 = group_scale_bits<KB>(h2f(f2h(am1)));
+      const uint16_t sb2 = group_scale_bits<KB>(h2f(f2h(am2)));
+      const float r1 = quant_recip(h2f(sb1)), r2 = quant_recip(h2f(sb2));
+      uint32_t o1 = 0u - field_bias<KB, PPL>(), o2 = o1;
 #pragma unroll
       for (int k = 0; k < PPL; ++k) {
-        am1 = max(am1, __float_as_uint(z1[k]) & 0x7FFFFFFFu);
-        am2 = max(am2, __float_as_uint(z2[k]) & 0x7FFFFFFFu);
-      }
-      am1 = max(am1, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)am1, kQuadXor1, 0xF, 0xF, false));
-      am1 = max(am1, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)am1, kQuadXor2, 0xF, 0xF, false));
-      am2 = max(am2, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)am2, kQuadXor1, 0xF, 0xF, false));
-      am2 = max(am2, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)am2, kQuadXor2, 0xF, 0xF, false));
-      const uint16_t sb1 = group_scale_bits<KB>(__uint_as_float(am1));
-      const uint16_t sb2 = group_scale_bits<KB>(__uint_as_float(am2));
-      const float s1 = h2f(sb1), s2 = h2f(sb2);
-      const float r1 = __builtin_amdgcn_rcpf(s1), r2 = __builtin_amdgcn_rcpf(s2);
-      uint32_t o1 = 0u, o2 = 0u;
-#pragma unroll
-      for (int k = 0; k < PPL; ++k) {
-        o1 |= (uint32_t)(quant_code<KB>(z1[k], s1, r1) + KOFF) << (KB * k);
-        o2 |= (uint32_t)(quant_code<KB>(z2[k], s2, r2) + KOFF) << (KB * k);
+        o1 += quant_field<KB>((float)z1[k], r1) << (KB * k);
+        o2 += quant_field<KB>((float)z2[k], r2) << (KB * k);
       }
       if (moved) {
         uint8_t* kw = reinterpret_cast<uint8_t*>(s_kc) + t * KROW;
