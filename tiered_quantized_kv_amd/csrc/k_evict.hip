@@ -84,9 +84,13 @@ struct SelectArgs {
   int shared, batch;
   // prefill mode
   int L, n_sink, W;
+  int lds_keys;          // rows with M <= lds_keys keep their ordered keys in LDS
 };
 
+constexpr int kSelLdsKeys = 12288;   // 48 KB of LDS keys per row at most
+
 __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
+  extern __shared__ uint32_t skey[];     // [lds_keys] ordered keys of the row's middle scores
   __shared__ uint32_t hist[256];
   __shared__ int wsum[17];
   __shared__ uint32_t s_prefix;
@@ -118,6 +122,14 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
   uint32_t thr = 0;
   int n_eq_ev = 0;
   const bool by_pos = a.policy == FADE_POLICY_POSITION || sc == nullptr;
+  // The row's keys are read once into LDS when they fit; every pass below
+  // then reads LDS instead of global memory.
+  const bool in_lds = M <= a.lds_keys;   // uniform
+  if (n_ev > 0 && !by_pos && in_lds) {
+    for (int r = tid; r < M; r += kSelThreads) skey[r] = ordered_key(sc[r]);
+    __syncthreads();
+  }
+  auto key_at = [&](int r) -> uint32_t { return in_lds ? skey[r] : ordered_key(sc[r]); };
   if (n_ev > 0 && !by_pos) {
     uint32_t prefix = 0, mask = 0;
     int kk = n_ev;
@@ -125,18 +137,34 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
       for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
       __syncthreads();
       for (int r = tid; r < M; r += kSelThreads) {
-        const uint32_t key = ordered_key(sc[r]);
+        const uint32_t key = key_at(r);
         if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
       }
       __syncthreads();
-      if (tid == 0) {
-        int cum = 0, d = 0;
-        for (; d < 256; ++d) {
-          if (cum + (int)hist[d] >= kk) break;
-          cum += (int)hist[d];
+      if (tid < 64) {
+        // The bin holding the kk-th smallest key: lane l sums bins 4l..4l+3,
+        // an inclusive scan over the wave finds the first lane whose running
+        // count reaches kk, and that lane walks its four bins.
+        const uint32_t h0 = hist[4 * tid], h1 = hist[4 * tid + 1], h2 = hist[4 * tid + 2], h3 = hist[4 * tid + 3];
+        const int c = (int)(h0 + h1 + h2 + h3);
+        int incl = c;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int y = __shfl_up(incl, o);
+          if (tid >= o) incl += y;
         }
-        s_prefix = prefix | ((uint32_t)d << shift);
-        s_kk = kk - cum;
+        const uint64_t reach = __ballot(incl >= kk);
+        const int l0 = (int)__builtin_ctzll(reach);
+        if (tid == l0) {
+          int cum = incl - c, d = 4 * tid;
+          const uint32_t hb[4] = {h0, h1, h2, h3};
+          for (int k = 0; k < 3 && cum + (int)hb[k] < kk; ++k) {
+            cum += (int)hb[k];
+            ++d;
+          }
+          s_prefix = prefix | ((uint32_t)d << shift);
+          s_kk = kk - cum;
+        }
       }
       __syncthreads();
       prefix = s_prefix;
@@ -156,7 +184,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
     const int r = c0 + tid;
     bool ev = false;
     if (by_score) {
-      const uint32_t key = r < M ? ordered_key(sc[r]) : 0u;
+      const uint32_t key = r < M ? key_at(r) : 0u;
       const bool eq = r < M && key == thr;
       int tot_eq;
       const int eq_rank = block_excl_scan(eq ? 1 : 0, &tot_eq, wsum) + base_eq;
@@ -637,7 +665,8 @@ hipError_t launch_evict(const Shape& s, const fade_layer_cache& c, int policy, i
   sa.batch = s.batch;
   sa.n_sink = s.n_sink;
   sa.W = s.W;
-  hipLaunchKernelGGL(k_select, dim3(rows), dim3(kSelThreads), 0, st, sa);
+  sa.lds_keys = s.cap_mid <= kSelLdsKeys ? s.cap_mid : 0;
+  hipLaunchKernelGGL(k_select, dim3(rows), dim3(kSelThreads), (size_t)sa.lds_keys * 4, st, sa);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int half = s.D / 2;
@@ -810,7 +839,8 @@ hipError_t launch_prefill_build(const Shape& s, const fade_layer_cache& c, const
   sa.L = L;
   sa.n_sink = s.n_sink;
   sa.W = s.W;
-  hipLaunchKernelGGL(k_select, dim3(rows), dim3(kSelThreads), 0, st, sa);
+  sa.lds_keys = L <= kSelLdsKeys ? L : 0;
+  hipLaunchKernelGGL(k_select, dim3(rows), dim3(kSelThreads), (size_t)sa.lds_keys * 4, st, sa);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (L > 0) {
