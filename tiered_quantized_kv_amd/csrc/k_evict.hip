@@ -51,14 +51,16 @@ __device__ int block_excl_scan(int v, int* total, int* wsum) {
   }
   if (lane == 63) wsum[w] = x;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int i = 0; i < nw; ++i) {
-      const int t = wsum[i];
-      wsum[i] = acc;
-      acc += t;
+  if (w == 0) {
+    const int t = lane < nw ? wsum[lane] : 0;
+    int y = t;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(y, o);
+      if (lane >= o) y += u;
     }
-    wsum[nw] = acc;
+    if (lane < nw) wsum[lane] = y - t;
+    if (lane == nw - 1) wsum[nw] = y;
   }
   __syncthreads();
   const int res = x - v + wsum[w];
@@ -85,6 +87,10 @@ struct SelectArgs {
   // prefill mode
   int L, n_sink, W;
   int lds_keys;          // rows with M <= lds_keys keep their ordered keys in LDS
+  // decode mode: workgroups past the rows build the cos/sin table of the shifts
+  int rows, n_delta, half;
+  RopeFreqs fr;
+  double2* tab;
 };
 
 constexpr int kSelLdsKeys = 12288;   // 48 KB of LDS keys per row at most
@@ -94,9 +100,20 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
   __shared__ uint32_t hist[256];
   __shared__ int wsum[17];
   __shared__ uint32_t s_prefix;
-  __shared__ int s_kk;
+  __shared__ int s_kk, s_eqcnt;
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
+  if (a.decode && row >= a.rows) {
+    // cos / sin of -delta * f_i for delta in [0, n_delta), float64
+    const int i = (row - a.rows) * kSelThreads + tid;
+    if (i < a.n_delta * a.half) {
+      const int delta = i / a.half, f = i - delta * a.half;
+      double sn, cs;
+      sincos((double)delta * a.fr.f[f], &sn, &cs);
+      a.tab[i] = make_double2(cs, -sn);
+    }
+    return;
+  }
   int S, M, R;
   if (a.decode) {
     const int32_t* L = a.lens + 4 * row;
@@ -125,12 +142,43 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
   // The row's keys are read once into LDS when they fit; every pass below
   // then reads LDS instead of global memory.
   const bool in_lds = M <= a.lds_keys;   // uniform
-  if (n_ev > 0 && !by_pos && in_lds) {
+  // A single eviction (the steady state of decode) is the (score, slot)
+  // smallest slot: a block argmin, and closed-form new slots below.
+  const bool single = n_ev == 1 && !by_pos;
+  __shared__ unsigned long long s_best[kSelThreads / 64];
+  __shared__ int s_e1;
+  int e1 = -1;
+  if (single) {
+    unsigned long long best = ~0ull;
+    for (int r = tid; r < M; r += kSelThreads)
+      best = min(best, ((unsigned long long)ordered_key(sc[r]) << 32) | (unsigned)r);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const unsigned lo = (unsigned)__shfl_xor((int)(unsigned)best, o);
+      const unsigned hi = (unsigned)__shfl_xor((int)(unsigned)(best >> 32), o);
+      best = min(best, ((unsigned long long)hi << 32) | lo);
+    }
+    if ((tid & 63) == 0) s_best[tid >> 6] = best;
+    __syncthreads();
+    if (tid < 64) {
+      unsigned long long v = tid < kSelThreads / 64 ? s_best[tid] : ~0ull;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const unsigned lo = (unsigned)__shfl_xor((int)(unsigned)v, o);
+        const unsigned hi = (unsigned)__shfl_xor((int)(unsigned)(v >> 32), o);
+        v = min(v, ((unsigned long long)hi << 32) | lo);
+      }
+      if (tid == 0) s_e1 = (int)(unsigned)v;
+    }
+    __syncthreads();
+    e1 = s_e1;
+  }
+  if (n_ev > 0 && !by_pos && in_lds && !single) {
     for (int r = tid; r < M; r += kSelThreads) skey[r] = ordered_key(sc[r]);
     __syncthreads();
   }
   auto key_at = [&](int r) -> uint32_t { return in_lds ? skey[r] : ordered_key(sc[r]); };
-  if (n_ev > 0 && !by_pos) {
+  if (n_ev > 0 && !by_pos && !single) {
     uint32_t prefix = 0, mask = 0;
     int kk = n_ev;
     for (int shift = 24; shift >= 0; shift -= 8) {
@@ -164,6 +212,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
           }
           s_prefix = prefix | ((uint32_t)d << shift);
           s_kk = kk - cum;
+          s_eqcnt = (int)hist[d];     // after the last pass: the number of keys equal to the cutoff
         }
       }
       __syncthreads();
@@ -174,58 +223,63 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
     thr = prefix;
     n_eq_ev = kk;
   }
-  // Assign new slots in ascending slot order.
+  // Assign new slots in ascending slot order. In decode mode the row's
+  // scores are compacted in the same pass: each chunk's values are read
+  // before the scan's barriers and written after them, and destinations never
+  // exceed sources, so later chunks' sources are untouched.
   __shared__ int s_first_ev;
-  if (tid == 0) s_first_ev = M;
+  if (tid == 0) s_first_ev = single ? e1 : M;
   __syncthreads();
   int base_eq = 0, base_keep = 0;
-  const bool by_score = n_ev > 0 && !by_pos;   // uniform over the workgroup
+  const bool by_score = n_ev > 0 && !by_pos && !single;   // uniform over the workgroup
+  // every key equal to the cutoff is evicted (the usual case): no tie ranks
+  const bool all_eq = !by_score || n_eq_ev >= s_eqcnt;
+  float* srow = (a.decode && n_ev > 0 && a.cache_scores) ? a.cache_scores + (size_t)row * a.cap_T : nullptr;
   for (int c0 = 0; c0 < M; c0 += kSelThreads) {
     const int r = c0 + tid;
+    const float sv = srow && r < M ? srow[S + r] : 0.f;
     bool ev = false;
-    if (by_score) {
+    if (single) {
+      ev = r == e1;
+    } else if (by_score) {
       const uint32_t key = r < M ? key_at(r) : 0u;
       const bool eq = r < M && key == thr;
-      int tot_eq;
-      const int eq_rank = block_excl_scan(eq ? 1 : 0, &tot_eq, wsum) + base_eq;
-      base_eq += tot_eq;
-      ev = r < M && (key < thr || (eq && eq_rank < n_eq_ev));
+      if (all_eq) {
+        ev = r < M && key <= thr;
+      } else {
+        int tot_eq;
+        const int eq_rank = block_excl_scan(eq ? 1 : 0, &tot_eq, wsum) + base_eq;
+        base_eq += tot_eq;
+        ev = r < M && (key < thr || (eq && eq_rank < n_eq_ev));
+      }
     } else if (n_ev > 0) {
       ev = r < n_ev;
     }
     const bool keep = r < M && !ev;
-    {
+    int keep_rank;
+    if (single) {
+      keep_rank = r - (r > e1 ? 1 : 0);
+      __syncthreads();                  // this chunk's score reads before its writes
+    } else {
       const uint64_t evm = __ballot(r < M && ev);     // first evicted slot, one atomic per wave
       if ((tid & 63) == 0 && evm) atomicMin(&s_first_ev, c0 + (tid & ~63) + (int)__builtin_ctzll(evm));
+      int tot_keep;
+      keep_rank = block_excl_scan(keep ? 1 : 0, &tot_keep, wsum) + base_keep;
+      base_keep += tot_keep;
     }
-    int tot_keep;
-    const int keep_rank = block_excl_scan(keep ? 1 : 0, &tot_keep, wsum) + base_keep;
-    base_keep += tot_keep;
     if (r < M) map[r] = keep ? keep_rank : -1;
+    if (srow && keep) srow[S + keep_rank] = sv;
   }
   __syncthreads();
   if (tid == 0) a.info[kInfo * row + 4] = s_first_ev;
   if (!a.decode || n_ev == 0) return;
-  // Compact this row's scores in place (destinations never exceed sources).
-  if (a.cache_scores) {
-    float* srow = a.cache_scores + (size_t)row * a.cap_T;
-    const int total = M + R;
-    for (int c0 = 0; c0 < total; c0 += kSelThreads) {
-      const int u = c0 + tid;
-      int dst = -1;
-      float v = 0.f;
-      if (u < total) {
-        if (u < M) {
-          const int d = map[u];
-          if (d >= 0) dst = S + d;
-        } else {
-          dst = S + (M - n_ev) + (u - M);
-        }
-        if (dst >= 0) v = srow[S + u];
-      }
+  // The recent-ring scores follow the survivors: S + M + i -> S + M - n_ev + i.
+  if (srow) {
+    for (int c0 = 0; c0 < R; c0 += kSelThreads) {
+      const int i = c0 + tid;
+      const float v = i < R ? srow[S + M + i] : 0.f;
       __syncthreads();
-      if (dst >= 0) srow[dst] = v;
-      __syncthreads();
+      if (i < R) srow[S + M - n_ev + i] = v;
     }
   }
   if (tid == 0) {
@@ -235,16 +289,6 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
       a.lens[4 * row + 1] = M - n_ev;
     }
   }
-}
-
-// cos / sin of -delta * f_i, delta in [0, n_delta), float64.
-__global__ void k_rope_table(RopeFreqs fr, int half, int n_delta, double2* tab) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n_delta * half) return;
-  const int delta = i / half, f = i - delta * half;
-  double s, c;
-  sincos((double)delta * fr.f[f], &s, &c);
-  tab[i] = make_double2(c, -s);
 }
 
 struct CompactArgs {
@@ -666,14 +710,15 @@ hipError_t launch_evict(const Shape& s, const fade_layer_cache& c, int policy, i
   sa.n_sink = s.n_sink;
   sa.W = s.W;
   sa.lds_keys = s.cap_mid <= kSelLdsKeys ? s.cap_mid : 0;
-  hipLaunchKernelGGL(k_select, dim3(rows), dim3(kSelThreads), (size_t)sa.lds_keys * 4, st, sa);
+  sa.rows = rows;
+  sa.half = s.D / 2;
+  sa.n_delta = max_evict + 1;
+  sa.fr = fr;
+  sa.tab = tab;
+  const int n_tab = sa.n_delta * sa.half;
+  hipLaunchKernelGGL(k_select, dim3(rows + (n_tab + kSelThreads - 1) / kSelThreads), dim3(kSelThreads),
+                     (size_t)sa.lds_keys * 4, st, sa);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int half = s.D / 2;
-  const int n_tab = (max_evict + 1) * half;
-  hipLaunchKernelGGL(k_rope_table, dim3((n_tab + 255) / 256), dim3(256), 0, st, fr, half,
-                     max_evict + 1, tab);
-  e = hipGetLastError();
   if (e != hipSuccess) return e;
   CompactArgs ca;
   ca.s = s;
