@@ -40,7 +40,29 @@ enum fade_status {
   FADE_ERR_HIP = 5            /* a HIP runtime call or launch failed         */
 };
 
-enum fade_rope_type { FADE_ROPE_DEFAULT = 0, FADE_ROPE_LLAMA3 = 1 };
+/* RoPE frequency schemes (FADE post, section "RoPE方案兼容性"; the pairing is
+ * rotate-half, channel i with i + d/2). With f_i = theta^(-2i/d):
+ *   DEFAULT  f_i
+ *   LLAMA3   llama3 band scaling (factor, low/high frequency factors, original
+ *            context length)
+ *   LINEAR   position interpolation: f_i / factor
+ *   NTK      NTK-aware base: theta' = theta * factor^(d / (d - 2))
+ *   YARN     YaRN ramp: r_i = original * f_i / (2 pi) rotations over the original
+ *            context, g = clamp((r_i - low) / (high - low), 0, 1) with low, high =
+ *            rope_low_freq_factor, rope_high_freq_factor (YaRN's beta_slow,
+ *            beta_fast, e.g. 1 and 32), f_i' = (1 - g) f_i / factor + g f_i. Its
+ *            attention temperature scales q and k, which the caller applies
+ *            when rotating them; it cancels in the re-rotation of cached keys.
+ *   NONE     no rotary embedding (e.g. ALiBi models): nothing is rotated and
+ *            moved middle keys keep their codes and scales, like values. */
+enum fade_rope_type {
+  FADE_ROPE_DEFAULT = 0,
+  FADE_ROPE_LLAMA3 = 1,
+  FADE_ROPE_LINEAR = 2,
+  FADE_ROPE_NTK = 3,
+  FADE_ROPE_YARN = 4,
+  FADE_ROPE_NONE = 5
+};
 enum fade_dtype { FADE_DTYPE_F16 = 0, FADE_DTYPE_BF16 = 1, FADE_DTYPE_F32 = 2 };
 enum fade_score_mode { FADE_SCORE_PREFILL = 0, FADE_SCORE_ACCUM = 1, FADE_SCORE_EMA = 2 };
 enum fade_policy { FADE_POLICY_SCORE = 0, FADE_POLICY_POSITION = 1 };
@@ -68,8 +90,9 @@ enum fade_ws_op {
  *   middle_k_bits   4 or 2;  middle_v_bits 4 or 2 (INT2 V is the optional
  *                   deep tier, FADE post "量化与Bit-Packing")
  *   group_size      quantization group along head_dim; must be 32
- *   rope_*          RoPE of the model; llama3 uses factor, low/high
- *                   frequency factors and the original context length
+ *   rope_*          RoPE of the model (fade_rope_type): llama3 and yarn use
+ *                   factor, low/high factors and the original context length;
+ *                   linear and ntk use factor
  *   q_dtype         FADE_DTYPE_F16 or FADE_DTYPE_BF16 (decode query)
  *   out_dtype       FADE_DTYPE_F16, FADE_DTYPE_BF16 or FADE_DTYPE_F32
  */

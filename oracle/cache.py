@@ -239,7 +239,9 @@ def evict(cache, budget, policy="score", evicted=None):
     mk_u = cache.mid_k_u[:, kept].copy()
     mk_s = cache.mid_k_s[:, kept].copy()
     moved = old_pos != new_pos
-    if moved.any():
+    # Without a rotary embedding there is nothing to re-rotate: moved keys
+    # keep their codes and scales, like values.
+    if moved.any() and c.rope_type != "none":
         khat = quant.dequantize(mk_u[:, moved], mk_s[:, moved], c.middle_k_bits, g)
         rot = rope.rerope_fp16(khat, old_pos[moved], new_pos[moved], freqs)
         u2, s2 = quant.quantize(rot, c.middle_k_bits, g)

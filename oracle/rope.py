@@ -16,6 +16,21 @@ names the schemes but prints no formula, so:
       (1 - sigma) * inv_freq_i / factor + sigma * inv_freq_i
   which is continuous at both band edges.
 
+Further schemes (FADE post, same section: the scheme list goes beyond the
+two above; the post gives no formulas, so these are the published
+definitions, written from their statements):
+* linear (position interpolation): inv_freq_i / factor, i.e. R(p) becomes the
+  default R(p / factor).
+* ntk (NTK-aware base): theta' = theta * factor^(d/(d-2)); the highest
+  frequency is kept and the lowest divided by exactly `factor`.
+* yarn (YaRN frequency ramp): r_i = orig * inv_freq_i / (2*pi) rotations over
+  the original context; gamma = clamp((r_i - beta_slow) / (beta_fast -
+  beta_slow), 0, 1); inv_freq_i' = (1 - gamma) * inv_freq_i / factor + gamma *
+  inv_freq_i. beta_slow / beta_fast travel in the low / high factor fields.
+  YaRN's attention temperature scales q and k by the caller; it cancels in
+  the re-rotation of a cached key.
+* none: no rotary embedding (ALiBi models); every frequency is 0.
+
 Rotation by position p: for each pair (x_i, x_{i+d/2}) and angle
 a = p * inv_freq_i,
     x_i'       = x_i * cos a - x_{i+d/2} * sin a
@@ -32,9 +47,19 @@ def inv_freq(head_dim, theta, rope_type="default", factor=1.0,
     if head_dim % 2:
         raise ValueError("head_dim must be even")
     i = np.arange(head_dim // 2, dtype=np.float64)
+    if rope_type == "none":
+        return np.zeros(head_dim // 2)
+    if rope_type == "ntk":
+        theta = float(theta) * float(factor) ** (head_dim / (head_dim - 2.0))
     f = np.power(float(theta), -2.0 * i / head_dim)
-    if rope_type == "default":
+    if rope_type in ("default", "ntk"):
         return f
+    if rope_type == "linear":
+        return f / factor
+    if rope_type == "yarn":
+        rotations = original_max_position * f / (2.0 * np.pi)
+        gamma = np.clip((rotations - low_freq_factor) / (high_freq_factor - low_freq_factor), 0.0, 1.0)
+        return (1.0 - gamma) * f / factor + gamma * f
     if rope_type != "llama3":
         raise ValueError(f"unsupported rope_type {rope_type!r}")
     wavelen = 2.0 * np.pi / f

@@ -11,13 +11,23 @@ from oracle import quant, rope
 from tiered_quantized_kv_amd import fade, synth
 
 DEV = "cuda"
+ROPE_NAMES = ["default", "llama3", "linear", "ntk", "yarn", "none"]
+# One parameter set per further RoPE scheme (the published defaults' shapes:
+# YaRN's beta_slow / beta_fast = 1 / 32 travel in the low / high fields).
+ROPE_KW = {
+    "linear": dict(rope_type="linear", rope_theta=1e4, rope_factor=4.0),
+    "ntk": dict(rope_type="ntk", rope_theta=1e4, rope_factor=8.0),
+    "yarn": dict(rope_type="yarn", rope_theta=1e4, rope_factor=8.0, rope_low_freq_factor=1.0,
+                 rope_high_freq_factor=32.0, rope_original_max_position=4096),
+    "none": dict(rope_type="none"),
+}
 
 
 def ocfg(c):
     return oc.Config(head_dim=c.head_dim, n_q_heads=c.n_q_heads, n_kv_heads=c.n_kv_heads, n_sink=c.n_sink,
                      recent_window=c.recent_window, int4_budget=c.int4_budget, middle_k_bits=c.middle_k_bits,
                      middle_v_bits=c.middle_v_bits, group_size=32, rope_theta=c.rope_theta,
-                     rope_type={0: "default", 1: "llama3"}[c.rope_type], rope_factor=c.rope_factor,
+                     rope_type=ROPE_NAMES[c.rope_type], rope_factor=c.rope_factor,
                      rope_low_freq_factor=c.rope_low_freq_factor, rope_high_freq_factor=c.rope_high_freq_factor,
                      rope_original_max_position=c.rope_original_max_position)
 

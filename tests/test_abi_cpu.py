@@ -106,3 +106,33 @@ def test_validation_rejects_before_launch():
     # score policy without a score array
     st = lib.fade_evict_rerope(ctypes.byref(cfg), ctypes.byref(c), fade.POLICY_SCORE, 0, null, 0, null)
     assert st == fade.FADE_ERR_INVALID_ARG
+
+
+def test_rope_scheme_validation():
+    """Each RoPE scheme's parameters are checked on the host, before any launch
+    (a zero-row rotation is a no-op once the configuration is valid)."""
+    lib = fade.lib()
+    null = ctypes.c_void_p(0)
+
+    def st(cfg):
+        return lib.fade_rope_rotate(ctypes.byref(cfg), null, fade.DTYPE_F16, 0, null, 0, 1, null)
+
+    ok = [_cfg(rope_type="linear", rope_factor=4.0), _cfg(rope_type="ntk", rope_factor=8.0),
+          _cfg(rope_type="yarn", rope_factor=8.0, rope_low_freq_factor=1.0, rope_high_freq_factor=32.0,
+               rope_original_max_position=4096),
+          _cfg(rope_type="yarn", rope_factor=8.0, rope_low_freq_factor=0.0, rope_high_freq_factor=32.0),
+          _cfg(rope_type="none", rope_theta=0.0)]
+    for c in ok:
+        assert st(c) == fade.FADE_OK
+    bad = [_cfg(rope_type="linear", rope_factor=0.0), _cfg(rope_type="ntk", rope_factor=-1.0),
+           _cfg(rope_type="yarn", rope_factor=8.0, rope_low_freq_factor=32.0, rope_high_freq_factor=1.0),
+           _cfg(rope_type="yarn", rope_factor=8.0, rope_original_max_position=0),
+           _cfg(rope_type="llama3", rope_factor=8.0, rope_low_freq_factor=0.0),
+           _cfg(rope_type="default", rope_theta=1.0)]
+    for c in bad:
+        assert st(c) == fade.FADE_ERR_INVALID_ARG
+    c = _cfg()
+    c.rope_type = 6
+    assert st(c) == fade.FADE_ERR_UNSUPPORTED
+    c.rope_type = -1
+    assert st(c) == fade.FADE_ERR_UNSUPPORTED

@@ -10,7 +10,7 @@ from oracle import cache as oc
 from oracle import rope
 from tiered_quantized_kv_amd import fade, synth
 
-from .gpu_helpers import DEV, assert_state_equal, build_both, dev16, ocfg, seq_state
+from .gpu_helpers import DEV, ROPE_KW, assert_state_equal, build_both, dev16, ocfg, seq_state
 
 pytestmark = pytest.mark.gpu
 
@@ -112,6 +112,31 @@ def test_decode_eviction_compaction(policy, d, kb, vb, budget, extra):
     for b in range(B):
         refs[b].cfg = oc_cfg
         oc.evict(refs[b], budget, "position" if policy == "position" else "score")
+        assert_state_equal(seq_state(tc, b), refs[b])
+
+
+@pytest.mark.parametrize("rtype", ["linear", "ntk", "yarn", "none"])
+def test_rope_schemes_prefill_and_decode_eviction(rtype):
+    """Each further RoPE scheme through both compactions: the fp16 re-RoPE of a
+    prefill build with score eviction, then a decode-time eviction event that
+    re-rotates the recent ring and requantizes moved middle keys (without a
+    rotary embedding keys move bit-for-bit, like values)."""
+    kw = ROPE_KW[rtype]
+    budget, extra = 300, 37
+    L = 4 + budget + extra + 32
+    B = 2
+    cfg0 = _cfg(d=128, hq=8, hkv=2, n_sink=4, w=32, budget=budget + extra, kb=4, vb=2, **kw)
+    sc = _scores(B, L + 400, 250, ties=True)
+    tc, refs, _ = build_both(cfg0, B, L + 400, 251, cap_mid=budget + extra, scores32=sc)
+    for b in range(B):
+        assert_state_equal(seq_state(tc, b), refs[b])
+    cfg = _cfg(d=128, hq=8, hkv=2, n_sink=4, w=32, budget=budget, kb=4, vb=2, **kw)
+    ws = fade.workspace(cfg, fade.WS_EVICT, B, budget + extra)
+    fade.fade_evict_rerope(cfg, tc, fade.POLICY_SCORE, ws)
+    torch.cuda.synchronize()
+    for b in range(B):
+        refs[b].cfg = ocfg(cfg)
+        oc.evict(refs[b], budget, "score")
         assert_state_equal(seq_state(tc, b), refs[b])
 
 

@@ -8,7 +8,7 @@ import torch
 from oracle import h2o, quant, rope
 from tiered_quantized_kv_amd import fade, synth
 
-from .gpu_helpers import DEV, bits16, dev16, ocfg
+from .gpu_helpers import DEV, ROPE_KW, bits16, dev16, ocfg
 
 pytestmark = pytest.mark.gpu
 
@@ -93,9 +93,11 @@ def test_quantize_gather_scatter_rows():
 
 
 @pytest.mark.parametrize("d,theta,rtype,dtype", [(64, 1e4, "default", "f16"), (128, 1e6, "default", "f16"),
-                                                 (64, 5e5, "llama3", "f16"), (128, 5e5, "default", "bf16")])
+                                                 (64, 5e5, "llama3", "f16"), (128, 5e5, "default", "bf16"),
+                                                 (128, 0, "linear", "f16"), (64, 0, "ntk", "bf16"),
+                                                 (128, 0, "yarn", "f16"), (64, 0, "none", "f16")])
 def test_rope_rotate_matches_oracle(d, theta, rtype, dtype):
-    kw = dict(rope_theta=theta, rope_type=rtype)
+    kw = dict(rope_theta=theta, rope_type=rtype) if rtype in ("default", "llama3") else dict(ROPE_KW[rtype])
     if rtype == "llama3":
         kw.update(rope_factor=32.0, rope_low_freq_factor=1.0, rope_high_freq_factor=4.0,
                   rope_original_max_position=8192)

@@ -188,3 +188,33 @@ def test_compressed_bytes_reproduce_page_llama_figures():
     tiered = accounting.compressed_bytes(d, hkv, 4, 2, 32, [fp16_slots] * layers,
                                          [mid] * layers) / mib
     assert abs(tiered - vals["tiered_mib"]) < 0.05
+
+
+def test_no_rotary_keys_move_like_values():
+    """Without a rotary embedding (ALiBi models) eviction moves middle keys
+    bit-for-bit, codes and scales, exactly as values move."""
+    cfg = _cfg(int4_budget=12, recent_window=6, rope_type="none", middle_k_bits=4, middle_v_bits=2)
+    L = 40
+    _, k16, v16 = _prefill(cfg, L, 38)
+    scores = synth.normal(synth.rng(39), L) ** 2
+    c = oc.build_from_prefill(cfg, k16, v16, scores)
+    # prefill: the middle survivors are the plain quantization of the stored keys
+    kept = 4 + np.sort(np.argsort(scores[4:L - 6], kind="stable")[L - 10 - 12:])
+    ku, ks = quant.quantize(k16[:, kept], 4, 32)
+    assert np.array_equal(c.mid_k_u, ku) and np.array_equal(c.mid_k_s, ks)
+    assert np.array_equal(c.rec_k, k16[:, L - 6:])
+    gen = synth.rng(40)
+    for _ in range(6):
+        kn = synth.normal(gen, 2, 64).astype(np.float16)
+        vn = synth.normal(gen, 2, 64).astype(np.float16)
+        q = synth.normal(gen, 1, 8, 64).astype(np.float16)
+        bk, bs, brk = c.mid_k_u.copy(), c.mid_k_s.copy(), c.rec_k.copy()
+        _, _, ev = oc.decode_step([c], q, kn[None], vn[None], mode="accum")
+        e = int(ev[0][0])
+        # the demoted key enters the middle tier quantized as stored
+        du, ds = quant.quantize(brk[:, :1], 4, 32)
+        full_u = np.concatenate([bk, du], axis=1)
+        full_s = np.concatenate([bs, ds], axis=1)
+        assert np.array_equal(np.delete(full_u, e, axis=1), c.mid_k_u)
+        assert np.array_equal(np.delete(full_s, e, axis=1), c.mid_k_s)
+        assert np.array_equal(c.rec_k[:, -1], kn)

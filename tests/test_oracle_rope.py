@@ -1,6 +1,7 @@
 """Pins for oracle.rope (CPU only): identities of rotations, complex
 multiplication as an independent route, the relative-position property, and
-the llama3 band rule's closed-form edges."""
+the llama3 band rule's closed-form edges, and the linear, NTK-aware, YaRN
+and no-rotary schemes against their defining properties."""
 import numpy as np
 import pytest
 
@@ -148,3 +149,90 @@ def test_round_bf16_matches_exact_rational_rounding():
         n = round(q)                                      # ties to even
         assert Fraction(float(g)) == n * ulp, (v, g)
 
+
+
+# ---- further schemes: linear, NTK-aware, YaRN, none ------------------------
+
+def test_linear_is_position_interpolation():
+    """Position interpolation: rotating at p with factor s equals the standard
+    rotation at p / s (an independent route through rotate)."""
+    d, theta, s = 128, 1e4, 4.0
+    base = rope.inv_freq(d, theta)
+    lin = rope.inv_freq(d, theta, "linear", factor=s)
+    x = _x(11, 20, d)
+    p = np.arange(20) * 401.0
+    assert np.allclose(rope.rotate(x, p, lin), rope.rotate(x, p / s, base), atol=1e-11)
+    assert np.array_equal(rope.inv_freq(d, theta, "linear", factor=1.0), base)
+
+
+@pytest.mark.parametrize("d,theta,s", [(64, 1e4, 8.0), (128, 1e6, 2.0), (128, 5e5, 16.0)])
+def test_ntk_keeps_highest_and_divides_lowest_by_factor(d, theta, s):
+    f = rope.inv_freq(d, theta, "ntk", factor=s)
+    base = rope.inv_freq(d, theta)
+    assert f[0] == 1.0
+    assert np.isclose(f[-1] * s, base[-1], rtol=1e-12)
+    # still a geometric sequence, with a common ratio between the standard
+    # one and the standard one of theta * s^(d/(d-2))
+    r = f[1:] / f[:-1]
+    assert np.allclose(r, r[0], rtol=1e-12) and r[0] < base[1] / base[0]
+    assert np.array_equal(rope.inv_freq(d, theta, "ntk", factor=1.0), base)
+
+
+def test_yarn_ramp_bands_and_edges():
+    """YaRN: dimensions that turn more than beta_fast times over the original
+    context keep their frequency, fewer than beta_slow times are divided by the
+    factor, in between the blend is linear in the number of rotations."""
+    d, theta, s, lo, hi, orig = 128, 1e4, 8.0, 1.0, 32.0, 4096
+    base = rope.inv_freq(d, theta)
+    got = rope.inv_freq(d, theta, "yarn", s, lo, hi, orig)
+    rot = orig * base / (2 * np.pi)
+    keep, scale = rot > hi, rot < lo
+    mid = ~(keep | scale)
+    assert keep.any() and scale.any() and mid.any()
+    assert np.array_equal(got[keep], base[keep])
+    assert np.allclose(got[scale], base[scale] / s, rtol=1e-15)
+    assert np.all(got[mid] < base[mid]) and np.all(got[mid] > base[mid] / s)
+    # midpoint of the ramp (rot = (lo + hi) / 2) is the average of both rules
+    k = 12
+    orig_mid = (lo + hi) / 2 * 2 * np.pi / base[k]
+    v = rope.inv_freq(d, theta, "yarn", s, lo, hi, orig_mid)[k]
+    assert np.isclose(v, (base[k] + base[k] / s) / 2, rtol=1e-13)
+    # continuity: a frequency placed on either edge takes that side's rule
+    for r_edge, expect in ((hi, base[k]), (lo, base[k] / s)):
+        for nudge in (1 - 1e-12, 1.0, 1 + 1e-12):
+            o = r_edge * 2 * np.pi / base[k] * nudge
+            assert np.isclose(rope.inv_freq(d, theta, "yarn", s, lo, hi, o)[k], expect, rtol=1e-9)
+
+
+def test_yarn_equals_llama3_band_rule():
+    """The llama3 rule written in wavelengths is the YaRN ramp written in
+    rotations (orig / wavelength = rotations) with the same two factors."""
+    for d, theta, s, lo, hi, orig in ((64, 5e5, 32.0, 1.0, 4.0, 8192), (128, 1e4, 8.0, 1.0, 32.0, 4096)):
+        a = rope.inv_freq(d, theta, "yarn", s, lo, hi, orig)
+        b = rope.inv_freq(d, theta, "llama3", s, lo, hi, orig)
+        assert np.allclose(a, b, rtol=1e-13)
+
+
+def test_none_is_identity():
+    f = rope.inv_freq(64, 1e4, "none")
+    assert f.shape == (32,) and not f.any()
+    x = _x(12, 30, 64)
+    p = np.arange(30) * 12345.0
+    assert np.array_equal(rope.rotate(x, p, f), x)
+    k16 = x.astype(np.float16)
+    assert np.array_equal(rope.rerope_fp16(k16, p, p[::-1], f), k16)
+
+
+@pytest.mark.parametrize("rtype", ["linear", "ntk", "yarn"])
+def test_scaled_schemes_keep_rotation_identities(rtype):
+    f = rope.inv_freq(128, 5e5, rtype, 8.0, 1.0, 32.0, 8192)
+    x = _x(13, 25, 128)
+    p1 = np.arange(25) * 5000.0
+    p2 = np.arange(25) * 3.0 + 7
+    assert np.allclose(rope.rotate(rope.unrotate(x, p1, f), p1, f), x, atol=1e-12)
+    assert np.allclose(rope.rotate(rope.rotate(x, p1, f), p2 - p1, f), rope.rotate(x, p2, f), atol=1e-10)
+
+
+def test_unknown_scheme_rejected():
+    with pytest.raises(ValueError):
+        rope.inv_freq(64, 1e4, "dynamic")

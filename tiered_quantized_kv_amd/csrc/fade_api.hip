@@ -25,13 +25,16 @@ int check_cfg(const fade_config* c) {
   if ((c->middle_k_bits != 2 && c->middle_k_bits != 4) || (c->middle_v_bits != 2 && c->middle_v_bits != 4))
     return FADE_ERR_UNSUPPORTED;
   if (c->group_size != 32) return FADE_ERR_UNSUPPORTED;
-  if (c->rope_type != FADE_ROPE_DEFAULT && c->rope_type != FADE_ROPE_LLAMA3) return FADE_ERR_UNSUPPORTED;
-  if (!(c->rope_theta > 1.0)) return FADE_ERR_INVALID_ARG;
-  if (c->rope_type == FADE_ROPE_LLAMA3) {
+  if (c->rope_type < FADE_ROPE_DEFAULT || c->rope_type > FADE_ROPE_NONE) return FADE_ERR_UNSUPPORTED;
+  if (c->rope_type != FADE_ROPE_NONE && !(c->rope_theta > 1.0)) return FADE_ERR_INVALID_ARG;
+  if (c->rope_type == FADE_ROPE_LLAMA3 || c->rope_type == FADE_ROPE_YARN) {
     if (!(c->rope_factor > 0.0) || !(c->rope_high_freq_factor > c->rope_low_freq_factor) ||
-        !(c->rope_low_freq_factor > 0.0) || c->rope_original_max_position <= 0)
+        !(c->rope_low_freq_factor >= 0.0) || c->rope_original_max_position <= 0)
       return FADE_ERR_INVALID_ARG;
+    if (c->rope_type == FADE_ROPE_LLAMA3 && !(c->rope_low_freq_factor > 0.0)) return FADE_ERR_INVALID_ARG;
   }
+  if ((c->rope_type == FADE_ROPE_LINEAR || c->rope_type == FADE_ROPE_NTK) && !(c->rope_factor > 0.0))
+    return FADE_ERR_INVALID_ARG;
   if (c->q_dtype != FADE_DTYPE_F16 && c->q_dtype != FADE_DTYPE_BF16) return FADE_ERR_UNSUPPORTED;
   if (c->out_dtype != FADE_DTYPE_F16 && c->out_dtype != FADE_DTYPE_BF16 && c->out_dtype != FADE_DTYPE_F32)
     return FADE_ERR_UNSUPPORTED;
@@ -79,10 +82,25 @@ RopeFreqs host_freqs(const fade_config* c) {
   RopeFreqs r;
   memset(&r, 0, sizeof(r));
   const int half = c->head_dim / 2;
+  r.rotates = c->rope_type != FADE_ROPE_NONE;
+  // NTK-aware scaling stretches the base so that the lowest frequency is
+  // divided by exactly the factor while the highest is kept
+  const double theta = c->rope_type == FADE_ROPE_NTK
+                           ? c->rope_theta * pow(c->rope_factor, (double)c->head_dim / (c->head_dim - 2))
+                           : c->rope_theta;
   for (int i = 0; i < half; ++i) {
-    const double f = pow(c->rope_theta, -2.0 * i / c->head_dim);
+    const double f = pow(theta, -2.0 * i / c->head_dim);
     double out = f;
-    if (c->rope_type == FADE_ROPE_LLAMA3) {
+    if (c->rope_type == FADE_ROPE_NONE) {
+      out = 0.0;
+    } else if (c->rope_type == FADE_ROPE_LINEAR) {
+      out = f / c->rope_factor;
+    } else if (c->rope_type == FADE_ROPE_YARN) {
+      const double rot = c->rope_original_max_position * f / (2.0 * M_PI);
+      double gm = (rot - c->rope_low_freq_factor) / (c->rope_high_freq_factor - c->rope_low_freq_factor);
+      gm = gm < 0.0 ? 0.0 : (gm > 1.0 ? 1.0 : gm);
+      out = (1.0 - gm) * f / c->rope_factor + gm * f;
+    } else if (c->rope_type == FADE_ROPE_LLAMA3) {
       const double wl = 2.0 * M_PI / f;
       const double long_wl = c->rope_original_max_position / c->rope_low_freq_factor;
       const double short_wl = c->rope_original_max_position / c->rope_high_freq_factor;

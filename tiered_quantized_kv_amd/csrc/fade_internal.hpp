@@ -15,6 +15,7 @@ constexpr int kMaxHalfDim = 64;     // head_dim <= 128
 // Per-pair RoPE frequencies computed on the host in float64.
 struct RopeFreqs {
   double f[kMaxHalfDim];
+  int rotates;           // 0 when the model has no rotary embedding
 };
 
 // Shape summary derived from fade_config + fade_layer_cache.

@@ -302,6 +302,7 @@ struct CompactArgs {
   size_t spill_stride;        // bytes of one (sequence, head, chunk) spill region
   int2* spill_info;           // [B][Hkv][nchunks] = {first destination, spilled rows}
   uint8_t* spill;             // [B][Hkv][nchunks] regions: K codes | V codes | K scales | V scales
+  int requant_keys;           // 0 without a rotary embedding: keys move like values
 };
 
 constexpr int kCompactRows = 128;   // middle rows per compaction workgroup
@@ -403,6 +404,7 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
 
   if (cidx == a.nchunks) {
     // Recent ring: every entry shifts by -n_ev positions; rotate fp16 K in place.
+    if (!a.requant_keys) return;
     const int32_t* L = a.c.lens + 4 * b;
     const int R = min(max(L[2], 0), s.ring), head = min(max(L[3], 0), s.ring - 1);
     const int slots = s.n_sink + s.ring;
@@ -493,8 +495,8 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
   // group lies in 4 adjacent lanes, so its amax is a local max and two quad
   // DPP steps, and (INT4) the lane's 8 codes of a half are one packed word.
   // The lane's cos/sin entries are reloaded only when its row's shift
-  // changes.
-  {
+  // changes. Without a rotary embedding the staged codes are written as they are.
+  if (a.requant_keys) {
     constexpr int PPL = 8, LPR = HALF / PPL, RPW2 = 64 / LPR;
     constexpr int CW = PPL * KB / 8;            // bytes of 8 codes (4 or 2)
     const int m = lane % LPR, rsub = lane / LPR;
@@ -732,6 +734,7 @@ hipError_t launch_evict(const Shape& s, const fade_layer_cache& c, int policy, i
   ca.spill_stride = spill_stride_bytes(s, spill_rows);
   ca.spill_info = spill_info;
   ca.spill = spill;
+  ca.requant_keys = fr.rotates;
   if (s.D == 128) launch_compact_d<128>(ca, st);
   else launch_compact_d<64>(ca, st);
   return hipGetLastError();
