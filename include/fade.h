@@ -54,14 +54,24 @@ enum fade_status {
  *            attention temperature scales q and k, which the caller applies
  *            when rotating them; it cancels in the re-rotation of cached keys.
  *   NONE     no rotary embedding (e.g. ALiBi models): nothing is rotated and
- *            moved middle keys keep their codes and scales, like values. */
+ *            moved middle keys keep their codes and scales, like values.
+ *   DYNAMIC  dynamic NTK: the NTK base of the length s = rope_seq_len,
+ *            theta' = theta * (factor * s / original - (factor - 1))^(d / (d - 2))
+ *            when s > original, theta otherwise. One call uses one base: a
+ *            re-rotation by a position shift is taken at the base of the
+ *            length the caller passes (the length current at that call).
+ *   PROPORTIONAL  proportional RoPE (Gemma 4, partial_rotary_factor p =
+ *            rope_factor in [0, 1]): the first floor(p * d / 2) pairs keep f_i,
+ *            the remaining (lowest-frequency) pairs are not rotated. */
 enum fade_rope_type {
   FADE_ROPE_DEFAULT = 0,
   FADE_ROPE_LLAMA3 = 1,
   FADE_ROPE_LINEAR = 2,
   FADE_ROPE_NTK = 3,
   FADE_ROPE_YARN = 4,
-  FADE_ROPE_NONE = 5
+  FADE_ROPE_NONE = 5,
+  FADE_ROPE_DYNAMIC = 6,
+  FADE_ROPE_PROPORTIONAL = 7
 };
 enum fade_dtype { FADE_DTYPE_F16 = 0, FADE_DTYPE_BF16 = 1, FADE_DTYPE_F32 = 2 };
 enum fade_score_mode { FADE_SCORE_PREFILL = 0, FADE_SCORE_ACCUM = 1, FADE_SCORE_EMA = 2 };
@@ -77,7 +87,7 @@ enum fade_ws_op {
  * Static configuration of one attention layer's cache (host struct, read
  * only). Fields follow the FADE post, section "自定义配置" (custom config):
  * n_sink, recent_window, int4_budget, middle_k_bits, middle_v_bits; and
- * section "RoPE方案兼容性" for the RoPE variants (standard and llama3).
+ * section "RoPE方案兼容性" for the RoPE variants.
  *   head_dim        64 or 128
  *   n_q_heads       query heads; n_q_heads / n_kv_heads = n_rep in {1,2,4,8}
  *                   (GQA: query head h reads KV head h / n_rep)
@@ -92,7 +102,11 @@ enum fade_ws_op {
  *   group_size      quantization group along head_dim; must be 32
  *   rope_*          RoPE of the model (fade_rope_type): llama3 and yarn use
  *                   factor, low/high factors and the original context length;
- *                   linear and ntk use factor
+ *                   linear and ntk use factor; dynamic uses factor, the
+ *                   original context length and rope_seq_len; proportional
+ *                   uses factor as the rotary fraction
+ *   rope_seq_len    sequence length that fixes dynamic NTK's base for this
+ *                   call (>= 0; ignored by the other schemes)
  *   q_dtype         FADE_DTYPE_F16 or FADE_DTYPE_BF16 (decode query)
  *   out_dtype       FADE_DTYPE_F16, FADE_DTYPE_BF16 or FADE_DTYPE_F32
  */
@@ -114,7 +128,7 @@ typedef struct fade_config {
   int32_t rope_original_max_position;
   int32_t q_dtype;
   int32_t out_dtype;
-  int32_t reserved;
+  int32_t rope_seq_len;
 } fade_config;
 
 /*

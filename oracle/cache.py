@@ -61,12 +61,13 @@ class Config:
     rope_low_freq_factor: float = 1.0
     rope_high_freq_factor: float = 4.0
     rope_original_max_position: int = 8192
+    rope_seq_len: int = 0
 
     def freqs(self):
         return rope.inv_freq(self.head_dim, self.rope_theta, self.rope_type,
                              self.rope_factor, self.rope_low_freq_factor,
                              self.rope_high_freq_factor,
-                             self.rope_original_max_position)
+                             self.rope_original_max_position, self.rope_seq_len)
 
 
 def tier_layout(t, n_sink, recent):
@@ -239,9 +240,9 @@ def evict(cache, budget, policy="score", evicted=None):
     mk_u = cache.mid_k_u[:, kept].copy()
     mk_s = cache.mid_k_s[:, kept].copy()
     moved = old_pos != new_pos
-    # Without a rotary embedding there is nothing to re-rotate: moved keys
-    # keep their codes and scales, like values.
-    if moved.any() and c.rope_type != "none":
+    # Without a rotary embedding (every frequency 0) there is nothing to
+    # re-rotate: moved keys keep their codes and scales, like values.
+    if moved.any() and c.freqs().any():
         khat = quant.dequantize(mk_u[:, moved], mk_s[:, moved], c.middle_k_bits, g)
         rot = rope.rerope_fp16(khat, old_pos[moved], new_pos[moved], freqs)
         u2, s2 = quant.quantize(rot, c.middle_k_bits, g)

@@ -30,6 +30,15 @@ definitions, written from their statements):
   YaRN's attention temperature scales q and k by the caller; it cancels in
   the re-rotation of a cached key.
 * none: no rotary embedding (ALiBi models); every frequency is 0.
+* dynamic (dynamic NTK): the NTK base of the current length s,
+  theta' = theta * (factor * s / orig - (factor - 1))^(d/(d-2)) once s > orig,
+  theta up to orig. Reading: one table per call, fixed by the length the
+  caller passes; a re-rotation by a position shift uses that one base.
+* proportional (Gemma 4, partial_rotary_factor p, carried in `factor`): the
+  first floor(p * d / 2) pairs keep the standard frequency, the remaining
+  lowest-frequency pairs are not rotated (frequency 0). Reading: the pairing
+  stays rotate-half over the whole head, the frequencies keep their
+  proportion to d (the post names the scheme and its parameter only).
 
 Rotation by position p: for each pair (x_i, x_{i+d/2}) and angle
 a = p * inv_freq_i,
@@ -42,7 +51,7 @@ import numpy as np
 
 def inv_freq(head_dim, theta, rope_type="default", factor=1.0,
              low_freq_factor=1.0, high_freq_factor=4.0,
-             original_max_position=8192):
+             original_max_position=8192, seq_len=0):
     """Per-pair angular frequencies, float64 [head_dim // 2]."""
     if head_dim % 2:
         raise ValueError("head_dim must be even")
@@ -51,8 +60,14 @@ def inv_freq(head_dim, theta, rope_type="default", factor=1.0,
         return np.zeros(head_dim // 2)
     if rope_type == "ntk":
         theta = float(theta) * float(factor) ** (head_dim / (head_dim - 2.0))
+    if rope_type == "dynamic" and seq_len > original_max_position:
+        stretch = factor * seq_len / original_max_position - (factor - 1.0)
+        theta = float(theta) * stretch ** (head_dim / (head_dim - 2.0))
     f = np.power(float(theta), -2.0 * i / head_dim)
-    if rope_type in ("default", "ntk"):
+    if rope_type in ("default", "ntk", "dynamic"):
+        return f
+    if rope_type == "proportional":
+        f[int(np.floor(factor * head_dim / 2)):] = 0.0
         return f
     if rope_type == "linear":
         return f / factor

@@ -11,7 +11,7 @@ from oracle import quant, rope
 from tiered_quantized_kv_amd import fade, synth
 
 DEV = "cuda"
-ROPE_NAMES = ["default", "llama3", "linear", "ntk", "yarn", "none"]
+ROPE_NAMES = ["default", "llama3", "linear", "ntk", "yarn", "none", "dynamic", "proportional"]
 # One parameter set per further RoPE scheme (the published defaults' shapes:
 # YaRN's beta_slow / beta_fast = 1 / 32 travel in the low / high fields).
 ROPE_KW = {
@@ -20,6 +20,9 @@ ROPE_KW = {
     "yarn": dict(rope_type="yarn", rope_theta=1e4, rope_factor=8.0, rope_low_freq_factor=1.0,
                  rope_high_freq_factor=32.0, rope_original_max_position=4096),
     "none": dict(rope_type="none"),
+    "dynamic": dict(rope_type="dynamic", rope_theta=1e4, rope_factor=2.0, rope_original_max_position=2048,
+                    rope_seq_len=5000),
+    "proportional": dict(rope_type="proportional", rope_theta=1e6, rope_factor=0.25),
 }
 
 
@@ -29,7 +32,7 @@ def ocfg(c):
                      middle_v_bits=c.middle_v_bits, group_size=32, rope_theta=c.rope_theta,
                      rope_type=ROPE_NAMES[c.rope_type], rope_factor=c.rope_factor,
                      rope_low_freq_factor=c.rope_low_freq_factor, rope_high_freq_factor=c.rope_high_freq_factor,
-                     rope_original_max_position=c.rope_original_max_position)
+                     rope_original_max_position=c.rope_original_max_position, rope_seq_len=c.rope_seq_len)
 
 
 def dev16(a):

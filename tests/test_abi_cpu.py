@@ -132,7 +132,26 @@ def test_rope_scheme_validation():
     for c in bad:
         assert st(c) == fade.FADE_ERR_INVALID_ARG
     c = _cfg()
-    c.rope_type = 6
+    c.rope_type = 8
     assert st(c) == fade.FADE_ERR_UNSUPPORTED
     c.rope_type = -1
     assert st(c) == fade.FADE_ERR_UNSUPPORTED
+
+
+def test_dynamic_and_proportional_validation():
+    lib = fade.lib()
+    null = ctypes.c_void_p(0)
+
+    def st(cfg):
+        return lib.fade_rope_rotate(ctypes.byref(cfg), null, fade.DTYPE_F16, 0, null, 0, 1, null)
+
+    for c in (_cfg(rope_type="dynamic", rope_factor=2.0, rope_original_max_position=2048, rope_seq_len=5000),
+              _cfg(rope_type="dynamic", rope_factor=2.0, rope_seq_len=0),
+              _cfg(rope_type="proportional", rope_factor=0.25), _cfg(rope_type="proportional", rope_factor=0.0),
+              _cfg(rope_type="proportional", rope_factor=1.0)):
+        assert st(c) == fade.FADE_OK
+    for c in (_cfg(rope_type="dynamic", rope_factor=2.0, rope_seq_len=-1),
+              _cfg(rope_type="dynamic", rope_factor=0.0),
+              _cfg(rope_type="dynamic", rope_factor=2.0, rope_original_max_position=0),
+              _cfg(rope_type="proportional", rope_factor=1.5), _cfg(rope_type="proportional", rope_factor=-0.1)):
+        assert st(c) == fade.FADE_ERR_INVALID_ARG

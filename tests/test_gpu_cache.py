@@ -115,7 +115,7 @@ def test_decode_eviction_compaction(policy, d, kb, vb, budget, extra):
         assert_state_equal(seq_state(tc, b), refs[b])
 
 
-@pytest.mark.parametrize("rtype", ["linear", "ntk", "yarn", "none"])
+@pytest.mark.parametrize("rtype", ["linear", "ntk", "yarn", "none", "dynamic", "proportional"])
 def test_rope_schemes_prefill_and_decode_eviction(rtype):
     """Each further RoPE scheme through both compactions: the fp16 re-RoPE of a
     prefill build with score eviction, then a decode-time eviction event that

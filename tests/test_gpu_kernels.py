@@ -95,7 +95,8 @@ def test_quantize_gather_scatter_rows():
 @pytest.mark.parametrize("d,theta,rtype,dtype", [(64, 1e4, "default", "f16"), (128, 1e6, "default", "f16"),
                                                  (64, 5e5, "llama3", "f16"), (128, 5e5, "default", "bf16"),
                                                  (128, 0, "linear", "f16"), (64, 0, "ntk", "bf16"),
-                                                 (128, 0, "yarn", "f16"), (64, 0, "none", "f16")])
+                                                 (128, 0, "yarn", "f16"), (64, 0, "none", "f16"),
+                                                 (64, 0, "dynamic", "f16"), (128, 0, "proportional", "bf16")])
 def test_rope_rotate_matches_oracle(d, theta, rtype, dtype):
     kw = dict(rope_theta=theta, rope_type=rtype) if rtype in ("default", "llama3") else dict(ROPE_KW[rtype])
     if rtype == "llama3":

@@ -235,4 +235,33 @@ def test_scaled_schemes_keep_rotation_identities(rtype):
 
 def test_unknown_scheme_rejected():
     with pytest.raises(ValueError):
-        rope.inv_freq(64, 1e4, "dynamic")
+        rope.inv_freq(64, 1e4, "longrope")
+
+
+def test_dynamic_ntk_is_ntk_of_the_current_stretch():
+    """Dynamic NTK: up to the original context the standard table; beyond it
+    the NTK-aware table of the stretch factor*s/orig - (factor-1), which at
+    s = orig is 1 (continuous) and grows linearly with s."""
+    d, theta, fac, orig = 128, 1e4, 2.0, 2048
+    base = rope.inv_freq(d, theta)
+    for s in (0, 100, orig):
+        assert np.array_equal(rope.inv_freq(d, theta, "dynamic", fac, original_max_position=orig, seq_len=s), base)
+    for s, stretch in ((2 * orig, 3.0), (4 * orig, 7.0), (orig + 1, 1.0 + fac / orig)):
+        got = rope.inv_freq(d, theta, "dynamic", fac, original_max_position=orig, seq_len=s)
+        assert np.allclose(got, rope.inv_freq(d, theta, "ntk", stretch), rtol=1e-12)
+        assert np.isclose(got[-1] * stretch, base[-1], rtol=1e-12) and got[0] == 1.0
+
+
+@pytest.mark.parametrize("d,p,n_rot", [(128, 0.25, 16), (64, 0.5, 16), (128, 1.0, 64), (64, 0.0, 0), (128, 0.3, 19)])
+def test_proportional_rotates_only_leading_pairs(d, p, n_rot):
+    f = rope.inv_freq(d, 1e6, "proportional", p)
+    base = rope.inv_freq(d, 1e6)
+    assert np.array_equal(f[:n_rot], base[:n_rot]) and not f[n_rot:].any()
+    x = _x(14, 10, d)
+    pos = np.arange(10) * 777.0
+    y = rope.rotate(x, pos, f)
+    h = d // 2
+    keep = np.r_[np.arange(n_rot, h), np.arange(h + n_rot, d)]
+    assert np.array_equal(y[:, keep], x[:, keep])          # pass-through pairs
+    rot = np.r_[np.arange(n_rot), np.arange(h, h + n_rot)]
+    assert np.allclose(y[:, rot], rope.rotate(x, pos, base)[:, rot], atol=1e-12)

@@ -25,7 +25,7 @@ int check_cfg(const fade_config* c) {
   if ((c->middle_k_bits != 2 && c->middle_k_bits != 4) || (c->middle_v_bits != 2 && c->middle_v_bits != 4))
     return FADE_ERR_UNSUPPORTED;
   if (c->group_size != 32) return FADE_ERR_UNSUPPORTED;
-  if (c->rope_type < FADE_ROPE_DEFAULT || c->rope_type > FADE_ROPE_NONE) return FADE_ERR_UNSUPPORTED;
+  if (c->rope_type < FADE_ROPE_DEFAULT || c->rope_type > FADE_ROPE_PROPORTIONAL) return FADE_ERR_UNSUPPORTED;
   if (c->rope_type != FADE_ROPE_NONE && !(c->rope_theta > 1.0)) return FADE_ERR_INVALID_ARG;
   if (c->rope_type == FADE_ROPE_LLAMA3 || c->rope_type == FADE_ROPE_YARN) {
     if (!(c->rope_factor > 0.0) || !(c->rope_high_freq_factor > c->rope_low_freq_factor) ||
@@ -34,6 +34,11 @@ int check_cfg(const fade_config* c) {
     if (c->rope_type == FADE_ROPE_LLAMA3 && !(c->rope_low_freq_factor > 0.0)) return FADE_ERR_INVALID_ARG;
   }
   if ((c->rope_type == FADE_ROPE_LINEAR || c->rope_type == FADE_ROPE_NTK) && !(c->rope_factor > 0.0))
+    return FADE_ERR_INVALID_ARG;
+  if (c->rope_type == FADE_ROPE_DYNAMIC &&
+      (!(c->rope_factor > 0.0) || c->rope_original_max_position <= 0 || c->rope_seq_len < 0))
+    return FADE_ERR_INVALID_ARG;
+  if (c->rope_type == FADE_ROPE_PROPORTIONAL && !(c->rope_factor >= 0.0 && c->rope_factor <= 1.0))
     return FADE_ERR_INVALID_ARG;
   if (c->q_dtype != FADE_DTYPE_F16 && c->q_dtype != FADE_DTYPE_BF16) return FADE_ERR_UNSUPPORTED;
   if (c->out_dtype != FADE_DTYPE_F16 && c->out_dtype != FADE_DTYPE_BF16 && c->out_dtype != FADE_DTYPE_F32)
@@ -82,16 +87,24 @@ RopeFreqs host_freqs(const fade_config* c) {
   RopeFreqs r;
   memset(&r, 0, sizeof(r));
   const int half = c->head_dim / 2;
-  r.rotates = c->rope_type != FADE_ROPE_NONE;
+  // proportional RoPE rotates only its first pairs (the highest frequencies)
+  const int n_rot = c->rope_type == FADE_ROPE_NONE           ? 0
+                    : c->rope_type == FADE_ROPE_PROPORTIONAL ? (int)floor(c->rope_factor * c->head_dim / 2)
+                                                             : half;
+  r.rotates = n_rot > 0;
   // NTK-aware scaling stretches the base so that the lowest frequency is
-  // divided by exactly the factor while the highest is kept
-  const double theta = c->rope_type == FADE_ROPE_NTK
-                           ? c->rope_theta * pow(c->rope_factor, (double)c->head_dim / (c->head_dim - 2))
-                           : c->rope_theta;
+  // divided by exactly the factor while the highest is kept; dynamic NTK
+  // takes that stretch from the current length
+  double theta = c->rope_theta;
+  const double ntk_exp = (double)c->head_dim / (c->head_dim - 2);
+  if (c->rope_type == FADE_ROPE_NTK) theta = c->rope_theta * pow(c->rope_factor, ntk_exp);
+  if (c->rope_type == FADE_ROPE_DYNAMIC && c->rope_seq_len > c->rope_original_max_position)
+    theta = c->rope_theta *
+            pow(c->rope_factor * c->rope_seq_len / c->rope_original_max_position - (c->rope_factor - 1.0), ntk_exp);
   for (int i = 0; i < half; ++i) {
     const double f = pow(theta, -2.0 * i / c->head_dim);
     double out = f;
-    if (c->rope_type == FADE_ROPE_NONE) {
+    if (i >= n_rot) {
       out = 0.0;
     } else if (c->rope_type == FADE_ROPE_LINEAR) {
       out = f / c->rope_factor;
