@@ -30,7 +30,6 @@
 namespace fade {
 
 constexpr int kTile = 64;
-constexpr float kMasked = -1.0e30f;     // score of a masked (non-causal) slot
 
 // Column pass work split: the query tiles at or below a 64-key tile are cut
 // into chunks of qt_per 16-row tiles, one workgroup per (key tile, KV group,
@@ -57,6 +56,12 @@ size_t h2o_ws_bytes(int D, int Hq, int Hkv, int batch, int L) {
          align_up((size_t)colsum_chunks(Hkv, batch, L) * batch * Hkv * L * 4, 256);
 }
 
+// An empty asm statement that reads and rewrites a loaded fragment: the
+// load is waited for here, once, before the loop that uses it. Without it
+// the wait is placed inside the loop, where the counter can only express it
+// as "wait for everything", prefetches of later iterations included.
+__device__ __forceinline__ void settle(f16x8& v) { asm volatile("" : "+v"(v)); }
+
 __device__ __forceinline__ f16x8 load8(const uint16_t* p) {
   return __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(p));
 }
@@ -66,6 +71,22 @@ __device__ __forceinline__ f16x8 load8(const uint16_t* p) {
 // in LDS (triple buffered, one barrier per tile) and shared by those heads.
 // Each lane keeps its own running max and sum for the four rows it holds;
 // the 16 lanes of a row are merged once at the end.
+//  * Scores stay in the raw q.k domain; the softmax scale is folded into one
+//    fma per probability, 2^(s * scale - m). A masked score is -2^100, whose
+//    product with the scale is exact, so a lane that has seen only masked
+//    keys holds exactly that product as its max and contributes nothing
+//    after the merge.
+//  * Query loads past L are clamped to row L - 1 (those rows are never
+//    written); key rows past L read as zero and are masked.
+constexpr float kMaskedRaw = -0x1p100f;
+
+// max of four MFMA results without the NaN-quieting copies fmaxf implies
+__device__ __forceinline__ float max4(float a, float b, float c, float d) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3\n\tv_max_f32 %0, %0, %4" : "=&v"(r) : "v"(a), "v"(b), "v"(c), "v"(d));
+  return r;
+}
+
 template <int D, int HPW>
 __global__ __launch_bounds__(256) void k_h2o_rowlse(const uint16_t* __restrict__ q,
                                                     const uint16_t* __restrict__ k, int Hq, int Hkv,
@@ -84,7 +105,8 @@ __global__ __launch_bounds__(256) void k_h2o_rowlse(const uint16_t* __restrict__
   if (pair >= Hkv * batch) return;
   const int g = pair % Hkv, b = pair / Hkv;
   const int n_rep = Hq / Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r0 = rt * 16;
   const uint16_t* kb_ = k + ((size_t)(b * Hkv + g) * L) * D;
   const int n_kt = min(r0 + 15, L - 1) / kTile + 1;
@@ -98,6 +120,8 @@ __global__ __launch_bounds__(256) void k_h2o_rowlse(const uint16_t* __restrict__
       const int i = tid + 256 * c;
       const int r = i / (D / 8), c8 = i - r * (D / 8);
       const int key = kt * kTile + r;
+      // (keys past L read as zero; written as a select, which also keeps
+      // pre[] in registers)
       pre[c] = key < L ? *reinterpret_cast<const uint4*>(kb_ + (size_t)key * D + c8 * 8) : make_uint4(0, 0, 0, 0);
     }
   };
@@ -116,60 +140,64 @@ __global__ __launch_bounds__(256) void k_h2o_rowlse(const uint16_t* __restrict__
   f16x8 afrag[HPW][KB];
   float m_l[HPW][4], l_l[HPW][4];
   const int row_base = r0 + 4 * (lane >> 4);
+  const float m_init = kMaskedRaw * scale;       // exact
 #pragma unroll
   for (int j = 0; j < HPW; ++j) {
     const int hl = wave + 4 * j;
-    const int r = r0 + (lane & 15);
+    const int r = min(r0 + (lane & 15), L - 1);
     const uint16_t* qb = q + ((size_t)(b * Hq + g * n_rep + min(hl, n_rep - 1)) * L) * D;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-      afrag[j][kb] = r < L ? load8(qb + (size_t)r * D + kb * 32 + 8 * (lane >> 4)) : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    for (int kb = 0; kb < KB; ++kb) afrag[j][kb] = load8(qb + (size_t)r * D + kb * 32 + 8 * (lane >> 4));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      m_l[j][i] = kMasked;
+      m_l[j][i] = m_init;
       l_l[j][i] = 0.f;
     }
   }
   if (n_kt > 1) lstore(1);
+#pragma unroll
+  for (int j = 0; j < HPW; ++j)
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) settle(afrag[j][kb]);
   if (n_kt > 2) gload(2);
   __syncthreads();
   for (int kt = 0; kt < n_kt; ++kt) {
     const uint16_t* kt_lds = ktile[kt % 3];
-    const bool edge = kt == n_kt - 1;            // the diagonal tile (and the end of L)
 #pragma unroll
     for (int j = 0; j < HPW; ++j) {
       if (wave + 4 * j >= n_rep) continue;      // wave-uniform
-      float s[4][4];
+      f32x4 acc[4];
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
           const f16x8 bfrag = __builtin_bit_cast(
               f16x8, *reinterpret_cast<const uint4*>(&kt_lds[(nb * 16 + (lane & 15)) * PITCH + kb * 32 + 8 * (lane >> 4)]));
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(afrag[j][kb], bfrag, acc, 0, 0, 0);
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afrag[j][kb], bfrag, acc[nb], 0, 0, 0);
         }
+      if (kt == n_kt - 1) {                      // the diagonal tile (and the end of L)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[nb][i] = acc[i] * scale;
-        if (edge) {
+        for (int nb = 0; nb < 4; ++nb) {
           const int key = kt * kTile + nb * 16 + (lane & 15);
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (key > row_base + i || key >= L) s[nb][i] = kMasked;
+            if (key > row_base + i || key >= L) acc[nb][i] = kMaskedRaw;
         }
       }
-      // Masked scores are a large finite negative, so 2^(s - m) is exactly 0
-      // for them while a row has a live key, and the update needs no branch
-      // (rows past L keep finite garbage and are never written).
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float mt = fmaxf(fmaxf(s[0][i], s[1][i]), fmaxf(s[2][i], s[3][i]));
-        const float mn = fmaxf(m_l[j][i], mt);
-        float acc = l_l[j][i] * __builtin_amdgcn_exp2f(m_l[j][i] - mn);
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) acc += __builtin_amdgcn_exp2f(s[nb][i] - mn);
-        l_l[j][i] = acc;
+        const float mn = fmaxf(m_l[j][i], max4(acc[0][i], acc[1][i], acc[2][i], acc[3][i]) * scale);
+        l_l[j][i] *= __builtin_amdgcn_exp2f(m_l[j][i] - mn);
         m_l[j][i] = mn;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float acc_l = l_l[j][i];
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) acc_l += __builtin_amdgcn_exp2f(fmaf(acc[nb][i], scale, -m_l[j][i]));
+        l_l[j][i] = acc_l;
       }
     }
     // buffer (kt + 2) % 3 was last read in iteration kt - 1, before the
@@ -201,10 +229,14 @@ __global__ __launch_bounds__(256) void k_h2o_rowlse(const uint16_t* __restrict__
 
 // Column pass. Workgroup = (64 keys, KV group, query-row chunk); the keys are
 // MFMA B fragments in registers and the four waves walk the (query head of
-// the group, 16-row query tile) items of the chunk at or below the diagonal,
-// with the next item's query fragments and row LSE prefetched. Per-lane
-// column partials are reduced across rows, waves and (in k_h2o_reduce)
-// chunks and groups in a fixed order.
+// the group, 16-row query tile) items of the chunk at or below the diagonal.
+// Each wave keeps two items in flight in fixed registers (the next one's
+// loads are issued while one is computed), computes the four 16-key
+// blocks of an item as independent MFMA chains, and takes the causal / tail
+// mask only on the items that touch the diagonal or the end of L. Loads are
+// clamped to row L - 1 instead of predicated; what they read past L is
+// masked or never written. Per-lane column partials are reduced across rows,
+// waves and (in k_h2o_reduce) chunks and groups in a fixed order.
 template <int D>
 __global__ __launch_bounds__(256) void k_h2o_colsum(const uint16_t* __restrict__ q,
                                                     const uint16_t* __restrict__ k, int Hq, int Hkv,
@@ -212,6 +244,7 @@ __global__ __launch_bounds__(256) void k_h2o_colsum(const uint16_t* __restrict__
                                                     float scale, const float* __restrict__ lse,
                                                     float* __restrict__ part) {
   constexpr int KB = D / 32;
+  constexpr int kInFlight = 2;
   __shared__ float colred[4][kTile];
   // 1-D grid, XCD aware: workgroups are dealt to the 8 XCDs round-robin by
   // id, so id % 8 picks the XCD and id / 8 walks, on that XCD, all key tiles
@@ -226,7 +259,9 @@ __global__ __launch_bounds__(256) void k_h2o_colsum(const uint16_t* __restrict__
   const int c = pair / (Hkv * batch), bg = pair % (Hkv * batch);
   const int b = bg / Hkv, g = bg % Hkv;
   const int n_rep = Hq / Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lq = lane >> 4;
   const int k0 = kt * kTile;
   const uint16_t* kb_ = k + ((size_t)(b * Hkv + g) * L) * D;
   // query tiles of this workgroup: the chunk c of the tiles at or below the
@@ -238,81 +273,73 @@ __global__ __launch_bounds__(256) void k_h2o_colsum(const uint16_t* __restrict__
     f16x8 bfrag[4][KB];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-      const int key = k0 + nb * 16 + (lane & 15);
+      const int key = min(k0 + nb * 16 + lr, L - 1);
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-        bfrag[nb][kb] = key < L ? load8(kb_ + (size_t)key * D + kb * 32 + 8 * (lane >> 4)) : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      for (int kb = 0; kb < KB; ++kb) bfrag[nb][kb] = load8(kb_ + (size_t)key * D + kb * 32 + 8 * lq);
     }
     const int first_qt = qlo / 16;
     const int n_qt = (qhi - qlo + 15) / 16;
     const int items = n_rep * n_qt;
-    // Items (query head hl, 16-row tile first_qt + qi) in the order
-    // hl * n_qt + qi; wave w takes items w, w + 4, ... walked incrementally.
+    // Item idx = (query head idx / n_qt, tile first_qt + idx % n_qt); wave w
+    // takes items w, w + 4, ...
     struct Item {
       f16x8 a[KB];
       float lrow[4];
     };
     const size_t head0 = (size_t)(b * Hq + g * n_rep) * L;
-    auto fetch = [&](Item& it, int hl, int qi) {
+    auto fetch = [&](Item& it, int idx) {
+      const int hl = idx / n_qt, qi = idx - hl * n_qt;
       const size_t hrow = head0 + (size_t)hl * L;
       const int rt = (first_qt + qi) * 16;
-      const int r = rt + (lane & 15);
-      const uint16_t* qp = q + (hrow + r) * D + 8 * (lane >> 4);
+      const uint16_t* qp = q + (hrow + min(rt + lr, L - 1)) * D + 8 * lq;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) it.a[kb] = load8(qp + kb * 32);
+      const int rb = rt + 4 * lq;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) it.lrow[i] = lse[hrow + min(rb + i, L - 1)];
+    };
+    auto process = [&](const Item& it, int idx) {
+      const int hl = idx / n_qt;
+      const int rt = (first_qt + idx - hl * n_qt) * 16;
+      f32x4 acc[4];
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
-        it.a[kb] = r < L ? load8(qp + kb * 32) : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      const int rb = rt + 4 * (lane >> 4);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) it.lrow[i] = rb + i < L ? lse[hrow + rb + i] : 0.f;
-    };
-    auto advance = [&](int& hl, int& qi) {
-      qi += 4;
-      while (qi >= n_qt) {
-        qi -= n_qt;
-        ++hl;
-      }
-    };
-    int hl = 0, qi = wave;
-    while (qi >= n_qt && hl < n_rep) {
-      qi -= n_qt;
-      ++hl;
-    }
-    // two items in flight ahead of the one being computed
-    Item nx1, nx2;
-    int h1 = hl, q1 = qi;
-    advance(h1, q1);
-    if (wave < items) fetch(nx1, hl, qi);
-    if (wave + 4 < items) fetch(nx2, h1, q1);
-    for (int idx = wave; idx < items; idx += 4) {
-      const Item cur = nx1;
-      nx1 = nx2;
-      const int rt = (first_qt + qi) * 16;
-      int nhl = hl, nqi = qi;
-      advance(nhl, nqi);
-      int fhl = nhl, fqi = nqi;
-      advance(fhl, fqi);
-      if (idx + 8 < items) fetch(nx2, fhl, fqi);
-      const int rb = rt + 4 * (lane >> 4);
-      const bool edge = rt < k0 + kTile || rt + 16 > L;   // wave-uniform
+        for (int nb = 0; nb < 4; ++nb)
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(it.a[kb], bfrag[nb][kb], acc[nb], 0, 0, 0);
+      if (rt >= k0 + kTile && rt + 16 <= L) {    // wave-uniform: every (row, key) is live
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur.a[kb], bfrag[nb][kb], acc, 0, 0, 0);
-        if (edge) {
-          const int key = k0 + nb * 16 + (lane & 15);
+          for (int i = 0; i < 4; ++i) col[nb] += __builtin_amdgcn_exp2f(fmaf(acc[nb][i], scale, -it.lrow[i]));
+      } else {
+        const int rb = rt + 4 * lq;
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (key <= rb + i && rb + i < L && key < L)
-              col[nb] += __builtin_amdgcn_exp2f(fmaf(acc[i], scale, -cur.lrow[i]));
-        } else {
+        for (int nb = 0; nb < 4; ++nb) {
+          const int key = k0 + nb * 16 + lr;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) col[nb] += __builtin_amdgcn_exp2f(fmaf(acc[i], scale, -cur.lrow[i]));
+          for (int i = 0; i < 4; ++i) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(acc[nb][i], scale, -it.lrow[i]));
+            col[nb] += (key <= rb + i && rb + i < L) ? p : 0.f;
+          }
         }
       }
-      hl = nhl;
-      qi = nqi;
+    };
+    Item it[kInFlight];
+#pragma unroll
+    for (int u = 0; u < kInFlight; ++u)
+      if (wave + 4 * u < items) fetch(it[u], wave + 4 * u);
+    for (int idx = wave; idx < items; idx += 4 * kInFlight) {
+#pragma unroll
+      for (int u = 0; u < kInFlight; ++u) {
+        const int cur = idx + 4 * u;
+        if (cur < items) {                       // wave-uniform
+          process(it[u], cur);
+          if (cur + 4 * kInFlight < items) fetch(it[u], cur + 4 * kInFlight);
+        }
+      }
     }
   }
 #pragma unroll
