@@ -228,7 +228,7 @@ __global__ __launch_bounds__(256) void k_h2o_rowlse(const uint16_t* __restrict__
 }
 
 // Column pass. Workgroup = (64 keys, KV group, query-row chunk); the keys are
-// MFMA B fragments in registers and the four waves walk the (query head of
+// staged once in LDS and the four waves walk the (query head of
 // the group, 16-row query tile) items of the chunk at or below the diagonal.
 // Each wave keeps two items in flight in fixed registers (the next one's
 // loads are issued while one is computed), computes the four 16-key
@@ -245,6 +245,9 @@ __global__ __launch_bounds__(256) void k_h2o_colsum(const uint16_t* __restrict__
                                                     float* __restrict__ part) {
   constexpr int KB = D / 32;
   constexpr int kInFlight = 2;
+  constexpr int PITCH = D + 8;                  // halves per LDS key row
+  constexpr int CPT = kTile * (D / 8) / 256;    // 16-byte chunks per thread
+  __shared__ __align__(16) uint16_t ktile[kTile * PITCH];
   __shared__ float colred[4][kTile];
   // 1-D grid, XCD aware: workgroups are dealt to the 8 XCDs round-robin by
   // id, so id % 8 picks the XCD and id / 8 walks, on that XCD, all key tiles
@@ -270,13 +273,17 @@ __global__ __launch_bounds__(256) void k_h2o_colsum(const uint16_t* __restrict__
   const int qlo = qt_lo * 16, qhi = min(L, (qt_lo + qt_per) * 16);
   float col[4] = {0.f, 0.f, 0.f, 0.f};
   if (qlo < qhi) {                               // workgroup-uniform
-    f16x8 bfrag[4][KB];
+    // the 64 keys, staged once in LDS and read as MFMA B fragments per item
+    // (keeping them in registers instead costs two waves per SIMD)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int key = min(k0 + nb * 16 + lr, L - 1);
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) bfrag[nb][kb] = load8(kb_ + (size_t)key * D + kb * 32 + 8 * lq);
+    for (int u = 0; u < CPT; ++u) {
+      const int i = tid + 256 * u;
+      const int r = i / (D / 8), c8 = i - r * (D / 8);
+      const int key = min(k0 + r, L - 1);
+      *reinterpret_cast<uint4*>(&ktile[r * PITCH + c8 * 8]) =
+          *reinterpret_cast<const uint4*>(kb_ + (size_t)key * D + c8 * 8);
     }
+    __syncthreads();
     const int first_qt = qlo / 16;
     const int n_qt = (qhi - qlo + 15) / 16;
     const int items = n_rep * n_qt;
@@ -308,7 +315,11 @@ __global__ __launch_bounds__(256) void k_h2o_colsum(const uint16_t* __restrict__
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
-          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(it.a[kb], bfrag[nb][kb], acc[nb], 0, 0, 0);
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              it.a[kb],
+              __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(
+                                            &ktile[(nb * 16 + lr) * PITCH + kb * 32 + 8 * lq])),
+              acc[nb], 0, 0, 0);
       if (rt >= k0 + kTile && rt + 16 <= L) {    // wave-uniform: every (row, key) is live
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
