@@ -1,0 +1,109 @@
+"""Persistence, telemetry and debug snapshots of a TieredCache (host side,
+CPU tensors; no kernel runs). Pins: a save/load round trip restores every
+live byte; mismatched caches are refused; telemetry counts equal the lengths
+and its byte count equals the oracle's closed form."""
+import json
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import accounting
+from tiered_quantized_kv_amd import fade, persist, synth
+
+
+def _cfg(**kw):
+    base = dict(head_dim=64, n_q_heads=8, n_kv_heads=2, n_sink=4, recent_window=8, int4_budget=40,
+                middle_k_bits=4, middle_v_bits=2)
+    base.update(kw)
+    return fade.make_config(**base)
+
+
+def _filled(cfg, batch, cap_mid, seed, shared=False):
+    tc = fade.TieredCache(cfg, batch, cap_mid, shared=shared, device="cpu")
+    gen = synth.rng(seed)
+    for name in ("fp_k", "fp_v", "mid_k_scales", "mid_v_scales"):
+        t = getattr(tc, name)
+        t.copy_(torch.from_numpy(synth.normal(gen, *t.shape).astype(np.float16)))
+    for name in ("mid_k_codes", "mid_v_codes"):
+        t = getattr(tc, name)
+        t.copy_(torch.from_numpy(gen.integers(0, 256, size=t.shape).astype(np.uint8)))
+    mids = gen.integers(0, cap_mid + 1, size=batch)
+    for b in range(batch):
+        tc.lens[b] = torch.tensor([cfg.n_sink, int(mids[b]), cfg.recent_window, int(gen.integers(0, 9))])
+    tc.scores.copy_(torch.from_numpy(synth.normal(gen, *tc.scores.shape).astype(np.float32)))
+    return tc
+
+
+@pytest.mark.parametrize("shared", [False, True])
+def test_round_trip_restores_live_state(tmp_path, shared):
+    cfg = _cfg()
+    a = _filled(cfg, 3, 50, 1, shared)
+    path = str(tmp_path / "cache.safetensors")
+    persist.save(a, path)
+    b = fade.TieredCache(cfg, 3, 64, shared=shared, device="cpu")      # larger capacity is fine
+    persist.load(b, path)
+    m = int(a.lens[:, 1].max())
+    for name in ("fp_k", "fp_v", "lens"):
+        assert torch.equal(getattr(a, name), getattr(b, name)), name
+    t = int(a.lens[:, :3].sum(dim=1).max())
+    assert torch.equal(a.scores[:, :t], b.scores[:, :t]) and not b.scores[:, t:].any()
+    for name in ("mid_k_codes", "mid_v_codes", "mid_k_scales", "mid_v_scales"):
+        assert torch.equal(getattr(a, name)[:, :, :m], getattr(b, name)[:, :, :m]), name
+
+
+def test_mismatched_cache_is_refused(tmp_path):
+    cfg = _cfg()
+    a = _filled(cfg, 2, 50, 2)
+    path = str(tmp_path / "cache.safetensors")
+    persist.save(a, path)
+    for other in (fade.TieredCache(_cfg(n_sink=8), 2, 50, device="cpu"),
+                  fade.TieredCache(_cfg(middle_v_bits=4), 2, 50, device="cpu"),
+                  fade.TieredCache(cfg, 3, 50, device="cpu"),
+                  fade.TieredCache(cfg, 2, int(a.lens[:, 1].max()) - 1, device="cpu")):
+        with pytest.raises(ValueError):
+            persist.load(other, path)
+
+
+def test_telemetry_counts_and_bytes(tmp_path):
+    cfg = _cfg()
+    tc = _filled(cfg, 4, 40, 3)
+    path = tmp_path / "events.jsonl"
+    ex = persist.JsonlExporter(str(path))
+    tel = persist.attach_telemetry(tc, ex, layer=7)
+    tel.record(tc)
+    tel.record(tc, event="demote")
+    ex.close()
+    recs = [json.loads(l) for l in path.read_text().splitlines()]
+    assert [r["seq_no"] for r in recs] == [0, 1] and recs[1]["event"] == "demote"
+    r = recs[0]
+    assert r["layer"] == 7 and len(r["seqs"]) == 4
+    lens = tc.lens.numpy()
+    sc = tc.scores.numpy().astype(np.float64)
+    for b, q in enumerate(r["seqs"]):
+        s, m, w = (int(x) for x in lens[b, :3])
+        assert (q["sink"], q["middle"], q["recent"], q["live"]) == (s, m, w, s + m + w)
+        live = sc[b, :s + m + w]
+        assert q["score_min"] == live.min() and q["score_max"] == live.max()
+        assert np.isclose(q["score_mean"], live.mean(), rtol=1e-12)
+    want = accounting.compressed_bytes(64, 2, 4, 2, 32, [q["sink"] + q["recent"] for q in r["seqs"]],
+                                       [q["middle"] for q in r["seqs"]])
+    assert r["compressed_bytes"] == want
+
+
+def test_dump_debug(tmp_path):
+    tc = _filled(_cfg(), 2, 30, 4)
+    snap = persist.dump_debug(tc, str(tmp_path / "snap.json"), layer=3)
+    back = json.loads((tmp_path / "snap.json").read_text())
+    assert back == json.loads(json.dumps(snap, sort_keys=True))
+    assert back["lens"] == tc.lens.tolist() and back["record"]["layer"] == 3
+    assert back["config"]["n_sink"] == 4 and back["cap_mid"] == 30
+
+
+def test_budget_may_differ(tmp_path):
+    a = _filled(_cfg(int4_budget=-1), 2, 50, 5)
+    path = str(tmp_path / "cache.safetensors")
+    persist.save(a, path)
+    b = fade.TieredCache(_cfg(int4_budget=20), 2, 50, device="cpu")
+    persist.load(b, path)
+    assert torch.equal(a.lens, b.lens)

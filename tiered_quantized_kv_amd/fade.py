@@ -210,6 +210,10 @@ def fade_h2o_scores(cfg, mode, cache=None, q_prefill=None, k_prefill=None, batch
 def fade_evict_rerope(cfg, cache, policy, ws, max_evict=0, stream=None):
     _check(lib().fade_evict_rerope(ctypes.byref(cfg), cache.ref(), policy, max_evict, _p(ws), ws.numel(),
                                    _s(stream)), "fade_evict_rerope")
+    tel = getattr(cache, "telemetry", None)
+    if tel is not None:
+        (stream or torch.cuda.current_stream()).synchronize()
+        tel.record(cache)
 
 
 def fade_prefill_build(cfg, cache, k_prefill, v_prefill, L, prefill_scores, ws, stream=None):
