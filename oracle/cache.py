@@ -62,6 +62,7 @@ class Config:
     rope_high_freq_factor: float = 4.0
     rope_original_max_position: int = 8192
     rope_seq_len: int = 0
+    rope_interleaved: bool = False
 
     def freqs(self):
         return rope.inv_freq(self.head_dim, self.rope_theta, self.rope_type,
@@ -156,7 +157,7 @@ def build_from_prefill(cfg, k16, v16, scores=None):
     moved = survivors != new_pos
     if moved.any():
         k_surv[:, moved] = rope.rerope_fp16(k16[:, survivors[moved]],
-                                            survivors[moved], new_pos[moved], freqs)
+                                            survivors[moved], new_pos[moved], freqs, cfg.rope_interleaved)
     v_surv = v16[:, survivors]
     m2 = kept_mid.size
     mk = k_surv[:, s:s + m2]
@@ -244,7 +245,7 @@ def evict(cache, budget, policy="score", evicted=None):
     # re-rotate: moved keys keep their codes and scales, like values.
     if moved.any() and c.freqs().any():
         khat = quant.dequantize(mk_u[:, moved], mk_s[:, moved], c.middle_k_bits, g)
-        rot = rope.rerope_fp16(khat, old_pos[moved], new_pos[moved], freqs)
+        rot = rope.rerope_fp16(khat, old_pos[moved], new_pos[moved], freqs, c.rope_interleaved)
         u2, s2 = quant.quantize(rot, c.middle_k_bits, g)
         mk_u[:, moved] = u2
         mk_s[:, moved] = s2
@@ -255,7 +256,7 @@ def evict(cache, budget, policy="score", evicted=None):
     if r:
         old_r = s + m + np.arange(r)
         new_r = old_r - n_evict
-        cache.rec_k = rope.rerope_fp16(cache.rec_k, old_r, new_r, freqs)
+        cache.rec_k = rope.rerope_fp16(cache.rec_k, old_r, new_r, freqs, c.rope_interleaved)
     survivors = np.concatenate([np.arange(s), s + kept, s + m + np.arange(r)])
     cache.scores = cache.scores[survivors].copy()
     return evicted

@@ -40,6 +40,11 @@ definitions, written from their statements):
   stays rotate-half over the whole head, the frequencies keep their
   proportion to d (the post names the scheme and its parameter only).
 
+Pairing (survey next row: interleaved pairing): besides rotate-half, the
+GPT-J / Llama-1 layout pairs adjacent channels (x_{2i}, x_{2i+1}) with the
+same frequency f_i; it is the rotate-half rotation conjugated by the
+de-interleaving permutation of the channels.
+
 Rotation by position p: for each pair (x_i, x_{i+d/2}) and angle
 a = p * inv_freq_i,
     x_i'       = x_i * cos a - x_{i+d/2} * sin a
@@ -93,22 +98,30 @@ def inv_freq(head_dim, theta, rope_type="default", factor=1.0,
     return out
 
 
-def rotate(x, positions, freqs):
-    """Apply R(p) to x [..., d] at positions [...] (broadcast), float64."""
+def rotate(x, positions, freqs, interleaved=False):
+    """Apply R(p) to x [..., d] at positions [...] (broadcast), float64.
+    Pair i is (x_i, x_{i+d/2}) (rotate-half), or (x_{2i}, x_{2i+1}) with
+    interleaved=True (the GPT-J / Llama-1 layout)."""
     x = np.asarray(x, dtype=np.float64)
     half = x.shape[-1] // 2
     ang = np.asarray(positions, dtype=np.float64)[..., None] * freqs
     c, s = np.cos(ang), np.sin(ang)
+    if interleaved:
+        x1, x2 = x[..., 0::2], x[..., 1::2]
+        y = np.empty(np.broadcast_shapes(x.shape, ang.shape[:-1] + (2 * half,)))
+        y[..., 0::2] = x1 * c - x2 * s
+        y[..., 1::2] = x2 * c + x1 * s
+        return y
     x1, x2 = x[..., :half], x[..., half:]
     return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
 
 
-def unrotate(x, positions, freqs):
+def unrotate(x, positions, freqs, interleaved=False):
     """Apply R(p)^T = R(-p): the un-RoPE step."""
-    return rotate(x, -np.asarray(positions, dtype=np.float64), freqs)
+    return rotate(x, -np.asarray(positions, dtype=np.float64), freqs, interleaved)
 
 
-def rerope_fp16(k, old_pos, new_pos, freqs):
+def rerope_fp16(k, old_pos, new_pos, freqs, interleaved=False):
     """Un-RoPE a key at its old position, re-RoPE it at the new (compacted)
     position and round once to fp16 (FADE post, sections "驱逐策略" and
     "RoPE重计算": surviving keys are re-rotated on eviction; the pages do the
@@ -117,7 +130,7 @@ def rerope_fp16(k, old_pos, new_pos, freqs):
     float64 dequantized values of a middle-tier key."""
     x = np.asarray(k)
     x = x.astype(np.float64) if x.dtype != np.float64 else x
-    y = rotate(unrotate(x, old_pos, freqs), new_pos, freqs)
+    y = rotate(unrotate(x, old_pos, freqs, interleaved), new_pos, freqs, interleaved)
     return y.astype(np.float16)
 
 

@@ -265,3 +265,31 @@ def test_proportional_rotates_only_leading_pairs(d, p, n_rot):
     assert np.array_equal(y[:, keep], x[:, keep])          # pass-through pairs
     rot = np.r_[np.arange(n_rot), np.arange(h, h + n_rot)]
     assert np.allclose(y[:, rot], rope.rotate(x, pos, base)[:, rot], atol=1e-12)
+
+
+# ---- interleaved (GPT-J) pairing ---------------------------------------------
+
+def test_interleaved_is_rotate_half_under_the_deinterleave_permutation():
+    """Pairs (x_2i, x_2i+1) rotated by f_i equal the rotate-half rotation of
+    the channels reordered as (x_0, x_2, ..., x_1, x_3, ...), reordered back."""
+    d = 64
+    f = rope.inv_freq(d, 1e4, "yarn", 8.0, 1.0, 32.0, 4096)
+    x = _x(15, 12, d)
+    p = np.arange(12) * 1001.0
+    perm = np.r_[np.arange(0, d, 2), np.arange(1, d, 2)]
+    inv = np.argsort(perm)
+    want = rope.rotate(x[:, perm], p, f)[:, inv]
+    assert np.allclose(rope.rotate(x, p, f, interleaved=True), want, atol=1e-12)
+
+
+def test_interleaved_matches_complex_multiplication():
+    d = 128
+    f = rope.inv_freq(d, 5e5)
+    x = _x(16, 9, d)
+    p = np.array([0, 1, 3, 77, 1000, 4095, 65535, 100000, 131071], dtype=np.float64)
+    z = (x[:, 0::2] + 1j * x[:, 1::2]) * np.exp(1j * p[:, None] * f[None, :])
+    y = rope.rotate(x, p, f, interleaved=True)
+    assert np.allclose(y[:, 0::2], z.real, atol=1e-11) and np.allclose(y[:, 1::2], z.imag, atol=1e-11)
+    assert np.allclose(rope.unrotate(y, p, f, interleaved=True), x, atol=1e-11)
+    k16 = x.astype(np.float16)
+    assert np.array_equal(rope.rerope_fp16(k16, p, p, f, interleaved=True), k16)
