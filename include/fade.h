@@ -41,7 +41,8 @@ enum fade_status {
 };
 
 /* RoPE frequency schemes (FADE post, section "RoPE方案兼容性"; the pairing is
- * rotate-half, channel i with i + d/2). With f_i = theta^(-2i/d):
+ * rotate-half, channel i with i + d/2, unless FADE_ROPE_INTERLEAVED is set).
+ * With f_i = theta^(-2i/d):
  *   DEFAULT  f_i
  *   LLAMA3   llama3 band scaling (factor, low/high frequency factors, original
  *            context length)
@@ -71,7 +72,12 @@ enum fade_rope_type {
   FADE_ROPE_YARN = 4,
   FADE_ROPE_NONE = 5,
   FADE_ROPE_DYNAMIC = 6,
-  FADE_ROPE_PROPORTIONAL = 7
+  FADE_ROPE_PROPORTIONAL = 7,
+  FADE_ROPE_SCHEME_MASK = 0xFF,
+  /* Flag OR-ed into rope_type: the GPT-J / Llama-1 pairing, pair i = channels
+   * (2i, 2i + 1) with frequency f_i, instead of rotate-half (i, i + d/2).
+   * The stored layout and the quantization groups do not change. */
+  FADE_ROPE_INTERLEAVED = 0x100
 };
 enum fade_dtype { FADE_DTYPE_F16 = 0, FADE_DTYPE_BF16 = 1, FADE_DTYPE_F32 = 2 };
 enum fade_score_mode { FADE_SCORE_PREFILL = 0, FADE_SCORE_ACCUM = 1, FADE_SCORE_EMA = 2 };

@@ -30,9 +30,10 @@ def ocfg(c):
     return oc.Config(head_dim=c.head_dim, n_q_heads=c.n_q_heads, n_kv_heads=c.n_kv_heads, n_sink=c.n_sink,
                      recent_window=c.recent_window, int4_budget=c.int4_budget, middle_k_bits=c.middle_k_bits,
                      middle_v_bits=c.middle_v_bits, group_size=32, rope_theta=c.rope_theta,
-                     rope_type=ROPE_NAMES[c.rope_type], rope_factor=c.rope_factor,
+                     rope_type=ROPE_NAMES[c.rope_type & fade.ROPE_SCHEME_MASK], rope_factor=c.rope_factor,
                      rope_low_freq_factor=c.rope_low_freq_factor, rope_high_freq_factor=c.rope_high_freq_factor,
-                     rope_original_max_position=c.rope_original_max_position, rope_seq_len=c.rope_seq_len)
+                     rope_original_max_position=c.rope_original_max_position, rope_seq_len=c.rope_seq_len,
+                     rope_interleaved=bool(c.rope_type & fade.ROPE_INTERLEAVED))
 
 
 def dev16(a):
@@ -49,7 +50,7 @@ def prefill_inputs(cfg, batch, L, seed):
     ks, vs, raws = [], [], []
     for b in range(batch):
         k_raw, v = synth.kv_raw(synth.rng(seed, b), cfg.n_kv_heads, L, cfg.head_dim)
-        ks.append(rope.rotate(k_raw, np.arange(L), f).astype(np.float16))
+        ks.append(rope.rotate(k_raw, np.arange(L), f, ocfg(cfg).rope_interleaved).astype(np.float16))
         vs.append(v.astype(np.float16))
         raws.append(k_raw)
     return np.stack(ks), np.stack(vs), np.stack(raws)

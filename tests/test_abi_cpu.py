@@ -155,3 +155,20 @@ def test_dynamic_and_proportional_validation():
               _cfg(rope_type="dynamic", rope_factor=2.0, rope_original_max_position=0),
               _cfg(rope_type="proportional", rope_factor=1.5), _cfg(rope_type="proportional", rope_factor=-0.1)):
         assert st(c) == fade.FADE_ERR_INVALID_ARG
+
+
+def test_interleaved_flag_validation():
+    lib = fade.lib()
+    null = ctypes.c_void_p(0)
+
+    def st(cfg):
+        return lib.fade_rope_rotate(ctypes.byref(cfg), null, fade.DTYPE_F16, 0, null, 0, 1, null)
+
+    assert st(_cfg(rope_interleaved=True)) == fade.FADE_OK
+    c = _cfg(rope_type="yarn", rope_factor=8.0, rope_low_freq_factor=1.0, rope_high_freq_factor=32.0,
+             rope_interleaved=True)
+    assert c.rope_type == fade.ROPE_YARN | fade.ROPE_INTERLEAVED and st(c) == fade.FADE_OK
+    for bad in (0x200, 0x100 | 8, 0x1000):
+        c = _cfg()
+        c.rope_type = bad
+        assert st(c) == fade.FADE_ERR_UNSUPPORTED

@@ -140,6 +140,31 @@ def test_rope_schemes_prefill_and_decode_eviction(rtype):
         assert_state_equal(seq_state(tc, b), refs[b])
 
 
+@pytest.mark.parametrize("d,kb,vb,rtype", [(128, 4, 2, "default"), (64, 2, 4, "yarn"), (64, 4, 4, "proportional")])
+def test_interleaved_pairing_prefill_and_decode_eviction(d, kb, vb, rtype):
+    """GPT-J pairing through both compactions: the prefill build's fp16
+    re-RoPE (lanes trade values back to the storage layout), the ring
+    rotation and the middle rebuild over adjacent-channel pairs."""
+    kw = dict(ROPE_KW[rtype]) if rtype != "default" else dict(rope_theta=1e6)
+    kw["rope_interleaved"] = True
+    budget, extra = 300, 37
+    L = 4 + budget + extra + 32
+    B = 2
+    cfg0 = _cfg(d=d, hq=8, hkv=2, n_sink=4, w=32, budget=budget + extra, kb=kb, vb=vb, **kw)
+    sc = _scores(B, L + 400, 270 + d, ties=True)
+    tc, refs, _ = build_both(cfg0, B, L + 400, 271 + kb, cap_mid=budget + extra, scores32=sc)
+    for b in range(B):
+        assert_state_equal(seq_state(tc, b), refs[b])
+    cfg = _cfg(d=d, hq=8, hkv=2, n_sink=4, w=32, budget=budget, kb=kb, vb=vb, **kw)
+    ws = fade.workspace(cfg, fade.WS_EVICT, B, budget + extra)
+    fade.fade_evict_rerope(cfg, tc, fade.POLICY_SCORE, ws)
+    torch.cuda.synchronize()
+    for b in range(B):
+        refs[b].cfg = ocfg(cfg)
+        oc.evict(refs[b], budget, "score")
+        assert_state_equal(seq_state(tc, b), refs[b])
+
+
 def test_ragged_batch_via_sequence_views():
     """Per-sequence builds into one batched cache (ragged lengths), then one
     per-sequence score eviction on the whole batch."""

@@ -96,9 +96,13 @@ def test_quantize_gather_scatter_rows():
                                                  (64, 5e5, "llama3", "f16"), (128, 5e5, "default", "bf16"),
                                                  (128, 0, "linear", "f16"), (64, 0, "ntk", "bf16"),
                                                  (128, 0, "yarn", "f16"), (64, 0, "none", "f16"),
-                                                 (64, 0, "dynamic", "f16"), (128, 0, "proportional", "bf16")])
+                                                 (64, 0, "dynamic", "f16"), (128, 0, "proportional", "bf16"),
+                                                 (128, 1e6, "default+il", "f16"), (64, 0, "yarn+il", "bf16")])
 def test_rope_rotate_matches_oracle(d, theta, rtype, dtype):
+    il = rtype.endswith("+il")
+    rtype = rtype.replace("+il", "")
     kw = dict(rope_theta=theta, rope_type=rtype) if rtype in ("default", "llama3") else dict(ROPE_KW[rtype])
+    kw["rope_interleaved"] = il
     if rtype == "llama3":
         kw.update(rope_factor=32.0, rope_low_freq_factor=1.0, rope_high_freq_factor=4.0,
                   rope_original_max_position=8192)
@@ -113,7 +117,7 @@ def test_rope_rotate_matches_oracle(d, theta, rtype, dtype):
     fade.fade_rope_rotate(cfg, xd, fade.DTYPE_F16 if dtype == "f16" else fade.DTYPE_BF16, n,
                           torch.from_numpy(pos).to(DEV))
     torch.cuda.synchronize()
-    want = rope.rotate(x_in, pos, ocfg(cfg).freqs())
+    want = rope.rotate(x_in, pos, ocfg(cfg).freqs(), il)
     got = xd.float().cpu().numpy().astype(np.float64)
     if dtype == "f16":
         want_t = want.astype(np.float16).astype(np.float64)

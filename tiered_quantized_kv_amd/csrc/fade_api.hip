@@ -25,20 +25,22 @@ int check_cfg(const fade_config* c) {
   if ((c->middle_k_bits != 2 && c->middle_k_bits != 4) || (c->middle_v_bits != 2 && c->middle_v_bits != 4))
     return FADE_ERR_UNSUPPORTED;
   if (c->group_size != 32) return FADE_ERR_UNSUPPORTED;
-  if (c->rope_type < FADE_ROPE_DEFAULT || c->rope_type > FADE_ROPE_PROPORTIONAL) return FADE_ERR_UNSUPPORTED;
-  if (c->rope_type != FADE_ROPE_NONE && !(c->rope_theta > 1.0)) return FADE_ERR_INVALID_ARG;
-  if (c->rope_type == FADE_ROPE_LLAMA3 || c->rope_type == FADE_ROPE_YARN) {
+  if (c->rope_type & ~(FADE_ROPE_SCHEME_MASK | FADE_ROPE_INTERLEAVED)) return FADE_ERR_UNSUPPORTED;
+  const int scheme = c->rope_type & FADE_ROPE_SCHEME_MASK;
+  if (scheme > FADE_ROPE_PROPORTIONAL) return FADE_ERR_UNSUPPORTED;
+  if (scheme != FADE_ROPE_NONE && !(c->rope_theta > 1.0)) return FADE_ERR_INVALID_ARG;
+  if (scheme == FADE_ROPE_LLAMA3 || scheme == FADE_ROPE_YARN) {
     if (!(c->rope_factor > 0.0) || !(c->rope_high_freq_factor > c->rope_low_freq_factor) ||
         !(c->rope_low_freq_factor >= 0.0) || c->rope_original_max_position <= 0)
       return FADE_ERR_INVALID_ARG;
-    if (c->rope_type == FADE_ROPE_LLAMA3 && !(c->rope_low_freq_factor > 0.0)) return FADE_ERR_INVALID_ARG;
+    if (scheme == FADE_ROPE_LLAMA3 && !(c->rope_low_freq_factor > 0.0)) return FADE_ERR_INVALID_ARG;
   }
-  if ((c->rope_type == FADE_ROPE_LINEAR || c->rope_type == FADE_ROPE_NTK) && !(c->rope_factor > 0.0))
+  if ((scheme == FADE_ROPE_LINEAR || scheme == FADE_ROPE_NTK) && !(c->rope_factor > 0.0))
     return FADE_ERR_INVALID_ARG;
-  if (c->rope_type == FADE_ROPE_DYNAMIC &&
+  if (scheme == FADE_ROPE_DYNAMIC &&
       (!(c->rope_factor > 0.0) || c->rope_original_max_position <= 0 || c->rope_seq_len < 0))
     return FADE_ERR_INVALID_ARG;
-  if (c->rope_type == FADE_ROPE_PROPORTIONAL && !(c->rope_factor >= 0.0 && c->rope_factor <= 1.0))
+  if (scheme == FADE_ROPE_PROPORTIONAL && !(c->rope_factor >= 0.0 && c->rope_factor <= 1.0))
     return FADE_ERR_INVALID_ARG;
   if (c->q_dtype != FADE_DTYPE_F16 && c->q_dtype != FADE_DTYPE_BF16) return FADE_ERR_UNSUPPORTED;
   if (c->out_dtype != FADE_DTYPE_F16 && c->out_dtype != FADE_DTYPE_BF16 && c->out_dtype != FADE_DTYPE_F32)
@@ -87,9 +89,11 @@ RopeFreqs host_freqs(const fade_config* c) {
   RopeFreqs r;
   memset(&r, 0, sizeof(r));
   const int half = c->head_dim / 2;
+  const int scheme = c->rope_type & FADE_ROPE_SCHEME_MASK;
+  r.interleaved = (c->rope_type & FADE_ROPE_INTERLEAVED) != 0;
   // proportional RoPE rotates only its first pairs (the highest frequencies)
-  const int n_rot = c->rope_type == FADE_ROPE_NONE           ? 0
-                    : c->rope_type == FADE_ROPE_PROPORTIONAL ? (int)floor(c->rope_factor * c->head_dim / 2)
+  const int n_rot = scheme == FADE_ROPE_NONE           ? 0
+                    : scheme == FADE_ROPE_PROPORTIONAL ? (int)floor(c->rope_factor * c->head_dim / 2)
                                                              : half;
   r.rotates = n_rot > 0;
   // NTK-aware scaling stretches the base so that the lowest frequency is
@@ -97,8 +101,8 @@ RopeFreqs host_freqs(const fade_config* c) {
   // takes that stretch from the current length
   double theta = c->rope_theta;
   const double ntk_exp = (double)c->head_dim / (c->head_dim - 2);
-  if (c->rope_type == FADE_ROPE_NTK) theta = c->rope_theta * pow(c->rope_factor, ntk_exp);
-  if (c->rope_type == FADE_ROPE_DYNAMIC && c->rope_seq_len > c->rope_original_max_position)
+  if (scheme == FADE_ROPE_NTK) theta = c->rope_theta * pow(c->rope_factor, ntk_exp);
+  if (scheme == FADE_ROPE_DYNAMIC && c->rope_seq_len > c->rope_original_max_position)
     theta = c->rope_theta *
             pow(c->rope_factor * c->rope_seq_len / c->rope_original_max_position - (c->rope_factor - 1.0), ntk_exp);
   for (int i = 0; i < half; ++i) {
@@ -106,14 +110,14 @@ RopeFreqs host_freqs(const fade_config* c) {
     double out = f;
     if (i >= n_rot) {
       out = 0.0;
-    } else if (c->rope_type == FADE_ROPE_LINEAR) {
+    } else if (scheme == FADE_ROPE_LINEAR) {
       out = f / c->rope_factor;
-    } else if (c->rope_type == FADE_ROPE_YARN) {
+    } else if (scheme == FADE_ROPE_YARN) {
       const double rot = c->rope_original_max_position * f / (2.0 * M_PI);
       double gm = (rot - c->rope_low_freq_factor) / (c->rope_high_freq_factor - c->rope_low_freq_factor);
       gm = gm < 0.0 ? 0.0 : (gm > 1.0 ? 1.0 : gm);
       out = (1.0 - gm) * f / c->rope_factor + gm * f;
-    } else if (c->rope_type == FADE_ROPE_LLAMA3) {
+    } else if (scheme == FADE_ROPE_LLAMA3) {
       const double wl = 2.0 * M_PI / f;
       const double long_wl = c->rope_original_max_position / c->rope_low_freq_factor;
       const double short_wl = c->rope_original_max_position / c->rope_high_freq_factor;

@@ -16,6 +16,7 @@ constexpr int kMaxHalfDim = 64;     // head_dim <= 128
 struct RopeFreqs {
   double f[kMaxHalfDim];
   int rotates;           // 0 when the model has no rotary embedding
+  int interleaved;       // pair i = channels (2i, 2i + 1) instead of (i, i + d/2)
 };
 
 // Shape summary derived from fade_config + fade_layer_cache.

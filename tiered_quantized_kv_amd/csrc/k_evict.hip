@@ -303,6 +303,7 @@ struct CompactArgs {
   int2* spill_info;           // [B][Hkv][nchunks] = {first destination, spilled rows}
   uint8_t* spill;             // [B][Hkv][nchunks] regions: K codes | V codes | K scales | V scales
   int requant_keys;           // 0 without a rotary embedding: keys move like values
+  int interleaved;            // RoPE pair i = channels (2i, 2i + 1)
 };
 
 constexpr int kCompactRows = 128;   // middle rows per compaction workgroup
@@ -412,10 +413,11 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
     for (int t = wave * RPW + sub; t < R; t += 4 * RPW) {
       const int slot = s.n_sink + (head + t) % s.ring;
       uint16_t* kp = reinterpret_cast<uint16_t*>(a.c.fp_k) + (bg * slots + slot) * D;
+      const int c1 = a.interleaved ? 2 * p : p, c2 = a.interleaved ? 2 * p + 1 : p + HALF;
       uint16_t h1, h2;
-      rotate_pair(h2f(kp[p]), h2f(kp[p + HALF]), cs.x, cs.y, h1, h2);
-      kp[p] = h1;
-      kp[p + HALF] = h2;
+      rotate_pair(h2f(kp[c1]), h2f(kp[c2]), cs.x, cs.y, h1, h2);
+      kp[c1] = h1;
+      kp[c2] = h2;
     }
     return;
   }
@@ -496,7 +498,7 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
   // DPP steps, and (INT4) the lane's 8 codes of a half are one packed word.
   // The lane's cos/sin entries are reloaded only when its row's shift
   // changes. Without a rotary embedding the staged codes are written as they are.
-  if (a.requant_keys) {
+  if (a.requant_keys && !a.interleaved) {
     constexpr int PPL = 8, LPR = HALF / PPL, RPW2 = 64 / LPR;
     constexpr int CW = PPL * KB / 8;            // bytes of 8 codes (4 or 2)
     const int m = lane % LPR, rsub = lane / LPR;
@@ -569,6 +571,74 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
           s_ks[t * NG + g1] = sb1;
           s_ks[t * NG + g2] = sb2;
         }
+      }
+    }
+  }
+  if (a.requant_keys && a.interleaved) {
+    // Interleaved pairing: pair i is channels (2i, 2i + 1), so the lane's 8
+    // pairs [8m, 8m + 8) are the 16 adjacent channels [16m, 16m + 16), two
+    // code words of one 32-channel group shared with lane m ^ 1.
+    constexpr int PPL = 8, LPR = HALF / PPL, RPW2 = 64 / LPR;
+    constexpr int CW = PPL * KB / 8;            // bytes of 8 codes (4 or 2)
+    const int m = lane % LPR, rsub = lane / LPR, gq = m / 2;
+    int cur_delta = -1;
+    double2 csl[PPL];
+    for (int base = wave * RPW2; base < n_rows; base += 4 * RPW2) {
+      const int tt = base + rsub;
+      const bool valid = tt < n_rows;
+      const int t = lo + min(tt, n_rows - 1);
+      const int d = s_dst[t];
+      const bool moved = valid && d >= 0 && d != r0 + t;
+      const int delta = moved ? r0 + t - d : 0;
+      if (delta != cur_delta) {
+        const double2* tp = a.tab + (size_t)delta * HALF + PPL * m;
+#pragma unroll
+        for (int k = 0; k < PPL; ++k) csl[k] = tp[k];
+        cur_delta = delta;
+      }
+      const uint8_t* krow = reinterpret_cast<const uint8_t*>(s_kc) + t * KROW + 2 * CW * m;
+      uint32_t w1, w2;
+      if constexpr (CW == 4) {
+        w1 = *reinterpret_cast<const uint32_t*>(krow);
+        w2 = *reinterpret_cast<const uint32_t*>(krow + CW);
+      } else {
+        w1 = *reinterpret_cast<const uint16_t*>(krow);
+        w2 = *reinterpret_cast<const uint16_t*>(krow + CW);
+      }
+      float x[2 * PPL];
+      const float sc = h2f(s_ks[t * NG + gq]);
+      dequant8<KB>(w1, sc, x);
+      dequant8<KB>(w2, sc, x + PPL);
+      f16 z[2 * PPL];
+      float am = 0.f;
+#pragma unroll
+      for (int k = 0; k < PPL; ++k) {
+        const double a1 = (double)x[2 * k], a2 = (double)x[2 * k + 1];
+        const float f1 = d2f_odd_h(a1 * csl[k].x - a2 * csl[k].y);
+        const float f2 = d2f_odd_h(a2 * csl[k].x + a1 * csl[k].y);
+        z[2 * k] = (f16)f1;
+        z[2 * k + 1] = (f16)f2;
+        am = fmaxf(am, fmaxf(fabsf(f1), fabsf(f2)));
+      }
+      am = fmaxf(am, dpp_f<kQuadXor1>(am));
+      const uint16_t sb = group_scale_bits<KB>(h2f(f2h(am)));
+      const float r = quant_recip(h2f(sb));
+      uint32_t o1 = 0u - field_bias<KB, PPL>(), o2 = o1;
+#pragma unroll
+      for (int k = 0; k < PPL; ++k) {
+        o1 += quant_field<KB>((float)z[k], r) << (KB * k);
+        o2 += quant_field<KB>((float)z[PPL + k], r) << (KB * k);
+      }
+      if (moved) {
+        uint8_t* kw = reinterpret_cast<uint8_t*>(s_kc) + t * KROW + 2 * CW * m;
+        if constexpr (CW == 4) {
+          *reinterpret_cast<uint32_t*>(kw) = o1;
+          *reinterpret_cast<uint32_t*>(kw + CW) = o2;
+        } else {
+          *reinterpret_cast<uint16_t*>(kw) = (uint16_t)o1;
+          *reinterpret_cast<uint16_t*>(kw + CW) = (uint16_t)o2;
+        }
+        if ((m & 1) == 0) s_ks[t * NG + gq] = sb;
       }
     }
   }
@@ -735,6 +805,7 @@ hipError_t launch_evict(const Shape& s, const fade_layer_cache& c, int policy, i
   ca.spill_info = spill_info;
   ca.spill = spill;
   ca.requant_keys = fr.rotates;
+  ca.interleaved = fr.interleaved;
   if (s.D == 128) launch_compact_d<128>(ca, st);
   else launch_compact_d<64>(ca, st);
   return hipGetLastError();
@@ -800,15 +871,28 @@ __global__ __launch_bounds__(256) void k_build(BuildArgs a) {
       a.c.scores[(size_t)mrow * s.cap_T + newpos] = a.pscores ? a.pscores[(size_t)mrow * a.L + j] : 0.f;
     const uint16_t* kr = a.k + (bg * a.L + j) * D;
     const uint16_t* vr = a.v + (bg * a.L + j) * D;
-    const uint16_t k1 = kr[p], k2 = kr[p + HALF], v1 = vr[p], v2 = vr[p + HALF];
+    const uint16_t v1 = vr[p], v2 = vr[p + HALF];
     const int delta = j - newpos;
-    uint16_t y1 = k1, y2 = k2;
-    if (delta != 0) {
-      if (delta != cur_delta) {
-        sincos(-(double)delta * f, &sn, &cn);
-        cur_delta = delta;
-      }
-      rotate_pair(h2f(k1), h2f(k2), cn, sn, y1, y2);
+    if (delta != 0 && delta != cur_delta) {
+      sincos(-(double)delta * f, &sn, &cn);
+      cur_delta = delta;
+    }
+    uint16_t y1, y2;                            // channels p and p + HALF after the rotation
+    if (!a.fr.interleaved) {
+      y1 = kr[p];
+      y2 = kr[p + HALF];
+      if (delta != 0) rotate_pair(h2f(y1), h2f(y2), cn, sn, y1, y2);
+    } else {
+      // The lane rotates the adjacent pair (2p, 2p + 1); the row's lanes then
+      // trade values back to the (p, p + HALF) layout the stores and the
+      // quantizer use: channel c is component c % 2 of row lane c / 2.
+      uint16_t z1 = kr[2 * p], z2 = kr[2 * p + 1];
+      if (delta != 0) rotate_pair(h2f(z1), h2f(z2), cn, sn, z1, z2);
+      const int row0 = lane - p, l1 = row0 + p / 2, l2 = row0 + (p + HALF) / 2;
+      const int t0 = __shfl((int)z1, l1), t1 = __shfl((int)z2, l1);
+      const int t2 = __shfl((int)z1, l2), t3 = __shfl((int)z2, l2);
+      y1 = (uint16_t)((p & 1) ? t1 : t0);
+      y2 = (uint16_t)((p & 1) ? t3 : t2);
     }
     if (kind != 1) {
       const int slot = kind == 0 ? j : s.n_sink + (j - S - M);
@@ -923,13 +1007,14 @@ __global__ void k_rope_rotate(int D, uint16_t* x, int bf16, int64_t n_rows, cons
   const int f = (int)(i - r * half);
   const int64_t pos = positions ? (int64_t)positions[r] : (int64_t)pos_base + (r % pos_period);
   uint16_t* row = x + r * D;
-  const double a = bf16 ? (double)bf2f(row[f]) : (double)h2f(row[f]);
-  const double b = bf16 ? (double)bf2f(row[f + half]) : (double)h2f(row[f + half]);
+  const int c1 = fr.interleaved ? 2 * f : f, c2 = fr.interleaved ? 2 * f + 1 : f + half;
+  const double a = bf16 ? (double)bf2f(row[c1]) : (double)h2f(row[c1]);
+  const double b = bf16 ? (double)bf2f(row[c2]) : (double)h2f(row[c2]);
   double sn, cn;
   sincos((double)pos * fr.f[f], &sn, &cn);
   const double y1 = a * cn - b * sn, y2 = b * cn + a * sn;
-  row[f] = bf16 ? d2bf(y1) : d2h(y1);
-  row[f + half] = bf16 ? d2bf(y2) : d2h(y2);
+  row[c1] = bf16 ? d2bf(y1) : d2h(y1);
+  row[c2] = bf16 ? d2bf(y2) : d2h(y2);
 }
 
 hipError_t launch_rope_rotate(int D, uint16_t* x, int bf16, int64_t n_rows, const int32_t* positions,

@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(_HERE, "libfade.so")
 
 FADE_OK, FADE_ERR_INVALID_ARG, FADE_ERR_UNSUPPORTED, FADE_ERR_CAPACITY, FADE_ERR_WORKSPACE, FADE_ERR_HIP = range(6)
 ROPE_DEFAULT, ROPE_LLAMA3, ROPE_LINEAR, ROPE_NTK, ROPE_YARN, ROPE_NONE, ROPE_DYNAMIC, ROPE_PROPORTIONAL = range(8)
+ROPE_SCHEME_MASK, ROPE_INTERLEAVED = 0xFF, 0x100
 _ROPE = {"default": ROPE_DEFAULT, "llama3": ROPE_LLAMA3, "linear": ROPE_LINEAR, "ntk": ROPE_NTK,
          "yarn": ROPE_YARN, "none": ROPE_NONE, "dynamic": ROPE_DYNAMIC, "proportional": ROPE_PROPORTIONAL}
 DTYPE_F16, DTYPE_BF16, DTYPE_F32 = 0, 1, 2
@@ -95,10 +96,10 @@ def exported_symbols():
 def make_config(head_dim, n_q_heads, n_kv_heads, n_sink, recent_window, int4_budget, middle_k_bits=4,
                 middle_v_bits=4, rope_type="default", rope_theta=10000.0, rope_factor=1.0,
                 rope_low_freq_factor=1.0, rope_high_freq_factor=4.0, rope_original_max_position=8192,
-                q_dtype="f16", out_dtype="f32", group_size=32, rope_seq_len=0):
+                q_dtype="f16", out_dtype="f32", group_size=32, rope_seq_len=0, rope_interleaved=False):
     dt = {"f16": DTYPE_F16, "bf16": DTYPE_BF16, "f32": DTYPE_F32}
     return FadeConfig(head_dim, n_q_heads, n_kv_heads, n_sink, recent_window, int4_budget, middle_k_bits,
-                      middle_v_bits, group_size, _ROPE[rope_type],
+                      middle_v_bits, group_size, _ROPE[rope_type] | (ROPE_INTERLEAVED if rope_interleaved else 0),
                       float(rope_theta), float(rope_factor), float(rope_low_freq_factor),
                       float(rope_high_freq_factor), int(rope_original_max_position), dt[q_dtype],
                       dt[out_dtype], int(rope_seq_len))
