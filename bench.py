@@ -27,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0   # dense fp16 MFMA, MI355X
 
 
 def parse():
@@ -201,7 +202,7 @@ class Workload:
             self.M[b] = m
 
     # ---- one step --------------------------------------------------------------
-    def step(self, events=None):
+    def step(self, events=None, h2o_events=None):
         fade = self.fade
         t = self.step_idx
         due = self.w["int4_budget"] >= 0 and ((t + 1) % self.period == 0)
@@ -224,8 +225,12 @@ class Workload:
                 fade.fade_evict_rerope(self.cfg, tc, pol, self.ws_ev)
             if self.admit is not None:
                 qa, ka = self.admit[l]
+                if h2o_events is not None and h2o_events[l] is not None:
+                    h2o_events[l][0].record()
                 fade.fade_h2o_scores(self.cfg, fade.SCORE_PREFILL, q_prefill=qa, k_prefill=ka, batch=1,
                                      L=qa.shape[2], shared=0, scores_out=self.admit_scores, ws=self.ws_h2o)
+                if h2o_events is not None and h2o_events[l] is not None:
+                    h2o_events[l][1].record()
 
 
 class TimingEvent:
@@ -390,6 +395,9 @@ def main():
     TIME_EVERY = 4
     ev = [[(TimingEvent(), TimingEvent()) if l % TIME_EVERY == 0 else None for l in range(wl.layers)]
           for _ in range(steps)]
+    # the admitted sequence's H2O prefill column sums, on the layers in between
+    ev_h2o = [[(TimingEvent(), TimingEvent()) if wl.admit is not None and l % TIME_EVERY == 2 else None
+               for l in range(wl.layers)] for _ in range(steps)]
     dec_bytes, dec_tokens = 0, 0
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -400,7 +408,7 @@ def main():
         nb, nt = wl.decode_bytes_and_tokens()
         dec_bytes += nb * wl.layers
         dec_tokens += nt * wl.layers
-        wl.step(events=ev[s])
+        wl.step(events=ev[s], h2o_events=ev_h2o[s])
         wl.advance_mirror()
     t_end.record()
     torch.cuda.synchronize()
@@ -438,6 +446,19 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(a.workload)},
     }
+    if wl.admit is not None:
+        # MFMA-bound: algorithmic flops = one causal pass of Q K^T over the
+        # admitted prompt, 2 * Hq * L (L + 1) / 2 * d (the kernels run two
+        # passes, row statistics then column sums, so they execute twice this)
+        L = wl.admit[0][0].shape[2]
+        flops = float(wl.hq) * L * (L + 1) * wl.d
+        h2o_ms = sum(e[0].elapsed_time(e[1]) for row in ev_h2o for e in row if e is not None)
+        n_h2o = sum(1 for row in ev_h2o for e in row if e is not None)
+        us = h2o_ms * 1e3 / n_h2o
+        res["h2o_prefill"] = {"avg_us_per_launch": us, "prompt_tokens": L, "kernels": "k_h2o_rowlse + k_h2o_colsum + k_h2o_reduce",
+                              "flops_per_launch": flops, "bound": "mfma", "achieved": flops / (us * 1e-6) / 1e12,
+                              "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                              "frac": flops / (us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, "timed_launches": n_h2o}
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample ...", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(a.workload)

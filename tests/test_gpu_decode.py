@@ -110,7 +110,7 @@ def test_decode_output_dtypes(odt):
     cfg = _cfg(128, 32, 8, kb=4, vb=2, out_dtype=odt)
     tc, refs, _ = build_both(cfg, 1, 600, 320, cap_mid=600)
     got, _, want = _run_decode(cfg, tc, refs, 321, side=False)
-    ok, worst = out_close(got[0], want[0][0])
+    ok, worst = out_close(got[0], want[0][0], out_dtype=odt)
     assert ok, worst
 
 
@@ -154,3 +154,49 @@ def test_score_update(mode, shared):
     for r in range(1 if shared else B):
         assert np.allclose(after[r, :T], refs[r].scores, rtol=2e-6, atol=1e-9)
         assert np.array_equal(after[r, T:], before[r, T:])
+
+
+# Serving-sized batches: 48 sequences x 8 KV heads, ragged lengths including
+# caches with no middle tier, two decode steps with the demotion between.
+LARGE_BATCH = [
+    # d, hq, hkv, kb, vb, q_dtype, out_dtype
+    (128, 32, 8, 4, 2, "f16", "f32"),
+    (64, 32, 8, 4, 4, "bf16", "f16"),
+    (128, 16, 8, 2, 2, "f16", "bf16"),
+]
+
+
+@pytest.mark.parametrize("d,hq,hkv,kb,vb,qdt,odt", LARGE_BATCH)
+def test_decode_large_ragged_batch(d, hq, hkv, kb, vb, qdt, odt):
+    cfg = _cfg(d, hq, hkv, w=64, kb=kb, vb=vb, q_dtype=qdt, out_dtype=odt, rope_theta=5e5)
+    B = 48
+    gen = np.random.default_rng(350 + d + kb)
+    lengths = [int(x) for x in gen.integers(70, 420, B)]
+    lengths[:5] = [1, 5, 68, 69, 419]
+    cap = max(lengths)
+    tc = fade.TieredCache(cfg, B, cap)
+    refs = []
+    for b, L in enumerate(lengths):
+        k_raw, v = synth.kv_raw(synth.rng(351, b), hkv, L, d)
+        k16 = rope.rotate(k_raw, np.arange(L), ocfg(cfg).freqs()).astype(np.float16)
+        v16 = v.astype(np.float16)
+        ws = fade.workspace(cfg, fade.WS_PREFILL_BUILD, 1, L)
+        fade.fade_prefill_build(cfg, tc.seq_view(b), dev16(k16[None]), dev16(v16[None]), L, None, ws)
+        refs.append(oc.build_from_prefill(ocfg(cfg), k16, v16))
+    got, tok, want = _run_decode(cfg, tc, refs, 352)
+    for b in range(B):
+        ok, worst = out_close(got[b], want[b][0], out_dtype=odt)
+        assert ok, (b, worst)
+        T = refs[b].length
+        assert np.allclose(tok[b, :T], want[b][2], rtol=1e-5, atol=1e-8), b
+        assert np.all(tok[b, T:] == 0)
+        assert np.isclose(tok[b, :T].sum(), hq, rtol=1e-5)
+    # the next decode step, after the demotion that ends this one, without
+    # the side output
+    fade.fade_cache_demote(cfg, tc)
+    for r in refs:
+        oc.demote(r)
+    got2, _, want2 = _run_decode(cfg, tc, refs, 353, side=False)
+    for b in range(B):
+        ok, worst = out_close(got2[b], want2[b][0], out_dtype=odt)
+        assert ok, (b, worst)
