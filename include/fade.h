@@ -320,6 +320,37 @@ size_t fade_workspace_bytes(const fade_config* cfg, int32_t op, int32_t batch,
 uint64_t fade_compressed_bytes(const fade_config* cfg, const int32_t* fp16_slots,
                                const int32_t* mid_slots, int32_t n);
 
+/*
+ * Product-quantization codebook for KV vectors (FADE post, section
+ * "产品量化（PQ）": trained on calibration vectors, 256 centroids, uint8
+ * codes, about 2 bits per element). The vector is cut into 32 contiguous
+ * sub-vectors of l = head_dim / 32 elements (the reading under which a
+ * uint8 code gives 2 bits per element at head_dim 128), each with its own
+ * 256 centroids.
+ *   head_dim  64 or 128
+ *   x, out    fp16 [n_rows, head_dim], rows contiguous
+ *   codebook  fp16 [32][256][l]
+ *   codes     u8 [n_rows, 32]
+ * fade_pq_encode: nearest centroid by squared Euclidean distance, evaluated
+ *   in float64 on the exact fp16 values as ((e_0^2 + e_1^2) + ...) with every
+ *   product and sum rounded separately; ties go to the lowest index.
+ * fade_pq_decode: the centroids of the codes.
+ * fade_pq_train_step: one Lloyd iteration from codebook_in: encode x, then
+ *   each centroid becomes the mean of its members (exact sum, one float64
+ *   division, one rounding to fp16); a centroid with no members keeps its
+ *   value. codebook_out may equal codebook_in. workspace >=
+ *   fade_pq_workspace_bytes(head_dim, n_rows), 16-byte aligned.
+ * Pointers must be non-NULL (x, out, codebooks 2-byte aligned); n_rows >= 0.
+ */
+int fade_pq_encode(int32_t head_dim, const void* x, int64_t n_rows, const void* codebook,
+                   void* codes, void* stream);
+int fade_pq_decode(int32_t head_dim, const void* codes, int64_t n_rows, const void* codebook,
+                   void* out, void* stream);
+int fade_pq_train_step(int32_t head_dim, const void* x, int64_t n_rows, const void* codebook_in,
+                       void* codebook_out, void* workspace, size_t ws_bytes, void* stream);
+/* Workspace bytes of fade_pq_train_step; 0 for an unsupported head_dim. */
+size_t fade_pq_workspace_bytes(int32_t head_dim, int64_t n_rows);
+
 #ifdef __cplusplus
 }
 #endif

@@ -172,3 +172,27 @@ def test_interleaved_flag_validation():
         c = _cfg()
         c.rope_type = bad
         assert st(c) == fade.FADE_ERR_UNSUPPORTED
+
+
+def test_pq_validation_and_workspace():
+    lib = fade.lib()
+    null = ctypes.c_void_p(0)
+    p16 = ctypes.c_void_p(16)
+    # unsupported head_dim, negative rows, nulls with rows to do, odd alignment
+    assert lib.fade_pq_encode(96, p16, 4, p16, p16, null) == fade.FADE_ERR_UNSUPPORTED
+    assert lib.fade_pq_encode(128, p16, -1, p16, p16, null) == fade.FADE_ERR_INVALID_ARG
+    assert lib.fade_pq_encode(128, null, 4, p16, p16, null) == fade.FADE_ERR_INVALID_ARG
+    assert lib.fade_pq_encode(128, ctypes.c_void_p(17), 4, p16, p16, null) == fade.FADE_ERR_INVALID_ARG
+    assert lib.fade_pq_decode(64, p16, 4, null, p16, null) == fade.FADE_ERR_INVALID_ARG
+    # zero rows is a no-op even with nulls
+    assert lib.fade_pq_encode(128, null, 0, null, null, null) == fade.FADE_OK
+    assert lib.fade_pq_decode(64, null, 0, null, null, null) == fade.FADE_OK
+    # training: workspace checks come after the argument checks
+    ws = lib.fade_pq_workspace_bytes(128, 1000)
+    assert ws >= 32 * 256 * 4 * 8 + 32 * 256 * 4 + 1000 * 32
+    assert lib.fade_pq_workspace_bytes(128, 2000) > ws and lib.fade_pq_workspace_bytes(64, 1000) < ws
+    assert lib.fade_pq_workspace_bytes(100, 10) == 0
+    assert lib.fade_pq_train_step(128, p16, 1000, p16, p16, null, 0, null) == fade.FADE_ERR_WORKSPACE
+    assert lib.fade_pq_train_step(128, p16, 1000, p16, p16, p16, ws - 1, null) == fade.FADE_ERR_WORKSPACE
+    assert lib.fade_pq_train_step(128, null, 1000, p16, p16, p16, ws, null) == fade.FADE_ERR_INVALID_ARG
+    assert lib.fade_pq_train_step(128, p16, 1000, p16, null, p16, ws, null) == fade.FADE_ERR_INVALID_ARG

@@ -321,4 +321,45 @@ uint64_t fade_compressed_bytes(const fade_config* cfg, const int32_t* fp16_slots
   return total;
 }
 
+int fade_pq_encode(int32_t head_dim, const void* x, int64_t n_rows, const void* codebook, void* codes,
+                   void* stream) {
+  if (head_dim != 64 && head_dim != 128) return FADE_ERR_UNSUPPORTED;
+  if (n_rows < 0) return FADE_ERR_INVALID_ARG;
+  if (n_rows == 0) return FADE_OK;
+  if (!x || !codebook || !codes || !aligned(x, 2) || !aligned(codebook, 2)) return FADE_ERR_INVALID_ARG;
+  return hip_status(launch_pq_encode(head_dim, reinterpret_cast<const uint16_t*>(x), n_rows,
+                                     reinterpret_cast<const uint16_t*>(codebook), reinterpret_cast<uint8_t*>(codes),
+                                     reinterpret_cast<hipStream_t>(stream)));
+}
+
+int fade_pq_decode(int32_t head_dim, const void* codes, int64_t n_rows, const void* codebook, void* out,
+                   void* stream) {
+  if (head_dim != 64 && head_dim != 128) return FADE_ERR_UNSUPPORTED;
+  if (n_rows < 0) return FADE_ERR_INVALID_ARG;
+  if (n_rows == 0) return FADE_OK;
+  if (!codes || !codebook || !out || !aligned(codebook, 2) || !aligned(out, 2)) return FADE_ERR_INVALID_ARG;
+  return hip_status(launch_pq_decode(head_dim, reinterpret_cast<const uint8_t*>(codes), n_rows,
+                                     reinterpret_cast<const uint16_t*>(codebook), reinterpret_cast<uint16_t*>(out),
+                                     reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t fade_pq_workspace_bytes(int32_t head_dim, int64_t n_rows) {
+  if ((head_dim != 64 && head_dim != 128) || n_rows < 0) return 0;
+  return pq_ws_bytes(head_dim, n_rows);
+}
+
+int fade_pq_train_step(int32_t head_dim, const void* x, int64_t n_rows, const void* codebook_in,
+                       void* codebook_out, void* workspace, size_t ws_bytes, void* stream) {
+  if (head_dim != 64 && head_dim != 128) return FADE_ERR_UNSUPPORTED;
+  if (n_rows < 0) return FADE_ERR_INVALID_ARG;
+  if ((n_rows > 0 && !x) || !codebook_in || !codebook_out || !aligned(codebook_in, 2) ||
+      !aligned(codebook_out, 2) || (x && !aligned(x, 2)))
+    return FADE_ERR_INVALID_ARG;
+  if (!workspace || !aligned16(workspace) || ws_bytes < pq_ws_bytes(head_dim, n_rows)) return FADE_ERR_WORKSPACE;
+  return hip_status(launch_pq_train_step(head_dim, reinterpret_cast<const uint16_t*>(x), n_rows,
+                                         reinterpret_cast<const uint16_t*>(codebook_in),
+                                         reinterpret_cast<uint16_t*>(codebook_out), workspace,
+                                         reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -64,6 +64,15 @@ hipError_t launch_rope_rotate(int D, uint16_t* x, int bf16, int64_t n_rows,
                               const int32_t* positions, int pos_base, int pos_period,
                               const RopeFreqs& fr, hipStream_t st);
 
+// ---- product-quantization codebook (k_pq.hip) ------------------------------
+size_t pq_ws_bytes(int D, int64_t n);
+hipError_t launch_pq_encode(int D, const uint16_t* x, int64_t n, const uint16_t* cb, uint8_t* codes,
+                            hipStream_t st);
+hipError_t launch_pq_decode(int D, const uint8_t* codes, int64_t n, const uint16_t* cb, uint16_t* out,
+                            hipStream_t st);
+hipError_t launch_pq_train_step(int D, const uint16_t* x, int64_t n, const uint16_t* cb_in, uint16_t* cb_out,
+                                void* ws, hipStream_t st);
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace fade

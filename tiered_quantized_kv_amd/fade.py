@@ -71,6 +71,10 @@ _SIGS = {
                                         ctypes.c_int32, _P]),
     "fade_workspace_bytes": (ctypes.c_size_t, [_CFG, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]),
     "fade_compressed_bytes": (ctypes.c_uint64, [_CFG, _P, _P, ctypes.c_int32]),
+    "fade_pq_encode": (ctypes.c_int, [ctypes.c_int32, _P, ctypes.c_int64, _P, _P, _P]),
+    "fade_pq_decode": (ctypes.c_int, [ctypes.c_int32, _P, ctypes.c_int64, _P, _P, _P]),
+    "fade_pq_train_step": (ctypes.c_int, [ctypes.c_int32, _P, ctypes.c_int64, _P, _P, _P, ctypes.c_size_t, _P]),
+    "fade_pq_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int32, ctypes.c_int64]),
 }
 
 
@@ -233,3 +237,30 @@ def fade_compressed_bytes(cfg, fp16_slots, mid_slots):
     b = np.ascontiguousarray(mid_slots, dtype=np.int32)
     return int(lib().fade_compressed_bytes(ctypes.byref(cfg), a.ctypes.data_as(ctypes.c_void_p),
                                            b.ctypes.data_as(ctypes.c_void_p), len(a)))
+
+
+# ---- product-quantization codebook -------------------------------------------
+PQ_SUB, PQ_K = 32, 256
+
+
+def pq_workspace(head_dim, n_rows, device="cuda"):
+    n = max(int(lib().fade_pq_workspace_bytes(head_dim, n_rows)), 256)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def fade_pq_encode(x, codebook, codes, stream=None):
+    """x fp16 [n, d], codebook fp16 [32, 256, d/32] -> codes u8 [n, 32]."""
+    _check(lib().fade_pq_encode(x.shape[1], _p(x), x.shape[0], _p(codebook), _p(codes), _s(stream)),
+           "fade_pq_encode")
+
+
+def fade_pq_decode(codes, codebook, out, stream=None):
+    """codes u8 [n, 32] -> out fp16 [n, d]."""
+    _check(lib().fade_pq_decode(out.shape[1], _p(codes), codes.shape[0], _p(codebook), _p(out), _s(stream)),
+           "fade_pq_decode")
+
+
+def fade_pq_train_step(x, codebook_in, codebook_out, ws, stream=None):
+    """One Lloyd iteration of the codebook on the rows of x."""
+    _check(lib().fade_pq_train_step(x.shape[1], _p(x), x.shape[0], _p(codebook_in), _p(codebook_out), _p(ws),
+                                    ws.numel(), _s(stream)), "fade_pq_train_step")
