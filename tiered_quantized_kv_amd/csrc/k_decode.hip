@@ -495,7 +495,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
     // Each wave takes one slice of up to 64 consecutive tokens (a quarter of
     // the tier per round), one token per lane: QK^T on the MFMA (lanes past
     // the slice repeat its last token), then PV on VALU with one lane per CPL
-    // channels, its V elements loaded for up to 32 tokens at a time into the
+    // channels, its V elements loaded for up to 16 tokens at a time into the
     // registers the keys no longer need.
     constexpr int CPL = D / 64;
     const int fp_slots = a.n_sink + a.ring;
@@ -528,12 +528,15 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
           }
         }
       }
-      constexpr int VB32 = 32;
+      constexpr int VB32 = 16;
       uint32_t vv[VB32];
       auto load_v = [&](int g0, int nt) {
+        // each lane finds the slot of one token (lanes past nt repeat the
+        // last); token k's row address is then wave-uniform, read from lane k
+        const int my_slot = slot_of(base + g0 + min(lane, nt - 1));
 #pragma unroll
         for (int k = 0; k < VB32; ++k) {
-          const uint16_t* vr = fv + (size_t)slot_of(base + g0 + min(k, nt - 1)) * D;
+          const uint16_t* vr = fv + (size_t)__builtin_amdgcn_readlane(my_slot, k) * D;
           if constexpr (CPL == 2) vv[k] = *reinterpret_cast<const uint32_t*>(vr + 2 * lane);
           else vv[k] = vr[lane];
         }
@@ -616,66 +619,103 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
 // heads from the split partials, writes its share of the log-sum-exp merged
 // output, and, when requested, the side output a_j = sum_h 2^(s_hj - M_h) / L_h
 // of its 64 slots (four lane groups of 64 each sum a quarter of the heads).
+// With more than kFinishBatch splits, the splits of a head (and of an output
+// element) are shared by LN = 8 consecutive lanes, each loading every eighth
+// split in one batch, and combined with xor shuffles, so a merge costs one
+// round trip to memory rather than one per batch of splits; with few splits
+// one lane takes them all (LN = 1) and more elements are in flight.
 constexpr int kFinishSlots = 64;
+constexpr int kFinishBatch = 8;    // splits per lane per round
 
-template <int D>
+template <int LN>
+__device__ __forceinline__ float group_max(float x) {
+  if constexpr (LN == 8) {
+    x = fmaxf(x, __shfl_xor(x, 1));
+    x = fmaxf(x, __shfl_xor(x, 2));
+    x = fmaxf(x, __shfl_xor(x, 4));
+  }
+  return x;
+}
+template <int LN>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (LN == 8) {
+    x += __shfl_xor(x, 1);
+    x += __shfl_xor(x, 2);
+    x += __shfl_xor(x, 4);
+  }
+  return x;
+}
+
+template <int D, int LN>
 __global__ __launch_bounds__(256) void k_decode_finish(const float* __restrict__ part, int nsplit, int Hq,
                                                        void* out, int out_dtype,
                                                        const float* __restrict__ raw,
                                                        const int32_t* __restrict__ lens, int cap_T,
                                                        float* __restrict__ tok_attn) {
-  constexpr int kB = 8;           // loads in flight per thread
   extern __shared__ float ml[];   // [Hq][2] = (M_h, 1 / L_h), then [4][kFinishSlots] partial sums
   const int b = blockIdx.x, j = blockIdx.y, nb = gridDim.y, tid = threadIdx.x;
+  const int sub = tid % LN, grp = tid / LN, n_grp = blockDim.x / LN;
   const float* pb = part + (size_t)b * Hq * nsplit * (D + 2);
-  for (int h = tid; h < Hq; h += blockDim.x) {
-    const float* ph = pb + (size_t)h * nsplit * (D + 2) + D;
+  // statistics: lanes sub, sub + 8, ... of a head's splits, then the 8 lanes merged
+  for (int h0 = 0; h0 < Hq; h0 += n_grp) {
+    const int h = h0 + grp;                       // uniform over the 8 lanes of a group
+    const float* ph = pb + (size_t)min(h, Hq - 1) * nsplit * (D + 2) + D;
     float m = -INFINITY, l = 0.f;
-    for (int s0 = 0; s0 < nsplit; s0 += kB) {
-      float ms[kB], ls[kB];
+    for (int s0 = 0; s0 < nsplit; s0 += LN * kFinishBatch) {
+      float ms[kFinishBatch], ls[kFinishBatch];
 #pragma unroll
-      for (int u = 0; u < kB; ++u) {
-        const bool in = s0 + u < nsplit;
-        ms[u] = in ? ph[(s0 + u) * (D + 2)] : -INFINITY;
-        ls[u] = in ? ph[(s0 + u) * (D + 2) + 1] : 0.f;
+      for (int u = 0; u < kFinishBatch; ++u) {
+        const int sp = s0 + u * LN + sub;
+        const bool in = sp < nsplit;
+        ms[u] = in ? ph[(size_t)sp * (D + 2)] : -INFINITY;
+        ls[u] = in ? ph[(size_t)sp * (D + 2) + 1] : 0.f;
       }
       float mb = m;
 #pragma unroll
-      for (int u = 0; u < kB; ++u) mb = fmaxf(mb, ms[u]);
+      for (int u = 0; u < kFinishBatch; ++u) mb = fmaxf(mb, ms[u]);
       l = m == -INFINITY ? 0.f : l * __builtin_amdgcn_exp2f(m - mb);
 #pragma unroll
-      for (int u = 0; u < kB; ++u)
+      for (int u = 0; u < kFinishBatch; ++u)
         if (ms[u] != -INFINITY) l = fmaf(ls[u], __builtin_amdgcn_exp2f(ms[u] - mb), l);
       m = mb;
     }
-    ml[2 * h] = m;
-    ml[2 * h + 1] = 1.f / l;
+    const float M = group_max<LN>(m);
+    const float L = group_sum<LN>(m == -INFINITY ? 0.f : l * __builtin_amdgcn_exp2f(m - M));
+    if (sub == 0 && h < Hq) {
+      ml[2 * h] = M;
+      ml[2 * h + 1] = 1.f / L;
+    }
   }
   __syncthreads();
   const int n_out = Hq * D;
   const int e0 = (int)((long)j * n_out / nb), e1 = (int)((long)(j + 1) * n_out / nb);
-  for (int i = e0 + tid; i < e1; i += blockDim.x) {
-    const int h = i / D, c = i % D;
+  for (int i0 = e0; i0 < e1; i0 += n_grp) {
+    const int i = i0 + grp;                       // uniform over the 8 lanes of a group
+    const int ic = min(i, e1 - 1);
+    const int h = ic / D, c = ic % D;
     const float* ph = pb + (size_t)h * nsplit * (D + 2);
     const float m = ml[2 * h];
     float o = 0.f;
-    for (int s0 = 0; s0 < nsplit; s0 += kB) {
-      float ms[kB], vs[kB];
+    for (int s0 = 0; s0 < nsplit; s0 += LN * kFinishBatch) {
+      float ms[kFinishBatch], vs[kFinishBatch];
 #pragma unroll
-      for (int u = 0; u < kB; ++u) {
-        const bool in = s0 + u < nsplit;
-        ms[u] = in ? ph[(s0 + u) * (D + 2) + D] : -INFINITY;
-        vs[u] = in ? ph[(s0 + u) * (D + 2) + c] : 0.f;
+      for (int u = 0; u < kFinishBatch; ++u) {
+        const int sp = s0 + u * LN + sub;
+        const bool in = sp < nsplit;
+        ms[u] = in ? ph[(size_t)sp * (D + 2) + D] : -INFINITY;
+        vs[u] = in ? ph[(size_t)sp * (D + 2) + c] : 0.f;
       }
 #pragma unroll
-      for (int u = 0; u < kB; ++u)
+      for (int u = 0; u < kFinishBatch; ++u)
         if (ms[u] != -INFINITY) o = fmaf(vs[u], __builtin_amdgcn_exp2f(ms[u] - m), o);
     }
-    o *= ml[2 * h + 1];
-    const size_t oi = (size_t)b * n_out + i;
-    if (out_dtype == FADE_DTYPE_F32) reinterpret_cast<float*>(out)[oi] = o;
-    else if (out_dtype == FADE_DTYPE_BF16) reinterpret_cast<uint16_t*>(out)[oi] = f2bf(o);
-    else reinterpret_cast<uint16_t*>(out)[oi] = f2h(o);
+    o = group_sum<LN>(o) * ml[2 * h + 1];
+    if (sub == 0 && i < e1) {
+      const size_t oi = (size_t)b * n_out + i;
+      if (out_dtype == FADE_DTYPE_F32) reinterpret_cast<float*>(out)[oi] = o;
+      else if (out_dtype == FADE_DTYPE_BF16) reinterpret_cast<uint16_t*>(out)[oi] = f2bf(o);
+      else reinterpret_cast<uint16_t*>(out)[oi] = f2h(o);
+    }
   }
   if (!tok_attn) return;
   const int T = lens[4 * b] + lens[4 * b + 1] + lens[4 * b + 2];
@@ -684,15 +724,15 @@ __global__ __launch_bounds__(256) void k_decode_finish(const float* __restrict__
     const int u0 = tid % kFinishSlots, jj = j0 + u0, hg = tid / kFinishSlots;
     float acc = 0.f;
     if (jj < T && jj < cap_T) {
-      for (int h0 = hg; h0 < Hq; h0 += 4 * kB) {
-        float rv[kB];
+      for (int h0 = hg; h0 < Hq; h0 += 4 * kFinishBatch) {
+        float rv[kFinishBatch];
 #pragma unroll
-        for (int u = 0; u < kB; ++u) {
+        for (int u = 0; u < kFinishBatch; ++u) {
           const int h = h0 + 4 * u;
           rv[u] = h < Hq ? raw[((size_t)b * Hq + h) * cap_T + jj] : 0.f;
         }
 #pragma unroll
-        for (int u = 0; u < kB; ++u) {
+        for (int u = 0; u < kFinishBatch; ++u) {
           const int h = h0 + 4 * u;
           if (h < Hq) acc += __builtin_amdgcn_exp2f(rv[u] - ml[2 * h]) * ml[2 * h + 1];
         }
@@ -772,12 +812,22 @@ hipError_t launch_decode(const Shape& s, const fade_layer_cache& c, const void* 
   if (e != hipSuccess) return e;
   const dim3 fgrid(s.batch, (s.cap_T + kFinishSlots - 1) / kFinishSlots);
   const size_t flds = ((size_t)2 * s.Hq + 4 * kFinishSlots) * 4;
-  if (s.D == 128)
-    hipLaunchKernelGGL(k_decode_finish<128>, fgrid, dim3(256), flds, st, part, nsplit, s.Hq, out, out_dtype,
-                       raw, c.lens, s.cap_T, tok_attn);
-  else
-    hipLaunchKernelGGL(k_decode_finish<64>, fgrid, dim3(256), flds, st, part, nsplit, s.Hq, out, out_dtype,
-                       raw, c.lens, s.cap_T, tok_attn);
+  const bool wide = nsplit > kFinishBatch;
+  if (s.D == 128) {
+    if (wide)
+      hipLaunchKernelGGL((k_decode_finish<128, 8>), fgrid, dim3(256), flds, st, part, nsplit, s.Hq, out, out_dtype,
+                         raw, c.lens, s.cap_T, tok_attn);
+    else
+      hipLaunchKernelGGL((k_decode_finish<128, 1>), fgrid, dim3(256), flds, st, part, nsplit, s.Hq, out, out_dtype,
+                         raw, c.lens, s.cap_T, tok_attn);
+  } else {
+    if (wide)
+      hipLaunchKernelGGL((k_decode_finish<64, 8>), fgrid, dim3(256), flds, st, part, nsplit, s.Hq, out, out_dtype,
+                         raw, c.lens, s.cap_T, tok_attn);
+    else
+      hipLaunchKernelGGL((k_decode_finish<64, 1>), fgrid, dim3(256), flds, st, part, nsplit, s.Hq, out, out_dtype,
+                         raw, c.lens, s.cap_T, tok_attn);
+  }
   return hipGetLastError();
 }
 
