@@ -37,6 +37,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="c5", choices=["c1", "c2", "c3", "c4", "c5"])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--overlap-steps", type=int, default=16,
+                   help="extra timed steps, after the main ones, with the admitted sequence's H2O prefill pass "
+                        "on a stream of its own (0 = skip)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="run one device copy of this size before timing (HBM counter calibration)")
     return p.parse_args()
@@ -71,6 +74,7 @@ class Workload:
         self.cfg = fade.make_config(int4_budget=w["int4_budget"], **common)
         self.cfg_build = fade.make_config(int4_budget=-1 if name == "c5" else w["int4_budget"], **common)
         self.side = self.policy in ("h2o", "ema")
+        self.admit_stream = None      # set by use_admit_stream()
 
     # ---- setup (untimed) ---------------------------------------------------
     def _kv(self, seed, L):
@@ -201,12 +205,23 @@ class Workload:
                 m = budget
             self.M[b] = m
 
+    def use_admit_stream(self, on):
+        """The admitted sequence's prefill scoring shares no data with the
+        running batch's decode step; with `on` it runs on a stream of its own
+        (default priority) that joins the decode stream at the end of each
+        step."""
+        self.admit_stream = self.torch.cuda.Stream(device=self.dev) if (on and self.admit is not None) else None
+
     # ---- one step --------------------------------------------------------------
     def step(self, events=None, h2o_events=None):
         fade = self.fade
         t = self.step_idx
         due = self.w["int4_budget"] >= 0 and ((t + 1) % self.period == 0)
         pol = fade.POLICY_POSITION if self.policy == "position" else fade.POLICY_SCORE
+        torch = self.torch
+        main = torch.cuda.current_stream()
+        if self.admit_stream is not None:
+            self.admit_stream.wait_stream(main)
         for l in range(self.layers):
             tc = self.caches[l]
             q, kn, vn = self.pool[l][t % 4]
@@ -225,12 +240,15 @@ class Workload:
                 fade.fade_evict_rerope(self.cfg, tc, pol, self.ws_ev)
             if self.admit is not None:
                 qa, ka = self.admit[l]
-                if h2o_events is not None and h2o_events[l] is not None:
-                    h2o_events[l][0].record()
-                fade.fade_h2o_scores(self.cfg, fade.SCORE_PREFILL, q_prefill=qa, k_prefill=ka, batch=1,
-                                     L=qa.shape[2], shared=0, scores_out=self.admit_scores, ws=self.ws_h2o)
-                if h2o_events is not None and h2o_events[l] is not None:
-                    h2o_events[l][1].record()
+                with torch.cuda.stream(self.admit_stream if self.admit_stream is not None else main):
+                    if h2o_events is not None and h2o_events[l] is not None:
+                        h2o_events[l][0].record()
+                    fade.fade_h2o_scores(self.cfg, fade.SCORE_PREFILL, q_prefill=qa, k_prefill=ka, batch=1,
+                                         L=qa.shape[2], shared=0, scores_out=self.admit_scores, ws=self.ws_h2o)
+                    if h2o_events is not None and h2o_events[l] is not None:
+                        h2o_events[l][1].record()
+        if self.admit_stream is not None:
+            main.wait_stream(self.admit_stream)
 
 
 class TimingEvent:
@@ -375,7 +393,7 @@ def main():
     wl = Workload(a.workload, dev)
     print(f"[bench] setting up workload {a.workload} ...", file=sys.stderr, flush=True)
     t_setup = time.perf_counter()
-    wl.setup(a.warmup + steps)
+    wl.setup(a.warmup + steps + a.overlap_steps + 1)
     print(f"[bench] setup {time.perf_counter() - t_setup:.1f}s; warmup {a.warmup} steps", file=sys.stderr, flush=True)
     if a.calib_copy_mib:
         n = a.calib_copy_mib * (1 << 20) // 4
@@ -438,7 +456,8 @@ def main():
                                 "c4": "Llama-3-8B-like: 32 layers, B1, 32q/8kv, d128, prefill 131072 -> position budget 8192, W128, K4/V2, bf16 q",
                                 "c5": "ragged serving batch: 64 sequences, context U[1024,32768], 32 layers, 32q/8kv, d128, K4/V2, EMA 0.9 eviction to 2048 per sequence, one 2048-token H2O prefill pass per step"}[a.workload],
                    "name": a.workload, "layers": wl.layers, "batch": wl.B,
-                   "kv_tokens_attended_per_step": dec_tokens // steps},
+                   "kv_tokens_attended_per_step": dec_tokens // steps,
+                   "admit_prefill_stream": None if wl.admit is None else "decode"},
         "decode_attn": {"avg_us_per_launch": avg_dec_us, "bytes_per_launch": bytes_per_launch,
                         "kernels": "k_decode_tiers + k_decode_finish",
                         "timed_launches": timed, "timed_every_nth_layer": TIME_EVERY},
@@ -459,6 +478,30 @@ def main():
                               "flops_per_launch": flops, "bound": "mfma", "achieved": flops / (us * 1e-6) / 1e12,
                               "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                               "frac": flops / (us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, "timed_launches": n_h2o}
+    if wl.admit is not None and a.overlap_steps > 0:
+        # The same steps with the admitted sequence's prefill pass overlapped
+        # with the decode step on a second stream: whole-step throughput as a
+        # server would run it (the decode kernels then share the GPU, so the
+        # roofline above is taken from the serial steps).
+        wl.use_admit_stream(True)
+        wl.step()
+        wl.advance_mirror()
+        tok = 0
+        o0 = torch.cuda.Event(enable_timing=True)
+        o1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        o0.record()
+        for _ in range(a.overlap_steps):
+            tok += wl.decode_bytes_and_tokens()[1] * wl.layers
+            wl.step()
+            wl.advance_mirror()
+        o1.record()
+        torch.cuda.synchronize()
+        oms = o0.elapsed_time(o1)
+        res["admit_overlapped"] = {"value": tok / (oms * 1e-3), "unit": "tokens/s", "steps": a.overlap_steps,
+                                   "ms_per_step": oms / a.overlap_steps,
+                                   "note": "admitted sequence's H2O prefill pass on its own stream"}
+        wl.use_admit_stream(False)
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample ...", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(a.workload)
