@@ -54,3 +54,22 @@ def update_accum(scores, side):
 
 def update_ema(scores, side, beta):
     return beta * np.asarray(scores, dtype=np.float64) + (1.0 - beta) * np.asarray(side, dtype=np.float64)
+
+
+def prefill_colsum_rows(q, k, i0, i1):
+    """Contribution of the causal query rows i0 .. i1-1 to every column:
+    sum_h sum_{i0 <= i < i1} P_h[i, j], float64 [L]. Column j only receives
+    rows i >= j, so for i1 = L the columns j >= i0 are complete: the H2O
+    scores of the last L - i0 keys, computed from those rows alone."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    hq, L, d = q.shape
+    n_rep = hq // k.shape[0]
+    scores = np.zeros(L)
+    scale = 1.0 / np.sqrt(d)
+    for h in range(hq):
+        for i in range(i0, i1):
+            s = (k[h // n_rep, :i + 1] @ q[h, i]) * scale         # keys 0 .. i
+            e = np.exp(s - s.max())
+            scores[:i + 1] += e / e.sum()
+    return scores

@@ -66,6 +66,7 @@ CASES = [
     (128, 8, 8, 2, 2, 300, -1, 32, "f16", 2),       # MHA, INT2 K and V
     (64, 16, 8, 2, 4, 260, -1, 16, "f16", 1),       # n_rep 2
     (128, 32, 8, 4, 2, 2100, -1, 64, "f16", 2),     # several splits + ragged tail
+    (128, 8, 1, 4, 2, 20000, -1, 64, "f16", 1),     # one KV head, 80 splits: two rounds of the 8-lane merge
 ]
 
 

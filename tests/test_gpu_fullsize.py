@@ -145,3 +145,39 @@ def test_serving_batch_full_size_sampled():
         assert r.mid_len == min(budget, T0[b] - S - W + 1)
         if lowest[1] - lowest[0] > 1e-5 * abs(lowest[0]):
             assert_state_equal(seq_state(tc, b), r, check_scores=False)
+
+
+@pytest.mark.parametrize("name", ["c2", "c3"])
+def test_h2o_prefill_full_size_tail_and_total(name):
+    """H2O prefill column sums at the Qwen2.5-3B-like (4096 tokens, 16 / 2
+    heads, d 128) and Llama-3.2-1B-like (16 sequences summed, 8192 tokens,
+    32 / 8 heads, d 64) prefill shapes. Every causal row's probabilities sum
+    to one, so the scores total Hq * L per sequence; the last 8 keys are
+    compared with the oracle's column sums of the last 8 rows, which are
+    complete for those keys."""
+    from oracle import h2o
+    w = synth.WORKLOADS[name]
+    d, hq, hkv, L, B = w["head_dim"], w["n_q_heads"], w["n_kv_heads"], w["context"], w["batch"]
+    shared = bool(w.get("shared", False))
+    cfg = fade.make_config(head_dim=d, n_q_heads=hq, n_kv_heads=hkv, n_sink=w["n_sink"],
+                           recent_window=w["recent_window"], int4_budget=w["int4_budget"])
+    q = synth.torch_normal((B, hq, L, d), 2600 + d, DEV, torch.float16)
+    k = synth.torch_normal((B, hkv, L, d), 2700 + d, DEV, torch.float16)
+    rows = 1 if shared else B
+    out = torch.zeros(rows, L, dtype=torch.float32, device=DEV)
+    ws = fade.workspace(cfg, fade.WS_H2O_PREFILL, B, L)
+    fade.fade_h2o_scores(cfg, fade.SCORE_PREFILL, q_prefill=q, k_prefill=k, batch=B, L=L, shared=shared,
+                         scores_out=out, ws=ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.all(got >= 0)
+    assert np.allclose(got.sum(axis=1), hq * L * (B if shared else 1), rtol=1e-5)
+    m = 8
+    want = np.zeros((rows, L))
+    for b in range(B):
+        qb = np.zeros((hq, L, d))
+        qb[:, L - m:] = q[b, :, L - m:].float().cpu().numpy()
+        kb = k[b].float().cpu().numpy()
+        want[0 if shared else b] += h2o.prefill_colsum_rows(qb, kb, L - m, L)
+    assert np.allclose(got[:, L - m:], want[:, L - m:], rtol=1e-4, atol=1e-6), \
+        float(np.abs(got[:, L - m:] / want[:, L - m:] - 1).max())

@@ -111,3 +111,19 @@ def test_score_updates():
     for _ in range(7):
         e = h2o.update_ema(e, a, 0.9)
     assert np.allclose(e, a * (1 - 0.9 ** 7), rtol=1e-14)   # geometric series from 0
+
+
+def test_colsum_rows_blocks_add_up_and_complete_the_tail():
+    """Row blocks of prefill_colsum_rows add up to prefill_colsum, and the
+    columns at or after a block's first row are complete with the rows from
+    there on (only rows i >= j reach column j)."""
+    from oracle import h2o
+    gen = synth.rng(930)
+    q = synth.normal(gen, 4, 37, 8)
+    k = synth.normal(gen, 2, 37, 8)
+    full = h2o.prefill_colsum(q, k)
+    parts = h2o.prefill_colsum_rows(q, k, 0, 10) + h2o.prefill_colsum_rows(q, k, 10, 37)
+    assert np.allclose(parts, full, rtol=1e-12, atol=1e-12)
+    tail = h2o.prefill_colsum_rows(q, k, 30, 37)
+    assert np.allclose(tail[30:], full[30:], rtol=1e-12, atol=1e-12)
+    assert np.isclose(h2o.prefill_colsum_rows(q, k, 36, 37).sum(), 4.0)
