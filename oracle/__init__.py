@@ -20,13 +20,15 @@ value is rounded only where a step stores it. Where the pages are silent the
 plainest reading is taken; each reading is named where it is used.
 
 Modules:
-  rope        rotary embedding (standard and llama3 frequency scaling)
+  rope        rotary embedding (default, llama3, linear, ntk, yarn, dynamic,
+              proportional, none; rotate-half or interleaved pairing)
   quant       symmetric INTb quantizer, bit-packing, dequantizer
   attention   joint-softmax decode attention over all tiers, side output
   h2o         H2O prefill column sums, cumulative / EMA score updates
   cache       the three-tier cache: tier layout, prefill build, append,
               demotion, eviction with un-RoPE / re-RoPE compaction
   accounting  compressed-bytes closed form
+  pq          product-quantization codebook: Lloyd training, encode, decode
 
 Parity status: every function here is pinned by `tests/test_oracle_*.py`
 against closed forms, library routines, invariants or brute force.
