@@ -656,9 +656,10 @@ __global__ __launch_bounds__(256) void k_decode_finish(const float* __restrict__
   const int b = blockIdx.x, j = blockIdx.y, nb = gridDim.y, tid = threadIdx.x;
   const int sub = tid % LN, grp = tid / LN, n_grp = blockDim.x / LN;
   const float* pb = part + (size_t)b * Hq * nsplit * (D + 2);
-  // statistics: lanes sub, sub + 8, ... of a head's splits, then the 8 lanes merged
+  // statistics: lane sub of a group of LN takes splits sub, sub + LN, ...; the
+  // group's lanes are then merged
   for (int h0 = 0; h0 < Hq; h0 += n_grp) {
-    const int h = h0 + grp;                       // uniform over the 8 lanes of a group
+    const int h = h0 + grp;                       // uniform over the LN lanes of a group
     const float* ph = pb + (size_t)min(h, Hq - 1) * nsplit * (D + 2) + D;
     float m = -INFINITY, l = 0.f;
     for (int s0 = 0; s0 < nsplit; s0 += LN * kFinishBatch) {
@@ -690,7 +691,7 @@ __global__ __launch_bounds__(256) void k_decode_finish(const float* __restrict__
   const int n_out = Hq * D;
   const int e0 = (int)((long)j * n_out / nb), e1 = (int)((long)(j + 1) * n_out / nb);
   for (int i0 = e0; i0 < e1; i0 += n_grp) {
-    const int i = i0 + grp;                       // uniform over the 8 lanes of a group
+    const int i = i0 + grp;                       // uniform over the LN lanes of a group
     const int ic = min(i, e1 - 1);
     const int h = ic / D, c = ic % D;
     const float* ph = pb + (size_t)h * nsplit * (D + 2);
