@@ -811,9 +811,14 @@ hipError_t launch_decode(const Shape& s, const fade_layer_cache& c, const void* 
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 fgrid(s.batch, (s.cap_T + kFinishSlots - 1) / kFinishSlots);
-  const size_t flds = ((size_t)2 * s.Hq + 4 * kFinishSlots) * 4;
+  // Workgroups per sequence: each rebuilds the statistics, so with few splits
+  // fewer and longer ones pay less of that (two 64-slot blocks each with the
+  // side output, four blocks' share of the outputs without it); with many
+  // splits each output costs a round trip, so they stay one block each.
   const bool wide = nsplit > kFinishBatch;
+  const int blocks_per_wg = wide ? 1 : (tok_attn ? 2 : 4);
+  const dim3 fgrid(s.batch, (s.cap_T + blocks_per_wg * kFinishSlots - 1) / (blocks_per_wg * kFinishSlots));
+  const size_t flds = ((size_t)2 * s.Hq + 4 * kFinishSlots) * 4;
   if (s.D == 128) {
     if (wide)
       hipLaunchKernelGGL((k_decode_finish<128, 8>), fgrid, dim3(256), flds, st, part, nsplit, s.Hq, out, out_dtype,
