@@ -811,13 +811,23 @@ hipError_t launch_decode(const Shape& s, const fade_layer_cache& c, const void* 
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // Workgroups per sequence: each rebuilds the statistics, so with few splits
-  // fewer and longer ones pay less of that (two 64-slot blocks each with the
-  // side output, four blocks' share of the outputs without it); with many
-  // splits each output costs a round trip, so they stay one block each.
+  // Workgroups per sequence. Each rebuilds the statistics (Hq x nsplit
+  // partial heads), so their number follows the work that needs spreading:
+  // with the side output, the slots (two 64-slot blocks per workgroup with
+  // few splits, one with many), capped so that the statistics stay a small
+  // share of a workgroup's reads on long caches; without it, the outputs
+  // (one round of 32 elements per workgroup with many splits, 512 with few).
   const bool wide = nsplit > kFinishBatch;
-  const int blocks_per_wg = wide ? 1 : (tok_attn ? 2 : 4);
-  const dim3 fgrid(s.batch, (s.cap_T + blocks_per_wg * kFinishSlots - 1) / (blocks_per_wg * kFinishSlots));
+  int nb;
+  if (tok_attn) {
+    const int blocks = wide ? 1 : 2;
+    nb = (s.cap_T + blocks * kFinishSlots - 1) / (blocks * kFinishSlots);
+    nb = min(nb, max(1, s.cap_T / (16 * nsplit)));
+  } else {
+    const int per_wg = wide ? 256 / 8 : 512;
+    nb = (s.Hq * s.D + per_wg - 1) / per_wg;
+  }
+  const dim3 fgrid(s.batch, nb);
   const size_t flds = ((size_t)2 * s.Hq + 4 * kFinishSlots) * 4;
   if (s.D == 128) {
     if (wide)
