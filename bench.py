@@ -35,7 +35,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=None)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", default="c5", choices=["c1", "c2", "c3", "c4", "c5"])
+    p.add_argument("--workload", default="c5", choices=["c1", "c2", "c3", "c4", "c5", "s4"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--overlap-steps", type=int, default=16,
                    help="extra timed steps, after the main ones, with the admitted sequence's H2O prefill pass "
@@ -389,7 +389,7 @@ def main():
     fade.lib()
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    steps = a.steps if a.steps is not None else {"c1": 50, "c2": 64, "c3": 64, "c4": 32, "c5": 32}[a.workload]
+    steps = a.steps if a.steps is not None else {"c1": 50, "c2": 64, "c3": 64, "c4": 32, "c5": 32, "s4": 8}[a.workload]
     wl = Workload(a.workload, dev)
     print(f"[bench] setting up workload {a.workload} ...", file=sys.stderr, flush=True)
     t_setup = time.perf_counter()
@@ -454,6 +454,7 @@ def main():
                                 "c2": "Qwen2.5-3B-like: 36 layers, B1, 16q/2kv, d128, prefill 4096 H2O -> budget 400, K4/V2",
                                 "c3": "Llama-3.2-1B-like: 16 layers, B16 shared, 32q/8kv, d64, llama3 RoPE, budget 1024, K4/V4, evict every 256 steps",
                                 "c4": "Llama-3-8B-like: 32 layers, B1, 32q/8kv, d128, prefill 131072 -> position budget 8192, W128, K4/V2, bf16 q",
+                                "s4": "supplementary HBM stress point: Llama-3-8B-like shape, 32 layers, B1, 131072 tokens kept tiered (no eviction), W128, K4/V2, bf16 q",
                                 "c5": "ragged serving batch: 64 sequences, context U[1024,32768], 32 layers, 32q/8kv, d128, K4/V2, EMA 0.9 eviction to 2048 per sequence, one 2048-token H2O prefill pass per step"}[a.workload],
                    "name": a.workload, "layers": wl.layers, "batch": wl.B,
                    "kv_tokens_attended_per_step": dec_tokens // steps,

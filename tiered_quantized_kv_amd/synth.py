@@ -36,6 +36,12 @@ WORKLOADS = {
                context=131072, rope_type="default", rope_theta=5e5, n_sink=4,
                recent_window=128, int4_budget=8192, middle_k_bits=4, middle_v_bits=2,
                policy="position", decode_steps=64, q_dtype="bf16", evict_period=1),
+    # supplementary HBM stress point: the Llama-3-8B-like shape with the whole
+    # 131072-token context kept in the tiers (no eviction)
+    "s4": dict(index=6, layers=32, batch=1, n_q_heads=32, n_kv_heads=8, head_dim=128,
+               context=131072, rope_type="default", rope_theta=5e5, n_sink=4,
+               recent_window=128, int4_budget=-1, middle_k_bits=4, middle_v_bits=2,
+               policy="none", decode_steps=8, q_dtype="bf16", evict_period=1),
     "c5": dict(index=5, layers=32, batch=64, n_q_heads=32, n_kv_heads=8, head_dim=128,
                context_range=(1024, 32768), rope_type="default", rope_theta=5e5,
                n_sink=4, recent_window=64, int4_budget=2048, middle_k_bits=4,
