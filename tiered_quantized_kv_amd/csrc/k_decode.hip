@@ -49,6 +49,7 @@ struct DecodeArgs {
   float* part;        // [B, Hq, nsplit, D + 2]
   float* raw;         // [B, Hq, cap_T] (log2-domain scores) or nullptr
   int batch, Hkv, n_sink, ring, cap_mid, cap_T, chunk, nsplit;
+  int n_fp, fp_per;   // fp16-tier splits (0 .. n_fp - 1) and fp16 slots per split
   float qk_scale;     // log2(e) / sqrt(D)
 };
 
@@ -70,8 +71,19 @@ int decode_chunk(const Shape& s) {
   return chunk;
 }
 
+// FP16-tier splits: the fp16 tier (sinks + ring) is cut into as many
+// workgroups as it takes for none to stream more bytes than a middle split,
+// up to 4, so a long ring next to short middle chunks is not the last
+// workgroup to finish.
+int decode_fp_splits(const Shape& s) {
+  const long fp_bytes = (long)(s.n_sink + s.ring) * s.D * 4;
+  const long mid_bytes = (long)decode_chunk(s) * ((s.D * s.kb / 8 + s.D / 16) + (s.D * s.vb / 8 + s.D / 16));
+  const long n = (fp_bytes + mid_bytes - 1) / mid_bytes;
+  return (int)(n < 1 ? 1 : (n > 4 ? 4 : n));
+}
+
 int decode_nsplit(const Shape& s) {
-  return 1 + (s.cap_mid + decode_chunk(s) - 1) / decode_chunk(s);
+  return decode_fp_splits(s) + (s.cap_mid + decode_chunk(s) - 1) / decode_chunk(s);
 }
 
 size_t decode_ws_bytes(const Shape& s) {
@@ -205,12 +217,14 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
   float* wml = kf + HQ4 * 4;                                                 // [4][2][HQ4 * 4]
   unsigned char* wreg = smem + Lay::head_bytes;
 
-  // 1-D grid, middle splits first (split 1 of every (sequence, KV head),
-  // then split 2, ...) and the FP16 tier last: the long middle workgroups are
-  // dealt evenly over the CUs before the short ones fill the gaps.
+  // 1-D grid, middle splits first (split n_fp of every (sequence, KV head),
+  // then split n_fp + 1, ...) and the FP16-tier splits last: the long middle
+  // workgroups are dealt evenly over the CUs before the short ones fill the
+  // gaps.
   const int n_pairs = a.batch * a.Hkv;
   const int gsplit = blockIdx.x / n_pairs, pair = blockIdx.x - gsplit * n_pairs;
-  const int split = gsplit + 1 < a.nsplit ? gsplit + 1 : 0;
+  const int n_mid_splits = a.nsplit - a.n_fp;
+  const int split = gsplit < n_mid_splits ? gsplit + a.n_fp : gsplit - n_mid_splits;
   const int g = pair % a.Hkv, b = pair / a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int Hq = a.Hkv * NREP;
@@ -218,9 +232,10 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
   // Lengths are clamped to capacity so no value in lens can index out of bounds.
   const int S = min(max(L[0], 0), a.n_sink), M = min(max(L[1], 0), a.cap_mid);
   const int R = min(max(L[2], 0), a.ring), rhead = min(max(L[3], 0), a.ring - 1);
-  const bool fpt = split == 0;                       // FP16 tier
-  const int row0 = fpt ? 0 : (split - 1) * a.chunk;
-  const int n_tok = fpt ? S + R : min(a.chunk, M - row0);
+  const bool fpt = split < a.n_fp;                   // FP16 tier
+  const int row0 = fpt ? 0 : (split - a.n_fp) * a.chunk;
+  const int fp_lo = fpt ? split * a.fp_per : 0;     // this split's fp16 tokens [fp_lo, fp_lo + n_tok)
+  const int n_tok = fpt ? min(a.fp_per, S + R - fp_lo) : min(a.chunk, M - row0);
 
   float* part_base = a.part + ((size_t)(b * Hq + g * NREP) * a.nsplit + split) * (D + 2);
   const size_t part_hstride = (size_t)a.nsplit * (D + 2);
@@ -509,7 +524,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
       const bool valid = lane < ns;
       f32x4 d0[HQ4], d1[HQ4];
       {
-        const uint4* kp = reinterpret_cast<const uint4*>(fk + (size_t)slot_of(base + min(lane, ns - 1)) * D);
+        const uint4* kp = reinterpret_cast<const uint4*>(fk + (size_t)slot_of(fp_lo + base + min(lane, ns - 1)) * D);
         uint32_t w[D / 2];
 #pragma unroll
         for (int i = 0; i < D / 8; ++i) {
@@ -533,7 +548,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
       auto load_v = [&](int g0, int nt) {
         // each lane finds the slot of one token (lanes past nt repeat the
         // last); token k's row address is then wave-uniform, read from lane k
-        const int my_slot = slot_of(base + g0 + min(lane, nt - 1));
+        const int my_slot = slot_of(fp_lo + base + g0 + min(lane, nt - 1));
 #pragma unroll
         for (int k = 0; k < VB32; ++k) {
           const uint16_t* vr = fv + (size_t)__builtin_amdgcn_readlane(my_slot, k) * D;
@@ -543,7 +558,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
       };
       load_v(0, min(VB32, ns));
       float s2[HQ4 * 4];
-      const int tv = base + lane;
+      const int tv = fp_lo + base + lane;
       const int pos = tv < S ? tv : S + M + (tv - S);
 #pragma unroll
       for (int h = 0; h < HQ4 * 4; ++h) {
@@ -800,6 +815,8 @@ hipError_t launch_decode(const Shape& s, const fade_layer_cache& c, const void* 
   a.cap_T = s.cap_T;
   a.chunk = chunk;
   a.nsplit = nsplit;
+  a.n_fp = decode_fp_splits(s);
+  a.fp_per = (s.n_sink + s.ring + a.n_fp - 1) / a.n_fp;
   a.qk_scale = kLog2e / sqrtf((float)s.D);
   const dim3 grid(nsplit * s.Hkv * s.batch);
   if (s.D == 128) {
