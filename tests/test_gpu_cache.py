@@ -140,14 +140,17 @@ def test_rope_schemes_prefill_and_decode_eviction(rtype):
         assert_state_equal(seq_state(tc, b), refs[b])
 
 
+@pytest.mark.parametrize("policy,extra", [("score", 37), ("position", 37), ("score", 1)])
 @pytest.mark.parametrize("d,kb,vb,rtype", [(128, 4, 2, "default"), (64, 2, 4, "yarn"), (64, 4, 4, "proportional")])
-def test_interleaved_pairing_prefill_and_decode_eviction(d, kb, vb, rtype):
+def test_interleaved_pairing_prefill_and_decode_eviction(d, kb, vb, rtype, policy, extra):
     """GPT-J pairing through both compactions: the prefill build's fp16
     re-RoPE (lanes trade values back to the storage layout), the ring
-    rotation and the middle rebuild over adjacent-channel pairs."""
+    rotation and the middle rebuild over adjacent-channel pairs; the decode
+    event evicts by score (a general selection, or one token) or by position
+    (one run of 37 slots)."""
     kw = dict(ROPE_KW[rtype]) if rtype != "default" else dict(rope_theta=1e6)
     kw["rope_interleaved"] = True
-    budget, extra = 300, 37
+    budget = 300
     L = 4 + budget + extra + 32
     B = 2
     cfg0 = _cfg(d=d, hq=8, hkv=2, n_sink=4, w=32, budget=budget + extra, kb=kb, vb=vb, **kw)
@@ -157,11 +160,11 @@ def test_interleaved_pairing_prefill_and_decode_eviction(d, kb, vb, rtype):
         assert_state_equal(seq_state(tc, b), refs[b])
     cfg = _cfg(d=d, hq=8, hkv=2, n_sink=4, w=32, budget=budget, kb=kb, vb=vb, **kw)
     ws = fade.workspace(cfg, fade.WS_EVICT, B, budget + extra)
-    fade.fade_evict_rerope(cfg, tc, fade.POLICY_SCORE, ws)
+    fade.fade_evict_rerope(cfg, tc, fade.POLICY_POSITION if policy == "position" else fade.POLICY_SCORE, ws)
     torch.cuda.synchronize()
     for b in range(B):
         refs[b].cfg = ocfg(cfg)
-        oc.evict(refs[b], budget, "score")
+        oc.evict(refs[b], budget, policy)
         assert_state_equal(seq_state(tc, b), refs[b])
 
 

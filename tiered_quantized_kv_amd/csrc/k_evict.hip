@@ -32,7 +32,12 @@ namespace fade {
 
 constexpr int kSelThreads = 1024;
 constexpr int kInfo = 8;   // ints per row of the selection record:
-                           // {M, n_evict, S, R, first evicted middle slot (M if none)}
+                           // {M, n_evict, S, R, first evicted middle slot (M if none),
+                           //  1 if the evicted slots are the run [first, first + n_evict)
+                           //  and no map was written}
+
+// Destination of middle slot r when the evicted slots are the run [e, e + n).
+__device__ __forceinline__ int run_dst(int r, int e, int n) { return r < e ? r : (r < e + n ? -1 : r - n); }
 
 __device__ __forceinline__ uint32_t ordered_key(float f) {
   if (f == 0.f) f = 0.f;                       // -0 and +0 are the same score
@@ -223,55 +228,77 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
     thr = prefix;
     n_eq_ev = kk;
   }
-  // Assign new slots in ascending slot order. In decode mode the row's
-  // scores are compacted in the same pass: each chunk's values are read
-  // before the scan's barriers and written after them, and destinations never
-  // exceed sources, so later chunks' sources are untouched.
-  __shared__ int s_first_ev;
-  if (tid == 0) s_first_ev = single ? e1 : M;
-  __syncthreads();
-  int base_eq = 0, base_keep = 0;
-  const bool by_score = n_ev > 0 && !by_pos && !single;   // uniform over the workgroup
-  // every key equal to the cutoff is evicted (the usual case): no tie ranks
-  const bool all_eq = !by_score || n_eq_ev >= s_eqcnt;
+  // In decode mode a single eviction and the position policy evict one run of
+  // slots [first, first + n_ev) (first = the argmin, resp. 0): the compaction
+  // derives every destination from the run, so no map is written and only the
+  // score row is compacted (info[5] = 1 marks the run).
+  const bool run = a.decode && n_ev > 0 && (single || by_pos);
   float* srow = (a.decode && n_ev > 0 && a.cache_scores) ? a.cache_scores + (size_t)row * a.cap_T : nullptr;
-  for (int c0 = 0; c0 < M; c0 += kSelThreads) {
-    const int r = c0 + tid;
-    const float sv = srow && r < M ? srow[S + r] : 0.f;
-    bool ev = false;
-    if (single) {
-      ev = r == e1;
-    } else if (by_score) {
-      const uint32_t key = r < M ? key_at(r) : 0u;
-      const bool eq = r < M && key == thr;
-      if (all_eq) {
-        ev = r < M && key <= thr;
-      } else {
-        int tot_eq;
-        const int eq_rank = block_excl_scan(eq ? 1 : 0, &tot_eq, wsum) + base_eq;
-        base_eq += tot_eq;
-        ev = r < M && (key < thr || (eq && eq_rank < n_eq_ev));
+  __shared__ int s_first_ev;
+  if (a.decode && (run || n_ev == 0)) {
+    const int e = single ? e1 : (n_ev > 0 ? 0 : M);
+    if (srow) {
+      for (int c0 = 0; c0 < M; c0 += kSelThreads) {
+        const int r = c0 + tid;
+        const float sv = r < M ? srow[S + r] : 0.f;
+        __syncthreads();                // this chunk's reads before its writes
+        if (r < M && r >= e + n_ev) srow[S + r - n_ev] = sv;
       }
-    } else if (n_ev > 0) {
-      ev = r < n_ev;
     }
-    const bool keep = r < M && !ev;
-    int keep_rank;
-    if (single) {
-      keep_rank = r - (r > e1 ? 1 : 0);
-      __syncthreads();                  // this chunk's score reads before its writes
-    } else {
-      const uint64_t evm = __ballot(r < M && ev);     // first evicted slot, one atomic per wave
-      if ((tid & 63) == 0 && evm) atomicMin(&s_first_ev, c0 + (tid & ~63) + (int)__builtin_ctzll(evm));
-      int tot_keep;
-      keep_rank = block_excl_scan(keep ? 1 : 0, &tot_keep, wsum) + base_keep;
-      base_keep += tot_keep;
+    if (tid == 0) {
+      a.info[kInfo * row + 4] = e;
+      a.info[kInfo * row + 5] = run ? 1 : 0;
     }
-    if (r < M) map[r] = keep ? keep_rank : -1;
-    if (srow && keep) srow[S + keep_rank] = sv;
+  } else {
+    if (tid == 0) a.info[kInfo * row + 5] = 0;
+    // Assign new slots in ascending slot order. In decode mode the row's
+    // scores are compacted in the same pass: each chunk's values are read
+    // before the scan's barriers and written after them, and destinations never
+    // exceed sources, so later chunks' sources are untouched.
+    if (tid == 0) s_first_ev = single ? e1 : M;
+    __syncthreads();
+    int base_eq = 0, base_keep = 0;
+    const bool by_score = n_ev > 0 && !by_pos && !single;   // uniform over the workgroup
+    // every key equal to the cutoff is evicted (the usual case): no tie ranks
+    const bool all_eq = !by_score || n_eq_ev >= s_eqcnt;
+    for (int c0 = 0; c0 < M; c0 += kSelThreads) {
+      const int r = c0 + tid;
+      const float sv = srow && r < M ? srow[S + r] : 0.f;
+      bool ev = false;
+      if (single) {
+        ev = r == e1;
+      } else if (by_score) {
+        const uint32_t key = r < M ? key_at(r) : 0u;
+        const bool eq = r < M && key == thr;
+        if (all_eq) {
+          ev = r < M && key <= thr;
+        } else {
+          int tot_eq;
+          const int eq_rank = block_excl_scan(eq ? 1 : 0, &tot_eq, wsum) + base_eq;
+          base_eq += tot_eq;
+          ev = r < M && (key < thr || (eq && eq_rank < n_eq_ev));
+        }
+      } else if (n_ev > 0) {
+        ev = r < n_ev;
+      }
+      const bool keep = r < M && !ev;
+      int keep_rank;
+      if (single) {
+        keep_rank = r - (r > e1 ? 1 : 0);
+        __syncthreads();                  // this chunk's score reads before its writes
+      } else {
+        const uint64_t evm = __ballot(r < M && ev);     // first evicted slot, one atomic per wave
+        if ((tid & 63) == 0 && evm) atomicMin(&s_first_ev, c0 + (tid & ~63) + (int)__builtin_ctzll(evm));
+        int tot_keep;
+        keep_rank = block_excl_scan(keep ? 1 : 0, &tot_keep, wsum) + base_keep;
+        base_keep += tot_keep;
+      }
+      if (r < M) map[r] = keep ? keep_rank : -1;
+      if (srow && keep) srow[S + keep_rank] = sv;
+    }
+    __syncthreads();
+    if (tid == 0) a.info[kInfo * row + 4] = s_first_ev;
   }
-  __syncthreads();
-  if (tid == 0) a.info[kInfo * row + 4] = s_first_ev;
   if (!a.decode || n_ev == 0) return;
   // The recent-ring scores follow the survivors: S + M + i -> S + M - n_ev + i.
   if (srow) {
@@ -307,6 +334,10 @@ struct CompactArgs {
 };
 
 constexpr int kCompactRows = 128;   // middle rows per compaction workgroup
+constexpr int kRingPairs = 1024;    // rotation pairs of the recent ring per workgroup
+constexpr int kRingPer = kRingPairs / 256;
+
+__host__ __device__ constexpr int ring_blocks(int ring, int D) { return (ring + kRingPairs / (D / 2) - 1) / (kRingPairs / (D / 2)); }
 
 // OR over aligned groups of N lanes (N = 8 or 16), result in every lane of
 // the group: quad xor 1, quad xor 2, half-row mirror, then row mirror.
@@ -371,7 +402,7 @@ __device__ __forceinline__ void rotate_pair(float x1, float x2, double c, double
 }
 
 // Middle-tier compaction of one chunk of kCompactRows rows of one (sequence,
-// KV head); the extra x-block re-rotates the recent ring in place.
+// KV head); the x-blocks past the chunks re-rotate the recent ring in place.
 //
 // Moved rows are staged in LDS with coalesced 16-byte loads. Each wave then
 // rebuilds 8 rows per pass (16 at D = 64) with one lane per 8 rotation pairs:
@@ -383,7 +414,6 @@ __device__ __forceinline__ void rotate_pair(float x1, float x2, double c, double
 template <int D, int KB, int VB>
 __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
   constexpr int HALF = D / 2;                   // rotation pairs per row
-  constexpr int RPW = 64 / HALF;                // rows per wave pass
   constexpr int NG = D / 32;
   constexpr int KROW = D * KB / 8, VROW = D * VB / 8;
   constexpr int CH = kCompactRows;
@@ -396,28 +426,46 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
   const int cidx = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const Shape& s = a.s;
   const int mrow = s.shared ? 0 : b;
-  const int M = a.info[kInfo * mrow + 0], n_ev = a.info[kInfo * mrow + 1];
+  const int4 inf0 = *reinterpret_cast<const int4*>(a.info + kInfo * mrow);
+  const int4 inf1 = *reinterpret_cast<const int4*>(a.info + kInfo * mrow + 4);
+  const int M = inf0.x, n_ev = inf0.y, first_ev = inf1.x;
+  const bool run = inf1.y != 0;
   if (n_ev == 0) return;
   const size_t bg = (size_t)(b * s.Hkv + g);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int p = lane % HALF, sub = lane / HALF;
 
-  if (cidx == a.nchunks) {
-    // Recent ring: every entry shifts by -n_ev positions; rotate fp16 K in place.
+  if (cidx >= a.nchunks) {
+    // Recent ring: every entry shifts by -n_ev positions; rotate fp16 K in
+    // place. Block cidx - nchunks takes kRingPairs / HALF ring entries, one
+    // lane per rotation pair and kRingPer entries per lane, all loads issued
+    // before the first store.
     if (!a.requant_keys) return;
     const int32_t* L = a.c.lens + 4 * b;
     const int R = min(max(L[2], 0), s.ring), head = min(max(L[3], 0), s.ring - 1);
     const int slots = s.n_sink + s.ring;
-    const double2 cs = a.tab[(size_t)n_ev * HALF + p];
-    for (int t = wave * RPW + sub; t < R; t += 4 * RPW) {
-      const int slot = s.n_sink + (head + t) % s.ring;
-      uint16_t* kp = reinterpret_cast<uint16_t*>(a.c.fp_k) + (bg * slots + slot) * D;
-      const int c1 = a.interleaved ? 2 * p : p, c2 = a.interleaved ? 2 * p + 1 : p + HALF;
+    constexpr int RSTEP = 256 / HALF;
+    const int pr = tid % HALF;
+    const int t0 = (cidx - a.nchunks) * (kRingPairs / HALF) + tid / HALF;
+    const int c1 = a.interleaved ? 2 * pr : pr, c2 = a.interleaved ? 2 * pr + 1 : pr + HALF;
+    const double2 cs = a.tab[(size_t)n_ev * HALF + pr];
+    uint16_t* kp[kRingPer];
+    float x1[kRingPer], x2[kRingPer];
+#pragma unroll
+    for (int j = 0; j < kRingPer; ++j) {
+      const int t = t0 + j * RSTEP;
+      kp[j] = t < R ? reinterpret_cast<uint16_t*>(a.c.fp_k) + (bg * slots + s.n_sink + (head + t) % s.ring) * D
+                    : nullptr;
+      x1[j] = kp[j] ? h2f(kp[j][c1]) : 0.f;
+      x2[j] = kp[j] ? h2f(kp[j][c2]) : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kRingPer; ++j) {
+      if (!kp[j]) continue;
       uint16_t h1, h2;
-      rotate_pair(h2f(kp[c1]), h2f(kp[c2]), cs.x, cs.y, h1, h2);
-      kp[c1] = h1;
-      kp[c2] = h2;
+      rotate_pair(x1[j], x2[j], cs.x, cs.y, h1, h2);
+      kp[j][c1] = h1;
+      kp[j][c2] = h2;
     }
     return;
   }
@@ -426,7 +474,7 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
   const int r0 = cidx * CH;
   if (r0 >= M) return;
   const int rows_here = min(CH, M - r0);
-  if (r0 + rows_here <= a.info[kInfo * mrow + 4]) {
+  if (r0 + rows_here <= first_ev) {
     // every row of this chunk lies before the first evicted slot: nothing moves
     if (tid == 0) a.spill_info[bg * a.nchunks + cidx] = make_int2(0, 0);
     return;
@@ -442,7 +490,7 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
   // moved row and kept count, merged with one LDS atomic per wave.
   for (int t0 = wave * 64; t0 < rows_here; t0 += 256) {
     const int t = t0 + lane;
-    const int d = t < rows_here ? map[r0 + t] : -1;
+    const int d = t < rows_here ? (run ? run_dst(r0 + t, first_ev, n_ev) : map[r0 + t]) : -1;
     if (t < rows_here) s_dst[t] = d;
     const uint64_t kept_m = __ballot(d >= 0);
     const uint64_t moved_m = __ballot(d >= 0 && d != r0 + t);
@@ -498,19 +546,22 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
   // DPP steps, and (INT4) the lane's 8 codes of a half are one packed word.
   // The lane's cos/sin entries are reloaded only when its row's shift
   // changes. Without a rotary embedding the staged codes are written as they are.
+  constexpr int PPL = 8, LPR = HALF / PPL;      // rotation pairs per lane, lanes per row
+  const int m = lane % LPR;
+  int cur_delta = -1;
+  double2 csl[PPL];
   if (a.requant_keys && !a.interleaved) {
-    constexpr int PPL = 8, LPR = HALF / PPL, RPW2 = 64 / LPR;
+    constexpr int RPW2 = 64 / LPR;
     constexpr int CW = PPL * KB / 8;            // bytes of 8 codes (4 or 2)
-    const int m = lane % LPR, rsub = lane / LPR;
-    int cur_delta = -1;
-    double2 csl[PPL];
+    const int rsub = lane / LPR;
     for (int base = wave * RPW2; base < n_rows; base += 4 * RPW2) {
       const int tt = base + rsub;
       const bool valid = tt < n_rows;
       const int t = lo + min(tt, n_rows - 1);
       const int d = s_dst[t];
       const bool moved = valid && d >= 0 && d != r0 + t;
-      const int delta = moved ? r0 + t - d : 0;
+      // rows that are not stored keep the lane's current entries
+      const int delta = moved ? r0 + t - d : max(cur_delta, 0);
       if (delta != cur_delta) {
         const double2* tp = a.tab + (size_t)delta * HALF + PPL * m;
 #pragma unroll
@@ -578,18 +629,16 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
     // Interleaved pairing: pair i is channels (2i, 2i + 1), so the lane's 8
     // pairs [8m, 8m + 8) are the 16 adjacent channels [16m, 16m + 16), two
     // code words of one 32-channel group shared with lane m ^ 1.
-    constexpr int PPL = 8, LPR = HALF / PPL, RPW2 = 64 / LPR;
+    constexpr int RPW2 = 64 / LPR;
     constexpr int CW = PPL * KB / 8;            // bytes of 8 codes (4 or 2)
-    const int m = lane % LPR, rsub = lane / LPR, gq = m / 2;
-    int cur_delta = -1;
-    double2 csl[PPL];
+    const int rsub = lane / LPR, gq = m / 2;
     for (int base = wave * RPW2; base < n_rows; base += 4 * RPW2) {
       const int tt = base + rsub;
       const bool valid = tt < n_rows;
       const int t = lo + min(tt, n_rows - 1);
       const int d = s_dst[t];
       const bool moved = valid && d >= 0 && d != r0 + t;
-      const int delta = moved ? r0 + t - d : 0;
+      const int delta = moved ? r0 + t - d : max(cur_delta, 0);
       if (delta != cur_delta) {
         const double2* tp = a.tab + (size_t)delta * HALF + PPL * m;
 #pragma unroll
@@ -735,7 +784,8 @@ size_t evict_ws_bytes(const Shape& s, int max_evict) {
 
 template <int D, int KB, int VB>
 static void launch_compact_t(const CompactArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((k_compact<D, KB, VB>), dim3(a.nchunks + 1, a.s.Hkv, a.s.batch), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((k_compact<D, KB, VB>), dim3(a.nchunks + ring_blocks(a.s.ring, D), a.s.Hkv, a.s.batch),
+                     dim3(256), 0, st, a);
   hipLaunchKernelGGL((k_spill_copy<D, KB, VB>), dim3(a.nchunks, a.s.Hkv, a.s.batch), dim3(256), 0, st, a);
 }
 
