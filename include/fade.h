@@ -351,6 +351,28 @@ int fade_pq_train_step(int32_t head_dim, const void* x, int64_t n_rows, const vo
 /* Workspace bytes of fade_pq_train_step; 0 for an unsupported head_dim. */
 size_t fade_pq_workspace_bytes(int32_t head_dim, int64_t n_rows);
 
+/* Decode attention over a PQ-coded block of keys and values (FADE post,
+ * section "产品量化（PQ）": the codebook is the alternative to the INT2 tier;
+ * the attention follows the reading of the tiered decode: one softmax over all
+ * tokens, scale 1/sqrt(head_dim), query head h reads KV head h / (n_q_heads /
+ * n_kv_heads)). Keys and values are the centroids their codes name.
+ *   q           device fp16 [batch][n_q_heads][head_dim]
+ *   k_codes,
+ *   v_codes     device uint8 [batch][n_kv_heads][n_tokens][32] (fade_pq_encode
+ *               rows), 16-byte aligned
+ *   k_codebook,
+ *   v_codebook  device fp16 [32][256][head_dim / 32], 16-byte aligned
+ *   out         device float32 [batch][n_q_heads][head_dim], written whole
+ *               (zeros when n_tokens == 0)
+ * Scores and the softmax are float32; the values are summed per sub-space and
+ * centroid before the value codebook is applied. head_dim 64 or 128
+ * (FADE_ERR_UNSUPPORTED otherwise); n_q_heads a multiple of n_kv_heads,
+ * 0 <= batch <= 65535, n_tokens >= 0 (FADE_ERR_INVALID_ARG otherwise, also for
+ * NULL or misaligned pointers). Asynchronous on stream; nothing is allocated. */
+int fade_pq_decode_attn(int32_t head_dim, int32_t n_q_heads, int32_t n_kv_heads, int32_t batch, int64_t n_tokens,
+                        const void* q, const void* k_codes, const void* v_codes, const void* k_codebook,
+                        const void* v_codebook, void* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -22,6 +22,11 @@ centroids, encodes vectors to uint8 codes and decodes them back, at about
   64-bit integers), divided in float64 and rounded once to fp16; a centroid
   with no members keeps its value.
 * Decoding: the centroid itself (fp16).
+* Attention over PQ-coded keys and values (the codebook as a cache tier in
+  place of INT2): keys and values are the decoded centroids, and the
+  attention is the tiered decode's (one softmax over all tokens, scale
+  1/sqrt(d), query head h reads KV head h // n_rep), taken from
+  attention.decode_attention. With no tokens the output is zero.
 """
 import numpy as np
 
@@ -114,3 +119,16 @@ def objective(x, codebook):
     cb = np.asarray(codebook, dtype=np.float16).astype(np.float64)
     subs = _split(x, cb.shape[0])
     return float(sum(distances(subs[s], cb[s]).min(axis=1).sum() for s in range(cb.shape[0])))
+
+
+def decode_attention(q, k_codes, v_codes, k_codebook, v_codebook):
+    """q [Hq, d]; k_codes, v_codes uint8 [Hkv, N, n_sub]; codebooks fp16
+    [n_sub, K, l] -> out [Hq, d] float64 over the decoded keys and values."""
+    from .attention import decode_attention as dense
+    q = np.asarray(q, dtype=np.float64)
+    hkv, n, _ = k_codes.shape
+    if n == 0:
+        return np.zeros_like(q)
+    k_hat = np.stack([decode(k_codes[g], k_codebook) for g in range(hkv)]).astype(np.float64)
+    v_hat = np.stack([decode(v_codes[g], v_codebook) for g in range(hkv)]).astype(np.float64)
+    return dense(q, k_hat, v_hat)[0]

@@ -196,3 +196,23 @@ def test_pq_validation_and_workspace():
     assert lib.fade_pq_train_step(128, p16, 1000, p16, p16, p16, ws - 1, null) == fade.FADE_ERR_WORKSPACE
     assert lib.fade_pq_train_step(128, null, 1000, p16, p16, p16, ws, null) == fade.FADE_ERR_INVALID_ARG
     assert lib.fade_pq_train_step(128, p16, 1000, p16, null, p16, ws, null) == fade.FADE_ERR_INVALID_ARG
+
+
+def test_pq_decode_attn_validation():
+    """Argument checks of fade_pq_decode_attn, all answered before any device call."""
+    lib = fade.lib()
+    null = ctypes.c_void_p(0)
+    p16 = ctypes.c_void_p(16)
+    f = lib.fade_pq_decode_attn
+    assert f(96, 8, 2, 1, 10, p16, p16, p16, p16, p16, p16, null) == fade.FADE_ERR_UNSUPPORTED
+    assert f(128, 8, 3, 1, 10, p16, p16, p16, p16, p16, p16, null) == fade.FADE_ERR_INVALID_ARG   # GQA ratio
+    assert f(128, 0, 1, 1, 10, p16, p16, p16, p16, p16, p16, null) == fade.FADE_ERR_INVALID_ARG
+    assert f(128, 8, 2, -1, 10, p16, p16, p16, p16, p16, p16, null) == fade.FADE_ERR_INVALID_ARG
+    assert f(128, 8, 2, 70000, 10, p16, p16, p16, p16, p16, p16, null) == fade.FADE_ERR_INVALID_ARG
+    assert f(128, 8, 2, 1, -1, p16, p16, p16, p16, p16, p16, null) == fade.FADE_ERR_INVALID_ARG
+    assert f(128, 8, 2, 1, 10, null, p16, p16, p16, p16, p16, null) == fade.FADE_ERR_INVALID_ARG
+    assert f(128, 8, 2, 1, 10, p16, null, p16, p16, p16, p16, null) == fade.FADE_ERR_INVALID_ARG
+    assert f(128, 8, 2, 1, 10, p16, ctypes.c_void_p(24), p16, p16, p16, p16, null) == fade.FADE_ERR_INVALID_ARG
+    assert f(128, 8, 2, 1, 10, p16, p16, p16, p16, p16, ctypes.c_void_p(18), null) == fade.FADE_ERR_INVALID_ARG
+    assert f(128, 8, 2, 1, 10, p16, p16, p16, ctypes.c_void_p(24), p16, p16, null) == fade.FADE_ERR_INVALID_ARG
+    assert f(64, 4, 4, 0, 10, null, null, null, null, null, null, null) == fade.FADE_OK              # empty batch

@@ -11,6 +11,8 @@ import torch
 from oracle import pq
 from tiered_quantized_kv_amd import fade, synth
 
+from .gpu_helpers import out_close
+
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
@@ -82,3 +84,27 @@ def test_pq_train_matches_oracle(d, n, iters):
     want = pq.update(x, pq.encode(x, want), want)
     assert np.array_equal(a.cpu().numpy().view(np.uint16), want.view(np.uint16))
     assert pq.objective(x, want) < pq.objective(x, cb0)
+
+
+@pytest.mark.parametrize("d,hq,hkv,B,n", [(128, 8, 2, 2, 1000), (128, 32, 8, 1, 4099), (64, 4, 4, 3, 257),
+                                          (64, 8, 1, 2, 1), (128, 8, 2, 2, 0)])
+def test_pq_decode_attn_matches_oracle(d, hq, hkv, B, n):
+    """Attention over PQ-coded keys and values against the oracle (float64 over
+    the decoded centroids). Codebooks are N(0, 1) fp16, codes uniform; the
+    query is scaled by 2 so the softmax is far from uniform. Several
+    256-token strides and a ragged tail, n_rep 1 / 4 / 8, and no tokens."""
+    gen = synth.rng(530 + n)
+    l = d // pq.N_SUB
+    kcb = gen.standard_normal((pq.N_SUB, pq.K, l)).astype(np.float16)
+    vcb = gen.standard_normal((pq.N_SUB, pq.K, l)).astype(np.float16)
+    kc = gen.integers(0, pq.K, size=(B, hkv, n, pq.N_SUB)).astype(np.uint8)
+    vc = gen.integers(0, pq.K, size=(B, hkv, n, pq.N_SUB)).astype(np.uint8)
+    q = (2 * gen.standard_normal((B, hq, d))).astype(np.float16)
+    out = torch.full((B, hq, d), float("nan"), dtype=torch.float32, device=DEV)
+    fade.fade_pq_decode_attn(_dev(q), _dev(kc), _dev(vc), _dev(kcb), _dev(vcb), out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    for b in range(B):
+        want = pq.decode_attention(q[b].astype(np.float64), kc[b], vc[b], kcb, vcb)
+        ok, worst = out_close(got[b], want)
+        assert ok, (b, worst)

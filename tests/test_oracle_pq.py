@@ -90,3 +90,63 @@ def test_two_bits_per_element_at_d128():
     assert pq.sub_len(128) == 4 and 8 / pq.sub_len(128) == 2.0
     with pytest.raises(ValueError):
         pq.sub_len(100)
+
+
+def _brute_pq_attention(q, k_codes, v_codes, kcb, vcb):
+    """Tiny-case brute force written out in plain Python: every key and value
+    vector assembled sub-space by sub-space from the codebooks, scores as
+    explicit sums, the softmax with math.exp over exact float64 sums."""
+    import math
+    hq, d = q.shape
+    hkv, n, n_sub = k_codes.shape
+    l = d // n_sub
+    out = np.zeros((hq, d))
+    for h in range(hq):
+        g = h // (hq // hkv)
+        keys, vals = [], []
+        for t in range(n):
+            kv, vv = [], []
+            for s in range(n_sub):
+                kv += [float(kcb[s, int(k_codes[g, t, s]), e]) for e in range(l)]
+                vv += [float(vcb[s, int(v_codes[g, t, s]), e]) for e in range(l)]
+            keys.append(kv)
+            vals.append(vv)
+        sc = [sum(float(q[h, i]) * keys[t][i] for i in range(d)) / math.sqrt(d) for t in range(n)]
+        m = max(sc)
+        w = [math.exp(x - m) for x in sc]
+        z = sum(w)
+        for i in range(d):
+            out[h, i] = sum(w[t] * vals[t][i] for t in range(n)) / z
+    return out
+
+
+def test_pq_attention_brute_force_tiny():
+    gen = synth.rng(520)
+    d, hq, hkv, n = 64, 4, 2, 5
+    kcb = gen.standard_normal((pq.N_SUB, pq.K, d // pq.N_SUB)).astype(np.float16)
+    vcb = gen.standard_normal((pq.N_SUB, pq.K, d // pq.N_SUB)).astype(np.float16)
+    kc = gen.integers(0, pq.K, size=(hkv, n, pq.N_SUB)).astype(np.uint8)
+    vc = gen.integers(0, pq.K, size=(hkv, n, pq.N_SUB)).astype(np.uint8)
+    q = gen.standard_normal((hq, d)).astype(np.float16).astype(np.float64)
+    got = pq.decode_attention(q, kc, vc, kcb, vcb)
+    want = _brute_pq_attention(q, kc, vc, kcb, vcb)
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_pq_attention_equal_keys_average_the_values():
+    """Identical key codes give every token the same probability, so each
+    head's output is the plain mean of its decoded values; no tokens give 0."""
+    gen = synth.rng(521)
+    d, hq, hkv, n = 128, 8, 2, 37
+    kcb = gen.standard_normal((pq.N_SUB, pq.K, d // pq.N_SUB)).astype(np.float16)
+    vcb = gen.standard_normal((pq.N_SUB, pq.K, d // pq.N_SUB)).astype(np.float16)
+    kc = np.repeat(gen.integers(0, pq.K, size=(hkv, 1, pq.N_SUB)), n, axis=1).astype(np.uint8)
+    vc = gen.integers(0, pq.K, size=(hkv, n, pq.N_SUB)).astype(np.uint8)
+    q = gen.standard_normal((hq, d))
+    got = pq.decode_attention(q, kc, vc, kcb, vcb)
+    for h in range(hq):
+        g = h // (hq // hkv)
+        mean = pq.decode(vc[g], vcb).astype(np.float64).mean(axis=0)
+        assert np.allclose(got[h], mean, rtol=1e-12, atol=1e-13)
+    empty = np.zeros((hkv, 0, pq.N_SUB), dtype=np.uint8)
+    assert np.array_equal(pq.decode_attention(q, empty, empty, kcb, vcb), np.zeros((hq, d)))

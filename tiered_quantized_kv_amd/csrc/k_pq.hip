@@ -17,8 +17,16 @@
 //                  is an integer multiple of 2^-24), the mean divided in
 //                  float64 and rounded once to fp16; a centroid with no
 //                  members keeps its value.
+//   k_pq_attn      decode attention over PQ-coded keys and values, one
+//                  workgroup per (sequence, query head): the query's inner
+//                  products with every key centroid form a [sub-space][centroid]
+//                  table in LDS, so a token's score is 32 table reads; the
+//                  value centroids are gathered from an LDS copy of the value
+//                  codebook, one lane per sub-space.
 // Roofline: encode is fp64 ALU work (256 centroids x (3 l + 1) float64
-// operations per sub-vector); decode and the update are memory streams.
+// operations per sub-vector); decode and the update are memory streams; the
+// attention reads 64 code bytes per token and KV head (2 bits per element)
+// and is bound by its LDS table reads and centroid gathers.
 #include "fade_common.hpp"
 #include "fade_internal.hpp"
 
@@ -170,6 +178,175 @@ hipError_t launch_pq_train_step(int D, const uint16_t* x, int64_t n, const uint1
   }
   if (D == 128) hipLaunchKernelGGL(k_pq_finish<4>, dim3((n_sums + 255) / 256), dim3(256), 0, st, sums, cnt, cb_in, cb_out);
   else hipLaunchKernelGGL(k_pq_finish<2>, dim3((n_sums + 255) / 256), dim3(256), 0, st, sums, cnt, cb_in, cb_out);
+  return hipGetLastError();
+}
+
+// Decode attention over PQ codes. Query head h of sequence b reads KV head
+// h / n_rep. Scores are scale * sum_s T[s][code_s] with T[s][k] the fp32
+// inner product of the query's sub-vector s with key centroid k (one lane per
+// token, 32 table reads); softmax in fp32 with the maximum subtracted (a
+// first pass finds it). The value sum is gathered with one lane per
+// sub-space: each wave walks its 64 tokens two at a time, lane s of each half
+// reads the token's value code s and adds p times that centroid (the value
+// codebook sits in LDS), so no two lanes ever update the same accumulator.
+// The next 256 tokens' codes are fetched before the current ones are used.
+
+// The L fp16 elements of one centroid (8-byte aligned at L = 4, 4-byte at L = 2).
+template <int L>
+__device__ __forceinline__ void centroid(const uint16_t* p, float (&v)[L]) {
+  if constexpr (L == 4) {
+    const uint2 w = *reinterpret_cast<const uint2*>(p);
+    v[0] = h2f((uint16_t)(w.x & 0xFFFFu));
+    v[1] = h2f((uint16_t)(w.x >> 16));
+    v[2] = h2f((uint16_t)(w.y & 0xFFFFu));
+    v[3] = h2f((uint16_t)(w.y >> 16));
+  } else {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+    v[0] = h2f((uint16_t)(w & 0xFFFFu));
+    v[1] = h2f((uint16_t)(w >> 16));
+  }
+}
+
+template <int L>
+__global__ __launch_bounds__(256) void k_pq_attn(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kcodes,
+                                                 const uint8_t* __restrict__ vcodes, const uint16_t* __restrict__ kcb,
+                                                 const uint16_t* __restrict__ vcb, float* __restrict__ out,
+                                                 int n_q_heads, int n_rep, int64_t n_tok, float scale) {
+  constexpr int D = L * kPqSub;
+  constexpr int PER = kPqSub * kPqK / 256;        // table entries per lane
+  constexpr int VCB16 = kPqSub * kPqK * L * 2 / 16;   // 16-byte units of a codebook
+  __shared__ float tab[kPqSub * kPqK];
+  __shared__ __align__(16) uint16_t vcl[kPqSub * kPqK * L];
+  __shared__ __align__(16) uint32_t vbuf[256 * 8];   // value codes of the current 256 tokens
+  __shared__ float pbuf[256];
+  __shared__ float qs[D];
+  __shared__ float part[4 * D];
+  __shared__ float red[4];
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n_kv = n_q_heads / n_rep, g = h / n_rep;
+  const size_t qh = (size_t)b * n_q_heads + h;
+  if (tid < D) qs[tid] = h2f(q[qh * D + tid]);
+#pragma unroll
+  for (int j = 0; j < VCB16 / 256; ++j)
+    reinterpret_cast<uint4*>(vcl)[tid + 256 * j] = reinterpret_cast<const uint4*>(vcb)[tid + 256 * j];
+  __syncthreads();
+  // entry i = s * 256 + k
+#pragma unroll 16
+  for (int j = 0; j < PER; ++j) {
+    const int i = tid + 256 * j;
+    float c[L];
+    centroid<L>(kcb + (size_t)i * L, c);
+    const int sub = i / kPqK;
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < L; ++e) acc = __builtin_fmaf(qs[sub * L + e], c[e], acc);
+    tab[i] = acc;
+  }
+  __syncthreads();
+  const size_t row0 = ((size_t)b * n_kv + g) * (size_t)n_tok;
+  const uint4* kr = reinterpret_cast<const uint4*>(kcodes + row0 * kPqSub);
+  const uint4* vr = reinterpret_cast<const uint4*>(vcodes + row0 * kPqSub);
+  auto score = [&](const uint4& c0, const uint4& c1) -> float {
+    const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc += tab[(4 * j + k) * kPqK + ((w[j] >> (8 * k)) & 0xFFu)];
+    return acc * scale;
+  };
+  // pass 1: the maximum score
+  float mx = -INFINITY;
+  {
+    uint4 n0 = make_uint4(0, 0, 0, 0), n1 = n0;
+    if (tid < n_tok) {
+      n0 = kr[2 * tid];
+      n1 = kr[2 * tid + 1];
+    }
+    for (int64_t t = tid; t < n_tok; t += 256) {
+      const uint4 c0 = n0, c1 = n1;
+      if (t + 256 < n_tok) {
+        n0 = kr[2 * (t + 256)];
+        n1 = kr[2 * (t + 256) + 1];
+      }
+      mx = fmaxf(mx, score(c0, c1));
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  // pass 2: probabilities, then the value gather of each wave's 64 tokens
+  float sum = 0.f;
+  const int sub = lane & 31, half = lane >> 5;
+  float acc[L];
+#pragma unroll
+  for (int e = 0; e < L; ++e) acc[e] = 0.f;
+  {
+    uint4 n0 = make_uint4(0, 0, 0, 0), n1 = n0, m0 = n0, m1 = n0;
+    if (tid < n_tok) {
+      n0 = kr[2 * tid];
+      n1 = kr[2 * tid + 1];
+      m0 = vr[2 * tid];
+      m1 = vr[2 * tid + 1];
+    }
+    for (int64_t c0 = 0; c0 < n_tok; c0 += 256) {   // the same trip count in every wave
+      const int64_t t = c0 + tid;
+      const uint4 k0 = n0, k1 = n1, d0 = m0, d1 = m1;
+      if (t + 256 < n_tok) {
+        n0 = kr[2 * (t + 256)];
+        n1 = kr[2 * (t + 256) + 1];
+        m0 = vr[2 * (t + 256)];
+        m1 = vr[2 * (t + 256) + 1];
+      }
+      // past the end p is 0 (the codes there are stale in-range bytes)
+      const float p = t < n_tok ? expf(score(k0, k1) - mx) : 0.f;
+      sum += p;
+      pbuf[tid] = p;
+      reinterpret_cast<uint4*>(vbuf)[2 * tid] = d0;
+      reinterpret_cast<uint4*>(vbuf)[2 * tid + 1] = d1;
+      __syncthreads();
+      const uint8_t* vb = reinterpret_cast<const uint8_t*>(vbuf);
+#pragma unroll 8
+      for (int u = 0; u < 32; ++u) {
+        const int tk = wave * 64 + 2 * u + half;
+        const float pw = pbuf[tk];
+        float c[L];
+        centroid<L>(vcl + (sub * kPqK + vb[tk * kPqSub + sub]) * L, c);
+#pragma unroll
+        for (int e = 0; e < L; ++e) acc[e] = __builtin_fmaf(pw, c[e], acc[e]);
+      }
+      __syncthreads();                                // buffers are rewritten by the next chunk
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+#pragma unroll
+  for (int e = 0; e < L; ++e) acc[e] += __shfl_xor(acc[e], 32);
+  if (lane == 0) red[wave] = sum;
+  if (half == 0) {
+#pragma unroll
+    for (int e = 0; e < L; ++e) part[wave * D + sub * L + e] = acc[e];
+  }
+  __syncthreads();
+  sum = (red[0] + red[1]) + (red[2] + red[3]);
+  const float inv = sum > 0.f ? 1.f / sum : 0.f;
+  if (tid < D) out[qh * D + tid] = ((part[tid] + part[D + tid]) + (part[2 * D + tid] + part[3 * D + tid])) * inv;
+}
+
+hipError_t launch_pq_attn(int D, const uint16_t* q, const uint8_t* kcodes, const uint8_t* vcodes,
+                          const uint16_t* kcb, const uint16_t* vcb, float* out, int batch, int n_q_heads, int n_kv_heads,
+                          int64_t n_tok, hipStream_t st) {
+  const dim3 grid(n_q_heads, batch);
+  const int n_rep = n_q_heads / n_kv_heads;
+  const float scale = 1.0f / sqrtf((float)D);
+  if (D == 128)
+    hipLaunchKernelGGL(k_pq_attn<4>, grid, dim3(256), 0, st, q, kcodes, vcodes, kcb, vcb, out, n_q_heads, n_rep, n_tok, scale);
+  else
+    hipLaunchKernelGGL(k_pq_attn<2>, grid, dim3(256), 0, st, q, kcodes, vcodes, kcb, vcb, out, n_q_heads, n_rep, n_tok, scale);
   return hipGetLastError();
 }
 

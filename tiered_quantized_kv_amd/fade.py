@@ -75,6 +75,8 @@ _SIGS = {
     "fade_pq_decode": (ctypes.c_int, [ctypes.c_int32, _P, ctypes.c_int64, _P, _P, _P]),
     "fade_pq_train_step": (ctypes.c_int, [ctypes.c_int32, _P, ctypes.c_int64, _P, _P, _P, ctypes.c_size_t, _P]),
     "fade_pq_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int32, ctypes.c_int64]),
+    "fade_pq_decode_attn": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P]),
 }
 
 
@@ -264,3 +266,12 @@ def fade_pq_train_step(x, codebook_in, codebook_out, ws, stream=None):
     """One Lloyd iteration of the codebook on the rows of x."""
     _check(lib().fade_pq_train_step(x.shape[1], _p(x), x.shape[0], _p(codebook_in), _p(codebook_out), _p(ws),
                                     ws.numel(), _s(stream)), "fade_pq_train_step")
+
+
+def fade_pq_decode_attn(q, k_codes, v_codes, k_codebook, v_codebook, out, stream=None):
+    """q fp16 [B, Hq, d]; k_codes, v_codes u8 [B, Hkv, N, 32]; codebooks fp16
+    [32, 256, d / 32] -> out float32 [B, Hq, d]."""
+    B, hq, d = q.shape
+    hkv, n = k_codes.shape[1], k_codes.shape[2]
+    _check(lib().fade_pq_decode_attn(d, hq, hkv, B, n, _p(q), _p(k_codes), _p(v_codes), _p(k_codebook),
+                                     _p(v_codebook), _p(out), _s(stream)), "fade_pq_decode_attn")
