@@ -184,8 +184,8 @@ hipError_t launch_pq_train_step(int D, const uint16_t* x, int64_t n, const uint1
 // Decode attention over PQ codes. Query head h of sequence b reads KV head
 // h / n_rep. Scores are scale * sum_s T[s][code_s] with T[s][k] the fp32
 // inner product of the query's sub-vector s with key centroid k (one lane per
-// token, 32 table reads); softmax in fp32 with the maximum subtracted (a
-// first pass finds it). The value sum is gathered with one lane per
+// token, 32 table reads); softmax in fp32 against a running maximum (online
+// rescaling per 256-token chunk). The value sum is gathered with one lane per
 // sub-space: each wave walks its 64 tokens two at a time, lane s of each half
 // reads the token's value code s and adds p times that centroid (the value
 // codebook sits in LDS), so no two lanes ever update the same accumulator.
@@ -256,31 +256,12 @@ __global__ __launch_bounds__(256) void k_pq_attn(const uint16_t* __restrict__ q,
       for (int k = 0; k < 4; ++k) acc += tab[(4 * j + k) * kPqK + ((w[j] >> (8 * k)) & 0xFFu)];
     return acc * scale;
   };
-  // pass 1: the maximum score
-  float mx = -INFINITY;
-  {
-    uint4 n0 = make_uint4(0, 0, 0, 0), n1 = n0;
-    if (tid < n_tok) {
-      n0 = kr[2 * tid];
-      n1 = kr[2 * tid + 1];
-    }
-    for (int64_t t = tid; t < n_tok; t += 256) {
-      const uint4 c0 = n0, c1 = n1;
-      if (t + 256 < n_tok) {
-        n0 = kr[2 * (t + 256)];
-        n1 = kr[2 * (t + 256) + 1];
-      }
-      mx = fmaxf(mx, score(c0, c1));
-    }
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-  if (lane == 0) red[wave] = mx;
-  __syncthreads();
-  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  // pass 2: probabilities, then the value gather of each wave's 64 tokens
-  float sum = 0.f;
+  // One pass in chunks of 256 tokens with a running maximum: each chunk's
+  // maximum is taken over the workgroup before its probabilities are formed,
+  // and the lane's accumulators and probability sum are rescaled when the
+  // maximum grows. Each wave then gathers the value centroids of its 64
+  // tokens, two at a time, one lane per sub-space.
+  float mrun = -INFINITY, sum = 0.f;
   const int sub = lane & 31, half = lane >> 5;
   float acc[L];
 #pragma unroll
@@ -302,12 +283,24 @@ __global__ __launch_bounds__(256) void k_pq_attn(const uint16_t* __restrict__ q,
         m0 = vr[2 * (t + 256)];
         m1 = vr[2 * (t + 256) + 1];
       }
-      // past the end p is 0 (the codes there are stale in-range bytes)
-      const float p = t < n_tok ? expf(score(k0, k1) - mx) : 0.f;
-      sum += p;
-      pbuf[tid] = p;
+      // past the end the score is -inf and p is 0 (the codes there are stale
+      // in-range bytes)
+      const float sc = t < n_tok ? score(k0, k1) : -INFINITY;
+      float cm = sc;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) cm = fmaxf(cm, __shfl_xor(cm, o));
+      if (lane == 0) red[wave] = cm;
       reinterpret_cast<uint4*>(vbuf)[2 * tid] = d0;
       reinterpret_cast<uint4*>(vbuf)[2 * tid + 1] = d1;
+      __syncthreads();
+      const float mnew = fmaxf(mrun, fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+      const float f = expf(mrun - mnew);             // 0 on the first chunk
+      mrun = mnew;
+      const float p = expf(sc - mnew);
+      sum = sum * f + p;
+#pragma unroll
+      for (int e = 0; e < L; ++e) acc[e] *= f;
+      pbuf[tid] = p;
       __syncthreads();
       const uint8_t* vb = reinterpret_cast<const uint8_t*>(vbuf);
 #pragma unroll 8
