@@ -40,6 +40,8 @@ def parse():
     p.add_argument("--overlap-steps", type=int, default=16,
                    help="extra timed steps, after the main ones, with the admitted sequence's H2O prefill pass "
                         "on a stream of its own (0 = skip)")
+    p.add_argument("--pq-calls", type=int, default=20,
+                   help="timed calls of the PQ decode attention at the workload's middle-tier size (0 = skip)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="run one device copy of this size before timing (HBM counter calibration)")
     return p.parse_args()
@@ -378,6 +380,40 @@ def cpu_baseline(name, budget_s=20.0):
                       f"demote, evict; float64 numpy, {dt:.1f} s"}
 
 
+def time_pq_attention(wl, calls):
+    """fade_pq_decode_attn at the workload's shape over as many PQ-coded
+    tokens as its middle tier holds (the INT4 budget, or the whole context
+    without one): seeded uniform codes, N(0, 1) fp16 codebooks and queries.
+    Timed with a pair of events around `calls` back-to-back launches."""
+    import torch
+    from tiered_quantized_kv_amd import fade
+    w = wl.w
+    B, hq, hkv, d = wl.B, wl.hq, wl.hkv, wl.d
+    n = w["int4_budget"] if w["int4_budget"] >= 0 else w.get("context", w.get("context_range", (0, 0))[1])
+    g = torch.Generator(device="cuda").manual_seed(wl.seed + 77)
+    kc = torch.randint(0, fade.PQ_K, (B, hkv, n, fade.PQ_SUB), device="cuda", dtype=torch.uint8, generator=g)
+    vc = torch.randint(0, fade.PQ_K, (B, hkv, n, fade.PQ_SUB), device="cuda", dtype=torch.uint8, generator=g)
+    kcb = torch.randn(fade.PQ_SUB, fade.PQ_K, d // fade.PQ_SUB, device="cuda", generator=g).half()
+    vcb = torch.randn(fade.PQ_SUB, fade.PQ_K, d // fade.PQ_SUB, device="cuda", generator=g).half()
+    q = torch.randn(B, hq, d, device="cuda", generator=g).half()
+    out = torch.empty(B, hq, d, device="cuda")
+    for _ in range(3):
+        fade.fade_pq_decode_attn(q, kc, vc, kcb, vcb, out)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(calls):
+        fade.fade_pq_decode_attn(q, kc, vc, kcb, vcb, out)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000 / calls
+    code_bytes = B * hkv * n * 2 * fade.PQ_SUB
+    return {"avg_us_per_launch": us, "calls": calls, "batch": B, "tokens": n, "kernels": "k_pq_attn",
+            "code_bytes_per_launch": code_bytes, "achieved_GBps": code_bytes / us / 1e3, "bound": "lds",
+            "note": "attention over PQ-coded keys and values (2 bits per element), middle-tier size; "
+                    "synthetic codes"}
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -503,6 +539,8 @@ def main():
                                    "ms_per_step": oms / a.overlap_steps,
                                    "note": "admitted sequence's H2O prefill pass on its own stream"}
         wl.use_admit_stream(False)
+    if a.pq_calls > 0:
+        res["pq_decode_attn"] = time_pq_attention(wl, a.pq_calls)
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample ...", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(a.workload)
