@@ -92,7 +92,8 @@ def test_append_and_demote_sequence():
 
 @pytest.mark.parametrize("policy", ["position", "score"])
 @pytest.mark.parametrize("d,kb,vb,budget,extra", [(64, 4, 4, 200, 1), (128, 4, 2, 300, 1),
-                                                  (64, 4, 2, 500, 255), (128, 2, 4, 90, 37)])
+                                                  (64, 4, 2, 500, 255), (128, 2, 4, 90, 37),
+                                                  (128, 4, 2, 300, 5), (64, 2, 4, 250, 8)])
 def test_decode_eviction_compaction(policy, d, kb, vb, budget, extra):
     """Build a cache holding budget + extra middle tokens, then run one eviction
     event on both sides with identical float32 scores."""
@@ -112,6 +113,30 @@ def test_decode_eviction_compaction(policy, d, kb, vb, budget, extra):
     for b in range(B):
         refs[b].cfg = oc_cfg
         oc.evict(refs[b], budget, "position" if policy == "position" else "score")
+        assert_state_equal(seq_state(tc, b), refs[b])
+
+
+@pytest.mark.parametrize("victim", [0, 126, 127, 128, 255, 299, 300])
+def test_single_eviction_at_chunk_edges(victim):
+    """One score eviction whose victim sits on either side of a 128-row chunk
+    boundary (and at the first and last middle slot): the compaction of a
+    one-slot run takes its last destination rows from the next chunk's first
+    row, copied aside before any row moves."""
+    d, budget = 128, 300
+    cfg_big = _cfg(d=d, hq=8, hkv=2, n_sink=4, w=32, budget=-1, kb=4, vb=2, rope_theta=1e6)
+    L = 4 + budget + 1 + 32
+    B = 2
+    sc = _scores(B, L, 290 + victim, ties=False) + np.float32(1.0)
+    sc[:, 4 + victim] = np.float32(0.5)             # middle slot `victim` holds the unique minimum
+    tc, refs, _ = build_both(cfg_big, B, L, 291, cap_mid=budget + 1, scores32=sc)
+    cfg = _cfg(d=d, hq=8, hkv=2, n_sink=4, w=32, budget=budget, kb=4, vb=2, rope_theta=1e6)
+    ws = fade.workspace(cfg, fade.WS_EVICT, B, budget + 1)
+    fade.fade_evict_rerope(cfg, tc, fade.POLICY_SCORE, ws)
+    torch.cuda.synchronize()
+    for b in range(B):
+        refs[b].cfg = ocfg(cfg)
+        assert int(np.argmin(refs[b].scores[4:4 + budget + 1])) == victim
+        oc.evict(refs[b], budget, "score")
         assert_state_equal(seq_state(tc, b), refs[b])
 
 

@@ -31,6 +31,8 @@
 namespace fade {
 
 constexpr int kSelThreads = 1024;
+constexpr int kCompactRows = 128;   // middle rows per compaction workgroup
+constexpr int kHalo = 8;            // run evictions of at most this many slots compact without a spill
 constexpr int kInfo = 8;   // ints per row of the selection record:
                            // {M, n_evict, S, R, first evicted middle slot (M if none),
                            //  1 if the evicted slots are the run [first, first + n_evict)
@@ -96,6 +98,14 @@ struct SelectArgs {
   int rows, n_delta, half;
   RopeFreqs fr;
   double2* tab;
+  // halo mode (decode, every event a run of at most kHalo slots): the first
+  // n_ev rows of every chunk after the first are copied to the spill region
+  // of the chunk before it, read by that chunk's compaction
+  int halo;
+  fade_layer_cache c;
+  int Hkv, cap_mid, krow, vrow, sbytes, nchunks, spill_rows;
+  size_t spill_stride;
+  uint8_t* spill;
 };
 
 constexpr int kSelLdsKeys = 12288;   // 48 KB of LDS keys per row at most
@@ -109,13 +119,55 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
   if (a.decode && row >= a.rows) {
-    // cos / sin of -delta * f_i for delta in [0, n_delta), float64
-    const int i = (row - a.rows) * kSelThreads + tid;
-    if (i < a.n_delta * a.half) {
-      const int delta = i / a.half, f = i - delta * a.half;
-      double sn, cs;
-      sincos((double)delta * a.fr.f[f], &sn, &cs);
-      a.tab[i] = make_double2(cs, -sn);
+    const int xb = row - a.rows, tab_blocks = (a.n_delta * a.half + kSelThreads - 1) / kSelThreads;
+    if (xb < tab_blocks) {
+      // cos / sin of -delta * f_i for delta in [0, n_delta), float64
+      const int i = xb * kSelThreads + tid;
+      if (i < a.n_delta * a.half) {
+        const int delta = i / a.half, f = i - delta * a.half;
+        double sn, cs;
+        sincos((double)delta * a.fr.f[f], &sn, &cs);
+        a.tab[i] = make_double2(cs, -sn);
+      }
+      return;
+    }
+    // Halo mode: the middle rows [(c + 1) CH, (c + 1) CH + n_ev) of every
+    // (sequence, KV head, chunk c), as they are before the compaction, go to
+    // chunk c's spill region. U lanes per (sequence, head, chunk): one per
+    // 16 bytes of key codes, one per 16 bytes of value codes, one for the key
+    // scales and one for the value scales of a row. The count n_ev is derived
+    // from the lengths the same way the selection row derives it.
+    const int nc = a.nchunks - 1;
+    const int ku = a.krow / 16, vu = a.vrow / 16, U = ku + vu + 2, sw = a.sbytes / 4;
+    const int jt = (xb - tab_blocks) * kSelThreads + tid;
+    const int j = jt / U, u = jt - j * U;
+    if (!a.halo || nc <= 0 || j >= a.batch * a.Hkv * nc) return;
+    const int c = j % nc, gg = (j / nc) % a.Hkv, bb = j / (nc * a.Hkv);
+    const int32_t* Lr = a.lens + 4 * (a.shared ? 0 : bb);
+    const int M = min(max(Lr[1], 0), a.map_stride);
+    int n_ev = (a.budget >= 0 && M > a.budget) ? M - a.budget : 0;
+    if (n_ev > a.max_evict) n_ev = 0;
+    const int src = (c + 1) * kCompactRows;
+    const int n = min(n_ev, M - src);
+    if (n <= 0) return;
+    const size_t bg = (size_t)bb * a.Hkv + gg;
+    const size_t r = bg * a.cap_mid + src;
+    uint8_t* h = a.spill + (bg * a.nchunks + c) * a.spill_stride;
+    for (int rr = 0; rr < n; ++rr) {
+      if (u < ku) {
+        reinterpret_cast<uint4*>(h)[rr * ku + u] =
+            reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.c.mid_k_codes) + r * a.krow)[rr * ku + u];
+      } else if (u < ku + vu) {
+        reinterpret_cast<uint4*>(h + (size_t)a.spill_rows * a.krow)[rr * vu + u - ku] =
+            reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.c.mid_v_codes) + r * a.vrow)[rr * vu + u - ku];
+      } else {
+        const bool vsc = u > ku + vu;
+        const uint32_t* sp = reinterpret_cast<const uint32_t*>(
+            reinterpret_cast<const uint8_t*>(vsc ? a.c.mid_v_scales : a.c.mid_k_scales) + r * a.sbytes);
+        uint32_t* dp = reinterpret_cast<uint32_t*>(
+            h + (size_t)a.spill_rows * (a.krow + a.vrow) + (vsc ? (size_t)a.spill_rows * a.sbytes : 0));
+        for (int w = 0; w < sw; ++w) dp[rr * sw + w] = sp[rr * sw + w];
+      }
     }
     return;
   }
@@ -309,13 +361,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
       if (i < R) srow[S + M - n_ev + i] = v;
     }
   }
-  if (tid == 0) {
-    if (a.shared) {
-      for (int b = 0; b < a.batch; ++b) a.lens[4 * b + 1] = M - n_ev;
-    } else {
-      a.lens[4 * row + 1] = M - n_ev;
-    }
-  }
+  // the new middle length is written by the compaction, so that every
+  // workgroup of this launch reads the length as it was
 }
 
 struct CompactArgs {
@@ -331,9 +378,9 @@ struct CompactArgs {
   uint8_t* spill;             // [B][Hkv][nchunks] regions: K codes | V codes | K scales | V scales
   int requant_keys;           // 0 without a rotary embedding: keys move like values
   int interleaved;            // RoPE pair i = channels (2i, 2i + 1)
+  int halo;                   // every event is a run of at most kHalo slots (see SelectArgs)
 };
 
-constexpr int kCompactRows = 128;   // middle rows per compaction workgroup
 constexpr int kRingPairs = 1024;    // rotation pairs of the recent ring per workgroup
 constexpr int kRingPer = kRingPairs / 256;
 
@@ -417,11 +464,12 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
   constexpr int NG = D / 32;
   constexpr int KROW = D * KB / 8, VROW = D * VB / 8;
   constexpr int CH = kCompactRows;
-  __shared__ __align__(16) uint32_t s_kc[CH * KROW / 4];
-  __shared__ __align__(16) uint32_t s_vc[CH * VROW / 4];
-  __shared__ __align__(16) uint16_t s_ks[CH * NG];
-  __shared__ __align__(16) uint16_t s_vs[CH * NG];
-  __shared__ int s_dst[CH];
+  constexpr int CHH = CH + kHalo;               // staged rows: the chunk and a halo
+  __shared__ __align__(16) uint32_t s_kc[CHH * KROW / 4];
+  __shared__ __align__(16) uint32_t s_vc[CHH * VROW / 4];
+  __shared__ __align__(16) uint16_t s_ks[CHH * NG];
+  __shared__ __align__(16) uint16_t s_vs[CHH * NG];
+  __shared__ int s_dst[CHH];
   __shared__ int s_first, s_lo, s_kept;
   const int cidx = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const Shape& s = a.s;
@@ -431,6 +479,7 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
   const int M = inf0.x, n_ev = inf0.y, first_ev = inf1.x;
   const bool run = inf1.y != 0;
   if (n_ev == 0) return;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) a.c.lens[4 * b + 1] = M - n_ev;
   const size_t bg = (size_t)(b * s.Hkv + g);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -473,69 +522,101 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
   const int32_t* map = a.map + (size_t)mrow * a.map_stride;
   const int r0 = cidx * CH;
   if (r0 >= M) return;
-  const int rows_here = min(CH, M - r0);
-  if (r0 + rows_here <= first_ev) {
-    // every row of this chunk lies before the first evicted slot: nothing moves
-    if (tid == 0) a.spill_info[bg * a.nchunks + cidx] = make_int2(0, 0);
-    return;
-  }
-  if (tid == 0) {
-    s_first = 0x7fffffff;
-    s_lo = CH;
-    s_kept = 0;
-  }
-  __syncthreads();
-  // Survivors keep their order, so the first destination is that of the
-  // first kept row; per-wave ballots give each wave's first kept row, first
-  // moved row and kept count, merged with one LDS atomic per wave.
-  for (int t0 = wave * 64; t0 < rows_here; t0 += 256) {
-    const int t = t0 + lane;
-    const int d = t < rows_here ? (run ? run_dst(r0 + t, first_ev, n_ev) : map[r0 + t]) : -1;
-    if (t < rows_here) s_dst[t] = d;
-    const uint64_t kept_m = __ballot(d >= 0);
-    const uint64_t moved_m = __ballot(d >= 0 && d != r0 + t);
-    const int dfirst = __shfl(d, kept_m ? (int)__builtin_ctzll(kept_m) : 0);   // whole wave
-    if (lane == 0 && kept_m) {
-      atomicMin(&s_first, dfirst);
-      atomicAdd(&s_kept, (int)__builtin_popcountll(kept_m));
-      if (moved_m) atomicMin(&s_lo, t0 + (int)__builtin_ctzll(moved_m));
-    }
-  }
-  __syncthreads();
-  const int first = s_first, lo = s_lo, kept = s_kept;
-  if (tid == 0) {
-    // survivors of this chunk take the consecutive slots [first, first + kept)
-    const int cnt = first < r0 ? min(r0 - first, kept) : 0;
-    a.spill_info[bg * a.nchunks + cidx] = make_int2(first, cnt);
-  }
-  if (lo >= rows_here) return;                  // nothing moves in this chunk
-  const int n_rows = rows_here - lo;
   uint8_t* kc = reinterpret_cast<uint8_t*>(a.c.mid_k_codes);
   uint8_t* vc = reinterpret_cast<uint8_t*>(a.c.mid_v_codes);
   uint8_t* ks = reinterpret_cast<uint8_t*>(a.c.mid_k_scales);
   uint8_t* vs = reinterpret_cast<uint8_t*>(a.c.mid_v_scales);
-  const size_t row_lo = bg * s.cap_mid + r0 + lo;
-
-  // ---- stage rows [lo, rows_here) ----
-  {
-    const uint4* src = reinterpret_cast<const uint4*>(kc + row_lo * KROW);
-    uint4* dst = reinterpret_cast<uint4*>(s_kc) + lo * (KROW / 16);
-    for (int i = tid; i < n_rows * (KROW / 16); i += 256) dst[i] = src[i];
-  }
-  {
-    const uint4* src = reinterpret_cast<const uint4*>(vc + row_lo * VROW);
-    uint4* dst = reinterpret_cast<uint4*>(s_vc) + lo * (VROW / 16);
-    for (int i = tid; i < n_rows * (VROW / 16); i += 256) dst[i] = src[i];
-  }
-  {
-    const uint32_t* src_k = reinterpret_cast<const uint32_t*>(ks + row_lo * 2 * NG);
-    const uint32_t* src_v = reinterpret_cast<const uint32_t*>(vs + row_lo * 2 * NG);
-    uint32_t* dk = reinterpret_cast<uint32_t*>(s_ks) + lo * (NG / 2);
-    uint32_t* dv = reinterpret_cast<uint32_t*>(s_vs) + lo * (NG / 2);
-    for (int i = tid; i < n_rows * (NG / 2); i += 256) {
+  // Copies n rows (codes and scales) to the staged rows [at, at + n).
+  auto stage = [&](const uint8_t* k_src, const uint8_t* v_src, const uint8_t* ks_src, const uint8_t* vs_src,
+                   int at, int n) {
+    {
+      const uint4* src = reinterpret_cast<const uint4*>(k_src);
+      uint4* dst = reinterpret_cast<uint4*>(s_kc) + at * (KROW / 16);
+      for (int i = tid; i < n * (KROW / 16); i += 256) dst[i] = src[i];
+    }
+    {
+      const uint4* src = reinterpret_cast<const uint4*>(v_src);
+      uint4* dst = reinterpret_cast<uint4*>(s_vc) + at * (VROW / 16);
+      for (int i = tid; i < n * (VROW / 16); i += 256) dst[i] = src[i];
+    }
+    const uint32_t* src_k = reinterpret_cast<const uint32_t*>(ks_src);
+    const uint32_t* src_v = reinterpret_cast<const uint32_t*>(vs_src);
+    uint32_t* dk = reinterpret_cast<uint32_t*>(s_ks) + at * (NG / 2);
+    uint32_t* dv = reinterpret_cast<uint32_t*>(s_vs) + at * (NG / 2);
+    for (int i = tid; i < n * (NG / 2); i += 256) {
       dk[i] = src_k[i];
       dv[i] = src_v[i];
     }
+  };
+  int first = 0, lo, n_rows;
+  if (a.halo) {
+    // A run eviction of n_ev <= kHalo slots from first_ev: this chunk writes
+    // exactly its own destination slots in [max(r0, first_ev), min(r0 + CH,
+    // M - n_ev)), slot d from source d + n_ev: its own rows, then the next
+    // chunk's first n_ev rows, which the selection copied into this chunk's
+    // spill region before any row moved. No chunk writes a slot that another
+    // chunk reads, so no spill copy follows.
+    const int jlo = max(0, first_ev - r0), jn = min(CH, M - n_ev - r0);
+    if (jlo >= jn) return;
+    lo = jlo + n_ev;
+    n_rows = jn - jlo;
+    for (int t = tid; t < CHH; t += 256) s_dst[t] = (t >= lo && t < lo + n_rows) ? r0 + t - n_ev : -1;
+    const int own = min(lo + n_rows, CH) - lo;                 // rows [lo, lo + own) from the cache
+    if (own > 0) {
+      const size_t r = bg * s.cap_mid + r0 + lo;
+      stage(kc + r * KROW, vc + r * VROW, ks + r * 2 * NG, vs + r * 2 * NG, lo, own);
+    }
+    const int h0 = max(lo, CH), hn = lo + n_rows - h0;        // rows [h0, lo + n_rows) from the halo
+    if (hn > 0) {
+      const uint8_t* hb = a.spill + (bg * a.nchunks + cidx) * a.spill_stride;
+      const int hr = h0 - CH;
+      stage(hb + (size_t)hr * KROW, hb + (size_t)a.spill_rows * KROW + (size_t)hr * VROW,
+            hb + (size_t)a.spill_rows * (KROW + VROW) + (size_t)hr * 2 * NG,
+            hb + (size_t)a.spill_rows * (KROW + VROW + 2 * NG) + (size_t)hr * 2 * NG, h0, hn);
+    }
+  } else {
+    const int rows_here = min(CH, M - r0);
+    if (r0 + rows_here <= first_ev) {
+      // every row of this chunk lies before the first evicted slot: nothing moves
+      if (tid == 0) a.spill_info[bg * a.nchunks + cidx] = make_int2(0, 0);
+      return;
+    }
+    if (tid == 0) {
+      s_first = 0x7fffffff;
+      s_lo = CH;
+      s_kept = 0;
+    }
+    __syncthreads();
+    // Survivors keep their order, so the first destination is that of the
+    // first kept row; per-wave ballots give each wave's first kept row, first
+    // moved row and kept count, merged with one LDS atomic per wave.
+    for (int t0 = wave * 64; t0 < rows_here; t0 += 256) {
+      const int t = t0 + lane;
+      const int d = t < rows_here ? (run ? run_dst(r0 + t, first_ev, n_ev) : map[r0 + t]) : -1;
+      if (t < rows_here) s_dst[t] = d;
+      const uint64_t kept_m = __ballot(d >= 0);
+      const uint64_t moved_m = __ballot(d >= 0 && d != r0 + t);
+      const int dfirst = __shfl(d, kept_m ? (int)__builtin_ctzll(kept_m) : 0);   // whole wave
+      if (lane == 0 && kept_m) {
+        atomicMin(&s_first, dfirst);
+        atomicAdd(&s_kept, (int)__builtin_popcountll(kept_m));
+        if (moved_m) atomicMin(&s_lo, t0 + (int)__builtin_ctzll(moved_m));
+      }
+    }
+    __syncthreads();
+    first = s_first;
+    lo = s_lo;
+    const int kept = s_kept;
+    if (tid == 0) {
+      // survivors of this chunk take the consecutive slots [first, first + kept)
+      const int cnt = first < r0 ? min(r0 - first, kept) : 0;
+      a.spill_info[bg * a.nchunks + cidx] = make_int2(first, cnt);
+    }
+    if (lo >= rows_here) return;                  // nothing moves in this chunk
+    n_rows = rows_here - lo;
+    // ---- stage rows [lo, rows_here) ----
+    const size_t r = bg * s.cap_mid + r0 + lo;
+    stage(kc + r * KROW, vc + r * VROW, ks + r * 2 * NG, vs + r * 2 * NG, lo, n_rows);
   }
   __syncthreads();
 
@@ -786,7 +867,8 @@ template <int D, int KB, int VB>
 static void launch_compact_t(const CompactArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((k_compact<D, KB, VB>), dim3(a.nchunks + ring_blocks(a.s.ring, D), a.s.Hkv, a.s.batch),
                      dim3(256), 0, st, a);
-  hipLaunchKernelGGL((k_spill_copy<D, KB, VB>), dim3(a.nchunks, a.s.Hkv, a.s.batch), dim3(256), 0, st, a);
+  if (!a.halo)
+    hipLaunchKernelGGL((k_spill_copy<D, KB, VB>), dim3(a.nchunks, a.s.Hkv, a.s.batch), dim3(256), 0, st, a);
 }
 
 template <int D>
@@ -837,9 +919,25 @@ hipError_t launch_evict(const Shape& s, const fade_layer_cache& c, int policy, i
   sa.n_delta = max_evict + 1;
   sa.fr = fr;
   sa.tab = tab;
+  // every event is a run of at most kHalo slots: the position policy, or a
+  // score eviction bounded to one slot
+  const bool halo = max_evict <= kHalo && (policy == FADE_POLICY_POSITION || max_evict == 1);
+  sa.halo = halo ? 1 : 0;
+  sa.c = c;
+  sa.Hkv = s.Hkv;
+  sa.cap_mid = s.cap_mid;
+  sa.krow = s.D * s.kb / 8;
+  sa.vrow = s.D * s.vb / 8;
+  sa.sbytes = 2 * (s.D / 32);
+  sa.nchunks = nchunks;
+  sa.spill_rows = spill_rows;
+  sa.spill_stride = spill_stride_bytes(s, spill_rows);
+  sa.spill = spill;
   const int n_tab = sa.n_delta * sa.half;
-  hipLaunchKernelGGL(k_select, dim3(rows + (n_tab + kSelThreads - 1) / kSelThreads), dim3(kSelThreads),
-                     (size_t)sa.lds_keys * 4, st, sa);
+  const int halo_lanes = halo ? s.batch * s.Hkv * (nchunks - 1) * (sa.krow / 16 + sa.vrow / 16 + 2) : 0;
+  hipLaunchKernelGGL(k_select,
+                     dim3(rows + (n_tab + kSelThreads - 1) / kSelThreads + (halo_lanes + kSelThreads - 1) / kSelThreads),
+                     dim3(kSelThreads), (size_t)sa.lds_keys * 4, st, sa);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   CompactArgs ca;
@@ -856,6 +954,7 @@ hipError_t launch_evict(const Shape& s, const fade_layer_cache& c, int policy, i
   ca.spill = spill;
   ca.requant_keys = fr.rotates;
   ca.interleaved = fr.interleaved;
+  ca.halo = halo ? 1 : 0;
   if (s.D == 128) launch_compact_d<128>(ca, st);
   else launch_compact_d<64>(ca, st);
   return hipGetLastError();
