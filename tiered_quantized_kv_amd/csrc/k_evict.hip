@@ -526,26 +526,50 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
   uint8_t* vc = reinterpret_cast<uint8_t*>(a.c.mid_v_codes);
   uint8_t* ks = reinterpret_cast<uint8_t*>(a.c.mid_k_scales);
   uint8_t* vs = reinterpret_cast<uint8_t*>(a.c.mid_v_scales);
-  // Copies n rows (codes and scales) to the staged rows [at, at + n).
+  // Copies n rows (codes and scales) to the staged rows [at, at + n): a fixed
+  // number of loads per lane, all issued before the first LDS store (native
+  // vector arrays, so they stay in registers).
   auto stage = [&](const uint8_t* k_src, const uint8_t* v_src, const uint8_t* ks_src, const uint8_t* vs_src,
                    int at, int n) {
-    {
-      const uint4* src = reinterpret_cast<const uint4*>(k_src);
-      uint4* dst = reinterpret_cast<uint4*>(s_kc) + at * (KROW / 16);
-      for (int i = tid; i < n * (KROW / 16); i += 256) dst[i] = src[i];
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    constexpr int UK = (CHH * KROW / 16 + 255) / 256, UV = (CHH * VROW / 16 + 255) / 256;
+    constexpr int US = (CHH * NG / 2 + 255) / 256;
+    const int nk = n * (KROW / 16), nv = n * (VROW / 16), ns = n * (NG / 2);
+    const u32x4* sk = reinterpret_cast<const u32x4*>(k_src);
+    const u32x4* sv = reinterpret_cast<const u32x4*>(v_src);
+    const uint32_t* sks = reinterpret_cast<const uint32_t*>(ks_src);
+    const uint32_t* svs = reinterpret_cast<const uint32_t*>(vs_src);
+    u32x4 rk[UK], rv[UV];
+    uint32_t rks[US], rvs[US];
+#pragma unroll
+    for (int j = 0; j < UK; ++j)
+      if (tid + 256 * j < nk) rk[j] = sk[tid + 256 * j];
+#pragma unroll
+    for (int j = 0; j < UV; ++j)
+      if (tid + 256 * j < nv) rv[j] = sv[tid + 256 * j];
+#pragma unroll
+    for (int j = 0; j < US; ++j) {
+      if (tid + 256 * j < ns) {
+        rks[j] = sks[tid + 256 * j];
+        rvs[j] = svs[tid + 256 * j];
+      }
     }
-    {
-      const uint4* src = reinterpret_cast<const uint4*>(v_src);
-      uint4* dst = reinterpret_cast<uint4*>(s_vc) + at * (VROW / 16);
-      for (int i = tid; i < n * (VROW / 16); i += 256) dst[i] = src[i];
-    }
-    const uint32_t* src_k = reinterpret_cast<const uint32_t*>(ks_src);
-    const uint32_t* src_v = reinterpret_cast<const uint32_t*>(vs_src);
-    uint32_t* dk = reinterpret_cast<uint32_t*>(s_ks) + at * (NG / 2);
-    uint32_t* dv = reinterpret_cast<uint32_t*>(s_vs) + at * (NG / 2);
-    for (int i = tid; i < n * (NG / 2); i += 256) {
-      dk[i] = src_k[i];
-      dv[i] = src_v[i];
+    u32x4* dk = reinterpret_cast<u32x4*>(s_kc) + at * (KROW / 16);
+    u32x4* dv = reinterpret_cast<u32x4*>(s_vc) + at * (VROW / 16);
+    uint32_t* dks = reinterpret_cast<uint32_t*>(s_ks) + at * (NG / 2);
+    uint32_t* dvs = reinterpret_cast<uint32_t*>(s_vs) + at * (NG / 2);
+#pragma unroll
+    for (int j = 0; j < UK; ++j)
+      if (tid + 256 * j < nk) dk[tid + 256 * j] = rk[j];
+#pragma unroll
+    for (int j = 0; j < UV; ++j)
+      if (tid + 256 * j < nv) dv[tid + 256 * j] = rv[j];
+#pragma unroll
+    for (int j = 0; j < US; ++j) {
+      if (tid + 256 * j < ns) {
+        dks[tid + 256 * j] = rks[j];
+        dvs[tid + 256 * j] = rvs[j];
+      }
     }
   };
   int first = 0, lo, n_rows;
