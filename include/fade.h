@@ -273,7 +273,12 @@ int fade_h2o_scores(const fade_config* cfg, int32_t mode, fade_layer_cache* cach
  * values move bit-for-bit; unmoved slots are untouched; scores move with
  * their slots.
  *   max_evict  upper bound on M - int4_budget for this call (sizes the
- *              rotation table); 0 means cap_mid - int4_budget
+ *              rotation table); 0 means cap_mid - int4_budget. Sequences
+ *              whose M - int4_budget exceeds it are left as they are. A
+ *              bound of 1 (any policy; the per-step serving loop with
+ *              cap_mid = int4_budget + 1 gets it by default) or of at most 8
+ *              with FADE_POLICY_POSITION lets the compaction run as one
+ *              launch without a spill copy.
  *   workspace  >= fade_workspace_bytes(cfg, FADE_WS_EVICT, batch, cap_mid)
  */
 int fade_evict_rerope(const fade_config* cfg, fade_layer_cache* cache, int32_t policy,

@@ -20,7 +20,11 @@
 // slots, so each workgroup stages the moved rows of its own chunk in LDS,
 // waits, and then writes every destination that lies inside its own chunk;
 // destinations that fall into an earlier chunk go to a spill region that a
-// second kernel copies after the grid has drained. Keys of moved rows are
+// second kernel copies after the grid has drained. When every event is a run
+// of at most kHalo slots, the selection launch first copies the first n_ev
+// rows of each chunk aside (the halo of the chunk before it) and each
+// compaction workgroup writes exactly its own slots, so the second kernel is
+// not needed. Keys of moved rows are
 // dequantized, rotated by R(-delta) from a float64 cos/sin table, rounded to
 // fp16 once and requantized, one lane per rotation pair; values move as
 // packed bytes.
