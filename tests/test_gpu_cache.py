@@ -116,6 +116,30 @@ def test_decode_eviction_compaction(policy, d, kb, vb, budget, extra):
         assert_state_equal(seq_state(tc, b), refs[b])
 
 
+@pytest.mark.parametrize("policy,extra", [("score", 1), ("position", 1), ("position", 6), ("score", 37)])
+def test_shared_batch_decode_eviction(policy, extra):
+    """A shared score row (one selection for every sequence of the batch):
+    the decode-time event evicts the same slots from each sequence and sets
+    every sequence's middle length; runs of 1 and 6 slots take the halo path,
+    the 37-slot score event the general one."""
+    d, budget, B = 64, 200, 3
+    cfg_big = _cfg(d=d, hq=8, hkv=2, n_sink=4, w=32, budget=-1, kb=4, vb=2, rope_theta=1e6)
+    L = 4 + budget + extra + 32
+    sc = _scores(1, L, 295 + extra, ties=True)
+    tc, refs, _ = build_both(cfg_big, B, L, 296, cap_mid=budget + extra, scores32=sc, shared=True)
+    for b in range(B):
+        assert_state_equal(seq_state(tc, b), refs[b])
+    cfg = _cfg(d=d, hq=8, hkv=2, n_sink=4, w=32, budget=budget, kb=4, vb=2, rope_theta=1e6)
+    ws = fade.workspace(cfg, fade.WS_EVICT, B, budget + extra)
+    fade.fade_evict_rerope(cfg, tc, fade.POLICY_POSITION if policy == "position" else fade.POLICY_SCORE, ws)
+    torch.cuda.synchronize()
+    for b in range(B):
+        refs[b].cfg = ocfg(cfg)
+        oc.evict(refs[b], budget, policy)
+        assert refs[b].mid_len == budget
+        assert_state_equal(seq_state(tc, b), refs[b])
+
+
 @pytest.mark.parametrize("victim", [0, 126, 127, 128, 255, 299, 300])
 def test_single_eviction_at_chunk_edges(victim):
     """One score eviction whose victim sits on either side of a 128-row chunk
