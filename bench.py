@@ -397,18 +397,19 @@ def time_pq_attention(wl, calls):
     vcb = torch.randn(fade.PQ_SUB, fade.PQ_K, d // fade.PQ_SUB, device="cuda", generator=g).half()
     q = torch.randn(B, hq, d, device="cuda", generator=g).half()
     out = torch.empty(B, hq, d, device="cuda")
+    ws = fade.pq_attn_workspace(d, hq, B, n)
     for _ in range(3):
-        fade.fade_pq_decode_attn(q, kc, vc, kcb, vcb, out)
+        fade.fade_pq_decode_attn(q, kc, vc, kcb, vcb, out, ws)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
     for _ in range(calls):
-        fade.fade_pq_decode_attn(q, kc, vc, kcb, vcb, out)
+        fade.fade_pq_decode_attn(q, kc, vc, kcb, vcb, out, ws)
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1000 / calls
     code_bytes = B * hkv * n * 2 * fade.PQ_SUB
-    return {"avg_us_per_launch": us, "calls": calls, "batch": B, "tokens": n, "kernels": "k_pq_attn",
+    return {"avg_us_per_launch": us, "calls": calls, "batch": B, "tokens": n, "kernels": "k_pq_attn (+ k_pq_attn_merge with token splits)",
             "code_bytes_per_launch": code_bytes, "achieved_GBps": code_bytes / us / 1e3, "bound": "lds",
             "note": "attention over PQ-coded keys and values (2 bits per element), middle-tier size; "
                     "synthetic codes"}

@@ -369,14 +369,21 @@ size_t fade_pq_workspace_bytes(int32_t head_dim, int64_t n_rows);
  *   v_codebook  device fp16 [32][256][head_dim / 32], 16-byte aligned
  *   out         device float32 [batch][n_q_heads][head_dim], written whole
  *               (zeros when n_tokens == 0)
- * Scores and the softmax are float32; the values are summed per sub-space and
- * centroid before the value codebook is applied. head_dim 64 or 128
+ *   workspace   device, >= fade_pq_attn_workspace_bytes(head_dim, n_q_heads,
+ *               batch, n_tokens) bytes, 16-byte aligned (FADE_ERR_WORKSPACE
+ *               otherwise); unused when that size is 0
+ * Scores and the softmax are float32 (a running maximum per 256-token chunk;
+ * token splits merged by their maxima). head_dim 64 or 128
  * (FADE_ERR_UNSUPPORTED otherwise); n_q_heads a multiple of n_kv_heads,
  * 0 <= batch <= 65535, n_tokens >= 0 (FADE_ERR_INVALID_ARG otherwise, also for
  * NULL or misaligned pointers). Asynchronous on stream; nothing is allocated. */
 int fade_pq_decode_attn(int32_t head_dim, int32_t n_q_heads, int32_t n_kv_heads, int32_t batch, int64_t n_tokens,
                         const void* q, const void* k_codes, const void* v_codes, const void* k_codebook,
-                        const void* v_codebook, void* out, void* stream);
+                        const void* v_codebook, void* out, void* workspace, size_t ws_bytes, void* stream);
+/* Workspace bytes of fade_pq_decode_attn (partials of the token splits that
+ * fill the GPU when batch * n_q_heads is small); 0 when no split is needed
+ * (workspace may then be NULL) or for invalid arguments. */
+size_t fade_pq_attn_workspace_bytes(int32_t head_dim, int32_t n_q_heads, int32_t batch, int64_t n_tokens);
 
 #ifdef __cplusplus
 }

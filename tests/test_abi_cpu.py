@@ -203,7 +203,10 @@ def test_pq_decode_attn_validation():
     lib = fade.lib()
     null = ctypes.c_void_p(0)
     p16 = ctypes.c_void_p(16)
-    f = lib.fade_pq_decode_attn
+    f0 = lib.fade_pq_decode_attn
+
+    def f(*args):
+        return f0(*args[:-1], null, 0, args[-1])
     assert f(96, 8, 2, 1, 10, p16, p16, p16, p16, p16, p16, null) == fade.FADE_ERR_UNSUPPORTED
     assert f(128, 8, 3, 1, 10, p16, p16, p16, p16, p16, p16, null) == fade.FADE_ERR_INVALID_ARG   # GQA ratio
     assert f(128, 0, 1, 1, 10, p16, p16, p16, p16, p16, p16, null) == fade.FADE_ERR_INVALID_ARG
@@ -216,3 +219,11 @@ def test_pq_decode_attn_validation():
     assert f(128, 8, 2, 1, 10, p16, p16, p16, p16, p16, ctypes.c_void_p(18), null) == fade.FADE_ERR_INVALID_ARG
     assert f(128, 8, 2, 1, 10, p16, p16, p16, ctypes.c_void_p(24), p16, p16, null) == fade.FADE_ERR_INVALID_ARG
     assert f(64, 4, 4, 0, 10, null, null, null, null, null, null, null) == fade.FADE_OK              # empty batch
+    # token splits for a small batch need a workspace
+    ws = lib.fade_pq_attn_workspace_bytes(128, 32, 1, 8192)
+    assert ws >= 32 * 2 * (128 + 2) * 4
+    assert lib.fade_pq_attn_workspace_bytes(128, 32, 64, 2048) == 0          # enough workgroups without splits
+    assert lib.fade_pq_attn_workspace_bytes(128, 32, 1, 0) == 0
+    assert lib.fade_pq_attn_workspace_bytes(96, 32, 1, 8192) == 0
+    assert f0(128, 32, 8, 1, 8192, p16, p16, p16, p16, p16, p16, null, 0, null) == fade.FADE_ERR_WORKSPACE
+    assert f0(128, 32, 8, 1, 8192, p16, p16, p16, p16, p16, p16, p16, ws - 1, null) == fade.FADE_ERR_WORKSPACE

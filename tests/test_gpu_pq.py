@@ -87,12 +87,14 @@ def test_pq_train_matches_oracle(d, n, iters):
 
 
 @pytest.mark.parametrize("d,hq,hkv,B,n", [(128, 8, 2, 2, 1000), (128, 32, 8, 1, 4099), (64, 4, 4, 3, 257),
-                                          (64, 8, 1, 2, 1), (128, 8, 2, 2, 0)])
+                                          (64, 8, 1, 2, 1), (128, 8, 2, 2, 0), (128, 4, 1, 1, 20000),
+                                          (64, 32, 8, 64, 600)])
 def test_pq_decode_attn_matches_oracle(d, hq, hkv, B, n):
     """Attention over PQ-coded keys and values against the oracle (float64 over
     the decoded centroids). Codebooks are N(0, 1) fp16, codes uniform; the
     query is scaled by 2 so the softmax is far from uniform. Several
-    256-token strides and a ragged tail, n_rep 1 / 4 / 8, and no tokens."""
+    256-token strides and a ragged tail, n_rep 1 / 4 / 8, no tokens, and
+    small batches whose tokens are split over several workgroups (and merged)."""
     gen = synth.rng(530 + n)
     l = d // pq.N_SUB
     kcb = gen.standard_normal((pq.N_SUB, pq.K, l)).astype(np.float16)
@@ -101,7 +103,8 @@ def test_pq_decode_attn_matches_oracle(d, hq, hkv, B, n):
     vc = gen.integers(0, pq.K, size=(B, hkv, n, pq.N_SUB)).astype(np.uint8)
     q = (2 * gen.standard_normal((B, hq, d))).astype(np.float16)
     out = torch.full((B, hq, d), float("nan"), dtype=torch.float32, device=DEV)
-    fade.fade_pq_decode_attn(_dev(q), _dev(kc), _dev(vc), _dev(kcb), _dev(vcb), out)
+    ws = fade.pq_attn_workspace(d, hq, B, n)
+    fade.fade_pq_decode_attn(_dev(q), _dev(kc), _dev(vc), _dev(kcb), _dev(vcb), out, ws)
     torch.cuda.synchronize()
     got = out.cpu().numpy().astype(np.float64)
     for b in range(B):

@@ -362,9 +362,14 @@ int fade_pq_train_step(int32_t head_dim, const void* x, int64_t n_rows, const vo
                                          reinterpret_cast<hipStream_t>(stream)));
 }
 
+size_t fade_pq_attn_workspace_bytes(int32_t head_dim, int32_t n_q_heads, int32_t batch, int64_t n_tokens) {
+  if ((head_dim != 64 && head_dim != 128) || n_q_heads < 1 || batch < 0 || n_tokens < 0) return 0;
+  return pq_attn_ws_bytes(head_dim, batch, n_q_heads, n_tokens);
+}
+
 int fade_pq_decode_attn(int32_t head_dim, int32_t n_q_heads, int32_t n_kv_heads, int32_t batch, int64_t n_tokens,
                         const void* q, const void* k_codes, const void* v_codes, const void* k_codebook,
-                        const void* v_codebook, void* out, void* stream) {
+                        const void* v_codebook, void* out, void* workspace, size_t ws_bytes, void* stream) {
   if (head_dim != 64 && head_dim != 128) return FADE_ERR_UNSUPPORTED;
   if (n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads != 0 || batch < 0 || batch > 65535 || n_tokens < 0)
     return FADE_ERR_INVALID_ARG;
@@ -373,11 +378,13 @@ int fade_pq_decode_attn(int32_t head_dim, int32_t n_q_heads, int32_t n_kv_heads,
       !aligned16(v_codebook) || !aligned(out, 4))
     return FADE_ERR_INVALID_ARG;
   if (n_tokens > 0 && (!k_codes || !v_codes || !aligned16(k_codes) || !aligned16(v_codes))) return FADE_ERR_INVALID_ARG;
+  const size_t need = pq_attn_ws_bytes(head_dim, batch, n_q_heads, n_tokens);
+  if (need > 0 && (!workspace || !aligned16(workspace) || ws_bytes < need)) return FADE_ERR_WORKSPACE;
   return hip_status(launch_pq_attn(head_dim, reinterpret_cast<const uint16_t*>(q),
                                    reinterpret_cast<const uint8_t*>(k_codes), reinterpret_cast<const uint8_t*>(v_codes),
                                    reinterpret_cast<const uint16_t*>(k_codebook),
                                    reinterpret_cast<const uint16_t*>(v_codebook), reinterpret_cast<float*>(out), batch,
-                                   n_q_heads, n_kv_heads, n_tokens, reinterpret_cast<hipStream_t>(stream)));
+                                   n_q_heads, n_kv_heads, n_tokens, workspace, reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

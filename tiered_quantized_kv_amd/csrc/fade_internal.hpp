@@ -74,7 +74,8 @@ hipError_t launch_pq_train_step(int D, const uint16_t* x, int64_t n, const uint1
                                 void* ws, hipStream_t st);
 hipError_t launch_pq_attn(int D, const uint16_t* q, const uint8_t* kcodes, const uint8_t* vcodes,
                           const uint16_t* kcb, const uint16_t* vcb, float* out, int batch, int n_q_heads, int n_kv_heads,
-                          int64_t n_tok, hipStream_t st);
+                          int64_t n_tok, void* ws, hipStream_t st);
+size_t pq_attn_ws_bytes(int D, int batch, int n_q_heads, int64_t n_tok);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

@@ -211,7 +211,8 @@ template <int L>
 __global__ __launch_bounds__(256) void k_pq_attn(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kcodes,
                                                  const uint8_t* __restrict__ vcodes, const uint16_t* __restrict__ kcb,
                                                  const uint16_t* __restrict__ vcb, float* __restrict__ out,
-                                                 int n_q_heads, int n_rep, int64_t n_tok, float scale) {
+                                                 float* __restrict__ partials, int n_q_heads, int n_rep,
+                                                 int64_t n_tok, int64_t per_split, float scale) {
   constexpr int D = L * kPqSub;
   constexpr int PER = kPqSub * kPqK / 256;        // table entries per lane
   constexpr int VCB16 = kPqSub * kPqK * L * 2 / 16;   // 16-byte units of a codebook
@@ -222,10 +223,12 @@ __global__ __launch_bounds__(256) void k_pq_attn(const uint16_t* __restrict__ q,
   __shared__ float qs[D];
   __shared__ float part[4 * D];
   __shared__ float red[4];
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int h = blockIdx.x, b = blockIdx.y, split = blockIdx.z, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n_kv = n_q_heads / n_rep, g = h / n_rep;
   const size_t qh = (size_t)b * n_q_heads + h;
+  // this workgroup's tokens [t_lo, t_hi)
+  const int64_t t_lo = min((int64_t)split * per_split, n_tok), t_hi = min(t_lo + per_split, n_tok);
   if (tid < D) qs[tid] = h2f(q[qh * D + tid]);
 #pragma unroll
   for (int j = 0; j < VCB16 / 256; ++j)
@@ -268,16 +271,16 @@ __global__ __launch_bounds__(256) void k_pq_attn(const uint16_t* __restrict__ q,
   for (int e = 0; e < L; ++e) acc[e] = 0.f;
   {
     uint4 n0 = make_uint4(0, 0, 0, 0), n1 = n0, m0 = n0, m1 = n0;
-    if (tid < n_tok) {
-      n0 = kr[2 * tid];
-      n1 = kr[2 * tid + 1];
-      m0 = vr[2 * tid];
-      m1 = vr[2 * tid + 1];
+    if (t_lo + tid < t_hi) {
+      n0 = kr[2 * (t_lo + tid)];
+      n1 = kr[2 * (t_lo + tid) + 1];
+      m0 = vr[2 * (t_lo + tid)];
+      m1 = vr[2 * (t_lo + tid) + 1];
     }
-    for (int64_t c0 = 0; c0 < n_tok; c0 += 256) {   // the same trip count in every wave
+    for (int64_t c0 = t_lo; c0 < t_hi; c0 += 256) {   // the same trip count in every wave
       const int64_t t = c0 + tid;
       const uint4 k0 = n0, k1 = n1, d0 = m0, d1 = m1;
-      if (t + 256 < n_tok) {
+      if (t + 256 < t_hi) {
         n0 = kr[2 * (t + 256)];
         n1 = kr[2 * (t + 256) + 1];
         m0 = vr[2 * (t + 256)];
@@ -285,7 +288,7 @@ __global__ __launch_bounds__(256) void k_pq_attn(const uint16_t* __restrict__ q,
       }
       // past the end the score is -inf and p is 0 (the codes there are stale
       // in-range bytes)
-      const float sc = t < n_tok ? score(k0, k1) : -INFINITY;
+      const float sc = t < t_hi ? score(k0, k1) : -INFINITY;
       float cm = sc;
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) cm = fmaxf(cm, __shfl_xor(cm, o));
@@ -326,20 +329,76 @@ __global__ __launch_bounds__(256) void k_pq_attn(const uint16_t* __restrict__ q,
   }
   __syncthreads();
   sum = (red[0] + red[1]) + (red[2] + red[3]);
-  const float inv = sum > 0.f ? 1.f / sum : 0.f;
-  if (tid < D) out[qh * D + tid] = ((part[tid] + part[D + tid]) + (part[2 * D + tid] + part[3 * D + tid])) * inv;
+  const float o = tid < D ? (part[tid] + part[D + tid]) + (part[2 * D + tid] + part[3 * D + tid]) : 0.f;
+  if (gridDim.z == 1) {
+    const float inv = sum > 0.f ? 1.f / sum : 0.f;
+    if (tid < D) out[qh * D + tid] = o * inv;
+  } else {
+    // partial of this split: {running maximum, probability sum, D unnormalized sums}
+    float* pp = partials + (qh * gridDim.z + split) * (D + 2);
+    if (tid == 0) {
+      pp[0] = mrun;
+      pp[1] = sum;
+    }
+    if (tid < D) pp[2 + tid] = o;
+  }
+}
+
+// Merge of the token splits of one (sequence, query head): one lane per
+// output element; a split without tokens has maximum -inf and weight 0.
+template <int D>
+__global__ __launch_bounds__(128) void k_pq_attn_merge(const float* __restrict__ partials, int nsplit,
+                                                       float* __restrict__ out) {
+  const size_t qh = (size_t)blockIdx.y * gridDim.x + blockIdx.x;
+  const float* pp = partials + qh * nsplit * (D + 2);
+  float m = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) m = fmaxf(m, pp[s * (D + 2)]);
+  float l = 0.f, o = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float ms = pp[s * (D + 2)];
+    const float w = ms == -INFINITY ? 0.f : expf(ms - m);
+    l += w * pp[s * (D + 2) + 1];
+    if (threadIdx.x < D) o += w * pp[s * (D + 2) + 2 + threadIdx.x];
+  }
+  if (threadIdx.x < D) out[qh * D + threadIdx.x] = l > 0.f ? o / l : 0.f;
+}
+
+// Token splits per (sequence, query head): enough workgroups for about two
+// per compute unit, each split at least 1024 tokens.
+int pq_attn_splits(int batch, int n_q_heads, int64_t n_tok) {
+  const int64_t heads = (int64_t)batch * n_q_heads;
+  int64_t n = (512 + heads - 1) / heads;
+  const int64_t cap = (n_tok + 1023) / 1024;
+  if (n > cap) n = cap;
+  if (n > 64) n = 64;
+  return n < 1 ? 1 : (int)n;
+}
+
+size_t pq_attn_ws_bytes(int D, int batch, int n_q_heads, int64_t n_tok) {
+  const int ns = pq_attn_splits(batch, n_q_heads, n_tok);
+  return ns > 1 ? (size_t)batch * n_q_heads * ns * (D + 2) * 4 : 0;
 }
 
 hipError_t launch_pq_attn(int D, const uint16_t* q, const uint8_t* kcodes, const uint8_t* vcodes,
                           const uint16_t* kcb, const uint16_t* vcb, float* out, int batch, int n_q_heads, int n_kv_heads,
-                          int64_t n_tok, hipStream_t st) {
-  const dim3 grid(n_q_heads, batch);
+                          int64_t n_tok, void* ws, hipStream_t st) {
+  const int ns = pq_attn_splits(batch, n_q_heads, n_tok);
+  const int64_t per = ns > 1 ? ((n_tok + ns - 1) / ns + 255) / 256 * 256 : (n_tok > 0 ? n_tok : 1);
+  const dim3 grid(n_q_heads, batch, ns);
   const int n_rep = n_q_heads / n_kv_heads;
   const float scale = 1.0f / sqrtf((float)D);
+  float* part = reinterpret_cast<float*>(ws);
   if (D == 128)
-    hipLaunchKernelGGL(k_pq_attn<4>, grid, dim3(256), 0, st, q, kcodes, vcodes, kcb, vcb, out, n_q_heads, n_rep, n_tok, scale);
+    hipLaunchKernelGGL(k_pq_attn<4>, grid, dim3(256), 0, st, q, kcodes, vcodes, kcb, vcb, out, part, n_q_heads, n_rep,
+                       n_tok, per, scale);
   else
-    hipLaunchKernelGGL(k_pq_attn<2>, grid, dim3(256), 0, st, q, kcodes, vcodes, kcb, vcb, out, n_q_heads, n_rep, n_tok, scale);
+    hipLaunchKernelGGL(k_pq_attn<2>, grid, dim3(256), 0, st, q, kcodes, vcodes, kcb, vcb, out, part, n_q_heads, n_rep,
+                       n_tok, per, scale);
+  if (ns > 1) {
+    const dim3 mgrid(n_q_heads, batch);
+    if (D == 128) hipLaunchKernelGGL(k_pq_attn_merge<128>, mgrid, dim3(128), 0, st, part, ns, out);
+    else hipLaunchKernelGGL(k_pq_attn_merge<64>, mgrid, dim3(128), 0, st, part, ns, out);
+  }
   return hipGetLastError();
 }
 

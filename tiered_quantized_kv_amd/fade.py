@@ -76,7 +76,9 @@ _SIGS = {
     "fade_pq_train_step": (ctypes.c_int, [ctypes.c_int32, _P, ctypes.c_int64, _P, _P, _P, ctypes.c_size_t, _P]),
     "fade_pq_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int32, ctypes.c_int64]),
     "fade_pq_decode_attn": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                           ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P]),
+                                           ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "fade_pq_attn_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                       ctypes.c_int64]),
 }
 
 
@@ -268,10 +270,18 @@ def fade_pq_train_step(x, codebook_in, codebook_out, ws, stream=None):
                                     ws.numel(), _s(stream)), "fade_pq_train_step")
 
 
-def fade_pq_decode_attn(q, k_codes, v_codes, k_codebook, v_codebook, out, stream=None):
+def pq_attn_workspace(head_dim, n_q_heads, batch, n_tokens, device="cuda"):
+    """Workspace of fade_pq_decode_attn (None when the call needs none)."""
+    import torch
+    n = int(lib().fade_pq_attn_workspace_bytes(head_dim, n_q_heads, batch, n_tokens))
+    return torch.empty(n, dtype=torch.uint8, device=device) if n > 0 else None
+
+
+def fade_pq_decode_attn(q, k_codes, v_codes, k_codebook, v_codebook, out, ws=None, stream=None):
     """q fp16 [B, Hq, d]; k_codes, v_codes u8 [B, Hkv, N, 32]; codebooks fp16
-    [32, 256, d / 32] -> out float32 [B, Hq, d]."""
+    [32, 256, d / 32] -> out float32 [B, Hq, d]. ws: pq_attn_workspace(...)."""
     B, hq, d = q.shape
     hkv, n = k_codes.shape[1], k_codes.shape[2]
     _check(lib().fade_pq_decode_attn(d, hq, hkv, B, n, _p(q), _p(k_codes), _p(v_codes), _p(k_codebook),
-                                     _p(v_codebook), _p(out), _s(stream)), "fade_pq_decode_attn")
+                                     _p(v_codebook), _p(out), _p(ws), 0 if ws is None else ws.numel(), _s(stream)),
+           "fade_pq_decode_attn")
