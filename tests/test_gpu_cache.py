@@ -164,14 +164,17 @@ def test_single_eviction_at_chunk_edges(victim):
         assert_state_equal(seq_state(tc, b), refs[b])
 
 
-@pytest.mark.parametrize("rtype", ["linear", "ntk", "yarn", "none", "dynamic", "proportional"])
-def test_rope_schemes_prefill_and_decode_eviction(rtype):
+@pytest.mark.parametrize("rtype,policy,extra", [(r, "score", 37) for r in
+                                                 ["linear", "ntk", "yarn", "none", "dynamic", "proportional"]] +
+                         [("none", "position", 3), ("yarn", "score", 1), ("dynamic", "position", 8)])
+def test_rope_schemes_prefill_and_decode_eviction(rtype, policy, extra):
     """Each further RoPE scheme through both compactions: the fp16 re-RoPE of a
     prefill build with score eviction, then a decode-time eviction event that
     re-rotates the recent ring and requantizes moved middle keys (without a
-    rotary embedding keys move bit-for-bit, like values)."""
+    rotary embedding keys move bit-for-bit, like values); the one-slot score
+    event and the 3- and 8-slot position events take the halo path."""
     kw = ROPE_KW[rtype]
-    budget, extra = 300, 37
+    budget = 300
     L = 4 + budget + extra + 32
     B = 2
     cfg0 = _cfg(d=128, hq=8, hkv=2, n_sink=4, w=32, budget=budget + extra, kb=4, vb=2, **kw)
@@ -181,15 +184,15 @@ def test_rope_schemes_prefill_and_decode_eviction(rtype):
         assert_state_equal(seq_state(tc, b), refs[b])
     cfg = _cfg(d=128, hq=8, hkv=2, n_sink=4, w=32, budget=budget, kb=4, vb=2, **kw)
     ws = fade.workspace(cfg, fade.WS_EVICT, B, budget + extra)
-    fade.fade_evict_rerope(cfg, tc, fade.POLICY_SCORE, ws)
+    fade.fade_evict_rerope(cfg, tc, fade.POLICY_POSITION if policy == "position" else fade.POLICY_SCORE, ws)
     torch.cuda.synchronize()
     for b in range(B):
         refs[b].cfg = ocfg(cfg)
-        oc.evict(refs[b], budget, "score")
+        oc.evict(refs[b], budget, policy)
         assert_state_equal(seq_state(tc, b), refs[b])
 
 
-@pytest.mark.parametrize("policy,extra", [("score", 37), ("position", 37), ("score", 1)])
+@pytest.mark.parametrize("policy,extra", [("score", 37), ("position", 37), ("score", 1), ("position", 5)])
 @pytest.mark.parametrize("d,kb,vb,rtype", [(128, 4, 2, "default"), (64, 2, 4, "yarn"), (64, 4, 4, "proportional")])
 def test_interleaved_pairing_prefill_and_decode_eviction(d, kb, vb, rtype, policy, extra):
     """GPT-J pairing through both compactions: the prefill build's fp16
