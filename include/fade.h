@@ -372,7 +372,8 @@ size_t fade_pq_workspace_bytes(int32_t head_dim, int64_t n_rows);
  *   workspace   device, >= fade_pq_attn_workspace_bytes(head_dim, n_q_heads,
  *               batch, n_tokens) bytes, 16-byte aligned (FADE_ERR_WORKSPACE
  *               otherwise); unused when that size is 0
- * Scores and the softmax are float32 (a running maximum per 256-token chunk;
+ * Scores and the softmax are float32 (a running maximum per chunk of 512
+ * tokens at head_dim 128, 256 at 64;
  * token splits merged by their maxima). head_dim 64 or 128
  * (FADE_ERR_UNSUPPORTED otherwise); n_q_heads a multiple of n_kv_heads,
  * 0 <= batch <= 65535, n_tokens >= 0 (FADE_ERR_INVALID_ARG otherwise, also for

@@ -34,6 +34,9 @@ namespace fade {
 
 constexpr int kPqSub = 32;
 constexpr int kPqK = 256;
+// attention workgroup (lanes = tokens per chunk): 512 at d 128, 256 at d 64
+// (whose smaller LDS footprint then fits two workgroups per CU)
+constexpr int pq_attn_threads(int L) { return L == 4 ? 512 : 256; }
 
 size_t pq_ws_bytes(int D, int64_t n) {
   const int l = D / kPqSub;
@@ -185,11 +188,12 @@ hipError_t launch_pq_train_step(int D, const uint16_t* x, int64_t n, const uint1
 // h / n_rep. Scores are scale * sum_s T[s][code_s] with T[s][k] the fp32
 // inner product of the query's sub-vector s with key centroid k (one lane per
 // token, 32 table reads); softmax in fp32 against a running maximum (online
-// rescaling per 256-token chunk). The value sum is gathered with one lane per
-// sub-space: each wave walks its 64 tokens two at a time, lane s of each half
+// rescaling per chunk of NT tokens, NT the lanes of the workgroup). The value
+// sum is gathered with one lane per sub-space: each wave walks its 64 tokens
+// two at a time, lane s of each half
 // reads the token's value code s and adds p times that centroid (the value
 // codebook sits in LDS), so no two lanes ever update the same accumulator.
-// The next 256 tokens' codes are fetched before the current ones are used.
+// The next chunk's codes are fetched before the current ones are used.
 
 // The L fp16 elements of one centroid (8-byte aligned at L = 4, 4-byte at L = 2).
 template <int L>
@@ -207,22 +211,23 @@ __device__ __forceinline__ void centroid(const uint16_t* p, float (&v)[L]) {
   }
 }
 
-template <int L>
-__global__ __launch_bounds__(256) void k_pq_attn(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kcodes,
+template <int L, int NT = pq_attn_threads(L)>
+__global__ __launch_bounds__(NT) void k_pq_attn(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kcodes,
                                                  const uint8_t* __restrict__ vcodes, const uint16_t* __restrict__ kcb,
                                                  const uint16_t* __restrict__ vcb, float* __restrict__ out,
                                                  float* __restrict__ partials, int n_q_heads, int n_rep,
                                                  int64_t n_tok, int64_t per_split, float scale) {
   constexpr int D = L * kPqSub;
-  constexpr int PER = kPqSub * kPqK / 256;        // table entries per lane
+  constexpr int NW = NT / 64;                     // waves
+  constexpr int PER = kPqSub * kPqK / NT;         // table entries per lane
   constexpr int VCB16 = kPqSub * kPqK * L * 2 / 16;   // 16-byte units of a codebook
   __shared__ float tab[kPqSub * kPqK];
   __shared__ __align__(16) uint16_t vcl[kPqSub * kPqK * L];
-  __shared__ __align__(16) uint32_t vbuf[256 * 8];   // value codes of the current 256 tokens
-  __shared__ float pbuf[256];
+  __shared__ __align__(16) uint32_t vbuf[NT * 8];    // value codes of the current NT tokens
+  __shared__ float pbuf[NT];
   __shared__ float qs[D];
-  __shared__ float part[4 * D];
-  __shared__ float red[4];
+  __shared__ float part[NW * D];
+  __shared__ float red[NW];
   const int h = blockIdx.x, b = blockIdx.y, split = blockIdx.z, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n_kv = n_q_heads / n_rep, g = h / n_rep;
@@ -231,13 +236,13 @@ __global__ __launch_bounds__(256) void k_pq_attn(const uint16_t* __restrict__ q,
   const int64_t t_lo = min((int64_t)split * per_split, n_tok), t_hi = min(t_lo + per_split, n_tok);
   if (tid < D) qs[tid] = h2f(q[qh * D + tid]);
 #pragma unroll
-  for (int j = 0; j < VCB16 / 256; ++j)
-    reinterpret_cast<uint4*>(vcl)[tid + 256 * j] = reinterpret_cast<const uint4*>(vcb)[tid + 256 * j];
+  for (int j = 0; j < VCB16 / NT; ++j)
+    reinterpret_cast<uint4*>(vcl)[tid + NT * j] = reinterpret_cast<const uint4*>(vcb)[tid + NT * j];
   __syncthreads();
   // entry i = s * 256 + k
 #pragma unroll 16
   for (int j = 0; j < PER; ++j) {
-    const int i = tid + 256 * j;
+    const int i = tid + NT * j;
     float c[L];
     centroid<L>(kcb + (size_t)i * L, c);
     const int sub = i / kPqK;
@@ -259,7 +264,7 @@ __global__ __launch_bounds__(256) void k_pq_attn(const uint16_t* __restrict__ q,
       for (int k = 0; k < 4; ++k) acc += tab[(4 * j + k) * kPqK + ((w[j] >> (8 * k)) & 0xFFu)];
     return acc * scale;
   };
-  // One pass in chunks of 256 tokens with a running maximum: each chunk's
+  // One pass in chunks of NT tokens with a running maximum: each chunk's
   // maximum is taken over the workgroup before its probabilities are formed,
   // and the lane's accumulators and probability sum are rescaled when the
   // maximum grows. Each wave then gathers the value centroids of its 64
@@ -277,14 +282,14 @@ __global__ __launch_bounds__(256) void k_pq_attn(const uint16_t* __restrict__ q,
       m0 = vr[2 * (t_lo + tid)];
       m1 = vr[2 * (t_lo + tid) + 1];
     }
-    for (int64_t c0 = t_lo; c0 < t_hi; c0 += 256) {   // the same trip count in every wave
+    for (int64_t c0 = t_lo; c0 < t_hi; c0 += NT) {    // the same trip count in every wave
       const int64_t t = c0 + tid;
       const uint4 k0 = n0, k1 = n1, d0 = m0, d1 = m1;
-      if (t + 256 < t_hi) {
-        n0 = kr[2 * (t + 256)];
-        n1 = kr[2 * (t + 256) + 1];
-        m0 = vr[2 * (t + 256)];
-        m1 = vr[2 * (t + 256) + 1];
+      if (t + NT < t_hi) {
+        n0 = kr[2 * (t + NT)];
+        n1 = kr[2 * (t + NT) + 1];
+        m0 = vr[2 * (t + NT)];
+        m1 = vr[2 * (t + NT) + 1];
       }
       // past the end the score is -inf and p is 0 (the codes there are stale
       // in-range bytes)
@@ -296,7 +301,10 @@ __global__ __launch_bounds__(256) void k_pq_attn(const uint16_t* __restrict__ q,
       reinterpret_cast<uint4*>(vbuf)[2 * tid] = d0;
       reinterpret_cast<uint4*>(vbuf)[2 * tid + 1] = d1;
       __syncthreads();
-      const float mnew = fmaxf(mrun, fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+      float cmax = red[0];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) cmax = fmaxf(cmax, red[w]);
+      const float mnew = fmaxf(mrun, cmax);
       const float f = expf(mrun - mnew);             // 0 on the first chunk
       mrun = mnew;
       const float p = expf(sc - mnew);
@@ -328,8 +336,13 @@ __global__ __launch_bounds__(256) void k_pq_attn(const uint16_t* __restrict__ q,
     for (int e = 0; e < L; ++e) part[wave * D + sub * L + e] = acc[e];
   }
   __syncthreads();
-  sum = (red[0] + red[1]) + (red[2] + red[3]);
-  const float o = tid < D ? (part[tid] + part[D + tid]) + (part[2 * D + tid] + part[3 * D + tid]) : 0.f;
+  float tot = 0.f, o = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    tot += red[w];
+    if (tid < D) o += part[w * D + tid];
+  }
+  sum = tot;
   if (gridDim.z == 1) {
     const float inv = sum > 0.f ? 1.f / sum : 0.f;
     if (tid < D) out[qh * D + tid] = o * inv;
@@ -383,16 +396,17 @@ hipError_t launch_pq_attn(int D, const uint16_t* q, const uint8_t* kcodes, const
                           const uint16_t* kcb, const uint16_t* vcb, float* out, int batch, int n_q_heads, int n_kv_heads,
                           int64_t n_tok, void* ws, hipStream_t st) {
   const int ns = pq_attn_splits(batch, n_q_heads, n_tok);
-  const int64_t per = ns > 1 ? ((n_tok + ns - 1) / ns + 255) / 256 * 256 : (n_tok > 0 ? n_tok : 1);
+  const int nt = pq_attn_threads(D / kPqSub);
+  const int64_t per = ns > 1 ? ((n_tok + ns - 1) / ns + nt - 1) / nt * nt : (n_tok > 0 ? n_tok : 1);
   const dim3 grid(n_q_heads, batch, ns);
   const int n_rep = n_q_heads / n_kv_heads;
   const float scale = 1.0f / sqrtf((float)D);
   float* part = reinterpret_cast<float*>(ws);
   if (D == 128)
-    hipLaunchKernelGGL(k_pq_attn<4>, grid, dim3(256), 0, st, q, kcodes, vcodes, kcb, vcb, out, part, n_q_heads, n_rep,
+    hipLaunchKernelGGL(k_pq_attn<4>, grid, dim3(nt), 0, st, q, kcodes, vcodes, kcb, vcb, out, part, n_q_heads, n_rep,
                        n_tok, per, scale);
   else
-    hipLaunchKernelGGL(k_pq_attn<2>, grid, dim3(256), 0, st, q, kcodes, vcodes, kcb, vcb, out, part, n_q_heads, n_rep,
+    hipLaunchKernelGGL(k_pq_attn<2>, grid, dim3(nt), 0, st, q, kcodes, vcodes, kcb, vcb, out, part, n_q_heads, n_rep,
                        n_tok, per, scale);
   if (ns > 1) {
     const dim3 mgrid(n_q_heads, batch);
