@@ -88,13 +88,16 @@ def test_pq_train_matches_oracle(d, n, iters):
 
 @pytest.mark.parametrize("d,hq,hkv,B,n", [(128, 8, 2, 2, 1000), (128, 32, 8, 1, 4099), (64, 4, 4, 3, 257),
                                           (64, 8, 1, 2, 1), (128, 8, 2, 2, 0), (128, 4, 1, 1, 20000),
-                                          (64, 32, 8, 64, 600)])
+                                          (64, 32, 8, 64, 600), (128, 4, 4, 2, 700), (128, 4, 2, 1, 3000),
+                                          (128, 32, 8, 16, 300), (128, 16, 8, 32, 1100)])
 def test_pq_decode_attn_matches_oracle(d, hq, hkv, B, n):
     """Attention over PQ-coded keys and values against the oracle (float64 over
     the decoded centroids). Codebooks are N(0, 1) fp16, codes uniform; the
     query is scaled by 2 so the softmax is far from uniform. Several
-    256-token strides and a ragged tail, n_rep 1 / 4 / 8, no tokens, and
-    small batches whose tokens are split over several workgroups (and merged)."""
+    token chunks and a ragged tail, n_rep 1 / 2 / 4 / 8, no tokens, small
+    batches whose tokens are split over several workgroups (and merged), and
+    512 (sequence, query head) pairs at d 128, where two query heads share a
+    workgroup."""
     gen = synth.rng(530 + n)
     l = d // pq.N_SUB
     kcb = gen.standard_normal((pq.N_SUB, pq.K, l)).astype(np.float16)

@@ -211,7 +211,7 @@ __device__ __forceinline__ void centroid(const uint16_t* p, float (&v)[L]) {
   }
 }
 
-template <int L, int NT = pq_attn_threads(L)>
+template <int L, int HP, int NT = pq_attn_threads(L)>
 __global__ __launch_bounds__(NT) void k_pq_attn(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kcodes,
                                                  const uint8_t* __restrict__ vcodes, const uint16_t* __restrict__ kcb,
                                                  const uint16_t* __restrict__ vcb, float* __restrict__ out,
@@ -221,59 +221,59 @@ __global__ __launch_bounds__(NT) void k_pq_attn(const uint16_t* __restrict__ q, 
   constexpr int NW = NT / 64;                     // waves
   constexpr int PER = kPqSub * kPqK / NT;         // table entries per lane
   constexpr int VCB16 = kPqSub * kPqK * L * 2 / 16;   // 16-byte units of a codebook
-  __shared__ float tab[kPqSub * kPqK];
+  __shared__ float tab[HP][kPqSub * kPqK];
   __shared__ __align__(16) uint16_t vcl[kPqSub * kPqK * L];
   __shared__ __align__(16) uint32_t vbuf[NT * 8];    // value codes of the current NT tokens
-  __shared__ float pbuf[NT];
-  __shared__ float qs[D];
-  __shared__ float part[NW * D];
-  __shared__ float red[NW];
-  const int h = blockIdx.x, b = blockIdx.y, split = blockIdx.z, tid = threadIdx.x;
+  __shared__ float pbuf[HP][NT];
+  __shared__ float qs[HP][D];
+  __shared__ float part[NW * HP * D];
+  __shared__ float red[HP][NW];
+  // query heads h0 .. h0 + HP - 1 (HP divides n_rep: one KV head g)
+  const int h0 = blockIdx.x * HP, b = blockIdx.y, split = blockIdx.z, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int n_kv = n_q_heads / n_rep, g = h / n_rep;
-  const size_t qh = (size_t)b * n_q_heads + h;
+  const int n_kv = n_q_heads / n_rep, g = h0 / n_rep;
+  const size_t qh0 = (size_t)b * n_q_heads + h0;
   // this workgroup's tokens [t_lo, t_hi)
   const int64_t t_lo = min((int64_t)split * per_split, n_tok), t_hi = min(t_lo + per_split, n_tok);
-  if (tid < D) qs[tid] = h2f(q[qh * D + tid]);
+  for (int i = tid; i < HP * D; i += NT) qs[i / D][i % D] = h2f(q[qh0 * D + i]);
 #pragma unroll
   for (int j = 0; j < VCB16 / NT; ++j)
     reinterpret_cast<uint4*>(vcl)[tid + NT * j] = reinterpret_cast<const uint4*>(vcb)[tid + NT * j];
   __syncthreads();
-  // entry i = s * 256 + k
-#pragma unroll 16
+  // entry i = s * 256 + k; one centroid load serves the HP heads
+#pragma unroll 8
   for (int j = 0; j < PER; ++j) {
     const int i = tid + NT * j;
     float c[L];
     centroid<L>(kcb + (size_t)i * L, c);
     const int sub = i / kPqK;
-    float acc = 0.f;
 #pragma unroll
-    for (int e = 0; e < L; ++e) acc = __builtin_fmaf(qs[sub * L + e], c[e], acc);
-    tab[i] = acc;
+    for (int r = 0; r < HP; ++r) {
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < L; ++e) acc = __builtin_fmaf(qs[r][sub * L + e], c[e], acc);
+      tab[r][i] = acc;
+    }
   }
   __syncthreads();
   const size_t row0 = ((size_t)b * n_kv + g) * (size_t)n_tok;
   const uint4* kr = reinterpret_cast<const uint4*>(kcodes + row0 * kPqSub);
   const uint4* vr = reinterpret_cast<const uint4*>(vcodes + row0 * kPqSub);
-  auto score = [&](const uint4& c0, const uint4& c1) -> float {
-    const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-    float acc = 0.f;
+  // One pass in chunks of NT tokens with a running maximum per head: each
+  // chunk's maximum is taken over the workgroup before its probabilities are
+  // formed, and the lane's accumulators and probability sums are rescaled
+  // when a maximum grows. Each wave then gathers the value centroids of its
+  // 64 tokens, two at a time, one lane per sub-space; each gathered centroid
+  // serves the HP heads.
+  float mrun[HP], sum[HP], acc[HP][L];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+  for (int r = 0; r < HP; ++r) {
+    mrun[r] = -INFINITY;
+    sum[r] = 0.f;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) acc += tab[(4 * j + k) * kPqK + ((w[j] >> (8 * k)) & 0xFFu)];
-    return acc * scale;
-  };
-  // One pass in chunks of NT tokens with a running maximum: each chunk's
-  // maximum is taken over the workgroup before its probabilities are formed,
-  // and the lane's accumulators and probability sum are rescaled when the
-  // maximum grows. Each wave then gathers the value centroids of its 64
-  // tokens, two at a time, one lane per sub-space.
-  float mrun = -INFINITY, sum = 0.f;
+    for (int e = 0; e < L; ++e) acc[r][e] = 0.f;
+  }
   const int sub = lane & 31, half = lane >> 5;
-  float acc[L];
-#pragma unroll
-  for (int e = 0; e < L; ++e) acc[e] = 0.f;
   {
     uint4 n0 = make_uint4(0, 0, 0, 0), n1 = n0, m0 = n0, m1 = n0;
     if (t_lo + tid < t_hi) {
@@ -293,67 +293,100 @@ __global__ __launch_bounds__(NT) void k_pq_attn(const uint16_t* __restrict__ q, 
       }
       // past the end the score is -inf and p is 0 (the codes there are stale
       // in-range bytes)
-      const float sc = t < t_hi ? score(k0, k1) : -INFINITY;
-      float cm = sc;
+      float sc[HP];
+      {
+        const uint32_t w[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) cm = fmaxf(cm, __shfl_xor(cm, o));
-      if (lane == 0) red[wave] = cm;
+        for (int r = 0; r < HP; ++r) sc[r] = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int idx = (4 * j + k) * kPqK + ((w[j] >> (8 * k)) & 0xFFu);
+#pragma unroll
+            for (int r = 0; r < HP; ++r) sc[r] += tab[r][idx];
+          }
+#pragma unroll
+        for (int r = 0; r < HP; ++r) sc[r] = t < t_hi ? sc[r] * scale : -INFINITY;
+      }
+#pragma unroll
+      for (int r = 0; r < HP; ++r) {
+        float cm = sc[r];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) cm = fmaxf(cm, __shfl_xor(cm, o));
+        if (lane == 0) red[r][wave] = cm;
+      }
       reinterpret_cast<uint4*>(vbuf)[2 * tid] = d0;
       reinterpret_cast<uint4*>(vbuf)[2 * tid + 1] = d1;
       __syncthreads();
-      float cmax = red[0];
 #pragma unroll
-      for (int w = 1; w < NW; ++w) cmax = fmaxf(cmax, red[w]);
-      const float mnew = fmaxf(mrun, cmax);
-      const float f = expf(mrun - mnew);             // 0 on the first chunk
-      mrun = mnew;
-      const float p = expf(sc - mnew);
-      sum = sum * f + p;
+      for (int r = 0; r < HP; ++r) {
+        float cmax = red[r][0];
 #pragma unroll
-      for (int e = 0; e < L; ++e) acc[e] *= f;
-      pbuf[tid] = p;
+        for (int w = 1; w < NW; ++w) cmax = fmaxf(cmax, red[r][w]);
+        const float mnew = fmaxf(mrun[r], cmax);
+        const float f = expf(mrun[r] - mnew);          // 0 on the first chunk
+        mrun[r] = mnew;
+        const float p = expf(sc[r] - mnew);
+        sum[r] = sum[r] * f + p;
+#pragma unroll
+        for (int e = 0; e < L; ++e) acc[r][e] *= f;
+        pbuf[r][tid] = p;
+      }
       __syncthreads();
       const uint8_t* vb = reinterpret_cast<const uint8_t*>(vbuf);
 #pragma unroll 8
       for (int u = 0; u < 32; ++u) {
         const int tk = wave * 64 + 2 * u + half;
-        const float pw = pbuf[tk];
         float c[L];
         centroid<L>(vcl + (sub * kPqK + vb[tk * kPqSub + sub]) * L, c);
 #pragma unroll
-        for (int e = 0; e < L; ++e) acc[e] = __builtin_fmaf(pw, c[e], acc[e]);
+        for (int r = 0; r < HP; ++r) {
+          const float pw = pbuf[r][tk];
+#pragma unroll
+          for (int e = 0; e < L; ++e) acc[r][e] = __builtin_fmaf(pw, c[e], acc[r][e]);
+        }
       }
       __syncthreads();                                // buffers are rewritten by the next chunk
     }
   }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+  for (int r = 0; r < HP; ++r) {
 #pragma unroll
-  for (int e = 0; e < L; ++e) acc[e] += __shfl_xor(acc[e], 32);
-  if (lane == 0) red[wave] = sum;
-  if (half == 0) {
+    for (int o = 32; o > 0; o >>= 1) sum[r] += __shfl_xor(sum[r], o);
 #pragma unroll
-    for (int e = 0; e < L; ++e) part[wave * D + sub * L + e] = acc[e];
+    for (int e = 0; e < L; ++e) acc[r][e] += __shfl_xor(acc[r][e], 32);
+    if (lane == 0) red[r][wave] = sum[r];
+    if (half == 0) {
+#pragma unroll
+      for (int e = 0; e < L; ++e) part[(wave * HP + r) * D + sub * L + e] = acc[r][e];
+    }
   }
   __syncthreads();
-  float tot = 0.f, o = 0.f;
+  for (int i = tid; i < HP * D; i += NT) {
+    const int r = i / D, dd = i - r * D;
+    float tot = 0.f, o = 0.f;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    tot += red[w];
-    if (tid < D) o += part[w * D + tid];
-  }
-  sum = tot;
-  if (gridDim.z == 1) {
-    const float inv = sum > 0.f ? 1.f / sum : 0.f;
-    if (tid < D) out[qh * D + tid] = o * inv;
-  } else {
-    // partial of this split: {running maximum, probability sum, D unnormalized sums}
-    float* pp = partials + (qh * gridDim.z + split) * (D + 2);
-    if (tid == 0) {
-      pp[0] = mrun;
-      pp[1] = sum;
+    for (int w = 0; w < NW; ++w) {
+      tot += red[r][w];
+      o += part[(w * HP + r) * D + dd];
     }
-    if (tid < D) pp[2 + tid] = o;
+    const size_t qh = qh0 + r;
+    if (gridDim.z == 1) {
+      out[qh * D + dd] = tot > 0.f ? o / tot : 0.f;
+    } else {
+      // partial of this split: {running maximum, probability sum, D unnormalized sums}
+      float* pp = partials + (qh * gridDim.z + split) * (D + 2);
+      if (dd == 0) {
+        float mr = mrun[0];                          // (constant indices keep mrun in registers)
+#pragma unroll
+        for (int rr = 1; rr < HP; ++rr)
+          if (r == rr) mr = mrun[rr];
+        pp[0] = mr;
+        pp[1] = tot;
+      }
+      pp[2 + dd] = o;
+    }
   }
 }
 
@@ -398,16 +431,21 @@ hipError_t launch_pq_attn(int D, const uint16_t* q, const uint8_t* kcodes, const
   const int ns = pq_attn_splits(batch, n_q_heads, n_tok);
   const int nt = pq_attn_threads(D / kPqSub);
   const int64_t per = ns > 1 ? ((n_tok + ns - 1) / ns + nt - 1) / nt * nt : (n_tok > 0 ? n_tok : 1);
-  const dim3 grid(n_q_heads, batch, ns);
   const int n_rep = n_q_heads / n_kv_heads;
   const float scale = 1.0f / sqrtf((float)D);
   float* part = reinterpret_cast<float*>(ws);
-  if (D == 128)
-    hipLaunchKernelGGL(k_pq_attn<4>, grid, dim3(nt), 0, st, q, kcodes, vcodes, kcb, vcb, out, part, n_q_heads, n_rep,
-                       n_tok, per, scale);
+  // at d 128 with many (sequence, query head) pairs, two query heads of one KV
+  // head share a workgroup (and its value gathers); with few, one head per
+  // workgroup keeps more workgroups busy
+  if (D == 128 && n_rep % 2 == 0 && (int64_t)batch * n_q_heads >= 512)
+    hipLaunchKernelGGL((k_pq_attn<4, 2>), dim3(n_q_heads / 2, batch, ns), dim3(nt), 0, st, q, kcodes, vcodes, kcb, vcb,
+                       out, part, n_q_heads, n_rep, n_tok, per, scale);
+  else if (D == 128)
+    hipLaunchKernelGGL((k_pq_attn<4, 1>), dim3(n_q_heads, batch, ns), dim3(nt), 0, st, q, kcodes, vcodes, kcb, vcb, out,
+                       part, n_q_heads, n_rep, n_tok, per, scale);
   else
-    hipLaunchKernelGGL(k_pq_attn<2>, grid, dim3(nt), 0, st, q, kcodes, vcodes, kcb, vcb, out, part, n_q_heads, n_rep,
-                       n_tok, per, scale);
+    hipLaunchKernelGGL((k_pq_attn<2, 1>), dim3(n_q_heads, batch, ns), dim3(nt), 0, st, q, kcodes, vcodes, kcb, vcb, out,
+                       part, n_q_heads, n_rep, n_tok, per, scale);
   if (ns > 1) {
     const dim3 mgrid(n_q_heads, batch);
     if (D == 128) hipLaunchKernelGGL(k_pq_attn_merge<128>, mgrid, dim3(128), 0, st, part, ns, out);
