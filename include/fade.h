@@ -18,8 +18,11 @@
  *     FADE_ERR_HIP. Calls keep no global state and are thread-safe for
  *     distinct buffers.
  *   - Alignment: fp16 tiers, packed codes, queries, outputs, prefill
- *     tensors and workspaces must be 16-byte aligned; scales 2-byte, lens,
- *     scores and tok_attn 4-byte aligned.
+ *     tensors and workspaces must be 16-byte aligned; the middle tier's
+ *     scale arrays 8-byte aligned at head_dim 128 and 4-byte at 64 (a row's
+ *     scales are read as one vector); lens, scores, tok_attn and
+ *     kept_slots_out 4-byte aligned. A misaligned pointer is
+ *     FADE_ERR_INVALID_ARG.
  */
 #ifndef FADE_H
 #define FADE_H
@@ -181,7 +184,7 @@ typedef struct fade_layer_cache {
 /* Human-readable name of a status code; never NULL. */
 const char* fade_status_string(int status);
 
-/* ABI version of this header (major * 100 + minor). */
+/* ABI version of this header (major * 100 + minor): 200. */
 int fade_abi_version(void);
 
 /*
@@ -207,7 +210,10 @@ int fade_quantize_pack(const fade_config* cfg, const void* src, int64_t n_rows,
  * Append the newest token of every sequence: k_new / v_new are fp16
  * [batch, Hkv, head_dim] (k_new already rotated by the caller at position
  * = current cache length). The token fills the sink tier while it has fewer
- * than n_sink tokens, else the recent ring. Calling it while the ring holds
+ * than n_sink tokens, else the recent ring. When cache->scores is set, the
+ * new slot's score (position = the length before the append) is set to 0:
+ * a token starts with no accumulated attention (Transformer series (25),
+ * 1.3.1 H2O) and an empty EMA history. Calling it while the ring holds
  * recent_window + 1 tokens (no demotion since the last append) leaves that
  * sequence unchanged.
  */
@@ -272,6 +278,7 @@ int fade_h2o_scores(const fade_config* cfg, int32_t mode, fade_layer_cache* cach
  * delta in float64, rounded once to fp16, and (middle tier) requantized;
  * values move bit-for-bit; unmoved slots are untouched; scores move with
  * their slots.
+ * The compacted scores are cache->scores itself (compacted in place).
  *   max_evict  upper bound on M - int4_budget for this call (sizes the
  *              rotation table); 0 means cap_mid - int4_budget. Sequences
  *              whose M - int4_budget exceeds it are left as they are. A
@@ -279,10 +286,18 @@ int fade_h2o_scores(const fade_config* cfg, int32_t mode, fade_layer_cache* cach
  *              cap_mid = int4_budget + 1 gets it by default) or of at most 8
  *              with FADE_POLICY_POSITION lets the compaction run as one
  *              launch without a spill copy.
- *   workspace  >= fade_workspace_bytes(cfg, FADE_WS_EVICT, batch, cap_mid)
+ *   kept_slots_out  optional int32 [shared ? 1 : batch, cap_T]: entry j is
+ *              the slot position, before the event, of the token that holds
+ *              slot j after it, for j below the new live length; -1 from
+ *              there on. A row without an event gets the identity. NULL:
+ *              not written.
+ *   workspace  >= fade_workspace_bytes(cfg, FADE_WS_EVICT, batch, cap_mid);
+ *              unused (may be NULL) when int4_budget is -1 or cap_mid does
+ *              not exceed int4_budget
  */
 int fade_evict_rerope(const fade_config* cfg, fade_layer_cache* cache, int32_t policy,
-                      int32_t max_evict, void* workspace, size_t ws_bytes, void* stream);
+                      int32_t max_evict, int32_t* kept_slots_out, void* workspace, size_t ws_bytes,
+                      void* stream);
 
 /*
  * Build the tiers of an empty cache from a prefill of L tokens (k_prefill,

@@ -32,7 +32,7 @@ def test_library_exports_every_header_function():
 
 def test_status_strings_and_version():
     lib = fade.lib()
-    assert lib.fade_abi_version() == 100
+    assert lib.fade_abi_version() == 200
     for s in range(6):
         assert lib.fade_status_string(s)
     assert lib.fade_status_string(99) == b"unknown status"
@@ -95,6 +95,19 @@ def test_validation_rejects_before_launch():
     # misaligned pointer
     c = fade.LayerCache(1, 10, 4 + 10 + 65, 0, 17, 16, 16, 16, 16, 16, 16, None)
     assert lib.fade_cache_demote(ctypes.byref(cfg), ctypes.byref(c), null) == fade.FADE_ERR_INVALID_ARG
+    # scale arrays read as one vector per row: 8-byte alignment at head_dim 128
+    for addr in (18, 20):
+        c = fade.LayerCache(1, 4096, 4 + 4096 + 65, 0, 16, 16, 16, 16, addr, 16, 16, None)
+        assert lib.fade_cache_demote(ctypes.byref(cfg), ctypes.byref(c), null) == fade.FADE_ERR_INVALID_ARG
+        c = fade.LayerCache(1, 4096, 4 + 4096 + 65, 0, 16, 16, 16, 16, 16, addr, 16, None)
+        assert lib.fade_cache_demote(ctypes.byref(cfg), ctypes.byref(c), null) == fade.FADE_ERR_INVALID_ARG
+    # ... and 4-byte at head_dim 64: address 20 passes the alignment check and
+    # the call stops at the capacity check after it
+    cfg64 = _cfg(head_dim=64)
+    c = fade.LayerCache(1, 10, 4 + 10 + 65, 0, 16, 16, 16, 16, 20, 20, 16, None)
+    assert lib.fade_cache_demote(ctypes.byref(cfg64), ctypes.byref(c), null) == fade.FADE_ERR_CAPACITY
+    c = fade.LayerCache(1, 10, 4 + 10 + 65, 0, 16, 16, 16, 16, 18, 16, 16, None)
+    assert lib.fade_cache_demote(ctypes.byref(cfg64), ctypes.byref(c), null) == fade.FADE_ERR_INVALID_ARG
     # budget above capacity
     c = fade.LayerCache(1, 10, 4 + 10 + 65, 0, 16, 16, 16, 16, 16, 16, 16, None)
     assert lib.fade_cache_demote(ctypes.byref(cfg), ctypes.byref(c), null) == fade.FADE_ERR_CAPACITY
@@ -104,8 +117,15 @@ def test_validation_rejects_before_launch():
                                      ctypes.c_void_p(16), null, null, 0, null)
     assert st == fade.FADE_ERR_WORKSPACE
     # score policy without a score array
-    st = lib.fade_evict_rerope(ctypes.byref(cfg), ctypes.byref(c), fade.POLICY_SCORE, 0, null, 0, null)
+    st = lib.fade_evict_rerope(ctypes.byref(cfg), ctypes.byref(c), fade.POLICY_SCORE, 0, null, null, 0, null)
     assert st == fade.FADE_ERR_INVALID_ARG
+    # misaligned kept-slot output
+    st = lib.fade_evict_rerope(ctypes.byref(cfg), ctypes.byref(c), fade.POLICY_POSITION, 0, ctypes.c_void_p(18),
+                               null, 0, null)
+    assert st == fade.FADE_ERR_INVALID_ARG
+    # an event that needs a workspace, without one
+    st = lib.fade_evict_rerope(ctypes.byref(cfg), ctypes.byref(c), fade.POLICY_POSITION, 0, null, null, 0, null)
+    assert st == fade.FADE_ERR_WORKSPACE
 
 
 def test_rope_scheme_validation():

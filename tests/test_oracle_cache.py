@@ -218,3 +218,88 @@ def test_no_rotary_keys_move_like_values():
         assert np.array_equal(np.delete(full_u, e, axis=1), c.mid_k_u)
         assert np.array_equal(np.delete(full_s, e, axis=1), c.mid_k_s)
         assert np.array_equal(c.rec_k[:, -1], kn)
+
+
+def test_decode_eviction_rerotates_recent_ring_to_new_slots():
+    """After every decode-time eviction, each recent-ring key equals its raw
+    key rotated at the slot it now holds (the in-cache StreamingLLM position,
+    Transformer series (25) 1.2.2), up to the fp16 roundings it went through:
+    one when stored and one per re-rotation, each at most 2^-11 of the
+    pair's norm per component (rotations keep the norm). A wrong shift of
+    even one position turns the first pair by about 1 radian."""
+    cfg = _cfg(n_q_heads=4, n_kv_heads=2, int4_budget=12, recent_window=6, middle_v_bits=2)
+    L, W, half = 40, 6, 32
+    k_raw, k16, v16 = _prefill(cfg, L, 41)
+    scores = synth.normal(synth.rng(42), L) ** 2
+    c = oc.build_from_prefill(cfg, k16, v16, scores)
+    f = cfg.freqs()
+    # ring entries oldest first: raw key and fp16 roundings so far (stored at
+    # its prefill position, then re-rotated once by the prefill compaction)
+    ring = [(k_raw[:, j], 2) for j in range(L - W, L)]
+    gen = synth.rng(43)
+
+    def check():
+        S, M = c.n_sink_live, c.mid_len
+        assert c.rec_len == len(ring)
+        for i, (raw, n_round) in enumerate(ring):
+            want = rope.rotate(raw[:, None], np.full((2, 1), S + M + i), f)[:, 0]
+            norm = np.hypot(want[:, :half], want[:, half:])
+            tol = n_round * (2 ** 0.5 * 2.0 ** -11 * np.concatenate([norm, norm], axis=1) + 2.0 ** -24)
+            assert np.all(np.abs(c.rec_k[:, i].astype(np.float64) - want) <= tol), (i, S + M + i)
+
+    check()
+    for step in range(8):
+        t = c.length
+        raw_new = synth.normal(gen, 2, 64)
+        kn = rope.rotate(raw_new, np.full(2, t), f).astype(np.float16)
+        vn = synth.normal(gen, 2, 64).astype(np.float16)
+        q = rope.rotate(synth.normal(gen, 1, 4, 64), np.full((1, 4), t), f).astype(np.float16)
+        _, _, ev = oc.decode_step([c], q, kn[None], vn[None], mode="accum")
+        assert ev[0].size == 1
+        ring.append((raw_new, 1))
+        ring.pop(0)                                   # demoted into the middle tier
+        ring = [(raw, n + 1) for raw, n in ring]      # the eviction re-rotated the whole ring
+        check()
+        assert np.array_equal(c.sink_k, k16[:, :4])   # sinks never move
+
+
+def test_update_scores_shared_rows_hand_summed():
+    """Shared-batch rows (FADE post, "批处理支持": rows share tier decisions)
+    receive the sum of every row's side output; per-row mode keeps rows
+    apart. Values chosen so every result is exact in binary."""
+    from types import SimpleNamespace
+
+    def rows():
+        return [SimpleNamespace(scores=np.array([1.0, 2.0, 3.0])) for _ in range(2)]
+
+    a1, a2 = np.array([0.5, 0.25, 0.125]), np.array([0.25, 0.5, 1.0])
+    r = rows()
+    oc.update_scores(r, [a1, a2], "accum", shared=True)
+    assert all(x.scores.tolist() == [1.75, 2.75, 4.125] for x in r)
+    r = rows()
+    oc.update_scores(r, [a1, a2], "ema", beta=0.5, shared=True)
+    assert all(x.scores.tolist() == [0.875, 1.375, 2.0625] for x in r)
+    r = rows()
+    oc.update_scores(r, [a1, a2], "accum", shared=False)
+    assert r[0].scores.tolist() == [1.5, 2.25, 3.125] and r[1].scores.tolist() == [1.25, 2.5, 4.0]
+    r = rows()
+    oc.update_scores(r, [a1, a2], "ema", beta=0.75, shared=False)
+    assert r[0].scores.tolist() == [0.875, 1.5625, 2.28125]
+
+
+def test_appended_slot_score_starts_at_zero_after_eviction():
+    """A token appended after an eviction starts with score 0 whatever the
+    evicted slots held (the shifted score row does not leak into it)."""
+    cfg = _cfg(n_q_heads=4, n_kv_heads=2, int4_budget=12, recent_window=6)
+    k_raw, k16, v16 = _prefill(cfg, 40, 44)
+    c = oc.build_from_prefill(cfg, k16, v16, 1.0 + synth.normal(synth.rng(45), 40) ** 2)
+    f = cfg.freqs()
+    gen = synth.rng(46)
+    for _ in range(3):
+        t = c.length
+        kn = rope.rotate(synth.normal(gen, 2, 64), np.full(2, t), f).astype(np.float16)
+        vn = synth.normal(gen, 2, 64).astype(np.float16)
+        oc.append(c, kn, vn)
+        assert c.scores.size == t + 1 and c.scores[-1] == 0.0
+        oc.demote(c)
+        assert oc.evict(c, cfg.int4_budget).size == 1

@@ -77,7 +77,10 @@ int check_cache(const fade_config* c, const fade_layer_cache* k) {
   if (k->cap_mid > 0) {
     if (!k->mid_k_codes || !k->mid_v_codes || !aligned16(k->mid_k_codes) || !aligned16(k->mid_v_codes))
       return FADE_ERR_INVALID_ARG;
-    if (!k->mid_k_scales || !k->mid_v_scales || !aligned(k->mid_k_scales, 2) || !aligned(k->mid_v_scales, 2))
+    // the kernels read a row's scales as one vector: 8 bytes at head_dim 128,
+    // 4 bytes at 64
+    const uintptr_t sa = c->head_dim == 128 ? 8 : 4;
+    if (!k->mid_k_scales || !k->mid_v_scales || !aligned(k->mid_k_scales, sa) || !aligned(k->mid_v_scales, sa))
       return FADE_ERR_INVALID_ARG;
   }
   if (k->scores && !aligned(k->scores, 4)) return FADE_ERR_INVALID_ARG;
@@ -160,7 +163,7 @@ const char* fade_status_string(int status) {
   }
 }
 
-int fade_abi_version(void) { return 100; }
+int fade_abi_version(void) { return 200; }
 
 int fade_quantize_pack(const fade_config* cfg, const void* src, int64_t n_rows, int64_t src_row_stride,
                        const int32_t* src_row_idx, const int32_t* dst_row_idx, int32_t bits, void* codes,
@@ -236,18 +239,23 @@ int fade_h2o_scores(const fade_config* cfg, int32_t mode, fade_layer_cache* cach
 }
 
 int fade_evict_rerope(const fade_config* cfg, fade_layer_cache* cache, int32_t policy, int32_t max_evict,
-                      void* workspace, size_t ws_bytes, void* stream) {
+                      int32_t* kept_slots_out, void* workspace, size_t ws_bytes, void* stream) {
   int st = check_cfg(cfg);
   if (st) return st;
   if ((st = check_cache(cfg, cache))) return st;
   if (policy != FADE_POLICY_SCORE && policy != FADE_POLICY_POSITION) return FADE_ERR_INVALID_ARG;
   if (policy == FADE_POLICY_SCORE && !cache->scores) return FADE_ERR_INVALID_ARG;
-  if (cfg->int4_budget < 0) return FADE_OK;     // never evict
-  const int me = decode_max_evict(cfg, cache, max_evict);
-  if (me == 0) return FADE_OK;
+  if (kept_slots_out && !aligned(kept_slots_out, 4)) return FADE_ERR_INVALID_ARG;
+  // No event can run (never evict, or no middle slot over the budget fits
+  // the capacity): every survivor keeps its slot.
+  const int me = cfg->int4_budget < 0 ? 0 : decode_max_evict(cfg, cache, max_evict);
   const Shape s = make_shape(cfg, cache->batch, cache->cap_mid, cache->cap_T, cache->shared);
+  if (me == 0) {
+    if (!kept_slots_out) return FADE_OK;
+    return hip_status(launch_kept_identity(s, *cache, kept_slots_out, reinterpret_cast<hipStream_t>(stream)));
+  }
   if (!workspace || !aligned16(workspace) || ws_bytes < evict_ws_bytes(s, me)) return FADE_ERR_WORKSPACE;
-  return hip_status(launch_evict(s, *cache, policy, me, host_freqs(cfg), workspace,
+  return hip_status(launch_evict(s, *cache, policy, me, host_freqs(cfg), kept_slots_out, workspace,
                                  reinterpret_cast<hipStream_t>(stream)));
 }
 

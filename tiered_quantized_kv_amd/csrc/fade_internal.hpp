@@ -55,7 +55,8 @@ hipError_t launch_h2o_prefill(int D, int Hq, int Hkv, int batch, int L, int shar
 // ---- eviction, compaction, prefill build, RoPE (k_evict.hip) ----------------
 size_t evict_ws_bytes(const Shape& s, int max_evict);
 hipError_t launch_evict(const Shape& s, const fade_layer_cache& c, int policy, int max_evict,
-                        const RopeFreqs& fr, void* ws, hipStream_t st);
+                        const RopeFreqs& fr, int32_t* kept_slots, void* ws, hipStream_t st);
+hipError_t launch_kept_identity(const Shape& s, const fade_layer_cache& c, int32_t* kept, hipStream_t st);
 size_t prefill_build_ws_bytes(const Shape& s, int L);
 hipError_t launch_prefill_build(const Shape& s, const fade_layer_cache& c, const uint16_t* k,
                                 const uint16_t* v, int L, const float* scores,

@@ -891,6 +891,55 @@ size_t evict_ws_bytes(const Shape& s, int max_evict) {
   return n;
 }
 
+// Old slot position of every survivor, in its new slot order: kept[row][j] for
+// j below the new live length S + (M - n_ev) + R, -1 past it. Sinks and
+// the middle slots before the first evicted one keep their slots; the ring
+// entries move down by n_ev. A map event scatters its middle survivors
+// (map[r] = new middle index); a run event [e, e + n_ev) and an event that
+// was skipped (n_ev = 0, the identity) are gathered in closed form.
+__global__ __launch_bounds__(256) void k_kept_slots(const int32_t* __restrict__ info,
+                                                    const int32_t* __restrict__ map, int map_stride,
+                                                    int cap_T, int32_t* __restrict__ kept) {
+  const int row = blockIdx.y;
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  const int4 i0 = *reinterpret_cast<const int4*>(info + kInfo * row);
+  const int4 i1 = *reinterpret_cast<const int4*>(info + kInfo * row + 4);
+  const int M = i0.x, n_ev = i0.y, S = i0.z, R = i0.w, e = i1.x;
+  const bool by_map = n_ev > 0 && i1.y == 0;
+  const int M2 = M - n_ev, T2 = S + M2 + R;
+  int32_t* out = kept + (size_t)row * cap_T;
+  if (j >= cap_T) return;
+  if (by_map && j < M) {
+    const int d = map[(size_t)row * map_stride + j];
+    if (d >= 0) out[S + d] = S + j;
+  }
+  int v;
+  if (j >= T2) v = -1;
+  else if (j < S) v = j;
+  else if (j >= S + M2) v = j + n_ev;
+  else if (by_map) return;                      // written by the scatter above
+  else v = (n_ev == 0 || j - S < e) ? j : j + n_ev;
+  out[j] = v;
+}
+
+// Kept slots when no event can run: the identity over each row's live length.
+__global__ __launch_bounds__(256) void k_kept_identity(const int32_t* __restrict__ lens, int n_sink, int ring,
+                                                       int cap_mid, int cap_T, int32_t* __restrict__ kept) {
+  const int row = blockIdx.y;
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= cap_T) return;
+  const int32_t* L = lens + 4 * row;
+  const int T = min(max(L[0], 0), n_sink) + min(max(L[1], 0), cap_mid) + min(max(L[2], 0), ring);
+  kept[(size_t)row * cap_T + j] = j < T ? j : -1;
+}
+
+hipError_t launch_kept_identity(const Shape& s, const fade_layer_cache& c, int32_t* kept, hipStream_t st) {
+  const int rows = s.shared ? 1 : s.batch;
+  hipLaunchKernelGGL(k_kept_identity, dim3((s.cap_T + 255) / 256, rows), dim3(256), 0, st, c.lens, s.n_sink,
+                     s.ring, s.cap_mid, s.cap_T, kept);
+  return hipGetLastError();
+}
+
 template <int D, int KB, int VB>
 static void launch_compact_t(const CompactArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((k_compact<D, KB, VB>), dim3(a.nchunks + ring_blocks(a.s.ring, D), a.s.Hkv, a.s.batch),
@@ -909,7 +958,7 @@ static void launch_compact_d(const CompactArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_evict(const Shape& s, const fade_layer_cache& c, int policy, int max_evict,
-                        const RopeFreqs& fr, void* ws, hipStream_t st) {
+                        const RopeFreqs& fr, int32_t* kept_slots, void* ws, hipStream_t st) {
   const int rows = s.shared ? 1 : s.batch;
   const int nchunks = (s.cap_mid + kCompactRows - 1) / kCompactRows;
   const int spill_rows = max_evict < kCompactRows ? max_evict : kCompactRows;
@@ -985,6 +1034,10 @@ hipError_t launch_evict(const Shape& s, const fade_layer_cache& c, int policy, i
   ca.halo = halo ? 1 : 0;
   if (s.D == 128) launch_compact_d<128>(ca, st);
   else launch_compact_d<64>(ca, st);
+  e = hipGetLastError();
+  if (e != hipSuccess || !kept_slots) return e;
+  hipLaunchKernelGGL(k_kept_slots, dim3((s.cap_T + 255) / 256, rows), dim3(256), 0, st, info, map, s.cap_mid,
+                     s.cap_T, kept_slots);
   return hipGetLastError();
 }
 

@@ -76,13 +76,19 @@ hipError_t launch_quantize_rows(int D, int bits, const uint16_t* src, int64_t n_
   return hipGetLastError();
 }
 
-// Append the newest token of sequence blockIdx.x (all KV heads).
+// Append the newest token of sequence blockIdx.x (all KV heads). A new slot's
+// score starts at 0 (the cumulative H2O score of a token that has not been
+// attended yet, Transformer series (25) 1.3.1; the EMA of an empty history),
+// so the score entry at its position S + M + R is cleared here: an eviction
+// shifts the score row down and leaves the entries past the live length
+// holding old values.
 __global__ __launch_bounds__(256) void k_append(Shape s, fade_layer_cache c,
                                                 const uint16_t* __restrict__ k_new,
                                                 const uint16_t* __restrict__ v_new) {
   const int b = blockIdx.x;
   int32_t* L = c.lens + 4 * b;
   const int S = min(max(L[0], 0), s.n_sink), R = min(max(L[2], 0), s.ring);
+  const int M = min(max(L[1], 0), s.cap_mid);
   const int head = min(max(L[3], 0), s.ring - 1);
   int slot;
   bool to_sink = false;
@@ -107,6 +113,11 @@ __global__ __launch_bounds__(256) void k_append(Shape s, fade_layer_cache c,
     fk[dst] = kn[srcx];
     fv[dst] = vn[srcx];
   }
+  // A shared cache has one score row and identical lengths in every row:
+  // sequence 0 clears it.
+  const int pos = S + M + R;
+  if (threadIdx.x == 0 && c.scores && (!c.shared || b == 0) && pos < s.cap_T)
+    c.scores[(size_t)(c.shared ? 0 : b) * s.cap_T + pos] = 0.f;
   __syncthreads();
   if (threadIdx.x == 0) {
     if (to_sink) L[0] = S + 1;

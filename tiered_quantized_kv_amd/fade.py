@@ -65,7 +65,8 @@ _SIGS = {
     "fade_tiered_decode_attn": (ctypes.c_int, [_CFG, _CACHE, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "fade_h2o_scores": (ctypes.c_int, [_CFG, ctypes.c_int32, _CACHE, _P, _P, ctypes.c_int32, ctypes.c_int32,
                                        ctypes.c_int32, _P, _P, ctypes.c_float, _P, ctypes.c_size_t, _P]),
-    "fade_evict_rerope": (ctypes.c_int, [_CFG, _CACHE, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_size_t, _P]),
+    "fade_evict_rerope": (ctypes.c_int, [_CFG, _CACHE, ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_size_t,
+                                         _P]),
     "fade_prefill_build": (ctypes.c_int, [_CFG, _CACHE, _P, _P, ctypes.c_int32, _P, _P, ctypes.c_size_t, _P]),
     "fade_rope_rotate": (ctypes.c_int, [_CFG, _P, ctypes.c_int32, ctypes.c_int64, _P, ctypes.c_int32,
                                         ctypes.c_int32, _P]),
@@ -216,9 +217,11 @@ def fade_h2o_scores(cfg, mode, cache=None, q_prefill=None, k_prefill=None, batch
            "fade_h2o_scores")
 
 
-def fade_evict_rerope(cfg, cache, policy, ws, max_evict=0, stream=None):
-    _check(lib().fade_evict_rerope(ctypes.byref(cfg), cache.ref(), policy, max_evict, _p(ws), ws.numel(),
-                                   _s(stream)), "fade_evict_rerope")
+def fade_evict_rerope(cfg, cache, policy, ws, max_evict=0, stream=None, kept_slots=None):
+    """kept_slots: optional int32 [rows, cap_T] device tensor for the old slot
+    of every survivor (see include/fade.h)."""
+    _check(lib().fade_evict_rerope(ctypes.byref(cfg), cache.ref(), policy, max_evict, _p(kept_slots), _p(ws),
+                                   0 if ws is None else ws.numel(), _s(stream)), "fade_evict_rerope")
     tel = getattr(cache, "telemetry", None)
     if tel is not None:
         (stream or torch.cuda.current_stream()).synchronize()
