@@ -117,3 +117,170 @@ def out_close(gpu, ref, tol=2e-3, out_dtype="f32"):
     err = np.abs(gpu - ref)
     bound = tol + (tol + STORE_HALF_ULP[out_dtype]) * np.abs(ref)
     return bool(np.all(err <= bound)), float((err / bound).max())
+
+
+# ---- re-rotation where the oracle is not exact ---------------------------------
+# The oracle un-rotates at the old position and re-rotates at the new one in
+# float64, with angles up to |p| * f_0; its value is good to about |p| * 2^-52
+# of the pair's norm, the kernels' (one rotation by the shift) to about
+# 2^-52. Where the exact value lies that close to the midpoint between two
+# fp16 numbers, both roundings are correct. AMBIG bounds that band (relative
+# to the pair's norm) with a wide margin up to |p| ~ 1e6.
+AMBIG = 1e-9
+
+
+def rerope_choices(x, old_pos, new_pos, ocfg_):
+    """The oracle's fp16 re-rotation y16 of exact key values x [Hkv, n, d]
+    from old_pos to new_pos [n], the other fp16 neighbour nb of each
+    element's float64 value, and the mask of elements whose float64 value
+    lies within AMBIG (of its pair's norm) of the midpoint between them."""
+    f, il = ocfg_.freqs(), ocfg_.rope_interleaved
+    y = rope.rotate(rope.unrotate(np.asarray(x, np.float64), old_pos, f, il), new_pos, f, il)
+    y16 = y.astype(np.float16)
+    yd = y16.astype(np.float64)
+    up = np.nextafter(y16, np.float16(np.inf))
+    dn = np.nextafter(y16, np.float16(-np.inf))
+    nb = np.where(y > yd, up, dn)
+    mid = 0.5 * (yd + nb.astype(np.float64))
+    half = y.shape[-1] // 2
+    if il:
+        n = np.hypot(y[..., 0::2], y[..., 1::2])
+        norm = np.repeat(n, 2, axis=-1)
+    else:
+        n = np.hypot(y[..., :half], y[..., half:])
+        norm = np.concatenate([n, n], axis=-1)
+    return y16, nb, np.abs(y - mid) <= AMBIG * norm
+
+
+def adopt_fp16_rerope(gpu, ref, choice):
+    """FP16-tier keys after a re-rotation: each GPU value equals the
+    oracle's, or its other neighbour where the rounding is ambiguous.
+    Returns the GPU's values (every one a correct rounding) for the oracle
+    state to follow."""
+    y16, nb, amb = choice
+    g, r = bits16(gpu), bits16(ref)
+    assert np.array_equal(r, bits16(y16))
+    ok = (g == r) | (amb & (g == bits16(nb)))
+    assert np.all(ok), np.argwhere(~ok)[:4]
+    return np.array(gpu, dtype=np.float16)
+
+
+def adopt_group_rerope(gpu_packed, gpu_scales, ref_u, ref_s, choice, bits, group=32):
+    """Requantized middle keys after a re-rotation: a (row, group) whose GPU
+    codes or scale differ from the oracle's must hold an ambiguous element,
+    and equal the quantization of the oracle's fp16 values with some of those
+    elements taken at their other neighbour. Returns the GPU's (codes,
+    scales) for the oracle state to follow."""
+    y16, nb, amb = choice
+    d = ref_u.shape[-1]
+    gu = quant.unpack(gpu_packed, bits, d)
+    gs = np.asarray(gpu_scales, np.float16)
+    ng = d // group
+    du = (gu != ref_u).reshape(gu.shape[:-1] + (ng, group)).any(-1)
+    ds = bits16(gs) != bits16(ref_s)
+    for h, i, g in np.argwhere(du | ds):
+        sl = slice(g * group, (g + 1) * group)
+        idx = np.nonzero(amb[h, i, sl])[0]
+        assert 0 < idx.size <= 8, (h, i, g, idx.size)
+        found = False
+        for mask in range(1, 1 << idx.size):
+            z = y16[h, i, sl].copy()
+            for k, j in enumerate(idx):
+                if (mask >> k) & 1:
+                    z[j] = nb[h, i, g * group + j]
+            u, s = quant.quantize(z[None], bits, group)
+            if np.array_equal(u[0], gu[h, i, sl]) and bits16(s)[0, 0] == bits16(gs[h, i, g:g + 1])[0]:
+                found = True
+                break
+        assert found, (h, i, g)
+    return gu, gs
+
+
+def assert_scores_close(st, ref, rtol=2e-5, atol=1e-7):
+    """GPU float32 scores against the oracle's float64 ones: the side output is
+    within 1e-5 relative per step and the updates add float32 roundings."""
+    if "scores" in st and ref.scores is not None:
+        got = st["scores"].astype(np.float64)
+        assert got.shape == ref.scores.shape
+        assert np.allclose(got, ref.scores, rtol=rtol, atol=atol), float(np.abs(got - ref.scores).max())
+
+
+NEAR = 1e-5          # near-tie band of an eviction cutoff, relative
+
+
+def follow_eviction(r, kept_row, policy):
+    """Check the GPU's kept-slot list against the oracle's selection (near
+    ties aside), then run the oracle's eviction on the GPU's set. Returns
+    (followed a near tie, re-rotation choices of the moved middle rows and
+    of the ring, computed from the state before the event)."""
+    c = r.cfg
+    S, M, R = r.n_sink_live, r.mid_len, r.rec_len
+    n_ev = M - c.int4_budget if 0 <= c.int4_budget < M else 0
+    T2 = S + M - n_ev + R
+    kr = kept_row[:T2]
+    assert np.all(kept_row[T2:] == -1)
+    assert np.array_equal(kr[:S], np.arange(S))
+    assert np.array_equal(kr[S + M - n_ev:], S + M + np.arange(R))
+    mid_kept = kr[S:S + M - n_ev] - S
+    assert np.all(np.diff(mid_kept) > 0) and (mid_kept.size == 0 or (mid_kept[0] >= 0 and mid_kept[-1] < M))
+    if n_ev == 0:
+        return False, None, None
+    gpu_ev = np.setdiff1d(np.arange(M), mid_kept)
+    sc = np.arange(M, dtype=np.float64) if policy == "position" else r.scores[S:S + M]
+    own = oc.select_evicted(sc, n_ev)
+    forced = None
+    if not np.array_equal(gpu_ev, own):
+        assert policy == "score", (gpu_ev[:8], own[:8])
+        cut = np.sort(sc)[n_ev - 1]
+        band = np.abs(sc - cut) <= NEAR * abs(cut)
+        assert np.all(np.isin(np.nonzero((sc < cut) & ~band)[0], gpu_ev)), "GPU kept a slot clearly below the cutoff"
+        assert not np.any(np.isin(np.nonzero((sc > cut) & ~band)[0], gpu_ev)), "GPU evicted a slot clearly above"
+        forced = gpu_ev
+    old = S + mid_kept
+    new = S + np.arange(mid_kept.size)
+    moved = old != new
+    rotates = c.freqs().any()
+    mid_choice = ring_choice = None
+    if rotates and moved.any():
+        khat = quant.dequantize(r.mid_k_u[:, mid_kept[moved]], r.mid_k_s[:, mid_kept[moved]], c.middle_k_bits)
+        mid_choice = (np.nonzero(moved)[0], rerope_choices(khat, old[moved], new[moved], c))
+    if rotates and R:
+        ring_choice = rerope_choices(r.rec_k, S + M + np.arange(R), S + M - n_ev + np.arange(R), c)
+    oc.evict(r, c.int4_budget, policy, evicted=forced)
+    return forced is not None, mid_choice, ring_choice
+
+
+def adopt_rerope(st, r, mid_choice, ring_choice):
+    """Follow the GPU where a re-rotation's fp16 rounding was ambiguous (see
+    the module docstring); everything else must already be identical."""
+    c = r.cfg
+    if ring_choice is not None:
+        r.rec_k = adopt_fp16_rerope(st["rec_k"], r.rec_k, ring_choice)
+    if mid_choice is not None:
+        rows, choice = mid_choice
+        gu, gs = adopt_group_rerope(st["mid_k"][:, rows], st["mid_ks"][:, rows], r.mid_k_u[:, rows],
+                                    r.mid_k_s[:, rows], choice, c.middle_k_bits)
+        r.mid_k_u[:, rows] = gu
+        r.mid_k_s[:, rows] = gs
+
+
+def build_rerope_choices(ocfg_, k16, scores=None):
+    """Re-rotation choices of a prefill build (fade_prefill_build), computed
+    the way oracle.cache.build_from_prefill moves its survivors: (new middle
+    rows that moved, choices) and the ring's choices, for adopt_rerope."""
+    c = ocfg_
+    hkv, L, d = k16.shape
+    s, m, r = oc.tier_layout(L, c.n_sink, c.recent_window)
+    sc = np.arange(m, dtype=np.float64) if scores is None else np.asarray(scores, np.float64)[s:s + m]
+    n_ev = m - c.int4_budget if 0 <= c.int4_budget < m else 0
+    kept = s + np.setdiff1d(np.arange(m), oc.select_evicted(sc, n_ev))
+    new = s + np.arange(kept.size)
+    moved = kept != new
+    if not c.freqs().any():
+        return None, None
+    mid = (np.nonzero(moved)[0], rerope_choices(k16[:, kept[moved]], kept[moved], new[moved], c)) if moved.any() \
+        else None
+    ring = None
+    if r and n_ev:
+        ring = rerope_choices(k16[:, L - r:], np.arange(L - r, L), kept.size + s + np.arange(r), c)
+    return mid, ring

@@ -10,7 +10,8 @@ from oracle import cache as oc
 from oracle import rope
 from tiered_quantized_kv_amd import fade, synth
 
-from .gpu_helpers import DEV, ROPE_KW, assert_state_equal, build_both, dev16, ocfg, seq_state
+from .gpu_helpers import (DEV, ROPE_KW, adopt_rerope, assert_state_equal, build_both, build_rerope_choices, dev16,
+                          ocfg, seq_state)
 
 pytestmark = pytest.mark.gpu
 
@@ -61,8 +62,10 @@ def test_prefill_build_long_shift_bf16_free():
     """A large compaction shift (prefill 20000 -> 260 slots): keys re-RoPE'd by
     about -19700 positions in float64 still match bit-for-bit."""
     cfg = _cfg(d=128, hq=8, hkv=2, n_sink=4, w=128, budget=128, kb=4, vb=2, rope_theta=5e5)
-    tc, refs, _ = build_both(cfg, 1, 20000, 213, cap_mid=130)
-    assert_state_equal(seq_state(tc, 0), refs[0])
+    tc, refs, (k16, _, _) = build_both(cfg, 1, 20000, 213, cap_mid=130)
+    st = seq_state(tc, 0)
+    adopt_rerope(st, refs[0], *build_rerope_choices(ocfg(cfg), k16[0]))
+    assert_state_equal(st, refs[0])
 
 
 def test_append_and_demote_sequence():

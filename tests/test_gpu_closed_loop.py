@@ -1,0 +1,196 @@
+"""Multi-step closed-loop GPU parity of the whole decode loop against the
+oracle, through the C ABI.
+
+Every step runs, on both sides: append the new token -> tiered decode
+attention (with the side output when a score policy needs it) -> ACCUM / EMA
+score update -> demotion -> eviction with re-RoPE compaction when due (FADE
+post, "驱逐策略", "四种驱逐策略详解": EMA; Transformer series (25), 1.3.1 H2O:
+cumulative scores). After every step the attention output (2e-3 bar), the
+side output (1e-5 relative), the whole tier state (bit for bit) and the
+scores (float32 on the GPU against float64) are compared.
+
+Where several results are correct the oracle follows the GPU, and only there:
+* the eviction set: slots whose oracle score lies clearly below the cutoff
+  (the budget-th lowest) must be evicted and those clearly above kept; inside
+  the near-tie band (1e-5 relative of the cutoff) the GPU's float32 scores may
+  order either way, and the oracle then evicts the GPU's set (read back
+  through kept_slots_out);
+* a re-rotated key whose exact float64 value lies within 1e-9 of an fp16
+  rounding midpoint (the oracle's two large-angle rotations are good to
+  ~|p| 2^-52 only): the GPU may take the other neighbour, and the requantized
+  group must then be the quantization of that choice; the oracle takes it.
+
+Shapes are the benchmark workloads' shapes, shrunk in length:
+* Qwen2.5-3B-like: n_rep 8, d 128, K4/V2, budget 400, H2O prefill column
+  sums (oracle-computed) then ACCUM, eviction every step, 32 steps;
+* Llama-3.2-1B-like: 4 sequences sharing tier decisions, 32/8 heads, d 64,
+  llama3 RoPE, K4/V4, H2O shared sums then ACCUM, eviction every 16 steps
+  (16 tokens each), 33 steps;
+* serving batch: 8 ragged sequences (some still below the budget, one still
+  filling its sinks), 32/8 heads, d 128, K4/V2, EMA 0.9, budget 256 with
+  cap_mid = budget + 1 (the one-slot halo compaction the bench runs), 32 steps;
+* Llama-3-8B-like: position policy, W 128, bf16 queries, 16 steps.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import cache as oc
+from oracle import h2o, rope
+from tiered_quantized_kv_amd import fade, synth
+
+from .gpu_helpers import (DEV, adopt_rerope, assert_scores_close, assert_state_equal, dev16, follow_eviction, ocfg,
+                          out_close, seq_state)
+
+pytestmark = pytest.mark.gpu
+
+
+def _cfg(d, hq, hkv, n_sink, w, budget, kb, vb, q_dtype="f16", **kw):
+    return fade.make_config(head_dim=d, n_q_heads=hq, n_kv_heads=hkv, n_sink=n_sink, recent_window=w,
+                            int4_budget=budget, middle_k_bits=kb, middle_v_bits=vb, q_dtype=q_dtype,
+                            out_dtype="f32", **kw)
+
+
+def _prefill(cfg, oc_cfg, L, seed, b):
+    f, il = oc_cfg.freqs(), oc_cfg.rope_interleaved
+    k_raw, v = synth.kv_raw(synth.rng(seed, b), cfg.n_kv_heads, L, cfg.head_dim)
+    k16 = rope.rotate(k_raw, np.arange(L), f, il).astype(np.float16)
+    q16 = rope.rotate(synth.normal(synth.rng(seed, 1000 + b), cfg.n_q_heads, L, cfg.head_dim),
+                      np.arange(L), f, il).astype(np.float16)
+    return k16, v.astype(np.float16), q16
+
+
+def _build(cfg, lengths, seed, cap_mid, score_kind, shared):
+    """Prefill build on both sides. score_kind: 'h2o' (the oracle's causal
+    column sums of the prefill, summed over rows when shared), 'ema' (small
+    random positive scores of earlier steps) or None (position policy)."""
+    oc_cfg = ocfg(cfg)
+    B = len(lengths)
+    tc = fade.TieredCache(cfg, B, cap_mid, shared=shared, with_scores=score_kind is not None)
+    pre = [_prefill(cfg, oc_cfg, L, seed, b) for b, L in enumerate(lengths)]
+    if score_kind == "h2o":
+        sc = [h2o.prefill_colsum(q16.astype(np.float64), k16.astype(np.float64)) for k16, _, q16 in pre]
+        if shared:
+            sc = [np.sum(sc, axis=0)]
+        sc = [s.astype(np.float32) for s in sc]
+    elif score_kind == "ema":
+        sc = [(0.01 * synth.normal(synth.rng(seed, 2000 + b), L) ** 2 + 1e-3).astype(np.float32)
+              for b, L in enumerate(lengths)]
+    else:
+        sc = None
+    if shared:
+        L = lengths[0]
+        assert all(x == L for x in lengths)
+        ws = fade.workspace(cfg, fade.WS_PREFILL_BUILD, B, L)
+        fade.fade_prefill_build(cfg, tc, dev16(np.stack([p[0] for p in pre])), dev16(np.stack([p[1] for p in pre])),
+                                L, None if sc is None else torch.from_numpy(sc[0][None]).to(DEV), ws)
+    else:
+        for b, L in enumerate(lengths):
+            ws = fade.workspace(cfg, fade.WS_PREFILL_BUILD, 1, L)
+            fade.fade_prefill_build(cfg, tc.seq_view(b), dev16(pre[b][0][None]), dev16(pre[b][1][None]), L,
+                                    None if sc is None else torch.from_numpy(sc[b][None]).to(DEV), ws)
+    refs = []
+    for b in range(B):
+        s = None if sc is None else sc[0 if shared else b].astype(np.float64)
+        refs.append(oc.build_from_prefill(oc_cfg, pre[b][0], pre[b][1], s))
+    torch.cuda.synchronize()
+    return tc, refs
+
+
+def _run_loop(cfg, lengths, steps, mode, policy, period, seed, cap_mid, score_kind, shared=False, decay=0.9):
+    tc, refs = _build(cfg, lengths, seed, cap_mid, score_kind, shared)
+    for b, r in enumerate(refs):
+        assert_state_equal(seq_state(tc, b), r, check_scores=False)
+        assert_scores_close(seq_state(tc, b), r, rtol=0, atol=0)
+    oc_cfg = ocfg(cfg)
+    f, il = oc_cfg.freqs(), oc_cfg.rope_interleaved
+    B, hq, hkv, d = len(lengths), cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    rows = 1 if shared else B
+    kept = torch.full((rows, tc.cap_T), -7, dtype=torch.int32, device=DEV)
+    ws_dec = fade.workspace(cfg, fade.WS_DECODE, B, cap_mid)
+    ws_ev = fade.workspace(cfg, fade.WS_EVICT, B, cap_mid)
+    side = mode != "none"
+    gen = synth.rng(seed, 999)
+    bf16 = cfg.q_dtype == fade.DTYPE_BF16
+    n_forced = n_events = 0
+    for step in range(steps):
+        T = [r.length for r in refs]
+        kn = np.stack([rope.rotate(synth.normal(gen, hkv, d), np.full(hkv, T[b]), f, il)
+                       for b in range(B)]).astype(np.float16)
+        vn = synth.normal(gen, B, hkv, d).astype(np.float16)
+        qf = np.stack([rope.rotate(synth.normal(gen, hq, d), np.full(hq, T[b]), f, il) for b in range(B)])
+        qt = torch.from_numpy(qf.astype(np.float32)).to(torch.bfloat16) if bf16 else torch.from_numpy(
+            qf.astype(np.float16))
+        q_exact = qt.float().numpy().astype(np.float64)
+
+        fade.fade_cache_append(cfg, tc, dev16(kn), dev16(vn))
+        out = torch.zeros(B, hq, d, dtype=torch.float32, device=DEV)
+        tok = torch.full((B, tc.cap_T), -1.0, dtype=torch.float32, device=DEV) if side else None
+        fade.fade_tiered_decode_attn(cfg, tc, qt.to(DEV), out, tok, ws_dec)
+        if side:
+            fade.fade_h2o_scores(cfg, fade.SCORE_ACCUM if mode == "accum" else fade.SCORE_EMA, cache=tc,
+                                 tok_attn=tok, decay=decay)
+        fade.fade_cache_demote(cfg, tc)
+        evict_now = (step + 1) % period == 0
+        if evict_now:
+            fade.fade_evict_rerope(cfg, tc, fade.POLICY_POSITION if policy == "position" else fade.POLICY_SCORE,
+                                   ws_ev, kept_slots=kept)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().astype(np.float64)
+        tokh = tok.cpu().numpy() if side else None
+
+        sides = []
+        for b, r in enumerate(refs):
+            oc.append(r, kn[b], vn[b])
+            o, _, a = oc.attend(r, q_exact[b])
+            ok, worst = out_close(got[b], o)
+            assert ok, (step, b, worst)
+            if side:
+                t1 = T[b] + 1
+                assert np.allclose(tokh[b, :t1], a, rtol=1e-5, atol=1e-8), (step, b)
+                assert np.all(tokh[b, t1:] == 0), (step, b)
+            sides.append(a)
+        oc.update_scores(refs, sides, mode, decay, shared)
+        for r in refs:
+            oc.demote(r)
+        choices = [(None, None)] * B
+        if evict_now:
+            kh = kept.cpu().numpy()
+            for b, r in enumerate(refs):
+                forced, mc, rc = follow_eviction(r, kh[0 if shared else b], policy)
+                n_forced += forced
+                n_events += mc is not None or rc is not None
+                choices[b] = (mc, rc)
+        for b, r in enumerate(refs):
+            st = seq_state(tc, b)
+            adopt_rerope(st, r, *choices[b])
+            assert_state_equal(st, r, check_scores=False)
+            assert_scores_close(st, r)
+    return n_forced, n_events
+
+
+def test_closed_loop_qwen_like_accum_every_step():
+    cfg = _cfg(128, 16, 2, 4, 64, 400, 4, 2, rope_theta=1e6)
+    nf, ne = _run_loop(cfg, [1200], 32, "accum", "score", 1, 4100, cap_mid=464, score_kind="h2o")
+    assert ne >= 32
+
+
+def test_closed_loop_llama32_like_shared_period():
+    cfg = _cfg(64, 32, 8, 4, 64, 128, 4, 4, rope_type="llama3", rope_theta=5e5, rope_factor=32.0,
+               rope_low_freq_factor=1.0, rope_high_freq_factor=4.0, rope_original_max_position=8192)
+    nf, ne = _run_loop(cfg, [700] * 4, 33, "accum", "score", 16, 4200, cap_mid=128 + 16, score_kind="h2o",
+                       shared=True)
+    assert ne >= 2 * 4
+
+
+def test_closed_loop_serving_batch_ema():
+    cfg = _cfg(128, 32, 8, 4, 64, 256, 4, 2, rope_theta=5e5)
+    lengths = [1500, 300, 900, 2, 325, 700, 1100, 333]
+    nf, ne = _run_loop(cfg, lengths, 32, "ema", "score", 1, 4300, cap_mid=257, score_kind="ema")
+    assert ne > 0
+
+
+def test_closed_loop_llama3_8b_like_position():
+    cfg = _cfg(128, 32, 8, 4, 128, 512, 4, 2, q_dtype="bf16", rope_theta=5e5)
+    nf, ne = _run_loop(cfg, [3000], 16, "none", "position", 1, 4400, cap_mid=513, score_kind=None)
+    assert nf == 0 and ne == 16
