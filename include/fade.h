@@ -248,6 +248,25 @@ int fade_tiered_decode_attn(const fade_config* cfg, const fade_layer_cache* cach
                             void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * fade_tiered_decode_attn without a workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Same arguments, kernels and results as
+ * fade_tiered_decode_attn; the split partials and raw scores go to a
+ * library-held device array of FADE_NOALLOC_SCRATCH_BYTES per device, held
+ * until the process ends. The call allocates nothing: the array's device
+ * address is resolved on the first call on each device (the current device
+ * must be the stream's). FADE_ERR_WORKSPACE when
+ * fade_workspace_bytes(cfg, FADE_WS_DECODE, batch, cap_mid) exceeds the
+ * array (e.g. 64 sequences x 32 query heads with cap_mid 2049 need 20.5 MB).
+ * Every call on one device shares that device's array: calls that overlap
+ * on one device (concurrent streams, or another thread) race and must be
+ * serialized by the caller.
+ */
+#define FADE_NOALLOC_SCRATCH_BYTES (32u << 20)
+int fade_tiered_decode_attn_noalloc(const fade_config* cfg, const fade_layer_cache* cache,
+                                    const void* q, void* out, float* tok_attn, void* stream);
+
+/*
  * H2O / EMA scoring (Transformer series (25), 1.3.1 H2O: accumulated
  * attention = attention-matrix column sums; FADE post, "H2O策略" and
  * "EMA策略").

@@ -116,6 +116,13 @@ def test_validation_rejects_before_launch():
     st = lib.fade_tiered_decode_attn(ctypes.byref(cfg), ctypes.byref(c), ctypes.c_void_p(16),
                                      ctypes.c_void_p(16), null, null, 0, null)
     assert st == fade.FADE_ERR_WORKSPACE
+    # the no-allocation decode rejects a batch whose scratch needs more than the
+    # library-held array, before any HIP call
+    c = fade.LayerCache(64, 8192, 4 + 8192 + 65, 0, 16, 16, 16, 16, 16, 16, 16, None)
+    assert fade.workspace_bytes(cfg, fade.WS_DECODE, 64, 8192) > fade.NOALLOC_SCRATCH_BYTES
+    st = lib.fade_tiered_decode_attn_noalloc(ctypes.byref(cfg), ctypes.byref(c), ctypes.c_void_p(16),
+                                             ctypes.c_void_p(16), null, null)
+    assert st == fade.FADE_ERR_WORKSPACE
     # score policy without a score array
     st = lib.fade_evict_rerope(ctypes.byref(cfg), ctypes.byref(c), fade.POLICY_SCORE, 0, null, null, 0, null)
     assert st == fade.FADE_ERR_INVALID_ARG

@@ -213,6 +213,22 @@ int fade_tiered_decode_attn(const fade_config* cfg, const fade_layer_cache* cach
                                   workspace, reinterpret_cast<hipStream_t>(stream)));
 }
 
+int fade_tiered_decode_attn_noalloc(const fade_config* cfg, const fade_layer_cache* cache, const void* q,
+                                    void* out, float* tok_attn, void* stream) {
+  int st = check_cfg(cfg);
+  if (st) return st;
+  if ((st = check_cache(cfg, cache))) return st;
+  if (!q || !out || !aligned16(q) || !aligned16(out)) return FADE_ERR_INVALID_ARG;
+  if (tok_attn && !aligned(tok_attn, 4)) return FADE_ERR_INVALID_ARG;
+  const Shape s = make_shape(cfg, cache->batch, cache->cap_mid, cache->cap_T, cache->shared);
+  if (decode_ws_bytes(s) > kNoAllocScratchBytes) return FADE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const hipError_t e = noalloc_scratch(&ws);
+  if (e != hipSuccess || !ws) return FADE_ERR_HIP;
+  return hip_status(launch_decode(s, *cache, q, cfg->q_dtype == FADE_DTYPE_BF16, out, cfg->out_dtype, tok_attn, ws,
+                                  reinterpret_cast<hipStream_t>(stream)));
+}
+
 int fade_h2o_scores(const fade_config* cfg, int32_t mode, fade_layer_cache* cache, const void* q_prefill,
                     const void* k_prefill, int32_t batch, int32_t L, int32_t shared, float* scores_out,
                     const float* tok_attn, float decay, void* workspace, size_t ws_bytes, void* stream) {

@@ -45,6 +45,10 @@ hipError_t launch_decode(const Shape& s, const fade_layer_cache& c, const void* 
                          hipStream_t st);
 hipError_t launch_score_update(const Shape& s, const fade_layer_cache& c, int mode,
                                const float* tok_attn, float decay, hipStream_t st);
+// Library-held decode scratch (fade_tiered_decode_attn_noalloc): its device
+// address on the current device, resolved on the first call per device.
+constexpr size_t kNoAllocScratchBytes = (size_t)FADE_NOALLOC_SCRATCH_BYTES;
+hipError_t noalloc_scratch(void** ptr);
 
 // ---- H2O prefill column sums (k_h2o.hip) -----------------------------------
 size_t h2o_ws_bytes(int D, int Hq, int Hkv, int batch, int L);

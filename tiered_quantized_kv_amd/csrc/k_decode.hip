@@ -32,6 +32,8 @@
 //                     a_j = sum_h 2^(s_hj - M_h) / L_h per slot position.
 // Roofline: HBM. Algorithmic bytes per launch = live tier bytes + q + out
 // (+ the side output when requested).
+#include <mutex>
+
 #include "fade_common.hpp"
 #include "fade_internal.hpp"
 
@@ -862,6 +864,37 @@ hipError_t launch_decode(const Shape& s, const fade_layer_cache& c, const void* 
                          raw, c.lens, s.cap_T, tok_attn);
   }
   return hipGetLastError();
+}
+
+// ---- scratch for callers that cannot allocate ------------------------------------
+// The split partials and raw scores of fade_tiered_decode_attn_noalloc live in
+// this array instead of a caller workspace. In host code `scratch` names a
+// host-side stand-in, never a device address: the device address is resolved
+// once per device with hipGetSymbolAddress (with that device current) and
+// only that pointer is handed to kernels. Every call on one device shares the
+// device's copy, so calls that overlap on one device race.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 // ---- decode-time score update (ACCUM / EMA) ----------------------------------

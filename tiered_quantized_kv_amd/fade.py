@@ -63,6 +63,7 @@ _SIGS = {
     "fade_cache_append": (ctypes.c_int, [_CFG, _CACHE, _P, _P, _P]),
     "fade_cache_demote": (ctypes.c_int, [_CFG, _CACHE, _P]),
     "fade_tiered_decode_attn": (ctypes.c_int, [_CFG, _CACHE, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "fade_tiered_decode_attn_noalloc": (ctypes.c_int, [_CFG, _CACHE, _P, _P, _P, _P]),
     "fade_h2o_scores": (ctypes.c_int, [_CFG, ctypes.c_int32, _CACHE, _P, _P, ctypes.c_int32, ctypes.c_int32,
                                        ctypes.c_int32, _P, _P, ctypes.c_float, _P, ctypes.c_size_t, _P]),
     "fade_evict_rerope": (ctypes.c_int, [_CFG, _CACHE, ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_size_t,
@@ -207,6 +208,14 @@ def fade_cache_demote(cfg, cache, stream=None):
 def fade_tiered_decode_attn(cfg, cache, q, out, tok_attn, ws, stream=None):
     _check(lib().fade_tiered_decode_attn(ctypes.byref(cfg), cache.ref(), _p(q), _p(out), _p(tok_attn), _p(ws),
                                          ws.numel(), _s(stream)), "fade_tiered_decode_attn")
+
+
+def fade_tiered_decode_attn_noalloc(cfg, cache, q, out, tok_attn, stream=None):
+    _check(lib().fade_tiered_decode_attn_noalloc(ctypes.byref(cfg), cache.ref(), _p(q), _p(out), _p(tok_attn),
+                                                 _s(stream)), "fade_tiered_decode_attn_noalloc")
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 def fade_h2o_scores(cfg, mode, cache=None, q_prefill=None, k_prefill=None, batch=0, L=0, shared=0,
