@@ -67,6 +67,10 @@ CASES = [
     (64, 16, 8, 2, 4, 260, -1, 16, "f16", 1),       # n_rep 2
     (128, 32, 8, 4, 2, 2100, -1, 64, "f16", 2),     # several splits + ragged tail
     (128, 8, 1, 4, 2, 20000, -1, 64, "f16", 1),     # one KV head, 80 splits: two rounds of the 8-lane merge
+    # n_rep 1 and 2 leave rows of every 4x4x4 MFMA result unread; K4 and K2
+    (128, 16, 8, 4, 2, 700, -1, 64, "f16", 2),      # n_rep 2, K4/V2
+    (64, 8, 8, 4, 4, 500, -1, 32, "bf16", 1),       # n_rep 1, K4/V4, bf16 query
+    (64, 8, 8, 2, 2, 450, -1, 32, "f16", 2),        # n_rep 1, K2/V2
 ]
 
 

@@ -45,8 +45,7 @@ __device__ __forceinline__ float d2f_odd(double d) {
 // land far below fp16's smallest subnormal and still round to a signed zero.
 __device__ __forceinline__ float d2f_odd_h(double d) {
   const uint64_t u = (uint64_t)__double_as_longlong(d);
-  uint32_t st;   // 1 if any cleared bit was set (a 32-bit min; kept from becoming a 64-bit compare)
-  asm("v_min_u32 %0, 1, %1" : "=v"(st) : "v"((uint32_t)u & 0x1FFFFFFFu));
+  const uint32_t st = min((uint32_t)u & 0x1FFFFFFFu, 1u);   // 1 if any cleared bit was set
   const float f = (float)__longlong_as_double((long long)(u & ~(uint64_t)0x1FFFFFFFu));
   return __uint_as_float(__float_as_uint(f) | st);
 }
@@ -86,13 +85,13 @@ __device__ __forceinline__ float wave_max_u(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
 }
 
-// (x & mask) | bits in one VALU op with every operand in a VGPR (VOP3 on gfx9
-// takes no 32-bit literal and one scalar operand at most).
-__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t bits) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(mask), "v"(bits));
-  return r;
-}
+// (x & mask) | bits; with mask and bits held in VGPRs this is one
+// v_and_or_b32 (VOP3 on gfx9 takes no 32-bit literal and one scalar operand at
+// most). Plain C, not inline asm: the hazard recognizer does not count an
+// inline-asm definition as a VALU write, so an asm result placed in a
+// register that an in-flight MFMA still writes (a dead accumulator row) was
+// overwritten by that MFMA.
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t bits) { return (x & mask) | bits; }
 
 __device__ __forceinline__ float wave_sum(float x) {
   x += dpp_f<kRowRor1>(x);

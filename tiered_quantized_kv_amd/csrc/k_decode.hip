@@ -49,8 +49,8 @@ struct DecodeArgs {
   const int32_t* lens;
   const uint16_t* q;
   float* part;        // [B, Hq, nsplit, D + 2]
-  float* raw;         // [B, Hq, cap_T] (log2-domain scores) or nullptr
-  int batch, Hkv, n_sink, ring, cap_mid, cap_T, chunk, nsplit;
+  float* raw;         // [B, Hq, raw_stride] (log2-domain scores); written when SIDE
+  int batch, Hkv, n_sink, ring, cap_mid, cap_T, raw_stride, nsplit;
   int n_fp, fp_per;   // fp16-tier splits (0 .. n_fp - 1) and fp16 slots per split
   float qk_scale;     // log2(e) / sqrt(D)
 };
@@ -61,16 +61,27 @@ constexpr int kSub = 64;          // tokens per wave sub-chunk (one per lane)
 
 constexpr long kDecodeMiddleWGs = 1024;   // middle workgroups the split aims for
 
-int decode_chunk(const Shape& s) {
-  // Middle rows per split: the largest power-of-two multiple of four waves x
-  // one sub-chunk (up to 4096) that still gives about kDecodeMiddleWGs middle
-  // workgroups, so each wave streams several sub-chunks with its loads
-  // prefetched, and the grid still covers the chip.
+// Middle splits per (sequence, KV head): about kDecodeMiddleWGs middle
+// workgroups in all, so that the grid covers the chip, with at most 16 and at
+// least one 256-row unit (four waves x one sub-chunk) per split when the tier
+// is full. The kernel cuts the live middle tier M (not its capacity) into
+// this many equal ranges of whole sub-chunks, so no split idles while
+// another streams twice its share.
+int decode_mid_splits(const Shape& s) {
   const long pairs = (long)s.batch * s.Hkv;
   const int unit = 4 * kSub;
-  int chunk = 16 * unit;
-  while (chunk > unit && pairs * ((s.cap_mid + chunk - 1) / chunk) < kDecodeMiddleWGs) chunk /= 2;
-  return chunk;
+  const long most = (s.cap_mid + unit - 1) / unit;
+  long n = (kDecodeMiddleWGs + pairs - 1) / pairs;
+  n = max(n, (long)((s.cap_mid + 16 * unit - 1) / (16 * unit)));
+  n = min(n, most);
+  return (int)max(n, 1L);
+}
+
+// Middle rows per split when the tier is full (the host's estimate of a
+// split's work).
+int decode_chunk(const Shape& s) {
+  const int n = decode_mid_splits(s);
+  return ((s.cap_mid + n - 1) / n + kSub - 1) / kSub * kSub;
 }
 
 // FP16-tier splits: the fp16 tier (sinks + ring) is cut into as many
@@ -84,13 +95,16 @@ int decode_fp_splits(const Shape& s) {
   return (int)(n < 1 ? 1 : (n > 4 ? 4 : n));
 }
 
-int decode_nsplit(const Shape& s) {
-  return decode_fp_splits(s) + (s.cap_mid + decode_chunk(s) - 1) / decode_chunk(s);
-}
+int decode_nsplit(const Shape& s) { return decode_fp_splits(s) + decode_mid_splits(s); }
+
+// Raw scores of one query head: cap_T slots, then kSub pad entries that the
+// lanes past a split's last token write instead (their stores stay
+// unconditional, so the compiler can count the loads in flight).
+int decode_raw_stride(const Shape& s) { return s.cap_T + kSub; }
 
 size_t decode_ws_bytes(const Shape& s) {
   size_t n = align_up((size_t)s.batch * s.Hq * decode_nsplit(s) * (s.D + 2) * 4, 256);
-  n += align_up((size_t)s.batch * s.Hq * s.cap_T * 4, 256);   // raw scores
+  n += align_up((size_t)s.batch * s.Hq * decode_raw_stride(s) * 4, 256);   // raw scores
   return n;
 }
 
@@ -203,7 +217,7 @@ struct TierLayout {
   static_assert(64 * HQ4 * 4 * 4 <= pw_bytes + vt_bytes, "fp16-tier weights fit the wave tiles");
 };
 
-template <int D, int NREP, int KB, int VB, bool QBF>
+template <int D, int NREP, int KB, int VB, bool QBF, bool SIDE>
 __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
   using Lay = TierLayout<D, NREP, KB, VB>;
   constexpr int NG = Lay::NG, NI = Lay::NI, HQ4 = Lay::HQ4, U = Lay::U, PW = Lay::PW;
@@ -235,9 +249,11 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
   const int S = min(max(L[0], 0), a.n_sink), M = min(max(L[1], 0), a.cap_mid);
   const int R = min(max(L[2], 0), a.ring), rhead = min(max(L[3], 0), a.ring - 1);
   const bool fpt = split < a.n_fp;                   // FP16 tier
-  const int row0 = fpt ? 0 : (split - a.n_fp) * a.chunk;
+  // middle split: an equal share of the live rows, in whole sub-chunks
+  const int per = ((M + n_mid_splits - 1) / n_mid_splits + kSub - 1) / kSub * kSub;
+  const int row0 = fpt ? 0 : (split - a.n_fp) * per;
   const int fp_lo = fpt ? split * a.fp_per : 0;     // this split's fp16 tokens [fp_lo, fp_lo + n_tok)
-  const int n_tok = fpt ? min(a.fp_per, S + R - fp_lo) : min(a.chunk, M - row0);
+  const int n_tok = fpt ? min(a.fp_per, S + R - fp_lo) : min(per, M - row0);
 
   float* part_base = a.part + ((size_t)(b * Hq + g * NREP) * a.nsplit + split) * (D + 2);
   const size_t part_hstride = (size_t)a.nsplit * (D + 2);
@@ -337,7 +353,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
   }
   __syncthreads();
 
-  float* rawb = a.raw ? a.raw + (size_t)(b * Hq + g * NREP) * a.cap_T : nullptr;
+  float* rawb = SIDE ? a.raw + (size_t)(b * Hq + g * NREP) * a.raw_stride : nullptr;
   uint16_t* pw = reinterpret_cast<uint16_t*>(wreg + wave * Lay::wave_bytes);   // [HQ4][NG][4][PW]
   uint16_t* vt = pw + Lay::pw_bytes / 2;                                       // [2][U][PW]
   const uint32_t* qf32 = reinterpret_cast<const uint32_t*>(qf);
@@ -413,37 +429,46 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
         qreg[hq][i] = as_h4(av.x, av.y);
       }
     for (int base = wave * kSub; base < n_tok; base += 4 * kSub) {
-      const bool more = base + 4 * kSub < n_tok;   // wave-uniform
       const int t = base + lane;
       const bool valid = t < n_tok;
       // ---- QK^T ----
+      // One accumulator chain per 32-channel group, the chains interleaved
+      // step by step so consecutive MFMAs are independent; each group's sum
+      // keeps its channel order.
       float s2[HQ4 * 4];
 #pragma unroll
       for (int h = 0; h < HQ4 * 4; ++h) s2[h] = 0.f;
+      f32x4 d[NG][HQ4];
 #pragma unroll
-      for (int gi = 0; gi < NG; ++gi) {
-        f32x4 d[HQ4];
+      for (int gi = 0; gi < NG; ++gi)
 #pragma unroll
-        for (int hq = 0; hq < HQ4; ++hq) d[hq] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int hq = 0; hq < HQ4; ++hq) d[gi][hq] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int si = 0; si < 8; ++si) {
+      for (int si = 0; si < 8; ++si) {
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
           const int sidx = 8 * gi + si;
           const f16x4 bop = key_operand<KB>(cur.k, sidx, kcon);
 #pragma unroll
-          for (int hq = 0; hq < HQ4; ++hq) d[hq] = mfma4_ab<4>(qreg[hq][sidx >> 4], bop, d[hq], sidx & 15);
+          for (int hq = 0; hq < HQ4; ++hq) d[gi][hq] = mfma4_ab<4>(qreg[hq][sidx >> 4], bop, d[gi][hq], sidx & 15);
         }
+      }
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
         const uint32_t sw = cur.ks[gi >> 1];
         const float scl = h2f((uint16_t)((gi & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
 #pragma unroll
         for (int hq = 0; hq < HQ4; ++hq)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) s2[4 * hq + i] = fmaf(scl, d[hq][i], s2[4 * hq + i]);
+          for (int i = 0; i < 4; ++i) s2[4 * hq + i] = fmaf(scl, d[gi][hq][i], s2[4 * hq + i]);
       }
-      if (more) issue_k(cur, base + 4 * kSub);
+      // the next sub-chunk's keys; past the split's end every lane reads its
+      // last row again (unconditional, so the waits stay exact)
+      issue_k(cur, min(base + 4 * kSub, n_tok - 1));
 #pragma unroll
       for (int h = 0; h < HQ4 * 4; ++h) {
         s2[h] = valid ? s2[h] * kf[h] : -INFINITY;
-        if (h < NREP && rawb && valid) rawb[(size_t)h * a.cap_T + S + row0 + t] = s2[h];
+        if (SIDE && h < NREP) rawb[(size_t)h * a.raw_stride + (valid ? S + row0 + t : a.cap_T + lane)] = s2[h];
       }
       // ---- softmax ----
       float p[HQ4 * 4];
@@ -463,7 +488,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
         vt[u * PW + lane] = (uint16_t)((u & 1) ? (w >> 16) : (w & 0xFFFFu));
         vt[(U + u) * PW + lane] = (uint16_t)((u & 1) ? (wh >> 16) : (wh & 0xFFFFu));
       }
-      if (more) issue_v(cur, base + 4 * kSub);
+      issue_v(cur, min(base + 4 * kSub, n_tok - 1));
       wave_lds_sync();
       // ---- PV ----
       // Weight fragments: step st (tokens 4 st .. 4 st + 3) of column group
@@ -484,9 +509,9 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
           }
       }
 #pragma unroll
-      for (int sg = 0; sg < NSIG; ++sg) {
+      for (int t8 = 0; t8 < kSub / 8; ++t8) {
 #pragma unroll
-        for (int t8 = 0; t8 < kSub / 8; ++t8) {
+        for (int sg = 0; sg < NSIG; ++sg) {
           const uint4 x = *reinterpret_cast<const uint4*>(vt + vu[sg] * PW + 8 * t8);
           const uint32_t y0 = h2_bits(as_h2(and_or(x.x, vmask[sg], 0x64006400u)) - vsub[sg]);
           const uint32_t y1 = h2_bits(as_h2(and_or(x.y, vmask[sg], 0x64006400u)) - vsub[sg]);
@@ -565,7 +590,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
 #pragma unroll
       for (int h = 0; h < HQ4 * 4; ++h) {
         s2[h] = valid ? (d0[h / 4][h % 4] + d1[h / 4][h % 4]) * kf[h] : -INFINITY;
-        if (h < NREP && rawb && valid) rawb[(size_t)h * a.cap_T + pos] = s2[h];
+        if (SIDE && h < NREP) rawb[(size_t)h * a.raw_stride + (valid ? pos : a.cap_T + lane)] = s2[h];
       }
       float p[HQ4 * 4];
       softmax_step(s2, p, valid);
@@ -666,7 +691,7 @@ __device__ __forceinline__ float group_sum(float x) {
 template <int D, int LN>
 __global__ __launch_bounds__(256) void k_decode_finish(const float* __restrict__ part, int nsplit, int Hq,
                                                        void* out, int out_dtype,
-                                                       const float* __restrict__ raw,
+                                                       const float* __restrict__ raw, int raw_stride,
                                                        const int32_t* __restrict__ lens, int cap_T,
                                                        float* __restrict__ tok_attn) {
   extern __shared__ float ml[];   // [Hq][2] = (M_h, 1 / L_h), then [4][kFinishSlots] partial sums
@@ -747,7 +772,7 @@ __global__ __launch_bounds__(256) void k_decode_finish(const float* __restrict__
 #pragma unroll
         for (int u = 0; u < kFinishBatch; ++u) {
           const int h = h0 + 4 * u;
-          rv[u] = h < Hq ? raw[((size_t)b * Hq + h) * cap_T + jj] : 0.f;
+          rv[u] = h < Hq ? raw[((size_t)b * Hq + h) * raw_stride + jj] : 0.f;
         }
 #pragma unroll
         for (int u = 0; u < kFinishBatch; ++u) {
@@ -768,7 +793,10 @@ __global__ __launch_bounds__(256) void k_decode_finish(const float* __restrict__
 template <int D, int NREP, int KB, int VB, bool QBF>
 static void launch_tiers(const DecodeArgs& a, dim3 grid, hipStream_t st) {
   const size_t lds = (size_t)TierLayout<D, NREP, KB, VB>::total;
-  hipLaunchKernelGGL((k_decode_tiers<D, NREP, KB, VB, QBF>), grid, dim3(kThreads), lds, st, a);
+  if (a.raw)
+    hipLaunchKernelGGL((k_decode_tiers<D, NREP, KB, VB, QBF, true>), grid, dim3(kThreads), lds, st, a);
+  else
+    hipLaunchKernelGGL((k_decode_tiers<D, NREP, KB, VB, QBF, false>), grid, dim3(kThreads), lds, st, a);
 }
 
 template <int D, int NREP, bool QBF>
@@ -791,12 +819,12 @@ static void dispatch_rep(int n_rep, int kb, int vb, const DecodeArgs& a, dim3 gr
 
 hipError_t launch_decode(const Shape& s, const fade_layer_cache& c, const void* q, int q_bf16,
                          void* out, int out_dtype, float* tok_attn, void* ws, hipStream_t st) {
-  const int chunk = decode_chunk(s);
   const int nsplit = decode_nsplit(s);
   char* w = reinterpret_cast<char*>(ws);
   float* part = reinterpret_cast<float*>(w);
   w += align_up((size_t)s.batch * s.Hq * nsplit * (s.D + 2) * 4, 256);
   float* raw = reinterpret_cast<float*>(w);
+  const int raw_stride = decode_raw_stride(s);
 
   DecodeArgs a;
   a.fp_k = reinterpret_cast<const uint16_t*>(c.fp_k);
@@ -815,7 +843,7 @@ hipError_t launch_decode(const Shape& s, const fade_layer_cache& c, const void* 
   a.ring = s.ring;
   a.cap_mid = s.cap_mid;
   a.cap_T = s.cap_T;
-  a.chunk = chunk;
+  a.raw_stride = decode_raw_stride(s);
   a.nsplit = nsplit;
   a.n_fp = decode_fp_splits(s);
   a.fp_per = (s.n_sink + s.ring + a.n_fp - 1) / a.n_fp;
@@ -851,17 +879,17 @@ hipError_t launch_decode(const Shape& s, const fade_layer_cache& c, const void* 
   if (s.D == 128) {
     if (wide)
       hipLaunchKernelGGL((k_decode_finish<128, 8>), fgrid, dim3(256), flds, st, part, nsplit, s.Hq, out, out_dtype,
-                         raw, c.lens, s.cap_T, tok_attn);
+                         raw, raw_stride, c.lens, s.cap_T, tok_attn);
     else
       hipLaunchKernelGGL((k_decode_finish<128, 1>), fgrid, dim3(256), flds, st, part, nsplit, s.Hq, out, out_dtype,
-                         raw, c.lens, s.cap_T, tok_attn);
+                         raw, raw_stride, c.lens, s.cap_T, tok_attn);
   } else {
     if (wide)
       hipLaunchKernelGGL((k_decode_finish<64, 8>), fgrid, dim3(256), flds, st, part, nsplit, s.Hq, out, out_dtype,
-                         raw, c.lens, s.cap_T, tok_attn);
+                         raw, raw_stride, c.lens, s.cap_T, tok_attn);
     else
       hipLaunchKernelGGL((k_decode_finish<64, 1>), fgrid, dim3(256), flds, st, part, nsplit, s.Hq, out, out_dtype,
-                         raw, c.lens, s.cap_T, tok_attn);
+                         raw, raw_stride, c.lens, s.cap_T, tok_attn);
   }
   return hipGetLastError();
 }

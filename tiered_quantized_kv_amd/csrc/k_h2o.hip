@@ -80,11 +80,10 @@ __device__ __forceinline__ f16x8 load8(const uint16_t* p) {
 //    written); key rows past L read as zero and are masked.
 constexpr float kMaskedRaw = -0x1p100f;
 
-// max of four MFMA results without the NaN-quieting copies fmaxf implies
+// max of four MFMA results (plain C: an inline-asm definition is not seen as a
+// VALU write by the hazard recognizer, which matters next to in-flight MFMAs)
 __device__ __forceinline__ float max4(float a, float b, float c, float d) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3\n\tv_max_f32 %0, %0, %4" : "=&v"(r) : "v"(a), "v"(b), "v"(c), "v"(d));
-  return r;
+  return __builtin_fmaxf(__builtin_fmaxf(a, b), __builtin_fmaxf(c, d));
 }
 
 template <int D, int HPW>
