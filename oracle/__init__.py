@@ -26,7 +26,9 @@ Modules:
   attention   joint-softmax decode attention over all tiers, side output
   h2o         H2O prefill column sums, cumulative / EMA score updates
   cache       the three-tier cache: tier layout, prefill build, append,
-              demotion, eviction with un-RoPE / re-RoPE compaction
+              demotion, eviction with un-RoPE / re-RoPE compaction; the
+              optional INT2 overflow tier (int2_budget) and its two-level
+              event (demote the INT4 overflow, drop the INT2 overflow)
   accounting  compressed-bytes closed form
   pq          product-quantization codebook: Lloyd training, encode, decode
 

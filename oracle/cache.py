@@ -34,8 +34,31 @@ Readings taken where the pages are silent:
     bit-for-bit. Slots whose index does not change are untouched.
   * At prefill the order is score -> select -> compact / re-RoPE on the fp16
     prefill -> quantize the middle survivors.
+
+INT2 overflow tier (FADE post, "第三层：INT2深度压缩（可选）": part of the
+tokens may be compressed further to 2 bits, read together with "驱逐策略"),
+on when int2_budget >= 0:
+  * Slot order: sinks | INT2 tier | INT4 middle | recent; a slot's position is
+    still its index in the compacted cache. The INT2 tier sits before the
+    INT4 tier so that a token demoted from the recent window to the INT4 tail
+    keeps its position (the INT4 tail slot is the first recent slot).
+  * An event demotes the INT4 tier's overflow (the M4 - int4_budget slots the
+    policy would evict: lowest (score, slot) first) into the INT2 tier instead
+    of dropping it. The demoted slots go to the end of the INT2 tier in their
+    INT4 order; only the INT2 tier's own overflow over int2_budget is
+    dropped, chosen the same way among the old INT2 slots and the demoted
+    ones (every old INT2 slot has a lower slot index than a demoted one, so
+    the position policy drops the oldest INT2 slots first).
+  * A demoted key is dequantized, rotated from its old slot to its new one
+    (the identity when the slot is the same), rounded once to fp16 and
+    quantized at 2 bits; a demoted value is dequantized, rounded to fp16 and
+    quantized at 2 bits. A surviving INT2 key whose slot changes is
+    re-rotated the same way and stays at 2 bits; values move bit-for-bit.
+  * Tokens only move down the tiers: an INT2 slot is never promoted back.
+  * At prefill the build keeps int4_budget + int2_budget candidates in the
+    INT4 layout, then the same event demotes the int2_budget lowest of them.
 """
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 
 import numpy as np
 
@@ -63,6 +86,7 @@ class Config:
     rope_original_max_position: int = 8192
     rope_seq_len: int = 0
     rope_interleaved: bool = False
+    int2_budget: int = -1       # INT2 overflow tier capacity after an event; -1: no such tier
 
     def freqs(self):
         return rope.inv_freq(self.head_dim, self.rope_theta, self.rope_type,
@@ -101,6 +125,16 @@ class SeqCache:
     rec_k: np.ndarray           # float16 [Hkv, R, d], oldest first
     rec_v: np.ndarray
     scores: np.ndarray = field(default=None)   # float64 [T]
+    low_k_u: np.ndarray = field(default=None)  # uint8 codes [Hkv, M2, d], 2 bits (INT2 tier)
+    low_k_s: np.ndarray = field(default=None)  # float16 scales [Hkv, M2, d/G]
+    low_v_u: np.ndarray = field(default=None)
+    low_v_s: np.ndarray = field(default=None)
+
+    def __post_init__(self):
+        if self.low_k_u is None:
+            hkv, d = self.sink_k.shape[0], self.sink_k.shape[2]
+            self.low_k_u, self.low_k_s = _empty_codes(hkv, d, self.cfg.group_size)
+            self.low_v_u, self.low_v_s = _empty_codes(hkv, d, self.cfg.group_size)
 
     @property
     def n_sink_live(self):
@@ -115,8 +149,12 @@ class SeqCache:
         return self.rec_k.shape[1]
 
     @property
+    def low_len(self):
+        return self.low_k_u.shape[1]
+
+    @property
     def length(self):
-        return self.n_sink_live + self.mid_len + self.rec_len
+        return self.n_sink_live + self.mid_len + self.low_len + self.rec_len
 
     def dense(self):
         """(k_hat, v_hat) float64 [Hkv, T, d] in slot order."""
@@ -124,11 +162,16 @@ class SeqCache:
         g = c.group_size
         mk = quant.dequantize(self.mid_k_u, self.mid_k_s, c.middle_k_bits, g)
         mv = quant.dequantize(self.mid_v_u, self.mid_v_s, c.middle_v_bits, g)
-        k = np.concatenate([self.sink_k.astype(np.float64), mk,
+        lk = quant.dequantize(self.low_k_u, self.low_k_s, LOW_BITS, g)
+        lv = quant.dequantize(self.low_v_u, self.low_v_s, LOW_BITS, g)
+        k = np.concatenate([self.sink_k.astype(np.float64), lk, mk,
                             self.rec_k.astype(np.float64)], axis=1)
-        v = np.concatenate([self.sink_v.astype(np.float64), mv,
+        v = np.concatenate([self.sink_v.astype(np.float64), lv, mv,
                             self.rec_v.astype(np.float64)], axis=1)
         return k, v
+
+
+LOW_BITS = 2           # the INT2 tier's K and V bits
 
 
 def _empty_codes(hkv, d, g):
@@ -143,6 +186,15 @@ def build_from_prefill(cfg, k16, v16, scores=None):
     (older middle tokens evicted first)."""
     k16 = np.asarray(k16, dtype=np.float16)
     v16 = np.asarray(v16, dtype=np.float16)
+    if cfg.int2_budget >= 0:
+        # the INT4 layout first holds int4_budget + int2_budget candidates;
+        # the event that follows demotes the lowest int2_budget of them
+        wide = replace(cfg, int2_budget=-1,
+                       int4_budget=cfg.int4_budget + cfg.int2_budget if cfg.int4_budget >= 0 else -1)
+        cache = build_from_prefill(wide, k16, v16, scores)
+        cache.cfg = cfg
+        evict(cache, cfg.int4_budget, "position" if scores is None else "score")
+        return cache
     hkv, L, d = k16.shape
     s, m, r = tier_layout(L, cfg.n_sink, cfg.recent_window)
     mid_scores = (np.arange(m, dtype=np.float64) if scores is None
@@ -212,15 +264,20 @@ def demote(cache):
         cache.rec_v = cache.rec_v[:, 1:]
 
 
-def evict(cache, budget, policy="score", evicted=None):
+def evict(cache, budget, policy="score", evicted=None, dropped=None):
     """Eviction event: if the middle tier holds more than `budget` tokens,
     evict down to `budget` and compact with un-RoPE / re-RoPE.
 
     policy "score" ranks by cache.scores (H2O or EMA), "position" by slot.
     `evicted` may force the evicted middle indices (used by multi-step tests
     to follow the device's choice inside a near-tie band).
-    Returns the sorted evicted middle indices."""
+    Returns the sorted evicted middle indices. With an INT2 tier
+    (cfg.int2_budget >= 0) the event is evict_tiered's, which returns
+    (demoted INT4 indices, dropped candidate indices); `evicted` then forces
+    the demoted set and `dropped` the dropped one."""
     c = cache.cfg
+    if c.int2_budget >= 0:
+        return evict_tiered(cache, budget, policy, evicted, dropped)
     m = cache.mid_len
     s = cache.n_sink_live
     if budget < 0 or m <= budget:
@@ -260,6 +317,96 @@ def evict(cache, budget, policy="score", evicted=None):
     survivors = np.concatenate([np.arange(s), s + kept, s + m + np.arange(r)])
     cache.scores = cache.scores[survivors].copy()
     return evicted
+
+
+def evict_tiered(cache, budget, policy="score", demoted=None, dropped=None):
+    """Event with the INT2 overflow tier (see the module docstring): demote
+    the INT4 tier's overflow into the INT2 tier, drop the INT2 tier's
+    overflow over cfg.int2_budget, and re-rotate every key whose slot
+    changes.
+
+    Returns (demoted, dropped): the demoted INT4 indices (ascending) and the
+    dropped indices into the candidate list [the old INT2 slots in order,
+    then the demoted INT4 slots in order]. `demoted` / `dropped` force either
+    choice (tests following the device inside a near-tie band)."""
+    c = cache.cfg
+    g = c.group_size
+    s, m4, m2, r = cache.n_sink_live, cache.mid_len, cache.low_len, cache.rec_len
+    sc = cache.scores
+    n_dem = m4 - budget if 0 <= budget < m4 else 0
+    if demoted is None:
+        key4 = np.arange(m4, dtype=np.float64) if policy == "position" else sc[s + m2:s + m2 + m4]
+        demoted = select_evicted(key4, n_dem)
+    demoted = np.asarray(demoted, dtype=np.int64)
+    assert demoted.size == n_dem
+    cand_slots = np.concatenate([s + np.arange(m2), s + m2 + demoted]).astype(np.int64)
+    n_drop = max(0, cand_slots.size - c.int2_budget)
+    if dropped is None:
+        keyc = cand_slots.astype(np.float64) if policy == "position" else sc[cand_slots]
+        dropped = select_evicted(keyc, n_drop)
+    dropped = np.asarray(dropped, dtype=np.int64)
+    assert dropped.size == n_drop
+    keep4 = np.ones(m4, dtype=bool)
+    keep4[demoted] = False
+    kept4 = np.nonzero(keep4)[0]
+    keepc = np.ones(cand_slots.size, dtype=bool)
+    keepc[dropped] = False
+    keptc = np.nonzero(keepc)[0]
+    m4n, m2n = kept4.size, keptc.size
+    freqs = c.freqs()
+    rotates = freqs.any()
+    il = c.rope_interleaved
+
+    def moved_key(u, sc16, bits_in, old, new, bits_out):
+        """Keys [Hkv, n, d] from old to new slots: dequantize, rotate, round to
+        fp16 once, quantize at bits_out."""
+        khat = quant.dequantize(u, sc16, bits_in, g)
+        z = rope.rerope_fp16(khat, old, new, freqs, il) if rotates else khat.astype(np.float16)
+        return quant.quantize(z, bits_out, g)
+
+    # INT4 survivors keep their order at slots s + m2n ..
+    mk_u = cache.mid_k_u[:, kept4].copy()
+    mk_s = cache.mid_k_s[:, kept4].copy()
+    old4, new4 = s + m2 + kept4, s + m2n + np.arange(m4n)
+    mv4 = old4 != new4
+    if mv4.any() and rotates:
+        u2, s2 = moved_key(mk_u[:, mv4], mk_s[:, mv4], c.middle_k_bits, old4[mv4], new4[mv4], c.middle_k_bits)
+        mk_u[:, mv4], mk_s[:, mv4] = u2, s2
+    # INT2 tier: kept candidates in candidate order at s ..
+    hkv, d = cache.sink_k.shape[0], cache.sink_k.shape[2]
+    lk_u = np.zeros((hkv, m2n, d), np.uint8)
+    lk_s = np.zeros((hkv, m2n, d // g), np.float16)
+    lv_u = np.zeros((hkv, m2n, d), np.uint8)
+    lv_s = np.zeros((hkv, m2n, d // g), np.float16)
+    for j, ci in enumerate(keptc):
+        new = s + j
+        old = cand_slots[ci]
+        if ci >= m2:                        # demoted from INT4: always requantized
+            i4 = demoted[ci - m2]
+            ku, ks = moved_key(cache.mid_k_u[:, i4:i4 + 1], cache.mid_k_s[:, i4:i4 + 1], c.middle_k_bits,
+                               np.array([old]), np.array([new]), LOW_BITS)
+            vhat = quant.dequantize(cache.mid_v_u[:, i4:i4 + 1], cache.mid_v_s[:, i4:i4 + 1],
+                                    c.middle_v_bits, g).astype(np.float16)
+            vu, vs = quant.quantize(vhat, LOW_BITS, g)
+        else:                               # an old INT2 slot
+            i2 = ci
+            ku, ks = cache.low_k_u[:, i2:i2 + 1], cache.low_k_s[:, i2:i2 + 1]
+            if old != new and rotates:
+                ku, ks = moved_key(ku, ks, LOW_BITS, np.array([old]), np.array([new]), LOW_BITS)
+            vu, vs = cache.low_v_u[:, i2:i2 + 1], cache.low_v_s[:, i2:i2 + 1]
+        lk_u[:, j:j + 1], lk_s[:, j:j + 1] = ku, ks
+        lv_u[:, j:j + 1], lv_s[:, j:j + 1] = vu, vs
+    # recent ring: every entry moves down by the dropped count
+    if r and n_drop and rotates:
+        old_r = s + m4 + m2 + np.arange(r)
+        cache.rec_k = rope.rerope_fp16(cache.rec_k, old_r, old_r - n_drop, freqs, il)
+    survivors = np.concatenate([np.arange(s), cand_slots[keptc], s + m2 + kept4, s + m4 + m2 + np.arange(r)])
+    cache.scores = cache.scores[survivors].copy()
+    cache.mid_k_u, cache.mid_k_s = mk_u, mk_s
+    cache.mid_v_u = cache.mid_v_u[:, kept4].copy()
+    cache.mid_v_s = cache.mid_v_s[:, kept4].copy()
+    cache.low_k_u, cache.low_k_s, cache.low_v_u, cache.low_v_s = lk_u, lk_s, lv_u, lv_s
+    return demoted, dropped
 
 
 def update_scores(caches, sides, mode, beta=0.9, shared=False):
