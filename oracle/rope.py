@@ -131,6 +131,12 @@ def rerope_fp16(k, old_pos, new_pos, freqs, interleaved=False):
     x = np.asarray(k)
     x = x.astype(np.float64) if x.dtype != np.float64 else x
     y = rotate(unrotate(x, old_pos, freqs, interleaved), new_pos, freqs, interleaved)
+    # A key that keeps its position is rotated by a zero angle, the identity:
+    # it is only rounded. The two rotations above cancel only to ~1e-16,
+    # which would decide the rounding of a dequantized value lying exactly on
+    # an fp16 midpoint (q * s often does).
+    same = np.broadcast_to(np.asarray(old_pos) == np.asarray(new_pos), y.shape[:-1])
+    y[same] = np.broadcast_to(x, y.shape)[same]
     return y.astype(np.float16)
 
 

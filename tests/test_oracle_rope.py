@@ -133,6 +133,37 @@ def test_rerope_matches_rotation_of_raw_key():
     assert np.array_equal(same, stored)
 
 
+def test_rerope_keeping_the_position_only_rounds_midpoints_to_even():
+    """A key that keeps its position is rotated by the identity and only
+    rounded: dequantized INT4 values q * s that lie exactly halfway between two
+    fp16 numbers round half to even, at every position (FADE post, "RoPE重计算";
+    a net zero rotation leaves the value as it is)."""
+    from fractions import Fraction
+    d = 128
+    f = rope.inv_freq(d, 5e5)
+    # 3 * (1 + 2^-10 + 2^-11 ...) style products: s = 1 + 2^-10 (fp16), q = 3
+    # gives 3 + 3 * 2^-10, exactly halfway between fp16 neighbours 3 + 2^-9 and
+    # 3 + 2^-8 (spacing 2^-9 on [2, 4)) -> ties to the even mantissa
+    s16 = np.float16(1 + 2.0 ** -10)
+    x = np.zeros((2, 3, d))
+    x[:, :, :] = 3.0 * float(s16)
+    x[:, :, 1::2] = -5.0 * float(s16)
+    pos = np.array([0.0, 37.0, 90001.0])
+    got = rope.rerope_fp16(x, pos, pos, f)
+    for v, g in ((3.0 * float(s16), got[0, 1, 0]), (-5.0 * float(s16), got[1, 2, 1])):
+        lo = np.float16(v)
+        exact = Fraction(v)
+        # the nearest fp16 value, ties to even, from exact rationals
+        cands = sorted({np.float16(v), np.nextafter(np.float16(v), np.float16(np.inf)),
+                        np.nextafter(np.float16(v), np.float16(-np.inf))}, key=lambda c: (abs(Fraction(float(c)) - exact),
+                                                                                      int(np.array(c).view(np.uint16)) & 1))
+        assert g == cands[0], (v, g, cands)
+    assert np.array_equal(got, x.astype(np.float16))
+    # a moved key is still rotated
+    moved = rope.rerope_fp16(x, pos, pos - 1, f)
+    assert not np.array_equal(moved, got)
+
+
 def test_round_bf16_matches_exact_rational_rounding():
     from fractions import Fraction
     gen = np.random.default_rng(9)
