@@ -118,6 +118,14 @@ enum fade_ws_op {
  *                   call (>= 0; ignored by the other schemes)
  *   q_dtype         FADE_DTYPE_F16 or FADE_DTYPE_BF16 (decode query)
  *   out_dtype       FADE_DTYPE_F16, FADE_DTYPE_BF16 or FADE_DTYPE_F32
+ *   int2_budget     INT2 overflow tier (FADE post, "第三层：INT2深度压缩（可选）"):
+ *                   -1 = none (tokens over int4_budget are evicted); >= 0 =
+ *                   the tier's capacity after an event. Then an event demotes
+ *                   the INT4 overflow (the slots the policy would evict) into
+ *                   the INT2 tier - K and V requantized at 2 bits, keys
+ *                   re-rotated to their new slot - and only the INT2 tier's
+ *                   own overflow is evicted. Slot order: sinks, INT2 tier,
+ *                   INT4 middle, recent. Needs int4_budget >= 0.
  */
 typedef struct fade_config {
   int32_t head_dim;
@@ -138,6 +146,7 @@ typedef struct fade_config {
   int32_t q_dtype;
   int32_t out_dtype;
   int32_t rope_seq_len;
+  int32_t int2_budget;
 } fade_config;
 
 /*
@@ -160,11 +169,19 @@ typedef struct fade_config {
  *                   rec_head}. Read and updated by the kernels only.
  *   scores          f32 [shared ? 1 : batch, cap_T] per-slot importance
  *                   (index = slot position); NULL when no policy uses it.
- *   cap_T           n_sink + cap_mid + recent_window + 1.
+ *   cap_T           slots of the scores row (see below).
  *   shared          1: all rows share tier decisions (FADE post
  *                   "批处理支持"); scores then has one row.
+ *   cap_low,        INT2 overflow tier (used when cfg->int2_budget >= 0,
+ *   low_*           otherwise ignored): codes u8 [batch, Hkv, cap_low,
+ *                   head_dim / 4] for K and for V, scales fp16 [batch, Hkv,
+ *                   cap_low, head_dim / 32]; low_lens int32 [batch] = the
+ *                   tier's live rows (kernels only). cap_low >= int2_budget.
+ * cap_T = n_sink + cap_mid + recent_window + 1, plus cap_low with an INT2
+ * tier.
  * Positions: a slot's RoPE position is its index in the compacted cache:
- * sinks 0.., middle rows n_sink_live + r, recent entries after the middle.
+ * sinks 0.., then the INT2 tier's rows (n_sink_live + j), then the INT4
+ * middle rows (n_sink_live + M2 + r), then the recent entries.
  */
 typedef struct fade_layer_cache {
   int32_t batch;
@@ -179,12 +196,19 @@ typedef struct fade_layer_cache {
   void* mid_v_scales;
   int32_t* lens;
   float* scores;
+  int32_t cap_low;
+  int32_t reserved;
+  void* low_k_codes;
+  void* low_v_codes;
+  void* low_k_scales;
+  void* low_v_scales;
+  int32_t* low_lens;
 } fade_layer_cache;
 
 /* Human-readable name of a status code; never NULL. */
 const char* fade_status_string(int status);
 
-/* ABI version of this header (major * 100 + minor): 200. */
+/* ABI version of this header (major * 100 + minor): 300. */
 int fade_abi_version(void);
 
 /*
@@ -349,6 +373,16 @@ int fade_rope_rotate(const fade_config* cfg, void* x, int32_t dtype, int64_t n_r
  * and `max_len` (see enum). Returns 0 for an invalid configuration. */
 size_t fade_workspace_bytes(const fade_config* cfg, int32_t op, int32_t batch,
                             int32_t max_len);
+
+/* Workspace bytes needed by `op` (enum fade_ws_op) on this cache, sized from
+ * its own capacities (cap_mid, cap_low, cap_T) and batch; max_len is the
+ * prefill length for FADE_WS_PREFILL_BUILD and is ignored otherwise
+ * (FADE_WS_H2O_PREFILL takes no cache and returns 0 here). The sizes
+ * fade_workspace_bytes gives assume cap_low = max(int2_budget, 1); a cache
+ * with more INT2 rows than that needs this query. Returns 0 for an invalid
+ * configuration or cache. */
+size_t fade_cache_workspace_bytes(const fade_config* cfg, const fade_layer_cache* cache, int32_t op,
+                                  int32_t max_len);
 
 /*
  * Compressed KV bytes (FADE post, "使用注意事项": KV-only accounting), host

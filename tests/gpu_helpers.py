@@ -29,7 +29,8 @@ ROPE_KW = {
 def ocfg(c):
     return oc.Config(head_dim=c.head_dim, n_q_heads=c.n_q_heads, n_kv_heads=c.n_kv_heads, n_sink=c.n_sink,
                      recent_window=c.recent_window, int4_budget=c.int4_budget, middle_k_bits=c.middle_k_bits,
-                     middle_v_bits=c.middle_v_bits, group_size=32, rope_theta=c.rope_theta,
+                     middle_v_bits=c.middle_v_bits, int2_budget=c.int2_budget, group_size=32,
+                     rope_theta=c.rope_theta,
                      rope_type=ROPE_NAMES[c.rope_type & fade.ROPE_SCHEME_MASK], rope_factor=c.rope_factor,
                      rope_low_freq_factor=c.rope_low_freq_factor, rope_high_freq_factor=c.rope_high_freq_factor,
                      rope_original_max_position=c.rope_original_max_position, rope_seq_len=c.rope_seq_len,
@@ -67,33 +68,55 @@ def seq_state(tc, b):
     st = dict(S=S, M=M, R=R, head=head, sink_k=fk[:, :S], sink_v=fv[:, :S], rec_k=fk[:, slots],
               rec_v=fv[:, slots], mid_k=tc.mid_k_codes[b, :, :M].cpu().numpy(),
               mid_ks=tc.mid_k_scales[b, :, :M].cpu().numpy(), mid_v=tc.mid_v_codes[b, :, :M].cpu().numpy(),
-              mid_vs=tc.mid_v_scales[b, :, :M].cpu().numpy())
+              mid_vs=tc.mid_v_scales[b, :, :M].cpu().numpy(), M2=0)
+    if getattr(tc, "low", False):
+        M2 = int(tc.low_lens[b].cpu())
+        st.update(M2=M2, low_k=tc.low_k_codes[b, :, :M2].cpu().numpy(), low_ks=tc.low_k_scales[b, :, :M2].cpu().numpy(),
+                  low_v=tc.low_v_codes[b, :, :M2].cpu().numpy(), low_vs=tc.low_v_scales[b, :, :M2].cpu().numpy())
     if tc.scores is not None:
-        st["scores"] = tc.scores[0 if tc.shared else b, :S + M + R].cpu().numpy()
+        st["scores"] = tc.scores[0 if tc.shared else b, :S + st["M2"] + M + R].cpu().numpy()
     return st
+
+
+def _same(name, got, want):
+    """Exact equality, with the first differing entries in the message."""
+    got, want = np.asarray(got), np.asarray(want)
+    if got.shape == want.shape and np.array_equal(got, want):
+        return
+    if got.shape != want.shape:
+        raise AssertionError(f"{name}: shape {got.shape} != {want.shape}")
+    idx = np.argwhere(got != want)
+    rows = [f"{tuple(int(x) for x in i)}: {got[tuple(i)]} != {want[tuple(i)]}" for i in idx[:6]]
+    raise AssertionError(f"{name}: {len(idx)} of {got.size} differ; " + "; ".join(rows))
 
 
 def assert_state_equal(st, ref, check_scores=True):
     c = ref.cfg
     assert (st["S"], st["M"], st["R"]) == (ref.n_sink_live, ref.mid_len, ref.rec_len)
-    assert np.array_equal(bits16(st["sink_k"]), bits16(ref.sink_k))
-    assert np.array_equal(bits16(st["sink_v"]), bits16(ref.sink_v))
-    assert np.array_equal(bits16(st["rec_v"]), bits16(ref.rec_v))
-    assert np.array_equal(bits16(st["rec_k"]), bits16(ref.rec_k))
-    assert np.array_equal(st["mid_k"], quant.pack(ref.mid_k_u, c.middle_k_bits))
-    assert np.array_equal(bits16(st["mid_ks"]), bits16(ref.mid_k_s))
-    assert np.array_equal(st["mid_v"], quant.pack(ref.mid_v_u, c.middle_v_bits))
-    assert np.array_equal(bits16(st["mid_vs"]), bits16(ref.mid_v_s))
+    _same("sink_k", bits16(st["sink_k"]), bits16(ref.sink_k))
+    _same("sink_v", bits16(st["sink_v"]), bits16(ref.sink_v))
+    _same("rec_v", bits16(st["rec_v"]), bits16(ref.rec_v))
+    _same("rec_k", bits16(st["rec_k"]), bits16(ref.rec_k))
+    _same("mid_k", st["mid_k"], quant.pack(ref.mid_k_u, c.middle_k_bits))
+    _same("mid_ks", bits16(st["mid_ks"]), bits16(ref.mid_k_s))
+    _same("mid_v", st["mid_v"], quant.pack(ref.mid_v_u, c.middle_v_bits))
+    _same("mid_vs", bits16(st["mid_vs"]), bits16(ref.mid_v_s))
+    assert st.get("M2", 0) == ref.low_len
+    if ref.low_len:
+        _same("low_k", st["low_k"], quant.pack(ref.low_k_u, 2))
+        _same("low_ks", bits16(st["low_ks"]), bits16(ref.low_k_s))
+        _same("low_v", st["low_v"], quant.pack(ref.low_v_u, 2))
+        _same("low_vs", bits16(st["low_vs"]), bits16(ref.low_v_s))
     if check_scores and "scores" in st and ref.scores is not None:
         assert np.array_equal(st["scores"].astype(np.float64), ref.scores)
 
 
-def build_both(cfg, batch, L, seed, cap_mid, scores32=None, shared=False):
+def build_both(cfg, batch, L, seed, cap_mid, scores32=None, shared=False, cap_low=None):
     """Build the same prefill on the GPU (fade_prefill_build) and in the
     oracle. scores32: float32 [rows, L] H2O scores (rows = 1 if shared)."""
     k16, v16, raw = prefill_inputs(cfg, batch, L, seed)
-    tc = fade.TieredCache(cfg, batch, cap_mid, shared=shared)
-    ws = fade.workspace(cfg, fade.WS_PREFILL_BUILD, batch, L)
+    tc = fade.TieredCache(cfg, batch, cap_mid, shared=shared, cap_low=cap_low)
+    ws = fade.workspace(cfg, fade.WS_PREFILL_BUILD, batch, L, cache=tc if cap_low is not None else None)
     sc_dev = None if scores32 is None else torch.from_numpy(np.ascontiguousarray(scores32, np.float32)).to(DEV)
     fade.fade_prefill_build(cfg, tc, dev16(k16), dev16(v16), L, sc_dev, ws)
     oc_cfg = ocfg(cfg)
@@ -284,3 +307,53 @@ def build_rerope_choices(ocfg_, k16, scores=None):
     if r and n_ev:
         ring = rerope_choices(k16[:, L - r:], np.arange(L - r, L), kept.size + s + np.arange(r), c)
     return mid, ring
+
+
+
+def follow_tier_event(r, kept_row, policy):
+    """The INT2-tier event (oracle.cache.evict_tiered) on the oracle side,
+    following the GPU's two choices read from its kept-slot output only where
+    they differ inside the near-tie band of the respective cutoff: which INT4
+    rows are demoted, and which of the old INT2 and demoted rows are dropped.
+    Returns True when the oracle had to follow."""
+    c = r.cfg
+    S, m4, m2, R = r.n_sink_live, r.mid_len, r.low_len, r.rec_len
+    n_dem = m4 - c.int4_budget if 0 <= c.int4_budget < m4 else 0
+    n_drop = max(0, m2 + n_dem - c.int2_budget)
+    m2n, m4n = m2 + n_dem - n_drop, m4 - n_dem
+    T2 = S + m2n + m4n + R
+    assert np.all(kept_row[T2:] == -1)
+    assert np.array_equal(kept_row[:S], np.arange(S))
+    assert np.array_equal(kept_row[S + m2n + m4n:T2], S + m2 + m4 + np.arange(R))
+    low_old = kept_row[S:S + m2n]
+    four_old = kept_row[S + m2n:S + m2n + m4n] - S - m2
+    assert np.all(np.diff(four_old) > 0)
+    gpu_dem = np.setdiff1d(np.arange(m4), four_old)
+    cand = np.concatenate([S + np.arange(m2), S + m2 + gpu_dem])
+    pos = {int(x): i for i, x in enumerate(cand)}
+    assert all(int(x) in pos for x in low_old)
+    kept_idx = np.array([pos[int(x)] for x in low_old], dtype=np.int64)
+    assert np.all(np.diff(kept_idx) > 0)
+    gpu_drop = np.setdiff1d(np.arange(cand.size), kept_idx)
+
+    def band_ok(keys, chosen, n):
+        if n == 0:
+            return chosen.size == 0
+        cut = np.sort(keys)[n - 1]
+        band = np.abs(keys - cut) <= NEAR * abs(cut)
+        below, above = np.nonzero((keys < cut) & ~band)[0], np.nonzero((keys > cut) & ~band)[0]
+        return chosen.size == n and np.all(np.isin(below, chosen)) and not np.any(np.isin(above, chosen))
+
+    sc = r.scores
+    key4 = np.arange(m4, dtype=np.float64) if policy == "position" else sc[S + m2:S + m2 + m4]
+    own_dem = oc.select_evicted(key4, n_dem)
+    followed = not np.array_equal(own_dem, gpu_dem)
+    if followed:
+        assert policy == "score" and band_ok(key4, gpu_dem, n_dem), (own_dem, gpu_dem)
+    keyc = cand.astype(np.float64) if policy == "position" else sc[cand]
+    own_drop = oc.select_evicted(keyc, n_drop)
+    if not np.array_equal(own_drop, gpu_drop):
+        assert policy == "score" and band_ok(keyc, gpu_drop, n_drop), (own_drop, gpu_drop)
+        followed = True
+    oc.evict_tiered(r, c.int4_budget, policy, demoted=gpu_dem, dropped=gpu_drop)
+    return followed

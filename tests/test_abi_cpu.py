@@ -32,7 +32,7 @@ def test_library_exports_every_header_function():
 
 def test_status_strings_and_version():
     lib = fade.lib()
-    assert lib.fade_abi_version() == 200
+    assert lib.fade_abi_version() == 300
     for s in range(6):
         assert lib.fade_status_string(s)
     assert lib.fade_status_string(99) == b"unknown status"
@@ -46,10 +46,13 @@ def _cfg(**kw):
 
 
 def test_struct_layout_matches_header():
-    # fade_config: 10 int32, 4 double, 4 int32 -> 10*4 (+0 pad) + 32 + 16 = 88
-    assert ctypes.sizeof(fade.FadeConfig) == 88
+    # fade_config: 10 int32, 4 double, 5 int32 -> 40 + 32 + 20 = 92, padded to 96
+    assert ctypes.sizeof(fade.FadeConfig) == 96
     assert fade.FadeConfig.rope_theta.offset == 40
-    assert ctypes.sizeof(fade.LayerCache) == 16 + 8 * 8
+    assert fade.FadeConfig.int2_budget.offset == 88
+    # fade_layer_cache: 4 int32, 8 pointers, 2 int32, 5 pointers
+    assert ctypes.sizeof(fade.LayerCache) == 16 + 8 * 8 + 8 + 5 * 8
+    assert fade.LayerCache.cap_low.offset == 80 and fade.LayerCache.low_lens.offset == 120
 
 
 @pytest.mark.parametrize("d,hkv,kb,vb", [(128, 8, 4, 2), (64, 8, 4, 4), (128, 2, 2, 2)])
@@ -70,6 +73,30 @@ def test_workspace_sizes_positive_and_monotone():
         assert 0 < a <= b
     bad = _cfg(head_dim=96)
     assert fade.workspace_bytes(bad, fade.WS_DECODE, 1, 10) == 0
+
+
+def test_cache_workspace_sizes_follow_the_cache():
+    """fade_cache_workspace_bytes sizes from the cache's own capacities: equal
+    to the capacity-keyed query where the cache has the shape that query
+    assumes (cap_low = int2_budget), larger where the INT2 tier holds more
+    rows, 0 for an invalid cache. Host arithmetic only."""
+    for i2 in (-1, 24):
+        cfg = _cfg(int4_budget=100, int2_budget=i2)
+        low = i2 >= 0
+        for cap_low in ((24, 40) if low else (0,)):
+            cap_T = 4 + 128 + cap_low + 65
+            ptrs = (16, 16, 16, 16, 16, 16, 16, None, cap_low, 0) + ((16, 16, 16, 16, 16) if low else
+                                                                    (None, None, None, None, None))
+            c = fade.LayerCache(3, 128, cap_T, 0, *ptrs)
+            for op in (fade.WS_DECODE, fade.WS_EVICT):
+                got = int(fade.lib().fade_cache_workspace_bytes(ctypes.byref(cfg), ctypes.byref(c), op, 0))
+                want = fade.workspace_bytes(cfg, op, 3, 128)
+                assert (got == want) if cap_low in (0, 24) else (got > want), (i2, cap_low, op, got, want)
+            got = int(fade.lib().fade_cache_workspace_bytes(ctypes.byref(cfg), ctypes.byref(c),
+                                                             fade.WS_PREFILL_BUILD, 500))
+            assert got > 0
+    bad = fade.LayerCache(3, 128, 999, 0, 16, 16, 16, 16, 16, 16, 16, None)
+    assert fade.lib().fade_cache_workspace_bytes(ctypes.byref(_cfg()), ctypes.byref(bad), fade.WS_DECODE, 0) == 0
 
 
 def test_validation_rejects_before_launch():
@@ -126,6 +153,19 @@ def test_validation_rejects_before_launch():
     # score policy without a score array
     st = lib.fade_evict_rerope(ctypes.byref(cfg), ctypes.byref(c), fade.POLICY_SCORE, 0, null, null, 0, null)
     assert st == fade.FADE_ERR_INVALID_ARG
+    # INT2 overflow tier: needs an INT4 budget, a capacity of at least its
+    # budget, and cap_T counting its rows
+    bad = _cfg(int4_budget=-1, int2_budget=10)
+    assert lib.fade_rope_rotate(ctypes.byref(bad), null, 0, 1, null, 0, 1, null) == fade.FADE_ERR_INVALID_ARG
+    cfg2 = _cfg(int4_budget=10, int2_budget=20)
+    c2 = fade.LayerCache(1, 10, 4 + 10 + 19 + 65, 0, 16, 16, 16, 16, 16, 16, 16, None, 19, 0, 16, 16, 16, 16, 16)
+    assert lib.fade_cache_demote(ctypes.byref(cfg2), ctypes.byref(c2), null) == fade.FADE_ERR_CAPACITY
+    c2 = fade.LayerCache(1, 10, 4 + 10 + 65, 0, 16, 16, 16, 16, 16, 16, 16, None, 20, 0, 16, 16, 16, 16, 16)
+    assert lib.fade_cache_demote(ctypes.byref(cfg2), ctypes.byref(c2), null) == fade.FADE_ERR_INVALID_ARG
+    c2 = fade.LayerCache(1, 10, 4 + 10 + 20 + 65, 0, 16, 16, 16, 16, 16, 16, 16, None, 20, 0, 16, 16, 18, 16, 16)
+    assert lib.fade_cache_demote(ctypes.byref(cfg2), ctypes.byref(c2), null) == fade.FADE_ERR_INVALID_ARG
+    c2 = fade.LayerCache(1, 10, 4 + 10 + 20 + 65, 0, 16, 16, 16, 16, 16, 16, 16, None, 20, 0, 16, 16, 16, 16, None)
+    assert lib.fade_cache_demote(ctypes.byref(cfg2), ctypes.byref(c2), null) == fade.FADE_ERR_INVALID_ARG
     # misaligned kept-slot output
     st = lib.fade_evict_rerope(ctypes.byref(cfg), ctypes.byref(c), fade.POLICY_POSITION, 0, ctypes.c_void_p(18),
                                null, 0, null)

@@ -45,10 +45,12 @@ int check_cfg(const fade_config* c) {
   if (c->q_dtype != FADE_DTYPE_F16 && c->q_dtype != FADE_DTYPE_BF16) return FADE_ERR_UNSUPPORTED;
   if (c->out_dtype != FADE_DTYPE_F16 && c->out_dtype != FADE_DTYPE_BF16 && c->out_dtype != FADE_DTYPE_F32)
     return FADE_ERR_UNSUPPORTED;
+  // the INT2 overflow tier takes the INT4 tier's overflow, so it needs a budget
+  if (c->int2_budget < -1 || (c->int2_budget >= 0 && c->int4_budget < 0)) return FADE_ERR_INVALID_ARG;
   return FADE_OK;
 }
 
-Shape make_shape(const fade_config* c, int batch, int cap_mid, int cap_T, int shared) {
+Shape make_shape(const fade_config* c, int batch, int cap_mid, int cap_T, int shared, int cap_low) {
   Shape s;
   s.D = c->head_dim;
   s.Hq = c->n_q_heads;
@@ -64,13 +66,33 @@ Shape make_shape(const fade_config* c, int batch, int cap_mid, int cap_T, int sh
   s.cap_mid = cap_mid;
   s.cap_T = cap_T;
   s.shared = shared;
+  s.low = c->int2_budget >= 0 ? 1 : 0;
+  s.low_budget = s.low ? c->int2_budget : 0;
+  s.cap_low = s.low ? cap_low : 0;
   return s;
 }
+Shape cache_shape(const fade_config* c, const fade_layer_cache* k) {
+  return make_shape(c, k->batch, k->cap_mid, k->cap_T, k->shared, k->cap_low);
+}
+// rows of the INT2 tier a workspace is sized for when no cache is at hand
+int ws_cap_low(const fade_config* c) { return c->int2_budget > 0 ? c->int2_budget : (c->int2_budget == 0 ? 1 : 0); }
 
 int check_cache(const fade_config* c, const fade_layer_cache* k) {
   if (!k) return FADE_ERR_INVALID_ARG;
   if (k->batch <= 0 || k->cap_mid < 0) return FADE_ERR_INVALID_ARG;
-  if (k->cap_T != c->n_sink + k->cap_mid + c->recent_window + 1) return FADE_ERR_INVALID_ARG;
+  const int low = c->int2_budget >= 0;
+  if (low && (k->cap_low < c->int2_budget || k->cap_low < 0)) return FADE_ERR_CAPACITY;
+  if (k->cap_T != c->n_sink + k->cap_mid + (low ? k->cap_low : 0) + c->recent_window + 1) return FADE_ERR_INVALID_ARG;
+  if (low) {
+    if (!k->low_lens || !aligned(k->low_lens, 4)) return FADE_ERR_INVALID_ARG;
+    if (k->cap_low > 0) {
+      const uintptr_t sa = c->head_dim == 128 ? 8 : 4;
+      if (!k->low_k_codes || !k->low_v_codes || !aligned16(k->low_k_codes) || !aligned16(k->low_v_codes))
+        return FADE_ERR_INVALID_ARG;
+      if (!k->low_k_scales || !k->low_v_scales || !aligned(k->low_k_scales, sa) || !aligned(k->low_v_scales, sa))
+        return FADE_ERR_INVALID_ARG;
+    }
+  }
   if (k->shared != 0 && k->shared != 1) return FADE_ERR_INVALID_ARG;
   if (!k->fp_k || !k->fp_v || !aligned16(k->fp_k) || !aligned16(k->fp_v)) return FADE_ERR_INVALID_ARG;
   if (!k->lens || !aligned(k->lens, 4)) return FADE_ERR_INVALID_ARG;
@@ -163,7 +185,7 @@ const char* fade_status_string(int status) {
   }
 }
 
-int fade_abi_version(void) { return 200; }
+int fade_abi_version(void) { return 300; }
 
 int fade_quantize_pack(const fade_config* cfg, const void* src, int64_t n_rows, int64_t src_row_stride,
                        const int32_t* src_row_idx, const int32_t* dst_row_idx, int32_t bits, void* codes,
@@ -187,7 +209,7 @@ int fade_cache_append(const fade_config* cfg, fade_layer_cache* cache, const voi
   if (st) return st;
   if ((st = check_cache(cfg, cache))) return st;
   if (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new)) return FADE_ERR_INVALID_ARG;
-  const Shape s = make_shape(cfg, cache->batch, cache->cap_mid, cache->cap_T, cache->shared);
+  const Shape s = cache_shape(cfg, cache);
   return hip_status(launch_append(s, *cache, reinterpret_cast<const uint16_t*>(k_new),
                                   reinterpret_cast<const uint16_t*>(v_new), reinterpret_cast<hipStream_t>(stream)));
 }
@@ -196,7 +218,7 @@ int fade_cache_demote(const fade_config* cfg, fade_layer_cache* cache, void* str
   int st = check_cfg(cfg);
   if (st) return st;
   if ((st = check_cache(cfg, cache))) return st;
-  const Shape s = make_shape(cfg, cache->batch, cache->cap_mid, cache->cap_T, cache->shared);
+  const Shape s = cache_shape(cfg, cache);
   return hip_status(launch_demote(s, *cache, reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -207,7 +229,7 @@ int fade_tiered_decode_attn(const fade_config* cfg, const fade_layer_cache* cach
   if ((st = check_cache(cfg, cache))) return st;
   if (!q || !out || !aligned16(q) || !aligned16(out)) return FADE_ERR_INVALID_ARG;
   if (tok_attn && !aligned(tok_attn, 4)) return FADE_ERR_INVALID_ARG;
-  const Shape s = make_shape(cfg, cache->batch, cache->cap_mid, cache->cap_T, cache->shared);
+  const Shape s = cache_shape(cfg, cache);
   if (!workspace || !aligned16(workspace) || ws_bytes < decode_ws_bytes(s)) return FADE_ERR_WORKSPACE;
   return hip_status(launch_decode(s, *cache, q, cfg->q_dtype == FADE_DTYPE_BF16, out, cfg->out_dtype, tok_attn,
                                   workspace, reinterpret_cast<hipStream_t>(stream)));
@@ -220,7 +242,7 @@ int fade_tiered_decode_attn_noalloc(const fade_config* cfg, const fade_layer_cac
   if ((st = check_cache(cfg, cache))) return st;
   if (!q || !out || !aligned16(q) || !aligned16(out)) return FADE_ERR_INVALID_ARG;
   if (tok_attn && !aligned(tok_attn, 4)) return FADE_ERR_INVALID_ARG;
-  const Shape s = make_shape(cfg, cache->batch, cache->cap_mid, cache->cap_T, cache->shared);
+  const Shape s = cache_shape(cfg, cache);
   if (decode_ws_bytes(s) > kNoAllocScratchBytes) return FADE_ERR_WORKSPACE;
   void* ws = nullptr;
   const hipError_t e = noalloc_scratch(&ws);
@@ -250,7 +272,7 @@ int fade_h2o_scores(const fade_config* cfg, int32_t mode, fade_layer_cache* cach
   if ((st = check_cache(cfg, cache))) return st;
   if (!cache->scores || !tok_attn) return FADE_ERR_INVALID_ARG;
   if (mode == FADE_SCORE_EMA && !(decay >= 0.f && decay <= 1.f)) return FADE_ERR_INVALID_ARG;
-  const Shape s = make_shape(cfg, cache->batch, cache->cap_mid, cache->cap_T, cache->shared);
+  const Shape s = cache_shape(cfg, cache);
   return hip_status(launch_score_update(s, *cache, mode, tok_attn, decay, hs));
 }
 
@@ -262,10 +284,16 @@ int fade_evict_rerope(const fade_config* cfg, fade_layer_cache* cache, int32_t p
   if (policy != FADE_POLICY_SCORE && policy != FADE_POLICY_POSITION) return FADE_ERR_INVALID_ARG;
   if (policy == FADE_POLICY_SCORE && !cache->scores) return FADE_ERR_INVALID_ARG;
   if (kept_slots_out && !aligned(kept_slots_out, 4)) return FADE_ERR_INVALID_ARG;
+  const Shape s = cache_shape(cfg, cache);
+  if (s.low) {
+    // INT2 overflow tier: demote the INT4 overflow, drop the INT2 overflow
+    if (!workspace || !aligned16(workspace) || ws_bytes < tier_event_ws_bytes(s)) return FADE_ERR_WORKSPACE;
+    return hip_status(launch_tier_event(s, *cache, policy, host_freqs(cfg), kept_slots_out, workspace,
+                                        reinterpret_cast<hipStream_t>(stream)));
+  }
   // No event can run (never evict, or no middle slot over the budget fits
   // the capacity): every survivor keeps its slot.
   const int me = cfg->int4_budget < 0 ? 0 : decode_max_evict(cfg, cache, max_evict);
-  const Shape s = make_shape(cfg, cache->batch, cache->cap_mid, cache->cap_T, cache->shared);
   if (me == 0) {
     if (!kept_slots_out) return FADE_OK;
     return hip_status(launch_kept_identity(s, *cache, kept_slots_out, reinterpret_cast<hipStream_t>(stream)));
@@ -290,7 +318,10 @@ int fade_prefill_build(const fade_config* cfg, fade_layer_cache* cache, const vo
   const int Mc = L - S - R;
   const int Mk = (cfg->int4_budget >= 0 && Mc > cfg->int4_budget) ? cfg->int4_budget : Mc;
   if (Mk > cache->cap_mid) return FADE_ERR_CAPACITY;
-  const Shape s = make_shape(cfg, cache->batch, cache->cap_mid, cache->cap_T, cache->shared);
+  // with the INT2 tier and H2O prefill scores the demotion ranks by the
+  // scores the build stores
+  if (cfg->int2_budget >= 0 && prefill_scores && !cache->scores) return FADE_ERR_INVALID_ARG;
+  const Shape s = cache_shape(cfg, cache);
   if (!workspace || !aligned16(workspace) || ws_bytes < prefill_build_ws_bytes(s, L)) return FADE_ERR_WORKSPACE;
   return hip_status(launch_prefill_build(s, *cache, reinterpret_cast<const uint16_t*>(k_prefill),
                                          reinterpret_cast<const uint16_t*>(v_prefill), L, prefill_scores,
@@ -313,18 +344,40 @@ int fade_rope_rotate(const fade_config* cfg, void* x, int32_t dtype, int64_t n_r
 
 size_t fade_workspace_bytes(const fade_config* cfg, int32_t op, int32_t batch, int32_t max_len) {
   if (check_cfg(cfg) || batch <= 0 || max_len < 0) return 0;
-  const int cap_T = cfg->n_sink + max_len + cfg->recent_window + 1;
+  const int cap_low = ws_cap_low(cfg);
+  const int cap_T = cfg->n_sink + max_len + cap_low + cfg->recent_window + 1;
   switch (op) {
     case FADE_WS_DECODE:
-      return decode_ws_bytes(make_shape(cfg, batch, max_len, cap_T, 0));
+      return decode_ws_bytes(make_shape(cfg, batch, max_len, cap_T, 0, cap_low));
     case FADE_WS_H2O_PREFILL:
       return h2o_ws_bytes(cfg->head_dim, cfg->n_q_heads, cfg->n_kv_heads, batch, max_len);
     case FADE_WS_EVICT: {
+      const Shape s = make_shape(cfg, batch, max_len, cap_T, 0, cap_low);
+      if (s.low) return tier_event_ws_bytes(s);
       const int full = cfg->int4_budget >= 0 ? max_len - cfg->int4_budget : 0;
-      return evict_ws_bytes(make_shape(cfg, batch, max_len, cap_T, 0), full > 0 ? full : 1);
+      return evict_ws_bytes(s, full > 0 ? full : 1);
     }
     case FADE_WS_PREFILL_BUILD:
-      return prefill_build_ws_bytes(make_shape(cfg, batch, 0, cap_T, 0), max_len);
+      return prefill_build_ws_bytes(make_shape(cfg, batch, 0, cap_T, 0, cap_low), max_len);
+    default:
+      return 0;
+  }
+}
+
+size_t fade_cache_workspace_bytes(const fade_config* cfg, const fade_layer_cache* cache, int32_t op,
+                                  int32_t max_len) {
+  if (check_cfg(cfg) || check_cache(cfg, cache) || max_len < 0) return 0;
+  const Shape s = cache_shape(cfg, cache);
+  switch (op) {
+    case FADE_WS_DECODE:
+      return decode_ws_bytes(s);
+    case FADE_WS_EVICT: {
+      if (s.low) return tier_event_ws_bytes(s);
+      const int me = cfg->int4_budget < 0 ? 0 : decode_max_evict(cfg, cache, 0);
+      return me > 0 ? evict_ws_bytes(s, me) : 0;
+    }
+    case FADE_WS_PREFILL_BUILD:
+      return prefill_build_ws_bytes(s, max_len);
     default:
       return 0;
   }

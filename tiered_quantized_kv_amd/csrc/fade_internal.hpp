@@ -25,7 +25,10 @@ struct Shape {
   int n_sink, W, ring;        // ring = W + 1
   int budget, kb, vb;
   int batch, cap_mid, cap_T, shared;
+  int low;                    // 1: the INT2 overflow tier is on
+  int low_budget, cap_low;    // its capacity after an event, and its rows
 };
+constexpr int kLowBits = 2;   // K and V bits of the INT2 overflow tier
 
 // ---- quantize / append / demote (k_quant.hip) -------------------------------
 hipError_t launch_quantize_rows(int D, int bits, const uint16_t* src, int64_t n_rows,
@@ -61,6 +64,10 @@ size_t evict_ws_bytes(const Shape& s, int max_evict);
 hipError_t launch_evict(const Shape& s, const fade_layer_cache& c, int policy, int max_evict,
                         const RopeFreqs& fr, int32_t* kept_slots, void* ws, hipStream_t st);
 hipError_t launch_kept_identity(const Shape& s, const fade_layer_cache& c, int32_t* kept, hipStream_t st);
+// the INT2 overflow tier's event (demote the INT4 overflow, drop the INT2 overflow)
+size_t tier_event_ws_bytes(const Shape& s);
+hipError_t launch_tier_event(const Shape& s, const fade_layer_cache& c, int policy, const RopeFreqs& fr,
+                             int32_t* kept, void* ws, hipStream_t st);
 size_t prefill_build_ws_bytes(const Shape& s, int L);
 hipError_t launch_prefill_build(const Shape& s, const fade_layer_cache& c, const uint16_t* k,
                                 const uint16_t* v, int L, const float* scores,

@@ -53,6 +53,15 @@ struct DecodeArgs {
   int batch, Hkv, n_sink, ring, cap_mid, cap_T, raw_stride, nsplit;
   int n_fp, fp_per;   // fp16-tier splits (0 .. n_fp - 1) and fp16 slots per split
   float qk_scale;     // log2(e) / sqrt(D)
+  // The packed tier this launch streams: the INT4 middle (length lens[4b+1])
+  // or the INT2 overflow tier (low_lens[b]); n_tier splits of it, whose
+  // partials go to splits split0 + n_fp ... The INT2 tier's slots come right
+  // after the sinks, the INT4 middle's after the INT2 tier.
+  const int32_t* tier_len;
+  int tier_len_stride;
+  const int32_t* low_lens;    // nullptr without an INT2 tier
+  int cap_low;                // its row capacity
+  int is_low, split0, n_tier;
 };
 
 constexpr int kThreads = 256;
@@ -95,7 +104,16 @@ int decode_fp_splits(const Shape& s) {
   return (int)(n < 1 ? 1 : (n > 4 ? 4 : n));
 }
 
-int decode_nsplit(const Shape& s) { return decode_fp_splits(s) + decode_mid_splits(s); }
+// Splits of the INT2 overflow tier: the same rule over its row capacity (the
+// kernel cuts the live length evenly, as for the middle tier).
+int decode_low_splits(const Shape& s) {
+  if (!s.low || s.cap_low <= 0) return 0;
+  Shape t = s;
+  t.cap_mid = s.cap_low;
+  return decode_mid_splits(t);
+}
+
+int decode_nsplit(const Shape& s) { return decode_fp_splits(s) + decode_mid_splits(s) + decode_low_splits(s); }
 
 // Raw scores of one query head: cap_T slots, then kSub pad entries that the
 // lanes past a split's last token write instead (their stores stay
@@ -239,20 +257,23 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
   // gaps.
   const int n_pairs = a.batch * a.Hkv;
   const int gsplit = blockIdx.x / n_pairs, pair = blockIdx.x - gsplit * n_pairs;
-  const int n_mid_splits = a.nsplit - a.n_fp;
-  const int split = gsplit < n_mid_splits ? gsplit + a.n_fp : gsplit - n_mid_splits;
+  const int n_mid_splits = a.n_tier;
+  const int lsplit = gsplit < n_mid_splits ? gsplit + a.n_fp : gsplit - n_mid_splits;   // this launch's
+  const int split = a.split0 + lsplit;                                                  // in the partials
   const int g = pair % a.Hkv, b = pair / a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int Hq = a.Hkv * NREP;
   const int32_t* L = a.lens + 4 * b;
   // Lengths are clamped to capacity so no value in lens can index out of bounds.
-  const int S = min(max(L[0], 0), a.n_sink), M = min(max(L[1], 0), a.cap_mid);
+  const int S = min(max(L[0], 0), a.n_sink), M = min(max(a.tier_len[(size_t)b * a.tier_len_stride], 0), a.cap_mid);
   const int R = min(max(L[2], 0), a.ring), rhead = min(max(L[3], 0), a.ring - 1);
-  const bool fpt = split < a.n_fp;                   // FP16 tier
+  const int M2 = a.low_lens ? min(max(a.low_lens[b], 0), a.cap_low) : 0;   // INT2 slots before the INT4 middle
+  const int mbase = S + (a.is_low ? 0 : M2);                // slot of this tier's row 0
+  const bool fpt = lsplit < a.n_fp;                   // FP16 tier
   // middle split: an equal share of the live rows, in whole sub-chunks
   const int per = ((M + n_mid_splits - 1) / n_mid_splits + kSub - 1) / kSub * kSub;
-  const int row0 = fpt ? 0 : (split - a.n_fp) * per;
-  const int fp_lo = fpt ? split * a.fp_per : 0;     // this split's fp16 tokens [fp_lo, fp_lo + n_tok)
+  const int row0 = fpt ? 0 : (lsplit - a.n_fp) * per;
+  const int fp_lo = fpt ? lsplit * a.fp_per : 0;     // this split's fp16 tokens [fp_lo, fp_lo + n_tok)
   const int n_tok = fpt ? min(a.fp_per, S + R - fp_lo) : min(per, M - row0);
 
   float* part_base = a.part + ((size_t)(b * Hq + g * NREP) * a.nsplit + split) * (D + 2);
@@ -468,7 +489,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
 #pragma unroll
       for (int h = 0; h < HQ4 * 4; ++h) {
         s2[h] = valid ? s2[h] * kf[h] : -INFINITY;
-        if (SIDE && h < NREP) rawb[(size_t)h * a.raw_stride + (valid ? S + row0 + t : a.cap_T + lane)] = s2[h];
+        if (SIDE && h < NREP) rawb[(size_t)h * a.raw_stride + (valid ? mbase + row0 + t : a.cap_T + lane)] = s2[h];
       }
       // ---- softmax ----
       float p[HQ4 * 4];
@@ -586,7 +607,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
       load_v(0, min(VB32, ns));
       float s2[HQ4 * 4];
       const int tv = fp_lo + base + lane;
-      const int pos = tv < S ? tv : S + M + (tv - S);
+      const int pos = tv < S ? tv : S + M2 + M + (tv - S);
 #pragma unroll
       for (int h = 0; h < HQ4 * 4; ++h) {
         s2[h] = valid ? (d0[h / 4][h % 4] + d1[h / 4][h % 4]) * kf[h] : -INFINITY;
@@ -692,7 +713,8 @@ template <int D, int LN>
 __global__ __launch_bounds__(256) void k_decode_finish(const float* __restrict__ part, int nsplit, int Hq,
                                                        void* out, int out_dtype,
                                                        const float* __restrict__ raw, int raw_stride,
-                                                       const int32_t* __restrict__ lens, int cap_T,
+                                                       const int32_t* __restrict__ lens,
+                                                       const int32_t* __restrict__ low_lens, int cap_T,
                                                        float* __restrict__ tok_attn) {
   extern __shared__ float ml[];   // [Hq][2] = (M_h, 1 / L_h), then [4][kFinishSlots] partial sums
   const int b = blockIdx.x, j = blockIdx.y, nb = gridDim.y, tid = threadIdx.x;
@@ -761,7 +783,7 @@ __global__ __launch_bounds__(256) void k_decode_finish(const float* __restrict__
     }
   }
   if (!tok_attn) return;
-  const int T = lens[4 * b] + lens[4 * b + 1] + lens[4 * b + 2];
+  const int T = lens[4 * b] + lens[4 * b + 1] + lens[4 * b + 2] + (low_lens ? low_lens[b] : 0);
   float* red = ml + 2 * Hq;
   for (int j0 = j * kFinishSlots; j0 < cap_T; j0 += nb * kFinishSlots) {
     const int u0 = tid % kFinishSlots, jj = j0 + u0, hg = tid / kFinishSlots;
@@ -848,16 +870,47 @@ hipError_t launch_decode(const Shape& s, const fade_layer_cache& c, const void* 
   a.n_fp = decode_fp_splits(s);
   a.fp_per = (s.n_sink + s.ring + a.n_fp - 1) / a.n_fp;
   a.qk_scale = kLog2e / sqrtf((float)s.D);
-  const dim3 grid(nsplit * s.Hkv * s.batch);
-  if (s.D == 128) {
-    if (q_bf16) dispatch_rep<128, true>(s.n_rep, s.kb, s.vb, a, grid, st);
-    else dispatch_rep<128, false>(s.n_rep, s.kb, s.vb, a, grid, st);
-  } else {
-    if (q_bf16) dispatch_rep<64, true>(s.n_rep, s.kb, s.vb, a, grid, st);
-    else dispatch_rep<64, false>(s.n_rep, s.kb, s.vb, a, grid, st);
-  }
+  a.tier_len = c.lens + 1;
+  a.tier_len_stride = 4;
+  a.low_lens = s.low ? c.low_lens : nullptr;
+  a.cap_low = s.low ? s.cap_low : 0;
+  a.is_low = 0;
+  a.split0 = 0;
+  a.n_tier = decode_mid_splits(s);
+  const int n_main = a.n_fp + a.n_tier;
+  auto dispatch = [&](const DecodeArgs& da, int n_splits, int kb, int vb) {
+    const dim3 grid(n_splits * s.Hkv * s.batch);
+    if (s.D == 128) {
+      if (q_bf16) dispatch_rep<128, true>(s.n_rep, kb, vb, da, grid, st);
+      else dispatch_rep<128, false>(s.n_rep, kb, vb, da, grid, st);
+    } else {
+      if (q_bf16) dispatch_rep<64, true>(s.n_rep, kb, vb, da, grid, st);
+      else dispatch_rep<64, false>(s.n_rep, kb, vb, da, grid, st);
+    }
+  };
+  dispatch(a, n_main, s.kb, s.vb);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const int n_low = decode_low_splits(s);
+  if (n_low > 0) {
+    // the INT2 overflow tier: K and V at 2 bits, its own splits after the
+    // main launch's in the partials
+    DecodeArgs l = a;
+    l.kc = reinterpret_cast<const uint8_t*>(c.low_k_codes);
+    l.vc = reinterpret_cast<const uint8_t*>(c.low_v_codes);
+    l.ks = reinterpret_cast<const uint16_t*>(c.low_k_scales);
+    l.vs = reinterpret_cast<const uint16_t*>(c.low_v_scales);
+    l.cap_mid = s.cap_low;
+    l.tier_len = c.low_lens;
+    l.tier_len_stride = 1;
+    l.is_low = 1;
+    l.n_fp = 0;
+    l.split0 = n_main;
+    l.n_tier = n_low;
+    dispatch(l, n_low, kLowBits, kLowBits);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   // Workgroups per sequence. Each rebuilds the statistics (Hq x nsplit
   // partial heads), so their number follows the work that needs spreading:
   // with the side output, the slots (two 64-slot blocks per workgroup with
@@ -879,17 +932,17 @@ hipError_t launch_decode(const Shape& s, const fade_layer_cache& c, const void* 
   if (s.D == 128) {
     if (wide)
       hipLaunchKernelGGL((k_decode_finish<128, 8>), fgrid, dim3(256), flds, st, part, nsplit, s.Hq, out, out_dtype,
-                         raw, raw_stride, c.lens, s.cap_T, tok_attn);
+                         raw, raw_stride, c.lens, s.low ? c.low_lens : nullptr, s.cap_T, tok_attn);
     else
       hipLaunchKernelGGL((k_decode_finish<128, 1>), fgrid, dim3(256), flds, st, part, nsplit, s.Hq, out, out_dtype,
-                         raw, raw_stride, c.lens, s.cap_T, tok_attn);
+                         raw, raw_stride, c.lens, s.low ? c.low_lens : nullptr, s.cap_T, tok_attn);
   } else {
     if (wide)
       hipLaunchKernelGGL((k_decode_finish<64, 8>), fgrid, dim3(256), flds, st, part, nsplit, s.Hq, out, out_dtype,
-                         raw, raw_stride, c.lens, s.cap_T, tok_attn);
+                         raw, raw_stride, c.lens, s.low ? c.low_lens : nullptr, s.cap_T, tok_attn);
     else
       hipLaunchKernelGGL((k_decode_finish<64, 1>), fgrid, dim3(256), flds, st, part, nsplit, s.Hq, out, out_dtype,
-                         raw, raw_stride, c.lens, s.cap_T, tok_attn);
+                         raw, raw_stride, c.lens, s.low ? c.low_lens : nullptr, s.cap_T, tok_attn);
   }
   return hipGetLastError();
 }
@@ -928,11 +981,12 @@ hipError_t noalloc_scratch(void** ptr) {
 // ---- decode-time score update (ACCUM / EMA) ----------------------------------
 __global__ __launch_bounds__(256) void k_score_update(float* __restrict__ scores,
                                                       const float* __restrict__ tok_attn,
-                                                      const int32_t* __restrict__ lens, int batch,
+                                                      const int32_t* __restrict__ lens,
+                                                      const int32_t* __restrict__ low_lens, int batch,
                                                       int cap_T, int shared, int mode, float decay) {
   const int row = blockIdx.y;
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
-  const int T = lens[4 * row] + lens[4 * row + 1] + lens[4 * row + 2];
+  const int T = lens[4 * row] + lens[4 * row + 1] + lens[4 * row + 2] + (low_lens ? low_lens[row] : 0);
   if (j >= T || j >= cap_T) return;
   float a;
   if (shared) {
@@ -950,7 +1004,7 @@ hipError_t launch_score_update(const Shape& s, const fade_layer_cache& c, int mo
                                const float* tok_attn, float decay, hipStream_t st) {
   const int rows = s.shared ? 1 : s.batch;
   hipLaunchKernelGGL(k_score_update, dim3((s.cap_T + 255) / 256, rows), dim3(256), 0, st, c.scores,
-                     tok_attn, c.lens, s.batch, s.cap_T, s.shared, mode, decay);
+                     tok_attn, c.lens, s.low ? c.low_lens : nullptr, s.batch, s.cap_T, s.shared, mode, decay);
   return hipGetLastError();
 }
 

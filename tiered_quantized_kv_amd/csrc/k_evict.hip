@@ -1042,9 +1042,23 @@ hipError_t launch_evict(const Shape& s, const fade_layer_cache& c, int policy, i
 }
 
 // ---- prefill build -------------------------------------------------------------
+// With the INT2 overflow tier the build first keeps int4_budget + int2_budget
+// candidates in an INT4 staging copy in the workspace (the wide layout), then
+// the tier event demotes the lowest int2_budget of them straight into the
+// cache.
+size_t tier_event_ws_bytes_src(const Shape& s, int src_cap4, bool staged);
+static int wide_budget(const Shape& s) { return s.budget + s.low_budget; }
+static size_t wide_stage_bytes(const Shape& s) {
+  const size_t rows = (size_t)s.batch * s.Hkv * max(1, wide_budget(s));
+  return align_up(rows * s.D * s.kb / 8, 256) + align_up(rows * s.D * s.vb / 8, 256) +
+         2 * align_up(rows * (s.D / 32) * 2, 256);
+}
+
 size_t prefill_build_ws_bytes(const Shape& s, int L) {
   const int rows = s.shared ? 1 : s.batch;
-  return align_up((size_t)rows * kInfo * 4, 256) + align_up((size_t)rows * (L > 0 ? L : 1) * 4, 256);
+  size_t n = align_up((size_t)rows * kInfo * 4, 256) + align_up((size_t)rows * (L > 0 ? L : 1) * 4, 256);
+  if (s.low) n += wide_stage_bytes(s) + tier_event_ws_bytes_src(s, max(1, wide_budget(s)), false);
+  return n;
 }
 
 struct BuildArgs {
@@ -1161,7 +1175,7 @@ __global__ __launch_bounds__(256) void k_build(BuildArgs a) {
   }
 }
 
-__global__ void k_build_lens(const int32_t* info, int32_t* lens, int batch, int shared) {
+__global__ void k_build_lens(const int32_t* info, int32_t* lens, int32_t* low_lens, int batch, int shared) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= batch) return;
   const int r = shared ? 0 : b;
@@ -1169,6 +1183,7 @@ __global__ void k_build_lens(const int32_t* info, int32_t* lens, int batch, int 
   lens[4 * b + 1] = info[kInfo * r + 0] - info[kInfo * r + 1];
   lens[4 * b + 2] = info[kInfo * r + 3];
   lens[4 * b + 3] = 0;
+  if (low_lens) low_lens[b] = 0;
 }
 
 template <int D>
@@ -1180,14 +1195,43 @@ static void launch_build_d(const BuildArgs& a, dim3 grid, hipStream_t st) {
   else hipLaunchKernelGGL((k_build<D, 2, 2>), grid, dim3(256), 0, st, a);
 }
 
-hipError_t launch_prefill_build(const Shape& s, const fade_layer_cache& c, const uint16_t* k,
+hipError_t launch_tier_event_from(const Shape& s, const fade_layer_cache& c, int policy, const RopeFreqs& fr,
+                                  const uint8_t* kc, const uint8_t* vc, const uint16_t* ks, const uint16_t* vs,
+                                  int src_cap4, void* ws, hipStream_t st);
+
+hipError_t launch_prefill_build(const Shape& s0, const fade_layer_cache& c0, const uint16_t* k,
                                 const uint16_t* v, int L, const float* scores, const RopeFreqs& fr,
                                 void* ws, hipStream_t st) {
-  const int rows = s.shared ? 1 : s.batch;
+  const int rows = s0.shared ? 1 : s0.batch;
   char* w = reinterpret_cast<char*>(ws);
   int32_t* info = reinterpret_cast<int32_t*>(w);
   w += align_up((size_t)rows * kInfo * 4, 256);
   int32_t* map = reinterpret_cast<int32_t*>(w);
+  w += align_up((size_t)rows * (L > 0 ? L : 1) * 4, 256);
+  // with the INT2 tier: build the wide layout into staging rows
+  Shape s = s0;
+  fade_layer_cache c = c0;
+  uint8_t *wkc = nullptr, *wvc = nullptr;
+  uint16_t *wks = nullptr, *wvs = nullptr;
+  if (s0.low) {
+    const int wide = max(1, wide_budget(s0));
+    const size_t rws = (size_t)s0.batch * s0.Hkv * wide;
+    wkc = reinterpret_cast<uint8_t*>(w);
+    w += align_up(rws * s0.D * s0.kb / 8, 256);
+    wvc = reinterpret_cast<uint8_t*>(w);
+    w += align_up(rws * s0.D * s0.vb / 8, 256);
+    wks = reinterpret_cast<uint16_t*>(w);
+    w += align_up(rws * (s0.D / 32) * 2, 256);
+    wvs = reinterpret_cast<uint16_t*>(w);
+    w += align_up(rws * (s0.D / 32) * 2, 256);
+    s.budget = wide_budget(s0);
+    s.cap_mid = wide;
+    c.cap_mid = wide;
+    c.mid_k_codes = wkc;
+    c.mid_v_codes = wvc;
+    c.mid_k_scales = wks;
+    c.mid_v_scales = wvs;
+  }
   SelectArgs sa{};
   sa.scores = scores;
   sa.score_stride = L;
@@ -1222,9 +1266,14 @@ hipError_t launch_prefill_build(const Shape& s, const fade_layer_cache& c, const
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(k_build_lens, dim3((s.batch + 63) / 64), dim3(64), 0, st, info, c.lens, s.batch,
+  hipLaunchKernelGGL(k_build_lens, dim3((s.batch + 63) / 64), dim3(64), 0, st, info, c.lens,
+                     s0.low ? c0.low_lens : nullptr, s.batch,
                      s.shared);
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess || !s0.low) return e;
+  // demote the wide layout's lowest int2_budget into the INT2 tier
+  return launch_tier_event_from(s0, c0, scores ? FADE_POLICY_SCORE : FADE_POLICY_POSITION, fr, wkc, wvc, wks, wvs,
+                                max(1, wide_budget(s0)), w, st);
 }
 
 // ---- RoPE rotation of rows (caller's q / new key) --------------------------------
@@ -1254,6 +1303,510 @@ hipError_t launch_rope_rotate(int D, uint16_t* x, int bf16, int64_t n_rows, cons
   hipLaunchKernelGGL(k_rope_rotate, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, D, x, bf16,
                      n_rows, positions, pos_base, pos_period, fr);
   return hipGetLastError();
+}
+
+
+// ---- INT2 overflow tier: demote the INT4 overflow, drop the INT2 overflow -----------
+//
+// FADE post, "第三层：INT2深度压缩（可选）" read with "驱逐策略": when the INT4
+// middle tier holds more than int4_budget rows, the rows the policy would
+// evict are demoted into the INT2 tier instead (keys dequantized, rotated to
+// their new slot, rounded once to fp16 and quantized at 2 bits; values
+// dequantized, rounded to fp16 and quantized at 2 bits); only the INT2 tier's
+// overflow over int2_budget is evicted. Slot order: sinks | INT2 | INT4 |
+// recent. Demoted rows join the INT2 tier's end in their INT4 order.
+//
+// k_tier_select (one workgroup per score row) ranks with exact 64-bit keys
+// (order-preserving score bits << 32 | slot; the slot alone for the position
+// policy), so every key is unique and an 8-pass radix select gives the exact
+// (score ascending, slot ascending) cut. It writes the row's plan (the source
+// of every new INT2 and INT4 row), moves the scores to their new slots and
+// records the kept slots. k_tier_move (one wave per new row and KV head)
+// rebuilds each row into a staging copy (or straight into the cache when the
+// sources are elsewhere, as after a prefill build) and re-rotates the recent
+// ring in place; k_tier_copy copies the staging rows back and writes the new
+// lengths. Not on the serving workload's per-step path: written for
+// exactness, not speed.
+
+constexpr int kTierInfo = 8;   // {S, M4, M2, R, M4n, M2n, n_dem, n_drop}
+
+struct TierArgs {
+  Shape s;
+  fade_layer_cache c;          // the cache (lengths, fp16 tier, scores, destinations)
+  int policy;
+  // sources of the INT4 rows (the cache's middle tier, or a prefill staging
+  // copy with its own row capacity) and of the INT2 rows (the cache's)
+  const uint8_t* src_kc;
+  const uint8_t* src_vc;
+  const uint16_t* src_ks;
+  const uint16_t* src_vs;
+  int src_cap4;
+  // destinations of the rebuilt rows
+  uint8_t *dst_kc, *dst_vc, *dst_lkc, *dst_lvc;
+  uint16_t *dst_ks, *dst_vs, *dst_lks, *dst_lvs;
+  int dst_cap4, dst_capl;
+  int32_t* info;               // [rows][kTierInfo]
+  int32_t* lsrc;               // [rows][plan_l]: new INT2 row j's source (>= 0 INT2 row, -1 - i INT4 row i)
+  int32_t* i4src;              // [rows][plan_4]: new INT4 row i's source INT4 row
+  int plan_l, plan_4;
+  float* score_tmp;            // [rows][cap_T]
+  int32_t* kept;               // optional [rows][cap_T]
+  RopeFreqs fr;
+};
+
+// k smallest of n unique 64-bit keys: returns the k-th smallest (keys <= it
+// are the k smallest). k >= 1. Radix select, 8 bits per pass, LDS histogram.
+template <typename KeyF>
+__device__ unsigned long long kth_smallest_u64(KeyF key, int n, int k, uint32_t* hist, unsigned long long* s_pref,
+                                               int* s_k) {
+  const int tid = threadIdx.x;
+  unsigned long long prefix = 0ull, mask = 0ull;
+  int kk = k;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 256; i += blockDim.x) hist[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += blockDim.x) {
+      const unsigned long long kv = key(i);
+      if ((kv & mask) == prefix) atomicAdd(&hist[(kv >> shift) & 255ull], 1u);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int cum = 0, d = 0;
+      while (cum + (int)hist[d] < kk) {
+        cum += (int)hist[d];
+        ++d;
+      }
+      *s_pref = prefix | ((unsigned long long)d << shift);
+      *s_k = kk - cum;
+    }
+    __syncthreads();
+    prefix = *s_pref;
+    kk = *s_k;
+    mask |= 255ull << shift;
+    __syncthreads();
+  }
+  return prefix;
+}
+
+__global__ __launch_bounds__(kSelThreads) void k_tier_select(TierArgs a) {
+  __shared__ uint32_t hist[256];
+  __shared__ int wsum[17];
+  __shared__ unsigned long long s_pref;
+  __shared__ int s_k;
+  const Shape& s = a.s;
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const int32_t* L = a.c.lens + 4 * row;     // a shared cache reads sequence 0
+  const int S = min(max(L[0], 0), s.n_sink), M4 = min(max(L[1], 0), a.src_cap4);
+  const int R = min(max(L[2], 0), s.ring), M2 = min(max(a.c.low_lens[row], 0), s.cap_low);
+  const int n_dem = s.budget >= 0 && M4 > s.budget ? M4 - s.budget : 0;
+  const int n_drop = max(0, M2 + n_dem - s.low_budget);
+  const int M4n = M4 - n_dem, M2n = M2 + n_dem - n_drop;
+  float* sc = a.c.scores ? a.c.scores + (size_t)row * s.cap_T : nullptr;
+  const bool by_pos = a.policy == FADE_POLICY_POSITION || !sc;
+  // the old score row is copied first: the keys are read from the copy while
+  // the new row is written in place
+  const int T_old = S + M2 + M4 + R;
+  float* tmp = a.score_tmp + (size_t)row * s.cap_T;
+  if (sc)
+    for (int j = tid; j < T_old; j += blockDim.x) tmp[j] = sc[j];
+  __syncthreads();
+  auto key_at = [&](int slot) -> unsigned long long {
+    return by_pos ? (unsigned long long)slot : ((unsigned long long)ordered_key(tmp[slot]) << 32) | (unsigned)slot;
+  };
+  // stage 1: the n_dem lowest INT4 rows are demoted
+  unsigned long long thr4 = 0ull;
+  if (n_dem > 0) thr4 = kth_smallest_u64([&](int i) { return key_at(S + M2 + i); }, M4, n_dem, hist, &s_pref, &s_k);
+  auto demoted = [&](int i) { return n_dem > 0 && key_at(S + M2 + i) <= thr4; };
+  // stage 2: among the old INT2 rows and the demoted ones, the n_drop lowest
+  // are dropped (every candidate key is unique; non-candidates never count)
+  unsigned long long thrc = 0ull;
+  if (n_drop > 0) {
+    const unsigned long long none = ~0ull;
+    thrc = kth_smallest_u64(
+        [&](int i) { return i < M2 ? key_at(S + i) : (demoted(i - M2) ? key_at(S + M2 + (i - M2)) : none); },
+        M2 + M4, n_drop, hist, &s_pref, &s_k);
+  }
+  auto dropped_key = [&](unsigned long long k) { return n_drop > 0 && k <= thrc; };
+  // new INT2 rows: kept candidates in order (old INT2 rows, then demoted INT4 rows)
+  int base = 0;
+  for (int c0 = 0; c0 < M2 + M4; c0 += blockDim.x) {
+    const int i = c0 + tid;
+    bool keep = false;
+    int src = 0, old_slot = 0;
+    if (i < M2) {
+      old_slot = S + i;
+      keep = !dropped_key(key_at(old_slot));
+      src = i;
+    } else if (i < M2 + M4 && demoted(i - M2)) {
+      old_slot = S + M2 + (i - M2);
+      keep = !dropped_key(key_at(old_slot));
+      src = -1 - (i - M2);
+    }
+    int tot;
+    const int r = block_excl_scan(keep ? 1 : 0, &tot, wsum) + base;
+    base += tot;
+    if (keep) {
+      a.lsrc[(size_t)row * a.plan_l + r] = src;
+      if (sc) sc[S + r] = tmp[old_slot];
+      if (a.kept) a.kept[(size_t)row * s.cap_T + S + r] = old_slot;
+    }
+  }
+  // new INT4 rows: the rows not demoted, in order
+  base = 0;
+  for (int c0 = 0; c0 < M4; c0 += blockDim.x) {
+    const int i = c0 + tid;
+    const bool keep = i < M4 && !demoted(i);
+    int tot;
+    const int r = block_excl_scan(keep ? 1 : 0, &tot, wsum) + base;
+    base += tot;
+    if (keep) {
+      a.i4src[(size_t)row * a.plan_4 + r] = i;
+      if (sc) sc[S + M2n + r] = tmp[S + M2 + i];
+      if (a.kept) a.kept[(size_t)row * s.cap_T + S + M2n + r] = S + M2 + i;
+    }
+  }
+  // recent slots move down by the dropped count; sinks stay
+  for (int i = tid; i < R; i += blockDim.x) {
+    if (sc) sc[S + M2n + M4n + i] = tmp[S + M2 + M4 + i];
+    if (a.kept) a.kept[(size_t)row * s.cap_T + S + M2n + M4n + i] = S + M2 + M4 + i;
+  }
+  if (a.kept) {
+    for (int j = tid; j < s.cap_T; j += blockDim.x) {
+      if (j < S) a.kept[(size_t)row * s.cap_T + j] = j;
+      else if (j >= S + M2n + M4n + R) a.kept[(size_t)row * s.cap_T + j] = -1;
+    }
+  }
+  if (tid == 0) {
+    int32_t* inf = a.info + (size_t)row * kTierInfo;
+    inf[0] = S; inf[1] = M4; inf[2] = M2; inf[3] = R;
+    inf[4] = M4n; inf[5] = M2n; inf[6] = n_dem; inf[7] = n_drop;
+  }
+}
+
+// Channel c of a packed row of `bits`-bit offset-binary codes, dequantized.
+__device__ __forceinline__ float dequant_ch(const uint8_t* row, const uint16_t* scales, int c, int bits) {
+  const int byte = c * bits / 8, sh = (c * bits) % 8;
+  const int q = (int)((row[byte] >> sh) & ((1u << bits) - 1u)) - (1 << (bits - 1));
+  return (float)q * h2f(scales[c / 32]);
+}
+
+// Quantize one row given as fp16 values: lane p < HALF holds channels p and
+// p + HALF (groups are half-waves), the layout quant_lane expects.
+template <int BITS>
+__device__ __forceinline__ void quant_row_lanes(uint16_t y1, uint16_t y2, int p, int HALF, bool live, uint8_t* codes,
+                                                uint16_t* scales) {
+  constexpr int PER = 32 / BITS;
+  const int c = p % 32;
+  uint16_t s1, s2;
+  const uint32_t w1 = quant_lane<BITS>(h2f(y1), c, s1);
+  const uint32_t w2 = quant_lane<BITS>(h2f(y2), c, s2);
+  if (!live) return;
+  uint32_t* cw = reinterpret_cast<uint32_t*>(codes);
+  if (c % PER == 0) {
+    cw[p / PER] = w1;
+    cw[(p + HALF) / PER] = w2;
+  }
+  if (c == 0) {
+    scales[p / 32] = s1;
+    scales[(p + HALF) / 32] = s2;
+  }
+}
+
+// One new row of one KV head: its key re-rotated by delta (delta = 0: not
+// rotated) and requantized from src_bits to dst_bits, its value requantized
+// (or copied when the bits stay). One wave, lane p = rotation pair p.
+__device__ void rebuild_row(const uint8_t* skc, const uint16_t* sks, const uint8_t* svc, const uint16_t* svs,
+                            int src_kb, int src_vb, uint8_t* dkc, uint16_t* dks, uint8_t* dvc, uint16_t* dvs,
+                            int dst_kb, int dst_vb, int delta, int D, const RopeFreqs& fr) {
+  const int lane = threadIdx.x & 63, HALF = D / 2;
+  const bool live = lane < HALF;
+  const int p = live ? lane : lane - HALF;          // idle lanes mirror a live one (no stores)
+  const bool requant_k = dst_kb != src_kb || (delta != 0 && fr.rotates);
+  if (!requant_k) {
+    const int kw = D * src_kb / 32;                 // 32-bit words of the key codes
+    for (int i = lane; i < kw; i += 64)
+      reinterpret_cast<uint32_t*>(dkc)[i] = reinterpret_cast<const uint32_t*>(skc)[i];
+    if (lane < D / 32) dks[lane] = sks[lane];
+  } else {
+    uint16_t y1, y2;
+    if (!fr.interleaved) {
+      const float x1 = dequant_ch(skc, sks, p, src_kb), x2 = dequant_ch(skc, sks, p + HALF, src_kb);
+      if (delta != 0 && fr.rotates) {
+        double sn, cn;
+        sincos(-(double)delta * fr.f[p], &sn, &cn);
+        rotate_pair(x1, x2, cn, sn, y1, y2);
+      } else {
+        y1 = f2h(x1);
+        y2 = f2h(x2);
+      }
+    } else {
+      // pair p is channels (2p, 2p + 1); rotate it, then trade values back to
+      // the (p, p + HALF) layout of the quantizer
+      const float x1 = dequant_ch(skc, sks, 2 * p, src_kb), x2 = dequant_ch(skc, sks, 2 * p + 1, src_kb);
+      uint16_t z1, z2;
+      if (delta != 0 && fr.rotates) {
+        double sn, cn;
+        sincos(-(double)delta * fr.f[p], &sn, &cn);
+        rotate_pair(x1, x2, cn, sn, z1, z2);
+      } else {
+        z1 = f2h(x1);
+        z2 = f2h(x2);
+      }
+      const int base = live ? 0 : HALF;            // the half of the wave this lane mirrors
+      const int l1 = base + p / 2, l2 = base + (p + HALF) / 2;
+      const int t0 = __shfl((int)z1, l1), t1 = __shfl((int)z2, l1);
+      const int t2 = __shfl((int)z1, l2), t3 = __shfl((int)z2, l2);
+      y1 = (uint16_t)((p & 1) ? t1 : t0);
+      y2 = (uint16_t)((p & 1) ? t3 : t2);
+    }
+    if (dst_kb == 4) quant_row_lanes<4>(y1, y2, p, HALF, live, dkc, dks);
+    else quant_row_lanes<2>(y1, y2, p, HALF, live, dkc, dks);
+  }
+  if (dst_vb == src_vb) {
+    const int vw = D * src_vb / 32;
+    for (int i = lane; i < vw; i += 64)
+      reinterpret_cast<uint32_t*>(dvc)[i] = reinterpret_cast<const uint32_t*>(svc)[i];
+    if (lane < D / 32) dvs[lane] = svs[lane];
+  } else {
+    const uint16_t v1 = f2h(dequant_ch(svc, svs, p, src_vb)), v2 = f2h(dequant_ch(svc, svs, p + HALF, src_vb));
+    if (dst_vb == 4) quant_row_lanes<4>(v1, v2, p, HALF, live, dvc, dvs);
+    else quant_row_lanes<2>(v1, v2, p, HALF, live, dvc, dvs);
+  }
+}
+
+// blockIdx.x: new INT2 rows [0, plan_l), then new INT4 rows, then the ring's
+// re-rotation blocks; blockIdx.y: KV head; blockIdx.z: sequence. 64 threads.
+__global__ __launch_bounds__(64) void k_tier_move(TierArgs a) {
+  const Shape& s = a.s;
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int mrow = s.shared ? 0 : b;
+  const int32_t* inf = a.info + (size_t)mrow * kTierInfo;
+  const int S = inf[0], M4 = inf[1], M2 = inf[2], R = inf[3], M4n = inf[4], M2n = inf[5], n_drop = inf[7];
+  const int D = s.D;
+  const size_t bg = (size_t)b * s.Hkv + g;
+  const int x = blockIdx.x;
+  const int KR4 = D * s.kb / 8, VR4 = D * s.vb / 8, LR = D * kLowBits / 8, NG = D / 32;
+  if (x < a.plan_l) {
+    if (x >= M2n) return;
+    const int src = a.lsrc[(size_t)mrow * a.plan_l + x];
+    const int new_slot = S + x;
+    if (src >= 0) {
+      const size_t sr = bg * s.cap_low + src;
+      rebuild_row(reinterpret_cast<const uint8_t*>(a.c.low_k_codes) + sr * LR,
+                  reinterpret_cast<const uint16_t*>(a.c.low_k_scales) + sr * NG,
+                  reinterpret_cast<const uint8_t*>(a.c.low_v_codes) + sr * LR,
+                  reinterpret_cast<const uint16_t*>(a.c.low_v_scales) + sr * NG, kLowBits, kLowBits,
+                  a.dst_lkc + (bg * a.dst_capl + x) * LR, a.dst_lks + (bg * a.dst_capl + x) * NG,
+                  a.dst_lvc + (bg * a.dst_capl + x) * LR, a.dst_lvs + (bg * a.dst_capl + x) * NG, kLowBits,
+                  kLowBits, (S + src) - new_slot, D, a.fr);
+    } else {
+      const int i = -1 - src;
+      const size_t sr = bg * a.src_cap4 + i;
+      rebuild_row(a.src_kc + sr * KR4, a.src_ks + sr * NG, a.src_vc + sr * VR4, a.src_vs + sr * NG, s.kb, s.vb,
+                  a.dst_lkc + (bg * a.dst_capl + x) * LR, a.dst_lks + (bg * a.dst_capl + x) * NG,
+                  a.dst_lvc + (bg * a.dst_capl + x) * LR, a.dst_lvs + (bg * a.dst_capl + x) * NG, kLowBits,
+                  kLowBits, (S + M2 + i) - new_slot, D, a.fr);
+    }
+    return;
+  }
+  const int y = x - a.plan_l;
+  if (y < a.plan_4) {
+    if (y >= M4n) return;
+    const int i = a.i4src[(size_t)mrow * a.plan_4 + y];
+    const size_t sr = bg * a.src_cap4 + i;
+    rebuild_row(a.src_kc + sr * KR4, a.src_ks + sr * NG, a.src_vc + sr * VR4, a.src_vs + sr * NG, s.kb, s.vb,
+                a.dst_kc + (bg * a.dst_cap4 + y) * KR4, a.dst_ks + (bg * a.dst_cap4 + y) * NG,
+                a.dst_vc + (bg * a.dst_cap4 + y) * VR4, a.dst_vs + (bg * a.dst_cap4 + y) * NG, s.kb, s.vb,
+                (S + M2 + i) - (S + M2n + y), D, a.fr);
+    return;
+  }
+  // the recent ring moves down by n_drop slots: rotate its fp16 keys in place,
+  // one entry per block
+  const int t = y - a.plan_4;
+  if (t >= R || n_drop == 0 || !a.fr.rotates) return;
+  const int lane = threadIdx.x, HALF = D / 2;
+  if (lane >= HALF) return;
+  const int32_t* L = a.c.lens + 4 * b;
+  const int head = min(max(L[3], 0), s.ring - 1);
+  uint16_t* kr = reinterpret_cast<uint16_t*>(a.c.fp_k) + (bg * (s.n_sink + s.ring) + s.n_sink + (head + t) % s.ring) * D;
+  const int c1 = a.fr.interleaved ? 2 * lane : lane, c2 = a.fr.interleaved ? 2 * lane + 1 : lane + HALF;
+  const float x1 = h2f(kr[c1]), x2 = h2f(kr[c2]);
+  double sn, cn;
+  sincos(-(double)n_drop * a.fr.f[lane], &sn, &cn);
+  uint16_t y1, y2;
+  rotate_pair(x1, x2, cn, sn, y1, y2);
+  kr[c1] = y1;
+  kr[c2] = y2;
+  (void)M4;
+}
+
+// Staging rows back into the cache (when the rows were rebuilt in place) and
+// the new lengths. blockIdx.x: a 256-thread slice of the rows' 32-bit words.
+__global__ __launch_bounds__(256) void k_tier_copy(TierArgs a, int copy_rows) {
+  const Shape& s = a.s;
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int mrow = s.shared ? 0 : b;
+  const int32_t* inf = a.info + (size_t)mrow * kTierInfo;
+  const int M4n = inf[4], M2n = inf[5];
+  if (blockIdx.x == 0 && g == 0 && threadIdx.x == 0) {
+    a.c.lens[4 * b + 1] = M4n;
+    a.c.low_lens[b] = M2n;
+  }
+  if (!copy_rows) return;
+  const int D = s.D;
+  const size_t bg = (size_t)b * s.Hkv + g;
+  const int KW4 = D * s.kb / 32, VW4 = D * s.vb / 32, LW = D * kLowBits / 32, SW = D / 64;   // words per row
+  const int per4 = KW4 + VW4 + 2 * SW, perl = 2 * LW + 2 * SW;
+  const long n_words = (long)M4n * per4 + (long)M2n * perl;
+  for (long w = (long)blockIdx.x * blockDim.x + threadIdx.x; w < n_words; w += (long)gridDim.x * blockDim.x) {
+    if (w < (long)M4n * per4) {
+      const int r = (int)(w / per4), o = (int)(w % per4);
+      const size_t sr = bg * a.dst_cap4 + r, dr = bg * s.cap_mid + r;
+      const uint32_t* src;
+      uint32_t* dst;
+      int k = o;
+      if (k < KW4) { src = reinterpret_cast<const uint32_t*>(a.dst_kc + sr * KW4 * 4); dst = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(a.c.mid_k_codes) + dr * KW4 * 4); }
+      else if ((k -= KW4) < VW4) { src = reinterpret_cast<const uint32_t*>(a.dst_vc + sr * VW4 * 4); dst = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(a.c.mid_v_codes) + dr * VW4 * 4); }
+      else if ((k -= VW4) < SW) { src = reinterpret_cast<const uint32_t*>(a.dst_ks + sr * 2 * SW); dst = reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(a.c.mid_k_scales) + dr * 2 * SW); }
+      else { k -= SW; src = reinterpret_cast<const uint32_t*>(a.dst_vs + sr * 2 * SW); dst = reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(a.c.mid_v_scales) + dr * 2 * SW); }
+      dst[k] = src[k];
+    } else {
+      const long w2 = w - (long)M4n * per4;
+      const int r = (int)(w2 / perl), o = (int)(w2 % perl);
+      const size_t sr = bg * a.dst_capl + r, dr = bg * s.cap_low + r;
+      const uint32_t* src;
+      uint32_t* dst;
+      int k = o;
+      if (k < LW) { src = reinterpret_cast<const uint32_t*>(a.dst_lkc + sr * LW * 4); dst = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(a.c.low_k_codes) + dr * LW * 4); }
+      else if ((k -= LW) < LW) { src = reinterpret_cast<const uint32_t*>(a.dst_lvc + sr * LW * 4); dst = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(a.c.low_v_codes) + dr * LW * 4); }
+      else if ((k -= LW) < SW) { src = reinterpret_cast<const uint32_t*>(a.dst_lks + sr * 2 * SW); dst = reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(a.c.low_k_scales) + dr * 2 * SW); }
+      else { k -= SW; src = reinterpret_cast<const uint32_t*>(a.dst_lvs + sr * 2 * SW); dst = reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(a.c.low_v_scales) + dr * 2 * SW); }
+      dst[k] = src[k];
+    }
+  }
+}
+
+namespace {
+struct TierWs {
+  int32_t *info, *lsrc, *i4src, *kept_dummy;
+  float* score_tmp;
+  uint8_t *kc, *vc, *lkc, *lvc;
+  uint16_t *ks, *vs, *lks, *lvs;
+  int plan_l, plan_4, cap4, capl;
+  size_t bytes;
+};
+// Workspace layout of an event whose INT4 sources hold src_cap4 rows per
+// (sequence, head); staging rows only when staged.
+TierWs tier_ws_layout(const Shape& s, int src_cap4, bool staged, char* w) {
+  TierWs t{};
+  const int rows = s.shared ? 1 : s.batch;
+  t.plan_l = max(1, s.low_budget);
+  t.plan_4 = max(1, src_cap4);
+  t.cap4 = staged ? max(1, s.cap_mid) : 0;
+  t.capl = staged ? t.plan_l : 0;
+  const int D = s.D, NG = D / 32;
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    char* p = w ? w + off : nullptr;
+    off += align_up(n, 256);
+    return p;
+  };
+  t.info = reinterpret_cast<int32_t*>(take((size_t)rows * kTierInfo * 4));
+  t.lsrc = reinterpret_cast<int32_t*>(take((size_t)rows * t.plan_l * 4));
+  t.i4src = reinterpret_cast<int32_t*>(take((size_t)rows * t.plan_4 * 4));
+  t.score_tmp = reinterpret_cast<float*>(take((size_t)rows * s.cap_T * 4));
+  const size_t bh = (size_t)s.batch * s.Hkv;
+  t.kc = reinterpret_cast<uint8_t*>(take(bh * t.cap4 * D * s.kb / 8));
+  t.vc = reinterpret_cast<uint8_t*>(take(bh * t.cap4 * D * s.vb / 8));
+  t.ks = reinterpret_cast<uint16_t*>(take(bh * t.cap4 * NG * 2));
+  t.vs = reinterpret_cast<uint16_t*>(take(bh * t.cap4 * NG * 2));
+  t.lkc = reinterpret_cast<uint8_t*>(take(bh * t.capl * D * kLowBits / 8));
+  t.lvc = reinterpret_cast<uint8_t*>(take(bh * t.capl * D * kLowBits / 8));
+  t.lks = reinterpret_cast<uint16_t*>(take(bh * t.capl * NG * 2));
+  t.lvs = reinterpret_cast<uint16_t*>(take(bh * t.capl * NG * 2));
+  t.bytes = off;
+  return t;
+}
+
+// Runs the event: sources given in `a` (INT4 rows from a.src_*); staged:
+// rebuild into the workspace copies and copy back, else straight into the
+// cache (sources elsewhere).
+hipError_t run_tier_event(TierArgs a, const TierWs& t, bool staged, int32_t* kept, hipStream_t st) {
+  const Shape& s = a.s;
+  const int rows = s.shared ? 1 : s.batch;
+  a.info = t.info;
+  a.lsrc = t.lsrc;
+  a.i4src = t.i4src;
+  a.plan_l = t.plan_l;
+  a.plan_4 = t.plan_4;
+  a.score_tmp = t.score_tmp;
+  a.kept = kept;
+  if (staged) {
+    a.dst_kc = t.kc; a.dst_vc = t.vc; a.dst_ks = t.ks; a.dst_vs = t.vs;
+    a.dst_lkc = t.lkc; a.dst_lvc = t.lvc; a.dst_lks = t.lks; a.dst_lvs = t.lvs;
+    a.dst_cap4 = t.cap4;
+    a.dst_capl = t.capl;
+  } else {
+    a.dst_kc = reinterpret_cast<uint8_t*>(a.c.mid_k_codes);
+    a.dst_vc = reinterpret_cast<uint8_t*>(a.c.mid_v_codes);
+    a.dst_ks = reinterpret_cast<uint16_t*>(a.c.mid_k_scales);
+    a.dst_vs = reinterpret_cast<uint16_t*>(a.c.mid_v_scales);
+    a.dst_lkc = reinterpret_cast<uint8_t*>(a.c.low_k_codes);
+    a.dst_lvc = reinterpret_cast<uint8_t*>(a.c.low_v_codes);
+    a.dst_lks = reinterpret_cast<uint16_t*>(a.c.low_k_scales);
+    a.dst_lvs = reinterpret_cast<uint16_t*>(a.c.low_v_scales);
+    a.dst_cap4 = s.cap_mid;
+    a.dst_capl = s.cap_low;
+  }
+  hipLaunchKernelGGL(k_tier_select, dim3(rows), dim3(kSelThreads), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_tier_move, dim3(a.plan_l + a.plan_4 + s.ring, s.Hkv, s.batch), dim3(64), 0, st, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_tier_copy, dim3(staged ? 16 : 1, s.Hkv, s.batch), dim3(256), 0, st, a, staged ? 1 : 0);
+  return hipGetLastError();
+}
+}  // namespace
+
+size_t tier_event_ws_bytes(const Shape& s) { return tier_ws_layout(s, s.cap_mid, true, nullptr).bytes; }
+size_t tier_event_ws_bytes_src(const Shape& s, int src_cap4, bool staged) {
+  return tier_ws_layout(s, src_cap4, staged, nullptr).bytes;
+}
+
+// The event with INT4 sources outside the cache (a prefill build's wide
+// staging rows): rows are rebuilt straight into the cache.
+hipError_t launch_tier_event_from(const Shape& s, const fade_layer_cache& c, int policy, const RopeFreqs& fr,
+                                  const uint8_t* kc, const uint8_t* vc, const uint16_t* ks, const uint16_t* vs,
+                                  int src_cap4, void* ws, hipStream_t st) {
+  const TierWs t = tier_ws_layout(s, src_cap4, false, reinterpret_cast<char*>(ws));
+  TierArgs a{};
+  a.s = s;
+  a.c = c;
+  a.policy = policy;
+  a.src_kc = kc;
+  a.src_vc = vc;
+  a.src_ks = ks;
+  a.src_vs = vs;
+  a.src_cap4 = src_cap4;
+  a.fr = fr;
+  return run_tier_event(a, t, false, nullptr, st);
+}
+
+hipError_t launch_tier_event(const Shape& s, const fade_layer_cache& c, int policy, const RopeFreqs& fr,
+                             int32_t* kept, void* ws, hipStream_t st) {
+  const TierWs t = tier_ws_layout(s, s.cap_mid, true, reinterpret_cast<char*>(ws));
+  TierArgs a{};
+  a.s = s;
+  a.c = c;
+  a.policy = policy;
+  a.src_kc = reinterpret_cast<const uint8_t*>(c.mid_k_codes);
+  a.src_vc = reinterpret_cast<const uint8_t*>(c.mid_v_codes);
+  a.src_ks = reinterpret_cast<const uint16_t*>(c.mid_k_scales);
+  a.src_vs = reinterpret_cast<const uint16_t*>(c.mid_v_scales);
+  a.src_cap4 = s.cap_mid;
+  a.fr = fr;
+  return run_tier_event(a, t, true, kept, st);
 }
 
 }  // namespace fade

@@ -79,7 +79,8 @@ hipError_t launch_quantize_rows(int D, int bits, const uint16_t* src, int64_t n_
 // Append the newest token of sequence blockIdx.x (all KV heads). A new slot's
 // score starts at 0 (the cumulative H2O score of a token that has not been
 // attended yet, Transformer series (25) 1.3.1; the EMA of an empty history),
-// so the score entry at its position S + M + R is cleared here: an eviction
+// so the score entry at its position S + M2 + M + R (M2: the INT2 overflow
+// tier's rows, 0 without one) is cleared here: an eviction
 // shifts the score row down and leaves the entries past the live length
 // holding old values.
 __global__ __launch_bounds__(256) void k_append(Shape s, fade_layer_cache c,
@@ -115,7 +116,7 @@ __global__ __launch_bounds__(256) void k_append(Shape s, fade_layer_cache c,
   }
   // A shared cache has one score row and identical lengths in every row:
   // sequence 0 clears it.
-  const int pos = S + M + R;
+  const int pos = S + (s.low ? max(c.low_lens[b], 0) : 0) + M + R;
   if (threadIdx.x == 0 && c.scores && (!c.shared || b == 0) && pos < s.cap_T)
     c.scores[(size_t)(c.shared ? 0 : b) * s.cap_T + pos] = 0.f;
   __syncthreads();

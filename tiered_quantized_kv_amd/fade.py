@@ -37,7 +37,7 @@ class FadeConfig(ctypes.Structure):
         ("rope_type", ctypes.c_int32), ("rope_theta", ctypes.c_double), ("rope_factor", ctypes.c_double),
         ("rope_low_freq_factor", ctypes.c_double), ("rope_high_freq_factor", ctypes.c_double),
         ("rope_original_max_position", ctypes.c_int32), ("q_dtype", ctypes.c_int32),
-        ("out_dtype", ctypes.c_int32), ("rope_seq_len", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32), ("rope_seq_len", ctypes.c_int32), ("int2_budget", ctypes.c_int32),
     ]
 
 
@@ -48,6 +48,9 @@ class LayerCache(ctypes.Structure):
         ("mid_k_codes", ctypes.c_void_p), ("mid_v_codes", ctypes.c_void_p),
         ("mid_k_scales", ctypes.c_void_p), ("mid_v_scales", ctypes.c_void_p),
         ("lens", ctypes.c_void_p), ("scores", ctypes.c_void_p),
+        ("cap_low", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("low_k_codes", ctypes.c_void_p), ("low_v_codes", ctypes.c_void_p),
+        ("low_k_scales", ctypes.c_void_p), ("low_v_scales", ctypes.c_void_p), ("low_lens", ctypes.c_void_p),
     ]
 
 
@@ -72,6 +75,7 @@ _SIGS = {
     "fade_rope_rotate": (ctypes.c_int, [_CFG, _P, ctypes.c_int32, ctypes.c_int64, _P, ctypes.c_int32,
                                         ctypes.c_int32, _P]),
     "fade_workspace_bytes": (ctypes.c_size_t, [_CFG, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]),
+    "fade_cache_workspace_bytes": (ctypes.c_size_t, [_CFG, _CACHE, ctypes.c_int32, ctypes.c_int32]),
     "fade_compressed_bytes": (ctypes.c_uint64, [_CFG, _P, _P, ctypes.c_int32]),
     "fade_pq_encode": (ctypes.c_int, [ctypes.c_int32, _P, ctypes.c_int64, _P, _P, _P]),
     "fade_pq_decode": (ctypes.c_int, [ctypes.c_int32, _P, ctypes.c_int64, _P, _P, _P]),
@@ -106,13 +110,14 @@ def exported_symbols():
 def make_config(head_dim, n_q_heads, n_kv_heads, n_sink, recent_window, int4_budget, middle_k_bits=4,
                 middle_v_bits=4, rope_type="default", rope_theta=10000.0, rope_factor=1.0,
                 rope_low_freq_factor=1.0, rope_high_freq_factor=4.0, rope_original_max_position=8192,
-                q_dtype="f16", out_dtype="f32", group_size=32, rope_seq_len=0, rope_interleaved=False):
+                q_dtype="f16", out_dtype="f32", group_size=32, rope_seq_len=0, rope_interleaved=False,
+                int2_budget=-1):
     dt = {"f16": DTYPE_F16, "bf16": DTYPE_BF16, "f32": DTYPE_F32}
     return FadeConfig(head_dim, n_q_heads, n_kv_heads, n_sink, recent_window, int4_budget, middle_k_bits,
                       middle_v_bits, group_size, _ROPE[rope_type] | (ROPE_INTERLEAVED if rope_interleaved else 0),
                       float(rope_theta), float(rope_factor), float(rope_low_freq_factor),
                       float(rope_high_freq_factor), int(rope_original_max_position), dt[q_dtype],
-                      dt[out_dtype], int(rope_seq_len))
+                      dt[out_dtype], int(rope_seq_len), int(int2_budget))
 
 
 def _p(t):
@@ -130,12 +135,17 @@ def _check(status, where):
         raise FadeError(status, where)
 
 
-def workspace_bytes(cfg, op, batch, max_len):
+def workspace_bytes(cfg, op, batch, max_len, cache=None):
+    """fade_workspace_bytes, or fade_cache_workspace_bytes when a cache (a
+    TieredCache or one of its views) is given: then the size follows the
+    cache's own capacities and max_len is only the prefill length."""
+    if cache is not None:
+        return int(lib().fade_cache_workspace_bytes(ctypes.byref(cfg), cache.ref(), op, max_len))
     return int(lib().fade_workspace_bytes(ctypes.byref(cfg), op, batch, max_len))
 
 
-def workspace(cfg, op, batch, max_len, device="cuda"):
-    n = max(workspace_bytes(cfg, op, batch, max_len), 256)
+def workspace(cfg, op, batch, max_len, device="cuda", cache=None):
+    n = max(workspace_bytes(cfg, op, batch, max_len, cache), 256)
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
@@ -143,12 +153,14 @@ class TieredCache:
     """Device tensors of one layer's tiers plus the LayerCache struct that
     points at them (memory plumbing for the C ABI)."""
 
-    def __init__(self, cfg, batch, cap_mid, shared=False, with_scores=True, device="cuda"):
+    def __init__(self, cfg, batch, cap_mid, shared=False, with_scores=True, device="cuda", cap_low=None):
         d, hkv = cfg.head_dim, cfg.n_kv_heads
         self.cfg = cfg
         self.batch, self.cap_mid, self.shared = batch, cap_mid, int(bool(shared))
+        self.low = cfg.int2_budget >= 0
+        self.cap_low = (max(cfg.int2_budget, 0) if cap_low is None else cap_low) if self.low else 0
         self.slots = cfg.n_sink + cfg.recent_window + 1
-        self.cap_T = cfg.n_sink + cap_mid + cfg.recent_window + 1
+        self.cap_T = cfg.n_sink + cap_mid + self.cap_low + cfg.recent_window + 1
         f16 = torch.float16
         self.fp_k = torch.zeros(batch, hkv, self.slots, d, dtype=f16, device=device)
         self.fp_v = torch.zeros_like(self.fp_k)
@@ -160,10 +172,22 @@ class TieredCache:
         self.lens = torch.zeros(batch, 4, dtype=torch.int32, device=device)
         self.scores = (torch.zeros(1 if shared else batch, self.cap_T, dtype=torch.float32, device=device)
                        if with_scores else None)
-        self.struct = LayerCache(batch, cap_mid, self.cap_T, self.shared, self.fp_k.data_ptr(),
-                                 self.fp_v.data_ptr(), self.mid_k_codes.data_ptr(), self.mid_v_codes.data_ptr(),
-                                 self.mid_k_scales.data_ptr(), self.mid_v_scales.data_ptr(),
-                                 self.lens.data_ptr(), None if self.scores is None else self.scores.data_ptr())
+        # INT2 overflow tier (K and V at 2 bits), allocated when the config has one
+        cl = max(self.cap_low, 1)
+        self.low_k_codes = torch.zeros(batch, hkv, cl, d // 4, dtype=torch.uint8, device=device) if self.low else None
+        self.low_v_codes = torch.zeros_like(self.low_k_codes) if self.low else None
+        self.low_k_scales = torch.zeros(batch, hkv, cl, d // 32, dtype=f16, device=device) if self.low else None
+        self.low_v_scales = torch.zeros_like(self.low_k_scales) if self.low else None
+        self.low_lens = torch.zeros(batch, dtype=torch.int32, device=device) if self.low else None
+        self.struct = self._struct(self.fp_k, self.fp_v, self.mid_k_codes, self.mid_v_codes, self.mid_k_scales,
+                                   self.mid_v_scales, self.lens, self.scores, self.low_k_codes, self.low_v_codes,
+                                   self.low_k_scales, self.low_v_scales, self.low_lens, batch, self.shared)
+
+    def _struct(self, fk, fv, mkc, mvc, mks, mvs, lens, scores, lkc, lvc, lks, lvs, llens, batch, shared):
+        ptr = lambda t: None if t is None else t.data_ptr()
+        return LayerCache(batch, self.cap_mid, self.cap_T, shared, ptr(fk), ptr(fv), ptr(mkc), ptr(mvc), ptr(mks),
+                          ptr(mvs), ptr(lens), ptr(scores), self.cap_low, 0, ptr(lkc), ptr(lvc), ptr(lks), ptr(lvs),
+                          ptr(llens))
 
     def ref(self):
         return ctypes.byref(self.struct)
@@ -173,11 +197,12 @@ class TieredCache:
         for building ragged batches one sequence at a time."""
         v = _View()
         srow = 0 if self.shared else b
-        v.struct = LayerCache(1, self.cap_mid, self.cap_T, 0, self.fp_k[b].data_ptr(), self.fp_v[b].data_ptr(),
-                              self.mid_k_codes[b].data_ptr(), self.mid_v_codes[b].data_ptr(),
-                              self.mid_k_scales[b].data_ptr(), self.mid_v_scales[b].data_ptr(),
-                              self.lens[b].data_ptr(),
-                              None if self.scores is None else self.scores[srow].data_ptr())
+        at = lambda t: None if t is None else t[b]
+        v.struct = self._struct(self.fp_k[b], self.fp_v[b], self.mid_k_codes[b], self.mid_v_codes[b],
+                                self.mid_k_scales[b], self.mid_v_scales[b], self.lens[b],
+                                None if self.scores is None else self.scores[srow], at(self.low_k_codes),
+                                at(self.low_v_codes), at(self.low_k_scales), at(self.low_v_scales),
+                                None if self.low_lens is None else self.low_lens[b:b + 1], 1, 0)
         return v
 
 
