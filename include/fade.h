@@ -208,7 +208,7 @@ typedef struct fade_layer_cache {
 /* Human-readable name of a status code; never NULL. */
 const char* fade_status_string(int status);
 
-/* ABI version of this header (major * 100 + minor): 300. */
+/* ABI version of this header (major * 100 + minor): 301. */
 int fade_abi_version(void);
 
 /*
@@ -387,11 +387,14 @@ size_t fade_cache_workspace_bytes(const fade_config* cfg, const fade_layer_cache
 /*
  * Compressed KV bytes (FADE post, "使用注意事项": KV-only accounting), host
  * only: sum over n entries of
- *   Hkv * (fp16_slots[i] * d * 4 + mid_slots[i] * ((d*kb/8 + 2d/32) + (d*vb/8 + 2d/32))).
- * One entry per (layer, sequence). Returns 0 on invalid arguments.
+ *   Hkv * (fp16_slots[i] * d * 4 + mid_slots[i] * ((d*kb/8 + 2d/32) + (d*vb/8 + 2d/32))
+ *          + low_slots[i] * 2 * (d*2/8 + 2d/32)),
+ * the last term for the INT2 overflow tier (K and V at 2 bits); low_slots
+ * may be NULL (no such tier). One entry per (layer, sequence). Returns 0 on
+ * invalid arguments.
  */
 uint64_t fade_compressed_bytes(const fade_config* cfg, const int32_t* fp16_slots,
-                               const int32_t* mid_slots, int32_t n);
+                               const int32_t* mid_slots, const int32_t* low_slots, int32_t n);
 
 /*
  * Product-quantization codebook for KV vectors (FADE post, section

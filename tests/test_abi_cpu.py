@@ -32,7 +32,7 @@ def test_library_exports_every_header_function():
 
 def test_status_strings_and_version():
     lib = fade.lib()
-    assert lib.fade_abi_version() == 300
+    assert lib.fade_abi_version() == 301
     for s in range(6):
         assert lib.fade_status_string(s)
     assert lib.fade_status_string(99) == b"unknown status"
@@ -63,6 +63,12 @@ def test_compressed_bytes_matches_oracle_closed_form(d, hkv, kb, vb):
     mid = gen.integers(0, 9000, size=37)
     want = accounting.compressed_bytes(d, hkv, kb, vb, 32, fp.tolist(), mid.tolist())
     assert fade.fade_compressed_bytes(cfg, fp, mid) == want
+    low = gen.integers(0, 3000, size=37)
+    want = accounting.compressed_bytes(d, hkv, kb, vb, 32, fp.tolist(), mid.tolist(), low.tolist())
+    assert fade.fade_compressed_bytes(cfg, fp, mid, low) == want
+    bad = low.copy()
+    bad[5] = -1
+    assert fade.fade_compressed_bytes(cfg, fp, mid, bad) == 0
 
 
 def test_workspace_sizes_positive_and_monotone():

@@ -107,3 +107,56 @@ def test_budget_may_differ(tmp_path):
     b = fade.TieredCache(_cfg(int4_budget=20), 2, 50, device="cpu")
     persist.load(b, path)
     assert torch.equal(a.lens, b.lens)
+
+
+def _filled_low(cfg, batch, cap_mid, cap_low, seed):
+    tc = fade.TieredCache(cfg, batch, cap_mid, device="cpu", cap_low=cap_low)
+    filled = _filled(cfg, batch, cap_mid, seed)
+    for name in ("fp_k", "fp_v", "mid_k_scales", "mid_v_scales", "mid_k_codes", "mid_v_codes", "lens"):
+        getattr(tc, name).copy_(getattr(filled, name))
+    gen = synth.rng(seed, 1)
+    for name in ("low_k_scales", "low_v_scales"):
+        t = getattr(tc, name)
+        t.copy_(torch.from_numpy(synth.normal(gen, *t.shape).astype(np.float16)))
+    for name in ("low_k_codes", "low_v_codes"):
+        t = getattr(tc, name)
+        t.copy_(torch.from_numpy(gen.integers(0, 256, size=t.shape).astype(np.uint8)))
+    tc.low_lens.copy_(torch.from_numpy(gen.integers(0, cap_low + 1, size=batch).astype(np.int32)))
+    tc.scores.copy_(torch.from_numpy(synth.normal(gen, *tc.scores.shape).astype(np.float32)))
+    return tc
+
+
+def test_int2_tier_round_trip_telemetry_and_refusals(tmp_path):
+    """The INT2 overflow tier travels with the cache (FADE post, "会话持久化"
+    and "第三层：INT2深度压缩（可选）"): codes, scales and lengths restored, the
+    scores' live length counts its rows, telemetry counts it and its bytes
+    follow the oracle's closed form; a cache without the tier refuses it."""
+    cfg = _cfg(int2_budget=16)
+    a = _filled_low(cfg, 3, 44, 18, 11)
+    path = str(tmp_path / "low.safetensors")
+    persist.save(a, path)
+    b = fade.TieredCache(cfg, 3, 44, device="cpu", cap_low=20)
+    persist.load(b, path)
+    m2 = int(a.low_lens.max())
+    assert torch.equal(a.low_lens, b.low_lens) and torch.equal(a.lens, b.lens)
+    for name in ("low_k_codes", "low_v_codes", "low_k_scales", "low_v_scales"):
+        assert torch.equal(getattr(a, name)[:, :, :m2], getattr(b, name)[:, :, :m2]), name
+    t = int((a.lens[:, :3].sum(dim=1) + a.low_lens).max())
+    assert torch.equal(a.scores[:, :t], b.scores[:, :t]) and not b.scores[:, t:].any()
+    rec = persist.layer_record(a, 2)
+    lens, low = a.lens.numpy(), a.low_lens.numpy()
+    for bb, q in enumerate(rec["seqs"]):
+        s, m, w = (int(x) for x in lens[bb, :3])
+        assert (q["int2"], q["live"]) == (int(low[bb]), s + int(low[bb]) + m + w)
+    want = accounting.compressed_bytes(64, 2, 4, 2, 32, [q["sink"] + q["recent"] for q in rec["seqs"]],
+                                       [q["middle"] for q in rec["seqs"]], [q["int2"] for q in rec["seqs"]])
+    assert rec["compressed_bytes"] == want
+    for other in (fade.TieredCache(_cfg(), 3, 44, device="cpu"),
+                  fade.TieredCache(cfg, 3, 44, device="cpu", cap_low=m2 - 1)):
+        with pytest.raises(ValueError):
+            persist.load(other, path)
+    # and a cache with the tier refuses a state saved without it
+    plain = str(tmp_path / "plain.safetensors")
+    persist.save(_filled(_cfg(), 3, 44, 12), plain)
+    with pytest.raises(ValueError):
+        persist.load(fade.TieredCache(cfg, 3, 44, device="cpu"), plain)

@@ -185,7 +185,7 @@ const char* fade_status_string(int status) {
   }
 }
 
-int fade_abi_version(void) { return 300; }
+int fade_abi_version(void) { return 301; }
 
 int fade_quantize_pack(const fade_config* cfg, const void* src, int64_t n_rows, int64_t src_row_stride,
                        const int32_t* src_row_idx, const int32_t* dst_row_idx, int32_t bits, void* codes,
@@ -384,16 +384,18 @@ size_t fade_cache_workspace_bytes(const fade_config* cfg, const fade_layer_cache
 }
 
 uint64_t fade_compressed_bytes(const fade_config* cfg, const int32_t* fp16_slots, const int32_t* mid_slots,
-                               int32_t n) {
+                               const int32_t* low_slots, int32_t n) {
   if (check_cfg(cfg) || n < 0 || (n > 0 && (!fp16_slots || !mid_slots))) return 0;
   const uint64_t d = (uint64_t)cfg->head_dim;
   const uint64_t per_fp = (uint64_t)cfg->n_kv_heads * d * 4;
   const uint64_t per_mid = (uint64_t)cfg->n_kv_heads *
                            ((d * cfg->middle_k_bits / 8 + 2 * d / 32) + (d * cfg->middle_v_bits / 8 + 2 * d / 32));
+  const uint64_t per_low = (uint64_t)cfg->n_kv_heads * 2 * (d * kLowBits / 8 + 2 * d / 32);
   uint64_t total = 0;
   for (int32_t i = 0; i < n; ++i) {
-    if (fp16_slots[i] < 0 || mid_slots[i] < 0) return 0;
+    if (fp16_slots[i] < 0 || mid_slots[i] < 0 || (low_slots && low_slots[i] < 0)) return 0;
     total += (uint64_t)fp16_slots[i] * per_fp + (uint64_t)mid_slots[i] * per_mid;
+    if (low_slots) total += (uint64_t)low_slots[i] * per_low;
   }
   return total;
 }

@@ -76,7 +76,7 @@ _SIGS = {
                                         ctypes.c_int32, _P]),
     "fade_workspace_bytes": (ctypes.c_size_t, [_CFG, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]),
     "fade_cache_workspace_bytes": (ctypes.c_size_t, [_CFG, _CACHE, ctypes.c_int32, ctypes.c_int32]),
-    "fade_compressed_bytes": (ctypes.c_uint64, [_CFG, _P, _P, ctypes.c_int32]),
+    "fade_compressed_bytes": (ctypes.c_uint64, [_CFG, _P, _P, _P, ctypes.c_int32]),
     "fade_pq_encode": (ctypes.c_int, [ctypes.c_int32, _P, ctypes.c_int64, _P, _P, _P]),
     "fade_pq_decode": (ctypes.c_int, [ctypes.c_int32, _P, ctypes.c_int64, _P, _P, _P]),
     "fade_pq_train_step": (ctypes.c_int, [ctypes.c_int32, _P, ctypes.c_int64, _P, _P, _P, ctypes.c_size_t, _P]),
@@ -272,12 +272,16 @@ def fade_rope_rotate(cfg, x, dtype, n_rows, positions=None, pos_base=0, pos_peri
                                   _s(stream)), "fade_rope_rotate")
 
 
-def fade_compressed_bytes(cfg, fp16_slots, mid_slots):
+def fade_compressed_bytes(cfg, fp16_slots, mid_slots, low_slots=None):
     import numpy as np
     a = np.ascontiguousarray(fp16_slots, dtype=np.int32)
     b = np.ascontiguousarray(mid_slots, dtype=np.int32)
+    c = None if low_slots is None else np.ascontiguousarray(low_slots, dtype=np.int32)
+    if c is not None and c.shape != a.shape:
+        raise ValueError("low_slots needs one entry per fp16 entry")
     return int(lib().fade_compressed_bytes(ctypes.byref(cfg), a.ctypes.data_as(ctypes.c_void_p),
-                                           b.ctypes.data_as(ctypes.c_void_p), len(a)))
+                                           b.ctypes.data_as(ctypes.c_void_p),
+                                           None if c is None else c.ctypes.data_as(ctypes.c_void_p), len(a)))
 
 
 # ---- product-quantization codebook -------------------------------------------
