@@ -30,7 +30,8 @@ Modules:
               optional INT2 overflow tier (int2_budget) and its two-level
               event (demote the INT4 overflow, drop the INT2 overflow)
   accounting  compressed-bytes closed form
-  pq          product-quantization codebook: Lloyd training, encode, decode
+  pq          product-quantization codebook: Lloyd training, encode, decode;
+              cache.middle_pq stores the middle tier as PQ codes
 
 Parity status: every function here is pinned by `tests/test_oracle_*.py`
 against closed forms, library routines, invariants or brute force.

@@ -57,12 +57,26 @@ on when int2_budget >= 0:
   * Tokens only move down the tiers: an INT2 slot is never promoted back.
   * At prefill the build keeps int4_budget + int2_budget candidates in the
     INT4 layout, then the same event demotes the int2_budget lowest of them.
+
+PQ middle tier (FADE post, "产品量化（PQ）": the product-quantization codebook
+as the alternative to the INT2 compression of cached vectors), on when
+middle_pq is set: the middle tier stores each token's K and V as PQ codes
+(uint8 per sub-space, oracle.pq) under the layer's two codebooks instead of
+INTb codes with scales. Everything else is the tiered cache above:
+  * demotion and the prefill build encode the fp16 row (the re-rotated key
+    at prefill) by its nearest centroids;
+  * attention reads the centroids the codes name;
+  * an eviction moves value codes unchanged; a surviving key whose slot
+    changes is decoded, re-rotated from its old slot to its new one, rounded
+    once to fp16 and encoded again (the PQ counterpart of dequantize ->
+    rotate -> requantize).
+The INT2 overflow tier and a PQ middle are not combined.
 """
 from dataclasses import dataclass, field, replace
 
 import numpy as np
 
-from . import quant, rope
+from . import pq, quant, rope
 from .attention import decode_attention
 from .h2o import update_accum, update_ema
 
@@ -87,6 +101,7 @@ class Config:
     rope_seq_len: int = 0
     rope_interleaved: bool = False
     int2_budget: int = -1       # INT2 overflow tier capacity after an event; -1: no such tier
+    middle_pq: bool = False     # middle tier as PQ codes under the layer's codebooks
 
     def freqs(self):
         return rope.inv_freq(self.head_dim, self.rope_theta, self.rope_type,
@@ -129,6 +144,8 @@ class SeqCache:
     low_k_s: np.ndarray = field(default=None)  # float16 scales [Hkv, M2, d/G]
     low_v_u: np.ndarray = field(default=None)
     low_v_s: np.ndarray = field(default=None)
+    pq_k_cb: np.ndarray = field(default=None)  # fp16 [32, 256, d/32] (PQ middle tier)
+    pq_v_cb: np.ndarray = field(default=None)
 
     def __post_init__(self):
         if self.low_k_u is None:
@@ -160,8 +177,12 @@ class SeqCache:
         """(k_hat, v_hat) float64 [Hkv, T, d] in slot order."""
         c = self.cfg
         g = c.group_size
-        mk = quant.dequantize(self.mid_k_u, self.mid_k_s, c.middle_k_bits, g)
-        mv = quant.dequantize(self.mid_v_u, self.mid_v_s, c.middle_v_bits, g)
+        if c.middle_pq:
+            mk = pq_decode_rows(self.mid_k_u, self.pq_k_cb).astype(np.float64)
+            mv = pq_decode_rows(self.mid_v_u, self.pq_v_cb).astype(np.float64)
+        else:
+            mk = quant.dequantize(self.mid_k_u, self.mid_k_s, c.middle_k_bits, g)
+            mv = quant.dequantize(self.mid_v_u, self.mid_v_s, c.middle_v_bits, g)
         lk = quant.dequantize(self.low_k_u, self.low_k_s, LOW_BITS, g)
         lv = quant.dequantize(self.low_v_u, self.low_v_s, LOW_BITS, g)
         k = np.concatenate([self.sink_k.astype(np.float64), lk, mk,
@@ -178,14 +199,53 @@ def _empty_codes(hkv, d, g):
     return (np.zeros((hkv, 0, d), np.uint8), np.zeros((hkv, 0, d // g), np.float16))
 
 
-def build_from_prefill(cfg, k16, v16, scores=None):
+def pq_encode_rows(x16, codebook):
+    """fp16 rows [Hkv, n, d] -> (codes uint8 [Hkv, n, 32], empty scales
+    [Hkv, n, 0]): the PQ middle tier's storage of the rows."""
+    x16 = np.asarray(x16, np.float16)
+    hkv, n, d = x16.shape
+    if n == 0:
+        codes = np.zeros((hkv, 0, pq.N_SUB), np.uint8)
+    else:
+        codes = np.stack([pq.encode(x16[h], codebook) for h in range(hkv)])
+    return codes, np.zeros((hkv, n, 0), np.float16)
+
+
+def pq_decode_rows(codes, codebook):
+    """codes uint8 [Hkv, n, 32] -> fp16 [Hkv, n, d]."""
+    codes = np.asarray(codes)
+    hkv, n, _ = codes.shape
+    cb = np.asarray(codebook, np.float16)
+    if n == 0:
+        return np.zeros((hkv, 0, cb.shape[0] * cb.shape[2]), np.float16)
+    return np.stack([pq.decode(codes[h], cb) for h in range(hkv)])
+
+
+def _mid_quantize(cfg, k16, v16, codebooks):
+    """Middle-tier storage of fp16 rows k16, v16 [Hkv, n, d]: INTb codes with
+    scales, or PQ codes under codebooks = (key codebook, value codebook)."""
+    if cfg.middle_pq:
+        return pq_encode_rows(k16, codebooks[0]) + pq_encode_rows(v16, codebooks[1])
+    hkv, n, d = k16.shape
+    if n == 0:
+        return _empty_codes(hkv, d, cfg.group_size) + _empty_codes(hkv, d, cfg.group_size)
+    return (quant.quantize(k16, cfg.middle_k_bits, cfg.group_size) +
+            quant.quantize(v16, cfg.middle_v_bits, cfg.group_size))
+
+
+def build_from_prefill(cfg, k16, v16, scores=None, pq_codebooks=None):
     """Tiered cache from a prefill of L tokens.
 
     k16, v16: fp16 [Hkv, L, d], keys rotated at positions 0..L-1.
     scores: float64 [L] H2O prefill scores, or None for the position policy
-    (older middle tokens evicted first)."""
+    (older middle tokens evicted first). pq_codebooks: (key, value) fp16
+    [32, 256, d/32] codebooks of a PQ middle tier (cfg.middle_pq)."""
     k16 = np.asarray(k16, dtype=np.float16)
     v16 = np.asarray(v16, dtype=np.float16)
+    if cfg.middle_pq:
+        if pq_codebooks is None or cfg.int2_budget >= 0:
+            raise ValueError("a PQ middle tier needs its codebooks and no INT2 overflow tier")
+        pq_codebooks = tuple(np.asarray(c, np.float16) for c in pq_codebooks)
     if cfg.int2_budget >= 0:
         # the INT4 layout first holds int4_budget + int2_budget candidates;
         # the event that follows demotes the lowest int2_budget of them
@@ -212,19 +272,14 @@ def build_from_prefill(cfg, k16, v16, scores=None):
                                             survivors[moved], new_pos[moved], freqs, cfg.rope_interleaved)
     v_surv = v16[:, survivors]
     m2 = kept_mid.size
-    mk = k_surv[:, s:s + m2]
-    mv = v_surv[:, s:s + m2]
-    g = cfg.group_size
-    if m2:
-        mk_u, mk_s = quant.quantize(mk, cfg.middle_k_bits, g)
-        mv_u, mv_s = quant.quantize(mv, cfg.middle_v_bits, g)
-    else:
-        mk_u, mk_s = _empty_codes(hkv, d, g)
-        mv_u, mv_s = _empty_codes(hkv, d, g)
+    mk_u, mk_s, mv_u, mv_s = _mid_quantize(cfg, k_surv[:, s:s + m2], v_surv[:, s:s + m2], pq_codebooks)
     sc = (np.zeros(survivors.size) if scores is None
           else np.asarray(scores, np.float64)[survivors].copy())
-    return SeqCache(cfg, k_surv[:, :s].copy(), v_surv[:, :s].copy(), mk_u, mk_s, mv_u, mv_s,
-                    k_surv[:, s + m2:].copy(), v_surv[:, s + m2:].copy(), sc)
+    cache = SeqCache(cfg, k_surv[:, :s].copy(), v_surv[:, :s].copy(), mk_u, mk_s, mv_u, mv_s,
+                     k_surv[:, s + m2:].copy(), v_surv[:, s + m2:].copy(), sc)
+    if cfg.middle_pq:
+        cache.pq_k_cb, cache.pq_v_cb = pq_codebooks
+    return cache
 
 
 def append(cache, k_new16, v_new16):
@@ -254,8 +309,7 @@ def demote(cache):
     c = cache.cfg
     while cache.rec_len > c.recent_window:
         k0, v0 = cache.rec_k[:, :1], cache.rec_v[:, :1]
-        ku, ks = quant.quantize(k0, c.middle_k_bits, c.group_size)
-        vu, vs = quant.quantize(v0, c.middle_v_bits, c.group_size)
+        ku, ks, vu, vs = _mid_quantize(c, k0, v0, (cache.pq_k_cb, cache.pq_v_cb))
         cache.mid_k_u = np.concatenate([cache.mid_k_u, ku], axis=1)
         cache.mid_k_s = np.concatenate([cache.mid_k_s, ks], axis=1)
         cache.mid_v_u = np.concatenate([cache.mid_v_u, vu], axis=1)
@@ -301,9 +355,14 @@ def evict(cache, budget, policy="score", evicted=None, dropped=None):
     # Without a rotary embedding (every frequency 0) there is nothing to
     # re-rotate: moved keys keep their codes and scales, like values.
     if moved.any() and c.freqs().any():
-        khat = quant.dequantize(mk_u[:, moved], mk_s[:, moved], c.middle_k_bits, g)
-        rot = rope.rerope_fp16(khat, old_pos[moved], new_pos[moved], freqs, c.rope_interleaved)
-        u2, s2 = quant.quantize(rot, c.middle_k_bits, g)
+        if c.middle_pq:
+            khat = pq_decode_rows(mk_u[:, moved], cache.pq_k_cb)
+            rot = rope.rerope_fp16(khat, old_pos[moved], new_pos[moved], freqs, c.rope_interleaved)
+            u2, s2 = pq_encode_rows(rot, cache.pq_k_cb)
+        else:
+            khat = quant.dequantize(mk_u[:, moved], mk_s[:, moved], c.middle_k_bits, g)
+            rot = rope.rerope_fp16(khat, old_pos[moved], new_pos[moved], freqs, c.rope_interleaved)
+            u2, s2 = quant.quantize(rot, c.middle_k_bits, g)
         mk_u[:, moved] = u2
         mk_s[:, moved] = s2
     cache.mid_k_u, cache.mid_k_s = mk_u, mk_s
@@ -331,6 +390,8 @@ def evict_tiered(cache, budget, policy="score", demoted=None, dropped=None):
     choice (tests following the device inside a near-tie band)."""
     c = cache.cfg
     g = c.group_size
+    if c.middle_pq:
+        raise ValueError("the INT2 overflow tier and a PQ middle tier are not combined")
     s, m4, m2, r = cache.n_sink_live, cache.mid_len, cache.low_len, cache.rec_len
     sc = cache.scores
     n_dem = m4 - budget if 0 <= budget < m4 else 0
