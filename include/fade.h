@@ -126,6 +126,19 @@ enum fade_ws_op {
  *                   re-rotated to their new slot - and only the INT2 tier's
  *                   own overflow is evicted. Slot order: sinks, INT2 tier,
  *                   INT4 middle, recent. Needs int4_budget >= 0.
+ *   middle_pq       0 or 1. 1: the middle tier stores K and V as product-
+ *                   quantization codes (FADE post, "产品量化（PQ）": the
+ *                   codebook as the alternative to INT2), one uint8 per
+ *                   sub-space (32 sub-vectors of head_dim / 32 elements)
+ *                   under the layer's key and value codebooks
+ *                   (fade_layer_cache.pq_*_codebook); middle_k_bits and
+ *                   middle_v_bits are then unused. Demotion and the prefill
+ *                   build encode each fp16 row by nearest centroids (as
+ *                   fade_pq_encode); attention reads the centroids; an
+ *                   eviction moves value codes and re-encodes a moved key
+ *                   after decoding it and re-rotating it to its new slot.
+ *                   Not combined with the INT2 overflow tier
+ *                   (FADE_ERR_UNSUPPORTED).
  */
 typedef struct fade_config {
   int32_t head_dim;
@@ -147,6 +160,7 @@ typedef struct fade_config {
   int32_t out_dtype;
   int32_t rope_seq_len;
   int32_t int2_budget;
+  int32_t middle_pq;
 } fade_config;
 
 /*
@@ -177,6 +191,11 @@ typedef struct fade_config {
  *                   head_dim / 4] for K and for V, scales fp16 [batch, Hkv,
  *                   cap_low, head_dim / 32]; low_lens int32 [batch] = the
  *                   tier's live rows (kernels only). cap_low >= int2_budget.
+ *   pq_k_codebook,  PQ middle tier (cfg->middle_pq = 1, otherwise ignored):
+ *   pq_v_codebook   fp16 [32][256][head_dim / 32] each, 16-byte aligned;
+ *                   mid_k_codes / mid_v_codes are then u8 [batch, Hkv,
+ *                   cap_mid, 32] (16-byte aligned) and the scale arrays are
+ *                   unused (may be NULL).
  * cap_T = n_sink + cap_mid + recent_window + 1, plus cap_low with an INT2
  * tier.
  * Positions: a slot's RoPE position is its index in the compacted cache:
@@ -203,12 +222,14 @@ typedef struct fade_layer_cache {
   void* low_k_scales;
   void* low_v_scales;
   int32_t* low_lens;
+  const void* pq_k_codebook;
+  const void* pq_v_codebook;
 } fade_layer_cache;
 
 /* Human-readable name of a status code; never NULL. */
 const char* fade_status_string(int status);
 
-/* ABI version of this header (major * 100 + minor): 301. */
+/* ABI version of this header (major * 100 + minor): 302. */
 int fade_abi_version(void);
 
 /*
@@ -390,8 +411,10 @@ size_t fade_cache_workspace_bytes(const fade_config* cfg, const fade_layer_cache
  *   Hkv * (fp16_slots[i] * d * 4 + mid_slots[i] * ((d*kb/8 + 2d/32) + (d*vb/8 + 2d/32))
  *          + low_slots[i] * 2 * (d*2/8 + 2d/32)),
  * the last term for the INT2 overflow tier (K and V at 2 bits); low_slots
- * may be NULL (no such tier). One entry per (layer, sequence). Returns 0 on
- * invalid arguments.
+ * may be NULL (no such tier). With a PQ middle tier (cfg->middle_pq) a middle
+ * slot is Hkv * 2 * 32 bytes (one code per sub-space for K and for V; the
+ * codebooks are per-layer parameters). One entry per (layer, sequence).
+ * Returns 0 on invalid arguments.
  */
 uint64_t fade_compressed_bytes(const fade_config* cfg, const int32_t* fp16_slots,
                                const int32_t* mid_slots, const int32_t* low_slots, int32_t n);

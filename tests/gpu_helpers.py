@@ -29,7 +29,8 @@ ROPE_KW = {
 def ocfg(c):
     return oc.Config(head_dim=c.head_dim, n_q_heads=c.n_q_heads, n_kv_heads=c.n_kv_heads, n_sink=c.n_sink,
                      recent_window=c.recent_window, int4_budget=c.int4_budget, middle_k_bits=c.middle_k_bits,
-                     middle_v_bits=c.middle_v_bits, int2_budget=c.int2_budget, group_size=32,
+                     middle_v_bits=c.middle_v_bits, int2_budget=c.int2_budget,
+                     middle_pq=bool(c.middle_pq), group_size=32,
                      rope_theta=c.rope_theta,
                      rope_type=ROPE_NAMES[c.rope_type & fade.ROPE_SCHEME_MASK], rope_factor=c.rope_factor,
                      rope_low_freq_factor=c.rope_low_freq_factor, rope_high_freq_factor=c.rope_high_freq_factor,
@@ -65,10 +66,13 @@ def seq_state(tc, b):
     slots = [c.n_sink + (head + i) % ring for i in range(R)]
     fk = tc.fp_k[b].cpu().numpy()
     fv = tc.fp_v[b].cpu().numpy()
+    hkv = fk.shape[0]
+    no_scales = np.zeros((hkv, M, 0), np.float16)          # a PQ middle tier has none
     st = dict(S=S, M=M, R=R, head=head, sink_k=fk[:, :S], sink_v=fv[:, :S], rec_k=fk[:, slots],
               rec_v=fv[:, slots], mid_k=tc.mid_k_codes[b, :, :M].cpu().numpy(),
-              mid_ks=tc.mid_k_scales[b, :, :M].cpu().numpy(), mid_v=tc.mid_v_codes[b, :, :M].cpu().numpy(),
-              mid_vs=tc.mid_v_scales[b, :, :M].cpu().numpy(), M2=0)
+              mid_ks=no_scales if tc.mid_k_scales is None else tc.mid_k_scales[b, :, :M].cpu().numpy(),
+              mid_v=tc.mid_v_codes[b, :, :M].cpu().numpy(),
+              mid_vs=no_scales if tc.mid_v_scales is None else tc.mid_v_scales[b, :, :M].cpu().numpy(), M2=0)
     if getattr(tc, "low", False):
         M2 = int(tc.low_lens[b].cpu())
         st.update(M2=M2, low_k=tc.low_k_codes[b, :, :M2].cpu().numpy(), low_ks=tc.low_k_scales[b, :, :M2].cpu().numpy(),
@@ -97,10 +101,14 @@ def assert_state_equal(st, ref, check_scores=True):
     _same("sink_v", bits16(st["sink_v"]), bits16(ref.sink_v))
     _same("rec_v", bits16(st["rec_v"]), bits16(ref.rec_v))
     _same("rec_k", bits16(st["rec_k"]), bits16(ref.rec_k))
-    _same("mid_k", st["mid_k"], quant.pack(ref.mid_k_u, c.middle_k_bits))
-    _same("mid_ks", bits16(st["mid_ks"]), bits16(ref.mid_k_s))
-    _same("mid_v", st["mid_v"], quant.pack(ref.mid_v_u, c.middle_v_bits))
-    _same("mid_vs", bits16(st["mid_vs"]), bits16(ref.mid_v_s))
+    if c.middle_pq:                                       # one code byte per sub-space
+        _same("mid_k", st["mid_k"], ref.mid_k_u)
+        _same("mid_v", st["mid_v"], ref.mid_v_u)
+    else:
+        _same("mid_k", st["mid_k"], quant.pack(ref.mid_k_u, c.middle_k_bits))
+        _same("mid_ks", bits16(st["mid_ks"]), bits16(ref.mid_k_s))
+        _same("mid_v", st["mid_v"], quant.pack(ref.mid_v_u, c.middle_v_bits))
+        _same("mid_vs", bits16(st["mid_vs"]), bits16(ref.mid_v_s))
     assert st.get("M2", 0) == ref.low_len
     if ref.low_len:
         _same("low_k", st["low_k"], quant.pack(ref.low_k_u, 2))
@@ -111,19 +119,22 @@ def assert_state_equal(st, ref, check_scores=True):
         assert np.array_equal(st["scores"].astype(np.float64), ref.scores)
 
 
-def build_both(cfg, batch, L, seed, cap_mid, scores32=None, shared=False, cap_low=None):
+def build_both(cfg, batch, L, seed, cap_mid, scores32=None, shared=False, cap_low=None, pq_cb=None):
     """Build the same prefill on the GPU (fade_prefill_build) and in the
-    oracle. scores32: float32 [rows, L] H2O scores (rows = 1 if shared)."""
+    oracle. scores32: float32 [rows, L] H2O scores (rows = 1 if shared).
+    pq_cb: (key, value) fp16 codebooks of a PQ middle tier."""
     k16, v16, raw = prefill_inputs(cfg, batch, L, seed)
-    tc = fade.TieredCache(cfg, batch, cap_mid, shared=shared, cap_low=cap_low)
-    ws = fade.workspace(cfg, fade.WS_PREFILL_BUILD, batch, L, cache=tc if cap_low is not None else None)
+    tc = fade.TieredCache(cfg, batch, cap_mid, shared=shared, cap_low=cap_low,
+                          pq_codebooks=None if pq_cb is None else tuple(dev16(x) for x in pq_cb))
+    ws = fade.workspace(cfg, fade.WS_PREFILL_BUILD, batch, L,
+                        cache=tc if (cap_low is not None or pq_cb is not None) else None)
     sc_dev = None if scores32 is None else torch.from_numpy(np.ascontiguousarray(scores32, np.float32)).to(DEV)
     fade.fade_prefill_build(cfg, tc, dev16(k16), dev16(v16), L, sc_dev, ws)
     oc_cfg = ocfg(cfg)
     refs = []
     for b in range(batch):
         s = None if scores32 is None else scores32[0 if shared else b].astype(np.float64)
-        refs.append(oc.build_from_prefill(oc_cfg, k16[b], v16[b], s))
+        refs.append(oc.build_from_prefill(oc_cfg, k16[b], v16[b], s, pq_cb))
     torch.cuda.synchronize()
     return tc, refs, (k16, v16, raw)
 

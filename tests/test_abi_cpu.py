@@ -32,7 +32,7 @@ def test_library_exports_every_header_function():
 
 def test_status_strings_and_version():
     lib = fade.lib()
-    assert lib.fade_abi_version() == 301
+    assert lib.fade_abi_version() == 302
     for s in range(6):
         assert lib.fade_status_string(s)
     assert lib.fade_status_string(99) == b"unknown status"
@@ -45,14 +45,33 @@ def _cfg(**kw):
     return fade.make_config(**base)
 
 
-def test_struct_layout_matches_header():
-    # fade_config: 10 int32, 4 double, 5 int32 -> 40 + 32 + 20 = 92, padded to 96
-    assert ctypes.sizeof(fade.FadeConfig) == 96
-    assert fade.FadeConfig.rope_theta.offset == 40
-    assert fade.FadeConfig.int2_budget.offset == 88
-    # fade_layer_cache: 4 int32, 8 pointers, 2 int32, 5 pointers
-    assert ctypes.sizeof(fade.LayerCache) == 16 + 8 * 8 + 8 + 5 * 8
-    assert fade.LayerCache.cap_low.offset == 80 and fade.LayerCache.low_lens.offset == 120
+def test_struct_layout_matches_header(tmp_path):
+    """The ctypes structs have the C header's layout: every field's offset and
+    both sizes, as a C compiler lays out include/fade.h."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    lines = ['#include <stddef.h>', '#include <stdio.h>', '#include "fade.h"', "int main(void) {"]
+    for cname, cls in (("fade_config", fade.FadeConfig), ("fade_layer_cache", fade.LayerCache)):
+        lines.append(f'  printf("{cname} sizeof %zu\\n", sizeof({cname}));')
+        for fname, _ in cls._fields_:
+            lines.append(f'  printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run([cc, "-I", inc, str(src), "-o", str(exe)], check=True)
+    got = {}
+    for line in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.splitlines():
+        cname, field, val = line.split()
+        got[(cname, field)] = int(val)
+    for cname, cls in (("fade_config", fade.FadeConfig), ("fade_layer_cache", fade.LayerCache)):
+        assert got[(cname, "sizeof")] == ctypes.sizeof(cls), cname
+        for fname, _ in cls._fields_:
+            assert got[(cname, fname)] == getattr(cls, fname).offset, (cname, fname)
 
 
 @pytest.mark.parametrize("d,hkv,kb,vb", [(128, 8, 4, 2), (64, 8, 4, 4), (128, 2, 2, 2)])
@@ -172,6 +191,24 @@ def test_validation_rejects_before_launch():
     assert lib.fade_cache_demote(ctypes.byref(cfg2), ctypes.byref(c2), null) == fade.FADE_ERR_INVALID_ARG
     c2 = fade.LayerCache(1, 10, 4 + 10 + 20 + 65, 0, 16, 16, 16, 16, 16, 16, 16, None, 20, 0, 16, 16, 16, 16, None)
     assert lib.fade_cache_demote(ctypes.byref(cfg2), ctypes.byref(c2), null) == fade.FADE_ERR_INVALID_ARG
+    # PQ middle tier: not with the INT2 tier; codebooks required, 16-byte
+    # aligned; the scale arrays are unused (NULL passes the check, which then
+    # stops at the missing workspace)
+    bad = _cfg(middle_pq=True, int2_budget=4)
+    assert lib.fade_rope_rotate(ctypes.byref(bad), null, 0, 1, null, 0, 1, null) == fade.FADE_ERR_UNSUPPORTED
+    bad = _cfg()
+    bad.middle_pq = 2
+    assert lib.fade_rope_rotate(ctypes.byref(bad), null, 0, 1, null, 0, 1, null) == fade.FADE_ERR_INVALID_ARG
+    cpq = _cfg(middle_pq=True)
+    for kcb, vcb in ((None, 16), (16, None), (24, 16)):
+        c3 = fade.LayerCache(1, 4096, 4 + 4096 + 65, 0, 16, 16, 16, 16, None, None, 16, None, 0, 0,
+                             None, None, None, None, None, kcb, vcb)
+        assert lib.fade_cache_demote(ctypes.byref(cpq), ctypes.byref(c3), null) == fade.FADE_ERR_INVALID_ARG
+    c3 = fade.LayerCache(1, 4096, 4 + 4096 + 65, 0, 16, 16, 16, 16, None, None, 16, None, 0, 0,
+                         None, None, None, None, None, 16, 16)
+    st = lib.fade_tiered_decode_attn(ctypes.byref(cpq), ctypes.byref(c3), ctypes.c_void_p(16),
+                                     ctypes.c_void_p(16), null, null, 0, null)
+    assert st == fade.FADE_ERR_WORKSPACE
     # misaligned kept-slot output
     st = lib.fade_evict_rerope(ctypes.byref(cfg), ctypes.byref(c), fade.POLICY_POSITION, 0, ctypes.c_void_p(18),
                                null, 0, null)

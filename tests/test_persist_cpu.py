@@ -160,3 +160,27 @@ def test_int2_tier_round_trip_telemetry_and_refusals(tmp_path):
     persist.save(_filled(_cfg(), 3, 44, 12), plain)
     with pytest.raises(ValueError):
         persist.load(fade.TieredCache(cfg, 3, 44, device="cpu"), plain)
+
+
+def test_pq_middle_round_trip(tmp_path):
+    """A PQ middle tier travels with its codebooks and has no scale arrays."""
+    cfg = _cfg(middle_pq=True)
+    gen = synth.rng(21)
+    cb = tuple(torch.from_numpy(synth.normal(gen, 32, 256, 2).astype(np.float16)) for _ in range(2))
+    a = fade.TieredCache(cfg, 2, 30, device="cpu", pq_codebooks=cb)
+    assert a.mid_k_scales is None and a.mid_k_codes.shape == (2, 2, 30, 32)
+    a.mid_k_codes.copy_(torch.from_numpy(gen.integers(0, 256, size=a.mid_k_codes.shape).astype(np.uint8)))
+    a.mid_v_codes.copy_(torch.from_numpy(gen.integers(0, 256, size=a.mid_v_codes.shape).astype(np.uint8)))
+    a.lens.copy_(torch.tensor([[4, 17, 8, 3], [4, 30, 8, 0]], dtype=torch.int32))
+    path = str(tmp_path / "pq.safetensors")
+    persist.save(a, path)
+    cb2 = tuple(torch.zeros(32, 256, 2, dtype=torch.float16) for _ in range(2))
+    b = fade.TieredCache(cfg, 2, 32, device="cpu", pq_codebooks=cb2)
+    persist.load(b, path)
+    assert torch.equal(b.pq_k_codebook, cb[0]) and torch.equal(b.pq_v_codebook, cb[1])
+    assert torch.equal(a.mid_k_codes[:, :, :30], b.mid_k_codes[:, :, :30])
+    with pytest.raises(ValueError):
+        persist.load(fade.TieredCache(_cfg(), 2, 32, device="cpu"), path)
+    rec = persist.layer_record(a, 0)
+    want = accounting.compressed_bytes(64, 2, 4, 2, 32, [12, 12], [17, 30], middle_pq=True)
+    assert rec["compressed_bytes"] == want

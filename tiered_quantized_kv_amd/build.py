@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfade.so")
-SOURCES = ["k_quant.hip", "k_decode.hip", "k_h2o.hip", "k_evict.hip", "k_pq.hip", "fade_api.hip"]
+SOURCES = ["k_quant.hip", "k_decode.hip", "k_h2o.hip", "k_evict.hip", "k_pq.hip", "k_pq_tier.hip", "fade_api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

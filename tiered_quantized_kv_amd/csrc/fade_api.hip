@@ -47,6 +47,8 @@ int check_cfg(const fade_config* c) {
     return FADE_ERR_UNSUPPORTED;
   // the INT2 overflow tier takes the INT4 tier's overflow, so it needs a budget
   if (c->int2_budget < -1 || (c->int2_budget >= 0 && c->int4_budget < 0)) return FADE_ERR_INVALID_ARG;
+  if (c->middle_pq != 0 && c->middle_pq != 1) return FADE_ERR_INVALID_ARG;
+  if (c->middle_pq && c->int2_budget >= 0) return FADE_ERR_UNSUPPORTED;
   return FADE_OK;
 }
 
@@ -69,6 +71,7 @@ Shape make_shape(const fade_config* c, int batch, int cap_mid, int cap_T, int sh
   s.low = c->int2_budget >= 0 ? 1 : 0;
   s.low_budget = s.low ? c->int2_budget : 0;
   s.cap_low = s.low ? cap_low : 0;
+  s.pq = c->middle_pq;
   return s;
 }
 Shape cache_shape(const fade_config* c, const fade_layer_cache* k) {
@@ -100,11 +103,15 @@ int check_cache(const fade_config* c, const fade_layer_cache* k) {
     if (!k->mid_k_codes || !k->mid_v_codes || !aligned16(k->mid_k_codes) || !aligned16(k->mid_v_codes))
       return FADE_ERR_INVALID_ARG;
     // the kernels read a row's scales as one vector: 8 bytes at head_dim 128,
-    // 4 bytes at 64
+    // 4 bytes at 64 (a PQ middle tier has none)
     const uintptr_t sa = c->head_dim == 128 ? 8 : 4;
-    if (!k->mid_k_scales || !k->mid_v_scales || !aligned(k->mid_k_scales, sa) || !aligned(k->mid_v_scales, sa))
+    if (!c->middle_pq &&
+        (!k->mid_k_scales || !k->mid_v_scales || !aligned(k->mid_k_scales, sa) || !aligned(k->mid_v_scales, sa)))
       return FADE_ERR_INVALID_ARG;
   }
+  if (c->middle_pq && (!k->pq_k_codebook || !k->pq_v_codebook || !aligned16(k->pq_k_codebook) ||
+                       !aligned16(k->pq_v_codebook)))
+    return FADE_ERR_INVALID_ARG;
   if (k->scores && !aligned(k->scores, 4)) return FADE_ERR_INVALID_ARG;
   if (c->int4_budget > k->cap_mid) return FADE_ERR_CAPACITY;
   return FADE_OK;
@@ -185,7 +192,7 @@ const char* fade_status_string(int status) {
   }
 }
 
-int fade_abi_version(void) { return 301; }
+int fade_abi_version(void) { return 302; }
 
 int fade_quantize_pack(const fade_config* cfg, const void* src, int64_t n_rows, int64_t src_row_stride,
                        const int32_t* src_row_idx, const int32_t* dst_row_idx, int32_t bits, void* codes,
@@ -219,7 +226,8 @@ int fade_cache_demote(const fade_config* cfg, fade_layer_cache* cache, void* str
   if (st) return st;
   if ((st = check_cache(cfg, cache))) return st;
   const Shape s = cache_shape(cfg, cache);
-  return hip_status(launch_demote(s, *cache, reinterpret_cast<hipStream_t>(stream)));
+  return hip_status(s.pq ? launch_demote_pq(s, *cache, reinterpret_cast<hipStream_t>(stream))
+                        : launch_demote(s, *cache, reinterpret_cast<hipStream_t>(stream)));
 }
 
 int fade_tiered_decode_attn(const fade_config* cfg, const fade_layer_cache* cache, const void* q, void* out,
@@ -285,8 +293,10 @@ int fade_evict_rerope(const fade_config* cfg, fade_layer_cache* cache, int32_t p
   if (policy == FADE_POLICY_SCORE && !cache->scores) return FADE_ERR_INVALID_ARG;
   if (kept_slots_out && !aligned(kept_slots_out, 4)) return FADE_ERR_INVALID_ARG;
   const Shape s = cache_shape(cfg, cache);
-  if (s.low) {
-    // INT2 overflow tier: demote the INT4 overflow, drop the INT2 overflow
+  if (s.low || s.pq) {
+    // INT2 overflow tier: demote the INT4 overflow, drop the INT2 overflow;
+    // PQ middle tier: the same staged event with no INT2 tier (every row over
+    // the budget is dropped), moved keys re-encoded
     if (!workspace || !aligned16(workspace) || ws_bytes < tier_event_ws_bytes(s)) return FADE_ERR_WORKSPACE;
     return hip_status(launch_tier_event(s, *cache, policy, host_freqs(cfg), kept_slots_out, workspace,
                                         reinterpret_cast<hipStream_t>(stream)));
@@ -353,7 +363,7 @@ size_t fade_workspace_bytes(const fade_config* cfg, int32_t op, int32_t batch, i
       return h2o_ws_bytes(cfg->head_dim, cfg->n_q_heads, cfg->n_kv_heads, batch, max_len);
     case FADE_WS_EVICT: {
       const Shape s = make_shape(cfg, batch, max_len, cap_T, 0, cap_low);
-      if (s.low) return tier_event_ws_bytes(s);
+      if (s.low || s.pq) return tier_event_ws_bytes(s);
       const int full = cfg->int4_budget >= 0 ? max_len - cfg->int4_budget : 0;
       return evict_ws_bytes(s, full > 0 ? full : 1);
     }
@@ -372,7 +382,7 @@ size_t fade_cache_workspace_bytes(const fade_config* cfg, const fade_layer_cache
     case FADE_WS_DECODE:
       return decode_ws_bytes(s);
     case FADE_WS_EVICT: {
-      if (s.low) return tier_event_ws_bytes(s);
+      if (s.low || s.pq) return tier_event_ws_bytes(s);
       const int me = cfg->int4_budget < 0 ? 0 : decode_max_evict(cfg, cache, 0);
       return me > 0 ? evict_ws_bytes(s, me) : 0;
     }
@@ -388,8 +398,9 @@ uint64_t fade_compressed_bytes(const fade_config* cfg, const int32_t* fp16_slots
   if (check_cfg(cfg) || n < 0 || (n > 0 && (!fp16_slots || !mid_slots))) return 0;
   const uint64_t d = (uint64_t)cfg->head_dim;
   const uint64_t per_fp = (uint64_t)cfg->n_kv_heads * d * 4;
-  const uint64_t per_mid = (uint64_t)cfg->n_kv_heads *
-                           ((d * cfg->middle_k_bits / 8 + 2 * d / 32) + (d * cfg->middle_v_bits / 8 + 2 * d / 32));
+  const uint64_t per_mid = cfg->middle_pq ? (uint64_t)cfg->n_kv_heads * 2 * 32
+                                          : (uint64_t)cfg->n_kv_heads * ((d * cfg->middle_k_bits / 8 + 2 * d / 32) +
+                                                                         (d * cfg->middle_v_bits / 8 + 2 * d / 32));
   const uint64_t per_low = (uint64_t)cfg->n_kv_heads * 2 * (d * kLowBits / 8 + 2 * d / 32);
   uint64_t total = 0;
   for (int32_t i = 0; i < n; ++i) {

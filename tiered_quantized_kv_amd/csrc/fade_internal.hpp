@@ -27,6 +27,7 @@ struct Shape {
   int batch, cap_mid, cap_T, shared;
   int low;                    // 1: the INT2 overflow tier is on
   int low_budget, cap_low;    // its capacity after an event, and its rows
+  int pq;                     // 1: the middle tier holds PQ codes (32 bytes per row for K and for V)
 };
 constexpr int kLowBits = 2;   // K and V bits of the INT2 overflow tier
 
@@ -88,6 +89,20 @@ hipError_t launch_pq_attn(int D, const uint16_t* q, const uint8_t* kcodes, const
                           const uint16_t* kcb, const uint16_t* vcb, float* out, int batch, int n_q_heads, int n_kv_heads,
                           int64_t n_tok, void* ws, hipStream_t st);
 size_t pq_attn_ws_bytes(int D, int batch, int n_q_heads, int64_t n_tok);
+
+// ---- PQ middle tier (k_pq_tier.hip) ------------------------------------------
+hipError_t launch_demote_pq(const Shape& s, const fade_layer_cache& c, hipStream_t st);
+// encodes rows r of x (batch x Hkv x cap rows) with r % cap below
+// lim[(lim_shared ? 0 : r / (Hkv * cap)) * lim_stride] and flags[r] set (if flags)
+hipError_t launch_pq_encode_rows(int D, const uint16_t* x, uint8_t* codes, const uint16_t* cb, const int32_t* lim,
+                                 int lim_stride, int lim_shared, const uint8_t* flags, int batch, int Hkv, int cap,
+                                 hipStream_t st);
+// the same with code rows (r / cap) * dst_cap + r % cap
+hipError_t launch_pq_encode_rows_to(int D, const uint16_t* x, uint8_t* codes, int dst_cap, const uint16_t* cb,
+                                    const int32_t* lim, int lim_stride, int lim_shared, const uint8_t* flags,
+                                    int batch, int Hkv, int cap, hipStream_t st);
+hipError_t launch_decode_pq_mid(const Shape& s, const fade_layer_cache& c, const void* q, int q_bf16, float* part,
+                                float* raw, int raw_stride, int nsplit, int n_fp, int n_mid, hipStream_t st);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

@@ -271,7 +271,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
   const int mbase = S + (a.is_low ? 0 : M2);                // slot of this tier's row 0
   const bool fpt = lsplit < a.n_fp;                   // FP16 tier
   // middle split: an equal share of the live rows, in whole sub-chunks
-  const int per = ((M + n_mid_splits - 1) / n_mid_splits + kSub - 1) / kSub * kSub;
+  const int per = n_mid_splits > 0 ? ((M + n_mid_splits - 1) / n_mid_splits + kSub - 1) / kSub * kSub : 0;
   const int row0 = fpt ? 0 : (lsplit - a.n_fp) * per;
   const int fp_lo = fpt ? lsplit * a.fp_per : 0;     // this split's fp16 tokens [fp_lo, fp_lo + n_tok)
   const int n_tok = fpt ? min(a.fp_per, S + R - fp_lo) : min(per, M - row0);
@@ -876,7 +876,7 @@ hipError_t launch_decode(const Shape& s, const fade_layer_cache& c, const void* 
   a.cap_low = s.low ? s.cap_low : 0;
   a.is_low = 0;
   a.split0 = 0;
-  a.n_tier = decode_mid_splits(s);
+  a.n_tier = s.pq ? 0 : decode_mid_splits(s);     // a PQ middle tier has its own kernel
   const int n_main = a.n_fp + a.n_tier;
   auto dispatch = [&](const DecodeArgs& da, int n_splits, int kb, int vb) {
     const dim3 grid(n_splits * s.Hkv * s.batch);
@@ -891,6 +891,11 @@ hipError_t launch_decode(const Shape& s, const fade_layer_cache& c, const void* 
   dispatch(a, n_main, s.kb, s.vb);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (s.pq) {
+    // the PQ middle tier's splits follow the fp16 tier's in the partials
+    e = launch_decode_pq_mid(s, c, q, q_bf16, part, a.raw, raw_stride, nsplit, a.n_fp, decode_mid_splits(s), st);
+    if (e != hipSuccess) return e;
+  }
   const int n_low = decode_low_splits(s);
   if (n_low > 0) {
     // the INT2 overflow tier: K and V at 2 bits, its own splits after the

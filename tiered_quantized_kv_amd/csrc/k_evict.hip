@@ -1054,10 +1054,19 @@ static size_t wide_stage_bytes(const Shape& s) {
          2 * align_up(rows * (s.D / 32) * 2, 256);
 }
 
+// A PQ middle tier stages the surviving middle rows as fp16 (keys after
+// their re-rotation), pq_stage_rows per (sequence, KV head), and encodes them
+// after the build.
+static int pq_stage_rows(const Shape& s, int L) { return max(1, min(s.cap_mid, L)); }
+static size_t pq_stage_bytes(const Shape& s, int L) {
+  return align_up((size_t)s.batch * s.Hkv * pq_stage_rows(s, L) * s.D * 2, 256);
+}
+
 size_t prefill_build_ws_bytes(const Shape& s, int L) {
   const int rows = s.shared ? 1 : s.batch;
   size_t n = align_up((size_t)rows * kInfo * 4, 256) + align_up((size_t)rows * (L > 0 ? L : 1) * 4, 256);
   if (s.low) n += wide_stage_bytes(s) + tier_event_ws_bytes_src(s, max(1, wide_budget(s)), false);
+  if (s.pq) n += 2 * pq_stage_bytes(s, L);
   return n;
 }
 
@@ -1071,6 +1080,9 @@ struct BuildArgs {
   const int32_t* map;       // [rows][L]
   const int32_t* info;      // [rows][kInfo]
   RopeFreqs fr;
+  uint16_t* pq_k;           // PQ middle tier: fp16 staging rows [batch][Hkv][pq_cap][D] of the
+  uint16_t* pq_v;           // middle survivors (nullptr otherwise)
+  int pq_cap;
 };
 
 constexpr int kBuildRows = 64;   // prefill tokens per build workgroup
@@ -1149,6 +1161,14 @@ __global__ __launch_bounds__(256) void k_build(BuildArgs a) {
       continue;
     }
     const size_t row = bg * s.cap_mid + d;
+    if (a.pq_k) {                               // encoded after the build
+      const size_t pr = bg * a.pq_cap + d;
+      a.pq_k[pr * D + p] = y1;
+      a.pq_k[pr * D + p + HALF] = y2;
+      a.pq_v[pr * D + p] = v1;
+      a.pq_v[pr * D + p + HALF] = v2;
+      continue;
+    }
     uint32_t* kc = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(a.c.mid_k_codes) + row * KROW);
     uint32_t* vc = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(a.c.mid_v_codes) + row * VROW);
     uint16_t* ks = reinterpret_cast<uint16_t*>(a.c.mid_k_scales) + row * NG;
@@ -1232,6 +1252,14 @@ hipError_t launch_prefill_build(const Shape& s0, const fade_layer_cache& c0, con
     c.mid_k_scales = wks;
     c.mid_v_scales = wvs;
   }
+  uint16_t *pqk = nullptr, *pqv = nullptr;
+  const int pq_cap = pq_stage_rows(s0, L);
+  if (s0.pq) {
+    pqk = reinterpret_cast<uint16_t*>(w);
+    w += pq_stage_bytes(s0, L);
+    pqv = reinterpret_cast<uint16_t*>(w);
+    w += pq_stage_bytes(s0, L);
+  }
   SelectArgs sa{};
   sa.scores = scores;
   sa.score_stride = L;
@@ -1260,6 +1288,9 @@ hipError_t launch_prefill_build(const Shape& s0, const fade_layer_cache& c0, con
     ba.map = map;
     ba.info = info;
     ba.fr = fr;
+    ba.pq_k = pqk;
+    ba.pq_v = pqv;
+    ba.pq_cap = pq_cap;
     const dim3 grid((L + kBuildRows - 1) / kBuildRows, s.Hkv, s.batch);
     if (s.D == 128) launch_build_d<128>(ba, grid, st);
     else launch_build_d<64>(ba, grid, st);
@@ -1270,7 +1301,19 @@ hipError_t launch_prefill_build(const Shape& s0, const fade_layer_cache& c0, con
                      s0.low ? c0.low_lens : nullptr, s.batch,
                      s.shared);
   e = hipGetLastError();
-  if (e != hipSuccess || !s0.low) return e;
+  if (e != hipSuccess) return e;
+  if (s0.pq) {
+    // encode the staged survivors (rows below each sequence's middle length)
+    // into the cache rows
+    e = launch_pq_encode_rows_to(s0.D, pqk, reinterpret_cast<uint8_t*>(c0.mid_k_codes), s0.cap_mid,
+                                 reinterpret_cast<const uint16_t*>(c0.pq_k_codebook), c0.lens + 1, 4, 0, nullptr,
+                                 s0.batch, s0.Hkv, pq_cap, st);
+    if (e != hipSuccess) return e;
+    return launch_pq_encode_rows_to(s0.D, pqv, reinterpret_cast<uint8_t*>(c0.mid_v_codes), s0.cap_mid,
+                                    reinterpret_cast<const uint16_t*>(c0.pq_v_codebook), c0.lens + 1, 4, 0, nullptr,
+                                    s0.batch, s0.Hkv, pq_cap, st);
+  }
+  if (!s0.low) return e;
   // demote the wide layout's lowest int2_budget into the INT2 tier
   return launch_tier_event_from(s0, c0, scores ? FADE_POLICY_SCORE : FADE_POLICY_POSITION, fr, wkc, wvc, wks, wvs,
                                 max(1, wide_budget(s0)), w, st);
@@ -1329,6 +1372,7 @@ hipError_t launch_rope_rotate(int D, uint16_t* x, int bf16, int64_t n_rows, cons
 // exactness, not speed.
 
 constexpr int kTierInfo = 8;   // {S, M4, M2, R, M4n, M2n, n_dem, n_drop}
+constexpr int kPqCodeBytes = 32;   // a PQ middle row: one code per sub-space
 
 struct TierArgs {
   Shape s;
@@ -1352,6 +1396,10 @@ struct TierArgs {
   float* score_tmp;            // [rows][cap_T]
   int32_t* kept;               // optional [rows][cap_T]
   RopeFreqs fr;
+  // PQ middle tier: moved keys are decoded and re-rotated into fp16 rows
+  // [batch][Hkv][dst_cap4][D], flagged, then encoded after the move
+  uint16_t* pq_k16;
+  uint8_t* pq_flags;
 };
 
 // k smallest of n unique 64-bit keys: returns the k-th smallest (keys <= it
@@ -1397,7 +1445,7 @@ __global__ __launch_bounds__(kSelThreads) void k_tier_select(TierArgs a) {
   const int row = blockIdx.x, tid = threadIdx.x;
   const int32_t* L = a.c.lens + 4 * row;     // a shared cache reads sequence 0
   const int S = min(max(L[0], 0), s.n_sink), M4 = min(max(L[1], 0), a.src_cap4);
-  const int R = min(max(L[2], 0), s.ring), M2 = min(max(a.c.low_lens[row], 0), s.cap_low);
+  const int R = min(max(L[2], 0), s.ring), M2 = s.low ? min(max(a.c.low_lens[row], 0), s.cap_low) : 0;
   const int n_dem = s.budget >= 0 && M4 > s.budget ? M4 - s.budget : 0;
   const int n_drop = max(0, M2 + n_dem - s.low_budget);
   const int M4n = M4 - n_dem, M2n = M2 + n_dem - n_drop;
@@ -1610,6 +1658,42 @@ __global__ __launch_bounds__(64) void k_tier_move(TierArgs a) {
     return;
   }
   const int y = x - a.plan_l;
+  if (y < a.plan_4 && s.pq) {
+    if (y >= M4n) return;
+    const int i = a.i4src[(size_t)mrow * a.plan_4 + y];
+    const size_t sr = bg * a.src_cap4 + i, dr = bg * a.dst_cap4 + y;
+    const int lane = threadIdx.x;
+    // value codes move unchanged
+    if (lane < 8)
+      reinterpret_cast<uint32_t*>(a.dst_vc + dr * kPqCodeBytes)[lane] =
+          reinterpret_cast<const uint32_t*>(a.src_vc + sr * kPqCodeBytes)[lane];
+    const int delta = (S + M2 + i) - (S + M2n + y);
+    if (delta == 0 || !a.fr.rotates) {
+      if (lane < 8)
+        reinterpret_cast<uint32_t*>(a.dst_kc + dr * kPqCodeBytes)[lane] =
+            reinterpret_cast<const uint32_t*>(a.src_kc + sr * kPqCodeBytes)[lane];
+      if (lane == 0) a.pq_flags[dr] = 0;
+      return;
+    }
+    // the key: decoded centroids, rotated by the slot shift, one fp16 rounding;
+    // encoded after the move
+    const int HALF = D / 2, Lsub = D / kPqCodeBytes;
+    if (lane < HALF) {
+      const int c1 = a.fr.interleaved ? 2 * lane : lane, c2 = a.fr.interleaved ? 2 * lane + 1 : lane + HALF;
+      const uint8_t* code = a.src_kc + sr * kPqCodeBytes;
+      const uint16_t* cb = reinterpret_cast<const uint16_t*>(a.c.pq_k_codebook);
+      const float x1 = h2f(cb[((c1 / Lsub) * 256 + code[c1 / Lsub]) * Lsub + c1 % Lsub]);
+      const float x2 = h2f(cb[((c2 / Lsub) * 256 + code[c2 / Lsub]) * Lsub + c2 % Lsub]);
+      double sn, cn;
+      sincos(-(double)delta * a.fr.f[lane], &sn, &cn);
+      uint16_t y1, y2;
+      rotate_pair(x1, x2, cn, sn, y1, y2);
+      a.pq_k16[dr * D + c1] = y1;
+      a.pq_k16[dr * D + c2] = y2;
+    }
+    if (lane == 0) a.pq_flags[dr] = 1;
+    return;
+  }
   if (y < a.plan_4) {
     if (y >= M4n) return;
     const int i = a.i4src[(size_t)mrow * a.plan_4 + y];
@@ -1650,12 +1734,15 @@ __global__ __launch_bounds__(256) void k_tier_copy(TierArgs a, int copy_rows) {
   const int M4n = inf[4], M2n = inf[5];
   if (blockIdx.x == 0 && g == 0 && threadIdx.x == 0) {
     a.c.lens[4 * b + 1] = M4n;
-    a.c.low_lens[b] = M2n;
+    if (s.low) a.c.low_lens[b] = M2n;
   }
   if (!copy_rows) return;
   const int D = s.D;
   const size_t bg = (size_t)b * s.Hkv + g;
-  const int KW4 = D * s.kb / 32, VW4 = D * s.vb / 32, LW = D * kLowBits / 32, SW = D / 64;   // words per row
+  // 32-bit words per row: codes of K, of V, scales of each (a PQ row: 32
+  // code bytes for K and for V, no scales)
+  const int KW4 = s.pq ? kPqCodeBytes / 4 : D * s.kb / 32, VW4 = s.pq ? kPqCodeBytes / 4 : D * s.vb / 32;
+  const int LW = D * kLowBits / 32, SW = s.pq ? 0 : D / 64;
   const int per4 = KW4 + VW4 + 2 * SW, perl = 2 * LW + 2 * SW;
   const long n_words = (long)M4n * per4 + (long)M2n * perl;
   for (long w = (long)blockIdx.x * blockDim.x + threadIdx.x; w < n_words; w += (long)gridDim.x * blockDim.x) {
@@ -1692,6 +1779,8 @@ struct TierWs {
   float* score_tmp;
   uint8_t *kc, *vc, *lkc, *lvc;
   uint16_t *ks, *vs, *lks, *lvs;
+  uint16_t* pq_k16;
+  uint8_t* pq_flags;
   int plan_l, plan_4, cap4, capl;
   size_t bytes;
 };
@@ -1716,10 +1805,12 @@ TierWs tier_ws_layout(const Shape& s, int src_cap4, bool staged, char* w) {
   t.i4src = reinterpret_cast<int32_t*>(take((size_t)rows * t.plan_4 * 4));
   t.score_tmp = reinterpret_cast<float*>(take((size_t)rows * s.cap_T * 4));
   const size_t bh = (size_t)s.batch * s.Hkv;
-  t.kc = reinterpret_cast<uint8_t*>(take(bh * t.cap4 * D * s.kb / 8));
-  t.vc = reinterpret_cast<uint8_t*>(take(bh * t.cap4 * D * s.vb / 8));
-  t.ks = reinterpret_cast<uint16_t*>(take(bh * t.cap4 * NG * 2));
-  t.vs = reinterpret_cast<uint16_t*>(take(bh * t.cap4 * NG * 2));
+  t.kc = reinterpret_cast<uint8_t*>(take(bh * t.cap4 * (s.pq ? kPqCodeBytes : D * s.kb / 8)));
+  t.vc = reinterpret_cast<uint8_t*>(take(bh * t.cap4 * (s.pq ? kPqCodeBytes : D * s.vb / 8)));
+  t.ks = reinterpret_cast<uint16_t*>(take(s.pq ? 0 : bh * t.cap4 * NG * 2));
+  t.vs = reinterpret_cast<uint16_t*>(take(s.pq ? 0 : bh * t.cap4 * NG * 2));
+  t.pq_k16 = reinterpret_cast<uint16_t*>(take(s.pq ? bh * t.cap4 * D * 2 : 0));
+  t.pq_flags = reinterpret_cast<uint8_t*>(take(s.pq ? bh * t.cap4 : 0));
   t.lkc = reinterpret_cast<uint8_t*>(take(bh * t.capl * D * kLowBits / 8));
   t.lvc = reinterpret_cast<uint8_t*>(take(bh * t.capl * D * kLowBits / 8));
   t.lks = reinterpret_cast<uint16_t*>(take(bh * t.capl * NG * 2));
@@ -1741,6 +1832,8 @@ hipError_t run_tier_event(TierArgs a, const TierWs& t, bool staged, int32_t* kep
   a.plan_4 = t.plan_4;
   a.score_tmp = t.score_tmp;
   a.kept = kept;
+  a.pq_k16 = t.pq_k16;
+  a.pq_flags = t.pq_flags;
   if (staged) {
     a.dst_kc = t.kc; a.dst_vc = t.vc; a.dst_ks = t.ks; a.dst_vs = t.vs;
     a.dst_lkc = t.lkc; a.dst_lvc = t.lvc; a.dst_lks = t.lks; a.dst_lvs = t.lvs;
@@ -1764,6 +1857,12 @@ hipError_t run_tier_event(TierArgs a, const TierWs& t, bool staged, int32_t* kep
   hipLaunchKernelGGL(k_tier_move, dim3(a.plan_l + a.plan_4 + s.ring, s.Hkv, s.batch), dim3(64), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (s.pq) {
+    // the moved keys (flagged rows below each row's new middle length)
+    e = launch_pq_encode_rows(s.D, a.pq_k16, a.dst_kc, reinterpret_cast<const uint16_t*>(a.c.pq_k_codebook),
+                              a.info + 4, kTierInfo, s.shared, a.pq_flags, s.batch, s.Hkv, a.dst_cap4, st);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(k_tier_copy, dim3(staged ? 16 : 1, s.Hkv, s.batch), dim3(256), 0, st, a, staged ? 1 : 0);
   return hipGetLastError();
 }

@@ -29,11 +29,9 @@
 // and is bound by its LDS table reads and centroid gathers.
 #include "fade_common.hpp"
 #include "fade_internal.hpp"
+#include "pq_common.hpp"
 
 namespace fade {
-
-constexpr int kPqSub = 32;
-constexpr int kPqK = 256;
 // attention workgroup (lanes = tokens per chunk): 512 at d 128, 256 at d 64
 // (whose smaller LDS footprint then fits two workgroups per CU)
 constexpr int pq_attn_threads(int L) { return L == 4 ? 512 : 256; }
@@ -51,10 +49,7 @@ __global__ __launch_bounds__(256) void k_pq_encode(const uint16_t* __restrict__ 
                                                    const uint16_t* __restrict__ cb, uint8_t* __restrict__ codes) {
   extern __shared__ uint16_t cbl[];   // [kPqK][kPqSub][L]
   constexpr int D = L * kPqSub;
-  for (int i = threadIdx.x; i < kPqSub * kPqK * L; i += 256) {
-    const int e = i % L, k = (i / L) % kPqK, s = i / (L * kPqK);
-    cbl[(k * kPqSub + s) * L + e] = cb[i];
-  }
+  pq_stage_codebook<L>(cb, cbl);
   __syncthreads();
   const int s = threadIdx.x % kPqSub;
   const int64_t row = (int64_t)blockIdx.x * (256 / kPqSub) + threadIdx.x / kPqSub;
@@ -62,26 +57,7 @@ __global__ __launch_bounds__(256) void k_pq_encode(const uint16_t* __restrict__ 
   double xv[L];
 #pragma unroll
   for (int e = 0; e < L; ++e) xv[e] = (double)h2f(x[row * D + s * L + e]);
-  double best = 0.0;
-  int arg = 0;
-  {
-#pragma clang fp contract(off)
-    for (int k = 0; k < kPqK; ++k) {
-      const uint16_t* c = cbl + (k * kPqSub + s) * L;
-      double acc = 0.0;
-#pragma unroll
-      for (int e = 0; e < L; ++e) {
-        const double d = xv[e] - (double)h2f(c[e]);   // exact: both are fp16 values
-        const double sq = d * d;
-        acc = e == 0 ? sq : acc + sq;
-      }
-      if (k == 0 || acc < best) {
-        best = acc;
-        arg = k;
-      }
-    }
-  }
-  codes[row * kPqSub + s] = (uint8_t)arg;
+  codes[row * kPqSub + s] = (uint8_t)pq_nearest<L>(xv, cbl + s * L, kPqSub * L);
 }
 
 template <int L>

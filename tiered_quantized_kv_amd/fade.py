@@ -38,6 +38,7 @@ class FadeConfig(ctypes.Structure):
         ("rope_low_freq_factor", ctypes.c_double), ("rope_high_freq_factor", ctypes.c_double),
         ("rope_original_max_position", ctypes.c_int32), ("q_dtype", ctypes.c_int32),
         ("out_dtype", ctypes.c_int32), ("rope_seq_len", ctypes.c_int32), ("int2_budget", ctypes.c_int32),
+        ("middle_pq", ctypes.c_int32),
     ]
 
 
@@ -51,6 +52,7 @@ class LayerCache(ctypes.Structure):
         ("cap_low", ctypes.c_int32), ("reserved", ctypes.c_int32),
         ("low_k_codes", ctypes.c_void_p), ("low_v_codes", ctypes.c_void_p),
         ("low_k_scales", ctypes.c_void_p), ("low_v_scales", ctypes.c_void_p), ("low_lens", ctypes.c_void_p),
+        ("pq_k_codebook", ctypes.c_void_p), ("pq_v_codebook", ctypes.c_void_p),
     ]
 
 
@@ -111,13 +113,13 @@ def make_config(head_dim, n_q_heads, n_kv_heads, n_sink, recent_window, int4_bud
                 middle_v_bits=4, rope_type="default", rope_theta=10000.0, rope_factor=1.0,
                 rope_low_freq_factor=1.0, rope_high_freq_factor=4.0, rope_original_max_position=8192,
                 q_dtype="f16", out_dtype="f32", group_size=32, rope_seq_len=0, rope_interleaved=False,
-                int2_budget=-1):
+                int2_budget=-1, middle_pq=False):
     dt = {"f16": DTYPE_F16, "bf16": DTYPE_BF16, "f32": DTYPE_F32}
     return FadeConfig(head_dim, n_q_heads, n_kv_heads, n_sink, recent_window, int4_budget, middle_k_bits,
                       middle_v_bits, group_size, _ROPE[rope_type] | (ROPE_INTERLEAVED if rope_interleaved else 0),
                       float(rope_theta), float(rope_factor), float(rope_low_freq_factor),
                       float(rope_high_freq_factor), int(rope_original_max_position), dt[q_dtype],
-                      dt[out_dtype], int(rope_seq_len), int(int2_budget))
+                      dt[out_dtype], int(rope_seq_len), int(int2_budget), int(bool(middle_pq)))
 
 
 def _p(t):
@@ -153,8 +155,16 @@ class TieredCache:
     """Device tensors of one layer's tiers plus the LayerCache struct that
     points at them (memory plumbing for the C ABI)."""
 
-    def __init__(self, cfg, batch, cap_mid, shared=False, with_scores=True, device="cuda", cap_low=None):
+    def __init__(self, cfg, batch, cap_mid, shared=False, with_scores=True, device="cuda", cap_low=None,
+                 pq_codebooks=None):
+        """pq_codebooks: (key, value) fp16 tensors [32, 256, head_dim / 32] on
+        `device`, required with cfg.middle_pq (the middle tier then holds 32
+        code bytes per row for K and for V, and no scales)."""
         d, hkv = cfg.head_dim, cfg.n_kv_heads
+        self.pq = bool(cfg.middle_pq)
+        if self.pq and pq_codebooks is None:
+            raise ValueError("a PQ middle tier needs its key and value codebooks")
+        self.pq_k_codebook, self.pq_v_codebook = (pq_codebooks if self.pq else (None, None))
         self.cfg = cfg
         self.batch, self.cap_mid, self.shared = batch, cap_mid, int(bool(shared))
         self.low = cfg.int2_budget >= 0
@@ -165,10 +175,11 @@ class TieredCache:
         self.fp_k = torch.zeros(batch, hkv, self.slots, d, dtype=f16, device=device)
         self.fp_v = torch.zeros_like(self.fp_k)
         cm = max(cap_mid, 1)
-        self.mid_k_codes = torch.zeros(batch, hkv, cm, d * cfg.middle_k_bits // 8, dtype=torch.uint8, device=device)
-        self.mid_v_codes = torch.zeros(batch, hkv, cm, d * cfg.middle_v_bits // 8, dtype=torch.uint8, device=device)
-        self.mid_k_scales = torch.zeros(batch, hkv, cm, d // 32, dtype=f16, device=device)
-        self.mid_v_scales = torch.zeros_like(self.mid_k_scales)
+        kw, vw = (PQ_SUB, PQ_SUB) if self.pq else (d * cfg.middle_k_bits // 8, d * cfg.middle_v_bits // 8)
+        self.mid_k_codes = torch.zeros(batch, hkv, cm, kw, dtype=torch.uint8, device=device)
+        self.mid_v_codes = torch.zeros(batch, hkv, cm, vw, dtype=torch.uint8, device=device)
+        self.mid_k_scales = None if self.pq else torch.zeros(batch, hkv, cm, d // 32, dtype=f16, device=device)
+        self.mid_v_scales = None if self.pq else torch.zeros_like(self.mid_k_scales)
         self.lens = torch.zeros(batch, 4, dtype=torch.int32, device=device)
         self.scores = (torch.zeros(1 if shared else batch, self.cap_T, dtype=torch.float32, device=device)
                        if with_scores else None)
@@ -187,7 +198,7 @@ class TieredCache:
         ptr = lambda t: None if t is None else t.data_ptr()
         return LayerCache(batch, self.cap_mid, self.cap_T, shared, ptr(fk), ptr(fv), ptr(mkc), ptr(mvc), ptr(mks),
                           ptr(mvs), ptr(lens), ptr(scores), self.cap_low, 0, ptr(lkc), ptr(lvc), ptr(lks), ptr(lvs),
-                          ptr(llens))
+                          ptr(llens), ptr(self.pq_k_codebook), ptr(self.pq_v_codebook))
 
     def ref(self):
         return ctypes.byref(self.struct)
@@ -199,7 +210,7 @@ class TieredCache:
         srow = 0 if self.shared else b
         at = lambda t: None if t is None else t[b]
         v.struct = self._struct(self.fp_k[b], self.fp_v[b], self.mid_k_codes[b], self.mid_v_codes[b],
-                                self.mid_k_scales[b], self.mid_v_scales[b], self.lens[b],
+                                at(self.mid_k_scales), at(self.mid_v_scales), self.lens[b],
                                 None if self.scores is None else self.scores[srow], at(self.low_k_codes),
                                 at(self.low_v_codes), at(self.low_k_scales), at(self.low_v_scales),
                                 None if self.low_lens is None else self.low_lens[b:b + 1], 1, 0)

@@ -5,9 +5,9 @@ here):
 
 * Persistence (FADE post, section "会话持久化"): the compressed cache is
   saved and restored as it is - packed codes, fp16 scales, the fp16 sink and
-  recent tiers, the INT2 overflow tier when there is one, the per-sequence
-  lengths and the per-slot scores - so a restored cache attends, scores and
-  evicts exactly as the saved one would.
+  recent tiers, the INT2 overflow tier when there is one, a PQ middle tier's
+  codebooks, the per-sequence lengths and the per-slot scores - so a
+  restored cache attends, scores and evicts exactly as the saved one would.
   Files are safetensors (no code runs on load); the configuration travels in
   the file's metadata and must match the cache it is loaded into.
 * Telemetry (section "遥测与调试"): one JSON line per tier reassignment
@@ -25,6 +25,7 @@ from . import fade
 
 _TENSORS = ("fp_k", "fp_v", "mid_k_codes", "mid_v_codes", "mid_k_scales", "mid_v_scales", "lens", "scores")
 _LOW_TENSORS = ("low_k_codes", "low_v_codes", "low_k_scales", "low_v_scales", "low_lens")
+_PQ_TENSORS = ("pq_k_codebook", "pq_v_codebook")   # the layer's codebooks of a PQ middle tier
 _CFG_FIELDS = ("head_dim", "n_q_heads", "n_kv_heads", "n_sink", "recent_window", "int4_budget",
                "middle_k_bits", "middle_v_bits", "group_size", "rope_type", "rope_theta", "rope_factor",
                "rope_low_freq_factor", "rope_high_freq_factor", "rope_original_max_position")
@@ -35,12 +36,13 @@ def _config_meta(cache):
     # cache may be restored under a different one.
     meta = {f: repr(getattr(cache.cfg, f)) for f in _CFG_FIELDS if f != "int4_budget"}
     meta.update(batch=str(cache.batch), shared=str(cache.shared), with_scores=str(cache.scores is not None),
-                int2_tier=str(bool(getattr(cache, "low", False))))
+                int2_tier=str(bool(getattr(cache, "low", False))), middle_pq=str(bool(getattr(cache, "pq", False))))
     return meta
 
 
 def _names(cache):
-    return _TENSORS + (_LOW_TENSORS if getattr(cache, "low", False) else ())
+    return (_TENSORS + (_LOW_TENSORS if getattr(cache, "low", False) else ()) +
+            (_PQ_TENSORS if getattr(cache, "pq", False) else ()))
 
 
 def _lens(cache):
@@ -89,12 +91,15 @@ def load_cache_state_dict(cache, sd, meta=None):
         raise ValueError("saved INT2 tier is longer than this cache's capacity")
     if meta is not None:
         want = _config_meta(cache)
-        diff = {k: (meta.get(k), v) for k, v in want.items() if meta.get(k, "False" if k == "int2_tier" else None) != v}
+        diff = {k: (meta.get(k), v) for k, v in want.items()
+                if meta.get(k, "False" if k in ("int2_tier", "middle_pq") else None) != v}
         if diff:
             raise ValueError(f"cache state does not match this cache: {diff}")
     names = _names(cache)
     if any(n in sd for n in _LOW_TENSORS) and not getattr(cache, "low", False):
         raise ValueError("cache state holds an INT2 tier this cache does not have")
+    if any(n in sd for n in _PQ_TENSORS) and not getattr(cache, "pq", False):
+        raise ValueError("cache state holds a PQ middle tier this cache does not have")
     # validate everything before the first copy
     for name in names:
         dst = getattr(cache, name)
