@@ -42,6 +42,9 @@ def parse():
                         "on a stream of its own (0 = skip)")
     p.add_argument("--pq-calls", type=int, default=20,
                    help="timed calls of the PQ decode attention at the workload's middle-tier size (0 = skip)")
+    p.add_argument("--shape-calls", type=int, default=40,
+                   help="timed decode-attention calls at each further shape (C4, S4, the PQ middle tier at the "
+                        "workload's shape) on directly filled caches (0 = skip)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="run one device copy of this size before timing (HBM counter calibration)")
     return p.parse_args()
@@ -181,6 +184,12 @@ class Workload:
         self.step_idx = 0
         self.M = list(self.M0)       # host mirror of middle lengths (at attention time)
         torch.cuda.synchronize()
+
+    def release(self):
+        """Drop the device tiers and inputs (after the timed steps)."""
+        self.caches, self.pool, self.admit = [], [], None
+        self.torch.cuda.synchronize()
+        self.torch.cuda.empty_cache()
 
     # ---- accounting --------------------------------------------------------
     def decode_bytes_and_tokens(self):
@@ -374,10 +383,103 @@ def cpu_baseline(name, budget_s=20.0):
         if time.perf_counter() - t0 > budget_s or reps >= 3:
             break
     dt = time.perf_counter() - t0
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{reps} x one layer of one decode step of workload {name} ({B} sequences, "
-                      f"{tokens // reps} KV tokens attended per layer-step): append, attend, score update, "
-                      f"demote, evict; float64 numpy, {dt:.1f} s"}
+    res = {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"{reps} x one layer of one decode step of workload {name} ({B} sequences, "
+                     f"{tokens // reps} KV tokens attended per layer-step): append, attend, score update, "
+                     f"demote, evict; float64 numpy, {dt:.1f} s"}
+    # host facts: what the numbers ran on
+    try:
+        from threadpoolctl import threadpool_info
+        blas = sorted({f"{i.get('internal_api')} ({os.path.basename(i.get('filepath', ''))}, "
+                       f"{i.get('num_threads')} threads)" for i in threadpool_info()})
+    except Exception:
+        blas = []
+    res["host"] = {"os_cpu_count": os.cpu_count(),
+                   "affinity_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None,
+                   "blas": blas, "numpy": np.__version__}
+    if w.get("admit_prefill"):
+        # the step's H2O prefill leg (one admitted prompt per layer-step):
+        # oracle column sums over a sample of the query heads, scaled to all
+        from oracle import h2o
+        La, hs = w["admit_prefill"], 4
+        qa = rope.rotate(synth.normal(gen, hs, La, cfg.head_dim), np.arange(La), f).astype(np.float16)
+        ka = rope.rotate(synth.normal(gen, 1, La, cfg.head_dim), np.arange(La), f).astype(np.float16)
+        t1 = time.perf_counter()
+        h2o.prefill_colsum(qa.astype(np.float64), ka.astype(np.float64))
+        th = (time.perf_counter() - t1) * cfg.n_q_heads / hs
+        res["h2o_prefill_leg"] = {"s_per_layer": th, "prompt_tokens": La,
+                                  "sample": f"{hs} of {cfg.n_q_heads} query heads, scaled"}
+        # whole layer-step: decode part plus the prefill leg
+        res["value_with_h2o_leg"] = (tokens / reps) / (dt / reps + th)
+    return res
+
+
+def time_decode_direct(name, calls, pq=False, n_caches=4):
+    """Decode attention alone at a workload's shape, on caches filled directly
+    with seeded synthetic tiers (no prefill build): fp16 sinks and a full
+    recent ring, the middle tier full at its steady-state length (the INT4
+    budget, or the whole context without one) with uniform random codes and
+    scales in [0.05, 0.3) (or uniform PQ codes under N(0, 1) codebooks with
+    pq). `n_caches` caches are used in turn so that no call finds the previous
+    one's bytes in the last-level cache. Timed with a pair of events around
+    `calls` back-to-back launches (k_decode_tiers + k_decode_finish, plus
+    k_decode_pq with pq), on the launch stream. Bytes: the live tiers, q, out
+    and the side output when the workload's policy uses one."""
+    import torch
+    from tiered_quantized_kv_amd import fade, synth
+    w = synth.WORKLOADS[name]
+    d, hq, hkv = w["head_dim"], w["n_q_heads"], w["n_kv_heads"]
+    B = w["batch"]
+    n_sink, W = w["n_sink"], w["recent_window"]
+    M = w["int4_budget"] if w["int4_budget"] >= 0 else w["context"] - n_sink - W
+    side = w["policy"] in ("h2o", "ema")
+    cfg = fade.make_config(head_dim=d, n_q_heads=hq, n_kv_heads=hkv, n_sink=n_sink, recent_window=W,
+                           int4_budget=max(w["int4_budget"], -1), middle_k_bits=w["middle_k_bits"],
+                           middle_v_bits=w["middle_v_bits"], q_dtype=w["q_dtype"], out_dtype="f16",
+                           rope_theta=w["rope_theta"], middle_pq=pq)
+    g = torch.Generator(device="cuda").manual_seed(synth.base_seed(name) + (991 if pq else 997))
+    caches = []
+    for _ in range(n_caches):
+        cbs = None
+        if pq:
+            cbs = tuple(torch.randn(fade.PQ_SUB, fade.PQ_K, d // fade.PQ_SUB, device="cuda", generator=g).half()
+                        for _ in range(2))
+        tc = fade.TieredCache(cfg, B, M + 1, with_scores=False, pq_codebooks=cbs)
+        tc.fp_k.copy_(torch.randn(tc.fp_k.shape, device="cuda", generator=g).half())
+        tc.fp_v.copy_(torch.randn(tc.fp_v.shape, device="cuda", generator=g).half())
+        for t in (tc.mid_k_codes, tc.mid_v_codes):
+            t.copy_(torch.randint(0, 256, t.shape, device="cuda", dtype=torch.uint8, generator=g))
+        for t in (tc.mid_k_scales, tc.mid_v_scales):
+            if t is not None:
+                t.copy_((0.05 + 0.25 * torch.rand(t.shape, device="cuda", generator=g)).half())
+        tc.lens.copy_(torch.tensor([[n_sink, M, W + 1, 0]] * B, dtype=torch.int32))
+        caches.append(tc)
+    qdt = torch.bfloat16 if w["q_dtype"] == "bf16" else torch.float16
+    q = torch.randn(B, hq, d, device="cuda", generator=g).to(qdt)
+    out = torch.empty(B, hq, d, device="cuda", dtype=torch.float16)
+    tok = torch.empty(B, caches[0].cap_T, device="cuda") if side else None
+    ws = fade.workspace(cfg, fade.WS_DECODE, B, M + 1, cache=caches[0])
+    for i in range(3):
+        fade.fade_tiered_decode_attn(cfg, caches[i % n_caches], q, out, tok, ws)
+    e0, e1 = TimingEvent(), TimingEvent()
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(calls):
+        fade.fade_tiered_decode_attn(cfg, caches[i % n_caches], q, out, tok, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000 / calls
+    F = n_sink + W + 1
+    per_mid = hkv * (2 * fade.PQ_SUB if pq else
+                     (d * w["middle_k_bits"] // 8 + d // 16) + (d * w["middle_v_bits"] // 8 + d // 16))
+    nbytes = B * (F * hkv * d * 4 + M * per_mid) + B * hq * d * 2 * 2 + (B * (F + M) * 4 if side else 0)
+    achieved = nbytes / (us * 1e-6) / 1e9
+    return {"avg_us_per_launch": us, "calls": calls, "batch": B, "middle_tokens": M, "side_output": side,
+            "middle": "pq codes (32 B per row for K and V)" if pq else f"K{w['middle_k_bits']}/V{w['middle_v_bits']}",
+            "bytes_per_launch": nbytes, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+            "kernels": "k_decode_tiers + k_decode_finish" + (" + k_decode_pq" if pq else ""),
+            "tokens_per_s": B * (F + M) / (us * 1e-6)}
 
 
 def time_pq_attention(wl, calls):
@@ -498,7 +600,9 @@ def main():
                    "admit_prefill_stream": None if wl.admit is None else "decode"},
         "decode_attn": {"avg_us_per_launch": avg_dec_us, "bytes_per_launch": bytes_per_launch,
                         "kernels": "k_decode_tiers + k_decode_finish",
-                        "timed_launches": timed, "timed_every_nth_layer": TIME_EVERY},
+                        "timed_launches": timed, "timed_every_nth_layer": TIME_EVERY,
+                        # the same metric over decode-attention kernel time alone
+                        "tokens_per_s": dec_tokens / (steps * wl.layers) / (avg_dec_us * 1e-6)},
         "wall_s_timed": wall,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(a.workload)},
@@ -542,6 +646,20 @@ def main():
         wl.use_admit_stream(False)
     if a.pq_calls > 0:
         res["pq_decode_attn"] = time_pq_attention(wl, a.pq_calls)
+    if a.shape_calls > 0:
+        # decode attention alone at the other single-GPU shapes, and over a PQ
+        # middle tier at this workload's shape
+        wl.release()
+        shapes = {}
+        for nm in ("c4", "s4"):
+            if nm != a.workload:
+                print(f"[bench] decode attention at shape {nm} ...", file=sys.stderr, flush=True)
+                shapes[nm] = time_decode_direct(nm, a.shape_calls)
+                torch.cuda.empty_cache()
+        res["decode_attn_shapes"] = shapes
+        print("[bench] decode attention over a PQ middle tier ...", file=sys.stderr, flush=True)
+        res["pq_tier_decode_attn"] = time_decode_direct(a.workload, a.shape_calls, pq=True)
+        torch.cuda.empty_cache()
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample ...", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(a.workload)

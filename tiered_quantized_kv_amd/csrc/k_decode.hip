@@ -78,6 +78,13 @@ constexpr long kDecodeMiddleWGs = 1024;   // middle workgroups the split aims fo
 // another streams twice its share.
 int decode_mid_splits(const Shape& s) {
   const long pairs = (long)s.batch * s.Hkv;
+  if (s.pq) {
+    // PQ middle tier: about one work item per workgroup of its persistent
+    // grid (one per CU, each holding both codebooks), at least 512 rows each
+    long n = (256 + pairs - 1) / pairs;
+    n = std::min(n, std::max(1L, (long)(s.cap_mid + 511) / 512));
+    return (int)std::max(n, 1L);
+  }
   const int unit = 4 * kSub;
   const long most = (s.cap_mid + unit - 1) / unit;
   long n = (kDecodeMiddleWGs + pairs - 1) / pairs;

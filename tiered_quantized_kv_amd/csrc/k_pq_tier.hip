@@ -158,43 +158,75 @@ __device__ __forceinline__ void pq_wave_lds_sync() {
   asm volatile("" ::: "memory");
 }
 
+// The NREP weights of one token (vector LDS reads).
+template <int NREP>
+__device__ __forceinline__ void pq_load_weights(const float* src, float (&p)[NREP]) {
+  if constexpr (NREP >= 4) {
+#pragma unroll
+    for (int i = 0; i < NREP / 4; ++i) {
+      const float4 v = reinterpret_cast<const float4*>(src)[i];
+      p[4 * i] = v.x;
+      p[4 * i + 1] = v.y;
+      p[4 * i + 2] = v.z;
+      p[4 * i + 3] = v.w;
+    }
+  } else if constexpr (NREP == 2) {
+    const float2 v = *reinterpret_cast<const float2*>(src);
+    p[0] = v.x;
+    p[1] = v.y;
+  } else {
+    p[0] = src[0];
+  }
+}
+
+// waves per workgroup: 8 where the LDS holds their buffers beside both
+// codebooks (two waves per SIMD at one workgroup per CU), else 4
+constexpr int pq_waves(int nrep) { return nrep <= 4 ? 8 : 4; }
+
 template <int L, int NREP>
 struct PqLayout {
   static constexpr int D = L * kPqSub;
+  static constexpr int NW = pq_waves(NREP);
   static constexpr int cb_bytes = kPqSub * kPqK * L * 2;
   static constexpr int wave_bytes = 64 * NREP * 4 + 64 * kPqSub;     // weights [64][NREP] f32, value codes [64][32]
-  static constexpr int merge_bytes = 4 * NREP * D * 4;               // per-wave unnormalized sums
-  static constexpr int area = wave_bytes * 4 > merge_bytes ? wave_bytes * 4 : merge_bytes;
-  static constexpr int total = 2 * cb_bytes + area + 4 * 2 * 16 * 4;
+  static constexpr int merge_bytes = NW * NREP * D * 4;              // per-wave unnormalized sums
+  static constexpr int area = wave_bytes * NW > merge_bytes ? wave_bytes * NW : merge_bytes;
+  static constexpr int total = 2 * cb_bytes + area + NW * 2 * 16 * 4;
 };
 
-// 256 threads = 4 waves; a wave takes 64-token chunks 4r + wave. QK^T of a
+// NW waves (8 at n_rep <= 4, else 4); a wave takes 64-token chunks wave,
+// wave + NW, ... of its work item. QK^T of a
 // 16-token group: A = the gathered key centroids (lane l: token l % 16,
 // channels 16 kb + 4 (l / 16) .. + 3), B = the query heads (lane l: head
 // l % 16, the same channels; heads >= NREP are zero), D / 16 MFMAs of
 // 16x16x16 per group (8 at head_dim 128, 4 at 64); lane l then holds the
 // scores of head l % 16 for tokens 4 (l / 16) + j of the group.
 template <int L, int NREP, bool SIDE>
-__global__ __launch_bounds__(256) void k_decode_pq(PqDecodeArgs a) {
+__global__ __launch_bounds__(pq_waves(NREP) * 64) void k_decode_pq(PqDecodeArgs a) {
   using Lay = PqLayout<L, NREP>;
   constexpr int D = Lay::D;
+  constexpr int NW = Lay::NW, NT = NW * 64;
   constexpr int NKB = D / 16;                     // 16-channel blocks
   __shared__ __align__(16) unsigned char smem[Lay::total];
   uint16_t* cbk = reinterpret_cast<uint16_t*>(smem);                   // [sub][k][L] (as in global)
   uint16_t* cbv = reinterpret_cast<uint16_t*>(smem + Lay::cb_bytes);   // [k][sub][L]
   unsigned char* area = smem + 2 * Lay::cb_bytes;
-  float* wml = reinterpret_cast<float*>(area + Lay::area);             // [4][2][16]
+  float* wml = reinterpret_cast<float*>(area + Lay::area);             // [NW][2][16]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   float* pw = reinterpret_cast<float*>(area + wave * Lay::wave_bytes);         // [64][NREP]
   uint8_t* vcw = reinterpret_cast<uint8_t*>(pw + 64 * NREP);                   // [64][32]
   {
-    const uint32_t* gk = reinterpret_cast<const uint32_t*>(a.kcb);
-    uint32_t* lk = reinterpret_cast<uint32_t*>(cbk);
-    for (int i = tid; i < Lay::cb_bytes / 4; i += 256) lk[i] = gk[i];
-    for (int i = tid; i < kPqSub * kPqK; i += 256) {
+    // key codebook as in global memory (16-byte copies); value codebook
+    // transposed to [k][sub][L], one centroid (L halves) per copy
+    const uint4* gk = reinterpret_cast<const uint4*>(a.kcb);
+    uint4* lk = reinterpret_cast<uint4*>(cbk);
+    for (int i = tid; i < Lay::cb_bytes / 16; i += NT) lk[i] = gk[i];
+    for (int i = tid; i < kPqSub * kPqK; i += NT) {
       const int sub = i / kPqK, k = i - sub * kPqK;
-#pragma unroll
-      for (int e = 0; e < L; ++e) cbv[(k * kPqSub + sub) * L + e] = a.vcb[i * L + e];
+      if constexpr (L == 4)
+        *reinterpret_cast<uint2*>(cbv + (k * kPqSub + sub) * 4) = reinterpret_cast<const uint2*>(a.vcb)[i];
+      else
+        *reinterpret_cast<uint32_t*>(cbv + (k * kPqSub + sub) * 2) = reinterpret_cast<const uint32_t*>(a.vcb)[i];
     }
   }
   __syncthreads();
@@ -215,7 +247,7 @@ __global__ __launch_bounds__(256) void k_decode_pq(PqDecodeArgs a) {
     float* part_base = a.part + ((size_t)(b * Hq + g * NREP) * a.nsplit + split) * (D + 2);
     const size_t part_hstride = (size_t)a.nsplit * (D + 2);
     if (n_tok <= 0) {
-      for (int i = tid; i < NREP * (D + 2); i += 256) {
+      for (int i = tid; i < NREP * (D + 2); i += NT) {
         const int h = i / (D + 2), c = i - h * (D + 2);
         part_base[h * part_hstride + c] = c == D ? -INFINITY : 0.f;
       }
@@ -247,26 +279,41 @@ __global__ __launch_bounds__(256) void k_decode_pq(PqDecodeArgs a) {
     const uint8_t* vbase = a.vc + (bg * a.cap_mid + row0) * kPqSub;
     float* rawb = SIDE ? a.raw + (size_t)(b * Hq + g * NREP) * a.raw_stride : nullptr;
     const int n_chunks = (n_tok + 63) / 64;
-    const int rounds = (n_chunks + 3) / 4;
-    for (int r = 0; r < rounds; ++r) {
-      const int chunk = 4 * r + wave;
-      if (chunk >= n_chunks) continue;            // per wave; no workgroup barrier inside
+    // this wave's chunks are wave, wave + NW, ...; the code rows of the next
+    // one are loaded while the current one is computed
+    struct CodeRegs {
+      uint4 k[4][2];                              // key rows of tokens 16 grp + hl
+      uint4 v[2];                                 // value row of token `lane`
+    };
+    auto load_chunk = [&](CodeRegs& cr, int chunk) {
+      const int c0 = chunk * 64, nt = min(64, n_tok - c0);
+      const uint4* vs = reinterpret_cast<const uint4*>(vbase + (size_t)(c0 + min(lane, nt - 1)) * kPqSub);
+      cr.v[0] = vs[0];
+      cr.v[1] = vs[1];
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+        const uint4* ks = reinterpret_cast<const uint4*>(kbase + (size_t)(c0 + min(16 * grp + hl, nt - 1)) * kPqSub);
+        cr.k[grp][0] = ks[0];
+        cr.k[grp][1] = ks[1];
+      }
+    };
+    CodeRegs nxt;
+    if (wave < n_chunks) load_chunk(nxt, wave);
+    for (int chunk = wave; chunk < n_chunks; chunk += NW) {   // per wave; no workgroup barrier inside
+      const CodeRegs cur = nxt;
+      if (chunk + NW < n_chunks) load_chunk(nxt, chunk + NW);
       const int c0 = chunk * 64;
       const int nt = min(64, n_tok - c0);
       // value code rows of the chunk into LDS (lane = token)
       {
-        const int t = min(lane, nt - 1);
-        const uint4* src = reinterpret_cast<const uint4*>(vbase + (size_t)(c0 + t) * kPqSub);
         uint4* dst = reinterpret_cast<uint4*>(vcw + lane * kPqSub);
-        dst[0] = src[0];
-        dst[1] = src[1];
+        dst[0] = cur.v[0];
+        dst[1] = cur.v[1];
       }
       float sc[4][4];                             // [group][j]: head hl, token 16 grp + 4 quad + j
 #pragma unroll
       for (int grp = 0; grp < 4; ++grp) {
-        const int t = min(16 * grp + hl, nt - 1);
-        const uint4* src = reinterpret_cast<const uint4*>(kbase + (size_t)(c0 + t) * kPqSub);
-        const uint4 w0 = src[0], w1 = src[1];
+        const uint4 w0 = cur.k[grp][0], w1 = cur.k[grp][1];
         const uint32_t cw[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
         pq_f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -339,30 +386,31 @@ __global__ __launch_bounds__(256) void k_decode_pq(PqDecodeArgs a) {
       pq_wave_lds_sync();
       // PV: lane (sub_pv, par) adds p times the value centroid of sub-space
       // sub_pv for the tokens of parity par
-      for (int t2 = 0; t2 < nt; t2 += 2) {
-        const int t = t2 + par;
-        if (t < nt) {
-          const int code = vcw[t * kPqSub + sub_pv];
-          const uint16_t* cv = cbv + (code * kPqSub + sub_pv) * L;
-          float cf[L];
-          if constexpr (L == 4) {
-            const uint2 w = *reinterpret_cast<const uint2*>(cv);
-            cf[0] = h2f((uint16_t)(w.x & 0xFFFFu));
-            cf[1] = h2f((uint16_t)(w.x >> 16));
-            cf[2] = h2f((uint16_t)(w.y & 0xFFFFu));
-            cf[3] = h2f((uint16_t)(w.y >> 16));
-          } else {
-            const uint32_t w = *reinterpret_cast<const uint32_t*>(cv);
-            cf[0] = h2f((uint16_t)(w & 0xFFFFu));
-            cf[1] = h2f((uint16_t)(w >> 16));
-          }
-#pragma unroll
-          for (int h = 0; h < NREP; ++h) {
-            const float p = pw[t * NREP + h];
-#pragma unroll
-            for (int e = 0; e < L; ++e) o[h][e] = fmaf(p, cf[e], o[h][e]);
-          }
+      // All 32 token pairs of the chunk, unrolled: a token past the chunk's
+      // end has weight 0 and a valid (repeated) code row.
+#pragma unroll 8
+      for (int it = 0; it < 32; ++it) {
+        const int t = 2 * it + par;
+        const int code = vcw[t * kPqSub + sub_pv];
+        const uint16_t* cv = cbv + (code * kPqSub + sub_pv) * L;
+        float cf[L];
+        if constexpr (L == 4) {
+          const uint2 w = *reinterpret_cast<const uint2*>(cv);
+          cf[0] = h2f((uint16_t)(w.x & 0xFFFFu));
+          cf[1] = h2f((uint16_t)(w.x >> 16));
+          cf[2] = h2f((uint16_t)(w.y & 0xFFFFu));
+          cf[3] = h2f((uint16_t)(w.y >> 16));
+        } else {
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(cv);
+          cf[0] = h2f((uint16_t)(w & 0xFFFFu));
+          cf[1] = h2f((uint16_t)(w >> 16));
         }
+        float pt[NREP];
+        pq_load_weights<NREP>(pw + t * NREP, pt);
+#pragma unroll
+        for (int h = 0; h < NREP; ++h)
+#pragma unroll
+          for (int e = 0; e < L; ++e) o[h][e] = fmaf(pt[h], cf[e], o[h][e]);
       }
       pq_wave_lds_sync();
     }
@@ -386,14 +434,14 @@ __global__ __launch_bounds__(256) void k_decode_pq(PqDecodeArgs a) {
       wml[wave * 32 + 16 + lane] = lsum;
     }
     __syncthreads();
-    for (int i = tid; i < NREP * (D + 2); i += 256) {
+    for (int i = tid; i < NREP * (D + 2); i += NT) {
       const int h = i / (D + 2), c = i - h * (D + 2);
       float mxw = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) mxw = fmaxf(mxw, wml[w * 32 + h]);
+      for (int w = 0; w < NW; ++w) mxw = fmaxf(mxw, wml[w * 32 + h]);
       float acc = 0.f, ls = 0.f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
+      for (int w = 0; w < NW; ++w) {
         const float mw = wml[w * 32 + h];
         if (mw == -INFINITY) continue;
         const float e = __builtin_amdgcn_exp2f(mw - mxw);
@@ -408,10 +456,11 @@ __global__ __launch_bounds__(256) void k_decode_pq(PqDecodeArgs a) {
 
 template <int L, int NREP>
 static void launch_pq_mid_t(const PqDecodeArgs& a, int blocks, hipStream_t st) {
+  constexpr int NT = PqLayout<L, NREP>::NW * 64;
   if (a.raw)
-    hipLaunchKernelGGL((k_decode_pq<L, NREP, true>), dim3(blocks), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_decode_pq<L, NREP, true>), dim3(blocks), dim3(NT), 0, st, a);
   else
-    hipLaunchKernelGGL((k_decode_pq<L, NREP, false>), dim3(blocks), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_decode_pq<L, NREP, false>), dim3(blocks), dim3(NT), 0, st, a);
 }
 
 template <int L>
