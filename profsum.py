@@ -1,9 +1,9 @@
 """Reduce rocprofv3 CSV output to short per-kernel text summaries.
 
-    python -m tiered_quantized_kv_amd.profsum stats  <kernel_stats.csv>  [--match REGEX]
-    python -m tiered_quantized_kv_amd.profsum counters <counter_collection.csv> [--match REGEX]
+    python3 profsum.py stats  <kernel_stats.csv>  [--match REGEX]
+    python3 profsum.py counters <counter_collection.csv> [--match REGEX]
         [--delete]
-    python -m tiered_quantized_kv_amd.profsum traffic --fetch F.csv --write W.csv --match REGEX
+    python3 profsum.py traffic --fetch F.csv --write W.csv --match REGEX
         --copy-match REGEX --copy-bytes N --source FILE [FILE ...] [--delete]
 
 `stats` lists calls and average / min / max duration per kernel (from
