@@ -28,9 +28,15 @@ FLAGS = [
 ]
 
 
+# Per-source flags. The H2O prefill kernels take their MFMA results into
+# VGPRs: the fp32 score tiles feed VALU exp / sum work at once, and the
+# accumulator-to-VGPR copy per score is then not needed.
+EXTRA = {"k_h2o.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l)

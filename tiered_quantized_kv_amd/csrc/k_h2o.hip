@@ -8,15 +8,17 @@
 // softmax_i(q_i . k / sqrt(d))_j.
 //
 // Two passes, both QK^T on v_mfma_f32_16x16x32_f16 (fp16 in, fp32 out):
-//   k_h2o_rowlse   (L/16) x Hkv x B workgroups: 16 query rows of every query head of
-//                  a KV group stream the causal 64-key tiles of that group
-//                  (staged once in LDS for all its heads) and keep an online
+//   k_h2o_rowlse   (L/32) x Hkv x B workgroups when that fills the GPU, else L/16: 32
+//                  query rows (two 16-row tiles; else one) of every query head of a
+//                  KV group stream the causal 64-key tiles of that group
+//                  (staged once in LDS for all its heads; each key fragment
+//                  read from LDS serves both row tiles) and keep an online
 //                  max / sum; writes the log2-domain LSE of each row.
-//   k_h2o_colsum   (L/64) x Hkv x B x chunks workgroups: 64 keys held as MFMA B
-//                  fragments in registers; the waves walk the (query head,
-//                  16-row query tile) items of a chunk of query tiles at or
-//                  below the diagonal, accumulating p = 2^(s - LSE_i)
-//                  per key.
+//   k_h2o_colsum2  (L/256) x Hkv x B x chunks workgroups: 256 keys, 64 per
+//                  wave held as MFMA B fragments in registers; the (query tile,
+//                  query head) items of a chunk of query tiles stream through
+//                  LDS in triple-buffered stages shared by the four waves,
+//                  accumulating p = 2^(s - LSE_i) per key.
 //   k_h2o_reduce   sums the partials over chunks, KV groups (and the batch
 //                  rows when shared) in a fixed order.
 // MFMA 16x16x32 lane layout: A row = lane % 16, k = 8 * (lane / 16) + [0, 8);
@@ -31,29 +33,13 @@ namespace fade {
 
 constexpr int kTile = 64;
 
-// Column pass work split: the query tiles at or below a 64-key tile are cut
-// into chunks of qt_per 16-row tiles, one workgroup per (key tile, KV group,
-// row, chunk); enough chunks for about 4096 workgroups, each at least eight
-// tiles long. Chunks past a key tile's causal range exit at once.
-static void colsum_split(int Hkv, int batch, int L, int& n_chunks, int& qt_per) {
-  const long tiles = (L + kTile - 1) / kTile;
-  const int n_qt = (L + 15) / 16;
-  const long base = tiles * Hkv * batch;
-  int nch = (int)((4096 + base - 1) / base);
-  nch = max(1, min(nch, (n_qt + 7) / 8));
-  qt_per = (n_qt + nch - 1) / nch;
-  n_chunks = (n_qt + qt_per - 1) / qt_per;
-}
-static int colsum_chunks(int Hkv, int batch, int L) {
-  int nch, qp;
-  colsum_split(Hkv, batch, L, nch, qp);
-  return nch;
-}
+static void colsum2_split(int n_rep, int Hkv, int batch, int L, int& n_chunks, int& qt_per);
 
 size_t h2o_ws_bytes(int D, int Hq, int Hkv, int batch, int L) {
   (void)D;
-  return align_up((size_t)batch * Hq * L * 4, 256) +
-         align_up((size_t)colsum_chunks(Hkv, batch, L) * batch * Hkv * L * 4, 256);
+  int nch, qt_per;
+  colsum2_split(Hq / Hkv, Hkv, batch, L, nch, qt_per);
+  return align_up((size_t)batch * Hq * L * 4, 256) + align_up((size_t)nch * batch * Hkv * L * 4, 256);
 }
 
 // An empty asm statement that reads and rewrites a loaded fragment: the
@@ -86,7 +72,7 @@ __device__ __forceinline__ float max4(float a, float b, float c, float d) {
   return __builtin_fmaxf(__builtin_fmaxf(a, b), __builtin_fmaxf(c, d));
 }
 
-template <int D, int HPW>
+template <int D, int HPW, int RT>
 __global__ __launch_bounds__(256) void k_h2o_rowlse(const uint16_t* __restrict__ q,
                                                     const uint16_t* __restrict__ k, int Hq, int Hkv,
                                                     int L, int batch, float scale, float* __restrict__ lse) {
@@ -95,20 +81,20 @@ __global__ __launch_bounds__(256) void k_h2o_rowlse(const uint16_t* __restrict__
   constexpr int CPT = kTile * (D / 8) / 256;    // 16-byte chunks per thread per tile
   __shared__ __align__(16) uint16_t ktile[3][kTile * PITCH];
   // 1-D grid, XCD aware: id % 8 picks the XCD, and each XCD walks the row
-  // tiles of one (row, KV group) at a time, longest rows (most key tiles)
-  // first, so that group's keys stay in that XCD's L2.
-  const int n_rt = (L + 15) / 16;
+  // blocks (RT 16-row tiles) of one (row, KV group) at a time, longest rows
+  // (most key tiles) first, so that group's keys stay in that XCD's L2.
+  const int n_rb = ((L + 15) / 16 + RT - 1) / RT;
   const int id = blockIdx.x, xcd = id % 8, slot = id / 8;
-  const int rt = n_rt - 1 - slot % n_rt;
-  const int pair = (slot / n_rt) * 8 + xcd;
+  const int rb = n_rb - 1 - slot % n_rb;
+  const int pair = (slot / n_rb) * 8 + xcd;
   if (pair >= Hkv * batch) return;
   const int g = pair % Hkv, b = pair / Hkv;
   const int n_rep = Hq / Hkv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int r0 = rt * 16;
+  const int r0 = rb * 16 * RT;
   const uint16_t* kb_ = k + ((size_t)(b * Hkv + g) * L) * D;
-  const int n_kt = min(r0 + 15, L - 1) / kTile + 1;
+  const int n_kt = min(r0 + 16 * RT - 1, L - 1) / kTile + 1;
 
   // Key tiles are triple buffered: tile kt + 2 is loaded into registers while
   // tile kt is used, and stored to LDS after it.
@@ -136,28 +122,32 @@ __global__ __launch_bounds__(256) void k_h2o_rowlse(const uint16_t* __restrict__
   lstore(0);
   if (n_kt > 1) gload(1);
 
-  f16x8 afrag[HPW][KB];
-  float m_l[HPW][4], l_l[HPW][4];
-  const int row_base = r0 + 4 * (lane >> 4);
+  // item (t, j): row tile t of the block, query head wave + 4 j
+  f16x8 afrag[RT][HPW][KB];
+  float m_l[RT][HPW][4], l_l[RT][HPW][4];
   const float m_init = kMaskedRaw * scale;       // exact
 #pragma unroll
-  for (int j = 0; j < HPW; ++j) {
-    const int hl = wave + 4 * j;
-    const int r = min(r0 + (lane & 15), L - 1);
-    const uint16_t* qb = q + ((size_t)(b * Hq + g * n_rep + min(hl, n_rep - 1)) * L) * D;
+  for (int t = 0; t < RT; ++t)
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) afrag[j][kb] = load8(qb + (size_t)r * D + kb * 32 + 8 * (lane >> 4));
+    for (int j = 0; j < HPW; ++j) {
+      const int hl = wave + 4 * j;
+      const int r = min(r0 + 16 * t + (lane & 15), L - 1);
+      const uint16_t* qb = q + ((size_t)(b * Hq + g * n_rep + min(hl, n_rep - 1)) * L) * D;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      m_l[j][i] = m_init;
-      l_l[j][i] = 0.f;
+      for (int kb = 0; kb < KB; ++kb) afrag[t][j][kb] = load8(qb + (size_t)r * D + kb * 32 + 8 * (lane >> 4));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        m_l[t][j][i] = m_init;
+        l_l[t][j][i] = 0.f;
+      }
     }
-  }
   if (n_kt > 1) lstore(1);
 #pragma unroll
-  for (int j = 0; j < HPW; ++j)
+  for (int t = 0; t < RT; ++t)
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) settle(afrag[j][kb]);
+    for (int j = 0; j < HPW; ++j)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) settle(afrag[t][j][kb]);
   if (n_kt > 2) gload(2);
   __syncthreads();
   for (int kt = 0; kt < n_kt; ++kt) {
@@ -165,38 +155,47 @@ __global__ __launch_bounds__(256) void k_h2o_rowlse(const uint16_t* __restrict__
 #pragma unroll
     for (int j = 0; j < HPW; ++j) {
       if (wave + 4 * j >= n_rep) continue;      // wave-uniform
-      f32x4 acc[4];
+      // every B fragment read from LDS serves the RT row tiles
+      f32x4 acc[RT][4];
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) acc[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
           const f16x8 bfrag = __builtin_bit_cast(
               f16x8, *reinterpret_cast<const uint4*>(&kt_lds[(nb * 16 + (lane & 15)) * PITCH + kb * 32 + 8 * (lane >> 4)]));
-          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afrag[j][kb], bfrag, acc[nb], 0, 0, 0);
+#pragma unroll
+          for (int t = 0; t < RT; ++t)
+            acc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afrag[t][j][kb], bfrag, acc[t][nb], 0, 0, 0);
         }
-      if (kt == n_kt - 1) {                      // the diagonal tile (and the end of L)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const int key = kt * kTile + nb * 16 + (lane & 15);
+      for (int t = 0; t < RT; ++t) {
+        const int row_base = r0 + 16 * t + 4 * (lane >> 4);
+        if (kt == n_kt - 1) {                    // the diagonal tile (and the end of L)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (key > row_base + i || key >= L) acc[nb][i] = kMaskedRaw;
+          for (int nb = 0; nb < 4; ++nb) {
+            const int key = kt * kTile + nb * 16 + (lane & 15);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (key > row_base + i || key >= L) acc[t][nb][i] = kMaskedRaw;
+          }
         }
-      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float mn = fmaxf(m_l[j][i], max4(acc[0][i], acc[1][i], acc[2][i], acc[3][i]) * scale);
-        l_l[j][i] *= __builtin_amdgcn_exp2f(m_l[j][i] - mn);
-        m_l[j][i] = mn;
-      }
+        for (int i = 0; i < 4; ++i) {
+          const float mn = fmaxf(m_l[t][j][i], max4(acc[t][0][i], acc[t][1][i], acc[t][2][i], acc[t][3][i]) * scale);
+          l_l[t][j][i] *= __builtin_amdgcn_exp2f(m_l[t][j][i] - mn);
+          m_l[t][j][i] = mn;
+        }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float acc_l = l_l[j][i];
+        for (int i = 0; i < 4; ++i) {
+          float acc_l = l_l[t][j][i];
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) acc_l += __builtin_amdgcn_exp2f(fmaf(acc[nb][i], scale, -m_l[j][i]));
-        l_l[j][i] = acc_l;
+          for (int nb = 0; nb < 4; ++nb) acc_l += __builtin_amdgcn_exp2f(fmaf(acc[t][nb][i], scale, -m_l[t][j][i]));
+          l_l[t][j][i] = acc_l;
+        }
       }
     }
     // buffer (kt + 2) % 3 was last read in iteration kt - 1, before the
@@ -207,56 +206,70 @@ __global__ __launch_bounds__(256) void k_h2o_rowlse(const uint16_t* __restrict__
   }
   // merge the 16 lanes of each row: LSE = M + log2(sum_lanes l * 2^(m - M))
 #pragma unroll
-  for (int j = 0; j < HPW; ++j) {
-    const int hl = wave + 4 * j;
-    if (hl >= n_rep) continue;
+  for (int t = 0; t < RT; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float M = m_l[j][i];
-      M = fmaxf(M, dpp_f<kRowRor1>(M));
-      M = fmaxf(M, dpp_f<kRowRor2>(M));
-      M = fmaxf(M, dpp_f<kRowRor4>(M));
-      M = fmaxf(M, dpp_f<kRowRor8>(M));
-      float l = l_l[j][i] * __builtin_amdgcn_exp2f(m_l[j][i] - M);
-      l = row_sum_strided<1>(l);
-      const int row = row_base + i;
-      if ((lane & 15) == 0 && row < L)
-        lse[(size_t)(b * Hq + g * n_rep + hl) * L + row] = M + __builtin_amdgcn_logf(l);
+    for (int j = 0; j < HPW; ++j) {
+      const int hl = wave + 4 * j;
+      if (hl >= n_rep) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float M = m_l[t][j][i];
+        M = fmaxf(M, dpp_f<kRowRor1>(M));
+        M = fmaxf(M, dpp_f<kRowRor2>(M));
+        M = fmaxf(M, dpp_f<kRowRor4>(M));
+        M = fmaxf(M, dpp_f<kRowRor8>(M));
+        float l = l_l[t][j][i] * __builtin_amdgcn_exp2f(m_l[t][j][i] - M);
+        l = row_sum_strided<1>(l);
+        const int row = r0 + 16 * t + 4 * (lane >> 4) + i;
+        if ((lane & 15) == 0 && row < L)
+          lse[(size_t)(b * Hq + g * n_rep + hl) * L + row] = M + __builtin_amdgcn_logf(l);
+      }
     }
-  }
 }
 
-// Column pass. Workgroup = (64 keys, KV group, query-row chunk); the keys are
-// staged once in LDS and the four waves walk the (query head of
-// the group, 16-row query tile) items of the chunk at or below the diagonal.
-// Each wave keeps two items in flight in fixed registers (the next one's
-// loads are issued while one is computed), computes the four 16-key
-// blocks of an item as independent MFMA chains, and takes the causal / tail
-// mask only on the items that touch the diagonal or the end of L. Loads are
-// clamped to row L - 1 instead of predicated; what they read past L is
-// masked or never written. Per-lane column partials are reduced across rows,
-// waves and (in k_h2o_reduce) chunks and groups in a fixed order.
+// Column pass, key-block form. Workgroup = (256 keys, KV group, chunk of query
+// tiles); wave w holds keys [64 w, 64 w + 64) of the block as MFMA B fragments
+// in registers, and the workgroup streams the chunk's (query tile, query head)
+// items through LDS in stages of four (triple buffered, one barrier per
+// stage): every wave runs every item against its own keys, so one query load
+// serves 256 keys and no key is re-read. A wave skips items whose rows all lie
+// before its keys and masks only items that touch its diagonal or the end of
+// L. Chunks are absolute ranges of query tiles (so workgroups of one chunk
+// share the query rows in L2); a workgroup whose chunk lies before its keys
+// writes zeros.
+constexpr int kKeyBlock = 256;
+constexpr int kColItems = 4;                     // items per stage
+
+static void colsum2_split(int n_rep, int Hkv, int batch, int L, int& n_chunks, int& qt_per) {
+  const int n_qt = (L + 15) / 16;
+  const long kb = (L + kKeyBlock - 1) / kKeyBlock;
+  const long base = kb * Hkv * batch;
+  // about 2048 workgroups (half of them past the causal range), at least two
+  // stages each
+  int per = (int)((long)n_qt * base / 2048);
+  per = max(per, (2 * kColItems + n_rep - 1) / n_rep);
+  per = max(1, min(per, n_qt));
+  qt_per = per;
+  n_chunks = (n_qt + per - 1) / per;
+}
+
 template <int D>
-__global__ __launch_bounds__(256) void k_h2o_colsum(const uint16_t* __restrict__ q,
-                                                    const uint16_t* __restrict__ k, int Hq, int Hkv,
-                                                    int L, int batch, int n_chunks, int qt_per,
-                                                    float scale, const float* __restrict__ lse,
-                                                    float* __restrict__ part) {
+__global__ __launch_bounds__(256) void k_h2o_colsum2(const uint16_t* __restrict__ q,
+                                                     const uint16_t* __restrict__ k, int Hq, int Hkv,
+                                                     int L, int batch, int n_chunks, int qt_per,
+                                                     float scale, const float* __restrict__ lse,
+                                                     float* __restrict__ part) {
   constexpr int KB = D / 32;
-  constexpr int kInFlight = 2;
-  constexpr int PITCH = D + 8;                  // halves per LDS key row
-  constexpr int CPT = kTile * (D / 8) / 256;    // 16-byte chunks per thread
-  __shared__ __align__(16) uint16_t ktile[kTile * PITCH];
-  __shared__ float colred[4][kTile];
-  // 1-D grid, XCD aware: workgroups are dealt to the 8 XCDs round-robin by
-  // id, so id % 8 picks the XCD and id / 8 walks, on that XCD, all key tiles
-  // of one (chunk, row, KV group) before the next: the chunk's query rows are
-  // fetched into that XCD's L2 once and reused by every key tile.
-  const int tiles = (L + kTile - 1) / kTile;
+  constexpr int PITCH = D + 8;                                // halves per LDS query row
+  constexpr int SROWS = kColItems * 16;                       // query rows per stage
+  constexpr int CPT = SROWS * (D / 8) / 256;                  // 16-byte chunks per thread per stage
+  __shared__ __align__(16) uint16_t qbuf[3][SROWS * PITCH];
+  __shared__ __align__(16) float lbuf[3][SROWS];
+  const int n_kb = (L + kKeyBlock - 1) / kKeyBlock;
   const int n_pairs = Hkv * batch * n_chunks;
   const int id = blockIdx.x, xcd = id % 8, slot = id / 8;
-  const int kt = slot % tiles;
-  const int pair = (slot / tiles) * 8 + xcd;
+  const int kbi = slot % n_kb;
+  const int pair = (slot / n_kb) * 8 + xcd;
   if (pair >= n_pairs) return;
   const int c = pair / (Hkv * batch), bg = pair % (Hkv * batch);
   const int b = bg / Hkv, g = bg % Hkv;
@@ -264,92 +277,120 @@ __global__ __launch_bounds__(256) void k_h2o_colsum(const uint16_t* __restrict__
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lq = lane >> 4;
-  const int k0 = kt * kTile;
-  const uint16_t* kb_ = k + ((size_t)(b * Hkv + g) * L) * D;
-  // query tiles of this workgroup: the chunk c of the tiles at or below the
-  // key tile's first key
-  const int qt_lo = k0 / 16 + c * qt_per;
-  const int qlo = qt_lo * 16, qhi = min(L, (qt_lo + qt_per) * 16);
+  const int k0 = kbi * kKeyBlock, kw0 = k0 + 64 * wave;     // this wave's first key
+  const int n_qt = (L + 15) / 16;
+  // the chunk's query tiles, from the first one that reaches the key block
+  const int qt_lo = max(c * qt_per, k0 / 16), qt_hi = min((c + 1) * qt_per, n_qt);
+  const int n_items = qt_lo < qt_hi ? (qt_hi - qt_lo) * n_rep : 0;
+  const int n_stages = (n_items + kColItems - 1) / kColItems;
   float col[4] = {0.f, 0.f, 0.f, 0.f};
-  if (qlo < qhi) {                               // workgroup-uniform
-    // the 64 keys, staged once in LDS and read as MFMA B fragments per item
-    // (keeping them in registers instead costs two waves per SIMD)
+  if (n_stages > 0) {                                          // workgroup-uniform
+    // this wave's 64 keys as B fragments: key nb * 16 + lr, channels
+    // kb * 32 + 8 lq .. + 8 (keys past L read row L - 1 and are masked)
+    const uint16_t* kb_ = k + ((size_t)(b * Hkv + g) * L) * D;
+    f16x8 kf[4][KB];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int key = min(kw0 + nb * 16 + lr, L - 1);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) kf[nb][kb] = load8(kb_ + (size_t)key * D + kb * 32 + 8 * lq);
+    }
+    const size_t head0 = (size_t)(b * Hq + g * n_rep) * L;
+    // item i: query tile qt_lo + i / n_rep, query head i % n_rep
+    // native vector arrays: HIP's uint4 is a struct, whose copies keep an
+    // array of them in scratch memory
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    struct StageRegs {
+      u32x4 v[CPT];
+      float l;
+    };
+    // this thread's stage rows: row rr_u = x / (D / 8) of the stage (item
+    // rr_u / 16, row rr_u % 16 of its tile) and 16-byte chunk x % (D / 8);
+    // n_rep is a power of two, so an item splits into (tile, head) by shifts
+    const int lg = __builtin_ctz((unsigned)n_rep);
+    int sj[CPT], sr[CPT], sc8[CPT];
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-      const int i = tid + 256 * u;
-      const int r = i / (D / 8), c8 = i - r * (D / 8);
-      const int key = min(k0 + r, L - 1);
-      *reinterpret_cast<uint4*>(&ktile[r * PITCH + c8 * 8]) =
-          *reinterpret_cast<const uint4*>(kb_ + (size_t)key * D + c8 * 8);
+      const int x = tid + 256 * u;
+      const int rr = x / (D / 8);
+      sj[u] = rr / 16;
+      sr[u] = rr % 16;
+      sc8[u] = x % (D / 8);
     }
+    const uint16_t* qh = q + head0 * D;
+    auto gload = [&](int st) {
+      StageRegs r;
+#pragma unroll
+      for (int u = 0; u < CPT; ++u) {
+        const int it = min(st * kColItems + sj[u], n_items - 1);
+        const int row = min(((qt_lo + (it >> lg)) << 4) + sr[u], L - 1);
+        r.v[u] = *reinterpret_cast<const u32x4*>(qh + ((size_t)(it & (n_rep - 1)) * L + row) * D + sc8[u] * 8);
+      }
+      const int it = min(st * kColItems + ((tid >> 4) & (kColItems - 1)), n_items - 1);
+      const int row = min(((qt_lo + (it >> lg)) << 4) + (tid & 15), L - 1);
+      r.l = tid < SROWS ? lse[head0 + (size_t)(it & (n_rep - 1)) * L + row] : 0.f;
+      return r;
+    };
+    auto lstore = [&](int buf, StageRegs r) {
+#pragma unroll
+      for (int u = 0; u < CPT; ++u)
+        *reinterpret_cast<u32x4*>(&qbuf[buf][(sj[u] * 16 + sr[u]) * PITCH + sc8[u] * 8]) = r.v[u];
+      if (tid < SROWS) lbuf[buf][tid] = r.l;
+    };
+    StageRegs pre = gload(0);
+    lstore(0, pre);
+    if (n_stages > 1) {
+      pre = gload(1);
+      lstore(1, pre);
+    }
+    if (n_stages > 2) pre = gload(2);
     __syncthreads();
-    const int first_qt = qlo / 16;
-    const int n_qt = (qhi - qlo + 15) / 16;
-    const int items = n_rep * n_qt;
-    // Item idx = (query head idx / n_qt, tile first_qt + idx % n_qt); wave w
-    // takes items w, w + 4, ...
-    struct Item {
-      f16x8 a[KB];
-      float lrow[4];
-    };
-    const size_t head0 = (size_t)(b * Hq + g * n_rep) * L;
-    auto fetch = [&](Item& it, int idx) {
-      const int hl = idx / n_qt, qi = idx - hl * n_qt;
-      const size_t hrow = head0 + (size_t)hl * L;
-      const int rt = (first_qt + qi) * 16;
-      const uint16_t* qp = q + (hrow + min(rt + lr, L - 1)) * D + 8 * lq;
+    for (int st = 0; st < n_stages; ++st) {
+      const int buf = st % 3;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) it.a[kb] = load8(qp + kb * 32);
-      const int rb = rt + 4 * lq;
+      for (int j = 0; j < kColItems; ++j) {
+        const int it = st * kColItems + j;
+        if (it >= n_items) break;                              // workgroup-uniform
+        const int rt = (qt_lo + it / n_rep) * 16;
+        if (rt + 15 < kw0) continue;                           // wave-uniform: rows before every key
+        f16x8 af[KB];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) it.lrow[i] = lse[hrow + min(rb + i, L - 1)];
-    };
-    auto process = [&](const Item& it, int idx) {
-      const int hl = idx / n_qt;
-      const int rt = (first_qt + idx - hl * n_qt) * 16;
-      f32x4 acc[4];
+        for (int kb = 0; kb < KB; ++kb)
+          af[kb] = __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(
+                                                 &qbuf[buf][(j * 16 + lr) * PITCH + kb * 32 + 8 * lq]));
+        const float4 lr4 = *reinterpret_cast<const float4*>(&lbuf[buf][j * 16 + 4 * lq]);
+        const float lrow[4] = {lr4.x, lr4.y, lr4.z, lr4.w};
+        f32x4 acc[4];
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-              it.a[kb],
-              __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(
-                                            &ktile[(nb * 16 + lr) * PITCH + kb * 32 + 8 * lq])),
-              acc[nb], 0, 0, 0);
-      if (rt >= k0 + kTile && rt + 16 <= L) {    // wave-uniform: every (row, key) is live
+          for (int nb = 0; nb < 4; ++nb)
+            acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[kb], kf[nb][kb], acc[nb], 0, 0, 0);
+        if (rt >= kw0 + 64 && rt + 16 <= L) {                  // wave-uniform: every (row, key) is live
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
+          for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) col[nb] += __builtin_amdgcn_exp2f(fmaf(acc[nb][i], scale, -it.lrow[i]));
-      } else {
-        const int rb = rt + 4 * lq;
+            for (int i = 0; i < 4; ++i) col[nb] += __builtin_amdgcn_exp2f(fmaf(acc[nb][i], scale, -lrow[i]));
+        } else {
+          const int rb = rt + 4 * lq;
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const int key = k0 + nb * 16 + lr;
+          for (int nb = 0; nb < 4; ++nb) {
+            const int key = kw0 + nb * 16 + lr;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(acc[nb][i], scale, -it.lrow[i]));
-            col[nb] += (key <= rb + i && rb + i < L) ? p : 0.f;
+            for (int i = 0; i < 4; ++i) {
+              const float p = __builtin_amdgcn_exp2f(fmaf(acc[nb][i], scale, -lrow[i]));
+              col[nb] += (key <= rb + i && rb + i < L) ? p : 0.f;
+            }
           }
         }
       }
-    };
-    Item it[kInFlight];
-#pragma unroll
-    for (int u = 0; u < kInFlight; ++u)
-      if (wave + 4 * u < items) fetch(it[u], wave + 4 * u);
-    for (int idx = wave; idx < items; idx += 4 * kInFlight) {
-#pragma unroll
-      for (int u = 0; u < kInFlight; ++u) {
-        const int cur = idx + 4 * u;
-        if (cur < items) {                       // wave-uniform
-          process(it[u], cur);
-          if (cur + 4 * kInFlight < items) fetch(it[u], cur + 4 * kInFlight);
-        }
-      }
+      // buffer (st + 2) % 3 was last read in stage st - 1, before the barrier
+      // that ended it
+      if (st + 2 < n_stages) lstore((st + 2) % 3, pre);
+      if (st + 3 < n_stages) pre = gload(st + 3);
+      __syncthreads();
     }
   }
 #pragma unroll
@@ -361,37 +402,35 @@ __global__ __launch_bounds__(256) void k_h2o_colsum(const uint16_t* __restrict__
   }
   if (lane < 16) {
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) colred[wave][nb * 16 + lane] = col[nb];
-  }
-  __syncthreads();
-  if (tid < kTile) {
-    const int key = k0 + tid;
-    if (key < L) {
-      const float v = ((colred[0][tid] + colred[1][tid]) + colred[2][tid]) + colred[3][tid];
-      part[((size_t)(c * batch + b) * Hkv + g) * L + key] = v;
+    for (int nb = 0; nb < 4; ++nb) {
+      const int key = kw0 + nb * 16 + lane;
+      if (key < L) part[((size_t)(c * batch + b) * Hkv + g) * L + key] = col[nb];
     }
   }
 }
 
 // Sums the column partials over chunks, KV groups and (shared) batch rows in
-// a fixed order: four lanes per key each sum a quarter of the (row, group,
-// chunk) partials with eight loads in flight, then the quarters are added.
+// a fixed order: 16 keys per workgroup, 16 lanes per key; lane u sums the
+// partials u, u + 16, ... (ordered (b, g, c)) with eight loads in flight, and
+// the 16 lane sums of a key are added in lane order. Consecutive threads read
+// consecutive keys of one partial row.
+constexpr int kRedKeys = 16;
 __global__ __launch_bounds__(256) void k_h2o_reduce(const float* __restrict__ part, int Hkv, int L,
                                                     int batch, int n_chunks, int shared,
                                                     float* __restrict__ out) {
-  __shared__ float red[4][64];
+  __shared__ float red[16][kRedKeys];
   const int r = blockIdx.y;
-  const int u = threadIdx.x & 63, qtr = threadIdx.x >> 6;
-  const int j = blockIdx.x * 64 + u;
+  const int kk = threadIdx.x % kRedKeys, u = threadIdx.x / kRedKeys;
+  const int j = blockIdx.x * kRedKeys + kk;
   const int b0 = shared ? 0 : r, nb = shared ? batch : 1;
   const int n = nb * Hkv * n_chunks;              // partials per key, ordered (b, g, c)
   float acc = 0.f;
   if (j < L) {
-    for (int i0 = qtr; i0 < n; i0 += 32) {
+    for (int i0 = u; i0 < n; i0 += 16 * 8) {
       float v[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const int i = i0 + 4 * k;
+        const int i = i0 + 16 * k;
         if (i < n) {
           const int c = i % n_chunks, bg = i / n_chunks;
           const int g = bg % Hkv, b = b0 + bg / Hkv;
@@ -404,9 +443,14 @@ __global__ __launch_bounds__(256) void k_h2o_reduce(const float* __restrict__ pa
       for (int k = 0; k < 8; ++k) acc += v[k];
     }
   }
-  red[qtr][u] = acc;
+  red[u][kk] = acc;
   __syncthreads();
-  if (qtr == 0 && j < L) out[(size_t)r * L + j] = ((red[0][u] + red[1][u]) + red[2][u]) + red[3][u];
+  if (u == 0 && j < L) {
+    float t = red[0][kk];
+#pragma unroll
+    for (int x = 1; x < 16; ++x) t += red[x][kk];
+    out[(size_t)r * L + j] = t;
+  }
 }
 
 hipError_t launch_h2o_prefill(int D, int Hq, int Hkv, int batch, int L, int shared,
@@ -417,30 +461,39 @@ hipError_t launch_h2o_prefill(int D, int Hq, int Hkv, int batch, int L, int shar
   float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
                                          align_up((size_t)batch * Hq * L * 4, 256));
   const float scale = kLog2e / sqrtf((float)D);
-  const int tiles = (L + kTile - 1) / kTile;
-  int nch, qt_per;
-  colsum_split(Hkv, batch, L, nch, qt_per);
   const int n_rep = Hq / Hkv;
+  int nch, qt_per;
+  colsum2_split(n_rep, Hkv, batch, L, nch, qt_per);
+  const int n_kb = (L + kKeyBlock - 1) / kKeyBlock;
   const int n_pairs8 = (Hkv * batch * nch + 7) / 8 * 8;
-  const dim3 grow(((L + 15) / 16) * ((Hkv * batch + 7) / 8 * 8)), gcol(tiles * n_pairs8);
+  // row pass: two 16-row tiles per workgroup with one head per wave (every
+  // staged key fragment serves both) when that still gives about 1024
+  // workgroups, else one tile; one tile with two heads per wave at n_rep 8
+  const int rt_per = (n_rep <= 4 && (long)((L + 31) / 32) * Hkv * batch >= 1024) ? 2 : 1;
+  const int n_rb = ((L + 15) / 16 + rt_per - 1) / rt_per;
+  const dim3 grow(n_rb * ((Hkv * batch + 7) / 8 * 8)), gcol(n_kb * n_pairs8);
   if (D == 128) {
     if (n_rep > 4)
-      hipLaunchKernelGGL((k_h2o_rowlse<128, 2>), grow, dim3(256), 0, st, q, k, Hq, Hkv, L, batch, scale, lse);
+      hipLaunchKernelGGL((k_h2o_rowlse<128, 2, 1>), grow, dim3(256), 0, st, q, k, Hq, Hkv, L, batch, scale, lse);
+    else if (rt_per == 2)
+      hipLaunchKernelGGL((k_h2o_rowlse<128, 1, 2>), grow, dim3(256), 0, st, q, k, Hq, Hkv, L, batch, scale, lse);
     else
-      hipLaunchKernelGGL((k_h2o_rowlse<128, 1>), grow, dim3(256), 0, st, q, k, Hq, Hkv, L, batch, scale, lse);
-    hipLaunchKernelGGL(k_h2o_colsum<128>, gcol, dim3(256), 0, st, q, k, Hq, Hkv, L, batch, nch, qt_per, scale, lse, part);
+      hipLaunchKernelGGL((k_h2o_rowlse<128, 1, 1>), grow, dim3(256), 0, st, q, k, Hq, Hkv, L, batch, scale, lse);
+    hipLaunchKernelGGL(k_h2o_colsum2<128>, gcol, dim3(256), 0, st, q, k, Hq, Hkv, L, batch, nch, qt_per, scale, lse, part);
   } else {
     if (n_rep > 4)
-      hipLaunchKernelGGL((k_h2o_rowlse<64, 2>), grow, dim3(256), 0, st, q, k, Hq, Hkv, L, batch, scale, lse);
+      hipLaunchKernelGGL((k_h2o_rowlse<64, 2, 1>), grow, dim3(256), 0, st, q, k, Hq, Hkv, L, batch, scale, lse);
+    else if (rt_per == 2)
+      hipLaunchKernelGGL((k_h2o_rowlse<64, 1, 2>), grow, dim3(256), 0, st, q, k, Hq, Hkv, L, batch, scale, lse);
     else
-      hipLaunchKernelGGL((k_h2o_rowlse<64, 1>), grow, dim3(256), 0, st, q, k, Hq, Hkv, L, batch, scale, lse);
-    hipLaunchKernelGGL(k_h2o_colsum<64>, gcol, dim3(256), 0, st, q, k, Hq, Hkv, L, batch, nch, qt_per, scale, lse, part);
+      hipLaunchKernelGGL((k_h2o_rowlse<64, 1, 1>), grow, dim3(256), 0, st, q, k, Hq, Hkv, L, batch, scale, lse);
+    hipLaunchKernelGGL(k_h2o_colsum2<64>, gcol, dim3(256), 0, st, q, k, Hq, Hkv, L, batch, nch, qt_per, scale, lse, part);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int rows = shared ? 1 : batch;
-  hipLaunchKernelGGL(k_h2o_reduce, dim3((L + 63) / 64, rows), dim3(256), 0, st, part, Hkv, L, batch, nch,
-                     shared, scores_out);
+  hipLaunchKernelGGL(k_h2o_reduce, dim3((L + kRedKeys - 1) / kRedKeys, rows), dim3(256), 0, st, part, Hkv, L, batch,
+                     nch, shared, scores_out);
   return hipGetLastError();
 }
 
