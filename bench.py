@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--shape-calls", type=int, default=40,
                    help="timed decode-attention calls at each further shape (C4, S4, the PQ middle tier at the "
                         "workload's shape) on directly filled caches (0 = skip)")
+    p.add_argument("--shape-only", default=None, choices=["c4", "s4", "pq"],
+                   help="time only decode attention at this shape (pq: a PQ middle tier at the workload's "
+                        "shape) on directly filled caches, print its record and exit (for profiling)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="run one device copy of this size before timing (HBM counter calibration)")
     return p.parse_args()
@@ -528,6 +531,12 @@ def main():
     fade.lib()
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if a.shape_only:
+        calls = a.shape_calls if a.shape_calls > 0 else 40
+        r = (time_decode_direct(a.workload, calls, pq=True) if a.shape_only == "pq"
+             else time_decode_direct(a.shape_only, calls))
+        print(json.dumps({"shape_only": a.shape_only, "workload": a.workload, **r}), flush=True)
+        return
     steps = a.steps if a.steps is not None else {"c1": 50, "c2": 64, "c3": 64, "c4": 32, "c5": 32, "s4": 8}[a.workload]
     wl = Workload(a.workload, dev)
     print(f"[bench] setting up workload {a.workload} ...", file=sys.stderr, flush=True)

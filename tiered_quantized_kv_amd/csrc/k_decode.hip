@@ -819,6 +819,69 @@ __global__ __launch_bounds__(256) void k_decode_finish(const float* __restrict__
   }
 }
 
+// Finish without the side output over many splits (long caches with few
+// sequences): one workgroup per (sequence, query head, part of the output
+// channels). The 256 threads first form the head's statistics over all of
+// its splits (block max, then block sum), then each of the part's CPW
+// channels is summed over the splits by 256 / CPW thread groups (split s to
+// group s % SG, consecutive threads on consecutive channels of a split, so
+// each split's channels are read in one coalesced run) and the group sums
+// are added in group order.
+template <int D, int CPW>
+__global__ __launch_bounds__(256) void k_decode_finish_head(const float* __restrict__ part, int nsplit, int Hq,
+                                                            void* out, int out_dtype) {
+  constexpr int SG = 256 / CPW;
+  __shared__ float red[256];
+  __shared__ float s_m, s_inv;
+  const int b = blockIdx.x, h = blockIdx.y, c0 = blockIdx.z * CPW, tid = threadIdx.x;
+  const float* ph = part + ((size_t)b * Hq + h) * nsplit * (D + 2);
+  // ---- statistics of head h ----
+  float m = -INFINITY;
+  for (int sp = tid; sp < nsplit; sp += 256) m = fmaxf(m, ph[(size_t)sp * (D + 2) + D]);
+  red[tid] = m;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
+    __syncthreads();
+  }
+  const float M = red[0];
+  __syncthreads();
+  float l = 0.f;
+  for (int sp = tid; sp < nsplit; sp += 256) {
+    const float ms = ph[(size_t)sp * (D + 2) + D];
+    if (ms != -INFINITY) l = fmaf(ph[(size_t)sp * (D + 2) + D + 1], __builtin_amdgcn_exp2f(ms - M), l);
+  }
+  red[tid] = l;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) red[tid] += red[tid + w];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    s_m = M;
+    s_inv = 1.f / red[0];
+  }
+  __syncthreads();
+  // ---- the part's channels ----
+  const int c = c0 + tid % CPW, sg = tid / CPW;
+  float o = 0.f;
+  for (int sp = sg; sp < nsplit; sp += SG) {
+    const float ms = ph[(size_t)sp * (D + 2) + D];
+    if (ms != -INFINITY) o = fmaf(ph[(size_t)sp * (D + 2) + c], __builtin_amdgcn_exp2f(ms - s_m), o);
+  }
+  red[tid] = o;
+  __syncthreads();
+  if (sg == 0) {
+    float t = red[tid];
+    for (int g = 1; g < SG; ++g) t += red[g * CPW + tid];
+    t *= s_inv;
+    const size_t oi = ((size_t)b * Hq + h) * D + c;
+    if (out_dtype == FADE_DTYPE_F32) reinterpret_cast<float*>(out)[oi] = t;
+    else if (out_dtype == FADE_DTYPE_BF16) reinterpret_cast<uint16_t*>(out)[oi] = f2bf(t);
+    else reinterpret_cast<uint16_t*>(out)[oi] = f2h(t);
+  }
+}
+
 template <int D, int NREP, int KB, int VB, bool QBF>
 static void launch_tiers(const DecodeArgs& a, dim3 grid, hipStream_t st) {
   const size_t lds = (size_t)TierLayout<D, NREP, KB, VB>::total;
@@ -927,8 +990,9 @@ hipError_t launch_decode(const Shape& s, const fade_layer_cache& c, const void* 
   // partial heads), so their number follows the work that needs spreading:
   // with the side output, the slots (two 64-slot blocks per workgroup with
   // few splits, one with many), capped so that the statistics stay a small
-  // share of a workgroup's reads on long caches; without it, the outputs
-  // (one round of 32 elements per workgroup with many splits, 512 with few).
+  // share of a workgroup's reads on long caches; without it and few splits,
+  // the outputs (512 elements per workgroup). Without it and many splits,
+  // k_decode_finish_head forms each head's statistics once.
   const bool wide = nsplit > kFinishBatch;
   int nb;
   if (tok_attn) {
@@ -936,8 +1000,20 @@ hipError_t launch_decode(const Shape& s, const fade_layer_cache& c, const void* 
     nb = (s.cap_T + blocks * kFinishSlots - 1) / (blocks * kFinishSlots);
     nb = min(nb, max(1, s.cap_T / (16 * nsplit)));
   } else {
-    const int per_wg = wide ? 256 / 8 : 512;
-    nb = (s.Hq * s.D + per_wg - 1) / per_wg;
+    nb = (s.Hq * s.D + 511) / 512;
+  }
+  if (wide && !tok_attn) {
+    // one workgroup per (sequence, head, 32 or 16 output channels)
+    const bool fine = (long)s.batch * s.Hq * (s.D / 32) < 512;
+    const dim3 hgrid(s.batch, s.Hq, s.D / (fine ? 16 : 32));
+    if (s.D == 128) {
+      if (fine) hipLaunchKernelGGL((k_decode_finish_head<128, 16>), hgrid, dim3(256), 0, st, part, nsplit, s.Hq, out, out_dtype);
+      else hipLaunchKernelGGL((k_decode_finish_head<128, 32>), hgrid, dim3(256), 0, st, part, nsplit, s.Hq, out, out_dtype);
+    } else {
+      if (fine) hipLaunchKernelGGL((k_decode_finish_head<64, 16>), hgrid, dim3(256), 0, st, part, nsplit, s.Hq, out, out_dtype);
+      else hipLaunchKernelGGL((k_decode_finish_head<64, 32>), hgrid, dim3(256), 0, st, part, nsplit, s.Hq, out, out_dtype);
+    }
+    return hipGetLastError();
   }
   const dim3 fgrid(s.batch, nb);
   const size_t flds = ((size_t)2 * s.Hq + 4 * kFinishSlots) * 4;
