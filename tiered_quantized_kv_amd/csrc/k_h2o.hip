@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256) void k_h2o_rowlse(const uint16_t* __restrict__
   // Key tiles are triple buffered: tile kt + 2 is loaded into registers while
   // tile kt is used, and stored to LDS after it.
   uint4 pre[CPT];
-  auto gload = [&](int kt) {
+  auto gload = [&](int kt, uint4 (&dst)[CPT]) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int i = tid + 256 * c;
@@ -107,20 +107,25 @@ __global__ __launch_bounds__(256) void k_h2o_rowlse(const uint16_t* __restrict__
       const int key = kt * kTile + r;
       // (keys past L read as zero; written as a select, which also keeps
       // pre[] in registers)
-      pre[c] = key < L ? *reinterpret_cast<const uint4*>(kb_ + (size_t)key * D + c8 * 8) : make_uint4(0, 0, 0, 0);
+      dst[c] = key < L ? *reinterpret_cast<const uint4*>(kb_ + (size_t)key * D + c8 * 8) : make_uint4(0, 0, 0, 0);
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](int buf, const uint4 (&src)[CPT]) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int i = tid + 256 * c;
       const int r = i / (D / 8), c8 = i - r * (D / 8);
-      *reinterpret_cast<uint4*>(&ktile[buf][r * PITCH + c8 * 8]) = pre[c];
+      *reinterpret_cast<uint4*>(&ktile[buf][r * PITCH + c8 * 8]) = src[c];
     }
   };
-  gload(0);
-  lstore(0);
-  if (n_kt > 1) gload(1);
+  // tiles 0 and 1 (tile 0 again when there is one) and the query fragments
+  // are all in flight before the first wait
+  {
+    uint4 pre0[CPT];
+    gload(0, pre0);
+    gload(min(1, n_kt - 1), pre);
+    lstore(0, pre0);
+  }
 
   // item (t, j): row tile t of the block, query head wave + 4 j
   f16x8 afrag[RT][HPW][KB];
@@ -141,14 +146,14 @@ __global__ __launch_bounds__(256) void k_h2o_rowlse(const uint16_t* __restrict__
         l_l[t][j][i] = 0.f;
       }
     }
-  if (n_kt > 1) lstore(1);
+  if (n_kt > 1) lstore(1, pre);
 #pragma unroll
   for (int t = 0; t < RT; ++t)
 #pragma unroll
     for (int j = 0; j < HPW; ++j)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) settle(afrag[t][j][kb]);
-  if (n_kt > 2) gload(2);
+  if (n_kt > 2) gload(2, pre);
   __syncthreads();
   for (int kt = 0; kt < n_kt; ++kt) {
     const uint16_t* kt_lds = ktile[kt % 3];
@@ -200,8 +205,8 @@ __global__ __launch_bounds__(256) void k_h2o_rowlse(const uint16_t* __restrict__
     }
     // buffer (kt + 2) % 3 was last read in iteration kt - 1, before the
     // barrier that ended it
-    if (kt + 2 < n_kt) lstore((kt + 2) % 3);
-    if (kt + 3 < n_kt) gload(kt + 3);
+    if (kt + 2 < n_kt) lstore((kt + 2) % 3, pre);
+    if (kt + 3 < n_kt) gload(kt + 3, pre);
     __syncthreads();
   }
   // merge the 16 lanes of each row: LSE = M + log2(sum_lanes l * 2^(m - M))
@@ -337,11 +342,13 @@ __global__ __launch_bounds__(256) void k_h2o_colsum2(const uint16_t* __restrict_
         *reinterpret_cast<u32x4*>(&qbuf[buf][(sj[u] * 16 + sr[u]) * PITCH + sc8[u] * 8]) = r.v[u];
       if (tid < SROWS) lbuf[buf][tid] = r.l;
     };
+    // stages 0 and 1 (stage 0 again when there is one) are in flight together
+    // with the key fragments before the first wait
     StageRegs pre = gload(0);
-    lstore(0, pre);
-    if (n_stages > 1) {
-      pre = gload(1);
-      lstore(1, pre);
+    {
+      const StageRegs p1 = gload(min(1, n_stages - 1));
+      lstore(0, pre);
+      if (n_stages > 1) lstore(1, p1);
     }
     if (n_stages > 2) pre = gload(2);
     __syncthreads();
