@@ -68,12 +68,13 @@ constexpr int kThreads = 256;
 constexpr float kLazyMax = 3.f;
 constexpr int kSub = 64;          // tokens per wave sub-chunk (one per lane)
 
-constexpr long kDecodeMiddleWGs = 1024;   // middle workgroups the split aims for
+constexpr long kDecodeMiddleWGs = 512;    // middle workgroups the split aims for
 
 // Middle splits per (sequence, KV head): about kDecodeMiddleWGs middle
-// workgroups in all, so that the grid covers the chip, with at most 16 and at
-// least one 256-row unit (four waves x one sub-chunk) per split when the tier
-// is full. The kernel cuts the live middle tier M (not its capacity) into
+// workgroups in all (two per CU; longer, fewer workgroups measured faster
+// than twice as many: each one's query set-up, wave merge and partial cost
+// more than the finer balance gains), with at most 16 and at least one
+// 256-row unit (four waves x one sub-chunk) per split when the tier is full. The kernel cuts the live middle tier M (not its capacity) into
 // this many equal ranges of whole sub-chunks, so no split idles while
 // another streams twice its share.
 int decode_mid_splits(const Shape& s) {
