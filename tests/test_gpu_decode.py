@@ -119,6 +119,27 @@ def test_decode_output_dtypes(odt):
     assert ok, worst
 
 
+# Without the side output and with more than 8 splits the merge takes one
+# workgroup per (sequence, head, channel part): 16 channels per part when
+# batch x heads x d / 32 < 512, else 32; d 64 and 128.
+MANY_SPLITS = [
+    # d, hq, hkv, kb, vb, L, batch
+    (64, 8, 2, 4, 4, 6000, 1),       # 16-channel parts, d 64
+    (128, 32, 8, 4, 2, 2400, 4),     # 32-channel parts, d 128
+    (64, 32, 8, 2, 4, 2000, 8),      # 32-channel parts, d 64, K2/V4
+]
+
+
+@pytest.mark.parametrize("d,hq,hkv,kb,vb,L,B", MANY_SPLITS)
+def test_decode_many_splits_without_side_output(d, hq, hkv, kb, vb, L, B):
+    cfg = _cfg(d, hq, hkv, kb=kb, vb=vb, out_dtype="f32", rope_theta=5e5)
+    tc, refs, _ = build_both(cfg, B, L, 360 + d + B, cap_mid=L)
+    got, _, want = _run_decode(cfg, tc, refs, 361 + d + B, side=False)
+    for b in range(B):
+        ok, worst = out_close(got[b], want[b][0])
+        assert ok, (b, worst)
+
+
 def test_decode_ragged_batch():
     cfg = _cfg(128, 32, 8, w=64, kb=4, vb=2, rope_theta=5e5)
     lengths = [70, 1500, 333, 2200, 69]
