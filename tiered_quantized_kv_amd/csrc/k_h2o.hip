@@ -98,25 +98,29 @@ __global__ __launch_bounds__(256) void k_h2o_rowlse(const uint16_t* __restrict__
 
   // Key tiles are triple buffered: tile kt + 2 is loaded into registers while
   // tile kt is used, and stored to LDS after it.
+  // Thread tid copies the 16-byte chunk tid % (D / 8) of tile rows
+  // tid / (D / 8) + RSTEP * c: fixed offsets from a workgroup-uniform tile base.
+  constexpr int RSTEP = 256 / (D / 8);
+  const int r_t = tid / (D / 8), c8_t = tid % (D / 8);
+  const uint32_t goff = (uint32_t)(r_t * D + c8_t * 8);
+  const int loff = r_t * PITCH + c8_t * 8;
   uint4 pre[CPT];
   auto gload = [&](int kt, uint4 (&dst)[CPT]) {
+    const uint16_t* tb = kb_ + (size_t)kt * kTile * D;
+    if ((kt + 1) * kTile <= L) {                 // workgroup-uniform: a whole tile
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int i = tid + 256 * c;
-      const int r = i / (D / 8), c8 = i - r * (D / 8);
-      const int key = kt * kTile + r;
-      // (keys past L read as zero; written as a select, which also keeps
-      // pre[] in registers)
-      dst[c] = key < L ? *reinterpret_cast<const uint4*>(kb_ + (size_t)key * D + c8 * 8) : make_uint4(0, 0, 0, 0);
+      for (int c = 0; c < CPT; ++c) dst[c] = *reinterpret_cast<const uint4*>(tb + goff + c * RSTEP * D);
+    } else {
+      // keys past L read as zero (a select, which also keeps pre[] in registers)
+#pragma unroll
+      for (int c = 0; c < CPT; ++c)
+        dst[c] = kt * kTile + r_t + c * RSTEP < L ? *reinterpret_cast<const uint4*>(tb + goff + c * RSTEP * D)
+                                                  : make_uint4(0, 0, 0, 0);
     }
   };
   auto lstore = [&](int buf, const uint4 (&src)[CPT]) {
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int i = tid + 256 * c;
-      const int r = i / (D / 8), c8 = i - r * (D / 8);
-      *reinterpret_cast<uint4*>(&ktile[buf][r * PITCH + c8 * 8]) = src[c];
-    }
+    for (int c = 0; c < CPT; ++c) *reinterpret_cast<uint4*>(&ktile[buf][loff + c * RSTEP * PITCH]) = src[c];
   };
   // tiles 0 and 1 (tile 0 again when there is one) and the query fragments
   // are all in flight before the first wait
@@ -160,12 +164,9 @@ __global__ __launch_bounds__(256) void k_h2o_rowlse(const uint16_t* __restrict__
 #pragma unroll
     for (int j = 0; j < HPW; ++j) {
       if (wave + 4 * j >= n_rep) continue;      // wave-uniform
-      // every B fragment read from LDS serves the RT row tiles
+      // every B fragment read from LDS serves the RT row tiles; the first
+      // k-step takes a zero accumulator as an inline constant
       f32x4 acc[RT][4];
-#pragma unroll
-      for (int t = 0; t < RT; ++t)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) acc[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -174,7 +175,8 @@ __global__ __launch_bounds__(256) void k_h2o_rowlse(const uint16_t* __restrict__
               f16x8, *reinterpret_cast<const uint4*>(&kt_lds[(nb * 16 + (lane & 15)) * PITCH + kb * 32 + 8 * (lane >> 4)]));
 #pragma unroll
           for (int t = 0; t < RT; ++t)
-            acc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afrag[t][j][kb], bfrag, acc[t][nb], 0, 0, 0);
+            acc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afrag[t][j][kb], bfrag,
+                                                               kb == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[t][nb], 0, 0, 0);
         }
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
