@@ -158,44 +158,46 @@ __device__ __forceinline__ void pq_wave_lds_sync() {
   asm volatile("" ::: "memory");
 }
 
-// The NREP weights of one token (vector LDS reads).
+// The NREP fp16 weights of one token (one vector LDS read), as floats.
 template <int NREP>
-__device__ __forceinline__ void pq_load_weights(const float* src, float (&p)[NREP]) {
+__device__ __forceinline__ void pq_load_weights(const uint16_t* src, float (&p)[NREP]) {
   if constexpr (NREP >= 4) {
 #pragma unroll
     for (int i = 0; i < NREP / 4; ++i) {
-      const float4 v = reinterpret_cast<const float4*>(src)[i];
-      p[4 * i] = v.x;
-      p[4 * i + 1] = v.y;
-      p[4 * i + 2] = v.z;
-      p[4 * i + 3] = v.w;
+      const uint2 v = reinterpret_cast<const uint2*>(src)[i];
+      p[4 * i] = h2f((uint16_t)(v.x & 0xFFFFu));
+      p[4 * i + 1] = h2f((uint16_t)(v.x >> 16));
+      p[4 * i + 2] = h2f((uint16_t)(v.y & 0xFFFFu));
+      p[4 * i + 3] = h2f((uint16_t)(v.y >> 16));
     }
   } else if constexpr (NREP == 2) {
-    const float2 v = *reinterpret_cast<const float2*>(src);
-    p[0] = v.x;
-    p[1] = v.y;
+    const uint32_t v = *reinterpret_cast<const uint32_t*>(src);
+    p[0] = h2f((uint16_t)(v & 0xFFFFu));
+    p[1] = h2f((uint16_t)(v >> 16));
   } else {
-    p[0] = src[0];
+    p[0] = h2f(src[0]);
   }
 }
 
-// waves per workgroup: 8 where the LDS holds their buffers beside both
-// codebooks (two waves per SIMD at one workgroup per CU), else 4
-constexpr int pq_waves(int nrep) { return nrep <= 4 ? 8 : 4; }
+// waves per workgroup: 12 where the LDS holds their buffers beside both
+// codebooks (three waves per SIMD at one workgroup per CU), else 4
+constexpr int pq_waves(int nrep) { return nrep <= 4 ? 12 : 4; }
 
 template <int L, int NREP>
 struct PqLayout {
   static constexpr int D = L * kPqSub;
   static constexpr int NW = pq_waves(NREP);
   static constexpr int cb_bytes = kPqSub * kPqK * L * 2;
-  static constexpr int wave_bytes = 64 * NREP * 4 + 64 * kPqSub;     // weights [64][NREP] f32, value codes [64][32]
+  static constexpr int wave_bytes = 64 * NREP * 2 + 64 * kPqSub;     // weights [64][NREP] fp16, value codes [64][32]
   static constexpr int merge_bytes = NW * NREP * D * 4;              // per-wave unnormalized sums
   static constexpr int area = wave_bytes * NW > merge_bytes ? wave_bytes * NW : merge_bytes;
   static constexpr int total = 2 * cb_bytes + area + NW * 2 * 16 * 4;
 };
 
-// NW waves (8 at n_rep <= 4, else 4); a wave takes 64-token chunks wave,
-// wave + NW, ... of its work item. QK^T of a
+// NW waves (12 at n_rep <= 4, else 4); a wave takes 64-token chunks wave,
+// wave + NW, ... of its work item, loading each chunk's code rows as it
+// starts it (the three waves per SIMD hide that latency; a register copy of
+// the next chunk's rows cost more in occupancy than it hid). QK^T of a
 // 16-token group: A = the gathered key centroids (lane l: token l % 16,
 // channels 16 kb + 4 (l / 16) .. + 3), B = the query heads (lane l: head
 // l % 16, the same channels; heads >= NREP are zero), D / 16 MFMAs of
@@ -213,7 +215,7 @@ __global__ __launch_bounds__(pq_waves(NREP) * 64) void k_decode_pq(PqDecodeArgs 
   unsigned char* area = smem + 2 * Lay::cb_bytes;
   float* wml = reinterpret_cast<float*>(area + Lay::area);             // [NW][2][16]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  float* pw = reinterpret_cast<float*>(area + wave * Lay::wave_bytes);         // [64][NREP]
+  uint16_t* pw = reinterpret_cast<uint16_t*>(area + wave * Lay::wave_bytes);   // [64][NREP] fp16
   uint8_t* vcw = reinterpret_cast<uint8_t*>(pw + 64 * NREP);                   // [64][32]
   {
     // key codebook as in global memory (16-byte copies); value codebook
@@ -279,8 +281,7 @@ __global__ __launch_bounds__(pq_waves(NREP) * 64) void k_decode_pq(PqDecodeArgs 
     const uint8_t* vbase = a.vc + (bg * a.cap_mid + row0) * kPqSub;
     float* rawb = SIDE ? a.raw + (size_t)(b * Hq + g * NREP) * a.raw_stride : nullptr;
     const int n_chunks = (n_tok + 63) / 64;
-    // this wave's chunks are wave, wave + NW, ...; the code rows of the next
-    // one are loaded while the current one is computed
+    // this wave's chunks are wave, wave + NW, ...
     struct CodeRegs {
       uint4 k[4][2];                              // key rows of tokens 16 grp + hl
       uint4 v[2];                                 // value row of token `lane`
@@ -297,11 +298,9 @@ __global__ __launch_bounds__(pq_waves(NREP) * 64) void k_decode_pq(PqDecodeArgs 
         cr.k[grp][1] = ks[1];
       }
     };
-    CodeRegs nxt;
-    if (wave < n_chunks) load_chunk(nxt, wave);
     for (int chunk = wave; chunk < n_chunks; chunk += NW) {   // per wave; no workgroup barrier inside
-      const CodeRegs cur = nxt;
-      if (chunk + NW < n_chunks) load_chunk(nxt, chunk + NW);
+      CodeRegs cur;
+      load_chunk(cur, chunk);
       const int c0 = chunk * 64;
       const int nt = min(64, n_tok - c0);
       // value code rows of the chunk into LDS (lane = token)
@@ -381,7 +380,7 @@ __global__ __launch_bounds__(pq_waves(NREP) * 64) void k_decode_pq(PqDecodeArgs 
         for (int j = 0; j < 4; ++j) {
           const float p = __builtin_amdgcn_exp2f(sc[grp][j] - m_run);  // 0 for -inf scores
           l_lane += p;
-          if (hl < NREP) pw[(16 * grp + 4 * quad + j) * NREP + hl] = p;
+          if (hl < NREP) pw[(16 * grp + 4 * quad + j) * NREP + hl] = f2h(p);   // p <= 2^kPqLazyMax
         }
       pq_wave_lds_sync();
       // PV: lane (sub_pv, par) adds p times the value centroid of sub-space
