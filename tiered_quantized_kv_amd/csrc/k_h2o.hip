@@ -65,6 +65,7 @@ __device__ __forceinline__ f16x8 load8(const uint16_t* p) {
 //  * Query loads past L are clamped to row L - 1 (those rows are never
 //    written); key rows past L read as zero and are masked.
 constexpr float kMaskedRaw = -0x1p100f;
+constexpr float kRowLazy = 3.f;
 
 // max of four MFMA results (plain C: an inline-asm definition is not seen as a
 // VALU write by the hazard recognizer, which matters next to in-flight MFMAs)
@@ -190,11 +191,24 @@ __global__ __launch_bounds__(256) void k_h2o_rowlse(const uint16_t* __restrict__
               if (key > row_base + i || key >= L) acc[t][nb][i] = kMaskedRaw;
           }
         }
+        // The reference maximum is raised only when a score exceeds it by
+        // more than kRowLazy (log2 units), for every row of the wave at once:
+        // after the first tiles the rescale (an exp2 per row) is rare, and
+        // every term of the sum stays below 2^kRowLazy.
+        float tmx[4];
+        bool raise = false;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float mn = fmaxf(m_l[t][j][i], max4(acc[t][0][i], acc[t][1][i], acc[t][2][i], acc[t][3][i]) * scale);
-          l_l[t][j][i] *= __builtin_amdgcn_exp2f(m_l[t][j][i] - mn);
-          m_l[t][j][i] = mn;
+          tmx[i] = max4(acc[t][0][i], acc[t][1][i], acc[t][2][i], acc[t][3][i]) * scale;
+          raise |= tmx[i] > m_l[t][j][i] + kRowLazy;
+        }
+        if (__any(raise)) {                      // wave-uniform
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float mn = fmaxf(m_l[t][j][i], tmx[i]);
+            l_l[t][j][i] *= __builtin_amdgcn_exp2f(m_l[t][j][i] - mn);
+            m_l[t][j][i] = mn;
+          }
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
