@@ -302,6 +302,12 @@ class TimingEvent:
             self._hip.hipEventDestroy(self.ev)
 
 
+def spread(us):
+    """Median and 10th / 90th percentiles of per-launch durations (us)."""
+    q = np.percentile(np.asarray(us, np.float64), [10, 50, 90])
+    return {"p10_us": float(q[0]), "median_us": float(q[1]), "p90_us": float(q[2])}
+
+
 def measured_traffic(name):
     """HBM bytes per decode-attention call from the committed counter summary
     of this workload (FETCH_SIZE and WRITE_SIZE passes, copy-calibrated), or
@@ -580,9 +586,9 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     total_ms = t_start.elapsed_time(t_end)
-    dec_ms = sum(e[0].elapsed_time(e[1]) for row in ev for e in row if e is not None)
-    timed = sum(1 for row in ev for e in row if e is not None)
-    avg_dec_us = dec_ms * 1e3 / timed
+    dec_us = [e[0].elapsed_time(e[1]) * 1e3 for row in ev for e in row if e is not None]
+    timed = len(dec_us)
+    avg_dec_us = sum(dec_us) / timed
     bytes_per_launch = dec_bytes / (steps * wl.layers)     # every layer of a step has the same bytes
     achieved = bytes_per_launch / (avg_dec_us * 1e-6) / 1e9
     res = {
@@ -607,7 +613,7 @@ def main():
                    "name": a.workload, "layers": wl.layers, "batch": wl.B,
                    "kv_tokens_attended_per_step": dec_tokens // steps,
                    "admit_prefill_stream": None if wl.admit is None else "decode"},
-        "decode_attn": {"avg_us_per_launch": avg_dec_us, "bytes_per_launch": bytes_per_launch,
+        "decode_attn": {"avg_us_per_launch": avg_dec_us, **spread(dec_us), "bytes_per_launch": bytes_per_launch,
                         "kernels": "k_decode_tiers + k_decode_finish",
                         "timed_launches": timed, "timed_every_nth_layer": TIME_EVERY,
                         # the same metric over decode-attention kernel time alone
@@ -622,10 +628,10 @@ def main():
         # passes, row statistics then column sums, so they execute twice this)
         L = wl.admit[0][0].shape[2]
         flops = float(wl.hq) * L * (L + 1) * wl.d
-        h2o_ms = sum(e[0].elapsed_time(e[1]) for row in ev_h2o for e in row if e is not None)
-        n_h2o = sum(1 for row in ev_h2o for e in row if e is not None)
-        us = h2o_ms * 1e3 / n_h2o
-        res["h2o_prefill"] = {"avg_us_per_launch": us, "prompt_tokens": L, "kernels": "k_h2o_rowlse + k_h2o_colsum2 + k_h2o_reduce",
+        h2o_us = [e[0].elapsed_time(e[1]) * 1e3 for row in ev_h2o for e in row if e is not None]
+        n_h2o = len(h2o_us)
+        us = sum(h2o_us) / n_h2o
+        res["h2o_prefill"] = {"avg_us_per_launch": us, **spread(h2o_us), "prompt_tokens": L, "kernels": "k_h2o_rowlse + k_h2o_colsum2 + k_h2o_reduce",
                               "flops_per_launch": flops, "bound": "mfma", "achieved": flops / (us * 1e-6) / 1e12,
                               "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                               "frac": flops / (us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, "timed_launches": n_h2o}
