@@ -3,15 +3,20 @@
 // packed middle tier is dequantized inside the attention kernel; one joint
 // softmax over sinks, middle and recent tokens).
 //
-// Work decomposition (one launch per layer):
-//   k_decode_tiers  nsplit x Hkv x batch workgroups, 256 threads. Split 0 streams
-//                   the FP16 tier (sinks + recent ring); split s >= 1 streams
-//                   middle rows [(s-1)*chunk, s*chunk). A workgroup serves
-//                   all n_rep query heads of its KV head, so every packed
-//                   byte is read from HBM once. Each wave takes 64-token
-//                   sub-chunks with one lane per token: the lane loads its
-//                   token's packed K row, K scales, V row and V scales with
-//                   16-byte loads (consecutive lanes read consecutive rows).
+// Work decomposition (one call per layer):
+//   k_decode_tiers  (n_fp + n_mid) x Hkv x batch workgroups, 256 threads, in a
+//                   1-D grid with the middle splits first. The n_fp FP16-tier
+//                   splits (up to 4) stream the sinks and the recent ring; the
+//                   n_mid middle splits cut the live middle rows into equal
+//                   ranges of whole 64-token sub-chunks. A second launch
+//                   streams the INT2 overflow tier when there is one (its
+//                   splits after these in the partials); a PQ middle tier is
+//                   k_decode_pq's (k_pq_tier.hip). A workgroup serves all
+//                   n_rep query heads of its KV head, so every packed byte is
+//                   read from HBM once. Each wave takes 64-token sub-chunks
+//                   with one lane per token: the lane loads its token's packed
+//                   K row, K scales, V row and V scales with 16-byte loads
+//                   (consecutive lanes read consecutive rows).
 //     QK^T  v_mfma_f32_4x4x4_16b_f16: A = four query heads (broadcast from
 //           block 0), B column = the lane's token, k = 4 channels. K codes
 //           are decoded to exact signed fp16 values (code - off) * 2^p with
@@ -20,8 +25,9 @@
 //           scaled by the group scale. (fp16 subnormal operands would save
 //           one op per pair, but this MFMA sums them about 40x less
 //           accurately than fp32, which the per-slot attention cannot take.)
-//     softmax  per head, running max kept wave-uniform; it is rebuilt (and
-//           the accumulators rescaled) only when a sub-chunk exceeds it.
+//     softmax  per head, running max kept wave-uniform; it is raised (and
+//           the accumulators rescaled) only when a score exceeds it by more
+//           than kLazyMax (log2 units).
 //     PV    the same MFMA with blocks = 4-channel column blocks: A = fp16
 //           weights p * v_scale of four tokens (broadcast per 32-channel
 //           group), B = the signed codes of those tokens for the lane's
@@ -29,7 +35,9 @@
 //           [16-bit unit][token] and decoded with the fp16 bias trick.
 //   k_decode_finish   per sequence: log-sum-exp merge of the splits for every
 //                     query head and the side output
-//                     a_j = sum_h 2^(s_hj - M_h) / L_h per slot position.
+//                     a_j = sum_h 2^(s_hj - M_h) / L_h per slot position
+//                     (k_decode_finish_head instead without the side output
+//                     over many splits).
 // Roofline: HBM. Algorithmic bytes per launch = live tier bytes + q + out
 // (+ the side output when requested).
 #include <mutex>

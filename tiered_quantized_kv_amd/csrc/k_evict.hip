@@ -24,11 +24,17 @@
 // of at most kHalo slots, the selection launch first copies the first n_ev
 // rows of each chunk aside (the halo of the chunk before it) and each
 // compaction workgroup writes exactly its own slots, so the second kernel is
-// not needed. Keys of moved rows are
-// dequantized, rotated by R(-delta) from a float64 cos/sin table, rounded to
-// fp16 once and requantized, one lane per rotation pair; values move as
-// packed bytes.
-// Roofline: HBM (bytes of the moved rows read + written).
+// not needed. Keys of moved rows are dequantized, rotated by R(-delta) from a
+// float64 cos/sin table, rounded to fp16 once and requantized, one lane per
+// eight rotation pairs; values move as packed bytes.
+//
+// With an INT2 overflow tier or a PQ middle tier an eviction is a staged tier
+// event instead: k_tier_select picks the demoted and the dropped rows,
+// k_tier_move rebuilds each new row into staging (dequantize or decode,
+// rotate, round, requantize or re-encode) and k_tier_copy writes the staging
+// back.
+// Roofline: HBM (bytes of the moved rows read + written), with the
+// requantization's VALU work as the co-bound (the bound on the serving batch).
 #include "fade_common.hpp"
 #include "fade_internal.hpp"
 
