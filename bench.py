@@ -48,6 +48,9 @@ def parse():
     p.add_argument("--shape-only", default=None, choices=["c4", "s4", "pq"],
                    help="time only decode attention at this shape (pq: a PQ middle tier at the workload's "
                         "shape) on directly filled caches, print its record and exit (for profiling)")
+    p.add_argument("--peaks", action="store_true",
+                   help="measure what library kernels reach on this GPU (a read-only reduction and a device copy "
+                        "over rotating 1 GiB buffers, an fp16 GEMM), print one record and exit")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="run one device copy of this size before timing (HBM counter calibration)")
     return p.parse_args()
@@ -308,6 +311,41 @@ def spread(us):
     return {"p10_us": float(q[0]), "median_us": float(q[1]), "p90_us": float(q[2])}
 
 
+def measure_peaks():
+    """What library kernels reach on this GPU, beside the published peaks the
+    roofline uses: HBM read rate of a sum over 1 GiB fp32 buffers (four in
+    turn, so no call finds the last one's bytes in the last-level cache),
+    copy rate (read + write bytes) of a device copy of the same size, and the
+    fp16 rate of an 8192^3 GEMM (torch.mm, fp32 accumulate)."""
+    import torch
+    n = (1 << 30) // 4
+    bufs = [torch.ones(n, device="cuda") for _ in range(4)]
+    dst = torch.empty(n, device="cuda")
+
+    def timed(fn, reps):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    t_read = timed(lambda i: bufs[i % 4].sum(), 20)
+    t_copy = timed(lambda i: dst.copy_(bufs[i % 4]), 20)
+    del bufs, dst
+    a = torch.randn(8192, 8192, device="cuda", dtype=torch.float16)
+    b = torch.randn(8192, 8192, device="cuda", dtype=torch.float16)
+    t_mm = timed(lambda i: torch.mm(a, b), 10)
+    return {"peaks": {"read_GBps": (1 << 30) / t_read / 1e9, "copy_GBps": 2 * (1 << 30) / t_copy / 1e9,
+                      "fp16_gemm_TFLOPs": 2 * 8192.0 ** 3 / t_mm / 1e12,
+                      "published": {"hbm_GBps": HBM_PEAK_GBS, "fp16_mfma_TFLOPs": MFMA_F16_PEAK_TFLOPS},
+                      "note": "library kernels (torch sum, copy, mm), 1 GiB fp32 buffers, 8192^3 fp16 GEMM"}}
+
+
 def measured_traffic(name):
     """HBM bytes per decode-attention call from the committed counter summary
     of this workload (FETCH_SIZE and WRITE_SIZE passes, copy-calibrated), or
@@ -537,6 +575,9 @@ def main():
     fade.lib()
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if a.peaks:
+        print(json.dumps(measure_peaks()), flush=True)
+        return
     if a.shape_only:
         calls = a.shape_calls if a.shape_calls > 0 else 40
         r = (time_decode_direct(a.workload, calls, pq=True) if a.shape_only == "pq"
