@@ -29,7 +29,9 @@ Shapes are the benchmark workloads' shapes, shrunk in length:
 * serving batch: 8 ragged sequences (some still below the budget, one still
   filling its sinks), 32/8 heads, d 128, K4/V2, EMA 0.9, budget 256 with
   cap_mid = budget + 1 (the one-slot halo compaction the bench runs), 32 steps;
-* Llama-3-8B-like: position policy, W 128, bf16 queries, 16 steps.
+* Llama-3-8B-like: position policy, W 128, bf16 queries, 16 steps;
+* degenerate configurations: no sinks, a recent window of one or two tokens,
+  a middle budget of zero or one row, one-token prefills.
 """
 import numpy as np
 import pytest
@@ -194,3 +196,18 @@ def test_closed_loop_llama3_8b_like_position():
     cfg = _cfg(128, 32, 8, 4, 128, 512, 4, 2, q_dtype="bf16", rope_theta=5e5)
     nf, ne = _run_loop(cfg, [3000], 16, "none", "position", 1, 4400, cap_mid=513, score_kind=None)
     assert nf == 0 and ne == 16
+
+
+# Degenerate configurations the interface admits: no sinks, a one- or
+# two-token recent window, a middle budget of zero or one row, one-token and
+# very short prefills.
+def test_closed_loop_no_sinks_window1_budget0_ema():
+    cfg = _cfg(64, 8, 2, 0, 1, 0, 4, 2, rope_theta=1e4)
+    nf, ne = _run_loop(cfg, [50, 3, 1], 12, "ema", "score", 1, 4500, cap_mid=1, score_kind="ema")
+    assert ne > 0
+
+
+def test_closed_loop_no_sinks_position_budget1():
+    cfg = _cfg(128, 16, 4, 0, 2, 1, 2, 2, rope_theta=1e4)
+    nf, ne = _run_loop(cfg, [40, 2, 1], 12, "none", "position", 1, 4600, cap_mid=2, score_kind=None)
+    assert nf == 0 and ne > 0
