@@ -244,3 +244,12 @@ def test_pq_closed_loop_position():
     cfg = _cfg(d=128, hq=16, hkv=8, w=32, budget=120)
     refs, n = _loop(cfg, [1500], 10, "none", "position", 1, 950, cap_mid=121)
     assert n == 10
+
+
+def test_pq_closed_loop_no_sinks_window1_budget0():
+    """Degenerate configuration: no sinks, a one-token recent window and a
+    middle budget of zero (each demoted row is evicted at the next event);
+    one-token and two-token prefills."""
+    cfg = _cfg(d=64, hq=8, hkv=2, n_sink=0, w=1, budget=0)
+    refs, n = _loop(cfg, [60, 2, 1], 10, "ema", "score", 1, 960, cap_mid=1)
+    assert n > 0 and all(r.mid_len == 0 for r in refs)

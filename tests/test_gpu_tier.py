@@ -225,3 +225,12 @@ def test_tier_closed_loop_interleaved_llama3():
                rope_original_max_position=8192, rope_interleaved=True)
     refs, n = _loop(cfg, [420, 260, 180], 20, "accum", "score", 2, 780, cap_mid=50, cap_low=26, score_kind="ema")
     assert n == 10 * 3 and all(r.low_len == 24 for r in refs)
+
+
+def test_tier_closed_loop_no_sinks_window1_int4_budget0():
+    """Degenerate configuration: no sinks, a one-token recent window, an INT4
+    budget of zero (every event demotes the whole INT4 tier) and an INT2
+    budget of one row; one-token and two-token prefills."""
+    cfg = _cfg(d=64, hq=8, hkv=2, n_sink=0, w=1, b4=0, b2=1, kb=4, vb=2)
+    refs, n = _loop(cfg, [60, 2, 1], 12, "ema", "score", 1, 790, cap_mid=1, cap_low=1, score_kind="ema")
+    assert n > 0 and all(r.low_len == 1 and r.mid_len == 0 for r in refs)
