@@ -31,7 +31,8 @@ Shapes are the benchmark workloads' shapes, shrunk in length:
   cap_mid = budget + 1 (the one-slot halo compaction the bench runs), 32 steps;
 * Llama-3-8B-like: position policy, W 128, bf16 queries, 16 steps;
 * degenerate configurations: no sinks, a recent window of one or two tokens,
-  a middle budget of zero or one row, one-token prefills.
+  a middle budget of zero or one row, one-token prefills; the largest sink
+  count and recent window (64, 1024).
 """
 import numpy as np
 import pytest
@@ -211,3 +212,12 @@ def test_closed_loop_no_sinks_position_budget1():
     cfg = _cfg(128, 16, 4, 0, 2, 1, 2, 2, rope_theta=1e4)
     nf, ne = _run_loop(cfg, [40, 2, 1], 12, "none", "position", 1, 4600, cap_mid=2, score_kind=None)
     assert nf == 0 and ne > 0
+
+
+def test_closed_loop_max_sinks_and_window():
+    """The largest sink count and recent window the interface admits (64 and
+    1024: a 1025-slot ring, several fp16-tier splits and ring-rotation
+    workgroups per sequence)."""
+    cfg = _cfg(128, 32, 8, 64, 1024, 256, 4, 2, rope_theta=5e5)
+    nf, ne = _run_loop(cfg, [1500, 1200], 6, "ema", "score", 1, 4700, cap_mid=257, score_kind="ema")
+    assert ne > 0
