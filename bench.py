@@ -212,6 +212,36 @@ class Workload:
         tokens = sum(F + m for m in self.M)
         return kv + qo + side, tokens
 
+    def moved_bytes(self, kept):
+        """HBM bytes an eviction call moves, from its kept-slot map (old slot of
+        the token at each new slot) and the lengths after it: every moved
+        middle row is read and written (packed K and V codes and scales) for
+        each KV head, every moved recent token's fp16 key is read and written
+        in place, every moved score is read and written, and the selection
+        reads the old middle tier's scores."""
+        w = self.w
+        d, hkv = self.d, self.hkv
+        row = d * w["middle_k_bits"] // 8 + d * w["middle_v_bits"] // 8 + 2 * 2 * (d // 32)
+        total = 0
+        per_row = self.B if self.shared else 1        # a shared row's event moves every sequence's rows
+        for l, tc in enumerate(self.caches):
+            k = kept[l].cpu().numpy()
+            lens = tc.lens.cpu().numpy()
+            for b in range(k.shape[0]):
+                S, M = int(lens[b, 0]), int(lens[b, 1])
+                kb = k[b]
+                live = kb >= 0
+                moved = live & (kb != np.arange(kb.size))
+                if not moved.any():
+                    continue
+                mid = int(moved[S:S + M].sum())
+                ring = int(moved[S + M:].sum())
+                # the first recent token's old slot ends the old middle tier
+                ring_old = kb[S + M:][kb[S + M:] >= 0]
+                m_old = int(ring_old.min()) - S if ring_old.size else M
+                total += per_row * hkv * (2 * mid * row + 2 * ring * 2 * d) + 8 * (mid + ring) + 4 * m_old
+        return total / len(self.caches)
+
     def advance_mirror(self):
         budget = self.w["int4_budget"]
         self.step_idx += 1
@@ -230,7 +260,7 @@ class Workload:
         self.admit_stream = self.torch.cuda.Stream(device=self.dev) if (on and self.admit is not None) else None
 
     # ---- one step --------------------------------------------------------------
-    def step(self, events=None, h2o_events=None):
+    def step(self, events=None, h2o_events=None, evict_events=None, kept=None):
         fade = self.fade
         t = self.step_idx
         due = self.w["int4_budget"] >= 0 and ((t + 1) % self.period == 0)
@@ -254,7 +284,11 @@ class Workload:
                 fade.fade_h2o_scores(self.cfg, fade.SCORE_EMA, cache=tc, tok_attn=self.tok, decay=self.w["ema_decay"])
             fade.fade_cache_demote(self.cfg, tc)
             if due:
-                fade.fade_evict_rerope(self.cfg, tc, pol, self.ws_ev)
+                if evict_events is not None and evict_events[l] is not None:
+                    evict_events[l][0].record()
+                fade.fade_evict_rerope(self.cfg, tc, pol, self.ws_ev, kept_slots=None if kept is None else kept[l])
+                if evict_events is not None and evict_events[l] is not None:
+                    evict_events[l][1].record()
             if self.admit is not None:
                 qa, ka = self.admit[l]
                 with torch.cuda.stream(self.admit_stream if self.admit_stream is not None else main):
@@ -283,11 +317,13 @@ class TimingEvent:
         if TimingEvent._hip is None:
             TimingEvent._hip = ctypes.CDLL("libamdhip64.so.7")
         self.ev = ctypes.c_void_p()
+        self.recorded = False
         rc = self._hip.hipEventCreateWithFlags(ctypes.byref(self.ev), ctypes.c_uint(self.kDisableSystemFence))
         if rc != 0:
             raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
 
     def record(self):
+        self.recorded = True
         import torch
         rc = self._hip.hipEventRecord(self.ev, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
         if rc != 0:
@@ -611,6 +647,9 @@ def main():
     # the admitted sequence's H2O prefill column sums, on the layers in between
     ev_h2o = [[(TimingEvent(), TimingEvent()) if wl.admit is not None and l % TIME_EVERY == 2 else None
                for l in range(wl.layers)] for _ in range(steps)]
+    # the eviction call (selection + compaction), on the layers after the decode ones
+    ev_evict = [[(TimingEvent(), TimingEvent()) if l % TIME_EVERY == 1 else None for l in range(wl.layers)]
+                for _ in range(steps)]
     dec_bytes, dec_tokens = 0, 0
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -621,7 +660,7 @@ def main():
         nb, nt = wl.decode_bytes_and_tokens()
         dec_bytes += nb * wl.layers
         dec_tokens += nt * wl.layers
-        wl.step(events=ev[s], h2o_events=ev_h2o[s])
+        wl.step(events=ev[s], h2o_events=ev_h2o[s], evict_events=ev_evict[s])
         wl.advance_mirror()
     t_end.record()
     torch.cuda.synchronize()
@@ -676,6 +715,25 @@ def main():
                               "flops_per_launch": flops, "bound": "mfma", "achieved": flops / (us * 1e-6) / 1e12,
                               "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                               "frac": flops / (us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, "timed_launches": n_h2o}
+    evict_us = [e[0].elapsed_time(e[1]) * 1e3 for row in ev_evict for e in row if e is not None and e[0].recorded]
+    if evict_us and wl.w["int4_budget"] >= 0:
+        # bytes moved per eviction call, from one more (untimed) step that
+        # returns every layer's kept-slot map
+        import torch
+        kept = [torch.full((wl.caches[0].lens.shape[0] if not wl.shared else 1, wl.caches[0].cap_T), -7,
+                           dtype=torch.int32, device=dev) for _ in range(wl.layers)]
+        if (wl.step_idx + 1) % wl.period == 0:
+            wl.step(kept=kept)
+            torch.cuda.synchronize()
+            mb = wl.moved_bytes(kept)
+            wl.advance_mirror()
+            eus = sum(evict_us) / len(evict_us)
+            res["evict_rerope"] = {"avg_us_per_launch": eus, **spread(evict_us), "kernels": "k_select + k_compact",
+                                   "moved_bytes_per_launch": mb, "bound": "valu",
+                                   "hbm_achieved_GBps": mb / (eus * 1e-6) / 1e9,
+                                   "hbm_frac": mb / (eus * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                                   "note": "moved bytes from one extra untimed step's kept-slot maps; "
+                                           "VALU-bound by the float64 re-rotation and requantization"}
     if wl.admit is not None and a.overlap_steps > 0:
         # The same steps with the admitted sequence's prefill pass overlapped
         # with the decode step on a second stream: whole-step throughput as a
