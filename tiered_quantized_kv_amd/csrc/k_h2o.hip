@@ -392,7 +392,7 @@ __global__ __launch_bounds__(256) void k_h2o_colsum2(const uint16_t* __restrict_
       for (int j = 0; j < kColItems; ++j) {
         const int it = st * kColItems + j;
         if (it >= n_items) break;                              // workgroup-uniform
-        const int rt = (qt_lo + it / n_rep) * 16;
+        const int rt = (qt_lo + (it >> lg)) * 16;
         if (rt + 15 < kw0) continue;                           // wave-uniform: rows before every key
         f16x8 af[KB];
 #pragma unroll
