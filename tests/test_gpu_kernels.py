@@ -126,10 +126,13 @@ def test_rope_rotate_matches_oracle(d, theta, rtype, dtype):
     assert np.array_equal(got, want_t)
 
 
+# The last two cases reach the row pass's two-tile form ((L / 32) x Hkv x batch
+# at least 1024, n_rep <= 4) with a ragged L.
 @pytest.mark.parametrize("d,hq,hkv,L,batch,shared", [(128, 16, 2, 300, 1, False), (64, 32, 8, 200, 2, True),
                                                      (64, 8, 8, 129, 1, False), (128, 8, 1, 64, 1, False),
                                                      (128, 32, 8, 2048, 1, False), (128, 64, 8, 1201, 2, True),
-                                                     (64, 16, 8, 1027, 3, False)])
+                                                     (64, 16, 8, 1027, 3, False), (64, 16, 4, 2000, 5, False),
+                                                     (128, 16, 8, 1030, 4, True)])
 def test_h2o_prefill_colsum(d, hq, hkv, L, batch, shared):
     cfg = _cfg(d, hq, hkv)
     gen = synth.rng(104, d, L)

@@ -98,7 +98,11 @@ __global__ __launch_bounds__(256) void k_h2o_rowlse(const uint16_t* __restrict__
                                                     int L, int batch, float scale, float* __restrict__ lse) {
   constexpr int KB = D / 32;
   constexpr int CPT = kTile * (D / 8) / 256;    // 16-byte chunks per thread per tile
-  __shared__ __align__(16) uint16_t ktile[3][kTile * D];   // swizzled rows (swz)
+  // Key tiles in flight: three buffers for one row tile; two for two row
+  // tiles, whose register budget then allows four waves per SIMD (125
+  // VGPRs) and four workgroups per CU (32 KB each).
+  constexpr int NBUF = RT == 2 ? 2 : 3;
+  __shared__ __align__(16) uint16_t ktile[NBUF][kTile * D];   // swizzled rows (swz)
   // 1-D grid, XCD aware: id % 8 picks the XCD, and each XCD walks the row
   // blocks (RT 16-row tiles) of one (row, KV group) at a time, longest rows
   // (most key tiles) first, so that group's keys stay in that XCD's L2.
@@ -115,8 +119,9 @@ __global__ __launch_bounds__(256) void k_h2o_rowlse(const uint16_t* __restrict__
   const uint16_t* kb_ = k + ((size_t)(b * Hkv + g) * L) * D;
   const int n_kt = min(r0 + 16 * RT - 1, L - 1) / kTile + 1;
 
-  // Key tiles are triple buffered: tile kt + 2 is loaded into registers while
-  // tile kt is used, and stored to LDS after it.
+  // Key tiles rotate through NBUF LDS buffers: tile kt + NBUF is loaded into
+  // registers while tile kt is used, and tile kt + NBUF - 1 (loaded during
+  // the previous tile) is stored to LDS after it.
   // Thread tid copies the 16-byte chunk tid % (D / 8) of tile rows
   // tid / (D / 8) + RSTEP * c: fixed offsets from a workgroup-uniform tile base
   // (RSTEP is a multiple of D / 8, so the rows' swizzle does not depend on c).
@@ -170,17 +175,17 @@ __global__ __launch_bounds__(256) void k_h2o_rowlse(const uint16_t* __restrict__
         l_l[t][j][i] = 0.f;
       }
     }
-  if (n_kt > 1) lstore(1, pre);
+  if (NBUF == 3 && n_kt > 1) lstore(1, pre);
 #pragma unroll
   for (int t = 0; t < RT; ++t)
 #pragma unroll
     for (int j = 0; j < HPW; ++j)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) settle(afrag[t][j][kb]);
-  if (n_kt > 2) gload(2, pre);
+  if (NBUF == 3 && n_kt > 2) gload(2, pre);
   __syncthreads();
   for (int kt = 0; kt < n_kt; ++kt) {
-    const uint16_t* kt_lds = ktile[kt % 3];
+    const uint16_t* kt_lds = ktile[kt % NBUF];
 #pragma unroll
     for (int j = 0; j < HPW; ++j) {
       if (wave + 4 * j >= n_rep) continue;      // wave-uniform
@@ -238,10 +243,10 @@ __global__ __launch_bounds__(256) void k_h2o_rowlse(const uint16_t* __restrict__
         }
       }
     }
-    // buffer (kt + 2) % 3 was last read in iteration kt - 1, before the
-    // barrier that ended it
-    if (kt + 2 < n_kt) lstore((kt + 2) % 3, pre);
-    if (kt + 3 < n_kt) gload(kt + 3, pre);
+    // buffer (kt + NBUF - 1) % NBUF was last read in iteration kt - 1, before
+    // the barrier that ended it
+    if (kt + NBUF - 1 < n_kt) lstore((kt + NBUF - 1) % NBUF, pre);
+    if (kt + NBUF < n_kt) gload(kt + NBUF, pre);
     __syncthreads();
   }
   // merge the 16 lanes of each row: LSE = M + log2(sum_lanes l * 2^(m - M))
