@@ -449,6 +449,41 @@ __device__ __forceinline__ void dequant8(uint32_t w, float sc, float* x) {
   }
 }
 
+// The rebuild loops' rounding and packing, written so that each step is one
+// instruction: the compiler forms min(x, 1) as a compare and a select, and a
+// sum of shifted fields as separate shifts and three-operand adds. Plain VALU
+// instructions with no memory operand; this file issues no MFMA.
+// d2f_odd_h with its sticky bit from one v_min_u32: the same bits.
+__device__ __forceinline__ float d2f_odd_h1(double d) {
+  const uint64_t u = (uint64_t)__double_as_longlong(d);
+  uint32_t st;
+  asm("v_min_u32_e32 %0, 1, %1" : "=v"(st) : "v"((uint32_t)u & 0x1FFFFFFFu));
+  const float f = (float)__longlong_as_double((long long)(u & ~(uint64_t)0x1FFFFFFFu));
+  return __uint_as_float(__float_as_uint(f) | st);
+}
+// (a << S) + b in one v_lshl_add_u32
+template <int S>
+__device__ __forceinline__ uint32_t lshl_add(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_lshl_add_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "n"(S), "v"(b));
+  return r;
+}
+// The packed word of N fields of BITS from quant_field values q[k] (field k at
+// bit BITS * k), the fields' base bits removed.
+template <int BITS, int N>
+__device__ __forceinline__ uint32_t pack_fields(const uint32_t (&q)[N]) {
+  uint32_t o = q[0] - field_bias<BITS, N>();
+  if constexpr (N > 1) o = lshl_add<BITS * 1>(q[1], o);
+  if constexpr (N > 2) o = lshl_add<BITS * 2>(q[2], o);
+  if constexpr (N > 3) o = lshl_add<BITS * 3>(q[3], o);
+  if constexpr (N > 4) o = lshl_add<BITS * 4>(q[4], o);
+  if constexpr (N > 5) o = lshl_add<BITS * 5>(q[5], o);
+  if constexpr (N > 6) o = lshl_add<BITS * 6>(q[6], o);
+  if constexpr (N > 7) o = lshl_add<BITS * 7>(q[7], o);
+  static_assert(N <= 8, "at most 8 fields");
+  return o;
+}
+
 // Rotation of a key pair by the float64 (cos, sin) of a shift, rounded once
 // to fp16: y1 = x1 cos - x2 sin, y2 = x2 cos + x1 sin.
 __device__ __forceinline__ void rotate_pair(float x1, float x2, double c, double sn, uint16_t& h1,
@@ -701,8 +736,8 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
 #pragma unroll
       for (int k = 0; k < PPL; ++k) {
         const double a1 = (double)x1[k], a2 = (double)x2[k];
-        const float f1 = d2f_odd_h(a1 * csl[k].x - a2 * csl[k].y);
-        const float f2 = d2f_odd_h(a2 * csl[k].x + a1 * csl[k].y);
+        const float f1 = d2f_odd_h1(a1 * csl[k].x - a2 * csl[k].y);
+        const float f2 = d2f_odd_h1(a2 * csl[k].x + a1 * csl[k].y);
         z1[k] = (f16)f1;
         z2[k] = (f16)f2;
         // fp16 rounding is monotonic: the group amax of the rounded values is
@@ -718,12 +753,13 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
       const uint16_t sb1 = group_scale_bits<KB>(h2f(f2h(am1)));
       const uint16_t sb2 = group_scale_bits<KB>(h2f(f2h(am2)));
       const float r1 = quant_recip(h2f(sb1)), r2 = quant_recip(h2f(sb2));
-      uint32_t o1 = 0u - field_bias<KB, PPL>(), o2 = o1;
+      uint32_t q1[PPL], q2[PPL];
 #pragma unroll
       for (int k = 0; k < PPL; ++k) {
-        o1 += quant_field<KB>((float)z1[k], r1) << (KB * k);
-        o2 += quant_field<KB>((float)z2[k], r2) << (KB * k);
+        q1[k] = quant_field<KB>((float)z1[k], r1);
+        q2[k] = quant_field<KB>((float)z2[k], r2);
       }
+      const uint32_t o1 = pack_fields<KB>(q1), o2 = pack_fields<KB>(q2);
       if (moved) {
         uint8_t* kw = reinterpret_cast<uint8_t*>(s_kc) + t * KROW;
         if constexpr (CW == 4) {
@@ -778,8 +814,8 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
 #pragma unroll
       for (int k = 0; k < PPL; ++k) {
         const double a1 = (double)x[2 * k], a2 = (double)x[2 * k + 1];
-        const float f1 = d2f_odd_h(a1 * csl[k].x - a2 * csl[k].y);
-        const float f2 = d2f_odd_h(a2 * csl[k].x + a1 * csl[k].y);
+        const float f1 = d2f_odd_h1(a1 * csl[k].x - a2 * csl[k].y);
+        const float f2 = d2f_odd_h1(a2 * csl[k].x + a1 * csl[k].y);
         z[2 * k] = (f16)f1;
         z[2 * k + 1] = (f16)f2;
         am = fmaxf(am, fmaxf(fabsf(f1), fabsf(f2)));
@@ -787,12 +823,13 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
       am = fmaxf(am, dpp_f<kQuadXor1>(am));
       const uint16_t sb = group_scale_bits<KB>(h2f(f2h(am)));
       const float r = quant_recip(h2f(sb));
-      uint32_t o1 = 0u - field_bias<KB, PPL>(), o2 = o1;
+      uint32_t q1[PPL], q2[PPL];
 #pragma unroll
       for (int k = 0; k < PPL; ++k) {
-        o1 += quant_field<KB>((float)z[k], r) << (KB * k);
-        o2 += quant_field<KB>((float)z[PPL + k], r) << (KB * k);
+        q1[k] = quant_field<KB>((float)z[k], r);
+        q2[k] = quant_field<KB>((float)z[PPL + k], r);
       }
+      const uint32_t o1 = pack_fields<KB>(q1), o2 = pack_fields<KB>(q2);
       if (moved) {
         uint8_t* kw = reinterpret_cast<uint8_t*>(s_kc) + t * KROW + 2 * CW * m;
         if constexpr (CW == 4) {
