@@ -289,9 +289,11 @@ static void colsum2_split(int n_rep, int Hkv, int batch, int L, int& n_chunks, i
   const int n_qt = (L + 15) / 16;
   const long kb = (L + kKeyBlock - 1) / kKeyBlock;
   const long base = kb * Hkv * batch;
-  // about 2048 workgroups (half of them past the causal range), at least two
-  // stages each
+  // about 2048 workgroups (half of them past the causal range), but chunks of
+  // at most 8 query tiles (half a key block) unless that takes the grid past
+  // about 16384 workgroups, and at least two stages each
   int per = (int)((long)n_qt * base / 2048);
+  per = min(per, max(8, (int)((long)n_qt * base / 16384)));
   per = max(per, (2 * kColItems + n_rep - 1) / n_rep);
   per = max(1, min(per, n_qt));
   qt_per = per;
