@@ -596,8 +596,10 @@ def time_pq_attention(wl, calls):
     code_bytes = B * hkv * n * 2 * fade.PQ_SUB
     return {"avg_us_per_launch": us, "calls": calls, "batch": B, "tokens": n, "kernels": "k_pq_attn (+ k_pq_attn_merge with token splits)",
             "code_bytes_per_launch": code_bytes, "achieved_GBps": code_bytes / us / 1e3, "bound": "lds",
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": code_bytes / us / 1e3 / HBM_PEAK_GBS,
             "note": "attention over PQ-coded keys and values (2 bits per element), middle-tier size; "
-                    "synthetic codes"}
+                    "synthetic codes; frac = code bytes read over the HBM peak, the kernel itself is bound "
+                    "by its LDS table reads and centroid gathers"}
 
 
 def main():
