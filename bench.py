@@ -278,11 +278,13 @@ class Workload:
             fade.fade_tiered_decode_attn(self.cfg, tc, q, self.out, self.tok, self.ws_dec)
             if events is not None and events[l] is not None:
                 events[l][1].record()
+            # score update (ACCUM / EMA) and demotion: one launch
             if self.policy == "h2o":
-                fade.fade_h2o_scores(self.cfg, fade.SCORE_ACCUM, cache=tc, tok_attn=self.tok)
+                fade.fade_score_update_demote(self.cfg, tc, fade.SCORE_ACCUM, self.tok)
             elif self.policy == "ema":
-                fade.fade_h2o_scores(self.cfg, fade.SCORE_EMA, cache=tc, tok_attn=self.tok, decay=self.w["ema_decay"])
-            fade.fade_cache_demote(self.cfg, tc)
+                fade.fade_score_update_demote(self.cfg, tc, fade.SCORE_EMA, self.tok, self.w["ema_decay"])
+            else:
+                fade.fade_cache_demote(self.cfg, tc)
             if due:
                 if evict_events is not None and evict_events[l] is not None:
                     evict_events[l][0].record()

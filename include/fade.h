@@ -332,6 +332,23 @@ int fade_h2o_scores(const fade_config* cfg, int32_t mode, fade_layer_cache* cach
                     void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * The two steps of a decode step that follow attention, in one launch: the
+ * ACCUM / EMA score update of fade_h2o_scores (mode FADE_SCORE_ACCUM or
+ * FADE_SCORE_EMA, tok_attn and decay as there; Transformer series (25),
+ * 1.3.1 H2O; FADE post, "EMA策略"), then fade_cache_demote (FADE post,
+ * "核心机制"). The cache ends in the same state, bit for bit, as after
+ * those two calls in that order: demotion keeps every slot's position and
+ * the live length, so it does not touch the scores the update reads.
+ * cache->scores and tok_attn (f32 [batch, cap_T], 4-byte aligned) are
+ * required. Errors as the two calls: FADE_ERR_INVALID_ARG for another mode,
+ * a missing scores row or side output, or decay outside [0, 1] (EMA); the
+ * cache checks of fade_cache_demote. A PQ middle tier runs the two steps as
+ * two launches. No workspace; nothing is allocated.
+ */
+int fade_score_update_demote(const fade_config* cfg, fade_layer_cache* cache, int32_t mode,
+                             const float* tok_attn, float decay, void* stream);
+
+/*
  * Eviction event with un-RoPE / re-RoPE compaction (FADE post, sections
  * "驱逐策略" and "RoPE重计算"; Transformer series (25), 1.2.2 StreamingLLM
  * for in-cache positions). For every sequence (or once for a shared cache)

@@ -218,6 +218,29 @@ def test_validation_rejects_before_launch():
     assert st == fade.FADE_ERR_WORKSPACE
 
 
+def test_score_update_demote_validation():
+    """fade_score_update_demote rejects what fade_h2o_scores (ACCUM / EMA) and
+    fade_cache_demote reject, before any launch."""
+    lib = fade.lib()
+    cfg = _cfg()
+    null = ctypes.c_void_p(0)
+    good = ctypes.c_void_p(16)
+    call = lambda c, mode, tok, decay: lib.fade_score_update_demote(ctypes.byref(cfg), ctypes.byref(c), mode, tok,
+                                                                    ctypes.c_float(decay), null)
+    with_scores = fade.LayerCache(1, 4096, 4 + 4096 + 65, 0, 16, 16, 16, 16, 16, 16, 16, 16)
+    no_scores = fade.LayerCache(1, 4096, 4 + 4096 + 65, 0, 16, 16, 16, 16, 16, 16, 16, None)
+    assert call(with_scores, fade.SCORE_PREFILL, good, 0.0) == fade.FADE_ERR_INVALID_ARG    # prefill is not a decode mode
+    assert call(with_scores, 7, good, 0.0) == fade.FADE_ERR_INVALID_ARG
+    assert call(no_scores, fade.SCORE_ACCUM, good, 0.0) == fade.FADE_ERR_INVALID_ARG        # no score row
+    assert call(with_scores, fade.SCORE_ACCUM, null, 0.0) == fade.FADE_ERR_INVALID_ARG      # no side output
+    assert call(with_scores, fade.SCORE_ACCUM, ctypes.c_void_p(18), 0.0) == fade.FADE_ERR_INVALID_ARG   # misaligned
+    for decay in (-0.1, 1.5, float("nan")):
+        assert call(with_scores, fade.SCORE_EMA, good, decay) == fade.FADE_ERR_INVALID_ARG
+    # the cache checks of fade_cache_demote: a wrong cap_T
+    bad = fade.LayerCache(1, 10, 999, 0, 16, 16, 16, 16, 16, 16, 16, 16)
+    assert call(bad, fade.SCORE_ACCUM, good, 0.0) == fade.FADE_ERR_INVALID_ARG
+
+
 def test_rope_scheme_validation():
     """Each RoPE scheme's parameters are checked on the host, before any launch
     (a zero-row rotation is a no-op once the configuration is valid)."""

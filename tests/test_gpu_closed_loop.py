@@ -100,7 +100,11 @@ def _build(cfg, lengths, seed, cap_mid, score_kind, shared):
     return tc, refs
 
 
-def _run_loop(cfg, lengths, steps, mode, policy, period, seed, cap_mid, score_kind, shared=False, decay=0.9):
+def _run_loop(cfg, lengths, steps, mode, policy, period, seed, cap_mid, score_kind, shared=False, decay=0.9,
+              fused=False, trace=None):
+    """fused: the score update and demotion as one fade_score_update_demote
+    call; trace: a list that receives every sequence's raw GPU state after
+    every step."""
     tc, refs = _build(cfg, lengths, seed, cap_mid, score_kind, shared)
     for b, r in enumerate(refs):
         assert_state_equal(seq_state(tc, b), r, check_scores=False)
@@ -130,10 +134,13 @@ def _run_loop(cfg, lengths, steps, mode, policy, period, seed, cap_mid, score_ki
         out = torch.zeros(B, hq, d, dtype=torch.float32, device=DEV)
         tok = torch.full((B, tc.cap_T), -1.0, dtype=torch.float32, device=DEV) if side else None
         fade.fade_tiered_decode_attn(cfg, tc, qt.to(DEV), out, tok, ws_dec)
-        if side:
-            fade.fade_h2o_scores(cfg, fade.SCORE_ACCUM if mode == "accum" else fade.SCORE_EMA, cache=tc,
-                                 tok_attn=tok, decay=decay)
-        fade.fade_cache_demote(cfg, tc)
+        smode = fade.SCORE_ACCUM if mode == "accum" else fade.SCORE_EMA
+        if side and fused:
+            fade.fade_score_update_demote(cfg, tc, smode, tok, decay)
+        else:
+            if side:
+                fade.fade_h2o_scores(cfg, smode, cache=tc, tok_attn=tok, decay=decay)
+            fade.fade_cache_demote(cfg, tc)
         evict_now = (step + 1) % period == 0
         if evict_now:
             fade.fade_evict_rerope(cfg, tc, fade.POLICY_POSITION if policy == "position" else fade.POLICY_SCORE,
@@ -164,6 +171,8 @@ def _run_loop(cfg, lengths, steps, mode, policy, period, seed, cap_mid, score_ki
                 n_forced += forced
                 n_events += mc is not None or rc is not None
                 choices[b] = (mc, rc)
+        if trace is not None:
+            trace.append([seq_state(tc, b) for b in range(B)])
         for b, r in enumerate(refs):
             st = seq_state(tc, b)
             adopt_rerope(st, r, *choices[b])
@@ -221,3 +230,39 @@ def test_closed_loop_max_sinks_and_window():
     cfg = _cfg(128, 32, 8, 64, 1024, 256, 4, 2, rope_theta=5e5)
     nf, ne = _run_loop(cfg, [1500, 1200], 6, "ema", "score", 1, 4700, cap_mid=257, score_kind="ema")
     assert ne > 0
+
+
+# The score update and demotion fused into one launch (fade_score_update_demote)
+# must leave exactly the state of the two calls: the loops below run it against
+# the oracle at the same bars, and the last one compares it with the two calls
+# bit for bit after every step.
+def test_closed_loop_serving_batch_ema_fused():
+    cfg = _cfg(128, 32, 8, 4, 64, 256, 4, 2, rope_theta=5e5)
+    lengths = [1500, 300, 900, 2, 325, 700, 1100, 333]
+    nf, ne = _run_loop(cfg, lengths, 16, "ema", "score", 1, 4310, cap_mid=257, score_kind="ema", fused=True)
+    assert ne > 0
+
+
+def test_closed_loop_llama32_like_shared_fused():
+    cfg = _cfg(64, 32, 8, 4, 64, 128, 4, 4, rope_type="llama3", rope_theta=5e5, rope_factor=32.0,
+               rope_low_freq_factor=1.0, rope_high_freq_factor=4.0, rope_original_max_position=8192)
+    nf, ne = _run_loop(cfg, [700] * 4, 17, "accum", "score", 16, 4210, cap_mid=128 + 16, score_kind="h2o",
+                       shared=True, fused=True)
+    assert ne >= 4
+
+
+@pytest.mark.parametrize("mode,shared", [("ema", False), ("accum", True)])
+def test_fused_score_update_demote_equals_two_calls(mode, shared):
+    cfg = _cfg(128, 16, 4, 4, 16, 64, 4, 2, rope_theta=5e5)
+    lengths = [400] * 3 if shared else [400, 90, 3]
+    kw = dict(steps=12, mode=mode, policy="score", period=3, seed=4320, cap_mid=64 + 3, score_kind="ema",
+              shared=shared)
+    t_sep, t_fus = [], []
+    _run_loop(cfg, lengths, trace=t_sep, **kw)
+    _run_loop(cfg, lengths, fused=True, trace=t_fus, **kw)
+    assert len(t_sep) == len(t_fus) == 12
+    for step, (a, b) in enumerate(zip(t_sep, t_fus)):
+        for q, (sa, sb) in enumerate(zip(a, b)):
+            assert sa.keys() == sb.keys()
+            for key in sa:
+                assert np.array_equal(np.asarray(sa[key]), np.asarray(sb[key])), (step, q, key)

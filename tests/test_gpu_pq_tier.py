@@ -164,7 +164,7 @@ def _follow(r, kept_row, policy):
     oc.evict(r, c.int4_budget, policy, evicted=forced)
 
 
-def _loop(cfg, lengths, steps, mode, policy, period, seed, cap_mid):
+def _loop(cfg, lengths, steps, mode, policy, period, seed, cap_mid, fused=False):
     cb = _codebooks(cfg, seed + 7)
     tc, refs = _ragged(cfg, lengths, cap_mid, seed, cb, score_kind=None if policy == "position" else "ema")
     for b, r in enumerate(refs):
@@ -191,10 +191,13 @@ def _loop(cfg, lengths, steps, mode, policy, period, seed, cap_mid):
         out = torch.zeros(B, hq, d, dtype=torch.float32, device=DEV)
         tok = torch.full((B, tc.cap_T), -1.0, dtype=torch.float32, device=DEV) if side else None
         fade.fade_tiered_decode_attn(cfg, tc, dev16(q), out, tok, ws_dec)
-        if side:
-            fade.fade_h2o_scores(cfg, fade.SCORE_ACCUM if mode == "accum" else fade.SCORE_EMA, cache=tc,
-                                 tok_attn=tok, decay=0.9)
-        fade.fade_cache_demote(cfg, tc)
+        smode = fade.SCORE_ACCUM if mode == "accum" else fade.SCORE_EMA
+        if side and fused:                       # one call: update, then demote
+            fade.fade_score_update_demote(cfg, tc, smode, tok, 0.9)
+        else:
+            if side:
+                fade.fade_h2o_scores(cfg, smode, cache=tc, tok_attn=tok, decay=0.9)
+            fade.fade_cache_demote(cfg, tc)
         evict_now = (step + 1) % period == 0
         if evict_now:
             fade.fade_evict_rerope(cfg, tc, fade.POLICY_POSITION if policy == "position" else fade.POLICY_SCORE,
@@ -253,3 +256,11 @@ def test_pq_closed_loop_no_sinks_window1_budget0():
     cfg = _cfg(d=64, hq=8, hkv=2, n_sink=0, w=1, budget=0)
     refs, n = _loop(cfg, [60, 2, 1], 10, "ema", "score", 1, 960, cap_mid=1)
     assert n > 0 and all(r.mid_len == 0 for r in refs)
+
+
+def test_pq_closed_loop_ema_fused():
+    """fade_score_update_demote on a PQ middle tier (two launches inside the
+    call) against the oracle."""
+    cfg = _cfg(d=128, hq=32, hkv=8, w=16, budget=96)
+    refs, n = _loop(cfg, [500, 150, 90, 260], 8, "ema", "score", 1, 931, cap_mid=97, fused=True)
+    assert n == 8 * 4

@@ -104,7 +104,7 @@ def test_tier_decode_attention_ragged():
         assert np.all(side[b, t1:] == 0)
 
 
-def _loop(cfg, lengths, steps, mode, policy, period, seed, cap_mid, cap_low, score_kind, shared=False):
+def _loop(cfg, lengths, steps, mode, policy, period, seed, cap_mid, cap_low, score_kind, shared=False, fused=False):
     oc_cfg = ocfg(cfg)
     f, il = oc_cfg.freqs(), oc_cfg.rope_interleaved
     B, hq, hkv, d = len(lengths), cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
@@ -154,10 +154,13 @@ def _loop(cfg, lengths, steps, mode, policy, period, seed, cap_mid, cap_low, sco
         out = torch.zeros(B, hq, d, dtype=torch.float32, device=DEV)
         tok = torch.full((B, tc.cap_T), -1.0, dtype=torch.float32, device=DEV) if side else None
         fade.fade_tiered_decode_attn(cfg, tc, dev16(q), out, tok, ws_dec)
-        if side:
-            fade.fade_h2o_scores(cfg, fade.SCORE_ACCUM if mode == "accum" else fade.SCORE_EMA, cache=tc,
-                                 tok_attn=tok, decay=0.9)
-        fade.fade_cache_demote(cfg, tc)
+        smode = fade.SCORE_ACCUM if mode == "accum" else fade.SCORE_EMA
+        if side and fused:                       # one call: update, then demote
+            fade.fade_score_update_demote(cfg, tc, smode, tok, 0.9)
+        else:
+            if side:
+                fade.fade_h2o_scores(cfg, smode, cache=tc, tok_attn=tok, decay=0.9)
+            fade.fade_cache_demote(cfg, tc)
         evict_now = (step + 1) % period == 0
         if evict_now:
             fade.fade_evict_rerope(cfg, tc, fade.POLICY_POSITION if policy == "position" else fade.POLICY_SCORE,
@@ -234,3 +237,13 @@ def test_tier_closed_loop_no_sinks_window1_int4_budget0():
     cfg = _cfg(d=64, hq=8, hkv=2, n_sink=0, w=1, b4=0, b2=1, kb=4, vb=2)
     refs, n = _loop(cfg, [60, 2, 1], 12, "ema", "score", 1, 790, cap_mid=1, cap_low=1, score_kind="ema")
     assert n > 0 and all(r.low_len == 1 and r.mid_len == 0 for r in refs)
+
+
+def test_tier_closed_loop_ema_every_step_fused():
+    """The score update and demotion as one fade_score_update_demote call,
+    against the oracle at the same bars (the INT2 overflow tier's live length
+    counts in the score row)."""
+    cfg = _cfg(d=128, hq=32, hkv=8, w=16, b4=64, b2=32)
+    refs, n = _loop(cfg, [600, 140, 97, 300], 12, "ema", "score", 1, 741, cap_mid=65, cap_low=33, score_kind="ema",
+                    fused=True)
+    assert n == 12 * 4

@@ -284,6 +284,24 @@ int fade_h2o_scores(const fade_config* cfg, int32_t mode, fade_layer_cache* cach
   return hip_status(launch_score_update(s, *cache, mode, tok_attn, decay, hs));
 }
 
+int fade_score_update_demote(const fade_config* cfg, fade_layer_cache* cache, int32_t mode, const float* tok_attn,
+                             float decay, void* stream) {
+  int st = check_cfg(cfg);
+  if (st) return st;
+  if (mode != FADE_SCORE_ACCUM && mode != FADE_SCORE_EMA) return FADE_ERR_INVALID_ARG;
+  if ((st = check_cache(cfg, cache))) return st;
+  if (!cache->scores || !tok_attn || !aligned(tok_attn, 4)) return FADE_ERR_INVALID_ARG;
+  if (mode == FADE_SCORE_EMA && !(decay >= 0.f && decay <= 1.f)) return FADE_ERR_INVALID_ARG;
+  const Shape s = cache_shape(cfg, cache);
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (s.pq) {
+    hipError_t e = launch_score_update(s, *cache, mode, tok_attn, decay, hs);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(launch_demote_pq(s, *cache, hs));
+  }
+  return hip_status(launch_score_update_demote(s, *cache, mode, tok_attn, decay, hs));
+}
+
 int fade_evict_rerope(const fade_config* cfg, fade_layer_cache* cache, int32_t policy, int32_t max_evict,
                       int32_t* kept_slots_out, void* workspace, size_t ws_bytes, void* stream) {
   int st = check_cfg(cfg);

@@ -39,6 +39,19 @@ hipError_t launch_quantize_rows(int D, int bits, const uint16_t* src, int64_t n_
 hipError_t launch_append(const Shape& s, const fade_layer_cache& c, const uint16_t* k_new,
                          const uint16_t* v_new, hipStream_t st);
 hipError_t launch_demote(const Shape& s, const fade_layer_cache& c, hipStream_t st);
+// the decode-time score update followed by demotion, one launch (INT4 / INT2
+// middle tiers)
+hipError_t launch_score_update_demote(const Shape& s, const fade_layer_cache& c, int mode,
+                                      const float* tok_attn, float decay, hipStream_t st);
+
+// One slot's decode-time score update (Transformer series (25), 1.3.1 H2O:
+// the accumulated attention; FADE post, "EMA策略": s = beta s + (1 - beta) a).
+// Shared by the score-update kernels, with the EMA's one fused multiply-add
+// written out: left to contraction, the compiler may fuse either product
+// depending on the surrounding code, and two kernels would round differently.
+__device__ __forceinline__ float score_update_value(float s, float a, int mode, float decay) {
+  return mode == FADE_SCORE_ACCUM ? s + a : __builtin_fmaf(decay, s, (1.f - decay) * a);
+}
 
 // ---- decode attention (k_decode.hip) ---------------------------------------
 int decode_chunk(const Shape& s);                 // middle rows per split

@@ -1093,8 +1093,7 @@ __global__ __launch_bounds__(256) void k_score_update(float* __restrict__ scores
     a = tok_attn[(size_t)row * cap_T + j];
   }
   float* s = scores + (size_t)row * cap_T + j;
-  if (mode == FADE_SCORE_ACCUM) *s = *s + a;
-  else *s = decay * *s + (1.f - decay) * a;
+  *s = score_update_value(*s, a, mode, decay);
 }
 
 hipError_t launch_score_update(const Shape& s, const fade_layer_cache& c, int mode,

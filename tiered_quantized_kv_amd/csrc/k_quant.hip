@@ -132,11 +132,15 @@ hipError_t launch_append(const Shape& s, const fade_layer_cache& c, const uint16
   return hipGetLastError();
 }
 
-// Demote the oldest recent tokens of sequence blockIdx.x into the middle tail.
-// One thread per (K or V, KV head, group).
-__global__ __launch_bounds__(256) void k_demote(Shape s, fade_layer_cache c) {
-  const int b = blockIdx.x;
-  int32_t* L = c.lens + 4 * b;
+// Demote the oldest recent tokens of sequence b into the middle tail with
+// threads t0, t0 + nt, ...: one thread per (K or V, KV head, group). Returns
+// the new (M, R, head); the caller writes them to the lengths after a
+// barrier, once every thread of the workgroup is past its reads of them.
+struct DemoteLens {
+  int M, R, head;
+};
+__device__ __forceinline__ DemoteLens demote_rows(const Shape& s, const fade_layer_cache& c, int b, int t0, int nt) {
+  const int32_t* L = c.lens + 4 * b;
   int M = min(max(L[1], 0), s.cap_mid), R = min(max(L[2], 0), s.ring);
   int head = min(max(L[3], 0), s.ring - 1);
   const int ng = s.D / kGroup;
@@ -144,7 +148,7 @@ __global__ __launch_bounds__(256) void k_demote(Shape s, fade_layer_cache c) {
   const int work = 2 * s.Hkv * ng;
   while (R > s.W && M < s.cap_mid) {
     const int slot = s.n_sink + head;
-    for (int t = threadIdx.x; t < work; t += blockDim.x) {
+    for (int t = t0; t < work; t += nt) {
       const int which = t / (s.Hkv * ng);
       const int rem = t - which * s.Hkv * ng;
       const int g = rem / ng, grp = rem - g * ng;
@@ -172,16 +176,79 @@ __global__ __launch_bounds__(256) void k_demote(Shape s, fade_layer_cache c) {
     --R;
     ++M;
   }
+  return DemoteLens{M, R, head};
+}
+__device__ __forceinline__ void demote_commit(const fade_layer_cache& c, int b, const DemoteLens& d) {
+  int32_t* L = c.lens + 4 * b;
+  L[1] = d.M;
+  L[2] = d.R;
+  L[3] = d.head;
+}
+
+__global__ __launch_bounds__(256) void k_demote(Shape s, fade_layer_cache c) {
+  const DemoteLens d = demote_rows(s, c, blockIdx.x, threadIdx.x, blockDim.x);
   __syncthreads();
-  if (threadIdx.x == 0) {
-    L[1] = M;
-    L[2] = R;
-    L[3] = head;
-  }
+  if (threadIdx.x == 0) demote_commit(c, blockIdx.x, d);
 }
 
 hipError_t launch_demote(const Shape& s, const fade_layer_cache& c, hipStream_t st) {
   hipLaunchKernelGGL(k_demote, dim3(s.batch), dim3(64), 0, st, s, c);
+  return hipGetLastError();
+}
+
+// The decode-time score update of sequence blockIdx.x's row (the shared row,
+// summed over the sequences' side outputs, by sequence 0 of a shared cache)
+// and the demotion of its oldest recent tokens: the two steps of a decode
+// step that follow attention, in one launch. Wave 0 demotes while waves 1-3
+// update the scores. Demotion keeps every slot's position (the score row's
+// index) and the live length and touches no score, and the new lengths are
+// written after the barrier that follows every read of them, so the result
+// equals the score update followed by the demotion.
+__global__ __launch_bounds__(256) void k_score_update_demote(Shape s, fade_layer_cache c, const float* __restrict__ tok_attn,
+                                                             int mode, float decay) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  DemoteLens d{0, 0, 0};
+  if (tid < 64) {                                // wave-uniform
+    d = demote_rows(s, c, b, tid, 64);
+  } else if (!s.shared || b == 0) {
+    const int32_t* L = c.lens + 4 * b;
+    const int T = L[0] + L[1] + L[2] + (s.low ? c.low_lens[b] : 0);
+    const int n = min(T, s.cap_T);
+    float* __restrict__ row = c.scores + (size_t)b * s.cap_T;   // b == 0 for a shared row
+    // eight slots per thread per round, every load of a round before its
+    // first store (the score row and the side output are separate buffers)
+    constexpr int U = 8, NT = 192;
+    for (int j0 = tid - 64; j0 < n; j0 += U * NT) {
+      float a[U], v[U];
+      if (!s.shared) {
+        const float* __restrict__ ta = tok_attn + (size_t)b * s.cap_T;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int j = min(j0 + u * NT, n - 1);
+          v[u] = row[j];
+          a[u] = ta[j];
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int j = min(j0 + u * NT, n - 1);
+          v[u] = row[j];
+          a[u] = 0.f;
+          for (int q = 0; q < s.batch; ++q) a[u] += tok_attn[(size_t)q * s.cap_T + j];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (j0 + u * NT < n) row[j0 + u * NT] = score_update_value(v[u], a[u], mode, decay);
+    }
+  }
+  __syncthreads();
+  if (tid == 0) demote_commit(c, b, d);
+}
+
+hipError_t launch_score_update_demote(const Shape& s, const fade_layer_cache& c, int mode,
+                                      const float* tok_attn, float decay, hipStream_t st) {
+  hipLaunchKernelGGL(k_score_update_demote, dim3(s.batch), dim3(256), 0, st, s, c, tok_attn, mode, decay);
   return hipGetLastError();
 }
 

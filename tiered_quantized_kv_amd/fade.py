@@ -67,6 +67,7 @@ _SIGS = {
     "fade_quantize_pack": (ctypes.c_int, [_CFG, _P, ctypes.c_int64, ctypes.c_int64, _P, _P, ctypes.c_int32, _P, _P, _P]),
     "fade_cache_append": (ctypes.c_int, [_CFG, _CACHE, _P, _P, _P]),
     "fade_cache_demote": (ctypes.c_int, [_CFG, _CACHE, _P]),
+    "fade_score_update_demote": (ctypes.c_int, [_CFG, _CACHE, ctypes.c_int32, _P, ctypes.c_float, _P]),
     "fade_tiered_decode_attn": (ctypes.c_int, [_CFG, _CACHE, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "fade_tiered_decode_attn_noalloc": (ctypes.c_int, [_CFG, _CACHE, _P, _P, _P, _P]),
     "fade_h2o_scores": (ctypes.c_int, [_CFG, ctypes.c_int32, _CACHE, _P, _P, ctypes.c_int32, ctypes.c_int32,
@@ -239,6 +240,11 @@ def fade_cache_append(cfg, cache, k_new, v_new, stream=None):
 
 def fade_cache_demote(cfg, cache, stream=None):
     _check(lib().fade_cache_demote(ctypes.byref(cfg), cache.ref(), _s(stream)), "fade_cache_demote")
+
+
+def fade_score_update_demote(cfg, cache, mode, tok_attn, decay=0.0, stream=None):
+    _check(lib().fade_score_update_demote(ctypes.byref(cfg), cache.ref(), mode, _p(tok_attn), ctypes.c_float(decay),
+                                          _s(stream)), "fade_score_update_demote")
 
 
 def fade_tiered_decode_attn(cfg, cache, q, out, tok_attn, ws, stream=None):
