@@ -199,8 +199,11 @@ class Workload:
 
     # ---- accounting --------------------------------------------------------
     def decode_bytes_and_tokens(self):
-        """Algorithmic bytes and attended tokens of one decode-attention call
-        (one layer) at the current step, from the host mirror."""
+        """Algorithmic bytes and attended tokens of one append + decode-attention
+        call (one layer) at the current step, from the host mirror: every live
+        row read once (the new token's from its input rows), the new token's
+        K and V rows written into the cache, q read, the output and the side
+        output written."""
         w = self.w
         d, hkv = self.d, self.hkv
         per_fp = hkv * d * 4
@@ -209,8 +212,9 @@ class Workload:
         kv = sum(F * per_fp + m * per_mid for m in self.M)
         qo = self.B * self.hq * d * 2 * 2
         side = sum(F + m for m in self.M) * 4 if self.side else 0
+        app = self.B * per_fp
         tokens = sum(F + m for m in self.M)
-        return kv + qo + side, tokens
+        return kv + qo + side + app, tokens
 
     def moved_bytes(self, kept):
         """HBM bytes an eviction call moves, from its kept-slot map (old slot of
@@ -272,10 +276,10 @@ class Workload:
         for l in range(self.layers):
             tc = self.caches[l]
             q, kn, vn = self.pool[l][t % 4]
-            fade.fade_cache_append(self.cfg, tc, kn, vn)
+            # the new token's append and the decode attention: one call
             if events is not None and events[l] is not None:
                 events[l][0].record()
-            fade.fade_tiered_decode_attn(self.cfg, tc, q, self.out, self.tok, self.ws_dec)
+            fade.fade_append_decode_attn(self.cfg, tc, kn, vn, q, self.out, self.tok, self.ws_dec)
             if events is not None and events[l] is not None:
                 events[l][1].record()
             # score update (ACCUM / EMA) and demotion: one launch

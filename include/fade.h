@@ -293,6 +293,22 @@ int fade_tiered_decode_attn(const fade_config* cfg, const fade_layer_cache* cach
                             void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * fade_cache_append followed by fade_tiered_decode_attn, in the decode
+ * launches (FADE post, "核心机制": the newest token enters the fp16 tiers and
+ * is attended with every tier). k_new / v_new as for fade_cache_append, the
+ * rest as for fade_tiered_decode_attn, with the same workspace. The cache
+ * ends in the same state, and out and tok_attn hold the same values, bit for
+ * bit, as after those two calls: the attention reads the new token's rows
+ * from k_new / v_new, the workgroup that attends it writes them into their
+ * slot, and the merge kernel then advances the lengths and clears the new
+ * slot's score. A full ring (no append) attends the cache as it is. Errors:
+ * those of the two calls.
+ */
+int fade_append_decode_attn(const fade_config* cfg, fade_layer_cache* cache,
+                            const void* k_new, const void* v_new, const void* q, void* out,
+                            float* tok_attn, void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * fade_tiered_decode_attn without a workspace, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation). Same arguments, kernels and results as

@@ -241,6 +241,37 @@ def test_score_update_demote_validation():
     assert call(bad, fade.SCORE_ACCUM, good, 0.0) == fade.FADE_ERR_INVALID_ARG
 
 
+def test_append_decode_attn_validation():
+    """fade_append_decode_attn rejects what fade_cache_append and
+    fade_tiered_decode_attn reject, before any launch."""
+    lib = fade.lib()
+    cfg = _cfg()
+    null = ctypes.c_void_p(0)
+    good = ctypes.c_void_p(16)
+    c = fade.LayerCache(1, 4096, 4 + 4096 + 65, 0, 16, 16, 16, 16, 16, 16, 16, None)
+
+    def call(k, v, q, out, tok, ws, ws_bytes, cache=c):
+        return lib.fade_append_decode_attn(ctypes.byref(cfg), ctypes.byref(cache), k, v, q, out, tok, ws, ws_bytes,
+                                           null)
+
+    big = 1 << 40
+    # the append's operands: present and 16-byte aligned
+    assert call(null, good, good, good, null, good, big) == fade.FADE_ERR_INVALID_ARG
+    assert call(good, null, good, good, null, good, big) == fade.FADE_ERR_INVALID_ARG
+    assert call(ctypes.c_void_p(24), good, good, good, null, good, big) == fade.FADE_ERR_INVALID_ARG
+    assert call(good, ctypes.c_void_p(24), good, good, null, good, big) == fade.FADE_ERR_INVALID_ARG
+    # the decode's: query, output, side output, workspace
+    assert call(good, good, null, good, null, good, big) == fade.FADE_ERR_INVALID_ARG
+    assert call(good, good, good, ctypes.c_void_p(8), null, good, big) == fade.FADE_ERR_INVALID_ARG
+    assert call(good, good, good, good, ctypes.c_void_p(18), good, big) == fade.FADE_ERR_INVALID_ARG
+    assert call(good, good, good, good, null, null, big) == fade.FADE_ERR_WORKSPACE
+    need = fade.workspace_bytes(cfg, fade.WS_DECODE, 1, 4096)
+    assert call(good, good, good, good, null, good, need - 1) == fade.FADE_ERR_WORKSPACE
+    # the cache checks: a wrong cap_T
+    bad = fade.LayerCache(1, 10, 999, 0, 16, 16, 16, 16, 16, 16, 16, None)
+    assert call(good, good, good, good, null, good, big, cache=bad) == fade.FADE_ERR_INVALID_ARG
+
+
 def test_rope_scheme_validation():
     """Each RoPE scheme's parameters are checked on the host, before any launch
     (a zero-row rotation is a no-op once the configuration is valid)."""

@@ -28,7 +28,8 @@ def test_decode_bytes_match_the_oracle_closed_form(name):
                                      [F] * wl.B, wl.M)
     qo = wl.B * wl.hq * wl.d * 2 * 2
     side = 4 * sum(F + m for m in wl.M) if wl.side else 0
-    assert nbytes == kv + qo + side
+    app = wl.B * wl.hkv * wl.d * 2 * 2           # the new token's fp16 K and V rows written into the cache
+    assert nbytes == kv + qo + side + app
     assert tokens == sum(F + m for m in wl.M)
 
 

@@ -101,10 +101,12 @@ def _build(cfg, lengths, seed, cap_mid, score_kind, shared):
 
 
 def _run_loop(cfg, lengths, steps, mode, policy, period, seed, cap_mid, score_kind, shared=False, decay=0.9,
-              fused=False, trace=None):
+              fused=False, trace=None, app_fused=False, outs=None):
     """fused: the score update and demotion as one fade_score_update_demote
+    call; app_fused: the append and the decode as one fade_append_decode_attn
     call; trace: a list that receives every sequence's raw GPU state after
-    every step."""
+    every step; outs: a list that receives each step's output and side
+    output."""
     tc, refs = _build(cfg, lengths, seed, cap_mid, score_kind, shared)
     for b, r in enumerate(refs):
         assert_state_equal(seq_state(tc, b), r, check_scores=False)
@@ -130,10 +132,13 @@ def _run_loop(cfg, lengths, steps, mode, policy, period, seed, cap_mid, score_ki
             qf.astype(np.float16))
         q_exact = qt.float().numpy().astype(np.float64)
 
-        fade.fade_cache_append(cfg, tc, dev16(kn), dev16(vn))
         out = torch.zeros(B, hq, d, dtype=torch.float32, device=DEV)
         tok = torch.full((B, tc.cap_T), -1.0, dtype=torch.float32, device=DEV) if side else None
-        fade.fade_tiered_decode_attn(cfg, tc, qt.to(DEV), out, tok, ws_dec)
+        if app_fused:
+            fade.fade_append_decode_attn(cfg, tc, dev16(kn), dev16(vn), qt.to(DEV), out, tok, ws_dec)
+        else:
+            fade.fade_cache_append(cfg, tc, dev16(kn), dev16(vn))
+            fade.fade_tiered_decode_attn(cfg, tc, qt.to(DEV), out, tok, ws_dec)
         smode = fade.SCORE_ACCUM if mode == "accum" else fade.SCORE_EMA
         if side and fused:
             fade.fade_score_update_demote(cfg, tc, smode, tok, decay)
@@ -148,6 +153,8 @@ def _run_loop(cfg, lengths, steps, mode, policy, period, seed, cap_mid, score_ki
         torch.cuda.synchronize()
         got = out.cpu().numpy().astype(np.float64)
         tokh = tok.cpu().numpy() if side else None
+        if outs is not None:
+            outs.append((got, tokh))
 
         sides = []
         for b, r in enumerate(refs):
@@ -266,3 +273,87 @@ def test_fused_score_update_demote_equals_two_calls(mode, shared):
             assert sa.keys() == sb.keys()
             for key in sa:
                 assert np.array_equal(np.asarray(sa[key]), np.asarray(sb[key])), (step, q, key)
+
+
+# The append folded into the decode launches (fade_append_decode_attn) must
+# leave the cache, the output and the side output exactly as the two calls
+# fade_cache_append + fade_tiered_decode_attn do: the loops run it against the
+# oracle, the comparisons below bit for bit after every step.
+def test_closed_loop_serving_batch_append_decode_fused():
+    cfg = _cfg(128, 32, 8, 4, 64, 256, 4, 2, rope_theta=5e5)
+    lengths = [1500, 300, 900, 2, 325, 700, 1100, 333]
+    nf, ne = _run_loop(cfg, lengths, 16, "ema", "score", 1, 4311, cap_mid=257, score_kind="ema", fused=True,
+                       app_fused=True)
+    assert ne > 0
+
+
+def test_closed_loop_llama32_like_shared_append_decode_fused():
+    cfg = _cfg(64, 32, 8, 4, 64, 128, 4, 4, rope_type="llama3", rope_theta=5e5, rope_factor=32.0,
+               rope_low_freq_factor=1.0, rope_high_freq_factor=4.0, rope_original_max_position=8192)
+    nf, ne = _run_loop(cfg, [700] * 4, 17, "accum", "score", 16, 4211, cap_mid=128 + 16, score_kind="h2o",
+                       shared=True, app_fused=True)
+    assert ne >= 4
+
+
+def _same_trace(t_a, t_b, o_a, o_b):
+    assert len(t_a) == len(t_b) and len(o_a) == len(o_b)
+    for step, (a, b) in enumerate(zip(t_a, t_b)):
+        for q, (sa, sb) in enumerate(zip(a, b)):
+            assert sa.keys() == sb.keys()
+            for key in sa:
+                assert np.array_equal(np.asarray(sa[key]), np.asarray(sb[key])), (step, q, key)
+    for step, ((ga, ta), (gb, tb)) in enumerate(zip(o_a, o_b)):
+        assert np.array_equal(ga, gb), step
+        assert (ta is None) == (tb is None)
+        if ta is not None:
+            assert np.array_equal(ta, tb), step
+
+
+@pytest.mark.parametrize("mode,shared,bf16", [("ema", False, False), ("accum", True, True), ("none", False, False)])
+def test_append_decode_fused_equals_two_calls(mode, shared, bf16):
+    """Bit-identical state, output and side output after every step, with the
+    sinks still filling in one sequence, head dims 128 and 64, and no side
+    output."""
+    d = 64 if shared else 128
+    cfg = _cfg(d, 16, 4, 4, 16, 64, 4, 2, q_dtype="bf16" if bf16 else "f16", rope_theta=5e5)
+    lengths = [400] * 3 if shared else [400, 90, 3, 1]
+    kw = dict(steps=12, mode=mode, policy="score" if mode != "none" else "position", period=3, seed=4321,
+              cap_mid=64 + 3, score_kind="ema" if mode != "none" else None, shared=shared)
+    t_sep, t_fus, o_sep, o_fus = [], [], [], []
+    _run_loop(cfg, lengths, trace=t_sep, outs=o_sep, **kw)
+    _run_loop(cfg, lengths, app_fused=True, trace=t_fus, outs=o_fus, **kw)
+    assert len(t_sep) == 12
+    _same_trace(t_sep, t_fus, o_sep, o_fus)
+
+
+def test_append_decode_fused_full_ring_equals_two_calls():
+    """No demotion between steps: the rings fill, and an append to a full ring
+    changes nothing in either path while the attention still runs over the
+    cache as it is."""
+    cfg = _cfg(128, 16, 4, 4, 8, 32, 4, 2, rope_theta=5e5)
+    lengths = [100, 30, 2]
+    B, hq, hkv, d = len(lengths), cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    runs = []
+    for fused in (False, True):
+        tc, refs = _build(cfg, lengths, 4330, 32 + 3, "h2o", False)
+        ws_dec = fade.workspace(cfg, fade.WS_DECODE, B, 32 + 3)
+        gen = synth.rng(4330, 5)
+        trace, outs = [], []
+        for step in range(14):
+            kn = synth.normal(gen, B, hkv, d).astype(np.float16)
+            vn = synth.normal(gen, B, hkv, d).astype(np.float16)
+            q = synth.normal(gen, B, hq, d).astype(np.float16)
+            out = torch.zeros(B, hq, d, dtype=torch.float32, device=DEV)
+            tok = torch.full((B, tc.cap_T), -1.0, dtype=torch.float32, device=DEV)
+            if fused:
+                fade.fade_append_decode_attn(cfg, tc, dev16(kn), dev16(vn), dev16(q), out, tok, ws_dec)
+            else:
+                fade.fade_cache_append(cfg, tc, dev16(kn), dev16(vn))
+                fade.fade_tiered_decode_attn(cfg, tc, dev16(q), out, tok, ws_dec)
+            torch.cuda.synchronize()
+            trace.append([seq_state(tc, b) for b in range(B)])
+            outs.append((out.cpu().numpy(), tok.cpu().numpy()))
+        runs.append((trace, outs))
+        lens = tc.lens.cpu().numpy().reshape(B, 4)
+        assert lens[0, 2] == lens[1, 2] == cfg.recent_window + 1      # the rings (window + 1 slots) are full
+    _same_trace(runs[0][0], runs[1][0], runs[0][1], runs[1][1])

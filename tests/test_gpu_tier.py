@@ -104,7 +104,7 @@ def test_tier_decode_attention_ragged():
         assert np.all(side[b, t1:] == 0)
 
 
-def _loop(cfg, lengths, steps, mode, policy, period, seed, cap_mid, cap_low, score_kind, shared=False, fused=False):
+def _loop(cfg, lengths, steps, mode, policy, period, seed, cap_mid, cap_low, score_kind, shared=False, fused=False, app_fused=False):
     oc_cfg = ocfg(cfg)
     f, il = oc_cfg.freqs(), oc_cfg.rope_interleaved
     B, hq, hkv, d = len(lengths), cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
@@ -150,10 +150,13 @@ def _loop(cfg, lengths, steps, mode, policy, period, seed, cap_mid, cap_low, sco
         vn = synth.normal(gen, B, hkv, d).astype(np.float16)
         q = np.stack([rope.rotate(synth.normal(gen, hq, d), np.full(hq, T[b]), f, il) for b in range(B)]).astype(
             np.float16)
-        fade.fade_cache_append(cfg, tc, dev16(kn), dev16(vn))
         out = torch.zeros(B, hq, d, dtype=torch.float32, device=DEV)
         tok = torch.full((B, tc.cap_T), -1.0, dtype=torch.float32, device=DEV) if side else None
-        fade.fade_tiered_decode_attn(cfg, tc, dev16(q), out, tok, ws_dec)
+        if app_fused:                            # one call: append, then attend
+            fade.fade_append_decode_attn(cfg, tc, dev16(kn), dev16(vn), dev16(q), out, tok, ws_dec)
+        else:
+            fade.fade_cache_append(cfg, tc, dev16(kn), dev16(vn))
+            fade.fade_tiered_decode_attn(cfg, tc, dev16(q), out, tok, ws_dec)
         smode = fade.SCORE_ACCUM if mode == "accum" else fade.SCORE_EMA
         if side and fused:                       # one call: update, then demote
             fade.fade_score_update_demote(cfg, tc, smode, tok, 0.9)
@@ -247,3 +250,14 @@ def test_tier_closed_loop_ema_every_step_fused():
     refs, n = _loop(cfg, [600, 140, 97, 300], 12, "ema", "score", 1, 741, cap_mid=65, cap_low=33, score_kind="ema",
                     fused=True)
     assert n == 12 * 4
+
+
+def test_tier_closed_loop_append_decode_fused():
+    """The append and the decode attention as one fade_append_decode_attn call
+    (and the score update with demotion as one call), against the oracle: the
+    INT2 tier's rows sit between the sinks and the INT4 middle in the side
+    output, the new token's row after the ring's."""
+    cfg = _cfg(d=128, hq=32, hkv=8, w=16, b4=64, b2=32)
+    refs, n = _loop(cfg, [600, 140, 97, 300, 3], 12, "ema", "score", 1, 742, cap_mid=65, cap_low=33,
+                    score_kind="ema", fused=True, app_fused=True)
+    assert n > 0

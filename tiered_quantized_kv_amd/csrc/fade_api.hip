@@ -243,6 +243,22 @@ int fade_tiered_decode_attn(const fade_config* cfg, const fade_layer_cache* cach
                                   workspace, reinterpret_cast<hipStream_t>(stream)));
 }
 
+int fade_append_decode_attn(const fade_config* cfg, fade_layer_cache* cache, const void* k_new, const void* v_new,
+                            const void* q, void* out, float* tok_attn, void* workspace, size_t ws_bytes,
+                            void* stream) {
+  int st = check_cfg(cfg);
+  if (st) return st;
+  if ((st = check_cache(cfg, cache))) return st;
+  if (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new)) return FADE_ERR_INVALID_ARG;
+  if (!q || !out || !aligned16(q) || !aligned16(out)) return FADE_ERR_INVALID_ARG;
+  if (tok_attn && !aligned(tok_attn, 4)) return FADE_ERR_INVALID_ARG;
+  const Shape s = cache_shape(cfg, cache);
+  if (!workspace || !aligned16(workspace) || ws_bytes < decode_ws_bytes(s)) return FADE_ERR_WORKSPACE;
+  return hip_status(launch_decode(s, *cache, q, cfg->q_dtype == FADE_DTYPE_BF16, out, cfg->out_dtype, tok_attn,
+                                  workspace, reinterpret_cast<hipStream_t>(stream),
+                                  reinterpret_cast<const uint16_t*>(k_new), reinterpret_cast<const uint16_t*>(v_new)));
+}
+
 int fade_tiered_decode_attn_noalloc(const fade_config* cfg, const fade_layer_cache* cache, const void* q,
                                     void* out, float* tok_attn, void* stream) {
   int st = check_cfg(cfg);

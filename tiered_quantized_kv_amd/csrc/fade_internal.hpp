@@ -44,6 +44,39 @@ hipError_t launch_demote(const Shape& s, const fade_layer_cache& c, hipStream_t 
 hipError_t launch_score_update_demote(const Shape& s, const fade_layer_cache& c, int mode,
                                       const float* tok_attn, float decay, hipStream_t st);
 
+// Where fade_cache_append puts sequence b's new token, from its lengths before
+// the append (FADE post, "核心机制": tokens enter the fp16 tiers; the sinks
+// fill first, then the recent ring): a sink slot while the sinks fill, else
+// the ring slot after the newest recent token; slot < 0 when the ring is full
+// (no append). pos is the token's position, its index in the score row; S and
+// R are the sink and recent counts before the append.
+struct AppendPlan {
+  int slot, to_sink, pos, S, R;
+};
+__device__ __forceinline__ AppendPlan append_plan(const int32_t* L, int low_len, int n_sink, int ring,
+                                                  int cap_mid) {
+  AppendPlan p;
+  p.S = min(max(L[0], 0), n_sink);
+  p.R = min(max(L[2], 0), ring);
+  const int M = min(max(L[1], 0), cap_mid);
+  const int head = min(max(L[3], 0), ring - 1);
+  p.pos = p.S + low_len + M + p.R;
+  p.to_sink = p.S < n_sink;
+  p.slot = p.to_sink ? p.S : (p.R < ring ? n_sink + (head + p.R) % ring : -1);
+  return p;
+}
+// The bookkeeping half of an append, once the rows are written: the new
+// slot's score starts at 0 (a token has no accumulated attention yet,
+// Transformer series (25), 1.3.1 H2O; an empty EMA history) and the sink or
+// recent count grows by one. score_row: the sequence's score row, or nullptr
+// when no score is kept (or another sequence clears a shared row).
+__device__ __forceinline__ void append_commit(int32_t* L, const AppendPlan& p, float* score_row, int cap_T) {
+  if (p.slot < 0) return;
+  if (score_row && p.pos < cap_T) score_row[p.pos] = 0.f;
+  if (p.to_sink) L[0] = p.S + 1;
+  else L[2] = p.R + 1;
+}
+
 // One slot's decode-time score update (Transformer series (25), 1.3.1 H2O:
 // the accumulated attention; FADE post, "EMA策略": s = beta s + (1 - beta) a).
 // Shared by the score-update kernels, with the EMA's one fused multiply-add
@@ -57,9 +90,11 @@ __device__ __forceinline__ float score_update_value(float s, float a, int mode, 
 int decode_chunk(const Shape& s);                 // middle rows per split
 int decode_nsplit(const Shape& s);                // splits incl. the fp16 split
 size_t decode_ws_bytes(const Shape& s);
+// k_new / v_new set: the append of fade_cache_append first, in the same
+// launches (fade_append_decode_attn)
 hipError_t launch_decode(const Shape& s, const fade_layer_cache& c, const void* q,
                          int q_bf16, void* out, int out_dtype, float* tok_attn, void* ws,
-                         hipStream_t st);
+                         hipStream_t st, const uint16_t* k_new = nullptr, const uint16_t* v_new = nullptr);
 hipError_t launch_score_update(const Shape& s, const fade_layer_cache& c, int mode,
                                const float* tok_attn, float decay, hipStream_t st);
 // Library-held decode scratch (fade_tiered_decode_attn_noalloc): its device
@@ -115,7 +150,8 @@ hipError_t launch_pq_encode_rows_to(int D, const uint16_t* x, uint8_t* codes, in
                                     const int32_t* lim, int lim_stride, int lim_shared, const uint8_t* flags,
                                     int batch, int Hkv, int cap, hipStream_t st);
 hipError_t launch_decode_pq_mid(const Shape& s, const fade_layer_cache& c, const void* q, int q_bf16, float* part,
-                                float* raw, int raw_stride, int nsplit, int n_fp, int n_mid, hipStream_t st);
+                                float* raw, int raw_stride, int nsplit, int n_fp, int n_mid, hipStream_t st,
+                                int append);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

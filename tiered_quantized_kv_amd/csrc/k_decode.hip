@@ -70,6 +70,14 @@ struct DecodeArgs {
   const int32_t* low_lens;    // nullptr without an INT2 tier
   int cap_low;                // its row capacity
   int is_low, split0, n_tier;
+  // fade_append_decode_attn: the new token's rows [B, Hkv, D] (k_new nullptr:
+  // no append), the cache's fp16 arrays they are written to, and each
+  // sequence's live length after the append, for the merge kernel
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint16_t* app_k;
+  uint16_t* app_v;
+  int32_t* t_live;
 };
 
 constexpr int kThreads = 256;
@@ -139,6 +147,7 @@ int decode_raw_stride(const Shape& s) { return s.cap_T + kSub; }
 size_t decode_ws_bytes(const Shape& s) {
   size_t n = align_up((size_t)s.batch * s.Hq * decode_nsplit(s) * (s.D + 2) * 4, 256);
   n += align_up((size_t)s.batch * s.Hq * decode_raw_stride(s) * 4, 256);   // raw scores
+  n += align_up((size_t)s.batch * 4, 256);                                  // live lengths (append)
   return n;
 }
 
@@ -280,9 +289,18 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int Hq = a.Hkv * NREP;
   const int32_t* L = a.lens + 4 * b;
+  // With a new token (k_new set) every workgroup reads the lengths as they
+  // are before it and works with those after it (append_plan: the rule of
+  // fade_cache_append): the token is one more sink or recent slot, whose rows
+  // come from k_new / v_new. The merge kernel writes the new lengths.
+  AppendPlan ap;
+  ap.slot = -1;
+  if (a.k_new) ap = append_plan(L, a.low_lens ? max(a.low_lens[b], 0) : 0, a.n_sink, a.ring, a.cap_mid);
+  const bool app = ap.slot >= 0;
   // Lengths are clamped to capacity so no value in lens can index out of bounds.
-  const int S = min(max(L[0], 0), a.n_sink), M = min(max(a.tier_len[(size_t)b * a.tier_len_stride], 0), a.cap_mid);
-  const int R = min(max(L[2], 0), a.ring), rhead = min(max(L[3], 0), a.ring - 1);
+  const int S = min(max(L[0], 0), a.n_sink) + (app && ap.to_sink);
+  const int M = min(max(a.tier_len[(size_t)b * a.tier_len_stride], 0), a.cap_mid);
+  const int R = min(max(L[2], 0), a.ring) + (app && !ap.to_sink), rhead = min(max(L[3], 0), a.ring - 1);
   const int M2 = a.low_lens ? min(max(a.low_lens[b], 0), a.cap_low) : 0;   // INT2 slots before the INT4 middle
   const int mbase = S + (a.is_low ? 0 : M2);                // slot of this tier's row 0
   const bool fpt = lsplit < a.n_fp;                   // FP16 tier
@@ -294,6 +312,10 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
 
   float* part_base = a.part + ((size_t)(b * Hq + g * NREP) * a.nsplit + split) * (D + 2);
   const size_t part_hstride = (size_t)a.nsplit * (D + 2);
+  // the live length after the append, once per sequence, as the merge kernel
+  // would read it from the lengths
+  if (a.t_live && !a.is_low && lsplit == 0 && g == 0 && tid == 0)
+    a.t_live[b] = L[0] + L[1] + L[2] + (a.low_lens ? a.low_lens[b] : 0) + (app ? 1 : 0);
   if (n_tok <= 0) {
     for (int i = tid; i < NREP * (D + 2); i += kThreads) {
       const int h = i / (D + 2), c = i - h * (D + 2);
@@ -582,13 +604,30 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
     const uint16_t* fv = a.fp_v + bg * fp_slots * D;
     float* pf = reinterpret_cast<float*>(pw);               // [64 tokens][HQ4 * 4] weights
     auto slot_of = [&](int tt) { return tt < S ? tt : a.n_sink + (rhead + (tt - S)) % a.ring; };
+    // a new token's rows are read from k_new / v_new (ap.slot is -1 without
+    // one); the split that holds it also writes them into its slot, which no
+    // other workgroup reads
+    const uint16_t* knew = app ? a.k_new + bg * D : nullptr;
+    const uint16_t* vnew = app ? a.v_new + bg * D : nullptr;
+    auto krow = [&](int slot) { return slot == ap.slot ? knew : fk + (size_t)slot * D; };
+    auto vrow = [&](int slot) { return slot == ap.slot ? vnew : fv + (size_t)slot * D; };
+    if (app) {
+      const int idx = ap.to_sink ? ap.S : ap.S + ap.R;       // the new token in sink-then-ring order
+      if (idx >= fp_lo && idx < fp_lo + n_tok) {
+        for (int i = tid; i < D / 4; i += kThreads) {        // K and V rows, 16 bytes a thread
+          const int isv = i >= D / 8, ch = i - isv * (D / 8);
+          uint16_t* dst = (isv ? a.app_v : a.app_k) + (bg * fp_slots + ap.slot) * D + 8 * ch;
+          *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>((isv ? vnew : knew) + 8 * ch);
+        }
+      }
+    }
     const int sz = min(kSub, (n_tok + 3) / 4);             // tokens per wave slice
     for (int base = wave * sz; base < n_tok; base += 4 * sz) {
       const int ns = min(sz, n_tok - base);              // wave-uniform
       const bool valid = lane < ns;
       f32x4 d0[HQ4], d1[HQ4];
       {
-        const uint4* kp = reinterpret_cast<const uint4*>(fk + (size_t)slot_of(fp_lo + base + min(lane, ns - 1)) * D);
+        const uint4* kp = reinterpret_cast<const uint4*>(krow(slot_of(fp_lo + base + min(lane, ns - 1))));
         uint32_t w[D / 2];
 #pragma unroll
         for (int i = 0; i < D / 8; ++i) {
@@ -615,7 +654,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
         const int my_slot = slot_of(fp_lo + base + g0 + min(lane, nt - 1));
 #pragma unroll
         for (int k = 0; k < VB32; ++k) {
-          const uint16_t* vr = fv + (size_t)__builtin_amdgcn_readlane(my_slot, k) * D;
+          const uint16_t* vr = vrow(__builtin_amdgcn_readlane(my_slot, k));
           if constexpr (CPL == 2) vv[k] = *reinterpret_cast<const uint32_t*>(vr + 2 * lane);
           else vv[k] = vr[lane];
         }
@@ -706,6 +745,24 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
 constexpr int kFinishSlots = 64;
 constexpr int kFinishBatch = 8;    // splits per lane per round
 
+// The append's bookkeeping for fade_append_decode_attn (t_live set): the merge
+// takes each sequence's live length from t_live, written by the tiers kernel,
+// instead of from the lengths, and one workgroup per sequence commits the
+// append (append_commit), no other reader of the lengths being left.
+struct AppendCommitArgs {
+  const int32_t* t_live;   // nullptr: no append
+  int32_t* lens;
+  const int32_t* low_lens;
+  float* scores;
+  int n_sink, ring, cap_mid, shared;
+};
+__device__ __forceinline__ void finish_commit(const AppendCommitArgs& x, int b, int cap_T) {
+  int32_t* L = x.lens + 4 * b;
+  const AppendPlan p = append_plan(L, x.low_lens ? max(x.low_lens[b], 0) : 0, x.n_sink, x.ring, x.cap_mid);
+  float* row = x.scores && (!x.shared || b == 0) ? x.scores + (size_t)(x.shared ? 0 : b) * cap_T : nullptr;
+  append_commit(L, p, row, cap_T);
+}
+
 template <int LN>
 __device__ __forceinline__ float group_max(float x) {
   if constexpr (LN == 8) {
@@ -731,7 +788,7 @@ __global__ __launch_bounds__(256) void k_decode_finish(const float* __restrict__
                                                        const float* __restrict__ raw, int raw_stride,
                                                        const int32_t* __restrict__ lens,
                                                        const int32_t* __restrict__ low_lens, int cap_T,
-                                                       float* __restrict__ tok_attn) {
+                                                       float* __restrict__ tok_attn, AppendCommitArgs ax) {
   extern __shared__ float ml[];   // [Hq][2] = (M_h, 1 / L_h), then [4][kFinishSlots] partial sums
   const int b = blockIdx.x, j = blockIdx.y, nb = gridDim.y, tid = threadIdx.x;
   const int sub = tid % LN, grp = tid / LN, n_grp = blockDim.x / LN;
@@ -798,8 +855,10 @@ __global__ __launch_bounds__(256) void k_decode_finish(const float* __restrict__
       else reinterpret_cast<uint16_t*>(out)[oi] = f2h(o);
     }
   }
+  if (ax.t_live && j == 0 && tid == 0) finish_commit(ax, b, cap_T);
   if (!tok_attn) return;
-  const int T = lens[4 * b] + lens[4 * b + 1] + lens[4 * b + 2] + (low_lens ? low_lens[b] : 0);
+  const int T = ax.t_live ? ax.t_live[b]
+                          : lens[4 * b] + lens[4 * b + 1] + lens[4 * b + 2] + (low_lens ? low_lens[b] : 0);
   float* red = ml + 2 * Hq;
   for (int j0 = j * kFinishSlots; j0 < cap_T; j0 += nb * kFinishSlots) {
     const int u0 = tid % kFinishSlots, jj = j0 + u0, hg = tid / kFinishSlots;
@@ -838,11 +897,13 @@ __global__ __launch_bounds__(256) void k_decode_finish(const float* __restrict__
 // are added in group order.
 template <int D, int CPW>
 __global__ __launch_bounds__(256) void k_decode_finish_head(const float* __restrict__ part, int nsplit, int Hq,
-                                                            void* out, int out_dtype) {
+                                                            void* out, int out_dtype, AppendCommitArgs ax,
+                                                            int cap_T) {
   constexpr int SG = 256 / CPW;
   __shared__ float red[256];
   __shared__ float s_m, s_inv;
   const int b = blockIdx.x, h = blockIdx.y, c0 = blockIdx.z * CPW, tid = threadIdx.x;
+  if (ax.t_live && h == 0 && blockIdx.z == 0 && tid == 0) finish_commit(ax, b, cap_T);
   const float* ph = part + ((size_t)b * Hq + h) * nsplit * (D + 2);
   // ---- statistics of head h ----
   float m = -INFINITY;
@@ -919,13 +980,25 @@ static void dispatch_rep(int n_rep, int kb, int vb, const DecodeArgs& a, dim3 gr
 }
 
 hipError_t launch_decode(const Shape& s, const fade_layer_cache& c, const void* q, int q_bf16,
-                         void* out, int out_dtype, float* tok_attn, void* ws, hipStream_t st) {
+                         void* out, int out_dtype, float* tok_attn, void* ws, hipStream_t st,
+                         const uint16_t* k_new, const uint16_t* v_new) {
   const int nsplit = decode_nsplit(s);
   char* w = reinterpret_cast<char*>(ws);
   float* part = reinterpret_cast<float*>(w);
   w += align_up((size_t)s.batch * s.Hq * nsplit * (s.D + 2) * 4, 256);
   float* raw = reinterpret_cast<float*>(w);
+  w += align_up((size_t)s.batch * s.Hq * decode_raw_stride(s) * 4, 256);
+  int32_t* t_live = reinterpret_cast<int32_t*>(w);
   const int raw_stride = decode_raw_stride(s);
+  AppendCommitArgs ax;
+  ax.t_live = k_new ? t_live : nullptr;
+  ax.lens = c.lens;
+  ax.low_lens = s.low ? c.low_lens : nullptr;
+  ax.scores = c.scores;
+  ax.n_sink = s.n_sink;
+  ax.ring = s.ring;
+  ax.cap_mid = s.cap_mid;
+  ax.shared = s.shared;
 
   DecodeArgs a;
   a.fp_k = reinterpret_cast<const uint16_t*>(c.fp_k);
@@ -956,6 +1029,11 @@ hipError_t launch_decode(const Shape& s, const fade_layer_cache& c, const void* 
   a.is_low = 0;
   a.split0 = 0;
   a.n_tier = s.pq ? 0 : decode_mid_splits(s);     // a PQ middle tier has its own kernel
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.app_k = reinterpret_cast<uint16_t*>(c.fp_k);
+  a.app_v = reinterpret_cast<uint16_t*>(c.fp_v);
+  a.t_live = k_new ? t_live : nullptr;
   const int n_main = a.n_fp + a.n_tier;
   auto dispatch = [&](const DecodeArgs& da, int n_splits, int kb, int vb) {
     const dim3 grid(n_splits * s.Hkv * s.batch);
@@ -972,7 +1050,8 @@ hipError_t launch_decode(const Shape& s, const fade_layer_cache& c, const void* 
   if (e != hipSuccess) return e;
   if (s.pq) {
     // the PQ middle tier's splits follow the fp16 tier's in the partials
-    e = launch_decode_pq_mid(s, c, q, q_bf16, part, a.raw, raw_stride, nsplit, a.n_fp, decode_mid_splits(s), st);
+    e = launch_decode_pq_mid(s, c, q, q_bf16, part, a.raw, raw_stride, nsplit, a.n_fp, decode_mid_splits(s), st,
+                             k_new != nullptr);
     if (e != hipSuccess) return e;
   }
   const int n_low = decode_low_splits(s);
@@ -1016,11 +1095,11 @@ hipError_t launch_decode(const Shape& s, const fade_layer_cache& c, const void* 
     const bool fine = (long)s.batch * s.Hq * (s.D / 32) < 512;
     const dim3 hgrid(s.batch, s.Hq, s.D / (fine ? 16 : 32));
     if (s.D == 128) {
-      if (fine) hipLaunchKernelGGL((k_decode_finish_head<128, 16>), hgrid, dim3(256), 0, st, part, nsplit, s.Hq, out, out_dtype);
-      else hipLaunchKernelGGL((k_decode_finish_head<128, 32>), hgrid, dim3(256), 0, st, part, nsplit, s.Hq, out, out_dtype);
+      if (fine) hipLaunchKernelGGL((k_decode_finish_head<128, 16>), hgrid, dim3(256), 0, st, part, nsplit, s.Hq, out, out_dtype, ax, s.cap_T);
+      else hipLaunchKernelGGL((k_decode_finish_head<128, 32>), hgrid, dim3(256), 0, st, part, nsplit, s.Hq, out, out_dtype, ax, s.cap_T);
     } else {
-      if (fine) hipLaunchKernelGGL((k_decode_finish_head<64, 16>), hgrid, dim3(256), 0, st, part, nsplit, s.Hq, out, out_dtype);
-      else hipLaunchKernelGGL((k_decode_finish_head<64, 32>), hgrid, dim3(256), 0, st, part, nsplit, s.Hq, out, out_dtype);
+      if (fine) hipLaunchKernelGGL((k_decode_finish_head<64, 16>), hgrid, dim3(256), 0, st, part, nsplit, s.Hq, out, out_dtype, ax, s.cap_T);
+      else hipLaunchKernelGGL((k_decode_finish_head<64, 32>), hgrid, dim3(256), 0, st, part, nsplit, s.Hq, out, out_dtype, ax, s.cap_T);
     }
     return hipGetLastError();
   }
@@ -1029,17 +1108,17 @@ hipError_t launch_decode(const Shape& s, const fade_layer_cache& c, const void* 
   if (s.D == 128) {
     if (wide)
       hipLaunchKernelGGL((k_decode_finish<128, 8>), fgrid, dim3(256), flds, st, part, nsplit, s.Hq, out, out_dtype,
-                         raw, raw_stride, c.lens, s.low ? c.low_lens : nullptr, s.cap_T, tok_attn);
+                         raw, raw_stride, c.lens, s.low ? c.low_lens : nullptr, s.cap_T, tok_attn, ax);
     else
       hipLaunchKernelGGL((k_decode_finish<128, 1>), fgrid, dim3(256), flds, st, part, nsplit, s.Hq, out, out_dtype,
-                         raw, raw_stride, c.lens, s.low ? c.low_lens : nullptr, s.cap_T, tok_attn);
+                         raw, raw_stride, c.lens, s.low ? c.low_lens : nullptr, s.cap_T, tok_attn, ax);
   } else {
     if (wide)
       hipLaunchKernelGGL((k_decode_finish<64, 8>), fgrid, dim3(256), flds, st, part, nsplit, s.Hq, out, out_dtype,
-                         raw, raw_stride, c.lens, s.low ? c.low_lens : nullptr, s.cap_T, tok_attn);
+                         raw, raw_stride, c.lens, s.low ? c.low_lens : nullptr, s.cap_T, tok_attn, ax);
     else
       hipLaunchKernelGGL((k_decode_finish<64, 1>), fgrid, dim3(256), flds, st, part, nsplit, s.Hq, out, out_dtype,
-                         raw, raw_stride, c.lens, s.low ? c.low_lens : nullptr, s.cap_T, tok_attn);
+                         raw, raw_stride, c.lens, s.low ? c.low_lens : nullptr, s.cap_T, tok_attn, ax);
   }
   return hipGetLastError();
 }

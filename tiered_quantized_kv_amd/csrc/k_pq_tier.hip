@@ -145,6 +145,7 @@ struct PqDecodeArgs {
   float* part;                // [B][Hq][nsplit][D + 2]
   float* raw;                 // [B][Hq][raw_stride] or nullptr
   int batch, Hkv, n_sink, cap_mid, raw_stride, nsplit, n_fp, n_mid;
+  int append;                 // a token is appended in the same call: sinks not yet full take it
   float qk_scale;
 };
 
@@ -241,7 +242,8 @@ __global__ __launch_bounds__(pq_waves(NREP) * 64) void k_decode_pq(PqDecodeArgs 
     const int lsplit = item / n_pairs, pair = item - lsplit * n_pairs;
     const int g = pair % a.Hkv, b = pair / a.Hkv;
     const int32_t* lens = a.lens + 4 * b;
-    const int S = min(max(lens[0], 0), a.n_sink), M = min(max(lens[1], 0), a.cap_mid);
+    const int S0 = min(max(lens[0], 0), a.n_sink), M = min(max(lens[1], 0), a.cap_mid);
+    const int S = S0 + (a.append && S0 < a.n_sink);   // sink count after an appended token
     const int per = ((M + a.n_mid - 1) / a.n_mid + 63) / 64 * 64;
     const int row0 = lsplit * per;
     const int n_tok = min(per, M - row0);
@@ -473,7 +475,8 @@ static void launch_pq_mid_l(int n_rep, const PqDecodeArgs& a, int blocks, hipStr
 }
 
 hipError_t launch_decode_pq_mid(const Shape& s, const fade_layer_cache& c, const void* q, int q_bf16, float* part,
-                                float* raw, int raw_stride, int nsplit, int n_fp, int n_mid, hipStream_t st) {
+                                float* raw, int raw_stride, int nsplit, int n_fp, int n_mid, hipStream_t st,
+                                int append) {
   PqDecodeArgs a;
   a.q = reinterpret_cast<const uint16_t*>(q);
   a.q_bf16 = q_bf16;
@@ -492,6 +495,7 @@ hipError_t launch_decode_pq_mid(const Shape& s, const fade_layer_cache& c, const
   a.nsplit = nsplit;
   a.n_fp = n_fp;
   a.n_mid = n_mid;
+  a.append = append;
   a.qk_scale = kLog2e / sqrtf((float)s.D);
   // one workgroup per CU holds both codebooks; the items are dealt over them
   const int items = s.batch * s.Hkv * n_mid;

@@ -88,19 +88,8 @@ __global__ __launch_bounds__(256) void k_append(Shape s, fade_layer_cache c,
                                                 const uint16_t* __restrict__ v_new) {
   const int b = blockIdx.x;
   int32_t* L = c.lens + 4 * b;
-  const int S = min(max(L[0], 0), s.n_sink), R = min(max(L[2], 0), s.ring);
-  const int M = min(max(L[1], 0), s.cap_mid);
-  const int head = min(max(L[3], 0), s.ring - 1);
-  int slot;
-  bool to_sink = false;
-  if (S < s.n_sink) {
-    slot = S;
-    to_sink = true;
-  } else if (R < s.ring) {
-    slot = s.n_sink + (head + R) % s.ring;
-  } else {
-    return;   // ring full: caller skipped demotion; leave the sequence unchanged
-  }
+  const AppendPlan ap = append_plan(L, s.low ? max(c.low_lens[b], 0) : 0, s.n_sink, s.ring, s.cap_mid);
+  if (ap.slot < 0) return;   // ring full: caller skipped demotion; leave the sequence unchanged
   const int slots = s.n_sink + s.ring;
   const int chunks = s.D / 8;                    // uint4 chunks per row
   uint4* fk = reinterpret_cast<uint4*>(c.fp_k);
@@ -109,21 +98,17 @@ __global__ __launch_bounds__(256) void k_append(Shape s, fade_layer_cache c,
   const uint4* vn = reinterpret_cast<const uint4*>(v_new);
   for (int t = threadIdx.x; t < s.Hkv * chunks; t += blockDim.x) {
     const int g = t / chunks, ch = t - g * chunks;
-    const size_t dst = ((size_t)(b * s.Hkv + g) * slots + slot) * chunks + ch;
+    const size_t dst = ((size_t)(b * s.Hkv + g) * slots + ap.slot) * chunks + ch;
     const size_t srcx = (size_t)(b * s.Hkv + g) * chunks + ch;
     fk[dst] = kn[srcx];
     fv[dst] = vn[srcx];
   }
-  // A shared cache has one score row and identical lengths in every row:
-  // sequence 0 clears it.
-  const int pos = S + (s.low ? max(c.low_lens[b], 0) : 0) + M + R;
-  if (threadIdx.x == 0 && c.scores && (!c.shared || b == 0) && pos < s.cap_T)
-    c.scores[(size_t)(c.shared ? 0 : b) * s.cap_T + pos] = 0.f;
+  // every thread has read the lengths; a shared cache has one score row and
+  // identical lengths in every row: sequence 0 clears it
   __syncthreads();
-  if (threadIdx.x == 0) {
-    if (to_sink) L[0] = S + 1;
-    else L[2] = R + 1;
-  }
+  if (threadIdx.x == 0)
+    append_commit(L, ap, c.scores && (!c.shared || b == 0) ? c.scores + (size_t)(c.shared ? 0 : b) * s.cap_T : nullptr,
+                  s.cap_T);
 }
 
 hipError_t launch_append(const Shape& s, const fade_layer_cache& c, const uint16_t* k_new,
