@@ -203,7 +203,10 @@ class Workload:
         call (one layer) at the current step, from the host mirror: every live
         row read once (the new token's from its input rows), the new token's
         K and V rows written into the cache, q read, the output and the side
-        output written."""
+        output written; with a score policy (one fade_append_decode_update
+        call) also every live score read and written and one token per
+        sequence demoted (its fp16 K and V rows read, its packed rows and
+        group scales written)."""
         w = self.w
         d, hkv = self.d, self.hkv
         per_fp = hkv * d * 4
@@ -213,8 +216,12 @@ class Workload:
         qo = self.B * self.hq * d * 2 * 2
         side = sum(F + m for m in self.M) * 4 if self.side else 0
         app = self.B * per_fp
+        upd = 0
+        if self.policy in ("h2o", "ema"):
+            packed = hkv * (d * (w["middle_k_bits"] + w["middle_v_bits"]) // 8 + 2 * 2 * (d // 32))
+            upd = sum(F + m for m in self.M) * 8 + self.B * (per_fp + packed)
         tokens = sum(F + m for m in self.M)
-        return kv + qo + side + app, tokens
+        return kv + qo + side + app + upd, tokens
 
     def moved_bytes(self, kept):
         """HBM bytes an eviction call moves, from its kept-slot map (old slot of
@@ -276,18 +283,19 @@ class Workload:
         for l in range(self.layers):
             tc = self.caches[l]
             q, kn, vn = self.pool[l][t % 4]
-            # the new token's append and the decode attention: one call
+            # the new token's append, the decode attention and, for a score
+            # policy, the score update (ACCUM / EMA) and the demotion: one call
             if events is not None and events[l] is not None:
                 events[l][0].record()
-            fade.fade_append_decode_attn(self.cfg, tc, kn, vn, q, self.out, self.tok, self.ws_dec)
+            if self.policy in ("h2o", "ema"):
+                mode = fade.SCORE_ACCUM if self.policy == "h2o" else fade.SCORE_EMA
+                fade.fade_append_decode_update(self.cfg, tc, kn, vn, q, self.out, self.tok, mode, self.ws_dec,
+                                               self.w["ema_decay"] if self.policy == "ema" else 0.0)
+            else:
+                fade.fade_append_decode_attn(self.cfg, tc, kn, vn, q, self.out, self.tok, self.ws_dec)
             if events is not None and events[l] is not None:
                 events[l][1].record()
-            # score update (ACCUM / EMA) and demotion: one launch
-            if self.policy == "h2o":
-                fade.fade_score_update_demote(self.cfg, tc, fade.SCORE_ACCUM, self.tok)
-            elif self.policy == "ema":
-                fade.fade_score_update_demote(self.cfg, tc, fade.SCORE_EMA, self.tok, self.w["ema_decay"])
-            else:
+            if self.policy not in ("h2o", "ema"):
                 fade.fade_cache_demote(self.cfg, tc)
             if due:
                 if evict_events is not None and evict_events[l] is not None:

@@ -309,6 +309,25 @@ int fade_append_decode_attn(const fade_config* cfg, fade_layer_cache* cache,
                             float* tok_attn, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * One whole decode step of a score policy short of the eviction:
+ * fade_append_decode_attn, then fade_score_update_demote (mode ACCUM or EMA,
+ * decay as there), in the decode launches (FADE post, "核心机制" and
+ * "EMA策略"; Transformer series (25), 1.3.1 H2O). tok_attn is required. The
+ * decode launch also quantizes the tokens that leave the recent window into
+ * the middle tier (middle rows no decode workgroup reads), and the merge
+ * kernel updates each slot's score as it writes the side output and commits
+ * the lengths. The cache, out and tok_attn end bit for bit as after the two
+ * calls. With a shared score row (one sum over every sequence's side output)
+ * or a PQ middle tier the update and demotion run as their own launches after
+ * the decode. Workspace: as for fade_tiered_decode_attn. Errors: those of the
+ * two calls.
+ */
+int fade_append_decode_update(const fade_config* cfg, fade_layer_cache* cache,
+                              const void* k_new, const void* v_new, const void* q, void* out,
+                              float* tok_attn, int32_t mode, float decay,
+                              void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * fade_tiered_decode_attn without a workspace, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation). Same arguments, kernels and results as

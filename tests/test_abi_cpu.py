@@ -272,6 +272,40 @@ def test_append_decode_attn_validation():
     assert call(good, good, good, good, null, good, big, cache=bad) == fade.FADE_ERR_INVALID_ARG
 
 
+def test_append_decode_update_validation():
+    """fade_append_decode_update rejects what fade_append_decode_attn and
+    fade_score_update_demote reject, before any launch."""
+    lib = fade.lib()
+    cfg = _cfg()
+    null = ctypes.c_void_p(0)
+    good = ctypes.c_void_p(16)
+    c = fade.LayerCache(1, 4096, 4 + 4096 + 65, 0, 16, 16, 16, 16, 16, 16, 16, 16)
+    big = 1 << 40
+
+    def call(k=good, v=good, q=good, out=good, tok=good, mode=fade.SCORE_EMA, decay=0.9, ws=good, ws_bytes=big,
+             cache=c):
+        return lib.fade_append_decode_update(ctypes.byref(cfg), ctypes.byref(cache), k, v, q, out, tok, mode,
+                                             ctypes.c_float(decay), ws, ws_bytes, null)
+
+    assert call(mode=fade.SCORE_PREFILL) == fade.FADE_ERR_INVALID_ARG     # not a decode mode
+    assert call(mode=7) == fade.FADE_ERR_INVALID_ARG
+    assert call(k=null) == fade.FADE_ERR_INVALID_ARG
+    assert call(v=ctypes.c_void_p(24)) == fade.FADE_ERR_INVALID_ARG
+    assert call(q=null) == fade.FADE_ERR_INVALID_ARG
+    assert call(out=ctypes.c_void_p(8)) == fade.FADE_ERR_INVALID_ARG
+    assert call(tok=null) == fade.FADE_ERR_INVALID_ARG                    # the update needs the side output
+    assert call(tok=ctypes.c_void_p(18)) == fade.FADE_ERR_INVALID_ARG
+    for decay in (-0.1, 1.5, float("nan")):
+        assert call(decay=decay) == fade.FADE_ERR_INVALID_ARG
+    no_scores = fade.LayerCache(1, 4096, 4 + 4096 + 65, 0, 16, 16, 16, 16, 16, 16, 16, None)
+    assert call(cache=no_scores) == fade.FADE_ERR_INVALID_ARG
+    assert call(ws=null) == fade.FADE_ERR_WORKSPACE
+    need = fade.workspace_bytes(cfg, fade.WS_DECODE, 1, 4096)
+    assert call(ws_bytes=need - 1) == fade.FADE_ERR_WORKSPACE
+    bad = fade.LayerCache(1, 10, 999, 0, 16, 16, 16, 16, 16, 16, 16, 16)
+    assert call(cache=bad) == fade.FADE_ERR_INVALID_ARG
+
+
 def test_rope_scheme_validation():
     """Each RoPE scheme's parameters are checked on the host, before any launch
     (a zero-row rotation is a no-op once the configuration is valid)."""

@@ -101,12 +101,13 @@ def _build(cfg, lengths, seed, cap_mid, score_kind, shared):
 
 
 def _run_loop(cfg, lengths, steps, mode, policy, period, seed, cap_mid, score_kind, shared=False, decay=0.9,
-              fused=False, trace=None, app_fused=False, outs=None):
+              fused=False, trace=None, app_fused=False, outs=None, step_fused=False):
     """fused: the score update and demotion as one fade_score_update_demote
     call; app_fused: the append and the decode as one fade_append_decode_attn
     call; trace: a list that receives every sequence's raw GPU state after
     every step; outs: a list that receives each step's output and side
-    output."""
+    output; step_fused: the append, decode, score update and demotion as one
+    fade_append_decode_update call."""
     tc, refs = _build(cfg, lengths, seed, cap_mid, score_kind, shared)
     for b, r in enumerate(refs):
         assert_state_equal(seq_state(tc, b), r, check_scores=False)
@@ -134,13 +135,17 @@ def _run_loop(cfg, lengths, steps, mode, policy, period, seed, cap_mid, score_ki
 
         out = torch.zeros(B, hq, d, dtype=torch.float32, device=DEV)
         tok = torch.full((B, tc.cap_T), -1.0, dtype=torch.float32, device=DEV) if side else None
-        if app_fused:
+        smode = fade.SCORE_ACCUM if mode == "accum" else fade.SCORE_EMA
+        if step_fused:
+            fade.fade_append_decode_update(cfg, tc, dev16(kn), dev16(vn), qt.to(DEV), out, tok, smode, ws_dec, decay)
+        elif app_fused:
             fade.fade_append_decode_attn(cfg, tc, dev16(kn), dev16(vn), qt.to(DEV), out, tok, ws_dec)
         else:
             fade.fade_cache_append(cfg, tc, dev16(kn), dev16(vn))
             fade.fade_tiered_decode_attn(cfg, tc, qt.to(DEV), out, tok, ws_dec)
-        smode = fade.SCORE_ACCUM if mode == "accum" else fade.SCORE_EMA
-        if side and fused:
+        if step_fused:
+            pass
+        elif side and fused:
             fade.fade_score_update_demote(cfg, tc, smode, tok, decay)
         else:
             if side:
@@ -357,3 +362,45 @@ def test_append_decode_fused_full_ring_equals_two_calls():
         lens = tc.lens.cpu().numpy().reshape(B, 4)
         assert lens[0, 2] == lens[1, 2] == cfg.recent_window + 1      # the rings (window + 1 slots) are full
     _same_trace(runs[0][0], runs[1][0], runs[0][1], runs[1][1])
+
+
+# The whole decode step short of the eviction as one call
+# (fade_append_decode_update: append, decode attention, score update and
+# demotion) against the oracle, and bit for bit against the separate calls.
+def test_closed_loop_serving_batch_step_fused():
+    cfg = _cfg(128, 32, 8, 4, 64, 256, 4, 2, rope_theta=5e5)
+    lengths = [1500, 300, 900, 2, 325, 700, 1100, 333]
+    nf, ne = _run_loop(cfg, lengths, 16, "ema", "score", 1, 4312, cap_mid=257, score_kind="ema", step_fused=True)
+    assert ne > 0
+
+
+def test_closed_loop_qwen_like_accum_step_fused():
+    cfg = _cfg(128, 16, 2, 4, 64, 400, 4, 2, rope_theta=1e6)
+    nf, ne = _run_loop(cfg, [1200], 24, "accum", "score", 1, 4101, cap_mid=464, score_kind="h2o", step_fused=True)
+    assert ne > 0
+
+
+def test_closed_loop_no_sinks_window1_step_fused():
+    """No sinks, a recent window of one token and a one-row middle budget: a
+    demotion every step, of the token appended one step before."""
+    cfg = _cfg(64, 8, 2, 0, 1, 0, 4, 2, rope_theta=1e4)
+    nf, ne = _run_loop(cfg, [50, 3, 1], 12, "ema", "score", 1, 4501, cap_mid=1, score_kind="ema", step_fused=True)
+    assert ne > 0
+
+
+@pytest.mark.parametrize("mode,shared,d,bf16", [("ema", False, 128, False), ("accum", False, 64, True),
+                                                ("accum", True, 64, False)])
+def test_step_fused_equals_separate_calls(mode, shared, d, bf16):
+    """State, output and side output after every step, bit for bit, against
+    fade_cache_append + fade_tiered_decode_attn + fade_score_update_demote;
+    sinks still filling in one sequence; a shared row takes the separate
+    update and demotion launches."""
+    cfg = _cfg(d, 16, 4, 4, 16, 64, 4, 2, q_dtype="bf16" if bf16 else "f16", rope_theta=5e5)
+    lengths = [400] * 3 if shared else [400, 90, 3, 1]
+    kw = dict(steps=12, mode=mode, policy="score", period=3, seed=4322, cap_mid=64 + 3, score_kind="ema",
+              shared=shared)
+    t_sep, t_fus, o_sep, o_fus = [], [], [], []
+    _run_loop(cfg, lengths, fused=True, trace=t_sep, outs=o_sep, **kw)
+    _run_loop(cfg, lengths, step_fused=True, trace=t_fus, outs=o_fus, **kw)
+    assert len(t_sep) == 12
+    _same_trace(t_sep, t_fus, o_sep, o_fus)

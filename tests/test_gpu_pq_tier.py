@@ -164,7 +164,7 @@ def _follow(r, kept_row, policy):
     oc.evict(r, c.int4_budget, policy, evicted=forced)
 
 
-def _loop(cfg, lengths, steps, mode, policy, period, seed, cap_mid, fused=False, app_fused=False):
+def _loop(cfg, lengths, steps, mode, policy, period, seed, cap_mid, fused=False, app_fused=False, step_fused=False):
     cb = _codebooks(cfg, seed + 7)
     tc, refs = _ragged(cfg, lengths, cap_mid, seed, cb, score_kind=None if policy == "position" else "ema")
     for b, r in enumerate(refs):
@@ -189,13 +189,17 @@ def _loop(cfg, lengths, steps, mode, policy, period, seed, cap_mid, fused=False,
             np.float16)
         out = torch.zeros(B, hq, d, dtype=torch.float32, device=DEV)
         tok = torch.full((B, tc.cap_T), -1.0, dtype=torch.float32, device=DEV) if side else None
-        if app_fused:                            # one call: append, then attend
+        smode = fade.SCORE_ACCUM if mode == "accum" else fade.SCORE_EMA
+        if step_fused:                           # one call: append, attend, update, demote
+            fade.fade_append_decode_update(cfg, tc, dev16(kn), dev16(vn), dev16(q), out, tok, smode, ws_dec, 0.9)
+        elif app_fused:                          # one call: append, then attend
             fade.fade_append_decode_attn(cfg, tc, dev16(kn), dev16(vn), dev16(q), out, tok, ws_dec)
         else:
             fade.fade_cache_append(cfg, tc, dev16(kn), dev16(vn))
             fade.fade_tiered_decode_attn(cfg, tc, dev16(q), out, tok, ws_dec)
-        smode = fade.SCORE_ACCUM if mode == "accum" else fade.SCORE_EMA
-        if side and fused:                       # one call: update, then demote
+        if step_fused:
+            pass
+        elif side and fused:                       # one call: update, then demote
             fade.fade_score_update_demote(cfg, tc, smode, tok, 0.9)
         else:
             if side:
@@ -275,4 +279,12 @@ def test_pq_closed_loop_append_decode_fused():
     sinks."""
     cfg = _cfg(d=128, hq=32, hkv=8, w=16, budget=96)
     refs, n = _loop(cfg, [500, 150, 2, 260], 8, "ema", "score", 1, 932, cap_mid=97, fused=True, app_fused=True)
+    assert n > 0
+
+
+def test_pq_closed_loop_step_fused():
+    """fade_append_decode_update over a PQ middle tier (the update and the PQ
+    demotion as launches of their own) against the oracle."""
+    cfg = _cfg(d=128, hq=32, hkv=8, w=16, budget=96)
+    refs, n = _loop(cfg, [500, 150, 2, 260], 8, "accum", "score", 1, 933, cap_mid=97, step_fused=True)
     assert n > 0

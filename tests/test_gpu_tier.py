@@ -104,7 +104,8 @@ def test_tier_decode_attention_ragged():
         assert np.all(side[b, t1:] == 0)
 
 
-def _loop(cfg, lengths, steps, mode, policy, period, seed, cap_mid, cap_low, score_kind, shared=False, fused=False, app_fused=False):
+def _loop(cfg, lengths, steps, mode, policy, period, seed, cap_mid, cap_low, score_kind, shared=False, fused=False, app_fused=False,
+          step_fused=False):
     oc_cfg = ocfg(cfg)
     f, il = oc_cfg.freqs(), oc_cfg.rope_interleaved
     B, hq, hkv, d = len(lengths), cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
@@ -152,13 +153,17 @@ def _loop(cfg, lengths, steps, mode, policy, period, seed, cap_mid, cap_low, sco
             np.float16)
         out = torch.zeros(B, hq, d, dtype=torch.float32, device=DEV)
         tok = torch.full((B, tc.cap_T), -1.0, dtype=torch.float32, device=DEV) if side else None
-        if app_fused:                            # one call: append, then attend
+        smode = fade.SCORE_ACCUM if mode == "accum" else fade.SCORE_EMA
+        if step_fused:                           # one call: append, attend, update, demote
+            fade.fade_append_decode_update(cfg, tc, dev16(kn), dev16(vn), dev16(q), out, tok, smode, ws_dec, 0.9)
+        elif app_fused:                          # one call: append, then attend
             fade.fade_append_decode_attn(cfg, tc, dev16(kn), dev16(vn), dev16(q), out, tok, ws_dec)
         else:
             fade.fade_cache_append(cfg, tc, dev16(kn), dev16(vn))
             fade.fade_tiered_decode_attn(cfg, tc, dev16(q), out, tok, ws_dec)
-        smode = fade.SCORE_ACCUM if mode == "accum" else fade.SCORE_EMA
-        if side and fused:                       # one call: update, then demote
+        if step_fused:
+            pass
+        elif side and fused:                       # one call: update, then demote
             fade.fade_score_update_demote(cfg, tc, smode, tok, 0.9)
         else:
             if side:
@@ -260,4 +265,13 @@ def test_tier_closed_loop_append_decode_fused():
     cfg = _cfg(d=128, hq=32, hkv=8, w=16, b4=64, b2=32)
     refs, n = _loop(cfg, [600, 140, 97, 300, 3], 12, "ema", "score", 1, 742, cap_mid=65, cap_low=33,
                     score_kind="ema", fused=True, app_fused=True)
+    assert n > 0
+
+
+def test_tier_closed_loop_step_fused():
+    """The append, decode attention, score update and demotion as one
+    fade_append_decode_update call against the oracle, with the INT2 tier."""
+    cfg = _cfg(d=128, hq=32, hkv=8, w=16, b4=64, b2=32)
+    refs, n = _loop(cfg, [600, 140, 97, 300, 3], 12, "ema", "score", 1, 743, cap_mid=65, cap_low=33,
+                    score_kind="ema", step_fused=True)
     assert n > 0

@@ -185,6 +185,31 @@ __device__ __forceinline__ void quant_group32(const float* x, uint32_t* packed, 
 }
 
 // Offset-removed code of channel c (0..31) of a packed group, as float.
+// 32 fp16 values (64 bytes, 16-byte aligned) as floats
+__device__ __forceinline__ void load_group32_f16(const uint16_t* p, float* x) {
+  const uint4* v = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 w = v[i];
+    const uint32_t words[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[8 * i + 2 * j] = h2f((uint16_t)(words[j] & 0xFFFFu));
+      x[8 * i + 2 * j + 1] = h2f((uint16_t)(words[j] >> 16));
+    }
+  }
+}
+
+// A group's packed code words (quant_group32's order) to their row bytes
+template <int BITS>
+__device__ __forceinline__ void store_group_codes(uint8_t* dst, const uint32_t* packed) {
+  if constexpr (BITS == 4) {
+    *reinterpret_cast<uint4*>(dst) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  } else {
+    *reinterpret_cast<uint2*>(dst) = make_uint2(packed[0], packed[1]);
+  }
+}
+
 template <int BITS>
 __device__ __forceinline__ float code_at(const uint32_t* packed, int c) {
   constexpr int kPerWord = 32 / BITS;

@@ -77,10 +77,62 @@ struct DecodeArgs {
   const uint16_t* v_new;
   uint16_t* app_k;
   uint16_t* app_v;
-  int32_t* t_live;
+  int32_t* t_live;            // [B][2]: live length after the append, the new token's position or -1
+  // fade_append_decode_update: the demotion of fade_cache_demote in the same
+  // launch (demote set), into the middle tier's arrays below
+  int demote, W, mid_kb, mid_vb;
+  uint8_t* dm_kc;
+  uint8_t* dm_vc;
+  uint16_t* dm_ks;
+  uint16_t* dm_vs;
 };
 
 constexpr int kThreads = 256;
+
+// The demotion of fade_cache_demote (FADE post, "核心机制": tokens that leave
+// the recent window are quantized into the middle tier) for one (sequence,
+// KV head), in the decode launch of fade_append_decode_update: the rule of
+// demote_rows on the lengths after the append, one thread per task = (K or
+// V, 32-channel group). It writes middle rows from M on, which no decode
+// workgroup of the launch reads (they read rows below M), and the row of a
+// token appended in this call comes from its input row; the merge kernel
+// writes the lengths.
+template <int D>
+__device__ void decode_demote(const DecodeArgs& a, int b, int g, const AppendPlan& ap, int task) {
+  constexpr int NG = D / kGroup;
+  const int32_t* L = a.lens + 4 * b;
+  int M = min(max(L[1], 0), a.cap_mid);
+  int R = min(max(L[2], 0), a.ring) + (ap.slot >= 0 && !ap.to_sink);
+  int head = min(max(L[3], 0), a.ring - 1);
+  const int which = task / NG, grp = task - which * NG;
+  const size_t bg = (size_t)b * a.Hkv + g;
+  const int slots = a.n_sink + a.ring;
+  const int bits = which ? a.mid_vb : a.mid_kb;
+  uint8_t* codes = which ? a.dm_vc : a.dm_kc;
+  uint16_t* scales = which ? a.dm_vs : a.dm_ks;
+  while (R > a.W && M < a.cap_mid) {
+    const int slot = a.n_sink + head;
+    const uint16_t* src = slot == ap.slot ? (which ? a.v_new : a.k_new) + bg * D
+                                          : (which ? a.fp_v : a.fp_k) + (bg * slots + slot) * D;
+    float x[kGroup];
+    load_group32_f16(src + grp * kGroup, x);
+    const size_t drow = bg * a.cap_mid + M;
+    uint16_t sc;
+    if (bits == 4) {
+      uint32_t pk[4];
+      quant_group32<4>(x, pk, sc);
+      store_group_codes<4>(codes + drow * (D / 2) + grp * 16, pk);
+    } else {
+      uint32_t pk[2];
+      quant_group32<2>(x, pk, sc);
+      store_group_codes<2>(codes + drow * (D / 4) + grp * 8, pk);
+    }
+    scales[drow * NG + grp] = sc;
+    head = (head + 1) % a.ring;
+    --R;
+    ++M;
+  }
+}
 constexpr float kLazyMax = 3.f;
 constexpr int kSub = 64;          // tokens per wave sub-chunk (one per lane)
 
@@ -147,7 +199,7 @@ int decode_raw_stride(const Shape& s) { return s.cap_T + kSub; }
 size_t decode_ws_bytes(const Shape& s) {
   size_t n = align_up((size_t)s.batch * s.Hq * decode_nsplit(s) * (s.D + 2) * 4, 256);
   n += align_up((size_t)s.batch * s.Hq * decode_raw_stride(s) * 4, 256);   // raw scores
-  n += align_up((size_t)s.batch * 4, 256);                                  // live lengths (append)
+  n += align_up((size_t)s.batch * 8, 256);                                  // live lengths (append)
   return n;
 }
 
@@ -314,8 +366,14 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
   const size_t part_hstride = (size_t)a.nsplit * (D + 2);
   // the live length after the append, once per sequence, as the merge kernel
   // would read it from the lengths
-  if (a.t_live && !a.is_low && lsplit == 0 && g == 0 && tid == 0)
-    a.t_live[b] = L[0] + L[1] + L[2] + (a.low_lens ? a.low_lens[b] : 0) + (app ? 1 : 0);
+  if (a.t_live && !a.is_low && lsplit == 0 && g == 0 && tid == 0) {
+    a.t_live[2 * b] = L[0] + L[1] + L[2] + (a.low_lens ? a.low_lens[b] : 0) + (app ? 1 : 0);
+    a.t_live[2 * b + 1] = app ? ap.pos : -1;
+  }
+  // the demotion, by the first middle split of each (sequence, KV head): a
+  // middle workgroup is among the first to start, ahead of the short fp16
+  // ones at the end of the grid
+  if (a.demote && !a.is_low && lsplit == a.n_fp && tid < 2 * (D / kGroup)) decode_demote<D>(a, b, g, ap, tid);
   if (n_tok <= 0) {
     for (int i = tid; i < NREP * (D + 2); i += kThreads) {
       const int h = i / (D + 2), c = i - h * (D + 2);
@@ -748,19 +806,43 @@ constexpr int kFinishBatch = 8;    // splits per lane per round
 // The append's bookkeeping for fade_append_decode_attn (t_live set): the merge
 // takes each sequence's live length from t_live, written by the tiers kernel,
 // instead of from the lengths, and one workgroup per sequence commits the
-// append (append_commit), no other reader of the lengths being left.
+// append (append_commit), no other reader of the lengths being left. With
+// fade_append_decode_update (demote set) the commit also takes the demotion
+// the tiers kernel made (demote_rows' rule: the same lengths), and the merge
+// applies the score update (upd >= 0: ACCUM / EMA) to each slot as it writes
+// the side output, the new token's slot starting from 0.
 struct AppendCommitArgs {
   const int32_t* t_live;   // nullptr: no append
   int32_t* lens;
   const int32_t* low_lens;
   float* scores;
   int n_sink, ring, cap_mid, shared;
+  int W, demote, upd;
+  float decay;
 };
 __device__ __forceinline__ void finish_commit(const AppendCommitArgs& x, int b, int cap_T) {
   int32_t* L = x.lens + 4 * b;
   const AppendPlan p = append_plan(L, x.low_lens ? max(x.low_lens[b], 0) : 0, x.n_sink, x.ring, x.cap_mid);
-  float* row = x.scores && (!x.shared || b == 0) ? x.scores + (size_t)(x.shared ? 0 : b) * cap_T : nullptr;
-  append_commit(L, p, row, cap_T);
+  // a fused score update writes the new slot's score itself
+  float* row = x.upd < 0 && x.scores && (!x.shared || b == 0) ? x.scores + (size_t)(x.shared ? 0 : b) * cap_T
+                                                               : nullptr;
+  if (!x.demote) {
+    append_commit(L, p, row, cap_T);
+    return;
+  }
+  const bool app = p.slot >= 0;
+  int M = min(max(L[1], 0), x.cap_mid), R = p.R + (app && !p.to_sink);
+  int head = min(max(L[3], 0), x.ring - 1);
+  while (R > x.W && M < x.cap_mid) {
+    head = (head + 1) % x.ring;
+    --R;
+    ++M;
+  }
+  if (app && row && p.pos < cap_T) row[p.pos] = 0.f;
+  if (app && p.to_sink) L[0] = p.S + 1;
+  L[1] = M;
+  L[2] = R;
+  L[3] = head;
 }
 
 template <int LN>
@@ -857,11 +939,17 @@ __global__ __launch_bounds__(256) void k_decode_finish(const float* __restrict__
   }
   if (ax.t_live && j == 0 && tid == 0) finish_commit(ax, b, cap_T);
   if (!tok_attn) return;
-  const int T = ax.t_live ? ax.t_live[b]
+  const int T = ax.t_live ? ax.t_live[2 * b]
                           : lens[4 * b] + lens[4 * b + 1] + lens[4 * b + 2] + (low_lens ? low_lens[b] : 0);
+  const int pos_new = ax.upd >= 0 ? ax.t_live[2 * b + 1] : -1;   // the appended token's slot, or -1
+  float* __restrict__ srow = ax.upd >= 0 ? ax.scores + (size_t)b * cap_T : nullptr;
   float* red = ml + 2 * Hq;
   for (int j0 = j * kFinishSlots; j0 < cap_T; j0 += nb * kFinishSlots) {
     const int u0 = tid % kFinishSlots, jj = j0 + u0, hg = tid / kFinishSlots;
+    // the slot's score for the fused update, loaded ahead of the raw scores
+    // so that its latency overlaps theirs
+    const bool upd_slot = srow && hg == 0 && jj < T && jj < cap_T;
+    const float s_old = upd_slot && jj != pos_new ? srow[jj] : 0.f;
     float acc = 0.f;
     if (jj < T && jj < cap_T) {
       for (int h0 = hg; h0 < Hq; h0 += 4 * kFinishBatch) {
@@ -880,9 +968,11 @@ __global__ __launch_bounds__(256) void k_decode_finish(const float* __restrict__
     }
     red[hg * kFinishSlots + u0] = acc;
     __syncthreads();
-    if (hg == 0 && jj < cap_T)
-      tok_attn[(size_t)b * cap_T + jj] = ((red[u0] + red[kFinishSlots + u0]) + red[2 * kFinishSlots + u0]) +
-                                         red[3 * kFinishSlots + u0];
+    if (hg == 0 && jj < cap_T) {
+      const float av = ((red[u0] + red[kFinishSlots + u0]) + red[2 * kFinishSlots + u0]) + red[3 * kFinishSlots + u0];
+      tok_attn[(size_t)b * cap_T + jj] = av;
+      if (upd_slot) srow[jj] = score_update_value(s_old, av, ax.upd, ax.decay);
+    }
     __syncthreads();
   }
 }
@@ -981,7 +1071,7 @@ static void dispatch_rep(int n_rep, int kb, int vb, const DecodeArgs& a, dim3 gr
 
 hipError_t launch_decode(const Shape& s, const fade_layer_cache& c, const void* q, int q_bf16,
                          void* out, int out_dtype, float* tok_attn, void* ws, hipStream_t st,
-                         const uint16_t* k_new, const uint16_t* v_new) {
+                         const uint16_t* k_new, const uint16_t* v_new, int upd_mode, float decay) {
   const int nsplit = decode_nsplit(s);
   char* w = reinterpret_cast<char*>(ws);
   float* part = reinterpret_cast<float*>(w);
@@ -999,6 +1089,13 @@ hipError_t launch_decode(const Shape& s, const fade_layer_cache& c, const void* 
   ax.ring = s.ring;
   ax.cap_mid = s.cap_mid;
   ax.shared = s.shared;
+  // the fused score update and demotion: per-sequence score rows, a packed
+  // middle tier and the side output only (the caller checks)
+  const bool upd = k_new && upd_mode >= 0;
+  ax.W = s.W;
+  ax.demote = upd;
+  ax.upd = upd ? upd_mode : -1;
+  ax.decay = decay;
 
   DecodeArgs a;
   a.fp_k = reinterpret_cast<const uint16_t*>(c.fp_k);
@@ -1034,6 +1131,14 @@ hipError_t launch_decode(const Shape& s, const fade_layer_cache& c, const void* 
   a.app_k = reinterpret_cast<uint16_t*>(c.fp_k);
   a.app_v = reinterpret_cast<uint16_t*>(c.fp_v);
   a.t_live = k_new ? t_live : nullptr;
+  a.demote = upd;
+  a.W = s.W;
+  a.mid_kb = s.kb;
+  a.mid_vb = s.vb;
+  a.dm_kc = reinterpret_cast<uint8_t*>(c.mid_k_codes);
+  a.dm_vc = reinterpret_cast<uint8_t*>(c.mid_v_codes);
+  a.dm_ks = reinterpret_cast<uint16_t*>(c.mid_k_scales);
+  a.dm_vs = reinterpret_cast<uint16_t*>(c.mid_v_scales);
   const int n_main = a.n_fp + a.n_tier;
   auto dispatch = [&](const DecodeArgs& da, int n_splits, int kb, int vb) {
     const dim3 grid(n_splits * s.Hkv * s.batch);

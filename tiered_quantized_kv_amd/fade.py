@@ -69,6 +69,8 @@ _SIGS = {
     "fade_cache_demote": (ctypes.c_int, [_CFG, _CACHE, _P]),
     "fade_score_update_demote": (ctypes.c_int, [_CFG, _CACHE, ctypes.c_int32, _P, ctypes.c_float, _P]),
     "fade_append_decode_attn": (ctypes.c_int, [_CFG, _CACHE, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "fade_append_decode_update": (ctypes.c_int, [_CFG, _CACHE, _P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_float,
+                                                 _P, ctypes.c_size_t, _P]),
     "fade_tiered_decode_attn": (ctypes.c_int, [_CFG, _CACHE, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "fade_tiered_decode_attn_noalloc": (ctypes.c_int, [_CFG, _CACHE, _P, _P, _P, _P]),
     "fade_h2o_scores": (ctypes.c_int, [_CFG, ctypes.c_int32, _CACHE, _P, _P, ctypes.c_int32, ctypes.c_int32,
@@ -256,6 +258,12 @@ def fade_tiered_decode_attn(cfg, cache, q, out, tok_attn, ws, stream=None):
 def fade_append_decode_attn(cfg, cache, k_new, v_new, q, out, tok_attn, ws, stream=None):
     _check(lib().fade_append_decode_attn(ctypes.byref(cfg), cache.ref(), _p(k_new), _p(v_new), _p(q), _p(out),
                                          _p(tok_attn), _p(ws), ws.numel(), _s(stream)), "fade_append_decode_attn")
+
+
+def fade_append_decode_update(cfg, cache, k_new, v_new, q, out, tok_attn, mode, ws, decay=0.0, stream=None):
+    _check(lib().fade_append_decode_update(ctypes.byref(cfg), cache.ref(), _p(k_new), _p(v_new), _p(q), _p(out),
+                                           _p(tok_attn), mode, decay, _p(ws), ws.numel(), _s(stream)),
+           "fade_append_decode_update")
 
 
 def fade_tiered_decode_attn_noalloc(cfg, cache, q, out, tok_attn, stream=None):
