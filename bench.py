@@ -203,10 +203,10 @@ class Workload:
         call (one layer) at the current step, from the host mirror: every live
         row read once (the new token's from its input rows), the new token's
         K and V rows written into the cache, q read, the output and the side
-        output written; with a score policy (one fade_append_decode_update
-        call) also every live score read and written and one token per
-        sequence demoted (its fp16 K and V rows read, its packed rows and
-        group scales written)."""
+        output written, one token per sequence demoted (its fp16 K and V rows
+        read, its packed rows and group scales written: one
+        fade_append_decode_update call), and with a score policy every live
+        score read and written."""
         w = self.w
         d, hkv = self.d, self.hkv
         per_fp = hkv * d * 4
@@ -216,10 +216,10 @@ class Workload:
         qo = self.B * self.hq * d * 2 * 2
         side = sum(F + m for m in self.M) * 4 if self.side else 0
         app = self.B * per_fp
-        upd = 0
+        packed = hkv * (d * (w["middle_k_bits"] + w["middle_v_bits"]) // 8 + 2 * 2 * (d // 32))
+        upd = self.B * (per_fp + packed)
         if self.policy in ("h2o", "ema"):
-            packed = hkv * (d * (w["middle_k_bits"] + w["middle_v_bits"]) // 8 + 2 * 2 * (d // 32))
-            upd = sum(F + m for m in self.M) * 8 + self.B * (per_fp + packed)
+            upd += sum(F + m for m in self.M) * 8
         tokens = sum(F + m for m in self.M)
         return kv + qo + side + app + upd, tokens
 
@@ -283,20 +283,15 @@ class Workload:
         for l in range(self.layers):
             tc = self.caches[l]
             q, kn, vn = self.pool[l][t % 4]
-            # the new token's append, the decode attention and, for a score
-            # policy, the score update (ACCUM / EMA) and the demotion: one call
+            # the new token's append, the decode attention, the score update
+            # (ACCUM / EMA; none for the position policy) and the demotion: one call
             if events is not None and events[l] is not None:
                 events[l][0].record()
-            if self.policy in ("h2o", "ema"):
-                mode = fade.SCORE_ACCUM if self.policy == "h2o" else fade.SCORE_EMA
-                fade.fade_append_decode_update(self.cfg, tc, kn, vn, q, self.out, self.tok, mode, self.ws_dec,
-                                               self.w["ema_decay"] if self.policy == "ema" else 0.0)
-            else:
-                fade.fade_append_decode_attn(self.cfg, tc, kn, vn, q, self.out, self.tok, self.ws_dec)
+            mode = {"h2o": fade.SCORE_ACCUM, "ema": fade.SCORE_EMA}.get(self.policy, fade.SCORE_NONE)
+            fade.fade_append_decode_update(self.cfg, tc, kn, vn, q, self.out, self.tok, mode, self.ws_dec,
+                                           self.w["ema_decay"] if self.policy == "ema" else 0.0)
             if events is not None and events[l] is not None:
                 events[l][1].record()
-            if self.policy not in ("h2o", "ema"):
-                fade.fade_cache_demote(self.cfg, tc)
             if due:
                 if evict_events is not None and evict_events[l] is not None:
                     evict_events[l][0].record()

@@ -83,7 +83,9 @@ enum fade_rope_type {
   FADE_ROPE_INTERLEAVED = 0x100
 };
 enum fade_dtype { FADE_DTYPE_F16 = 0, FADE_DTYPE_BF16 = 1, FADE_DTYPE_F32 = 2 };
-enum fade_score_mode { FADE_SCORE_PREFILL = 0, FADE_SCORE_ACCUM = 1, FADE_SCORE_EMA = 2 };
+/* FADE_SCORE_NONE: no score update (the position policy); taken by
+ * fade_append_decode_update only. */
+enum fade_score_mode { FADE_SCORE_PREFILL = 0, FADE_SCORE_ACCUM = 1, FADE_SCORE_EMA = 2, FADE_SCORE_NONE = 3 };
 enum fade_policy { FADE_POLICY_SCORE = 0, FADE_POLICY_POSITION = 1 };
 enum fade_ws_op {
   FADE_WS_DECODE = 0,         /* fade_tiered_decode_attn      (max_len = cap_mid) */
@@ -309,18 +311,19 @@ int fade_append_decode_attn(const fade_config* cfg, fade_layer_cache* cache,
                             float* tok_attn, void* workspace, size_t ws_bytes, void* stream);
 
 /*
- * One whole decode step of a score policy short of the eviction:
- * fade_append_decode_attn, then fade_score_update_demote (mode ACCUM or EMA,
- * decay as there), in the decode launches (FADE post, "核心机制" and
- * "EMA策略"; Transformer series (25), 1.3.1 H2O). tok_attn is required. The
- * decode launch also quantizes the tokens that leave the recent window into
- * the middle tier (middle rows no decode workgroup reads), and the merge
+ * One whole decode step short of the eviction: fade_append_decode_attn, then
+ * fade_score_update_demote (mode ACCUM or EMA, decay as there) or, with mode
+ * FADE_SCORE_NONE (the position policy), fade_cache_demote, in the decode
+ * launches (FADE post, "核心机制" and "EMA策略"; Transformer series (25),
+ * 1.3.1 H2O). tok_attn is required for ACCUM and EMA and optional for NONE.
+ * The decode launch also quantizes the tokens that leave the recent window
+ * into the middle tier (middle rows no decode workgroup reads), and the merge
  * kernel updates each slot's score as it writes the side output and commits
- * the lengths. The cache, out and tok_attn end bit for bit as after the two
- * calls. With a shared score row (one sum over every sequence's side output)
- * or a PQ middle tier the update and demotion run as their own launches after
- * the decode. Workspace: as for fade_tiered_decode_attn. Errors: those of the
- * two calls.
+ * the lengths. The cache, out and tok_attn end bit for bit as after the
+ * separate calls. With a PQ middle tier, or a shared score row (one sum over
+ * every sequence's side output) and a score update, the update and demotion
+ * run as their own launches after the decode. Workspace: as for
+ * fade_tiered_decode_attn. Errors: those of the separate calls.
  */
 int fade_append_decode_update(const fade_config* cfg, fade_layer_cache* cache,
                               const void* k_new, const void* v_new, const void* q, void* out,

@@ -289,6 +289,14 @@ def test_append_decode_update_validation():
 
     assert call(mode=fade.SCORE_PREFILL) == fade.FADE_ERR_INVALID_ARG     # not a decode mode
     assert call(mode=7) == fade.FADE_ERR_INVALID_ARG
+    # no score update (the position policy): neither a score row nor a side
+    # output is needed, and the call stops at the workspace check
+    no_scores = fade.LayerCache(1, 4096, 4 + 4096 + 65, 0, 16, 16, 16, 16, 16, 16, 16, None)
+    assert call(mode=fade.SCORE_NONE, tok=null, ws=null, cache=no_scores) == fade.FADE_ERR_WORKSPACE
+    assert call(mode=fade.SCORE_NONE, tok=ctypes.c_void_p(18)) == fade.FADE_ERR_INVALID_ARG
+    # the other score calls do not take it
+    assert lib.fade_score_update_demote(ctypes.byref(cfg), ctypes.byref(c), fade.SCORE_NONE, good,
+                                        ctypes.c_float(0.0), null) == fade.FADE_ERR_INVALID_ARG
     assert call(k=null) == fade.FADE_ERR_INVALID_ARG
     assert call(v=ctypes.c_void_p(24)) == fade.FADE_ERR_INVALID_ARG
     assert call(q=null) == fade.FADE_ERR_INVALID_ARG
@@ -297,7 +305,6 @@ def test_append_decode_update_validation():
     assert call(tok=ctypes.c_void_p(18)) == fade.FADE_ERR_INVALID_ARG
     for decay in (-0.1, 1.5, float("nan")):
         assert call(decay=decay) == fade.FADE_ERR_INVALID_ARG
-    no_scores = fade.LayerCache(1, 4096, 4 + 4096 + 65, 0, 16, 16, 16, 16, 16, 16, 16, None)
     assert call(cache=no_scores) == fade.FADE_ERR_INVALID_ARG
     assert call(ws=null) == fade.FADE_ERR_WORKSPACE
     need = fade.workspace_bytes(cfg, fade.WS_DECODE, 1, 4096)

@@ -29,12 +29,13 @@ def test_decode_bytes_match_the_oracle_closed_form(name):
     qo = wl.B * wl.hq * wl.d * 2 * 2
     side = 4 * sum(F + m for m in wl.M) if wl.side else 0
     app = wl.B * wl.hkv * wl.d * 2 * 2           # the new token's fp16 K and V rows written into the cache
-    upd = 0
+    # per sequence one demoted token: fp16 K and V rows read, packed K and V
+    # codes and group scales written; with a score policy every live score
+    # read and written
+    packed = wl.hkv * (wl.d * (w["middle_k_bits"] + w["middle_v_bits"]) // 8 + 4 * (wl.d // 32))
+    upd = wl.B * (wl.hkv * wl.d * 4 + packed)
     if wl.policy in ("h2o", "ema"):
-        # every live score read and written; per sequence one demoted token:
-        # fp16 K and V rows read, packed K and V codes and group scales written
-        packed = wl.hkv * (wl.d * (w["middle_k_bits"] + w["middle_v_bits"]) // 8 + 4 * (wl.d // 32))
-        upd = 8 * sum(F + m for m in wl.M) + wl.B * (wl.hkv * wl.d * 4 + packed)
+        upd += 8 * sum(F + m for m in wl.M)
     assert nbytes == kv + qo + side + app + upd
     assert tokens == sum(F + m for m in wl.M)
 

@@ -135,7 +135,7 @@ def _run_loop(cfg, lengths, steps, mode, policy, period, seed, cap_mid, score_ki
 
         out = torch.zeros(B, hq, d, dtype=torch.float32, device=DEV)
         tok = torch.full((B, tc.cap_T), -1.0, dtype=torch.float32, device=DEV) if side else None
-        smode = fade.SCORE_ACCUM if mode == "accum" else fade.SCORE_EMA
+        smode = {"accum": fade.SCORE_ACCUM, "ema": fade.SCORE_EMA}.get(mode, fade.SCORE_NONE)
         if step_fused:
             fade.fade_append_decode_update(cfg, tc, dev16(kn), dev16(vn), qt.to(DEV), out, tok, smode, ws_dec, decay)
         elif app_fused:
@@ -389,18 +389,29 @@ def test_closed_loop_no_sinks_window1_step_fused():
 
 
 @pytest.mark.parametrize("mode,shared,d,bf16", [("ema", False, 128, False), ("accum", False, 64, True),
-                                                ("accum", True, 64, False)])
+                                                ("accum", True, 64, False), ("none", False, 128, True),
+                                                ("none", True, 64, False)])
 def test_step_fused_equals_separate_calls(mode, shared, d, bf16):
     """State, output and side output after every step, bit for bit, against
-    fade_cache_append + fade_tiered_decode_attn + fade_score_update_demote;
-    sinks still filling in one sequence; a shared row takes the separate
-    update and demotion launches."""
+    fade_cache_append + fade_tiered_decode_attn + fade_score_update_demote
+    (fade_cache_demote without a score update: the position policy, no side
+    output); sinks still filling in one sequence; a shared row with a score
+    update takes the separate update and demotion launches."""
     cfg = _cfg(d, 16, 4, 4, 16, 64, 4, 2, q_dtype="bf16" if bf16 else "f16", rope_theta=5e5)
     lengths = [400] * 3 if shared else [400, 90, 3, 1]
-    kw = dict(steps=12, mode=mode, policy="score", period=3, seed=4322, cap_mid=64 + 3, score_kind="ema",
-              shared=shared)
+    score = mode != "none"
+    kw = dict(steps=12, mode=mode, policy="score" if score else "position", period=3, seed=4322, cap_mid=64 + 3,
+              score_kind="ema" if score else None, shared=shared)
     t_sep, t_fus, o_sep, o_fus = [], [], [], []
     _run_loop(cfg, lengths, fused=True, trace=t_sep, outs=o_sep, **kw)
     _run_loop(cfg, lengths, step_fused=True, trace=t_fus, outs=o_fus, **kw)
     assert len(t_sep) == 12
     _same_trace(t_sep, t_fus, o_sep, o_fus)
+
+
+def test_closed_loop_llama3_8b_like_position_step_fused():
+    """The position policy's decode step as one fade_append_decode_update call
+    (no score update, no side output) against the oracle, bf16 queries."""
+    cfg = _cfg(128, 32, 8, 4, 128, 512, 4, 2, q_dtype="bf16", rope_theta=5e5)
+    nf, ne = _run_loop(cfg, [3000], 16, "none", "position", 1, 4401, cap_mid=513, score_kind=None, step_fused=True)
+    assert nf == 0 and ne == 16

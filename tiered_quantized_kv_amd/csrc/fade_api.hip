@@ -323,11 +323,13 @@ int fade_append_decode_update(const fade_config* cfg, fade_layer_cache* cache, c
                               size_t ws_bytes, void* stream) {
   int st = check_cfg(cfg);
   if (st) return st;
-  if (mode != FADE_SCORE_ACCUM && mode != FADE_SCORE_EMA) return FADE_ERR_INVALID_ARG;
+  if (mode != FADE_SCORE_ACCUM && mode != FADE_SCORE_EMA && mode != FADE_SCORE_NONE) return FADE_ERR_INVALID_ARG;
   if ((st = check_cache(cfg, cache))) return st;
   if (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new)) return FADE_ERR_INVALID_ARG;
   if (!q || !out || !aligned16(q) || !aligned16(out)) return FADE_ERR_INVALID_ARG;
-  if (!cache->scores || !tok_attn || !aligned(tok_attn, 4)) return FADE_ERR_INVALID_ARG;
+  if (tok_attn && !aligned(tok_attn, 4)) return FADE_ERR_INVALID_ARG;
+  const bool update = mode != FADE_SCORE_NONE;
+  if (update && (!cache->scores || !tok_attn)) return FADE_ERR_INVALID_ARG;
   if (mode == FADE_SCORE_EMA && !(decay >= 0.f && decay <= 1.f)) return FADE_ERR_INVALID_ARG;
   const Shape s = cache_shape(cfg, cache);
   if (!workspace || !aligned16(workspace) || ws_bytes < decode_ws_bytes(s)) return FADE_ERR_WORKSPACE;
@@ -335,14 +337,15 @@ int fade_append_decode_update(const fade_config* cfg, fade_layer_cache* cache, c
   const uint16_t* kn = reinterpret_cast<const uint16_t*>(k_new);
   const uint16_t* vn = reinterpret_cast<const uint16_t*>(v_new);
   const int q_bf16 = cfg->q_dtype == FADE_DTYPE_BF16;
-  if (s.shared || s.pq) {
-    // a shared score row sums every sequence's side output, and a PQ middle
-    // tier demotes into codebook indices: the update and the demotion follow
+  if (s.pq || (s.shared && update)) {
+    // a PQ middle tier demotes into codebook indices, and a shared score row
+    // sums every sequence's side output: the update and the demotion follow
     // as their own launches
     hipError_t e = launch_decode(s, *cache, q, q_bf16, out, cfg->out_dtype, tok_attn, workspace, hs, kn, vn);
     if (e != hipSuccess) return hip_status(e);
     if (s.pq) {
-      if ((e = launch_score_update(s, *cache, mode, tok_attn, decay, hs)) != hipSuccess) return hip_status(e);
+      if (update && (e = launch_score_update(s, *cache, mode, tok_attn, decay, hs)) != hipSuccess)
+        return hip_status(e);
       return hip_status(launch_demote_pq(s, *cache, hs));
     }
     return hip_status(launch_score_update_demote(s, *cache, mode, tok_attn, decay, hs));

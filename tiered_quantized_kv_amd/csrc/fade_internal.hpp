@@ -91,10 +91,10 @@ int decode_chunk(const Shape& s);                 // middle rows per split
 int decode_nsplit(const Shape& s);                // splits incl. the fp16 split
 size_t decode_ws_bytes(const Shape& s);
 // k_new / v_new set: the append of fade_cache_append first, in the same
-// launches (fade_append_decode_attn); with upd_mode >= 0 (ACCUM / EMA) also
-// the score update and the demotion of fade_score_update_demote
-// (fade_append_decode_update: tok_attn set, per-sequence score rows, a packed
-// middle tier)
+// launches (fade_append_decode_attn); with upd_mode >= 0 also the demotion
+// and, for ACCUM / EMA, the score update of fade_score_update_demote
+// (fade_append_decode_update: a packed middle tier; for an update, tok_attn
+// set and per-sequence score rows)
 hipError_t launch_decode(const Shape& s, const fade_layer_cache& c, const void* q,
                          int q_bf16, void* out, int out_dtype, float* tok_attn, void* ws,
                          hipStream_t st, const uint16_t* k_new = nullptr, const uint16_t* v_new = nullptr,

@@ -1089,12 +1089,13 @@ hipError_t launch_decode(const Shape& s, const fade_layer_cache& c, const void* 
   ax.ring = s.ring;
   ax.cap_mid = s.cap_mid;
   ax.shared = s.shared;
-  // the fused score update and demotion: per-sequence score rows, a packed
-  // middle tier and the side output only (the caller checks)
+  // the fused demotion (upd_mode >= 0) and score update (ACCUM / EMA: per-
+  // sequence score rows and the side output; the caller checks), with a
+  // packed middle tier
   const bool upd = k_new && upd_mode >= 0;
   ax.W = s.W;
   ax.demote = upd;
-  ax.upd = upd ? upd_mode : -1;
+  ax.upd = upd && upd_mode != FADE_SCORE_NONE ? upd_mode : -1;
   ax.decay = decay;
 
   DecodeArgs a;

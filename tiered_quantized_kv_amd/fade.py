@@ -18,7 +18,7 @@ ROPE_SCHEME_MASK, ROPE_INTERLEAVED = 0xFF, 0x100
 _ROPE = {"default": ROPE_DEFAULT, "llama3": ROPE_LLAMA3, "linear": ROPE_LINEAR, "ntk": ROPE_NTK,
          "yarn": ROPE_YARN, "none": ROPE_NONE, "dynamic": ROPE_DYNAMIC, "proportional": ROPE_PROPORTIONAL}
 DTYPE_F16, DTYPE_BF16, DTYPE_F32 = 0, 1, 2
-SCORE_PREFILL, SCORE_ACCUM, SCORE_EMA = 0, 1, 2
+SCORE_PREFILL, SCORE_ACCUM, SCORE_EMA, SCORE_NONE = 0, 1, 2, 3
 POLICY_SCORE, POLICY_POSITION = 0, 1
 WS_DECODE, WS_H2O_PREFILL, WS_EVICT, WS_PREFILL_BUILD = 0, 1, 2, 3
 
