@@ -415,3 +415,43 @@ def test_closed_loop_llama3_8b_like_position_step_fused():
     cfg = _cfg(128, 32, 8, 4, 128, 512, 4, 2, q_dtype="bf16", rope_theta=5e5)
     nf, ne = _run_loop(cfg, [3000], 16, "none", "position", 1, 4401, cap_mid=513, score_kind=None, step_fused=True)
     assert nf == 0 and ne == 16
+
+
+@pytest.mark.parametrize("mode", ["ema", "none"])
+def test_step_fused_full_middle_equals_separate_calls(mode):
+    """No eviction: the middle tier reaches its capacity, the demotion stops,
+    the rings fill and the appends stop, in both paths alike, bit for bit
+    (the last sequence still fills its sinks and ring)."""
+    cfg = _cfg(128, 16, 4, 4, 8, 32, 4, 2, rope_theta=5e5)
+    lengths = [100, 60, 40, 2]
+    cap_mid = 32 + 3
+    B, hq, hkv, d = len(lengths), cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    smode = fade.SCORE_EMA if mode == "ema" else fade.SCORE_NONE
+    runs = []
+    for fused in (False, True):
+        tc, refs = _build(cfg, lengths, 4340, cap_mid, "ema" if mode == "ema" else None, False)
+        ws_dec = fade.workspace(cfg, fade.WS_DECODE, B, cap_mid)
+        gen = synth.rng(4340, 5)
+        trace, outs = [], []
+        for step in range(24):
+            kn = synth.normal(gen, B, hkv, d).astype(np.float16)
+            vn = synth.normal(gen, B, hkv, d).astype(np.float16)
+            q = synth.normal(gen, B, hq, d).astype(np.float16)
+            out = torch.zeros(B, hq, d, dtype=torch.float32, device=DEV)
+            tok = torch.full((B, tc.cap_T), -1.0, dtype=torch.float32, device=DEV) if mode == "ema" else None
+            if fused:
+                fade.fade_append_decode_update(cfg, tc, dev16(kn), dev16(vn), dev16(q), out, tok, smode, ws_dec, 0.9)
+            else:
+                fade.fade_cache_append(cfg, tc, dev16(kn), dev16(vn))
+                fade.fade_tiered_decode_attn(cfg, tc, dev16(q), out, tok, ws_dec)
+                if mode == "ema":
+                    fade.fade_score_update_demote(cfg, tc, smode, tok, 0.9)
+                else:
+                    fade.fade_cache_demote(cfg, tc)
+            torch.cuda.synchronize()
+            trace.append([seq_state(tc, b) for b in range(B)])
+            outs.append((out.cpu().numpy(), None if tok is None else tok.cpu().numpy()))
+        runs.append((trace, outs))
+        lens = tc.lens.cpu().numpy().reshape(B, 4)
+        assert (lens[:3, 1] == cap_mid).all() and (lens[:3, 2] == cfg.recent_window + 1).all()   # both full
+    _same_trace(runs[0][0], runs[1][0], runs[0][1], runs[1][1])
