@@ -455,3 +455,14 @@ def test_step_fused_full_middle_equals_separate_calls(mode):
         lens = tc.lens.cpu().numpy().reshape(B, 4)
         assert (lens[:3, 1] == cap_mid).all() and (lens[:3, 2] == cfg.recent_window + 1).all()   # both full
     _same_trace(runs[0][0], runs[1][0], runs[0][1], runs[1][1])
+
+
+def test_closed_loop_llama32_like_shared_step_fused():
+    """fade_append_decode_update with a shared ACCUM score row (the update
+    and demotion as a launch of their own after the decode) against the
+    oracle, with eviction every 16 steps."""
+    cfg = _cfg(64, 32, 8, 4, 64, 128, 4, 4, rope_type="llama3", rope_theta=5e5, rope_factor=32.0,
+               rope_low_freq_factor=1.0, rope_high_freq_factor=4.0, rope_original_max_position=8192)
+    nf, ne = _run_loop(cfg, [700] * 4, 17, "accum", "score", 16, 4212, cap_mid=128 + 16, score_kind="h2o",
+                       shared=True, step_fused=True)
+    assert ne >= 4
