@@ -370,10 +370,10 @@ __global__ __launch_bounds__(kThreads) void k_decode_tiers(DecodeArgs a) {
     a.t_live[2 * b] = L[0] + L[1] + L[2] + (a.low_lens ? a.low_lens[b] : 0) + (app ? 1 : 0);
     a.t_live[2 * b + 1] = app ? ap.pos : -1;
   }
-  // the demotion, by the first middle split of each (sequence, KV head): a
-  // middle workgroup is among the first to start, ahead of the short fp16
-  // ones at the end of the grid
-  if (a.demote && !a.is_low && lsplit == a.n_fp && tid < 2 * (D / kGroup)) decode_demote<D>(a, b, g, ap, tid);
+  // the demotion, by the first fp16-tier split of each (sequence, KV head):
+  // the fp16 workgroups end well before the middle ones they run beside, so
+  // the extra work stays off the kernel's critical path
+  if (a.demote && !a.is_low && lsplit == 0 && tid < 2 * (D / kGroup)) decode_demote<D>(a, b, g, ap, tid);
   if (n_tok <= 0) {
     for (int i = tid; i < NREP * (D + 2); i += kThreads) {
       const int h = i / (D + 2), c = i - h * (D + 2);
